@@ -1,0 +1,274 @@
+/*
+ * oracle.c - plain CPU oracle for OUT_PROD through a block-quantized weight.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library. The HIP library never calls it and it
+ * shares no code, header or table with the HIP library.
+ *
+ * What it computes. The llama.cpp PR "cuda: out_prod accepts a quantized
+ * src0" (commit message and section "What") states that the backward of
+ * mul_mat(W, x) with respect to x is out_prod(W, grad^T), and that OUT_PROD
+ * now takes a quantized (or F16/BF16) src0 with F32 src1 and dst. Written
+ * out, with W stored as N rows of K elements, G the F32 gradient (T x N) and
+ * dst F32 (T x K):
+ *
+ *     dst[t][k] = sum_{n=0}^{N-1} W[n][k] * G[t][n]
+ *
+ * where W[n][k] is the value the stored block decodes to. The same page
+ * (section "What") computes it as "decode W to F32, then an F32 GEMM", so the
+ * plain definition above, with decoded values, is the whole method; this
+ * file writes that definition out:
+ *
+ *   1. decode every row of W to F32 with a scalar block decoder;
+ *   2. for every output, sum the N products in increasing n in double,
+ *      also summing their absolute values (the error normaliser);
+ *   3. round the double sum to F32 once.
+ *
+ * The only loop tiling is over blocks of t rows (several t rows share one
+ * pass over W); it changes no output's summation order. Threads, when asked
+ * for, split the t rows and likewise change no summation order.
+ *
+ * Block formats (GGUF; the pages only name them): fp16 fields are
+ * little-endian binary16; see the decoder functions for each layout. Build
+ * with -O2 -ffp-contract=off and no fast-math.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_BF16 = 30 };
+
+/* IEEE-754 binary16 -> binary32: 1 sign bit, 5 exponent bits (bias 15), 10
+ * fraction bits. Exponent 0: subnormal, value = frac * 2^-24. Exponent 31:
+ * infinity (frac 0) or NaN. Otherwise (1024 + frac) * 2^(exp - 25). Every
+ * binary16 value is exactly representable in binary32. */
+float oracle_half_to_float(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);
+    }
+    return (float)(sign ? -v : v);
+}
+
+/* bfloat16 -> binary32: the 16 bits are the upper half of the binary32. */
+float oracle_bf16_to_float(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    return x;
+}
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* Q4_K sub-scale j and sub-min j (each 6 bits) from the 12-byte field s[].
+ * GGUF layout: for j < 4 the sub-scale is the low 6 bits of s[j] and the
+ * sub-min the low 6 bits of s[j+4]. For j >= 4 the low 4 bits of the
+ * sub-scale are the low nibble of s[j+4] and its high 2 bits are the top 2
+ * bits of s[j-4]; the low 4 bits of the sub-min are the high nibble of
+ * s[j+4] and its high 2 bits the top 2 bits of s[j]. */
+static void q4k_scale_min(const uint8_t *s, int j, int *sc, int *m) {
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* Decode one row of K elements. Returns 0, or -1 for an unknown type or a
+ * K that is not a whole number of blocks. */
+int oracle_decode_row(int type, const uint8_t *row, int64_t K, float *out) {
+    int64_t k, b;
+    switch (type) {
+    case T_F32:
+        memcpy(out, row, (size_t)K * 4);
+        return 0;
+    case T_F16:
+        for (k = 0; k < K; k++) out[k] = oracle_half_to_float(rd16(row + 2 * k));
+        return 0;
+    case T_BF16:
+        for (k = 0; k < K; k++) out[k] = oracle_bf16_to_float(rd16(row + 2 * k));
+        return 0;
+    case T_Q8_0:
+        /* 34-byte block of 32 elements: fp16 scale d, then 32 int8 codes;
+         * element j = d * code[j]. */
+        if (K % 32) return -1;
+        for (b = 0; b < K / 32; b++) {
+            const uint8_t *blk = row + 34 * b;
+            float d = oracle_half_to_float(rd16(blk));
+            for (int j = 0; j < 32; j++) out[32 * b + j] = d * (float)(int8_t)blk[2 + j];
+        }
+        return 0;
+    case T_Q4_0:
+        /* 18-byte block of 32 elements: fp16 scale d, then 16 code bytes.
+         * Element j < 16 is the low nibble of code byte j, element j + 16
+         * its high nibble; value = d * (nibble - 8). */
+        if (K % 32) return -1;
+        for (b = 0; b < K / 32; b++) {
+            const uint8_t *blk = row + 18 * b;
+            float d = oracle_half_to_float(rd16(blk));
+            for (int j = 0; j < 16; j++) {
+                int lo = blk[2 + j] & 15, hi = blk[2 + j] >> 4;
+                out[32 * b + j] = d * (float)(lo - 8);
+                out[32 * b + j + 16] = d * (float)(hi - 8);
+            }
+        }
+        return 0;
+    case T_Q4_K:
+        /* 144-byte super-block of 256 elements: fp16 d, fp16 dmin, 12 bytes
+         * of sub-scales/sub-mins, 128 code bytes. Element e lies in 64-wide
+         * chunk c = e / 64 at r = e % 64: for r < 32 its code is the low
+         * nibble of code byte 32c + r and it uses sub-block 2c; otherwise
+         * the high nibble of code byte 32c + r - 32, sub-block 2c + 1.
+         * value = (d * sc_j) * q - (dmin * m_j), each product exact in F32,
+         * one rounding in the subtraction. */
+        if (K % 256) return -1;
+        for (b = 0; b < K / 256; b++) {
+            const uint8_t *blk = row + 144 * b;
+            float d = oracle_half_to_float(rd16(blk));
+            float dmin = oracle_half_to_float(rd16(blk + 2));
+            const uint8_t *s = blk + 4;
+            const uint8_t *qs = blk + 16;
+            for (int e = 0; e < 256; e++) {
+                int c = e / 64, r = e % 64, q, j, sc, m;
+                if (r < 32) {
+                    q = qs[32 * c + r] & 15;
+                    j = 2 * c;
+                } else {
+                    q = qs[32 * c + r - 32] >> 4;
+                    j = 2 * c + 1;
+                }
+                q4k_scale_min(s, j, &sc, &m);
+                float a = d * (float)sc;
+                float mm = dmin * (float)m;
+                float v = a * (float)q;
+                out[256 * b + e] = v - mm;
+            }
+        }
+        return 0;
+    default:
+        return -1;
+    }
+}
+
+int64_t oracle_row_bytes(int type, int64_t K) {
+    switch (type) {
+    case T_F32: return 4 * K;
+    case T_F16: case T_BF16: return 2 * K;
+    case T_Q8_0: return K % 32 ? -1 : K / 32 * 34;
+    case T_Q4_0: return K % 32 ? -1 : K / 32 * 18;
+    case T_Q4_K: return K % 256 ? -1 : K / 256 * 144;
+    default: return -1;
+    }
+}
+
+/* Decode all N rows of W (row pitch = oracle_row_bytes) into out (N x K). */
+int oracle_dequantize(int type, const uint8_t *W, int64_t K, int64_t N, float *out) {
+    int64_t rb = oracle_row_bytes(type, K);
+    if (rb < 0) return -1;
+    for (int64_t n = 0; n < N; n++)
+        if (oracle_decode_row(type, W + n * rb, K, out + n * K)) return -1;
+    return 0;
+}
+
+enum { TBLOCK = 8 };
+
+typedef struct {
+    const float *w;        /* decoded W, N x K */
+    const float *G;        /* T x N */
+    const int64_t *rows;   /* which t rows to compute */
+    int64_t nrows, K, N;
+    float *dst;            /* nrows x K */
+    double *acc, *abssum;  /* nrows x K */
+    int tid, nthreads;
+} job_t;
+
+/* Rows [i0, i1) of the selected list: for n in increasing order, for each
+ * row of the block and each k, add the double product w[n][k] * G[t][n]. */
+static void contract_block(const job_t *j, int64_t i0, int64_t i1) {
+    const int64_t K = j->K, N = j->N;
+    for (int64_t i = i0; i < i1; i++) {
+        memset(j->acc + i * K, 0, (size_t)K * sizeof(double));
+        memset(j->abssum + i * K, 0, (size_t)K * sizeof(double));
+    }
+    for (int64_t n = 0; n < N; n++) {
+        const float *wn = j->w + n * K;
+        for (int64_t i = i0; i < i1; i++) {
+            double g = (double)j->G[j->rows[i] * N + n];
+            double *acc = j->acc + i * K;
+            double *as = j->abssum + i * K;
+            for (int64_t k = 0; k < K; k++) {
+                double p = (double)wn[k] * g;
+                acc[k] += p;
+                as[k] += fabs(p);
+            }
+        }
+    }
+    for (int64_t i = i0; i < i1; i++)
+        for (int64_t k = 0; k < K; k++) j->dst[i * K + k] = (float)j->acc[i * K + k];
+}
+
+static void *contract_worker(void *arg) {
+    const job_t *j = (const job_t *)arg;
+    int64_t nblocks = (j->nrows + TBLOCK - 1) / TBLOCK;
+    for (int64_t blk = j->tid; blk < nblocks; blk += j->nthreads) {
+        int64_t i0 = blk * TBLOCK;
+        int64_t i1 = i0 + TBLOCK < j->nrows ? i0 + TBLOCK : j->nrows;
+        contract_block(j, i0, i1);
+    }
+    return NULL;
+}
+
+/* dst[i][k] = sum_n W[n][k] * G[rows[i]][n] for the nrows selected t rows
+ * (rows == NULL selects t = 0 .. nrows-1). acc receives the double sums,
+ * abssum the double sums of |W[n][k] * G[t][n]|, dst the F32 rounding of
+ * acc. Returns 0, or -1 on a bad type/K or an allocation failure. */
+int oracle_out_prod(int type, const uint8_t *W, const float *G, int64_t K, int64_t N, int64_t T,
+                    const int64_t *rows, int64_t nrows, float *dst, double *acc, double *abssum,
+                    int nthreads) {
+    if (oracle_row_bytes(type, K) < 0 || K < 0 || N < 0 || T < 0 || nrows < 0) return -1;
+    if (K == 0 || nrows == 0) return 0;
+    int64_t *own_rows = NULL;
+    if (!rows) {
+        if (nrows > T) return -1;
+        own_rows = (int64_t *)malloc((size_t)nrows * sizeof(int64_t));
+        if (!own_rows) return -1;
+        for (int64_t i = 0; i < nrows; i++) own_rows[i] = i;
+        rows = own_rows;
+    }
+    for (int64_t i = 0; i < nrows; i++)
+        if (rows[i] < 0 || rows[i] >= T) { free(own_rows); return -1; }
+    float *w = (float *)malloc((size_t)(N > 0 ? N : 1) * (size_t)K * sizeof(float));
+    if (!w) { free(own_rows); return -1; }
+    if (oracle_dequantize(type, W, K, N, w)) { free(w); free(own_rows); return -1; }
+
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    job_t jobs[256];
+    pthread_t th[256];
+    for (int t = 0; t < nthreads; t++) {
+        jobs[t] = (job_t){w, G, rows, nrows, K, N, dst, acc, abssum, t, nthreads};
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; t++) {
+        if (pthread_create(&th[t], NULL, contract_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    /* Any worker that failed to start has its blocks done here. */
+    for (int t = started + 1; t < nthreads; t++) contract_worker(&jobs[t]);
+    contract_worker(&jobs[0]);
+    for (int t = 1; t <= started; t++) pthread_join(th[t], NULL);
+    free(w);
+    free(own_rows);
+    return 0;
+}

@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs for OUT_PROD through a block-quantized weight.
+
+This module only draws random numbers and lays them out as bytes. It holds
+none of the method's arithmetic: no decoding, no scaling, no contraction.
+Both the HIP path and the CPU oracle consume what it produces, and neither
+is imported here.
+
+Weight storage (one row of W = K elements along k, stored as consecutive
+blocks; fp16 fields are little-endian; GGUF block formats):
+
+  F32   4 bytes per element
+  F16   2 bytes per element (IEEE binary16)
+  BF16  2 bytes per element (upper half of a binary32)
+  Q8_0  34 bytes per 32 elements: fp16 scale, then 32 signed 8-bit codes
+  Q4_0  18 bytes per 32 elements: fp16 scale, then 16 bytes of 4-bit codes
+  Q4_K  144 bytes per 256 elements: fp16 scale, fp16 min-scale, 12 bytes
+        holding eight 6-bit sub-scales and eight 6-bit sub-mins, then 128
+        bytes of 4-bit codes
+
+Distributions (uniform ranges are [lo, hi) for floats and inclusive for
+integers; N(0, s) takes s as the standard deviation):
+
+  Q8_0  scale U[1e-3, 1e-2) rounded to fp16 (nearest-even), codes U{-127..127}
+  Q4_0  scale U[1e-3, 1e-2) rounded to fp16, codes U{0..15}
+  Q4_K  scale and min-scale U[1e-4, 1e-3) rounded to fp16, sub-scales and
+        sub-mins U{0..63}, codes U{0..15}
+  dense W ~ N(0, 0.02) in F32, then rounded to F16 or BF16 (nearest-even)
+  G     ~ N(0, sigma) in F32
+
+Uniform 4-bit codes are drawn as uniform bytes (each byte is two independent
+uniform nibbles). The Q4_K 12-byte scale field is drawn as 12 uniform bytes:
+the field packs exactly 16 x 6 = 96 bits, every bit belongs to exactly one
+sub-scale or sub-min, so uniform bytes are uniform 6-bit values for every
+sub-scale and sub-min whatever the bit order of the pack.
+
+Draw order for one case, from numpy Generator(PCG64(seed)): scales (the
+scale, then the Q4_K min-scale), then the Q4_K scale field, then codes (or
+the dense values), then G.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# GGUF tensor-type ids
+F32, F16, Q4_0, Q8_0, Q4_K, BF16 = 0, 1, 2, 8, 12, 30
+
+TYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0", Q4_0: "q4_0", Q4_K: "q4_k"}
+TYPE_IDS = {v: k for k, v in TYPE_NAMES.items()}
+
+# (elements per block, bytes per block)
+_GEOMETRY = {F32: (1, 4), F16: (1, 2), BF16: (1, 2), Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144)}
+
+
+def block_geometry(wtype: int) -> tuple[int, int]:
+    return _GEOMETRY[wtype]
+
+
+def row_bytes(wtype: int, K: int) -> int:
+    blk, nbytes = _GEOMETRY[wtype]
+    if K % blk:
+        raise ValueError(f"K={K} is not a multiple of the {TYPE_NAMES[wtype]} block ({blk})")
+    return K // blk * nbytes
+
+
+def _fp16_uniform(rng, lo, hi, shape):
+    return rng.uniform(lo, hi, size=shape).astype(np.float16)  # numpy rounds to nearest-even
+
+
+def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite F32 values to the nearest BF16, ties to even; returns uint16 bits."""
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def make_weight(wtype: int, N: int, K: int, rng: np.random.Generator) -> np.ndarray:
+    """Draw a W of N rows x K elements; returns uint8 bytes shaped (N, row_bytes)."""
+    rb = row_bytes(wtype, K)
+    if wtype in (F32, F16, BF16):
+        w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+        if wtype == F32:
+            raw = w.view(np.uint8)
+        elif wtype == F16:
+            raw = w.astype(np.float16).view(np.uint8)
+        else:
+            raw = _f32_to_bf16_bits(w).view(np.uint8)
+        return np.ascontiguousarray(raw.reshape(N, rb))
+    blk, nbytes = _GEOMETRY[wtype]
+    nb = K // blk
+    out = np.zeros((N, nb, nbytes), dtype=np.uint8)
+    if wtype == Q8_0:
+        d = _fp16_uniform(rng, 1e-3, 1e-2, (N, nb))
+        q = rng.integers(-127, 128, size=(N, nb, 32), dtype=np.int8)
+        out[:, :, 0:2] = d.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 2:34] = q.view(np.uint8)
+    elif wtype == Q4_0:
+        d = _fp16_uniform(rng, 1e-3, 1e-2, (N, nb))
+        qs = rng.integers(0, 256, size=(N, nb, 16), dtype=np.uint8)
+        out[:, :, 0:2] = d.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 2:18] = qs
+    elif wtype == Q4_K:
+        d = _fp16_uniform(rng, 1e-4, 1e-3, (N, nb))
+        dmin = _fp16_uniform(rng, 1e-4, 1e-3, (N, nb))
+        scales = rng.integers(0, 256, size=(N, nb, 12), dtype=np.uint8)
+        qs = rng.integers(0, 256, size=(N, nb, 128), dtype=np.uint8)
+        out[:, :, 0:2] = d.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 2:4] = dmin.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 4:16] = scales
+        out[:, :, 16:144] = qs
+    else:
+        raise ValueError(f"unknown weight type {wtype}")
+    return out.reshape(N, rb)
+
+
+def make_grad(T: int, N: int, sigma: float, rng: np.random.Generator) -> np.ndarray:
+    g = rng.standard_normal((T, N), dtype=np.float32)
+    if sigma != 1.0:
+        g *= np.float32(sigma)
+    return g
+
+
+def make_case(wtype: int, N: int, K: int, T: int, seed: int, g_sigma: float = 1.0) -> dict:
+    """One seeded (W, G) pair in the draw order stated in the module docstring."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    W = make_weight(wtype, N, K, rng)
+    G = make_grad(T, N, g_sigma, rng)
+    return {"type": wtype, "N": N, "K": K, "T": T, "W": W, "G": G, "seed": seed}
+
+
+# The five named workloads: the up (4096 -> 14336) projection of a 4096-wide
+# model with a 14336-wide MLP at T=4096 tokens, its down (14336 -> 4096)
+# projection at a LoRA-style T=16, the 5120 x 17408 projection whose F32 copy
+# the llama.cpp PR's Memory note sizes, a square 4096 dense projection, and a
+# tiny Q8_0 case.
+WORKLOADS = {
+    "q8_0_n128_k256_t64": dict(type=Q8_0, N=128, K=256, T=64, seed=1001, g_sigma=1.0),
+    "dense_n4096_k4096_t512": dict(type=None, N=4096, K=4096, T=512, seed=1002, g_sigma=1.0),
+    "q4_0_n17408_k5120_t2048": dict(type=Q4_0, N=17408, K=5120, T=2048, seed=1003, g_sigma=1e-2),
+    "q4_k_n14336_k4096_t4096": dict(type=Q4_K, N=14336, K=4096, T=4096, seed=1004, g_sigma=1.0),
+    "q4_k_n4096_k14336_t16": dict(type=Q4_K, N=4096, K=14336, T=16, seed=1005, g_sigma=1.0),
+}
+
+
+def workload(name: str, wtype: int | None = None) -> dict:
+    """Materialise a named workload (the dense one needs wtype F32, F16 or BF16)."""
+    spec = dict(WORKLOADS[name])
+    t = spec.pop("type")
+    if t is None:
+        if wtype not in (F32, F16, BF16):
+            raise ValueError("the dense workload needs wtype F32, F16 or BF16")
+        t = wtype
+    elif wtype is not None and wtype != t:
+        raise ValueError(f"workload {name} is {TYPE_NAMES[t]}")
+    return make_case(t, spec["N"], spec["K"], spec["T"], spec["seed"], spec["g_sigma"])
