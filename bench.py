@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of OUT_PROD through a resident Q4_K weight on one MI355X.
+
+One step = the whole hot path on the two Q4_K shapes of a 4096-wide model
+with a 14336-wide MLP:
+  large-T  W = 14336 x 4096 (N x K), G = 4096 x 14336, dst = 4096 x 4096
+           -> the tiled fused dequant + F32-MFMA kernel
+  skinny   W = 4096 x 14336, G = 16 x 4096, dst = 16 x 14336
+           -> the one-pass small-T kernel
+Inputs are seeded synthetic data (workloads.py) resident in HBM before the
+timed region. value = whole-step F32 TFLOP/s (2*T*N*K per call).
+
+Prints ONE JSON line. --gpus N > 1 is refused: the path runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+PEAK_F32_TFLOPS = 157.3  # MI355X dense MFMA F32
+PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
+LARGE = "q4_k_n14336_k4096_t4096"
+SKINNY = "q4_k_n4096_k14336_t16"
+PROFILES = os.path.join(REPO, "profiles")
+KERNEL_SOURCES = ["quantized_weight_backward_amd/csrc/retro_kernels.h",
+                  "quantized_weight_backward_amd/csrc/retro_decode.h",
+                  "quantized_weight_backward_amd/csrc/retro_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(REPO, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(tag: str):
+    """HBM bytes per launch from a committed counter summary, or None when
+    the summary is missing or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, f"{tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"source_sha256:\s*(\w+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(case: dict, target_s: float = 12.0) -> dict:
+    """The CPU oracle (double accumulation, as it stands) on sampled t rows of
+    the large-T workload, all host cores; FLOPs counted as 2*N*K per row."""
+    import numpy as np
+
+    import oracle
+
+    cores = max(1, min(64, os.cpu_count() or 1))
+    N, K = case["N"], case["K"]
+    rows = np.arange(8 * cores) % case["T"]
+    t0 = time.perf_counter()
+    oracle.out_prod(case["type"], case["W"], case["G"], K, rows=rows, nthreads=cores)
+    first = time.perf_counter() - t0
+    nrows = int(len(rows) * max(1.0, target_s / max(first, 1e-3)))
+    nrows = max(len(rows), min(nrows, case["T"]))
+    rows = np.arange(nrows)
+    t0 = time.perf_counter()
+    oracle.out_prod(case["type"], case["W"], case["G"], K, rows=rows, nthreads=cores)
+    secs = time.perf_counter() - t0
+    flops = 2.0 * N * K * nrows
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nrows} of {case['T']} t rows of {LARGE} (full decode of W included), "
+                      f"{secs:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import quantized_weight_backward_amd as q
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs cuda:0"
+    dev = torch.device("cuda:0")
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return 0
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    large = wl.workload(LARGE)
+    skinny = wl.workload(SKINNY)
+    Wl = torch.from_numpy(large["W"]).to(dev)
+    Gl = torch.from_numpy(large["G"]).to(dev)
+    Dl = torch.empty((large["T"], large["K"]), dtype=torch.float32, device=dev)
+    # several copies of the skinny W (33 MB each) so that consecutive calls
+    # cannot be served from the 256 MB Infinity Cache
+    n_rot = 12
+    Ws = [torch.from_numpy(skinny["W"]).to(dev) for _ in range(n_rot)]
+    Gs = torch.from_numpy(skinny["G"]).to(dev)
+    Ds = torch.empty((skinny["T"], skinny["K"]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    v_large = q.choice(q.Q4_K, large["K"], large["N"], large["T"])
+    v_skinny = q.choice(q.Q4_K, skinny["K"], skinny["N"], skinny["T"])
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        q.out_prod(q.Q4_K, Wl, Gl, large["K"], out=Dl)
+        if ev is not None:
+            ev[1].record(stream)
+        q.out_prod(q.Q4_K, Ws[i % n_rot], Gs, skinny["K"], out=Ds)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_large = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3  # seconds
+    t_skinny = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
+
+    fl_large = 2.0 * large["T"] * large["N"] * large["K"]
+    fl_skinny = 2.0 * skinny["T"] * skinny["N"] * skinny["K"]
+    wbytes = float(skinny["W"].nbytes)
+    avg_large = float(t_large.mean())
+    avg_skinny = float(t_skinny.mean())
+    achieved = fl_large / avg_large / 1e12
+    traffic = read_traffic(f"tile_{LARGE}")
+    ms_per_step = wall / args.steps * 1e3
+    value = (fl_large + fl_skinny) / (wall / args.steps) / 1e12
+
+    skinny_tflops = fl_skinny / avg_skinny / 1e12
+    skinny_gbs = wbytes / avg_skinny / 1e9
+    t_roof = max(wbytes / (PEAK_HBM_GBS * 1e9), fl_skinny / (PEAK_F32_TFLOPS * 1e12))
+
+    out = {
+        "metric": "OUT_PROD TFLOP/s and weight GB/s vs roofline, Q4_K 4096x14336 T=4096 and T=16",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Q4_K blocks and N(0,1) F32 gradients)",
+        "config": {"workload": f"{LARGE} + {SKINNY}", "weight_type": "q4_k",
+                   "large_t": {"N": large["N"], "K": large["K"], "T": large["T"],
+                               "kernel": q.VARIANT_NAMES[v_large]},
+                   "skinny": {"N": skinny["N"], "K": skinny["K"], "T": skinny["T"],
+                              "kernel": q.VARIANT_NAMES[v_skinny], "w_copies_rotated": n_rot}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": f"out_prod_tile_kernel ({q.VARIANT_NAMES[v_large]})",
+                     "avg_launch_ms": round(avg_large * 1e3, 4), "min_launch_ms": round(float(t_large.min()) * 1e3, 4),
+                     "flops_per_launch": fl_large},
+        "skinny": {"kernel": "out_prod_skinny_kernel", "avg_launch_us": round(avg_skinny * 1e6, 3),
+                   "min_launch_us": round(float(t_skinny.min()) * 1e6, 3),
+                   "tflops": round(skinny_tflops, 3), "weight_gbs": round(skinny_gbs, 1),
+                   "hbm_frac": round(skinny_gbs / PEAK_HBM_GBS, 4),
+                   "f32_mfma_frac": round(skinny_tflops / PEAK_F32_TFLOPS, 4),
+                   "binding_roof_frac": round(t_roof / avg_skinny, 4),
+                   "weight_bytes": wbytes},
+        "kernel_source": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(large)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+/*
+ * retro_out_prod.h - C ABI of the MI355X (gfx950) OUT_PROD library.
+ *
+ * OUT_PROD through a resident block-quantized weight:
+ *
+ *     dst[t][k] = sum_{n=0}^{N-1} W[n][k] * G[t][n]
+ *
+ * This is the backward of mul_mat(W, x) with respect to x (llama.cpp PR #3
+ * "cuda: out_prod accepts a quantized src0", commit message: the backward of
+ * mul_mat(W, x) w.r.t. x is out_prod(W, grad^T)). The PR admits a contiguous
+ * quantized, F16 or BF16 src0 with F32 src1 and dst (section "What"); the
+ * Retrograd CUDA status page lists OUT_PROD for F32, F16, BF16 and quantized
+ * types (section "What works on the GPU"). W[n][k] is the value the stored
+ * block decodes to.
+ *
+ * Layouts (all row-major and contiguous; the caller owns every buffer):
+ *   W    N rows; row n starts at byte n * retro_row_bytes(type, K) and holds
+ *        K elements along k as consecutive blocks of the given type.
+ *   G    T x N float32 (the gradient in its natural layout; the transposition
+ *        of grad^T is implied by the indexing).
+ *   dst  T x K float32, overwritten (never read, never accumulated into).
+ * Block formats (GGUF; fp16 fields little-endian):
+ *   RETRO_F32   4 bytes per element
+ *   RETRO_F16   2 bytes per element (IEEE binary16)
+ *   RETRO_BF16  2 bytes per element (upper half of a binary32)
+ *   RETRO_Q8_0  34 bytes / 32 elements: fp16 d, 32 int8 q; value d*q
+ *   RETRO_Q4_0  18 bytes / 32 elements: fp16 d, 16 bytes of nibbles; element
+ *               j<16 = low nibble of byte j, j+16 = its high nibble;
+ *               value d*(q-8)
+ *   RETRO_Q4_K  144 bytes / 256 elements: fp16 d, fp16 dmin, 12 bytes of
+ *               eight 6-bit sub-scales sc_j and sub-mins m_j (GGUF packing),
+ *               128 bytes of nibbles (each 64-element chunk c uses 32 bytes:
+ *               low nibbles are sub-block 2c, high nibbles sub-block 2c+1);
+ *               value (d*sc_j)*q - dmin*m_j
+ *
+ * Pointers: W, G and dst are device pointers (hipMalloc'd or equivalent) and
+ * must be 16-byte aligned. dst must not overlap W or G. stream is a
+ * hipStream_t passed as void* (NULL = the null stream).
+ *
+ * Execution: every compute call is asynchronous on the stream, allocates no
+ * memory (no dequantized copy of W exists at any size, so the scratch
+ * budget of the prior sliced design - Retrograd CUDA status, sections
+ * "Building" and "Limitations" - is zero) and never falls back to the CPU:
+ * an unsupported call returns an error. The library holds no mutable global
+ * state; calls are thread-safe.
+ *
+ * Errors: functions returning int return RETRO_OK (0) or a negative code;
+ * nothing throws across the ABI; retro_strerror names a code.
+ */
+#ifndef RETRO_OUT_PROD_H
+#define RETRO_OUT_PROD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight types: the GGUF tensor-type ids. */
+enum {
+    RETRO_F32 = 0,
+    RETRO_F16 = 1,
+    RETRO_Q4_0 = 2,
+    RETRO_Q8_0 = 8,
+    RETRO_Q4_K = 12,
+    RETRO_BF16 = 30
+};
+
+/* Error codes. */
+enum {
+    RETRO_OK = 0,
+    RETRO_E_TYPE = -1,  /* unknown or unsupported weight type */
+    RETRO_E_SHAPE = -2, /* negative size, K not a whole number of blocks, or a
+                           size whose byte count overflows the limits below */
+    RETRO_E_NULL = -3,  /* NULL buffer where the call would touch memory */
+    RETRO_E_ALIGN = -4, /* W, G or dst not 16-byte aligned */
+    RETRO_E_ALIAS = -5, /* dst overlaps W or G */
+    RETRO_E_HIP = -6,   /* the HIP runtime reported an error at launch */
+    RETRO_E_VARIANT = -7 /* retro_out_prod_variant: variant unknown or not
+                            applicable to this type/shape */
+};
+
+/* Size limits: K, N and T are each below 2^31, and T*K, T*N and
+ * N*retro_row_bytes(type, K) are each below 2^62. */
+
+/*
+ * dst[t][k] = sum_n W[n][k] * G[t][n] for t < T, k < K.
+ *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_K
+ *   W       device, N * retro_row_bytes(type, K) bytes
+ *   G       device, T * N floats
+ *   dst     device, T * K floats, overwritten
+ *   K       elements per W row (a multiple of the block: 32 for Q8_0/Q4_0,
+ *           256 for Q4_K, 1 otherwise)
+ *   N       rows of W = the reduction length
+ *   T       rows of G and dst
+ * T == 0 or K == 0: returns RETRO_OK without touching memory (pointers may
+ * be NULL). N == 0: dst is filled with zeros (the empty sum).
+ * Returns RETRO_OK once the kernel is enqueued; a launch failure reported by
+ * HIP returns RETRO_E_HIP.
+ */
+int retro_out_prod(int type, const void *W, const float *G, float *dst, int64_t K, int64_t N,
+                   int64_t T, void *stream);
+
+/*
+ * Decode W to float32: out[n][k] = W[n][k], out is N x K floats (device,
+ * 16-byte aligned, must not overlap W). The conversion the PR's converters
+ * perform (section "What": dequantize through the converters mul_mat
+ * already uses), exposed so that decoded values can be checked bit for bit.
+ * The fused kernels of retro_out_prod decode with the same device functions.
+ * K == 0 or N == 0: RETRO_OK, nothing touched.
+ */
+int retro_dequantize(int type, const void *W, float *out, int64_t K, int64_t N, void *stream);
+
+/*
+ * 1 if retro_out_prod(type, ..., K, N, T) with valid, aligned, non-aliasing
+ * buffers would run, 0 otherwise (the analogue of the PR's supports_op rule,
+ * section "What": any contiguous src0 with an F32 converter, src1 and dst
+ * F32). Touches no device.
+ */
+int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T);
+
+/* Bytes per W row: K/32*34 (Q8_0), K/32*18 (Q4_0), K/256*144 (Q4_K), 4K
+ * (F32), 2K (F16, BF16). -1 for an unknown type, a negative K or a K that is
+ * not a whole number of blocks. Touches no device. */
+int64_t retro_row_bytes(int type, int64_t K);
+
+/* A static, NUL-terminated description of an error code (never NULL). */
+const char *retro_strerror(int code);
+
+/*
+ * Kernel variants (for tests and benchmarks; retro_out_prod chooses one):
+ *   RETRO_VARIANT_AUTO      what retro_out_prod runs
+ *   RETRO_VARIANT_SKINNY    one pass over W, all of n per workgroup; T <= 16
+ *   RETRO_VARIANT_TILE_*    tiled F32-MFMA kernel, tile = rows of T x columns
+ *                           of K per workgroup (256-column tiles need K tiles
+ *                           that are whole Q4_K super-blocks; Q4_K takes only
+ *                           those)
+ */
+enum {
+    RETRO_VARIANT_AUTO = 0,
+    RETRO_VARIANT_SKINNY = 1,
+    RETRO_VARIANT_TILE_128x128 = 2,
+    RETRO_VARIANT_TILE_128x256 = 3,
+    RETRO_VARIANT_TILE_64x128 = 4,
+    RETRO_VARIANT_TILE_64x64 = 5,
+    RETRO_VARIANT_TILE_64x256 = 6
+};
+
+/* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the
+ * variant does not apply to the type or shape. Same contract otherwise. */
+int retro_out_prod_variant(int variant, int type, const void *W, const float *G, float *dst,
+                           int64_t K, int64_t N, int64_t T, void *stream);
+
+/* The variant retro_out_prod would run for this type and shape, or a
+ * negative error code (as retro_out_prod_supported would refuse). Touches no
+ * device. */
+int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETRO_OUT_PROD_H */

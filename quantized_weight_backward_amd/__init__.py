@@ -1,0 +1,160 @@
+"""Python binding of the MI355X OUT_PROD library (libretro_out_prod.so).
+
+    dst[t][k] = sum_n W[n][k] * G[t][n]
+
+the backward of mul_mat(W, x) with respect to x through a resident
+block-quantized (Q8_0, Q4_0, Q4_K), F16, BF16 or F32 weight W (llama.cpp PR
+#3 "cuda: out_prod accepts a quantized src0", commit message and section
+"What"). This module marshals torch tensors into the C ABI of
+include/retro_out_prod.h and nothing else: every step runs in the HIP
+library. There is no CPU path; if the library is not built, importing this
+package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import _build
+
+F32, F16, Q4_0, Q8_0, Q4_K, BF16 = 0, 1, 2, 8, 12, 30
+TYPES = {"f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0, "q4_k": Q4_K}
+
+OK = 0
+E_TYPE, E_SHAPE, E_NULL, E_ALIGN, E_ALIAS, E_HIP, E_VARIANT = -1, -2, -3, -4, -5, -6, -7
+
+VARIANT_AUTO = 0
+VARIANT_SKINNY = 1
+VARIANT_TILE_128x128 = 2
+VARIANT_TILE_128x256 = 3
+VARIANT_TILE_64x128 = 4
+VARIANT_TILE_64x64 = 5
+VARIANT_TILE_64x256 = 6
+VARIANT_NAMES = {
+    VARIANT_SKINNY: "skinny", VARIANT_TILE_128x128: "tile_128x128", VARIANT_TILE_128x256: "tile_128x256",
+    VARIANT_TILE_64x128: "tile_64x128", VARIANT_TILE_64x64: "tile_64x64", VARIANT_TILE_64x256: "tile_64x256",
+}
+
+LIB_PATH = _build.LIB_PATH
+
+# The exported symbols, as declared in include/retro_out_prod.h.
+EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_dequantize", "retro_out_prod_supported",
+           "retro_out_prod_choice", "retro_row_bytes", "retro_strerror")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+            "python -m quantized_weight_backward_amd._build")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    lib.retro_out_prod.restype = i32
+    lib.retro_out_prod.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp]
+    lib.retro_out_prod_variant.restype = i32
+    lib.retro_out_prod_variant.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, vp]
+    lib.retro_dequantize.restype = i32
+    lib.retro_dequantize.argtypes = [i32, vp, vp, i64, i64, vp]
+    lib.retro_out_prod_supported.restype = i32
+    lib.retro_out_prod_supported.argtypes = [i32, i64, i64, i64]
+    lib.retro_out_prod_choice.restype = i32
+    lib.retro_out_prod_choice.argtypes = [i32, i64, i64, i64]
+    lib.retro_row_bytes.restype = i64
+    lib.retro_row_bytes.argtypes = [i32, i64]
+    lib.retro_strerror.restype = ctypes.c_char_p
+    lib.retro_strerror.argtypes = [i32]
+    return lib
+
+
+lib = _load()
+
+
+class RetroError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"{strerror(code)} (code {code})")
+        self.code = code
+
+
+def strerror(code: int) -> str:
+    return lib.retro_strerror(int(code)).decode()
+
+
+def row_bytes(wtype: int, K: int) -> int:
+    return int(lib.retro_row_bytes(int(wtype), int(K)))
+
+
+def supported(wtype: int, K: int, N: int, T: int) -> bool:
+    return lib.retro_out_prod_supported(int(wtype), int(K), int(N), int(T)) == 1
+
+
+def choice(wtype: int, K: int, N: int, T: int) -> int:
+    return int(lib.retro_out_prod_choice(int(wtype), int(K), int(N), int(T)))
+
+
+def _check(code: int) -> None:
+    if code != OK:
+        raise RetroError(code)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _device_tensor(t, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, stream=None):
+    """dst = out_prod(W, G): W packed bytes (N rows), G float32 T x N, dst float32 T x K.
+
+    W is any contiguous device tensor holding N * row_bytes(wtype, K) bytes.
+    Runs asynchronously on `stream` (default: torch's current stream).
+    """
+    import torch
+
+    _device_tensor(W, "W")
+    _device_tensor(G, "G")
+    if G.dtype != torch.float32 or G.dim() != 2:
+        raise ValueError("G must be a 2-D float32 tensor (T x N)")
+    T, N = G.shape
+    rb = row_bytes(wtype, K)
+    if rb < 0:
+        _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
+    if W.numel() * W.element_size() != N * rb:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.float32, device=G.device)
+    else:
+        _device_tensor(out, "out")
+        if out.dtype != torch.float32 or tuple(out.shape) != (T, K):
+            raise ValueError("out must be float32 T x K")
+    _check(lib.retro_out_prod_variant(int(variant), int(wtype), _ptr(W), _ptr(G), _ptr(out), int(K), int(N),
+                                      int(T), _stream_handle(stream)))
+    return out
+
+
+def dequantize(wtype: int, W, K: int, N: int, out=None, stream=None):
+    """Decoded float32 N x K copy of W (a test hook; out_prod never makes one)."""
+    import torch
+
+    _device_tensor(W, "W")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=W.device)
+    else:
+        _device_tensor(out, "out")
+    _check(lib.retro_dequantize(int(wtype), _ptr(W), _ptr(out), int(K), int(N), _stream_handle(stream)))
+    return out

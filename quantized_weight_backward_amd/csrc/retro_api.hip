@@ -1,0 +1,293 @@
+// retro_api.hip - the C ABI declared in include/retro_out_prod.h: argument
+// validation, kernel choice and launch. Host code only; the kernels live in
+// retro_kernels.h.
+//
+// The entry points follow the OUT_PROD admission rule of llama.cpp PR #3
+// ("cuda: out_prod accepts a quantized src0", section "What": any contiguous
+// src0 with an F32 converter, src1 and dst F32), but where that PR
+// dequantizes into a pool copy and calls an F32 GEMM, every call here is one
+// fused kernel with no allocation, and an unsupported call is an error, never
+// a CPU fallback.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "retro_kernels.h"
+#include "retro_out_prod.h"
+
+namespace {
+
+using namespace retro;
+
+constexpr int kNumCUs = 256;  // MI355X
+constexpr int64_t kDimLimit = int64_t(1) << 31;
+constexpr int64_t kByteLimit = int64_t(1) << 62;
+constexpr int64_t kGridLimit = int64_t(1) << 30;
+
+struct Geometry {
+    int block, bytes;
+};
+
+bool geometry(int type, Geometry& g) {
+    switch (type) {
+        case RETRO_F32: g = {1, 4}; return true;
+        case RETRO_F16: g = {1, 2}; return true;
+        case RETRO_BF16: g = {1, 2}; return true;
+        case RETRO_Q8_0: g = {32, 34}; return true;
+        case RETRO_Q4_0: g = {32, 18}; return true;
+        case RETRO_Q4_K: g = {256, 144}; return true;
+        default: return false;
+    }
+}
+
+int64_t row_bytes_of(int type, int64_t K) {
+    Geometry g;
+    if (!geometry(type, g) || K < 0 || K % g.block) return -1;
+    return K / g.block * g.bytes;
+}
+
+// a * b < limit for non-negative a, b.
+bool product_below(int64_t a, int64_t b, int64_t limit) { return a == 0 || b < limit / a; }
+
+int check_shape(int type, int64_t K, int64_t N, int64_t T) {
+    Geometry g;
+    if (!geometry(type, g)) return RETRO_E_TYPE;
+    if (K < 0 || N < 0 || T < 0) return RETRO_E_SHAPE;
+    if (K % g.block) return RETRO_E_SHAPE;
+    if (K >= kDimLimit || N >= kDimLimit || T >= kDimLimit) return RETRO_E_SHAPE;
+    const int64_t pitch = K / g.block * g.bytes;
+    if (!product_below(T, K, kByteLimit) || !product_below(T, N, kByteLimit) ||
+        !product_below(N, pitch, kByteLimit))
+        return RETRO_E_SHAPE;
+    return RETRO_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct TileVariant {
+    int id, bt, bk;
+    double penalty;  // relative cost per output of the smaller tiles
+};
+
+constexpr TileVariant kTiles[] = {
+    {RETRO_VARIANT_TILE_128x256, 128, 256, 1.00},
+    {RETRO_VARIANT_TILE_128x128, 128, 128, 1.00},
+    {RETRO_VARIANT_TILE_64x256, 64, 256, 1.05},
+    {RETRO_VARIANT_TILE_64x128, 64, 128, 1.08},
+    {RETRO_VARIANT_TILE_64x64, 64, 64, 1.20},
+};
+
+const TileVariant* find_tile(int variant) {
+    for (const auto& v : kTiles)
+        if (v.id == variant) return &v;
+    return nullptr;
+}
+
+bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t T) {
+    if (type == RETRO_Q4_K && v.bk % 256) return false;
+    return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit;
+}
+
+bool skinny_applies(int64_t K, int64_t T) { return T <= 16 && cdiv(K, 64) < kGridLimit; }
+
+// Pick the tile that minimises (tiles per CU, rounded up) x tile area x
+// penalty: the rounding is the wave quantisation over 256 CUs.
+int choose(int type, int64_t K, int64_t N, int64_t T) {
+    (void)N;
+    if (skinny_applies(K, T)) return RETRO_VARIANT_SKINNY;
+    int best = -1;
+    double best_cost = 0;
+    for (const auto& v : kTiles) {
+        if (!tile_applies(v, type, K, T)) continue;
+        const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk);
+        const double cost = double(cdiv(nt, kNumCUs)) * v.bt * v.bk * v.penalty;
+        if (best < 0 || cost < best_cost) {
+            best = v.id;
+            best_cost = cost;
+        }
+    }
+    return best < 0 ? RETRO_E_SHAPE : best;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? RETRO_OK : RETRO_E_HIP; }
+
+template <int TYPE, int WA, int WB, int WGT, int WGK>
+int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+    using S = TileShape<TYPE, WA, WB, WGT, WGK>;
+    TileArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.G = G;
+    a.dst = dst;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(TYPE, K);
+    // Widest staging load that the row pitch and the tile span are both
+    // multiples of (the base pointer is 16-byte aligned).
+    int wvec = 16;
+    while (wvec > 2 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0)) wvec >>= 1;
+    a.wvec = wvec;
+    a.gvec = (N % 4 == 0) ? 1 : 0;
+    a.tiles_t = int(cdiv(T, S::BT));
+    a.tiles_k = int(cdiv(K, S::BK));
+    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
+    hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE>
+int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+    constexpr int kWaves = 8;
+    SkinnyArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.G = G;
+    a.dst = dst;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.wide = (K % 4 == 0) ? 1 : 0;
+    a.gvec = (N % 4 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves>), dim3(unsigned(cdiv(K, 64))), dim3(kWaves * 64), 0, st,
+                       a);
+    return launch_status();
+}
+
+template <int TYPE>
+int launch_variant(int variant, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                   hipStream_t st) {
+    switch (variant) {
+        case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, st);
+        default: break;
+    }
+    if constexpr (TYPE != kQ4_K) {
+        switch (variant) {
+            case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, st);
+            default: break;
+        }
+    }
+    return RETRO_E_VARIANT;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (na <= 0 || nb <= 0) return false;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + uint64_t(nb) && pb < pa + uint64_t(na);
+}
+
+int out_prod_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
+                  int64_t T, void* stream) {
+    const int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    if (T == 0 || K == 0) return RETRO_OK;
+    const int64_t w_bytes = N * row_bytes_of(type, K);
+    const int64_t g_bytes = T * N * 4;
+    const int64_t d_bytes = T * K * 4;
+    if (!dst || (N > 0 && (!W || !G))) return RETRO_E_NULL;
+    if (!aligned16(dst) || (N > 0 && (!aligned16(W) || !aligned16(G)))) return RETRO_E_ALIGN;
+    if (overlap(dst, d_bytes, W, w_bytes) || overlap(dst, d_bytes, G, g_bytes)) return RETRO_E_ALIAS;
+    if (variant == RETRO_VARIANT_AUTO) {
+        variant = choose(type, K, N, T);
+        if (variant < 0) return variant;
+    } else if (variant == RETRO_VARIANT_SKINNY) {
+        if (!skinny_applies(K, T)) return RETRO_E_VARIANT;
+    } else {
+        const TileVariant* tv = find_tile(variant);
+        if (!tv || !tile_applies(*tv, type, K, T)) return RETRO_E_VARIANT;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (type) {
+        case RETRO_F32: return launch_variant<kF32>(variant, W, G, dst, K, N, T, st);
+        case RETRO_F16: return launch_variant<kF16>(variant, W, G, dst, K, N, T, st);
+        case RETRO_BF16: return launch_variant<kBF16>(variant, W, G, dst, K, N, T, st);
+        case RETRO_Q8_0: return launch_variant<kQ8_0>(variant, W, G, dst, K, N, T, st);
+        case RETRO_Q4_0: return launch_variant<kQ4_0>(variant, W, G, dst, K, N, T, st);
+        case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, st);
+        default: return RETRO_E_TYPE;
+    }
+}
+
+template <int TYPE>
+int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t st) {
+    DequantArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.out = out;
+    a.K = int(K);
+    a.N = int(N);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.wide = (K % 4 == 0) ? 1 : 0;
+    a.gpr = int(cdiv(K, 4));
+    a.groups = N * int64_t(a.gpr);
+    hipLaunchKernelGGL((dequant_kernel<TYPE>), dim3(unsigned(cdiv(a.groups, 256))), dim3(256), 0, st, a);
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int retro_out_prod(int type, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                   void* stream) {
+    return out_prod_impl(RETRO_VARIANT_AUTO, type, W, G, dst, K, N, T, stream);
+}
+
+int retro_out_prod_variant(int variant, int type, const void* W, const float* G, float* dst, int64_t K,
+                           int64_t N, int64_t T, void* stream) {
+    return out_prod_impl(variant, type, W, G, dst, K, N, T, stream);
+}
+
+int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, void* stream) {
+    Geometry g;
+    if (!geometry(type, g)) return RETRO_E_TYPE;
+    if (K < 0 || N < 0 || K % g.block || K >= kDimLimit || N >= kDimLimit) return RETRO_E_SHAPE;
+    if (!product_below(N, K, kByteLimit / 4) || cdiv(N * cdiv(K, 4), 256) >= kGridLimit) return RETRO_E_SHAPE;
+    if (K == 0 || N == 0) return RETRO_OK;
+    if (!W || !out) return RETRO_E_NULL;
+    if (!aligned16(W) || !aligned16(out)) return RETRO_E_ALIGN;
+    if (overlap(out, N * K * 4, W, N * row_bytes_of(type, K))) return RETRO_E_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (type) {
+        case RETRO_F32: return launch_dequant<kF32>(W, out, K, N, st);
+        case RETRO_F16: return launch_dequant<kF16>(W, out, K, N, st);
+        case RETRO_BF16: return launch_dequant<kBF16>(W, out, K, N, st);
+        case RETRO_Q8_0: return launch_dequant<kQ8_0>(W, out, K, N, st);
+        case RETRO_Q4_0: return launch_dequant<kQ4_0>(W, out, K, N, st);
+        case RETRO_Q4_K: return launch_dequant<kQ4_K>(W, out, K, N, st);
+        default: return RETRO_E_TYPE;
+    }
+}
+
+int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T) {
+    if (check_shape(type, K, N, T) != RETRO_OK) return 0;
+    if (T == 0 || K == 0) return 1;
+    return choose(type, K, N, T) > 0 ? 1 : 0;
+}
+
+int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T) {
+    const int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    return choose(type, K, N, T);
+}
+
+int64_t retro_row_bytes(int type, int64_t K) { return row_bytes_of(type, K); }
+
+const char* retro_strerror(int code) {
+    switch (code) {
+        case RETRO_OK: return "ok";
+        case RETRO_E_TYPE: return "unknown or unsupported weight type";
+        case RETRO_E_SHAPE: return "bad shape: negative size, K not a whole number of blocks, or size over the limits";
+        case RETRO_E_NULL: return "NULL buffer";
+        case RETRO_E_ALIGN: return "W, G and dst must be 16-byte aligned";
+        case RETRO_E_ALIAS: return "dst overlaps W or G";
+        case RETRO_E_HIP: return "HIP launch error";
+        case RETRO_E_VARIANT: return "kernel variant unknown or not applicable to this type and shape";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

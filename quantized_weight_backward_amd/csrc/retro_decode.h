@@ -1,0 +1,107 @@
+// retro_decode.h - device decoders for the weight block formats (gfx950).
+//
+// Every kernel of the library (dequantize, tiled MFMA, skinny) turns stored
+// bytes into float32 through the primitives below, so one bit-exact check of
+// retro_dequantize covers the arithmetic of all of them.
+//
+// Exactness: a Q8_0/Q4_0 value d*q needs at most 11+8 significant bits, a
+// Q4_K product (d*sc)*q at most 11+6+4 = 21 and dmin*m at most 17, so every
+// product below is exact in float32 and only the Q4_K subtraction rounds
+// (once, to nearest-even). Whether the compiler fuses a*q - b into an FMA
+// therefore changes no bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace retro {
+
+// GGUF tensor-type ids.
+enum : int { kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ8_0 = 8, kQ4_K = 12, kBF16 = 30 };
+
+// kBlock: elements per block; kBytes: bytes per block; kGroup: elements one
+// thread decodes from one 16-byte code load in the tiled kernel.
+template <int TYPE> struct Format;
+template <> struct Format<kF32>  { static constexpr int kBlock = 1,   kBytes = 4,   kGroup = 4;  };
+template <> struct Format<kF16>  { static constexpr int kBlock = 1,   kBytes = 2,   kGroup = 8;  };
+template <> struct Format<kBF16> { static constexpr int kBlock = 1,   kBytes = 2,   kGroup = 8;  };
+template <> struct Format<kQ8_0> { static constexpr int kBlock = 32,  kBytes = 34,  kGroup = 16; };
+template <> struct Format<kQ4_0> { static constexpr int kBlock = 32,  kBytes = 18,  kGroup = 32; };
+template <> struct Format<kQ4_K> { static constexpr int kBlock = 256, kBytes = 144, kGroup = 32; };
+
+// IEEE binary16 bits -> float32 (v_cvt_f32_f16; exact, subnormals included).
+__device__ __forceinline__ float half_to_f32(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// bfloat16 bits -> float32: the bits are the upper half of the binary32.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Two binary16 / bfloat16 values packed in one little-endian word.
+__device__ __forceinline__ void f16x2(uint32_t w, float& lo, float& hi) {
+    lo = half_to_f32(w & 0xFFFFu);
+    hi = half_to_f32(w >> 16);
+}
+__device__ __forceinline__ void bf16x2(uint32_t w, float& lo, float& hi) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xFFFF0000u);
+}
+
+// Q8_0: four int8 codes (one little-endian word) times the block scale d.
+__device__ __forceinline__ void q8_0_x4(uint32_t w, float d, float out[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = static_cast<int>(static_cast<int8_t>((w >> (8 * i)) & 0xFFu));
+        out[i] = d * static_cast<float>(q);
+    }
+}
+
+// Q4_0: from four code bytes take the low (high = false) or high nibbles;
+// value d * (q - 8).
+__device__ __forceinline__ void q4_0_x4(uint32_t w, bool high, float d, float out[4]) {
+    const uint32_t s = high ? 4u : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = static_cast<int>((w >> (8 * i + s)) & 15u);
+        out[i] = d * static_cast<float>(q - 8);
+    }
+}
+
+// Q4_K sub-scale and sub-min j (0..7) from the 12-byte field, given as its
+// three little-endian words s0 (bytes 0-3), s1 (4-7), s2 (8-11). GGUF packing:
+// j < 4: sc = low 6 bits of byte j, m = low 6 bits of byte j+4.
+// j >= 4: sc = low nibble of byte j+4 | (top 2 bits of byte j-4) << 4,
+//         m  = high nibble of byte j+4 | (top 2 bits of byte j) << 4.
+__device__ __forceinline__ void q4_k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j,
+                                               uint32_t& sc, uint32_t& m) {
+    if (j < 4) {
+        sc = (s0 >> (8 * j)) & 63u;
+        m = (s1 >> (8 * j)) & 63u;
+    } else {
+        const int i = j - 4;
+        sc = ((s2 >> (8 * i)) & 15u) | (((s0 >> (8 * i + 6)) & 3u) << 4);
+        m = ((s2 >> (8 * i + 4)) & 15u) | (((s1 >> (8 * i + 6)) & 3u) << 4);
+    }
+}
+
+// Q4_K sub-block j of a super-block whose first 16 bytes are the words
+// h0 (d | dmin << 16), s0, s1, s2: a = d*sc_j and b = dmin*m_j (both exact).
+__device__ __forceinline__ void q4_k_coeffs(uint32_t h0, uint32_t s0, uint32_t s1, uint32_t s2, int j,
+                                            float& a, float& b) {
+    uint32_t sc, m;
+    q4_k_scale_min(s0, s1, s2, j, sc, m);
+    a = half_to_f32(h0 & 0xFFFFu) * static_cast<float>(sc);
+    b = half_to_f32(h0 >> 16) * static_cast<float>(m);
+}
+
+// Q4_K: from four code bytes take the low or high nibbles; value a*q - b.
+__device__ __forceinline__ void q4_k_x4(uint32_t w, bool high, float a, float b, float out[4]) {
+    const uint32_t s = high ? 4u : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t q = (w >> (8 * i + s)) & 15u;
+        out[i] = a * static_cast<float>(q) - b;
+    }
+}
+
+}  // namespace retro

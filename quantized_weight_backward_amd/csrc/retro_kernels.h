@@ -1,0 +1,536 @@
+// retro_kernels.h - OUT_PROD kernels for gfx950 (MI355X).
+//
+//   dst[t][k] = sum_n W[n][k] * G[t][n]
+//
+// As a GEMM: M = T (rows of G), N_gemm = K (columns of W), and the reduction
+// runs over n, across the rows of W. The block-quantized direction k is the
+// output-column direction, so one decoded weight feeds T outputs.
+//
+// Three kernels:
+//   tile     fused decode -> LDS -> v_mfma_f32_32x32x2_f32, one BT x BK tile of
+//            dst per workgroup, loop over n in chunks of 32 rows of W.
+//   skinny   T <= 16: v_mfma_f32_16x16x4_f32 with M = 16, one 64-column slab
+//            of dst per workgroup, all of n inside the workgroup (waves split
+//            n and reduce through LDS in a fixed order), one pass over W.
+//   dequant  decode-only, for bit-exact checks of the decoders.
+// None allocates memory and none materialises a decoded copy of W.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "retro_decode.h"
+
+namespace retro {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Staging helpers
+// ---------------------------------------------------------------------------
+
+// Load the 16 bytes at p, of which only the first `avail` are inside the
+// tile (avail may be <= 0); the rest read as zero. wvec (16, 8, 4 or 2) is the
+// widest load that p, the row pitch and every tile boundary are aligned to,
+// and avail is always a multiple of it.
+__device__ __forceinline__ uint4 load16_masked(const uint8_t* p, int avail, int wvec) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (avail <= 0) return v;
+    if (wvec == 16) return avail >= 16 ? *reinterpret_cast<const uint4*>(p) : v;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (wvec == 8) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (8 * q < avail) {
+                const uint2 x = *reinterpret_cast<const uint2*>(p + 8 * q);
+                w[2 * q] = x.x;
+                w[2 * q + 1] = x.y;
+            }
+    } else if (wvec == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (4 * q < avail) w[q] = *reinterpret_cast<const uint32_t*>(p + 4 * q);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (2 * q < avail) w[q >> 1] |= uint32_t(*reinterpret_cast<const uint16_t*>(p + 2 * q)) << (16 * (q & 1));
+    }
+    v.x = w[0];
+    v.y = w[1];
+    v.z = w[2];
+    v.w = w[3];
+    return v;
+}
+
+// Four code bytes starting at a 2-byte aligned LDS address.
+__device__ __forceinline__ uint32_t lds_word_a2(const uint8_t* p) {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+    return uint32_t(q[0]) | (uint32_t(q[1]) << 16);
+}
+
+// Map a workgroup id to a logical tile so that each XCD (workgroups are
+// dispatched round-robin over the 8 XCDs) owns a contiguous range of logical
+// tiles, then order logical tiles in groups of GT row-tiles so that
+// neighbours share rows of G and columns of W in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int b, int tiles_t, int tiles_k, int& tt, int& tk) {
+    const int nt = tiles_t * tiles_k;
+    const int per = nt >> 3, rem = nt & 7;
+    const int x = b & 7, i = b >> 3;
+    const int lin = x * per + (x < rem ? x : rem) + i;
+    constexpr int GT = 8;
+    const int span = GT * tiles_k;
+    const int group = lin / span;
+    const int first = group * GT;
+    const int gsize = min(tiles_t - first, GT);
+    const int in = lin - group * span;
+    tt = first + in % gsize;
+    tk = in / gsize;
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel
+// ---------------------------------------------------------------------------
+
+struct TileArgs {
+    const uint8_t* W;
+    const float* G;
+    float* dst;
+    int K, N, T;
+    long long pitch;  // bytes per W row
+    int wvec;         // W staging load width (16, 8, 4, 2)
+    int gvec;         // 1: G rows take float4 loads (N % 4 == 0)
+    int tiles_t, tiles_k;
+};
+
+template <int TYPE, int WA, int WB, int WGT, int WGK>
+struct TileShape {
+    using F = Format<TYPE>;
+    static constexpr int kThreads = 256;
+    static_assert(WGT * WGK == 4, "four waves per workgroup");
+    static constexpr int BT = 32 * WA * WGT;  // rows of T per tile
+    static constexpr int BK = 32 * WB * WGK;  // columns of K per tile
+    static constexpr int BN = 32;             // rows of W per chunk
+    static_assert(BK % F::kBlock == 0, "a K tile holds whole blocks");
+    static constexpr bool kDense = F::kBlock == 1;
+    // G chunk in LDS: BT rows of 32 floats, reduction index permuted (see
+    // kernel), row stride 36 floats: float4 fragment reads are conflict-free.
+    static constexpr int GP = BN + 4;
+    // Decoded W chunk in LDS: 32 rows of BK floats, row stride BK + 32 so the
+    // two lane halves of an MFMA operand read (rows 2s and 2s+1) hit disjoint
+    // banks.
+    static constexpr int BP = BK + 32;
+    // Packed W bytes of one full tile row, in 16-byte units.
+    static constexpr int SPAN = BK / F::kBlock * F::kBytes;
+    static constexpr int UPR = (SPAN + 15) / 16;
+    static constexpr int RAWP = UPR * 16 + 16;  // raw row stride in LDS (bytes)
+    static constexpr int WUNITS = BN * UPR;
+    static constexpr int WSLOTS = (WUNITS + kThreads - 1) / kThreads;
+    static constexpr int GSLOTS = BT * BN / 4 / kThreads;
+    static_assert(GSLOTS * kThreads * 4 == BT * BN, "G chunk splits evenly");
+    static constexpr int GE = F::kGroup;
+    static constexpr int GPR = BK / GE;  // decode groups per row
+    static constexpr int DPASS = (BN * GPR + kThreads - 1) / kThreads;
+    static constexpr int LDS_G = BT * GP * 4;
+    static constexpr int LDS_B = BN * BP * 4;
+    static constexpr int LDS_RAW = kDense ? 0 : BN * RAWP;
+};
+
+template <int TYPE, int WA, int WB, int WGT, int WGK>
+__global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
+    using S = TileShape<TYPE, WA, WB, WGT, WGK>;
+    using F = Format<TYPE>;
+    constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, BP = S::BP;
+
+    __shared__ __attribute__((aligned(16))) float Gs[BT * GP];
+    __shared__ __attribute__((aligned(16))) float Bs[BN * BP];
+    __shared__ __attribute__((aligned(16))) uint8_t Raw[S::kDense ? 16 : S::LDS_RAW];
+
+    const int tid = threadIdx.x;
+    int tt, tk;
+    tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, tt, tk);
+    const int t0 = tt * BT, k0 = tk * BK;
+    const int K = args.K, N = args.N, T = args.T;
+    const int kend = min(k0 + BK, K);
+    // Packed bytes of this tile's k range inside one W row.
+    const long long kb0 = (long long)(k0 / F::kBlock) * F::kBytes;
+    const int span = (kend - k0) / F::kBlock * F::kBytes;
+    const uint8_t* Wt = args.W + kb0;
+
+    float4 greg[S::GSLOTS];
+    uint4 wreg[S::WSLOTS];
+
+    // Global -> registers for the chunk of W rows [n0, n0 + 32).
+    auto load_chunk = [&](int n0) {
+#pragma unroll
+        for (int s = 0; s < S::GSLOTS; ++s) {
+            const int id = tid + S::kThreads * s;
+            const int r = id >> 3, j = id & 7;
+            const int t = t0 + r, n = n0 + 4 * j;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < T) {
+                const float* gp = args.G + (long long)t * N + n;
+                if (args.gvec) {
+                    if (n < N) v = *reinterpret_cast<const float4*>(gp);
+                } else {
+                    if (n < N) v.x = gp[0];
+                    if (n + 1 < N) v.y = gp[1];
+                    if (n + 2 < N) v.z = gp[2];
+                    if (n + 3 < N) v.w = gp[3];
+                }
+            }
+            greg[s] = v;
+        }
+#pragma unroll
+        for (int s = 0; s < S::WSLOTS; ++s) {
+            const int id = tid + S::kThreads * s;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (S::WUNITS % S::kThreads == 0 || id < S::WUNITS) {
+                const int r = id / S::UPR, u = id - r * S::UPR;
+                const int n = n0 + r;
+                if (n < N) v = load16_masked(Wt + (long long)n * args.pitch + 16 * u, span - 16 * u, args.wvec);
+            }
+            wreg[s] = v;
+        }
+    };
+
+    // Registers -> LDS. G goes to Gs with the reduction index permuted:
+    // W row n0 + 2s + h of the chunk sits at column 16h + s, so that lane half
+    // h of an MFMA operand finds its 16 steps contiguous. Dense W is decoded
+    // straight into Bs; packed W goes to Raw first.
+    auto store_chunk = [&]() {
+#pragma unroll
+        for (int s = 0; s < S::GSLOTS; ++s) {
+            const int id = tid + S::kThreads * s;
+            const int r = id >> 3, j = id & 7;
+            float* row = Gs + r * GP;
+            *reinterpret_cast<float2*>(row + 2 * j) = make_float2(greg[s].x, greg[s].z);
+            *reinterpret_cast<float2*>(row + 16 + 2 * j) = make_float2(greg[s].y, greg[s].w);
+        }
+#pragma unroll
+        for (int s = 0; s < S::WSLOTS; ++s) {
+            const int id = tid + S::kThreads * s;
+            if (S::WUNITS % S::kThreads == 0 || id < S::WUNITS) {
+                const int r = id / S::UPR, u = id - r * S::UPR;
+                const uint4 v = wreg[s];
+                if constexpr (S::kDense) {
+                    float* brow = Bs + r * BP;
+                    if constexpr (TYPE == kF32) {
+                        *reinterpret_cast<float4*>(brow + 4 * u) =
+                            make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                        __uint_as_float(v.w));
+                    } else {
+                        float e[8];
+                        if constexpr (TYPE == kF16) {
+                            f16x2(v.x, e[0], e[1]);
+                            f16x2(v.y, e[2], e[3]);
+                            f16x2(v.z, e[4], e[5]);
+                            f16x2(v.w, e[6], e[7]);
+                        } else {
+                            bf16x2(v.x, e[0], e[1]);
+                            bf16x2(v.y, e[2], e[3]);
+                            bf16x2(v.z, e[4], e[5]);
+                            bf16x2(v.w, e[6], e[7]);
+                        }
+                        *reinterpret_cast<float4*>(brow + 8 * u) = make_float4(e[0], e[1], e[2], e[3]);
+                        *reinterpret_cast<float4*>(brow + 8 * u + 4) = make_float4(e[4], e[5], e[6], e[7]);
+                    }
+                } else {
+                    *reinterpret_cast<uint4*>(Raw + r * S::RAWP + 16 * u) = v;
+                }
+            }
+        }
+    };
+
+    // Raw packed bytes in LDS -> decoded floats in Bs (packed formats only).
+    auto decode_chunk = [&]() {
+#pragma unroll
+        for (int p = 0; p < S::DPASS; ++p) {
+            const int id = tid + S::kThreads * p;
+            if ((BN * S::GPR) % S::kThreads == 0 || id < BN * S::GPR) {
+                const int r = id / S::GPR, g = id - r * S::GPR;
+                const uint8_t* raw = Raw + r * S::RAWP;
+                float* brow = Bs + r * BP;
+                if constexpr (TYPE == kQ4_K) {
+                    const int sb = g >> 3, c = (g >> 1) & 3, h = g & 1;
+                    const uint4 hd = *reinterpret_cast<const uint4*>(raw + 144 * sb);
+                    const uint4 cw = *reinterpret_cast<const uint4*>(raw + 144 * sb + 16 + 32 * c + 16 * h);
+                    float a0, b0, a1, b1;
+                    q4_k_coeffs(hd.x, hd.y, hd.z, hd.w, 2 * c, a0, b0);
+                    q4_k_coeffs(hd.x, hd.y, hd.z, hd.w, 2 * c + 1, a1, b1);
+                    const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+                    float* lo = brow + 256 * sb + 64 * c + 16 * h;
+                    float* hi = lo + 32;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float e[4];
+                        q4_k_x4(w[i], false, a0, b0, e);
+                        *reinterpret_cast<float4*>(lo + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                        q4_k_x4(w[i], true, a1, b1, e);
+                        *reinterpret_cast<float4*>(hi + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                    }
+                } else if constexpr (TYPE == kQ4_0) {
+                    const uint8_t* blk = raw + 18 * g;
+                    const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+                    float* lo = brow + 32 * g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t w = lds_word_a2(blk + 2 + 4 * i);
+                        float e[4];
+                        q4_0_x4(w, false, d, e);
+                        *reinterpret_cast<float4*>(lo + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                        q4_0_x4(w, true, d, e);
+                        *reinterpret_cast<float4*>(lo + 16 + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                    }
+                } else if constexpr (TYPE == kQ8_0) {
+                    const int b = g >> 1, h = g & 1;
+                    const uint8_t* blk = raw + 34 * b;
+                    const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+                    float* out = brow + 32 * b + 16 * h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t w = lds_word_a2(blk + 2 + 16 * h + 4 * i);
+                        float e[4];
+                        q8_0_x4(w, d, e);
+                        *reinterpret_cast<float4*>(out + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                    }
+                }
+            }
+        }
+    };
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wt = wave / WGK, wk = wave % WGK;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    f32x16 acc[WA][WB];
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+    const int nchunks = (N + BN - 1) / BN;
+    if (nchunks > 0) load_chunk(0);
+    for (int c = 0; c < nchunks; ++c) {
+        store_chunk();
+        __syncthreads();
+        if (c + 1 < nchunks) load_chunk((c + 1) * BN);
+        if constexpr (!S::kDense) {
+            decode_chunk();
+            __syncthreads();
+        }
+        // MFMA step s (0..15) contracts W rows n0 + 2s + h (lane half h):
+        // A[i][h] = G[t_i][n0 + 2s + h], B[h][j] = W[n0 + 2s + h][k_j].
+        const float* ga = Gs + (wt * 32 * WA + l32) * GP + 16 * h;
+        const float* bb = Bs + h * BP + wk * 32 * WB + l32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 av[WA];
+#pragma unroll
+            for (int a = 0; a < WA; ++a) av[a] = *reinterpret_cast<const f32x4*>(ga + 32 * a * GP + 4 * q);
+            float bv[4][WB];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int b = 0; b < WB; ++b) bv[r][b] = bb[(2 * (4 * q + r)) * BP + 32 * b];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int a = 0; a < WA; ++a)
+#pragma unroll
+                    for (int b = 0; b < WB; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][r], bv[r][b], acc[a][b], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // D layout of v_mfma_f32_32x32x2f32: lane l, register v holds
+    // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+        for (int b = 0; b < WB; ++b) {
+            const int k = k0 + wk * 32 * WB + 32 * b + l32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + wt * 32 * WA + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (t < T && k < K) args.dst[(long long)t * K + k] = acc[a][b][v];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny kernel (T <= 16)
+// ---------------------------------------------------------------------------
+
+struct SkinnyArgs {
+    const uint8_t* W;
+    const float* G;
+    float* dst;
+    int K, N, T;
+    long long pitch;
+    int wide;  // 1: W rows allow the widest load of 4 consecutive elements
+    int gvec;  // 1: G rows take float4 loads
+};
+
+// Four consecutive elements k, k+1, k+2, k+3 (k a multiple of 4) of W row
+// `row`; elements at or beyond K read as zero.
+template <int TYPE>
+__device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, int wide, float e[4]) {
+    if constexpr (TYPE == kF32) {
+        const float* p = reinterpret_cast<const float*>(row) + k;
+        if (wide && k + 4 <= K) {
+            const float4 v = *reinterpret_cast<const float4*>(p);
+            e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] = (k + i < K) ? p[i] : 0.f;
+        }
+    } else if constexpr (TYPE == kF16 || TYPE == kBF16) {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + k;
+        uint32_t w0 = 0, w1 = 0;
+        if (wide && k + 4 <= K) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            w0 = v.x;
+            w1 = v.y;
+        } else {
+            if (k < K) w0 |= p[0];
+            if (k + 1 < K) w0 |= uint32_t(p[1]) << 16;
+            if (k + 2 < K) w1 |= p[2];
+            if (k + 3 < K) w1 |= uint32_t(p[3]) << 16;
+        }
+        if constexpr (TYPE == kF16) {
+            f16x2(w0, e[0], e[1]);
+            f16x2(w1, e[2], e[3]);
+        } else {
+            bf16x2(w0, e[0], e[1]);
+            bf16x2(w1, e[2], e[3]);
+        }
+    } else if constexpr (TYPE == kQ8_0) {
+        if (k >= K) { e[0] = e[1] = e[2] = e[3] = 0.f; return; }
+        const uint8_t* blk = row + (k >> 5) * 34;
+        const int r = k & 31;
+        const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+        const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + 2 + r);
+        q8_0_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), d, e);
+    } else if constexpr (TYPE == kQ4_0) {
+        if (k >= K) { e[0] = e[1] = e[2] = e[3] = 0.f; return; }
+        const uint8_t* blk = row + (k >> 5) * 18;
+        const int r = k & 31;
+        const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+        const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + 2 + (r & 15));
+        q4_0_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), r >= 16, d, e);
+    } else {  // kQ4_K; K is a multiple of 256, so k < K always
+        const uint8_t* sbp = row + (k >> 8) * 144;
+        const int e256 = k & 255, c = e256 >> 6, r = e256 & 63;
+        const bool high = r >= 32;
+        const uint32_t* hw = reinterpret_cast<const uint32_t*>(sbp);
+        float a, b;
+        q4_k_coeffs(hw[0], hw[1], hw[2], hw[3], 2 * c + (high ? 1 : 0), a, b);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(sbp + 16 + 32 * c + (r & 31));
+        q4_k_x4(w, high, a, b, e);
+    }
+}
+
+template <int TYPE, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs args) {
+    constexpr int KS = 64;  // dst columns per workgroup
+    __shared__ __attribute__((aligned(16))) float part[NWAVES * 16 * KS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = args.K, N = args.N, T = args.T;
+    const int k0 = blockIdx.x * KS;
+    // MFMA 16x16x4 operands: lane l supplies A[i = l%16][kk = l/16] and
+    // B[kk = l/16][j = l%16]. Step s of a 16-row group starting at n0 uses W row
+    // n0 + 4*(l/16) + s for lane l, so a lane reads G[t][n0 + 4*(l/16) .. +3]
+    // with one float4. Column j of accumulator block b is dst column
+    // k0 + 4*j + b, so a lane decodes 4 consecutive elements per row.
+    const int j = lane & 15, rq = lane >> 4;
+    const int t = j;  // A row index = the t row of G
+    const int kl = k0 + 4 * j;
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int n0 = 16 * wave; n0 < N; n0 += 16 * NWAVES) {
+        const int nq = n0 + 4 * rq;
+        float gv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < T) {
+            const float* gp = args.G + (long long)t * N + nq;
+            if (args.gvec && nq + 4 <= N) {
+                const float4 v = *reinterpret_cast<const float4*>(gp);
+                gv[0] = v.x; gv[1] = v.y; gv[2] = v.z; gv[3] = v.w;
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) gv[s] = (nq + s < N) ? gp[s] : 0.f;
+            }
+        }
+        float wv[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int n = nq + s;
+            if (n < N) {
+                skinny_load4<TYPE>(args.W + (long long)n * args.pitch, kl, K, args.wide, wv[s]);
+            } else {
+                wv[s][0] = wv[s][1] = wv[s][2] = wv[s][3] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[s], wv[s][b], acc[b], 0, 0, 0);
+    }
+
+    // D layout of v_mfma_f32_16x16x4f32: lane l, register v holds row
+    // 4*(l/16) + v, column l%16. Partials of each wave go to LDS, then are
+    // summed over waves in increasing wave order (deterministic).
+    float* mine = part + wave * 16 * KS;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mine[(4 * rq + v) * KS + 4 * j + b] = acc[b][v];
+    __syncthreads();
+    for (int o = tid; o < 16 * KS; o += NWAVES * 64) {
+        const int tr = o / KS, kk = o - tr * KS;
+        float sum = part[o];
+#pragma unroll
+        for (int w = 1; w < NWAVES; ++w) sum += part[w * 16 * KS + o];
+        if (tr < T && k0 + kk < K) args.dst[(long long)tr * K + k0 + kk] = sum;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize kernel: out[n][k] = W[n][k]
+// ---------------------------------------------------------------------------
+
+struct DequantArgs {
+    const uint8_t* W;
+    float* out;
+    int K, N;
+    long long pitch;
+    int wide;
+    long long groups;  // N * groups_per_row
+    int gpr;           // groups per row
+};
+
+// One thread decodes 4 consecutive elements (k = 4 * g within row n) with
+// the same primitives the other kernels use.
+template <int TYPE>
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs args) {
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= args.groups) return;
+    const int n = (int)(gid / args.gpr);
+    const int k = 4 * (int)(gid - (long long)n * args.gpr);
+    float e[4];
+    skinny_load4<TYPE>(args.W + (long long)n * args.pitch, k, args.K, args.wide, e);
+    float* o = args.out + (long long)n * args.K + k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (k + i < args.K) o[i] = e[i];
+}
+
+}  // namespace retro

@@ -1,0 +1,139 @@
+"""The C ABI on the host (no GPU): the library loads, exports what the header
+declares, and every validation path returns its error before touching a
+device."""
+
+import os
+import re
+
+import pytest
+
+import workloads as wl
+from conftest import REPO
+
+q = pytest.importorskip("quantized_weight_backward_amd")  # raises if the library is missing
+
+HEADER = os.path.join(REPO, "include", "retro_out_prod.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(retro_\w+)\s*\(", text)))
+
+
+def test_library_is_the_in_tree_build():
+    assert os.path.dirname(q.LIB_PATH) == os.path.join(REPO, "quantized_weight_backward_amd")
+    assert os.path.exists(q.LIB_PATH)
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(q.EXPORTS), names
+    for name in names:
+        assert hasattr(q.lib, name), name
+
+
+def test_enum_values_match_header():
+    text = open(HEADER).read()
+    for name, value in [("RETRO_F32", q.F32), ("RETRO_F16", q.F16), ("RETRO_Q4_0", q.Q4_0), ("RETRO_Q8_0", q.Q8_0),
+                        ("RETRO_Q4_K", q.Q4_K), ("RETRO_BF16", q.BF16), ("RETRO_E_TYPE", q.E_TYPE),
+                        ("RETRO_E_SHAPE", q.E_SHAPE), ("RETRO_E_NULL", q.E_NULL), ("RETRO_E_ALIGN", q.E_ALIGN),
+                        ("RETRO_E_ALIAS", q.E_ALIAS), ("RETRO_E_HIP", q.E_HIP), ("RETRO_E_VARIANT", q.E_VARIANT),
+                        ("RETRO_VARIANT_SKINNY", q.VARIANT_SKINNY),
+                        ("RETRO_VARIANT_TILE_128x256", q.VARIANT_TILE_128x256),
+                        ("RETRO_VARIANT_TILE_64x64", q.VARIANT_TILE_64x64)]:
+        m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+        assert m and int(m.group(1)) == value, name
+
+
+@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K])
+def test_row_bytes_matches_the_format(wtype):
+    blk, nbytes = wl.block_geometry(wtype)
+    for nblocks in (0, 1, 3, 16, 56):
+        assert q.row_bytes(wtype, nblocks * blk) == nblocks * nbytes
+    if blk > 1:
+        assert q.row_bytes(wtype, blk + 1) == -1
+    assert q.row_bytes(wtype, -blk) == -1
+
+
+def test_row_bytes_of_the_workloads():
+    assert q.row_bytes(q.Q8_0, 256) == 272
+    assert q.row_bytes(q.Q4_0, 5120) == 2880
+    assert q.row_bytes(q.Q4_K, 4096) == 2304
+    assert q.row_bytes(q.Q4_K, 14336) == 8064
+    assert q.row_bytes(q.F16, 4096) == 8192
+    assert q.row_bytes(99, 256) == -1
+
+
+def test_supported():
+    assert q.supported(q.Q4_K, 4096, 14336, 4096)
+    assert q.supported(q.Q4_K, 14336, 4096, 16)
+    assert q.supported(q.F16, 7, 3, 1)
+    assert q.supported(q.Q8_0, 0, 0, 0)
+    assert not q.supported(q.Q4_K, 100, 1, 1)
+    assert not q.supported(q.Q4_0, 48, 1, 1)
+    assert not q.supported(77, 32, 1, 1)
+    assert not q.supported(q.F32, -1, 1, 1)
+    assert not q.supported(q.F32, 1, 1 << 31, 1)
+    assert not q.supported(q.F32, (1 << 31) - 1, 1, (1 << 31) - 1)  # T*K beyond the byte limit
+
+
+def test_choice():
+    assert q.choice(q.Q4_K, 14336, 4096, 16) == q.VARIANT_SKINNY
+    assert q.choice(q.Q4_K, 4096, 14336, 4096) in (q.VARIANT_TILE_128x256, q.VARIANT_TILE_64x256)
+    for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0):
+        assert q.choice(wtype, 4096, 4096, 512) in q.VARIANT_NAMES
+    assert q.choice(q.Q4_K, 100, 1, 1) == q.E_SHAPE
+    assert q.choice(5, 32, 1, 1) == q.E_TYPE
+
+
+def test_strerror_covers_every_code():
+    for code in (q.OK, q.E_TYPE, q.E_SHAPE, q.E_NULL, q.E_ALIGN, q.E_ALIAS, q.E_HIP, q.E_VARIANT):
+        s = q.strerror(code)
+        assert s and s != "unknown error code"
+    assert q.strerror(-99) == "unknown error code"
+
+
+def test_validation_errors_before_any_device_work():
+    lib = q.lib
+    # bad type / shape
+    assert lib.retro_out_prod(99, None, None, None, 32, 1, 1, None) == q.E_TYPE
+    assert lib.retro_out_prod(q.Q4_K, None, None, None, 128, 1, 1, None) == q.E_SHAPE
+    assert lib.retro_out_prod(q.Q4_0, None, None, None, 40, 1, 1, None) == q.E_SHAPE
+    assert lib.retro_out_prod(q.F32, None, None, None, -1, 1, 1, None) == q.E_SHAPE
+    assert lib.retro_out_prod(q.F32, None, None, None, 1, -1, 1, None) == q.E_SHAPE
+    assert lib.retro_out_prod(q.F32, None, None, None, 1, 1, 1 << 31, None) == q.E_SHAPE
+    # empty outputs are no-ops even with NULL buffers
+    assert lib.retro_out_prod(q.F32, None, None, None, 0, 5, 5, None) == q.OK
+    assert lib.retro_out_prod(q.Q4_K, None, None, None, 256, 5, 0, None) == q.OK
+    # NULL buffers
+    assert lib.retro_out_prod(q.F32, None, None, None, 4, 4, 4, None) == q.E_NULL
+    assert lib.retro_out_prod(q.F32, 0x1000, 0x2000, None, 4, 4, 4, None) == q.E_NULL
+    assert lib.retro_out_prod(q.F32, None, 0x2000, 0x3000, 4, 4, 4, None) == q.E_NULL
+    # misaligned (fake addresses, never dereferenced)
+    assert lib.retro_out_prod(q.F32, 0x100004, 0x200000, 0x300000, 4, 4, 4, None) == q.E_ALIGN
+    assert lib.retro_out_prod(q.F32, 0x100000, 0x200008, 0x300000, 4, 4, 4, None) == q.E_ALIGN
+    assert lib.retro_out_prod(q.F32, 0x100000, 0x200000, 0x300002, 4, 4, 4, None) == q.E_ALIGN
+    # aliasing: dst (4x4 floats = 64 B) overlapping W (4 rows x 16 B) or G
+    assert lib.retro_out_prod(q.F32, 0x100000, 0x200000, 0x100030, 4, 4, 4, None) == q.E_ALIAS
+    assert lib.retro_out_prod(q.F32, 0x100000, 0x200000, 0x1FFFD0, 4, 4, 4, None) == q.E_ALIAS
+    # variants
+    assert lib.retro_out_prod_variant(42, q.F32, 0x100000, 0x200000, 0x300000, 4, 4, 4, None) == q.E_VARIANT
+    assert lib.retro_out_prod_variant(q.VARIANT_SKINNY, q.F32, 0x100000, 0x200000, 0x300000, 4, 4, 17,
+                                      None) == q.E_VARIANT
+    assert lib.retro_out_prod_variant(q.VARIANT_TILE_128x128, q.Q4_K, 0x100000, 0x200000, 0x300000, 256, 4, 64,
+                                      None) == q.E_VARIANT
+    # dequantize
+    assert lib.retro_dequantize(99, None, None, 32, 1, None) == q.E_TYPE
+    assert lib.retro_dequantize(q.Q4_K, None, None, 32, 1, None) == q.E_SHAPE
+    assert lib.retro_dequantize(q.Q4_K, None, None, 0, 5, None) == q.OK
+    assert lib.retro_dequantize(q.Q4_K, None, None, 256, 5, None) == q.E_NULL
+    assert lib.retro_dequantize(q.Q4_K, 0x100001, 0x200000, 256, 5, None) == q.E_ALIGN
+    assert lib.retro_dequantize(q.Q4_K, 0x100000, 0x100100, 256, 5, None) == q.E_ALIAS
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        q.out_prod(q.F32, torch.zeros(16, dtype=torch.uint8), torch.zeros(1, 4), 1)

@@ -1,0 +1,315 @@
+"""Parity of the HIP library against the CPU oracle, on cuda:0.
+
+Bars (the project's acceptance criteria):
+  * decoded values bit-exact (retro_dequantize, and the fused kernels'
+    decode through an identity gradient);
+  * the contraction within NMSE <= 1e-7 and max relative error <= 1e-5 per
+    output, the error of an output taken relative to sum_n |W[n][k] G[t][n]|
+    (the literal |y - r| / |r| is unattainable for any F32-accumulating
+    contraction: outputs near zero by cancellation have unbounded relative
+    error).
+A tighter internal gate (max relative error <= 2e-6) catches a silent loss
+of precision (for example a gradient rounded to fp16), which the contract
+bars alone would let through.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+NMSE_MAX = 1e-7
+REL_MAX = 1e-5
+REL_TIGHT = 2e-6
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K]
+ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256"]
+
+
+@pytest.fixture(scope="module")
+def q():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import quantized_weight_backward_amd as q
+
+    return q
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def variant_id(q, name):
+    return {v: k for k, v in q.VARIANT_NAMES.items()}[name]
+
+
+def tile_variants(wtype):
+    if wtype == wl.Q4_K:
+        return ["tile_128x256", "tile_64x256"]
+    return ALL_TILES
+
+
+def run(q, c, variant="auto", prefill=float("nan")):
+    W, G = dev(c["W"]), dev(c["G"])
+    out = torch.full((c["T"], c["K"]), prefill, dtype=torch.float32, device="cuda")
+    v = q.VARIANT_AUTO if variant == "auto" else variant_id(q, variant)
+    q.out_prod(c["type"], W, G, c["K"], out=out, variant=v)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_close(y, acc, ab, label=""):
+    e = oracle.errors(y, acc, ab)
+    assert e["nonfinite"] == 0, (label, e)
+    assert e["nmse"] <= NMSE_MAX, (label, e)
+    assert e["max_rel"] <= REL_MAX, (label, e)
+    assert e["max_rel"] <= REL_TIGHT, (label, e)
+    return e
+
+
+# Shapes spanning several tiles with ragged tails in T, N and K, and the
+# alignment paths: (N % 4 != 0) -> scalar G loads; K chosen so that the W
+# row pitch is 16-, 8-, 4- or only 2-byte aligned.
+SMALL_K = {
+    wl.F32: (300, 256, 301),
+    wl.F16: (301, 264, 296),
+    wl.BF16: (300, 520, 302),
+    wl.Q8_0: (416, 768, 352),
+    wl.Q4_0: (512, 352, 416),
+    wl.Q4_K: (768, 512, 256),
+}
+SMALL_TN = ((200, 77), (130, 96), (67, 33))
+
+
+def small_case(wtype, i, seed):
+    T, N = SMALL_TN[i]
+    return wl.make_case(wtype, N, SMALL_K[wtype][i], T, seed)
+
+
+# --- decode ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("i", [0, 1, 2])
+def test_dequantize_bit_exact(q, wtype, i):
+    c = small_case(wtype, i, 100 + i)
+    ref = oracle.dequantize(wtype, c["W"], c["K"])
+    got = q.dequantize(wtype, dev(c["W"]), c["K"], c["N"]).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequantize_hand_built_blocks(q, golden):
+    for fixture, wtype in (("q8_0_blocks.txt", wl.Q8_0), ("q4_0_blocks.txt", wl.Q4_0)):
+        g = golden(fixture)
+        names = sorted(k[:-4] for k in g if k.endswith("_hex"))
+        raw = np.stack([np.array([int(t, 16) for t in g[n + "_hex"]], dtype=np.uint8) for n in names])
+        expected = np.stack([np.array([float(v) for v in g[n + "_expected"]], dtype=np.float32) for n in names])
+        got = q.dequantize(wtype, dev(raw), 32, len(names)).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), expected.view(np.uint32)), fixture
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+def test_fused_decode_through_identity_gradient(q, wtype):
+    """With T = N and G = I, out_prod(W, I) = decoded W exactly (every other
+    term is w * 0); this checks every tile kernel's and the skinny kernel's
+    decode without trusting retro_dequantize."""
+    for N, variants in ((48, tile_variants(wtype)), (16, ["skinny"] + tile_variants(wtype))):
+        c = wl.make_case(wtype, N, SMALL_K[wtype][0], N, seed=7)
+        ref = oracle.dequantize(wtype, c["W"], c["K"])
+        c["G"] = np.eye(N, dtype=np.float32)
+        for v in variants:
+            got = run(q, c, v)
+            assert np.array_equal(got, ref), (v, N)
+
+
+# --- contraction ----------------------------------------------------------------
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("i", [0, 1, 2])
+def test_tile_variants_match_oracle(q, wtype, i):
+    c = small_case(wtype, i, 200 + i)
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], c["K"], nthreads=ORACLE_THREADS)
+    for v in ["auto"] + tile_variants(wtype):
+        check_close(run(q, c, v), acc, ab, v)
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("T,N", [(1, 77), (5, 96), (16, 300), (16, 33), (3, 1)])
+def test_skinny_matches_oracle(q, wtype, T, N):
+    c = wl.make_case(wtype, N, SMALL_K[wtype][0], T, seed=300 + T + N)
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], c["K"], nthreads=ORACLE_THREADS)
+    assert q.choice(wtype, c["K"], N, T) == q.VARIANT_SKINNY
+    check_close(run(q, c, "skinny"), acc, ab, "skinny")
+    check_close(run(q, c, "auto"), acc, ab, "auto")
+    check_close(run(q, c, tile_variants(wtype)[-1]), acc, ab, "tile at small T")
+
+
+def test_q8_0_tiny_workload(q):
+    c = wl.workload("q8_0_n128_k256_t64")
+    dst, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"])
+    y = run(q, c)
+    check_close(y, acc, ab)
+
+
+@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q4_0, wl.Q4_K, wl.F16, wl.BF16])
+def test_f32_twin_on_device(q, wtype):
+    """out_prod(Qx, W) and out_prod(F32, dequant(W)) run the same tile on
+    identical B operands, so they agree bit for bit."""
+    c = small_case(wtype, 1, 400)
+    w32 = oracle.dequantize(wtype, c["W"], c["K"])
+    twin = dict(c, type=wl.F32, W=w32.view(np.uint8))
+    for v in tile_variants(wtype) + ["skinny"]:
+        if v == "skinny":
+            c2, t2 = dict(c, T=16, G=c["G"][:16]), dict(twin, T=16, G=c["G"][:16])
+        else:
+            c2, t2 = c, twin
+        a = run(q, c2, v)
+        b = run(q, t2, v)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), v
+
+
+# --- invariants -----------------------------------------------------------------
+
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q4_0, wl.BF16])
+def test_invariants(q, wtype):
+    c = small_case(wtype, 0, 500)
+    base = run(q, c)
+    # every output written (NaN prefill gone), two runs bitwise equal
+    assert np.isfinite(base).all()
+    assert np.array_equal(run(q, c, prefill=1e30).view(np.uint32), base.view(np.uint32))
+    # scaling G by 2 scales every output by exactly 2
+    two = run(q, dict(c, G=c["G"] * np.float32(2)))
+    assert np.array_equal(two, 2 * base)
+    # zero gradient
+    assert not run(q, dict(c, G=np.zeros_like(c["G"]))).any()
+    # permuting the rows of G permutes the rows of dst
+    perm = np.random.default_rng(1).permutation(c["T"])
+    pg = run(q, dict(c, G=c["G"][perm]))
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], c["K"], nthreads=ORACLE_THREADS)
+    check_close(pg, acc[perm], ab[perm])
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+def test_empty_reduction_fills_zeros(q, wtype):
+    K = SMALL_K[wtype][0]
+    for T in (7, 100):
+        c = {"type": wtype, "K": K, "N": 0, "T": T, "W": np.zeros((0, wl.row_bytes(wtype, K)), np.uint8),
+             "G": np.zeros((T, 0), np.float32)}
+        y = run(q, c)
+        assert np.array_equal(y, np.zeros((T, K), np.float32))
+
+
+def test_zero_size_calls_touch_nothing(q):
+    out = torch.full((0, 256), 1.0, device="cuda")
+    q.out_prod(wl.Q4_K, torch.zeros(0, dtype=torch.uint8, device="cuda"),
+               torch.zeros((0, 0), device="cuda"), 256, out=out)
+    assert q.lib.retro_out_prod(wl.Q4_K, None, None, None, 0, 5, 5, None) == 0
+    assert q.lib.retro_out_prod(wl.Q4_K, None, None, None, 256, 5, 0, None) == 0
+
+
+def test_no_allocation_during_a_call(q):
+    c = small_case(wl.Q4_K, 0, 600)
+    W, G = dev(c["W"]), dev(c["G"])
+    out = torch.empty((c["T"], c["K"]), device="cuda")
+    q.out_prod(wl.Q4_K, W, G, c["K"], out=out)  # warm (module load)
+    torch.cuda.synchronize()
+    before_alloc = torch.cuda.memory_allocated()
+    free_before, _ = torch.cuda.mem_get_info()
+    for _ in range(3):
+        q.out_prod(wl.Q4_K, W, G, c["K"], out=out)
+    torch.cuda.synchronize()
+    free_after, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == before_alloc
+    assert free_after == free_before
+
+
+def test_device_side_argument_errors(q):
+    c = small_case(wl.Q4_K, 1, 700)
+    W, G = dev(c["W"]), dev(c["G"])
+    T, N, K = c["T"], c["N"], c["K"]
+    big = torch.empty(T * K + 64, device="cuda")
+    out = big[:T * K]
+    lib = q.lib
+    args = lambda w, g, d: (wl.Q4_K, w, g, d, K, N, T, None)  # noqa: E731
+    assert lib.retro_out_prod(*args(W.data_ptr(), G.data_ptr(), out.data_ptr())) == 0
+    torch.cuda.synchronize()
+    assert lib.retro_out_prod(*args(W.data_ptr() + 4, G.data_ptr(), out.data_ptr())) == q.E_ALIGN
+    assert lib.retro_out_prod(*args(W.data_ptr(), G.data_ptr(), big.data_ptr() + 4)) == q.E_ALIGN
+    assert lib.retro_out_prod(*args(W.data_ptr(), G.data_ptr(), G.data_ptr())) == q.E_ALIAS
+    assert lib.retro_out_prod(*args(W.data_ptr(), G.data_ptr(), W.data_ptr())) == q.E_ALIAS
+    assert lib.retro_out_prod(*args(None, G.data_ptr(), out.data_ptr())) == q.E_NULL
+    assert lib.retro_out_prod_variant(q.VARIANT_TILE_128x128, *args(W.data_ptr(), G.data_ptr(),
+                                                                   out.data_ptr())) == q.E_VARIANT
+    with pytest.raises(q.RetroError):
+        q.out_prod(wl.Q4_K, W, G, K, variant=q.VARIANT_SKINNY)  # T > 16
+
+
+def test_runs_on_the_given_stream(q):
+    c = small_case(wl.Q8_0, 1, 800)
+    _, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"])
+    W, G = dev(c["W"]), dev(c["G"])
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = q.out_prod(c["type"], W, G, c["K"])
+    s.synchronize()
+    check_close(out.cpu().numpy(), acc, ab)
+
+
+# --- full-size workloads ----------------------------------------------------------
+
+FULL = [
+    ("q8_0_n128_k256_t64", None),
+    ("dense_n4096_k4096_t512", wl.F32),
+    ("dense_n4096_k4096_t512", wl.F16),
+    ("dense_n4096_k4096_t512", wl.BF16),
+    ("q4_0_n17408_k5120_t2048", None),
+    ("q4_k_n14336_k4096_t4096", None),
+    ("q4_k_n4096_k14336_t16", None),
+]
+
+
+@pytest.mark.parametrize("name,wtype", FULL)
+def test_full_size_sampled_rows(q, name, wtype):
+    """The launch configuration the benchmark times, checked on sampled t
+    rows that the oracle computes one by one (first, last and random rows),
+    plus whole-output properties: all finite, deterministic."""
+    c = wl.workload(name, wtype)
+    W, G = dev(c["W"]), dev(c["G"])
+    out = torch.full((c["T"], c["K"]), float("nan"), device="cuda")
+    q.out_prod(c["type"], W, G, c["K"], out=out)
+    again = q.out_prod(c["type"], W, G, c["K"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    assert torch.equal(out, again)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, c["T"] - 1], rng.integers(0, c["T"], size=14)]))
+    _, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"], rows=rows, nthreads=ORACLE_THREADS)
+    y = out[torch.from_numpy(rows).cuda()].cpu().numpy()
+    e = check_close(y, acc, ab, name)
+    print(f"{name} {wl.TYPE_NAMES[c['type']]}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
+
+
+@pytest.mark.parametrize("name", ["q4_0_n17408_k5120_t2048", "q4_k_n14336_k4096_t4096", "q4_k_n4096_k14336_t16"])
+def test_full_size_decode_through_identity(q, name):
+    """Full-size W through the benchmarked kernel with G = I (T = N): the
+    output is the decoded W, bit for bit."""
+    c = wl.workload(name)
+    N, K = c["N"], c["K"]
+    ref = oracle.dequantize(c["type"], c["W"], K)
+    W = dev(c["W"])
+    variant = q.choice(c["type"], K, N, c["T"])
+    if variant == q.VARIANT_SKINNY:
+        # T = N would leave the skinny range; check 16-row slices of W instead
+        for n0 in range(0, N, N // 8):
+            sl = slice(n0, n0 + 16)
+            out = q.out_prod(c["type"], W[sl], torch.eye(16, device="cuda"), K, variant=variant)
+            assert np.array_equal(out.cpu().numpy(), ref[sl]), n0
+    else:
+        out = q.out_prod(c["type"], W, torch.eye(N, device="cuda"), K, variant=variant)
+        assert np.array_equal(out.cpu().numpy(), ref)
