@@ -80,8 +80,8 @@ enum {
                             applicable to this type/shape */
 };
 
-/* Size limits: K, N and T are each below 2^31, and T*K, T*N and
- * N*retro_row_bytes(type, K) are each below 2^62. */
+/* Size limits: K, N and T are each below 2^31, T*K and T*N below 2^60, and
+ * N*retro_row_bytes(type, K) below 2^62 (retro_dequantize: N*K below 2^60). */
 
 /*
  * dst[t][k] = sum_n W[n][k] * G[t][n] for t < T, k < K.

@@ -16,6 +16,13 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
+# the system ROCm one this library links against. Whichever is loaded first
+# serves the whole process, and torch only works on its own, so torch must be
+# loaded before the library: then the library's kernels, torch's memory and
+# torch's streams all belong to one runtime.
+import torch  # noqa: F401
+
 from . import _build
 
 F32, F16, Q4_0, Q8_0, Q4_K, BF16 = 0, 1, 2, 8, 12, 30
@@ -98,8 +105,6 @@ def _check(code: int) -> None:
 
 
 def _stream_handle(stream) -> int:
-    import torch
-
     s = torch.cuda.current_stream() if stream is None else stream
     return int(s.cuda_stream)
 
@@ -109,8 +114,6 @@ def _ptr(t) -> int | None:
 
 
 def _device_tensor(t, name):
-    import torch
-
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
@@ -124,8 +127,6 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
     W is any contiguous device tensor holding N * row_bytes(wtype, K) bytes.
     Runs asynchronously on `stream` (default: torch's current stream).
     """
-    import torch
-
     _device_tensor(W, "W")
     _device_tensor(G, "G")
     if G.dtype != torch.float32 or G.dim() != 2:
@@ -149,12 +150,15 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
 
 def dequantize(wtype: int, W, K: int, N: int, out=None, stream=None):
     """Decoded float32 N x K copy of W (a test hook; out_prod never makes one)."""
-    import torch
-
     _device_tensor(W, "W")
+    rb = row_bytes(wtype, K)
+    if rb >= 0 and W.numel() * W.element_size() != N * rb:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
     if out is None:
         out = torch.empty((N, K), dtype=torch.float32, device=W.device)
     else:
         _device_tensor(out, "out")
+        if out.dtype != torch.float32 or tuple(out.shape) != (N, K):
+            raise ValueError("out must be float32 N x K")
     _check(lib.retro_dequantize(int(wtype), _ptr(W), _ptr(out), int(K), int(N), _stream_handle(stream)))
     return out

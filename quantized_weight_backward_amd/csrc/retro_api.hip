@@ -21,6 +21,7 @@ using namespace retro;
 constexpr int kNumCUs = 256;  // MI355X
 constexpr int64_t kDimLimit = int64_t(1) << 31;
 constexpr int64_t kByteLimit = int64_t(1) << 62;
+constexpr int64_t kCountLimit = int64_t(1) << 60;  // float counts: 4 * count < 2^62
 constexpr int64_t kGridLimit = int64_t(1) << 30;
 
 struct Geometry {
@@ -55,7 +56,7 @@ int check_shape(int type, int64_t K, int64_t N, int64_t T) {
     if (K % g.block) return RETRO_E_SHAPE;
     if (K >= kDimLimit || N >= kDimLimit || T >= kDimLimit) return RETRO_E_SHAPE;
     const int64_t pitch = K / g.block * g.bytes;
-    if (!product_below(T, K, kByteLimit) || !product_below(T, N, kByteLimit) ||
+    if (!product_below(T, K, kCountLimit) || !product_below(T, N, kCountLimit) ||
         !product_below(N, pitch, kByteLimit))
         return RETRO_E_SHAPE;
     return RETRO_OK;
@@ -108,6 +109,10 @@ int choose(int type, int64_t K, int64_t N, int64_t T) {
     return best < 0 ? RETRO_E_SHAPE : best;
 }
 
+// hipGetLastError reports the last error of any runtime call on this thread,
+// so it is cleared right before each launch (clear_last_error) and read right
+// after it (launch_status): the result is this launch's status only.
+void clear_last_error() { (void)hipGetLastError(); }
 int launch_status() { return hipGetLastError() == hipSuccess ? RETRO_OK : RETRO_E_HIP; }
 
 template <int TYPE, int WA, int WB, int WGT, int WGK>
@@ -130,6 +135,7 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
+    clear_last_error();
     hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt), dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
@@ -147,6 +153,7 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     a.pitch = row_bytes_of(TYPE, K);
     a.wide = (K % 4 == 0) ? 1 : 0;
     a.gvec = (N % 4 == 0) ? 1 : 0;
+    clear_last_error();
     hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves>), dim3(unsigned(cdiv(K, 64))), dim3(kWaves * 64), 0, st,
                        a);
     return launch_status();
@@ -223,6 +230,7 @@ int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t 
     a.wide = (K % 4 == 0) ? 1 : 0;
     a.gpr = int(cdiv(K, 4));
     a.groups = N * int64_t(a.gpr);
+    clear_last_error();
     hipLaunchKernelGGL((dequant_kernel<TYPE>), dim3(unsigned(cdiv(a.groups, 256))), dim3(256), 0, st, a);
     return launch_status();
 }
@@ -245,7 +253,7 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
     Geometry g;
     if (!geometry(type, g)) return RETRO_E_TYPE;
     if (K < 0 || N < 0 || K % g.block || K >= kDimLimit || N >= kDimLimit) return RETRO_E_SHAPE;
-    if (!product_below(N, K, kByteLimit / 4) || cdiv(N * cdiv(K, 4), 256) >= kGridLimit) return RETRO_E_SHAPE;
+    if (!product_below(N, K, kCountLimit) || cdiv(N * cdiv(K, 4), 256) >= kGridLimit) return RETRO_E_SHAPE;
     if (K == 0 || N == 0) return RETRO_OK;
     if (!W || !out) return RETRO_E_NULL;
     if (!aligned16(W) || !aligned16(out)) return RETRO_E_ALIGN;
