@@ -19,6 +19,13 @@ namespace {
 using namespace retro;
 
 constexpr int kNumCUs = 256;  // MI355X
+
+// Waves per skinny workgroup (each CU runs one skinny workgroup at the
+// benchmarked shapes, so this sets the waves per SIMD available to hide
+// memory latency).
+#ifndef RETRO_SKINNY_WAVES
+#define RETRO_SKINNY_WAVES 16
+#endif
 constexpr int64_t kDimLimit = int64_t(1) << 31;
 constexpr int64_t kByteLimit = int64_t(1) << 62;
 constexpr int64_t kCountLimit = int64_t(1) << 60;  // float counts: 4 * count < 2^62
@@ -88,13 +95,17 @@ bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t T) {
     return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit;
 }
 
-bool skinny_applies(int64_t K, int64_t T) { return T <= 16 && cdiv(K, 64) < kGridLimit; }
+// The skinny kernel addresses the rows of one 16-row group with 32-bit
+// offsets from the group's first row.
+bool skinny_applies(int type, int64_t K, int64_t T) {
+    return T <= 16 && cdiv(K, 64) < kGridLimit && 16 * row_bytes_of(type, K) < (int64_t(1) << 32);
+}
 
 // Pick the tile that minimises (tiles per CU, rounded up) x tile area x
 // penalty: the rounding is the wave quantisation over 256 CUs.
 int choose(int type, int64_t K, int64_t N, int64_t T) {
     (void)N;
-    if (skinny_applies(K, T)) return RETRO_VARIANT_SKINNY;
+    if (skinny_applies(type, K, T)) return RETRO_VARIANT_SKINNY;
     int best = -1;
     double best_cost = 0;
     for (const auto& v : kTiles) {
@@ -142,7 +153,7 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
 
 template <int TYPE>
 int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
-    constexpr int kWaves = 8;
+    constexpr int kWaves = RETRO_SKINNY_WAVES;
     SkinnyArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.G = G;
@@ -153,9 +164,12 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     a.pitch = row_bytes_of(TYPE, K);
     a.wide = (K % 4 == 0) ? 1 : 0;
     a.gvec = (N % 4 == 0) ? 1 : 0;
+    const dim3 grid(unsigned(cdiv(K, 64))), block(kWaves * 64);
     clear_last_error();
-    hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves>), dim3(unsigned(cdiv(K, 64))), dim3(kWaves * 64), 0, st,
-                       a);
+    if (a.wide && a.gvec)
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false>), grid, block, 0, st, a);
     return launch_status();
 }
 
@@ -202,7 +216,7 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         variant = choose(type, K, N, T);
         if (variant < 0) return variant;
     } else if (variant == RETRO_VARIANT_SKINNY) {
-        if (!skinny_applies(K, T)) return RETRO_E_VARIANT;
+        if (!skinny_applies(type, K, T)) return RETRO_E_VARIANT;
     } else {
         const TileVariant* tv = find_tile(variant);
         if (!tv || !tile_applies(*tv, type, K, T)) return RETRO_E_VARIANT;

@@ -56,13 +56,17 @@ __device__ __forceinline__ void q8_0_x4(uint32_t w, float d, float out[4]) {
     }
 }
 
+// The four low (high = false) or high nibbles of a code word, one per byte:
+// masking once lets each byte be converted by one byte-to-float instruction.
+__device__ __forceinline__ uint32_t nibbles(uint32_t w, bool high) { return (high ? (w >> 4) : w) & 0x0F0F0F0Fu; }
+
 // Q4_0: from four code bytes take the low (high = false) or high nibbles;
 // value d * (q - 8).
 __device__ __forceinline__ void q4_0_x4(uint32_t w, bool high, float d, float out[4]) {
-    const uint32_t s = high ? 4u : 0u;
+    const uint32_t m = nibbles(w, high);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int q = static_cast<int>((w >> (8 * i + s)) & 15u);
+        const int q = static_cast<int>((m >> (8 * i)) & 0xFFu);
         out[i] = d * static_cast<float>(q - 8);
     }
 }
@@ -96,12 +100,9 @@ __device__ __forceinline__ void q4_k_coeffs(uint32_t h0, uint32_t s0, uint32_t s
 
 // Q4_K: from four code bytes take the low or high nibbles; value a*q - b.
 __device__ __forceinline__ void q4_k_x4(uint32_t w, bool high, float a, float b, float out[4]) {
-    const uint32_t s = high ? 4u : 0u;
+    const uint32_t m = nibbles(w, high);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t q = (w >> (8 * i + s)) & 15u;
-        out[i] = a * static_cast<float>(q) - b;
-    }
+    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) - b;
 }
 
 }  // namespace retro

@@ -434,7 +434,165 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
     }
 }
 
-template <int TYPE, int NWAVES>
+// Per-lane raw data of one 16-row group (see out_prod_skinny_kernel for the
+// lane layout): the code words of the lane's 4 rows, the header words of the
+// (row, block) scale this lane decodes for the whole wave, and 4 G values.
+template <int TYPE>
+struct SkinnyRaw {
+    static constexpr int CW = (TYPE == kF32) ? 4 : (TYPE == kF16 || TYPE == kBF16) ? 2 : 1;
+    static constexpr int HW = (TYPE == kQ4_K) ? 4 : 1;
+    uint32_t code[4][CW];
+    uint32_t hdr[HW];
+    float g[4];
+};
+
+// Fill r for the 16-row group starting at n0.
+// MASKED = false: the whole group is inside W (n0 + 16 <= N), K % 4 == 0 and
+// N % 4 == 0; every load is then unconditional (no branch between the loads
+// of the next group and the contraction of the current one). Columns at or
+// beyond K and rows of G at or beyond T are clamped to valid addresses: they
+// only feed dst columns and rows that are never stored.
+// MASKED = true: any group and shape; out-of-range elements read as zero.
+template <int TYPE, bool MASKED>
+__device__ __forceinline__ void skinny_fetch(const SkinnyArgs& a, int n0, int k0, int lane, SkinnyRaw<TYPE>& r) {
+    const int j = lane & 15, rq = lane >> 4;
+    const int K = a.K, N = a.N;
+    const int nq = n0 + 4 * rq;
+    const int kl = MASKED ? k0 + 4 * j : min(k0 + 4 * j, K - 4);
+    const uint8_t* Wg = a.W + (long long)n0 * a.pitch;  // wave-uniform group base
+    // G[t = j][nq .. nq+3]
+    if constexpr (!MASKED) {
+        const int t = min(j, a.T - 1);
+        const float4 v = *reinterpret_cast<const float4*>(a.G + (long long)t * N + nq);
+        r.g[0] = v.x; r.g[1] = v.y; r.g[2] = v.z; r.g[3] = v.w;
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) r.g[s] = 0.f;
+        if (j < a.T) {
+            const float* gp = a.G + (long long)j * N + nq;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (nq + s < N) r.g[s] = gp[s];
+        }
+    }
+    // code words of rows nq + s, columns kl .. kl+3
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int w = 0; w < SkinnyRaw<TYPE>::CW; ++w) r.code[s][w] = 0u;
+        if (MASKED && nq + s >= N) continue;
+        const uint8_t* row = Wg + (unsigned)((4 * rq + s) * a.pitch);
+        if constexpr (TYPE == kF32) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(row) + kl;
+            if (!MASKED || (a.wide && kl + 4 <= K)) {
+                const uint4 v = *reinterpret_cast<const uint4*>(p);
+                r.code[s][0] = v.x; r.code[s][1] = v.y; r.code[s][2] = v.z; r.code[s][3] = v.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kl + i < K) r.code[s][i] = p[i];
+            }
+        } else if constexpr (TYPE == kF16 || TYPE == kBF16) {
+            const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + kl;
+            if (!MASKED || (a.wide && kl + 4 <= K)) {
+                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                r.code[s][0] = v.x;
+                r.code[s][1] = v.y;
+            } else {
+                if (kl < K) r.code[s][0] |= p[0];
+                if (kl + 1 < K) r.code[s][0] |= uint32_t(p[1]) << 16;
+                if (kl + 2 < K) r.code[s][1] |= p[2];
+                if (kl + 3 < K) r.code[s][1] |= uint32_t(p[3]) << 16;
+            }
+        } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+            if (!MASKED || kl < K) {
+                constexpr int BYTES = Format<TYPE>::kBytes;
+                const int off = (TYPE == kQ8_0) ? (kl & 31) : (kl & 15);
+                const uint16_t* c = reinterpret_cast<const uint16_t*>(row + (kl >> 5) * BYTES + 2 + off);
+                r.code[s][0] = uint32_t(c[0]) | (uint32_t(c[1]) << 16);
+            }
+        } else {  // kQ4_K
+            const int e = kl & 255;
+            r.code[s][0] = *reinterpret_cast<const uint32_t*>(row + (kl >> 8) * 144 + 16 + 32 * (e >> 6) + (e & 31));
+        }
+    }
+    // header of the scale pair (row n0 + (lane & 31) / 2, block/sub-block lane & 1)
+    const int hr = (lane & 31) >> 1, sel = lane & 1;
+    const uint8_t* hrow = Wg + (unsigned)(hr * a.pitch);
+    const bool hvalid = !MASKED || n0 + hr < N;
+    if constexpr (TYPE == kQ4_K) {
+        uint4 h = make_uint4(0u, 0u, 0u, 0u);
+        if (hvalid) h = *reinterpret_cast<const uint4*>(hrow + (k0 >> 8) * 144);
+        r.hdr[0] = h.x; r.hdr[1] = h.y; r.hdr[2] = h.z; r.hdr[3] = h.w;
+    } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+        const int kb = MASKED ? k0 + 32 * sel : min(k0 + 32 * sel, K - 32);
+        r.hdr[0] = 0u;
+        if (hvalid && (!MASKED || kb < K))
+            r.hdr[0] = *reinterpret_cast<const uint16_t*>(hrow + (kb >> 5) * Format<TYPE>::kBytes);
+    } else {
+        r.hdr[0] = 0u;
+    }
+}
+
+// Value of `v` held by lane `src` of this wave.
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+template <int TYPE>
+__device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, int lane, float wv[4][4]) {
+    const int j = lane & 15, rq = lane >> 4;
+    const int hi = (j >= 8) ? 1 : 0;  // second block / sub-block of the 64-column slab
+    if constexpr (TYPE == kF32) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[s][i] = __uint_as_float(r.code[s][i]);
+    } else if constexpr (TYPE == kF16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            f16x2(r.code[s][0], wv[s][0], wv[s][1]);
+            f16x2(r.code[s][1], wv[s][2], wv[s][3]);
+        }
+    } else if constexpr (TYPE == kBF16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x2(r.code[s][0], wv[s][0], wv[s][1]);
+            bf16x2(r.code[s][1], wv[s][2], wv[s][3]);
+        }
+    } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+        const float dmine = half_to_f32(r.hdr[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float d = lane_value(dmine, 2 * (4 * rq + s) + hi);
+            if constexpr (TYPE == kQ8_0) {
+                q8_0_x4(r.code[s][0], d, wv[s]);
+            } else {
+                q4_0_x4(r.code[s][0], ((4 * j) & 31) >= 16, d, wv[s]);
+            }
+        }
+    } else {  // kQ4_K: this lane's pair is sub-block 2c + (lane & 1)
+        const int c = (k0 & 255) >> 6;
+        float am, bm;
+        q4_k_coeffs(r.hdr[0], r.hdr[1], r.hdr[2], r.hdr[3], 2 * c + (lane & 1), am, bm);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int src = 2 * (4 * rq + s) + hi;
+            q4_k_x4(r.code[s][0], hi != 0, lane_value(am, src), lane_value(bm, src), wv[s]);
+        }
+    }
+}
+
+// dst[t][k0 .. k0+63] for all t < T (T <= 16). MFMA 16x16x4 operands: lane l
+// supplies A[i = l%16][kk = l/16] and B[kk = l/16][j = l%16]. Step s of a
+// 16-row group starting at n0 uses W row n0 + 4*(l/16) + s for lane l, so a
+// lane reads G[t][n0 + 4*(l/16) .. +3] with one float4. Column j of
+// accumulator block b is dst column k0 + 4*j + b, so a lane decodes 4
+// consecutive elements per row. Each wave walks its own 16-row groups with
+// the next group's loads in flight while the current one is decoded and
+// contracted; the scale of each (row, block) is decoded by one lane and
+// handed to the lanes that need it.
+template <int TYPE, int NWAVES, bool FAST>
 __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs args) {
     constexpr int KS = 64;  // dst columns per workgroup
     __shared__ __attribute__((aligned(16))) float part[NWAVES * 16 * KS];
@@ -442,47 +600,47 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = args.K, N = args.N, T = args.T;
     const int k0 = blockIdx.x * KS;
-    // MFMA 16x16x4 operands: lane l supplies A[i = l%16][kk = l/16] and
-    // B[kk = l/16][j = l%16]. Step s of a 16-row group starting at n0 uses W row
-    // n0 + 4*(l/16) + s for lane l, so a lane reads G[t][n0 + 4*(l/16) .. +3]
-    // with one float4. Column j of accumulator block b is dst column
-    // k0 + 4*j + b, so a lane decodes 4 consecutive elements per row.
     const int j = lane & 15, rq = lane >> 4;
-    const int t = j;  // A row index = the t row of G
-    const int kl = k0 + 4 * j;
 
     f32x4 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int n0 = 16 * wave; n0 < N; n0 += 16 * NWAVES) {
-        const int nq = n0 + 4 * rq;
-        float gv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t < T) {
-            const float* gp = args.G + (long long)t * N + nq;
-            if (args.gvec && nq + 4 <= N) {
-                const float4 v = *reinterpret_cast<const float4*>(gp);
-                gv[0] = v.x; gv[1] = v.y; gv[2] = v.z; gv[3] = v.w;
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) gv[s] = (nq + s < N) ? gp[s] : 0.f;
-            }
-        }
+    auto contract = [&](const SkinnyRaw<TYPE>& r) {
         float wv[4][4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int n = nq + s;
-            if (n < N) {
-                skinny_load4<TYPE>(args.W + (long long)n * args.pitch, kl, K, args.wide, wv[s]);
-            } else {
-                wv[s][0] = wv[s][1] = wv[s][2] = wv[s][3] = 0.f;
-            }
-        }
+        skinny_decode<TYPE>(r, k0, lane, wv);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[s], wv[s][b], acc[b], 0, 0, 0);
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.g[s], wv[s][b], acc[b], 0, 0, 0);
+    };
+
+    // Full 16-row groups: group g goes to wave g % NWAVES. The next group's
+    // loads are issued before the current group is contracted, alternating
+    // between two register buffers; past the wave's last group the fetch
+    // repeats a valid group and is not used.
+    const int nfull = FAST ? N / 16 : 0;
+    int g = wave;
+    if (g < nfull) {
+        SkinnyRaw<TYPE> ra, rb;
+        skinny_fetch<TYPE, false>(args, 16 * g, k0, lane, ra);
+        while (true) {
+            skinny_fetch<TYPE, false>(args, 16 * min(g + NWAVES, nfull - 1), k0, lane, rb);
+            contract(ra);
+            g += NWAVES;
+            if (g >= nfull) break;
+            skinny_fetch<TYPE, false>(args, 16 * min(g + NWAVES, nfull - 1), k0, lane, ra);
+            contract(rb);
+            g += NWAVES;
+            if (g >= nfull) break;
+        }
+    }
+    // Remaining (partial, or all groups of a shape off the fast path), masked.
+    for (; 16 * g < N; g += NWAVES) {
+        SkinnyRaw<TYPE> r;
+        skinny_fetch<TYPE, true>(args, 16 * g, k0, lane, r);
+        contract(r);
     }
 
     // D layout of v_mfma_f32_16x16x4f32: lane l, register v holds row
