@@ -58,14 +58,84 @@ def read_traffic(tag: str):
     return float(val.group(1))
 
 
-def cpu_baseline(case: dict, target_s: float = 12.0) -> dict:
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
+             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_FETCH_SIZE -o run -- "
+                  "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_WRITE_SIZE -o run -- "
+                  "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_FETCH_SIZE -o run -- "
+                       "python3 bench.py --copy-probe-mib 1024",
+    "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_WRITE_SIZE -o run -- "
+                       "python3 bench.py --copy-probe-mib 1024",
+}
+KERNELS = {  # summary tag -> (kernel-name prefix in rocprofv3 output, workload)
+    f"tile_{LARGE}": ("void retro::out_prod_tile_kernel<12, 2, 4, 2, 2>", LARGE),
+    f"skinny_{SKINNY}": ("void retro::out_prod_skinny_kernel<12, 16, true>", SKINNY),
+}
+
+
+def _mean_counter(path: str, prefix: str) -> tuple[float, int]:
+    import csv
+
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if r["Kernel_Name"].startswith(prefix)]
+    return (sum(vals) / len(vals) if vals else float("nan")), len(vals)
+
+
+def summarize(run_dir: str) -> None:
+    """Write profiles/<tag>_trace.md and <tag>_traffic.md from rocprofv3 output
+    (the commands in PROFILE_COMMANDS, run from the repository root)."""
+    import csv
+
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = list(csv.DictReader(open(os.path.join(run_dir, "prof_trace", "run_kernel_stats.csv"))))
+    copy_bytes = 1024 << 20
+    f_copy, _ = _mean_counter(os.path.join(run_dir, "pmc_copy_FETCH_SIZE", "run_counter_collection.csv"),
+                              "__amd_rocclr_copyBuffer")
+    w_copy, _ = _mean_counter(os.path.join(run_dir, "pmc_copy_WRITE_SIZE", "run_counter_collection.csv"),
+                              "__amd_rocclr_copyBuffer")
+    f_scale = copy_bytes / (f_copy * 1024)
+    w_scale = copy_bytes / (w_copy * 1024)
+    src = kernel_source_hash()
+    for tag, (prefix, workload) in KERNELS.items():
+        row = next(r for r in stats if r["Name"].startswith(prefix))
+        lines = [f"# {tag}: rocprofv3 kernel trace", "",
+                 f"Command (repository root): `{PROFILE_COMMANDS['trace']}`", "",
+                 f"Kernel: `{row['Name']}` (workload {workload})", "",
+                 "| calls | average (us) | min (us) | max (us) | share of GPU time |",
+                 "|---|---|---|---|---|",
+                 f"| {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | {float(row['MinNs']) / 1e3:.2f} | "
+                 f"{float(row['MaxNs']) / 1e3:.2f} | {float(row['Percentage']):.2f}% |", "",
+                 f"kernel source_sha256: {src}", ""]
+        open(os.path.join(PROFILES, f"{tag}_trace.md"), "w").write("\n".join(lines))
+        fetch, nf = _mean_counter(os.path.join(run_dir, "pmc_FETCH_SIZE", "run_counter_collection.csv"), prefix)
+        write, nw = _mean_counter(os.path.join(run_dir, "pmc_WRITE_SIZE", "run_counter_collection.csv"), prefix)
+        hbm = fetch * 1024 * f_scale + write * 1024 * w_scale
+        lines = [f"# {tag}: HBM traffic per launch (rocprofv3 counters)", "",
+                 "Commands (repository root):", "",
+                 *[f"- `{PROFILE_COMMANDS[k]}`" for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE",
+                                                           "copy_WRITE_SIZE")], "",
+                 "Calibration: a 1 GiB device-to-device copy reads and writes 1073741824 bytes; the counters "
+                 f"read FETCH_SIZE = {f_copy:.1f} KiB and WRITE_SIZE = {w_copy:.1f} KiB per copy launch, so "
+                 f"FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}.", "",
+                 "| counter | KiB per launch (mean) | launches | scaled bytes |", "|---|---|---|---|",
+                 f"| FETCH_SIZE | {fetch:.1f} | {nf} | {fetch * 1024 * f_scale:.4g} |",
+                 f"| WRITE_SIZE | {write:.1f} | {nw} | {write * 1024 * w_scale:.4g} |", "",
+                 f"hbm_bytes_per_launch: {hbm:.6g}",
+                 f"source_sha256: {src}", ""]
+        open(os.path.join(PROFILES, f"{tag}_traffic.md"), "w").write("\n".join(lines))
+        print(f"{tag}: avg {float(row['AverageNs']) / 1e3:.2f} us, traffic {hbm / 1e6:.1f} MB per launch")
+
+
+def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
     """The CPU oracle (double accumulation, as it stands) on sampled t rows of
     the large-T workload, all host cores; FLOPs counted as 2*N*K per row."""
     import numpy as np
 
     import oracle
 
-    cores = max(1, min(64, os.cpu_count() or 1))
+    cores = max(1, min(16, os.cpu_count() or 1))  # a one-GPU share of the host
     N, K = case["N"], case["K"]
     rows = np.arange(8 * cores) % case["T"]
     t0 = time.perf_counter()
@@ -91,7 +161,13 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this size (counter calibration)")
+    ap.add_argument("--summarize", metavar="RUN_DIR", default=None,
+                    help="write profiles/*.md from rocprofv3 output under RUN_DIR and exit (no GPU)")
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -198,7 +274,8 @@ def main() -> int:
                      "kernel": f"out_prod_tile_kernel ({q.VARIANT_NAMES[v_large]})",
                      "avg_launch_ms": round(avg_large * 1e3, 4), "min_launch_ms": round(float(t_large.min()) * 1e3, 4),
                      "flops_per_launch": fl_large},
-        "skinny": {"kernel": "out_prod_skinny_kernel", "avg_launch_us": round(avg_skinny * 1e6, 3),
+        "skinny": {"kernel": "out_prod_skinny_kernel", "traffic": read_traffic(f"skinny_{SKINNY}"),
+                   "avg_launch_us": round(avg_skinny * 1e6, 3),
                    "min_launch_us": round(float(t_skinny.min()) * 1e6, 3),
                    "tflops": round(skinny_tflops, 3), "weight_gbs": round(skinny_gbs, 1),
                    "hbm_frac": round(skinny_gbs / PEAK_HBM_GBS, 4),

@@ -31,6 +31,11 @@
  * Block formats (GGUF; the pages only name them): fp16 fields are
  * little-endian binary16; see the decoder functions for each layout. Build
  * with -O2 -ffp-contract=off and no fast-math.
+ *
+ * Parity unpinned against the pages: the bit order of the Q4_K 12-byte
+ * sub-scale/sub-min field. The pages print no Q4_K block; the order used is
+ * the GGUF one, and the tests pin the decoder to hand-packed fixtures of that
+ * reading and to a full pack bijection, not to values from the pages.
  */
 #include <math.h>
 #include <pthread.h>

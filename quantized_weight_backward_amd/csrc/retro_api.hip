@@ -95,17 +95,17 @@ bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t T) {
     return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit;
 }
 
-// The skinny kernel addresses the rows of one 16-row group with 32-bit
-// offsets from the group's first row.
-bool skinny_applies(int type, int64_t K, int64_t T) {
-    return T <= 16 && cdiv(K, 64) < kGridLimit && 16 * row_bytes_of(type, K) < (int64_t(1) << 32);
+// The skinny kernel addresses one 16-row group of W, and the 16 rows of G
+// it reads, through buffer descriptors whose sizes are signed 32-bit.
+bool skinny_applies(int type, int64_t K, int64_t N, int64_t T) {
+    return T <= 16 && cdiv(K, 64) < kGridLimit && 16 * row_bytes_of(type, K) < (int64_t(1) << 31) &&
+           16 * N * 4 < (int64_t(1) << 31);
 }
 
 // Pick the tile that minimises (tiles per CU, rounded up) x tile area x
 // penalty: the rounding is the wave quantisation over 256 CUs.
 int choose(int type, int64_t K, int64_t N, int64_t T) {
-    (void)N;
-    if (skinny_applies(type, K, T)) return RETRO_VARIANT_SKINNY;
+    if (skinny_applies(type, K, N, T)) return RETRO_VARIANT_SKINNY;
     int best = -1;
     double best_cost = 0;
     for (const auto& v : kTiles) {
@@ -216,7 +216,7 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         variant = choose(type, K, N, T);
         if (variant < 0) return variant;
     } else if (variant == RETRO_VARIANT_SKINNY) {
-        if (!skinny_applies(type, K, T)) return RETRO_E_VARIANT;
+        if (!skinny_applies(type, K, N, T)) return RETRO_E_VARIANT;
     } else {
         const TileVariant* tv = find_tile(variant);
         if (!tv || !tile_applies(*tv, type, K, T)) return RETRO_E_VARIANT;

@@ -56,9 +56,17 @@ __device__ __forceinline__ void q8_0_x4(uint32_t w, float d, float out[4]) {
     }
 }
 
-// The four low (high = false) or high nibbles of a code word, one per byte:
-// masking once lets each byte be converted by one byte-to-float instruction.
-__device__ __forceinline__ uint32_t nibbles(uint32_t w, bool high) { return (high ? (w >> 4) : w) & 0x0F0F0F0Fu; }
+// The four low (high = false) or high nibbles of a code word, one per byte.
+// The mask is applied once per word by an instruction the compiler cannot
+// see through, so that each byte is then converted by one byte-to-float
+// instruction (v_cvt_f32_ubyte0..3) rather than a bit-field extract plus a
+// conversion per element.
+__device__ __forceinline__ uint32_t nibbles(uint32_t w, bool high) {
+    const uint32_t x = high ? (w >> 4) : w;
+    uint32_t m;
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(m) : "v"(x));
+    return m;
+}
 
 // Q4_0: from four code bytes take the low (high = false) or high nibbles;
 // value d * (q - 8).

@@ -69,15 +69,21 @@ __device__ __forceinline__ uint32_t lds_word_a2(const uint8_t* p) {
     return uint32_t(q[0]) | (uint32_t(q[1]) << 16);
 }
 
-// Map a workgroup id to a logical tile so that each XCD (workgroups are
-// dispatched round-robin over the 8 XCDs) owns a contiguous range of logical
-// tiles, then order logical tiles in groups of GT row-tiles so that
-// neighbours share rows of G and columns of W in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int b, int tiles_t, int tiles_k, int& tt, int& tk) {
-    const int nt = tiles_t * tiles_k;
-    const int per = nt >> 3, rem = nt & 7;
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8), and each XCD has its own L2. xcd_remap turns a workgroup id
+// into a logical index such that every XCD owns one contiguous range of
+// logical indices (a bijection on [0, n)), so neighbouring logical work items
+// share their XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+    const int per = n >> 3, rem = n & 7;
     const int x = b & 7, i = b >> 3;
-    const int lin = x * per + (x < rem ? x : rem) + i;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+// Logical tile -> (row tile, column tile), in groups of GT row tiles so that
+// neighbours share rows of G and columns of W.
+__device__ __forceinline__ void tile_coords(int b, int tiles_t, int tiles_k, int& tt, int& tk) {
+    const int lin = xcd_remap(b, tiles_t * tiles_k);
     constexpr int GT = 8;
     const int span = GT * tiles_k;
     const int group = lin / span;
@@ -446,89 +452,153 @@ struct SkinnyRaw {
     float g[4];
 };
 
-// Fill r for the 16-row group starting at n0.
-// MASKED = false: the whole group is inside W (n0 + 16 <= N), K % 4 == 0 and
-// N % 4 == 0; every load is then unconditional (no branch between the loads
-// of the next group and the contraction of the current one). Columns at or
+// Byte offsets, relative to the first W row / G column of a 16-row group,
+// of everything one lane loads for that group on the fast path; they do not
+// change from group to group, so each group costs one uniform base pointer.
+struct SkinnyOffsets {
+    uint32_t code[4];  // code words of rows 4*(l/16) + s, columns k0 + 4*(l%16) ..
+    uint32_t hdr;      // header of the scale pair this lane decodes
+    uint32_t g;        // G[min(l%16, T-1)][4*(l/16)] (bytes from G + n0)
+};
+
+// Fast path (K % 4 == 0, N % 4 == 0, whole group inside W). Columns at or
 // beyond K and rows of G at or beyond T are clamped to valid addresses: they
 // only feed dst columns and rows that are never stored.
-// MASKED = true: any group and shape; out-of-range elements read as zero.
-template <int TYPE, bool MASKED>
-__device__ __forceinline__ void skinny_fetch(const SkinnyArgs& a, int n0, int k0, int lane, SkinnyRaw<TYPE>& r) {
+template <int TYPE>
+__device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int k0, int lane) {
+    const int j = lane & 15, rq = lane >> 4;
+    const int K = a.K;
+    const int kl = min(k0 + 4 * j, K - 4);
+    uint32_t col;
+    if constexpr (TYPE == kF32) {
+        col = 4u * kl;
+    } else if constexpr (TYPE == kF16 || TYPE == kBF16) {
+        col = 2u * kl;
+    } else if constexpr (TYPE == kQ8_0) {
+        col = (kl >> 5) * 34 + 2 + (kl & 31);
+    } else if constexpr (TYPE == kQ4_0) {
+        col = (kl >> 5) * 18 + 2 + (kl & 15);
+    } else {
+        const int e = kl & 255;
+        col = (kl >> 8) * 144 + 16 + 32 * (e >> 6) + (e & 31);
+    }
+    SkinnyOffsets o;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) o.code[s] = uint32_t((4 * rq + s) * a.pitch) + col;
+    const int hr = (lane & 31) >> 1, sel = lane & 1;
+    uint32_t hcol = 0;
+    if constexpr (TYPE == kQ4_K) hcol = (k0 >> 8) * 144;
+    if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) hcol = (min(k0 + 32 * sel, K - 32) >> 5) * Format<TYPE>::kBytes;
+    o.hdr = uint32_t(hr * a.pitch) + hcol;
+    o.g = uint32_t(((long long)min(j, a.T - 1) * a.N + 4 * rq) * 4);
+    return o;
+}
+
+// Buffer resource over [base, base + bytes): gfx9 descriptor, raw 32-bit
+// access, no stride. Loads at or past `bytes` return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int TYPE>
+__device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, const SkinnyOffsets& o,
+                                                  SkinnyRaw<TYPE>& r) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    // n0 is the same in every lane; readfirstlane makes that visible to the
+    // compiler, so the two descriptors (this group's 16 W rows; the G columns
+    // from n0 on) are built in scalar registers and every load is a fixed
+    // per-lane offset from them.
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.W + (long long)n0 * a.pitch, uint32_t(16 * a.pitch));
+    const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(a.G + n0, uint32_t(4 * ((long long)(a.T - 1) * a.N + 16)));
+    const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(gr, o.g, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.g[q] = __uint_as_float(gv[q]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (TYPE == kF32) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, o.code[s], 0, 0);
+            r.code[s][0] = v.x; r.code[s][1] = v.y; r.code[s][2] = v.z; r.code[s][3] = v.w;
+        } else if constexpr (TYPE == kF16 || TYPE == kBF16) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, o.code[s], 0, 0);
+            r.code[s][0] = v.x;
+            r.code[s][1] = v.y;
+        } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+            // code bytes sit at 2-byte alignment inside these blocks
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s], 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s] + 2, 0, 0);
+            r.code[s][0] = lo | (hi << 16);
+        } else {
+            r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
+        }
+    }
+    if constexpr (TYPE == kQ4_K) {
+        const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wr, o.hdr, 0, 0);
+        r.hdr[0] = h.x; r.hdr[1] = h.y; r.hdr[2] = h.z; r.hdr[3] = h.w;
+    } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+        r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
+    } else {
+        r.hdr[0] = 0u;
+    }
+}
+
+// Any group and shape: out-of-range elements read as zero.
+template <int TYPE>
+__device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0, int k0, int lane,
+                                                    SkinnyRaw<TYPE>& r) {
     const int j = lane & 15, rq = lane >> 4;
     const int K = a.K, N = a.N;
     const int nq = n0 + 4 * rq;
-    const int kl = MASKED ? k0 + 4 * j : min(k0 + 4 * j, K - 4);
-    const uint8_t* Wg = a.W + (long long)n0 * a.pitch;  // wave-uniform group base
-    // G[t = j][nq .. nq+3]
-    if constexpr (!MASKED) {
-        const int t = min(j, a.T - 1);
-        const float4 v = *reinterpret_cast<const float4*>(a.G + (long long)t * N + nq);
-        r.g[0] = v.x; r.g[1] = v.y; r.g[2] = v.z; r.g[3] = v.w;
-    } else {
+    const int kl = k0 + 4 * j;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) r.g[s] = 0.f;
-        if (j < a.T) {
-            const float* gp = a.G + (long long)j * N + nq;
+    for (int s = 0; s < 4; ++s) r.g[s] = 0.f;
+    if (j < a.T) {
+        const float* gp = a.G + (long long)j * N + nq;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                if (nq + s < N) r.g[s] = gp[s];
-        }
+        for (int s = 0; s < 4; ++s)
+            if (nq + s < N) r.g[s] = gp[s];
     }
-    // code words of rows nq + s, columns kl .. kl+3
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int w = 0; w < SkinnyRaw<TYPE>::CW; ++w) r.code[s][w] = 0u;
-        if (MASKED && nq + s >= N) continue;
-        const uint8_t* row = Wg + (unsigned)((4 * rq + s) * a.pitch);
+        if (nq + s >= N) continue;
+        const uint8_t* row = a.W + (long long)(nq + s) * a.pitch;
         if constexpr (TYPE == kF32) {
             const uint32_t* p = reinterpret_cast<const uint32_t*>(row) + kl;
-            if (!MASKED || (a.wide && kl + 4 <= K)) {
-                const uint4 v = *reinterpret_cast<const uint4*>(p);
-                r.code[s][0] = v.x; r.code[s][1] = v.y; r.code[s][2] = v.z; r.code[s][3] = v.w;
-            } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (kl + i < K) r.code[s][i] = p[i];
-            }
+            for (int i = 0; i < 4; ++i)
+                if (kl + i < K) r.code[s][i] = p[i];
         } else if constexpr (TYPE == kF16 || TYPE == kBF16) {
             const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + kl;
-            if (!MASKED || (a.wide && kl + 4 <= K)) {
-                const uint2 v = *reinterpret_cast<const uint2*>(p);
-                r.code[s][0] = v.x;
-                r.code[s][1] = v.y;
-            } else {
-                if (kl < K) r.code[s][0] |= p[0];
-                if (kl + 1 < K) r.code[s][0] |= uint32_t(p[1]) << 16;
-                if (kl + 2 < K) r.code[s][1] |= p[2];
-                if (kl + 3 < K) r.code[s][1] |= uint32_t(p[3]) << 16;
-            }
+            if (kl < K) r.code[s][0] |= p[0];
+            if (kl + 1 < K) r.code[s][0] |= uint32_t(p[1]) << 16;
+            if (kl + 2 < K) r.code[s][1] |= p[2];
+            if (kl + 3 < K) r.code[s][1] |= uint32_t(p[3]) << 16;
         } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
-            if (!MASKED || kl < K) {
+            if (kl < K) {
                 constexpr int BYTES = Format<TYPE>::kBytes;
                 const int off = (TYPE == kQ8_0) ? (kl & 31) : (kl & 15);
                 const uint16_t* c = reinterpret_cast<const uint16_t*>(row + (kl >> 5) * BYTES + 2 + off);
                 r.code[s][0] = uint32_t(c[0]) | (uint32_t(c[1]) << 16);
             }
-        } else {  // kQ4_K
+        } else {  // kQ4_K (K % 256 == 0, so kl < K)
             const int e = kl & 255;
             r.code[s][0] = *reinterpret_cast<const uint32_t*>(row + (kl >> 8) * 144 + 16 + 32 * (e >> 6) + (e & 31));
         }
     }
-    // header of the scale pair (row n0 + (lane & 31) / 2, block/sub-block lane & 1)
     const int hr = (lane & 31) >> 1, sel = lane & 1;
-    const uint8_t* hrow = Wg + (unsigned)(hr * a.pitch);
-    const bool hvalid = !MASKED || n0 + hr < N;
+    const bool hvalid = n0 + hr < N;
+    const uint8_t* hrow = a.W + (long long)(n0 + hr) * a.pitch;
     if constexpr (TYPE == kQ4_K) {
         uint4 h = make_uint4(0u, 0u, 0u, 0u);
         if (hvalid) h = *reinterpret_cast<const uint4*>(hrow + (k0 >> 8) * 144);
         r.hdr[0] = h.x; r.hdr[1] = h.y; r.hdr[2] = h.z; r.hdr[3] = h.w;
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
-        const int kb = MASKED ? k0 + 32 * sel : min(k0 + 32 * sel, K - 32);
+        const int kb = k0 + 32 * sel;
         r.hdr[0] = 0u;
-        if (hvalid && (!MASKED || kb < K))
-            r.hdr[0] = *reinterpret_cast<const uint16_t*>(hrow + (kb >> 5) * Format<TYPE>::kBytes);
+        if (hvalid && kb < K) r.hdr[0] = *reinterpret_cast<const uint16_t*>(hrow + (kb >> 5) * Format<TYPE>::kBytes);
     } else {
         r.hdr[0] = 0u;
     }
@@ -597,49 +667,68 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
     constexpr int KS = 64;  // dst columns per workgroup
     __shared__ __attribute__((aligned(16))) float part[NWAVES * 16 * KS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int K = args.K, N = args.N, T = args.T;
-    const int k0 = blockIdx.x * KS;
+    // Consecutive 64-column slabs read the same 128-byte lines of every W row
+    // (a Q4_K super-block spans four slabs): keep them on one XCD.
+    const int k0 = xcd_remap(blockIdx.x, gridDim.x) * KS;
     const int j = lane & 15, rq = lane >> 4;
 
     f32x4 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Decode a whole group, then issue its 16 MFMAs back to back (the fences
+    // keep the compiler from interleaving each MFMA with the decode of its
+    // own operand, which would stall on that dependency).
     auto contract = [&](const SkinnyRaw<TYPE>& r) {
         float wv[4][4];
         skinny_decode<TYPE>(r, k0, lane, wv);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
                 acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.g[s], wv[s][b], acc[b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Full 16-row groups: group g goes to wave g % NWAVES. The next group's
-    // loads are issued before the current group is contracted, alternating
-    // between two register buffers; past the wave's last group the fetch
-    // repeats a valid group and is not used.
+    // Full 16-row groups: group g goes to wave g % NWAVES. Loads run two
+    // groups ahead of the contraction, rotating through three register
+    // buffers; past the wave's last group the fetch repeats a valid group and
+    // is not used.
     const int nfull = FAST ? N / 16 : 0;
     int g = wave;
     if (g < nfull) {
-        SkinnyRaw<TYPE> ra, rb;
-        skinny_fetch<TYPE, false>(args, 16 * g, k0, lane, ra);
-        while (true) {
-            skinny_fetch<TYPE, false>(args, 16 * min(g + NWAVES, nfull - 1), k0, lane, rb);
-            contract(ra);
-            g += NWAVES;
-            if (g >= nfull) break;
-            skinny_fetch<TYPE, false>(args, 16 * min(g + NWAVES, nfull - 1), k0, lane, ra);
-            contract(rb);
-            g += NWAVES;
-            if (g >= nfull) break;
+        const int last = nfull - 1;
+        const int cnt = (nfull - wave + NWAVES - 1) / NWAVES;  // groups of this wave
+        const SkinnyOffsets off = skinny_offsets<TYPE>(args, k0, lane);
+        auto row0 = [&](int i) { return 16 * min(wave + i * NWAVES, last); };
+        SkinnyRaw<TYPE> r0, r1, r2;
+        skinny_fetch_fast<TYPE>(args, row0(0), off, r0);
+        skinny_fetch_fast<TYPE>(args, row0(1), off, r1);
+        // whole triples: no branch inside, so the loads of the next two groups
+        // stay in flight while a group is contracted
+        const int triples = cnt / 3;
+        for (int t3 = 0, i = 0; t3 < triples; ++t3, i += 3) {
+            skinny_fetch_fast<TYPE>(args, row0(i + 2), off, r2);
+            contract(r0);
+            skinny_fetch_fast<TYPE>(args, row0(i + 3), off, r0);
+            contract(r1);
+            skinny_fetch_fast<TYPE>(args, row0(i + 4), off, r1);
+            contract(r2);
         }
+        // 0, 1 or 2 groups left, already in r0 and r1
+        const int left = cnt - 3 * triples;
+        if (left >= 1) contract(r0);
+        if (left >= 2) contract(r1);
+        g = wave + cnt * NWAVES;
     }
     // Remaining (partial, or all groups of a shape off the fast path), masked.
     for (; 16 * g < N; g += NWAVES) {
         SkinnyRaw<TYPE> r;
-        skinny_fetch<TYPE, true>(args, 16 * g, k0, lane, r);
+        skinny_fetch_masked<TYPE>(args, 16 * g, k0, lane, r);
         contract(r);
     }
 
