@@ -4,7 +4,7 @@
 One step = the whole hot path on the two Q4_K shapes of a 4096-wide model
 with a 14336-wide MLP:
   large-T  W = 14336 x 4096 (N x K), G = 4096 x 14336, dst = 4096 x 4096
-           -> the tiled fused dequant + F32-MFMA kernel
+           -> the tiled fused dequant + F32-MFMA kernel (producer/consumer waves)
   skinny   W = 4096 x 14336, G = 16 x 4096, dst = 16 x 14336
            -> the one-pass small-T kernel
 Inputs are seeded synthetic data (workloads.py) resident in HBM before the
@@ -32,6 +32,7 @@ LARGE = "q4_k_n14336_k4096_t4096"
 SKINNY = "q4_k_n4096_k14336_t16"
 PROFILES = os.path.join(REPO, "profiles")
 KERNEL_SOURCES = ["quantized_weight_backward_amd/csrc/retro_kernels.h",
+                  "quantized_weight_backward_amd/csrc/retro_ws_kernel.h",
                   "quantized_weight_backward_amd/csrc/retro_decode.h",
                   "quantized_weight_backward_amd/csrc/retro_api.hip"]
 
@@ -59,21 +60,25 @@ def read_traffic(tag: str):
 
 
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d {out}/prof_trace -o run -- "
              "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
-    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_FETCH_SIZE -o run -- "
+    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/pmc_FETCH_SIZE -o run -- "
                   "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_WRITE_SIZE -o run -- "
+    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/pmc_WRITE_SIZE -o run -- "
                   "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-    "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_FETCH_SIZE -o run -- "
+    "mfma": "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES "
+            "GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS -f csv "
+            "-d {out}/pmc_mfma -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/pmc_copy_FETCH_SIZE -o run -- "
                        "python3 bench.py --copy-probe-mib 1024",
-    "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_WRITE_SIZE -o run -- "
+    "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/pmc_copy_WRITE_SIZE -o run -- "
                        "python3 bench.py --copy-probe-mib 1024",
 }
-KERNELS = {  # summary tag -> (kernel-name prefix in rocprofv3 output, workload)
-    f"tile_{LARGE}": ("void retro::out_prod_tile_kernel<12, 2, 4, 2, 2>", LARGE),
-    f"skinny_{SKINNY}": ("void retro::out_prod_skinny_kernel<12, 16, true>", SKINNY),
+KERNELS = {  # summary tag -> (kernel-name prefix in rocprofv3 output, workload, variant)
+    f"ws_{LARGE}": ("void retro::out_prod_ws_kernel<12, 2, 4>", LARGE, "ws_128x256"),
+    f"skinny_{SKINNY}": ("void retro::out_prod_skinny_kernel<12, 16, true>", SKINNY, "skinny"),
 }
+LARGE_TAG, SKINNY_TAG = f"ws_{LARGE}", f"skinny_{SKINNY}"
 
 
 def _mean_counter(path: str, prefix: str) -> tuple[float, int]:
@@ -83,9 +88,15 @@ def _mean_counter(path: str, prefix: str) -> tuple[float, int]:
     return (sum(vals) / len(vals) if vals else float("nan")), len(vals)
 
 
+def profile_command(name: str, run_dir: str) -> str:
+    """The rocprofv3 command of PROFILE_COMMANDS[name] writing under run_dir."""
+    return PROFILE_COMMANDS[name].format(out=os.path.relpath(run_dir, REPO).rstrip("/"))
+
+
 def summarize(run_dir: str) -> None:
-    """Write profiles/<tag>_trace.md and <tag>_traffic.md from rocprofv3 output
-    (the commands in PROFILE_COMMANDS, run from the repository root)."""
+    """Write profiles/<tag>_trace.md, <tag>_traffic.md and <tag>_counters.md
+    from rocprofv3 output under run_dir (the commands in PROFILE_COMMANDS with
+    {out} = run_dir, run from the repository root)."""
     import csv
 
     os.makedirs(PROFILES, exist_ok=True)
@@ -98,10 +109,10 @@ def summarize(run_dir: str) -> None:
     f_scale = copy_bytes / (f_copy * 1024)
     w_scale = copy_bytes / (w_copy * 1024)
     src = kernel_source_hash()
-    for tag, (prefix, workload) in KERNELS.items():
+    for tag, (prefix, workload, _) in KERNELS.items():
         row = next(r for r in stats if r["Name"].startswith(prefix))
         lines = [f"# {tag}: rocprofv3 kernel trace", "",
-                 f"Command (repository root): `{PROFILE_COMMANDS['trace']}`", "",
+                 f"Command (repository root): `{profile_command('trace', run_dir)}`", "",
                  f"Kernel: `{row['Name']}` (workload {workload})", "",
                  "| calls | average (us) | min (us) | max (us) | share of GPU time |",
                  "|---|---|---|---|---|",
@@ -114,7 +125,7 @@ def summarize(run_dir: str) -> None:
         hbm = fetch * 1024 * f_scale + write * 1024 * w_scale
         lines = [f"# {tag}: HBM traffic per launch (rocprofv3 counters)", "",
                  "Commands (repository root):", "",
-                 *[f"- `{PROFILE_COMMANDS[k]}`" for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE",
+                 *[f"- `{profile_command(k, run_dir)}`" for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE",
                                                            "copy_WRITE_SIZE")], "",
                  "Calibration: a 1 GiB device-to-device copy reads and writes 1073741824 bytes; the counters "
                  f"read FETCH_SIZE = {f_copy:.1f} KiB and WRITE_SIZE = {w_copy:.1f} KiB per copy launch, so "
@@ -125,7 +136,46 @@ def summarize(run_dir: str) -> None:
                  f"hbm_bytes_per_launch: {hbm:.6g}",
                  f"source_sha256: {src}", ""]
         open(os.path.join(PROFILES, f"{tag}_traffic.md"), "w").write("\n".join(lines))
+        mfma_csv = os.path.join(run_dir, "pmc_mfma", "run_counter_collection.csv")
+        if os.path.exists(mfma_csv):
+            write_counter_summary(tag, prefix, workload, mfma_csv, src, profile_command("mfma", run_dir))
         print(f"{tag}: avg {float(row['AverageNs']) / 1e3:.2f} us, traffic {hbm / 1e6:.1f} MB per launch")
+
+
+def write_counter_summary(tag: str, prefix: str, workload: str, path: str, src: str, command: str) -> None:
+    """profiles/<tag>_counters.md: per-launch means of the MFMA pass, with
+    the checks of the F32 MFMA work against 2*T*N*K (one MOP = 512 FLOPs)."""
+    import csv
+
+    import workloads as wl
+
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Kernel_Name"].startswith(prefix):
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = {k: sum(v) / len(v) for k, v in per.items()}
+    case = wl.WORKLOADS[workload]
+    flops = 2.0 * case["T"] * case["N"] * case["K"]
+    lines = [f"# {tag}: MFMA and LDS counters per launch (rocprofv3)", "",
+             f"Command (repository root): `{command}`", "",
+             "| counter | mean per launch |", "|---|---|",
+             *[f"| {k} | {v:.6g} |" for k, v in sorted(mean.items())], ""]
+    mops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_F32")
+    if mops:
+        lines += [f"F32 MFMA FLOPs counted: {mops * 512:.6g} (512 per MOP); 2*T*N*K = {flops:.6g}; "
+                  f"ratio {mops * 512 / flops:.4f} (above 1 by the tile padding of the last t and k tiles).", ""]
+    busy, cu = mean.get("SQ_VALU_MFMA_BUSY_CYCLES"), mean.get("SQ_BUSY_CU_CYCLES")
+    if busy and cu:
+        # MFMA busy cycles are summed over the 4 SIMDs of each CU, busy CU
+        # cycles over the CUs
+        lines += [f"MFMA busy fraction per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / (4 * SQ_BUSY_CU_CYCLES) = "
+                  f"{busy / (4 * cu):.4f}", ""]
+    valu = mean.get("SQ_INSTS_VALU")
+    if valu and cu:
+        lines += [f"VALU instructions per SIMD per busy cycle = SQ_INSTS_VALU / (4 * SQ_BUSY_CU_CYCLES) = "
+                  f"{valu / (4 * cu):.4f} (a wave64 VALU instruction occupies a SIMD for about 4 cycles)", ""]
+    lines += [f"source_sha256: {src}", ""]
+    open(os.path.join(PROFILES, f"{tag}_counters.md"), "w").write("\n".join(lines))
 
 
 def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
@@ -153,6 +203,11 @@ def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
                       f"{secs:.1f} s"}
 
 
+def kernel_family(variant: str) -> str:
+    return {"ws": "out_prod_ws_kernel", "tile": "out_prod_tile_kernel"}.get(variant.split("_")[0],
+                                                                         "out_prod_skinny_kernel")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,7 +226,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+              "(a sharded job would run this kernel on each GPU's own rows of G)", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -242,7 +297,7 @@ def main() -> int:
     avg_large = float(t_large.mean())
     avg_skinny = float(t_skinny.mean())
     achieved = fl_large / avg_large / 1e12
-    traffic = read_traffic(f"tile_{LARGE}")
+    traffic = read_traffic(LARGE_TAG) if q.VARIANT_NAMES[v_large] == KERNELS[LARGE_TAG][2] else None
     ms_per_step = wall / args.steps * 1e3
     value = (fl_large + fl_skinny) / (wall / args.steps) / 1e12
 
@@ -271,10 +326,10 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": f"out_prod_tile_kernel ({q.VARIANT_NAMES[v_large]})",
+                     "kernel": f"{kernel_family(q.VARIANT_NAMES[v_large])} ({q.VARIANT_NAMES[v_large]})",
                      "avg_launch_ms": round(avg_large * 1e3, 4), "min_launch_ms": round(float(t_large.min()) * 1e3, 4),
                      "flops_per_launch": fl_large},
-        "skinny": {"kernel": "out_prod_skinny_kernel", "traffic": read_traffic(f"skinny_{SKINNY}"),
+        "skinny": {"kernel": "out_prod_skinny_kernel", "traffic": read_traffic(SKINNY_TAG),
                    "avg_launch_us": round(avg_skinny * 1e6, 3),
                    "min_launch_us": round(float(t_skinny.min()) * 1e6, 3),
                    "tflops": round(skinny_tflops, 3), "weight_gbs": round(skinny_gbs, 1),

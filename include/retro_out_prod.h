@@ -135,6 +135,10 @@ const char *retro_strerror(int code);
  *                           of K per workgroup (256-column tiles need K tiles
  *                           that are whole Q4_K super-blocks; Q4_K takes only
  *                           those)
+ *   RETRO_VARIANT_WS_*      the same tiles computed by a workgroup whose
+ *                           waves are split into MFMA (consumer) and load/
+ *                           decode (producer) roles over double-buffered LDS;
+ *                           dense types need rows of a multiple of 16 bytes
  */
 enum {
     RETRO_VARIANT_AUTO = 0,
@@ -143,7 +147,11 @@ enum {
     RETRO_VARIANT_TILE_128x256 = 3,
     RETRO_VARIANT_TILE_64x128 = 4,
     RETRO_VARIANT_TILE_64x64 = 5,
-    RETRO_VARIANT_TILE_64x256 = 6
+    RETRO_VARIANT_TILE_64x256 = 6,
+    RETRO_VARIANT_WS_128x256 = 7,
+    RETRO_VARIANT_WS_64x256 = 8,
+    RETRO_VARIANT_WS_128x128 = 9,
+    RETRO_VARIANT_WS_64x128 = 10
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the
@@ -155,6 +163,10 @@ int retro_out_prod_variant(int variant, int type, const void *W, const float *G,
  * negative error code (as retro_out_prod_supported would refuse). Touches no
  * device. */
 int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T);
+
+/* 1 if retro_out_prod_variant(variant, type, ..., K, N, T) with valid buffers
+ * would run, 0 otherwise. Touches no device. */
+int retro_out_prod_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T);
 
 #ifdef __cplusplus
 }

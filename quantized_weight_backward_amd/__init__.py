@@ -38,16 +38,22 @@ VARIANT_TILE_128x256 = 3
 VARIANT_TILE_64x128 = 4
 VARIANT_TILE_64x64 = 5
 VARIANT_TILE_64x256 = 6
+VARIANT_WS_128x256 = 7
+VARIANT_WS_64x256 = 8
+VARIANT_WS_128x128 = 9
+VARIANT_WS_64x128 = 10
 VARIANT_NAMES = {
     VARIANT_SKINNY: "skinny", VARIANT_TILE_128x128: "tile_128x128", VARIANT_TILE_128x256: "tile_128x256",
     VARIANT_TILE_64x128: "tile_64x128", VARIANT_TILE_64x64: "tile_64x64", VARIANT_TILE_64x256: "tile_64x256",
+    VARIANT_WS_128x256: "ws_128x256", VARIANT_WS_64x256: "ws_64x256", VARIANT_WS_128x128: "ws_128x128",
+    VARIANT_WS_64x128: "ws_64x128",
 }
 
 LIB_PATH = _build.LIB_PATH
 
 # The exported symbols, as declared in include/retro_out_prod.h.
 EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_dequantize", "retro_out_prod_supported",
-           "retro_out_prod_choice", "retro_row_bytes", "retro_strerror")
+           "retro_out_prod_choice", "retro_out_prod_variant_applies", "retro_row_bytes", "retro_strerror")
 
 
 def _load() -> ctypes.CDLL:
@@ -67,6 +73,8 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod_supported.argtypes = [i32, i64, i64, i64]
     lib.retro_out_prod_choice.restype = i32
     lib.retro_out_prod_choice.argtypes = [i32, i64, i64, i64]
+    lib.retro_out_prod_variant_applies.restype = i32
+    lib.retro_out_prod_variant_applies.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_row_bytes.restype = i64
     lib.retro_row_bytes.argtypes = [i32, i64]
     lib.retro_strerror.restype = ctypes.c_char_p
@@ -97,6 +105,10 @@ def supported(wtype: int, K: int, N: int, T: int) -> bool:
 
 def choice(wtype: int, K: int, N: int, T: int) -> int:
     return int(lib.retro_out_prod_choice(int(wtype), int(K), int(N), int(T)))
+
+
+def variant_applies(variant: int, wtype: int, K: int, N: int, T: int) -> bool:
+    return lib.retro_out_prod_variant_applies(int(variant), int(wtype), int(K), int(N), int(T)) == 1
 
 
 def _check(code: int) -> None:

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include "retro_kernels.h"
+#include "retro_ws_kernel.h"
 #include "retro_out_prod.h"
 
 namespace {
@@ -74,15 +75,32 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct TileVariant {
     int id, bt, bk;
     double penalty;  // relative cost per output of the smaller tiles
+    bool ws;         // producer/consumer kernel (else the single-role tile kernel)
 };
 
 constexpr TileVariant kTiles[] = {
-    {RETRO_VARIANT_TILE_128x256, 128, 256, 1.00},
-    {RETRO_VARIANT_TILE_128x128, 128, 128, 1.00},
-    {RETRO_VARIANT_TILE_64x256, 64, 256, 1.05},
-    {RETRO_VARIANT_TILE_64x128, 64, 128, 1.08},
-    {RETRO_VARIANT_TILE_64x64, 64, 64, 1.20},
+    {RETRO_VARIANT_TILE_128x256, 128, 256, 1.00, false},
+    {RETRO_VARIANT_TILE_128x128, 128, 128, 1.00, false},
+    {RETRO_VARIANT_TILE_64x256, 64, 256, 1.05, false},
+    {RETRO_VARIANT_TILE_64x128, 64, 128, 1.08, false},
+    {RETRO_VARIANT_TILE_64x64, 64, 64, 1.20, false},
+    {RETRO_VARIANT_WS_128x256, 128, 256, 1.00, true},
+    {RETRO_VARIANT_WS_64x256, 64, 256, 1.04, true},
+    {RETRO_VARIANT_WS_128x128, 128, 128, 1.00, true},
+    {RETRO_VARIANT_WS_64x128, 64, 128, 1.02, true},
 };
+
+bool is_dense(int type) { return type == RETRO_F32 || type == RETRO_F16 || type == RETRO_BF16; }
+
+// Which kernel family runs a type, from measurements on MI355X: the
+// producer/consumer kernel wins where decoding is cheap per 4-byte write
+// (dense rows) or per 16-byte code unit (Q4_K); for Q8_0 and Q4_0, whose
+// 2-byte aligned blocks are read in halfwords, spreading the decode over all
+// waves of the single-role kernel is faster. The other family stays as the
+// fallback for shapes the preferred one does not take.
+bool prefers_ws(int type) { return is_dense(type) || type == RETRO_Q4_K; }
+constexpr double kOtherFamily = 1.3;
+
 
 const TileVariant* find_tile(int variant) {
     for (const auto& v : kTiles)
@@ -90,9 +108,15 @@ const TileVariant* find_tile(int variant) {
     return nullptr;
 }
 
-bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t T) {
+// The tiled kernel addresses a tile's BT rows of G and a chunk's 32 rows of
+// W with 32-bit offsets from per-chunk buffer bases.
+bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t T) {
     if (type == RETRO_Q4_K && v.bk % 256) return false;
-    return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit;
+    // the producer/consumer kernel loads dense rows in 16-byte units
+    if (v.ws && is_dense(type) && row_bytes_of(type, K) % 16)
+        return false;
+    return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit && int64_t(v.bt) * N * 4 < (int64_t(1) << 31) &&
+           33 * row_bytes_of(type, K) < (int64_t(1) << 31);
 }
 
 // The skinny kernel addresses one 16-row group of W, and the 16 rows of G
@@ -103,15 +127,16 @@ bool skinny_applies(int type, int64_t K, int64_t N, int64_t T) {
 }
 
 // Pick the tile that minimises (tiles per CU, rounded up) x tile area x
-// penalty: the rounding is the wave quantisation over 256 CUs.
+// relative cost: the rounding is the wave quantisation over 256 CUs.
 int choose(int type, int64_t K, int64_t N, int64_t T) {
     if (skinny_applies(type, K, N, T)) return RETRO_VARIANT_SKINNY;
     int best = -1;
     double best_cost = 0;
     for (const auto& v : kTiles) {
-        if (!tile_applies(v, type, K, T)) continue;
+        if (!tile_applies(v, type, K, N, T)) continue;
+        const double weight = v.penalty * (v.ws == prefers_ws(type) ? 1.0 : kOtherFamily);
         const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk);
-        const double cost = double(cdiv(nt, kNumCUs)) * v.bt * v.bk * v.penalty;
+        const double cost = double(cdiv(nt, kNumCUs)) * v.bt * v.bk * weight;
         if (best < 0 || cost < best_cost) {
             best = v.id;
             best_cost = cost;
@@ -151,6 +176,27 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     return launch_status();
 }
 
+template <int TYPE, int WA, int WB>
+int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+    using S = WsShape<TYPE, WA, WB>;
+    TileArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.G = G;
+    a.dst = dst;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.wvec = 16;
+    a.gvec = (N % 4 == 0) ? 1 : 0;
+    a.tiles_t = int(cdiv(T, S::BT));
+    a.tiles_k = int(cdiv(K, S::BK));
+    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
+    clear_last_error();
+    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    return launch_status();
+}
+
 template <int TYPE>
 int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
     constexpr int kWaves = RETRO_SKINNY_WAVES;
@@ -180,6 +226,8 @@ int launch_variant(int variant, const void* W, const float* G, float* dst, int64
         case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, st);
         case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, st);
         case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4>(W, G, dst, K, N, T, st);
         default: break;
     }
     if constexpr (TYPE != kQ4_K) {
@@ -187,6 +235,8 @@ int launch_variant(int variant, const void* W, const float* G, float* dst, int64
             case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, st);
             case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, st);
             case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2>(W, G, dst, K, N, T, st);
             default: break;
         }
     }
@@ -199,6 +249,14 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
     if (na <= 0 || nb <= 0) return false;
     const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
     return pa < pb + uint64_t(nb) && pb < pa + uint64_t(na);
+}
+
+// Whether a forced variant takes this type and shape (shape already checked).
+bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
+    if (variant == RETRO_VARIANT_AUTO) return choose(type, K, N, T) > 0;
+    if (variant == RETRO_VARIANT_SKINNY) return skinny_applies(type, K, N, T);
+    const TileVariant* tv = find_tile(variant);
+    return tv && tile_applies(*tv, type, K, N, T);
 }
 
 int out_prod_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
@@ -219,7 +277,7 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         if (!skinny_applies(type, K, N, T)) return RETRO_E_VARIANT;
     } else {
         const TileVariant* tv = find_tile(variant);
-        if (!tv || !tile_applies(*tv, type, K, T)) return RETRO_E_VARIANT;
+        if (!tv || !tile_applies(*tv, type, K, N, T)) return RETRO_E_VARIANT;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (type) {
@@ -288,6 +346,12 @@ int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T) {
     if (check_shape(type, K, N, T) != RETRO_OK) return 0;
     if (T == 0 || K == 0) return 1;
     return choose(type, K, N, T) > 0 ? 1 : 0;
+}
+
+int retro_out_prod_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
+    if (check_shape(type, K, N, T) != RETRO_OK) return 0;
+    if (T == 0 || K == 0) return 1;
+    return variant_applies(variant, type, K, N, T) ? 1 : 0;
 }
 
 int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T) {

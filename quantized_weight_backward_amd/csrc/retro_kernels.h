@@ -25,42 +25,17 @@ namespace retro {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Staging helpers
 // ---------------------------------------------------------------------------
 
-// Load the 16 bytes at p, of which only the first `avail` are inside the
-// tile (avail may be <= 0); the rest read as zero. wvec (16, 8, 4 or 2) is the
-// widest load that p, the row pitch and every tile boundary are aligned to,
-// and avail is always a multiple of it.
-__device__ __forceinline__ uint4 load16_masked(const uint8_t* p, int avail, int wvec) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (avail <= 0) return v;
-    if (wvec == 16) return avail >= 16 ? *reinterpret_cast<const uint4*>(p) : v;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (wvec == 8) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            if (8 * q < avail) {
-                const uint2 x = *reinterpret_cast<const uint2*>(p + 8 * q);
-                w[2 * q] = x.x;
-                w[2 * q + 1] = x.y;
-            }
-    } else if (wvec == 4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (4 * q < avail) w[q] = *reinterpret_cast<const uint32_t*>(p + 4 * q);
-    } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (2 * q < avail) w[q >> 1] |= uint32_t(*reinterpret_cast<const uint16_t*>(p + 2 * q)) << (16 * (q & 1));
-    }
-    v.x = w[0];
-    v.y = w[1];
-    v.z = w[2];
-    v.w = w[3];
-    return v;
+// Buffer resource over [base, base + bytes): gfx9 descriptor, raw 32-bit
+// access, no stride. Loads at or past `bytes` return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Four code bytes starting at a 2-byte aligned LDS address.
@@ -109,6 +84,21 @@ struct TileArgs {
     int tiles_t, tiles_k;
 };
 
+// Column swizzle of a decoded W tile in LDS: XOR column bits 2-4 with
+// higher bits, chosen per format so that the decode stores of one wave (8
+// lanes per LDS cycle, each writing a float4 at a format-specific stride) hit
+// distinct banks. Bits 0-1 are untouched (float4 stores stay contiguous) and
+// bits 5 and up are untouched (the 32 consecutive columns an MFMA operand
+// read covers stay inside their 32-word group, so those reads stay
+// conflict-free).
+template <int TYPE>
+__device__ __forceinline__ int lds_swizzle(int col) {
+    if constexpr (TYPE == kQ4_K) return col ^ (((col >> 6) & 3) << 2);
+    if constexpr (TYPE == kQ4_0) return col ^ (((col >> 5) & 7) << 2);
+    if constexpr (TYPE == kQ8_0) return col ^ (((col >> 5) & 3) << 2);
+    return col;
+}
+
 template <int TYPE, int WA, int WB, int WGT, int WGK>
 struct TileShape {
     using F = Format<TYPE>;
@@ -131,15 +121,19 @@ struct TileShape {
     static constexpr int UPR = (SPAN + 15) / 16;
     static constexpr int RAWP = UPR * 16 + 16;  // raw row stride in LDS (bytes)
     static constexpr int WUNITS = BN * UPR;
+    // Packed formats are staged through LDS as raw bytes (their blocks need
+    // not be 16-byte aligned) and decoded from there.
+    static constexpr bool kStaged = !kDense;
     static constexpr int WSLOTS = (WUNITS + kThreads - 1) / kThreads;
     static constexpr int GSLOTS = BT * BN / 4 / kThreads;
     static_assert(GSLOTS * kThreads * 4 == BT * BN, "G chunk splits evenly");
     static constexpr int GE = F::kGroup;
     static constexpr int GPR = BK / GE;  // decode groups per row
     static constexpr int DPASS = (BN * GPR + kThreads - 1) / kThreads;
+    static __device__ __forceinline__ int swz(int col) { return lds_swizzle<TYPE>(col); }
     static constexpr int LDS_G = BT * GP * 4;
     static constexpr int LDS_B = BN * BP * 4;
-    static constexpr int LDS_RAW = kDense ? 0 : BN * RAWP;
+    static constexpr int LDS_RAW = kStaged ? BN * RAWP : 0;
 };
 
 template <int TYPE, int WA, int WB, int WGT, int WGK>
@@ -150,51 +144,97 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 
     __shared__ __attribute__((aligned(16))) float Gs[BT * GP];
     __shared__ __attribute__((aligned(16))) float Bs[BN * BP];
-    __shared__ __attribute__((aligned(16))) uint8_t Raw[S::kDense ? 16 : S::LDS_RAW];
+    __shared__ __attribute__((aligned(16))) uint8_t Raw[S::kStaged ? S::LDS_RAW : 16];
 
     const int tid = threadIdx.x;
     int tt, tk;
     tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, tt, tk);
     const int t0 = tt * BT, k0 = tk * BK;
     const int K = args.K, N = args.N, T = args.T;
-    const int kend = min(k0 + BK, K);
-    // Packed bytes of this tile's k range inside one W row.
+    // Byte offset of this tile's k range inside one W row.
     const long long kb0 = (long long)(k0 / F::kBlock) * F::kBytes;
-    const int span = (kend - k0) / F::kBlock * F::kBytes;
-    const uint8_t* Wt = args.W + kb0;
 
     float4 greg[S::GSLOTS];
     uint4 wreg[S::WSLOTS];
 
-    // Global -> registers for the chunk of W rows [n0, n0 + 32).
+    // Byte offsets of this thread's staging loads from the chunk's buffer
+    // bases (the same for every chunk and tile): G slot s covers tile row
+    // r = id / 8, columns 4*(id % 8) .. +3 of the chunk; W slot s covers
+    // 16-byte unit u of tile row r.
+    uint32_t goff[S::GSLOTS], woff[S::WSLOTS];
+#pragma unroll
+    for (int s = 0; s < S::GSLOTS; ++s) {
+        const int id = tid + S::kThreads * s;
+        goff[s] = uint32_t(((id >> 3) * N + 4 * (id & 7)) * 4);
+    }
+#pragma unroll
+    for (int s = 0; s < S::WSLOTS; ++s) {
+        const int id = min(tid + S::kThreads * s, S::WUNITS - 1);
+        const int r = id / S::UPR, u = id - r * S::UPR;
+        woff[s] = uint32_t(r * args.pitch + 16 * u);
+    }
+    const long long g_end = (long long)T * N;         // elements of G
+    const long long w_end = (long long)N * args.pitch;  // bytes of W
+
+    // Global -> registers for the chunk of W rows [n0, n0 + 32). Both loads go
+    // through buffer descriptors based at the chunk's first element, so rows
+    // past the end of G (t >= T) and of W (n >= N) read as zero in hardware.
+    // Bytes of a row past this tile's K range belong to the next row: they
+    // only feed dst columns >= K, which are never stored. G columns >= N
+    // (possible only in the last chunk) are zeroed explicitly.
     auto load_chunk = [&](int n0) {
+        n0 = __builtin_amdgcn_readfirstlane(n0);
+        const long long gb = (long long)t0 * N + n0;
+        const __amdgpu_buffer_rsrc_t gr =
+            buffer_rsrc(args.G + gb, uint32_t(min(4 * (g_end - gb), (long long)0x7FFFFFFF)));
 #pragma unroll
         for (int s = 0; s < S::GSLOTS; ++s) {
-            const int id = tid + S::kThreads * s;
-            const int r = id >> 3, j = id & 7;
-            const int t = t0 + r, n = n0 + 4 * j;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < T) {
-                const float* gp = args.G + (long long)t * N + n;
-                if (args.gvec) {
-                    if (n < N) v = *reinterpret_cast<const float4*>(gp);
-                } else {
-                    if (n < N) v.x = gp[0];
-                    if (n + 1 < N) v.y = gp[1];
-                    if (n + 2 < N) v.z = gp[2];
-                    if (n + 3 < N) v.w = gp[3];
-                }
+            if (args.gvec) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, goff[s], 0, 0);
+                greg[s] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                      __uint_as_float(v.w));
+            } else {
+                greg[s].x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s], 0, 0));
+                greg[s].y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 4, 0, 0));
+                greg[s].z = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 8, 0, 0));
+                greg[s].w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 12, 0, 0));
             }
-            greg[s] = v;
         }
+        if (n0 + BN > N) {
+#pragma unroll
+            for (int s = 0; s < S::GSLOTS; ++s) {
+                const int n = n0 + 4 * ((tid + S::kThreads * s) & 7);
+                if (n >= N) greg[s].x = 0.f;
+                if (n + 1 >= N) greg[s].y = 0.f;
+                if (n + 2 >= N) greg[s].z = 0.f;
+                if (n + 3 >= N) greg[s].w = 0.f;
+            }
+        }
+        const long long wb = (long long)n0 * args.pitch + kb0;
+        const __amdgpu_buffer_rsrc_t wr =
+            buffer_rsrc(args.W + wb, uint32_t(min(w_end - wb, (long long)0x7FFFFFFF)));
 #pragma unroll
         for (int s = 0; s < S::WSLOTS; ++s) {
-            const int id = tid + S::kThreads * s;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (S::WUNITS % S::kThreads == 0 || id < S::WUNITS) {
-                const int r = id / S::UPR, u = id - r * S::UPR;
-                const int n = n0 + r;
-                if (n < N) v = load16_masked(Wt + (long long)n * args.pitch + 16 * u, span - 16 * u, args.wvec);
+            if (S::WUNITS % S::kThreads != 0 && tid + S::kThreads * s >= S::WUNITS) continue;
+            const uint32_t o = woff[s];
+            uint4 v;
+            if (args.wvec == 16) {
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 0);
+                v = make_uint4(x.x, x.y, x.z, x.w);
+            } else if (args.wvec == 8) {
+                const u32x2 x0 = __builtin_amdgcn_raw_buffer_load_b64(wr, o, 0, 0);
+                const u32x2 x1 = __builtin_amdgcn_raw_buffer_load_b64(wr, o + 8, 0, 0);
+                v = make_uint4(x0.x, x0.y, x1.x, x1.y);
+            } else if (args.wvec == 4) {
+                v = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(wr, o, 0, 0),
+                               __builtin_amdgcn_raw_buffer_load_b32(wr, o + 4, 0, 0),
+                               __builtin_amdgcn_raw_buffer_load_b32(wr, o + 8, 0, 0),
+                               __builtin_amdgcn_raw_buffer_load_b32(wr, o + 12, 0, 0));
+            } else {
+                uint32_t h[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) h[q] = __builtin_amdgcn_raw_buffer_load_b16(wr, o + 2 * q, 0, 0);
+                v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
             }
             wreg[s] = v;
         }
@@ -222,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                 if constexpr (S::kDense) {
                     float* brow = Bs + r * BP;
                     if constexpr (TYPE == kF32) {
-                        *reinterpret_cast<float4*>(brow + 4 * u) =
+                        *reinterpret_cast<float4*>(brow + S::swz(4 * u)) =
                             make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                                         __uint_as_float(v.w));
                     } else {
@@ -238,8 +278,8 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                             bf16x2(v.z, e[4], e[5]);
                             bf16x2(v.w, e[6], e[7]);
                         }
-                        *reinterpret_cast<float4*>(brow + 8 * u) = make_float4(e[0], e[1], e[2], e[3]);
-                        *reinterpret_cast<float4*>(brow + 8 * u + 4) = make_float4(e[4], e[5], e[6], e[7]);
+                        *reinterpret_cast<float4*>(brow + S::swz(8 * u)) = make_float4(e[0], e[1], e[2], e[3]);
+                        *reinterpret_cast<float4*>(brow + S::swz(8 * u + 4)) = make_float4(e[4], e[5], e[6], e[7]);
                     }
                 } else {
                     *reinterpret_cast<uint4*>(Raw + r * S::RAWP + 16 * u) = v;
@@ -248,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
         }
     };
 
-    // Raw packed bytes in LDS -> decoded floats in Bs (packed formats only).
+    // Raw packed bytes in LDS -> decoded floats in Bs (Q8_0, Q4_0).
     auto decode_chunk = [&]() {
 #pragma unroll
         for (int p = 0; p < S::DPASS; ++p) {
@@ -265,40 +305,40 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                     q4_k_coeffs(hd.x, hd.y, hd.z, hd.w, 2 * c, a0, b0);
                     q4_k_coeffs(hd.x, hd.y, hd.z, hd.w, 2 * c + 1, a1, b1);
                     const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-                    float* lo = brow + 256 * sb + 64 * c + 16 * h;
-                    float* hi = lo + 32;
+                    const int lo = 256 * sb + 64 * c + 16 * h, hi = lo + 32;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float e[4];
                         q4_k_x4(w[i], false, a0, b0, e);
-                        *reinterpret_cast<float4*>(lo + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                        *reinterpret_cast<float4*>(brow + S::swz(lo + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
                         q4_k_x4(w[i], true, a1, b1, e);
-                        *reinterpret_cast<float4*>(hi + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                        *reinterpret_cast<float4*>(brow + S::swz(hi + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
                     }
                 } else if constexpr (TYPE == kQ4_0) {
                     const uint8_t* blk = raw + 18 * g;
                     const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
-                    float* lo = brow + 32 * g;
+                    const int lo = 32 * g;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t w = lds_word_a2(blk + 2 + 4 * i);
                         float e[4];
                         q4_0_x4(w, false, d, e);
-                        *reinterpret_cast<float4*>(lo + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                        *reinterpret_cast<float4*>(brow + S::swz(lo + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
                         q4_0_x4(w, true, d, e);
-                        *reinterpret_cast<float4*>(lo + 16 + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                        *reinterpret_cast<float4*>(brow + S::swz(lo + 16 + 4 * i)) =
+                            make_float4(e[0], e[1], e[2], e[3]);
                     }
                 } else if constexpr (TYPE == kQ8_0) {
                     const int b = g >> 1, h = g & 1;
                     const uint8_t* blk = raw + 34 * b;
                     const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
-                    float* out = brow + 32 * b + 16 * h;
+                    const int out = 32 * b + 16 * h;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t w = lds_word_a2(blk + 2 + 16 * h + 4 * i);
                         float e[4];
                         q8_0_x4(w, d, e);
-                        *reinterpret_cast<float4*>(out + 4 * i) = make_float4(e[0], e[1], e[2], e[3]);
+                        *reinterpret_cast<float4*>(brow + S::swz(out + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
                     }
                 }
             }
@@ -323,14 +363,14 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
         store_chunk();
         __syncthreads();
         if (c + 1 < nchunks) load_chunk((c + 1) * BN);
-        if constexpr (!S::kDense) {
+        if constexpr (S::kStaged) {
             decode_chunk();
             __syncthreads();
         }
         // MFMA step s (0..15) contracts W rows n0 + 2s + h (lane half h):
         // A[i][h] = G[t_i][n0 + 2s + h], B[h][j] = W[n0 + 2s + h][k_j].
         const float* ga = Gs + (wt * 32 * WA + l32) * GP + 16 * h;
-        const float* bb = Bs + h * BP + wk * 32 * WB + l32;
+        const float* bb = Bs + h * BP;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             f32x4 av[WA];
@@ -340,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int b = 0; b < WB; ++b) bv[r][b] = bb[(2 * (4 * q + r)) * BP + 32 * b];
+                for (int b = 0; b < WB; ++b) bv[r][b] = bb[(2 * (4 * q + r)) * BP + S::swz(wk * 32 * WB + 32 * b + l32)];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -494,17 +534,9 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
     return o;
 }
 
-// Buffer resource over [base, base + bytes): gfx9 descriptor, raw 32-bit
-// access, no stride. Loads at or past `bytes` return zero instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 template <int TYPE>
 __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, const SkinnyOffsets& o,
                                                   SkinnyRaw<TYPE>& r) {
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     // n0 is the same in every lane; readfirstlane makes that visible to the
     // compiler, so the two descriptors (this group's 16 W rows; the G columns
     // from n0 on) are built in scalar registers and every load is a fixed

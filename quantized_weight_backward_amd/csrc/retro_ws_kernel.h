@@ -1,0 +1,380 @@
+// retro_ws_kernel.h - OUT_PROD tile kernel with producer and consumer waves.
+//
+// Same contraction and tile mapping as out_prod_tile_kernel, organised so
+// that the matrix pipe never waits on staging:
+//   * 8 waves per workgroup. Waves 0-3 (consumers, 2 x 2 over the tile) only
+//     read operands from LDS and issue v_mfma_f32_32x32x2_f32. Waves 4-7
+//     (producers) load G and packed W with buffer loads, decode W in
+//     registers and write both into LDS.
+//   * G and decoded W are double-buffered in LDS: while the consumers contract
+//     chunk c from buffer c % 2, the producers fill buffer (c + 1) % 2 with
+//     chunk c + 1, whose loads they issued one chunk earlier. One workgroup
+//     barrier per 32-row chunk.
+//   * Both operands are read as 16-byte vectors. G is kept t-major (a row of
+//     32 reduction values per t) and decoded W k-major (a column of 32
+//     reduction values per k), and MFMA step r of phase q contracts rows
+//     8q + 4h + r in lane half h, so each lane's four steps of a phase sit in
+//     one float4 of G and one float4 of W.
+// On gfx950 VALU work and F32 MFMA work take turns on a SIMD (they do not
+// overlap), so a SIMD holding one consumer and one producer wave spends its
+// time on MFMA plus decode and little else.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "retro_kernels.h"
+
+namespace retro {
+
+template <int TYPE, int WA, int WB>
+struct WsShape {
+    using F = Format<TYPE>;
+    static constexpr bool kDense = F::kBlock == 1;
+    static constexpr int kPThreads = 256;          // producer threads (waves 4-7)
+    static constexpr int kThreads = 2 * kPThreads;  // + 4 consumer waves
+    static constexpr int BT = 64 * WA;              // consumer waves 2 x 2, each (32*WA) x (32*WB)
+    static constexpr int BK = 64 * WB;
+    static constexpr int BN = 32;
+    static_assert(BK == 128 || BK == 256, "K tile of 128 or 256 columns");
+    static_assert(TYPE != kQ4_K || BK == 256, "Q4_K tiles hold whole super-blocks");
+    static constexpr int GP = BN + 4;  // floats per t row of G in LDS
+    static constexpr int WP = BN + 4;  // floats per k column of W in LDS
+    static constexpr int G_FLOATS = BT * GP;
+    static constexpr int W_FLOATS = BK * WP;
+    static constexpr int BUF_FLOATS = G_FLOATS + W_FLOATS;
+    static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // float4 of G per producer thread
+    static_assert(GSLOTS * kPThreads * 4 == BT * BN, "G chunk splits evenly");
+    // Dense W: 16-byte units (4 F32 or 8 F16/BF16 along k of one row).
+    static constexpr int EPU = 16 / F::kBytes;
+    static constexpr int DUNITS = kDense ? BN * BK / EPU / kPThreads : 0;
+    // Q8_0 / Q4_0: a 32-element block is split over QSPLIT producer threads,
+    // each holding CB code bytes of it.
+    static constexpr int QSPLIT = (TYPE == kQ8_0 || TYPE == kQ4_0) ? kPThreads / (BN * BK / 32) : 1;
+    static constexpr int CB = TYPE == kQ8_0 ? 32 / QSPLIT : 16 / QSPLIT;
+    // words of W each producer thread holds between load and decode
+    static constexpr int WWORDS = kDense ? 4 * DUNITS : (TYPE == kQ4_K) ? 8 : CB / 4 + 1;
+};
+
+// Float index of W element (row n, column k) of a chunk inside the W part of
+// an LDS buffer: column k holds its 32 rows with the 4-row groups permuted
+// by bits 4-6 of k, which spreads the producers' 4-byte writes over banks.
+// The permutation keeps every aligned 4-row group together and in order, so
+// a consumer still reads 4 rows as one float4.
+template <int WP>
+__device__ __forceinline__ int ws_w_index(int k, int n) {
+    return k * WP + (n ^ (((k >> 4) & 7) << 2));
+}
+
+template <int TYPE, int WA, int WB>
+__global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
+    using S = WsShape<TYPE, WA, WB>;
+    using F = Format<TYPE>;
+    constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, WP = S::WP;
+
+    __shared__ __attribute__((aligned(16))) float lds[2 * S::BUF_FLOATS];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tt, tk;
+    tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, tt, tk);
+    const int t0 = tt * BT, k0 = tk * BK;
+    const int K = args.K, N = args.N, T = args.T;
+    const int nchunks = (N + BN - 1) / BN;
+
+    // The two roles run separate loops with the same barrier sequence (one
+    // after the prologue, one per chunk): the role test is uniform per wave,
+    // and keeping the loops apart keeps the consumers' accumulators and the
+    // producers' staging registers from being allocated side by side.
+    if (wave >= 4) {
+        // ---------------- producer ----------------
+        const int p = tid - S::kPThreads;
+        const long long kb0 = (long long)(k0 / F::kBlock) * F::kBytes;
+        float4 greg[S::GSLOTS];
+        uint32_t wreg[S::WWORDS];
+        // Byte offsets of this thread's G loads from the chunk's base (the
+        // same for every chunk): slot s is t row id / 8, columns
+        // 4 (id % 8) .. + 3.
+        uint32_t goff[S::GSLOTS];
+#pragma unroll
+        for (int s = 0; s < S::GSLOTS; ++s) {
+            const int id = p + S::kPThreads * s;
+            goff[s] = uint32_t(((id >> 3) * N + 4 * (id & 7)) * 4);
+        }
+        // W: byte offset of this thread's block in the chunk, and the LDS
+        // float index of the first element it writes in each 16-column group.
+        uint32_t woff = 0;
+        int wlds[S::kDense ? S::DUNITS : 2];
+        if constexpr (S::kDense) {
+            constexpr int UPR = BK / S::EPU;  // units per row
+#pragma unroll
+            for (int s = 0; s < S::DUNITS; ++s) {
+                const int id = p + S::kPThreads * s, r = id / UPR, u = id - r * UPR;
+                wlds[s] = ws_w_index<WP>(S::EPU * u, r);
+            }
+        } else if constexpr (TYPE == kQ4_K) {
+            // code unit p % 8 (16 bytes) of row p / 8: low nibbles are columns
+            // 64c + 16h + 0..15, high nibbles 64c + 32 + 16h + 0..15
+            const int r = p >> 3, u = p & 7, c = u >> 1, h = u & 1;
+            woff = uint32_t(r * args.pitch);
+            wlds[0] = ws_w_index<WP>(64 * c + 16 * h, r);
+            wlds[1] = ws_w_index<WP>(64 * c + 32 + 16 * h, r);
+        } else {
+            // part s of block b of row r: code bytes CB s .. CB s + CB - 1
+            const int id = p / S::QSPLIT, s = p - id * S::QSPLIT;
+            const int r = id / (BK / 32), b = id - r * (BK / 32);
+            woff = uint32_t(r * args.pitch + b * F::kBytes);
+            if constexpr (TYPE == kQ8_0) {
+                // columns 32b + CB s + 0 .. CB - 1 (one or two 16-column groups)
+                wlds[0] = ws_w_index<WP>(32 * b + S::CB * s, r);
+                wlds[1] = ws_w_index<WP>(32 * b + S::CB * s + 16, r);
+            } else {
+                // byte j: low nibble is column 32b + j, high nibble 32b + 16 + j
+                wlds[0] = ws_w_index<WP>(32 * b, r) + S::CB * s * WP;
+                wlds[1] = ws_w_index<WP>(32 * b + 16, r) + S::CB * s * WP;
+            }
+        }
+        const long long g_end = (long long)T * N;
+        const long long w_end = (long long)N * args.pitch;
+
+        // Loads of chunk rows [n0, n0 + 32) into registers. Rows at or past N
+        // lie beyond the W buffer's range and read as zero; their G columns
+        // are zeroed below. Columns past K in the last k tile read bytes of
+        // the next row (or zero) and only reach outputs that are not stored.
+        auto load_chunk = [&](int n0) {
+            n0 = __builtin_amdgcn_readfirstlane(n0);
+            const long long gb = (long long)t0 * N + n0;
+            const __amdgpu_buffer_rsrc_t gr =
+                buffer_rsrc(args.G + gb, uint32_t(min(4 * (g_end - gb), (long long)0x7FFFFFFF)));
+#pragma unroll
+            for (int s = 0; s < S::GSLOTS; ++s) {
+                if (args.gvec) {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, goff[s], 0, 0);
+                    greg[s] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                          __uint_as_float(v.w));
+                } else {
+                    greg[s].x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s], 0, 0));
+                    greg[s].y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 4, 0, 0));
+                    greg[s].z = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 8, 0, 0));
+                    greg[s].w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 12, 0, 0));
+                }
+            }
+            if (n0 + BN > N) {
+#pragma unroll
+                for (int s = 0; s < S::GSLOTS; ++s) {
+                    const int n = n0 + 4 * ((p + S::kPThreads * s) & 7);
+                    if (n >= N) greg[s].x = 0.f;
+                    if (n + 1 >= N) greg[s].y = 0.f;
+                    if (n + 2 >= N) greg[s].z = 0.f;
+                    if (n + 3 >= N) greg[s].w = 0.f;
+                }
+            }
+            const long long wb = (long long)n0 * args.pitch + kb0;
+            const __amdgpu_buffer_rsrc_t wr =
+                buffer_rsrc(args.W + wb, uint32_t(min(w_end - wb, (long long)0x7FFFFFFF)));
+            if constexpr (S::kDense) {
+                constexpr int UPR = BK / S::EPU;
+#pragma unroll
+                for (int s = 0; s < S::DUNITS; ++s) {
+                    const int id = p + S::kPThreads * s, r = id / UPR, u = id - r * UPR;
+                    const u32x4 v =
+                        __builtin_amdgcn_raw_buffer_load_b128(wr, uint32_t(r * args.pitch + 16 * u), 0, 0);
+                    wreg[4 * s] = v.x;
+                    wreg[4 * s + 1] = v.y;
+                    wreg[4 * s + 2] = v.z;
+                    wreg[4 * s + 3] = v.w;
+                }
+            } else if constexpr (TYPE == kQ4_K) {
+                const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 16 + 16 * (p & 7), 0, 0);
+                const u32x4 hd = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
+                wreg[0] = cw.x; wreg[1] = cw.y; wreg[2] = cw.z; wreg[3] = cw.w;
+                wreg[4] = hd.x; wreg[5] = hd.y; wreg[6] = hd.z; wreg[7] = hd.w;
+            } else {  // Q8_0, Q4_0: 2-byte aligned blocks, read in halfwords
+                constexpr int CW = S::CB / 4;
+                const uint32_t codes = woff + 2 + S::CB * (p % S::QSPLIT);
+                wreg[CW] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff, 0, 0);
+#pragma unroll
+                for (int w = 0; w < CW; ++w) {
+                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, codes + 4 * w, 0, 0);
+                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, codes + 4 * w + 2, 0, 0);
+                    wreg[w] = lo | (hi << 16);
+                }
+            }
+        };
+
+        // Registers -> LDS buffer `buf`: G rows as loaded, W decoded to F32
+        // into its k-major columns (element j of a 16-column group is WP
+        // floats after element j - 1).
+        auto store_chunk = [&](int buf) {
+            float* gs = lds + buf * S::BUF_FLOATS;
+            float* ws = gs + S::G_FLOATS;
+#pragma unroll
+            for (int s = 0; s < S::GSLOTS; ++s) {
+                const int id = p + S::kPThreads * s;
+                *reinterpret_cast<float4*>(gs + (id >> 3) * GP + 4 * (id & 7)) = greg[s];
+            }
+            if constexpr (S::kDense) {
+#pragma unroll
+                for (int s = 0; s < S::DUNITS; ++s) {
+                    float* col = ws + wlds[s];
+                    if constexpr (TYPE == kF32) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) col[e * WP] = __uint_as_float(wreg[4 * s + e]);
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            float lo, hi;
+                            if constexpr (TYPE == kF16)
+                                f16x2(wreg[4 * s + w], lo, hi);
+                            else
+                                bf16x2(wreg[4 * s + w], lo, hi);
+                            col[(2 * w) * WP] = lo;
+                            col[(2 * w + 1) * WP] = hi;
+                        }
+                    }
+                }
+            } else if constexpr (TYPE == kQ4_K) {
+                const int c = (p & 7) >> 1;
+                float a0, b0, a1, b1;
+                q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c, a0, b0);
+                q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c + 1, a1, b1);
+                float* lo = ws + wlds[0];
+                float* hi = ws + wlds[1];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float e[4];
+                    q4_k_x4(wreg[i], false, a0, b0, e);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) lo[(4 * i + j) * WP] = e[j];
+                    q4_k_x4(wreg[i], true, a1, b1, e);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) hi[(4 * i + j) * WP] = e[j];
+                }
+            } else if constexpr (TYPE == kQ8_0) {
+                constexpr int CW = S::CB / 4;
+                const float d = half_to_f32(wreg[CW]);
+#pragma unroll
+                for (int w = 0; w < CW; ++w) {
+                    float e[4];
+                    q8_0_x4(wreg[w], d, e);
+                    // columns CB s + 4w + j: the first group for 4w < 16
+                    float* col = (4 * w < 16) ? ws + wlds[0] + (4 * w) * WP : ws + wlds[1] + (4 * w - 16) * WP;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) col[j * WP] = e[j];
+                }
+            } else {  // Q4_0
+                constexpr int CW = S::CB / 4;
+                const float d = half_to_f32(wreg[CW]);
+#pragma unroll
+                for (int w = 0; w < CW; ++w) {
+                    float e[4];
+                    q4_0_x4(wreg[w], false, d, e);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ws[wlds[0] + (4 * w + j) * WP] = e[j];
+                    q4_0_x4(wreg[w], true, d, e);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ws[wlds[1] + (4 * w + j) * WP] = e[j];
+                }
+            }
+        };
+
+        // Prologue: fill buffer 0 with chunk 0, start loading chunk 1.
+        if (nchunks > 0) {
+            load_chunk(0);
+            store_chunk(0);
+            if (nchunks > 1) load_chunk(BN);
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) {
+                store_chunk((c & 1) ^ 1);
+                if (c + 2 < nchunks) load_chunk((c + 2) * BN);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---------------- consumer ----------------
+    const int lane = tid & 63;
+    const int wt = wave >> 1, wk = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    f32x16 acc[WA][WB];
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+    // Phase q reads G[t][8q + 4h .. + 3] for the lane's t rows and
+    // W[8q + 4h .. + 3][k] for its k columns; the W index depends on q
+    // through the group permutation, so it is kept per phase.
+    const float* gbase = lds + (wt * 32 * WA + l32) * GP + 4 * h;
+    int widx[4][WB];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+            widx[q][b] = S::G_FLOATS + ws_w_index<WP>(wk * 32 * WB + 32 * b + l32, 8 * q + 4 * h);
+
+    auto read_phase = [&](auto buf_tag, int q, f32x4 (&av)[WA], f32x4 (&bv)[WB]) {
+        constexpr int off = decltype(buf_tag)::value * S::BUF_FLOATS;
+#pragma unroll
+        for (int a = 0; a < WA; ++a) av[a] = *reinterpret_cast<const f32x4*>(gbase + off + 32 * a * GP + 8 * q);
+#pragma unroll
+        for (int b = 0; b < WB; ++b) bv[b] = *reinterpret_cast<const f32x4*>(lds + off + widx[q][b]);
+    };
+    auto mfma_phase = [&](const f32x4 (&av)[WA], const f32x4 (&bv)[WB]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int a = 0; a < WA; ++a)
+#pragma unroll
+                for (int b = 0; b < WB; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][r], bv[b][r], acc[a][b], 0, 0, 0);
+    };
+    // One chunk from buffer BUF. Phase q + 1 is read while phase q's MFMAs
+    // run; phase 0 of the next chunk (buffer 1 - BUF) is read right after the
+    // barrier that publishes it, ahead of this chunk's last MFMAs. After the
+    // last chunk that read sees a stale buffer and its values are unused.
+    f32x4 a0[WA], a1[WA], b0[WB], b1[WB];
+    auto chunk = [&](auto buf_tag) {
+        using Next = std::integral_constant<int, 1 - decltype(buf_tag)::value>;
+        read_phase(buf_tag, 1, a1, b1);
+        mfma_phase(a0, b0);
+        read_phase(buf_tag, 2, a0, b0);
+        mfma_phase(a1, b1);
+        read_phase(buf_tag, 3, a1, b1);
+        mfma_phase(a0, b0);
+        __syncthreads();
+        read_phase(Next{}, 0, a0, b0);
+        mfma_phase(a1, b1);
+    };
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
+    __syncthreads();
+    read_phase(Buf0{}, 0, a0, b0);
+    for (int c = 0; c < nchunks; c += 2) {
+        chunk(Buf0{});
+        if (c + 1 < nchunks) chunk(Buf1{});
+    }
+
+    // D layout of v_mfma_f32_32x32x2f32: lane l, register v holds
+    // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+        for (int b = 0; b < WB; ++b) {
+            const int k = k0 + wk * 32 * WB + 32 * b + l32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + wt * 32 * WA + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (t < T && k < K) args.dst[(long long)t * K + k] = acc[a][b][v];
+            }
+        }
+}
+
+}  // namespace retro

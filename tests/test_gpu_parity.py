@@ -30,7 +30,8 @@ REL_TIGHT = 2e-6
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K]
-ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256"]
+ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
+             "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128"]
 
 
 @pytest.fixture(scope="module")
@@ -51,8 +52,15 @@ def variant_id(q, name):
 
 def tile_variants(wtype):
     if wtype == wl.Q4_K:
-        return ["tile_128x256", "tile_64x256"]
+        return ["tile_128x256", "tile_64x256", "ws_128x256", "ws_64x256"]
     return ALL_TILES
+
+
+def applies(q, c, variant):
+    """Whether a forced variant takes this type and shape (host-only query)."""
+    if variant == "auto":
+        return True
+    return q.variant_applies(variant_id(q, variant), c["type"], c["K"], c["N"], c["T"])
 
 
 def run(q, c, variant="auto", prefill=float("nan")):
@@ -123,6 +131,8 @@ def test_fused_decode_through_identity_gradient(q, wtype):
         ref = oracle.dequantize(wtype, c["W"], c["K"])
         c["G"] = np.eye(N, dtype=np.float32)
         for v in variants:
+            if not applies(q, c, v):
+                continue
             got = run(q, c, v)
             assert np.array_equal(got, ref), (v, N)
 
@@ -134,8 +144,12 @@ def test_fused_decode_through_identity_gradient(q, wtype):
 def test_tile_variants_match_oracle(q, wtype, i):
     c = small_case(wtype, i, 200 + i)
     _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], c["K"], nthreads=ORACLE_THREADS)
+    ran = 0
     for v in ["auto"] + tile_variants(wtype):
-        check_close(run(q, c, v), acc, ab, v)
+        if applies(q, c, v):
+            check_close(run(q, c, v), acc, ab, v)
+            ran += 1
+    assert ran >= 5
 
 
 @pytest.mark.parametrize("wtype", TYPES)
@@ -146,7 +160,11 @@ def test_skinny_matches_oracle(q, wtype, T, N):
     assert q.choice(wtype, c["K"], N, T) == q.VARIANT_SKINNY
     check_close(run(q, c, "skinny"), acc, ab, "skinny")
     check_close(run(q, c, "auto"), acc, ab, "auto")
-    check_close(run(q, c, tile_variants(wtype)[-1]), acc, ab, "tile at small T")
+    small_tile = "tile_64x256" if wtype == wl.Q4_K else "tile_64x64"
+    check_close(run(q, c, small_tile), acc, ab, "tile at small T")
+    for v in tile_variants(wtype):
+        if v.startswith("ws_") and applies(q, c, v):
+            check_close(run(q, c, v), acc, ab, v + " at small T")
 
 
 def test_q8_0_tiny_workload(q):
@@ -164,6 +182,8 @@ def test_f32_twin_on_device(q, wtype):
     w32 = oracle.dequantize(wtype, c["W"], c["K"])
     twin = dict(c, type=wl.F32, W=w32.view(np.uint8))
     for v in tile_variants(wtype) + ["skinny"]:
+        if not applies(q, twin, v) or not applies(q, c, v):
+            continue
         if v == "skinny":
             c2, t2 = dict(c, T=16, G=c["G"][:16]), dict(twin, T=16, G=c["G"][:16])
         else:
