@@ -138,7 +138,8 @@ const char *retro_strerror(int code);
  *   RETRO_VARIANT_WS_*      the same tiles computed by a workgroup whose
  *                           waves are split into MFMA (consumer) and load/
  *                           decode (producer) roles over double-buffered LDS;
- *                           dense types need rows of a multiple of 16 bytes
+ *                           needs N % 4 == 0 (and K % 4 == 0 for F32, F16,
+ *                           BF16); the TILE_* kernel takes the other shapes
  */
 enum {
     RETRO_VARIANT_AUTO = 0,

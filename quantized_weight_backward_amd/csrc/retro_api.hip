@@ -92,13 +92,12 @@ constexpr TileVariant kTiles[] = {
 
 bool is_dense(int type) { return type == RETRO_F32 || type == RETRO_F16 || type == RETRO_BF16; }
 
-// Which kernel family runs a type, from measurements on MI355X: the
-// producer/consumer kernel wins where decoding is cheap per 4-byte write
-// (dense rows) or per 16-byte code unit (Q4_K); for Q8_0 and Q4_0, whose
-// 2-byte aligned blocks are read in halfwords, spreading the decode over all
-// waves of the single-role kernel is faster. The other family stays as the
-// fallback for shapes the preferred one does not take.
-bool prefers_ws(int type) { return is_dense(type) || type == RETRO_Q4_K; }
+// The producer/consumer kernel measures faster than the single-role kernel
+// for every type on MI355X (Q4_K 0.84 vs 0.74 of the F32 peak at T = 4096,
+// Q4_0 0.76 vs 0.66, Q8_0 0.73 vs 0.67, dense T = 512 0.61-0.68 vs 0.50),
+// so it is preferred; the single-role kernel is the fallback for the shapes
+// it does not take (N % 4 != 0, or a dense K % 4 != 0).
+bool prefers_ws(int) { return true; }
 constexpr double kOtherFamily = 1.3;
 
 
@@ -112,9 +111,9 @@ const TileVariant* find_tile(int variant) {
 // W with 32-bit offsets from per-chunk buffer bases.
 bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t T) {
     if (type == RETRO_Q4_K && v.bk % 256) return false;
-    // the producer/consumer kernel loads dense rows in 16-byte units
-    if (v.ws && is_dense(type) && row_bytes_of(type, K) % 16)
-        return false;
+    // the producer/consumer kernel loads G rows in 16-byte units and dense W
+    // rows in 4-element units
+    if (v.ws && (N % 4 || (is_dense(type) && K % 4))) return false;
     return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit && int64_t(v.bt) * N * 4 < (int64_t(1) << 31) &&
            33 * row_bytes_of(type, K) < (int64_t(1) << 31);
 }

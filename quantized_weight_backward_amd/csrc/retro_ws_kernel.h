@@ -47,16 +47,36 @@ struct WsShape {
     static constexpr int BUF_FLOATS = G_FLOATS + W_FLOATS;
     static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // float4 of G per producer thread
     static_assert(GSLOTS * kPThreads * 4 == BT * BN, "G chunk splits evenly");
-    // Dense W: 16-byte units (4 F32 or 8 F16/BF16 along k of one row).
-    static constexpr int EPU = 16 / F::kBytes;
-    static constexpr int DUNITS = kDense ? BN * BK / EPU / kPThreads : 0;
+    // Dense W: units of 4 rows x 4 consecutive k (16 bytes of F32 or 8 of
+    // F16/BF16 per row, DWPR words), so that each k column of a unit is one
+    // float4 store into the k-major LDS layout.
+    static constexpr int DWPR = F::kBytes;
+    static constexpr int DUNITS = kDense ? (BN / 4) * (BK / 4) / kPThreads : 0;
+    static_assert(!kDense || DUNITS * kPThreads * 16 == BN * BK, "dense chunk splits evenly");
     // Q8_0 / Q4_0: a 32-element block is split over QSPLIT producer threads,
     // each holding CB code bytes of it.
     static constexpr int QSPLIT = (TYPE == kQ8_0 || TYPE == kQ4_0) ? kPThreads / (BN * BK / 32) : 1;
     static constexpr int CB = TYPE == kQ8_0 ? 32 / QSPLIT : 16 / QSPLIT;
     // words of W each producer thread holds between load and decode
-    static constexpr int WWORDS = kDense ? 4 * DUNITS : (TYPE == kQ4_K) ? 8 : CB / 4 + 1;
+    static constexpr int WWORDS = kDense ? 4 * DWPR * DUNITS : (TYPE == kQ4_K) ? 8 : CB / 4 + 1;
+    // Chunks whose loads a producer thread keeps in registers: the chunk
+    // being written to LDS plus RING - 1 in flight. Four when a chunk's
+    // staging fits in 32 registers (small tiles, whose chunks are short next
+    // to the global-load latency), else two. Even, so the LDS buffer of a
+    // slot's chunk is fixed.
+    static constexpr int SLOT_REGS = 4 * GSLOTS + WWORDS;
+    static constexpr int RING = SLOT_REGS <= 32 ? 4 : 2;
 };
+
+// f(integral_constant<int, 0>{}), ..., f(integral_constant<int, COUNT - 1>{})
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int COUNT, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, COUNT>{});
+}
 
 // Float index of W element (row n, column k) of a chunk inside the W part of
 // an LDS buffer: column k holds its 32 rows with the 4-row groups permuted
@@ -92,8 +112,9 @@ __global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
         // ---------------- producer ----------------
         const int p = tid - S::kPThreads;
         const long long kb0 = (long long)(k0 / F::kBlock) * F::kBytes;
-        float4 greg[S::GSLOTS];
-        uint32_t wreg[S::WWORDS];
+        constexpr int R = S::RING;
+        float4 gring[R][S::GSLOTS];
+        uint32_t wring[R][S::WWORDS];
         // Byte offsets of this thread's G loads from the chunk's base (the
         // same for every chunk): slot s is t row id / 8, columns
         // 4 (id % 8) .. + 3.
@@ -108,11 +129,11 @@ __global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
         uint32_t woff = 0;
         int wlds[S::kDense ? S::DUNITS : 2];
         if constexpr (S::kDense) {
-            constexpr int UPR = BK / S::EPU;  // units per row
+            // unit id: rows 4 (id / (BK / 4)) .. + 3, columns 4 (id % (BK / 4)) .. + 3
 #pragma unroll
             for (int s = 0; s < S::DUNITS; ++s) {
-                const int id = p + S::kPThreads * s, r = id / UPR, u = id - r * UPR;
-                wlds[s] = ws_w_index<WP>(S::EPU * u, r);
+                const int id = p + S::kPThreads * s, rg = id / (BK / 4), u = id - rg * (BK / 4);
+                wlds[s] = ws_w_index<WP>(4 * u, 4 * rg);
             }
         } else if constexpr (TYPE == kQ4_K) {
             // code unit p % 8 (16 bytes) of row p / 8: low nibbles are columns
@@ -139,52 +160,47 @@ __global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
         const long long g_end = (long long)T * N;
         const long long w_end = (long long)N * args.pitch;
 
-        // Loads of chunk rows [n0, n0 + 32) into registers. Rows at or past N
-        // lie beyond the W buffer's range and read as zero; their G columns
-        // are zeroed below. Columns past K in the last k tile read bytes of
-        // the next row (or zero) and only reach outputs that are not stored.
-        auto load_chunk = [&](int n0) {
+        // Loads of chunk rows [n0, n0 + 32) into registers, issued the same way
+        // for every chunk (no branch), so that the loads of later chunks stay
+        // in flight while an earlier slot is written to LDS. The buffer ranges
+        // end at the end of G and of W: rows at or past N read as zero, and a
+        // chunk past the last one reads zeros or rows it never uses. G columns
+        // at or past N in the last chunk (the next t row's values) are zeroed
+        // when the chunk is written to LDS. Columns past K in the last k tile
+        // read bytes of the next row (or zero) and only reach outputs that are
+        // not stored. G rows are 16-byte aligned (N % 4 == 0).
+        auto load_chunk = [&](auto slot, int n0) {
+            float4(&greg)[S::GSLOTS] = gring[decltype(slot)::value];
+            uint32_t(&wreg)[S::WWORDS] = wring[decltype(slot)::value];
             n0 = __builtin_amdgcn_readfirstlane(n0);
             const long long gb = (long long)t0 * N + n0;
             const __amdgpu_buffer_rsrc_t gr =
-                buffer_rsrc(args.G + gb, uint32_t(min(4 * (g_end - gb), (long long)0x7FFFFFFF)));
+                buffer_rsrc(args.G + gb, uint32_t(max(0ll, min(4 * (g_end - gb), (long long)0x7FFFFFFF))));
 #pragma unroll
             for (int s = 0; s < S::GSLOTS; ++s) {
-                if (args.gvec) {
-                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, goff[s], 0, 0);
-                    greg[s] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                                          __uint_as_float(v.w));
-                } else {
-                    greg[s].x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s], 0, 0));
-                    greg[s].y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 4, 0, 0));
-                    greg[s].z = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 8, 0, 0));
-                    greg[s].w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 12, 0, 0));
-                }
-            }
-            if (n0 + BN > N) {
-#pragma unroll
-                for (int s = 0; s < S::GSLOTS; ++s) {
-                    const int n = n0 + 4 * ((p + S::kPThreads * s) & 7);
-                    if (n >= N) greg[s].x = 0.f;
-                    if (n + 1 >= N) greg[s].y = 0.f;
-                    if (n + 2 >= N) greg[s].z = 0.f;
-                    if (n + 3 >= N) greg[s].w = 0.f;
-                }
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, goff[s], 0, 0);
+                greg[s] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                      __uint_as_float(v.w));
             }
             const long long wb = (long long)n0 * args.pitch + kb0;
             const __amdgpu_buffer_rsrc_t wr =
-                buffer_rsrc(args.W + wb, uint32_t(min(w_end - wb, (long long)0x7FFFFFFF)));
+                buffer_rsrc(args.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
             if constexpr (S::kDense) {
-                constexpr int UPR = BK / S::EPU;
 #pragma unroll
                 for (int s = 0; s < S::DUNITS; ++s) {
-                    const int id = p + S::kPThreads * s, r = id / UPR, u = id - r * UPR;
-                    const u32x4 v =
-                        __builtin_amdgcn_raw_buffer_load_b128(wr, uint32_t(r * args.pitch + 16 * u), 0, 0);
-                    wreg[4 * s] = v.x;
-                    wreg[4 * s + 1] = v.y;
-                    wreg[4 * s + 2] = v.z;
-                    wreg[4 * s + 3] = v.w;
+                    const int id = p + S::kPThreads * s, rg = id / (BK / 4), u = id - rg * (BK / 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t o = uint32_t((4 * rg + j) * args.pitch + 4 * S::DWPR * u);
+                        uint32_t* dstw = wreg + (4 * s + j) * S::DWPR;
+                        if constexpr (S::DWPR == 4) {
+                            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 0);
+                            dstw[0] = v.x; dstw[1] = v.y; dstw[2] = v.z; dstw[3] = v.w;
+                        } else {
+                            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, o, 0, 0);
+                            dstw[0] = v.x; dstw[1] = v.y;
+                        }
+                    }
                 }
             } else if constexpr (TYPE == kQ4_K) {
                 const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 16 + 16 * (p & 7), 0, 0);
@@ -204,12 +220,24 @@ __global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
             }
         };
 
-        // Registers -> LDS buffer `buf`: G rows as loaded, W decoded to F32
-        // into its k-major columns (element j of a 16-column group is WP
-        // floats after element j - 1).
-        auto store_chunk = [&](int buf) {
-            float* gs = lds + buf * S::BUF_FLOATS;
+        // Registers of `slot` -> LDS buffer `buf`: G rows as loaded, W decoded
+        // to F32 into its k-major columns (element j of a 16-column group is
+        // WP floats after element j - 1).
+        auto store_chunk = [&](auto slot, auto buf, int n0) {
+            float4(&greg)[S::GSLOTS] = gring[decltype(slot)::value];
+            const uint32_t(&wreg)[S::WWORDS] = wring[decltype(slot)::value];
+            float* gs = lds + decltype(buf)::value * S::BUF_FLOATS;
             float* ws = gs + S::G_FLOATS;
+            if (n0 + BN > N) {
+#pragma unroll
+                for (int s = 0; s < S::GSLOTS; ++s) {
+                    const int n = n0 + 4 * ((p + S::kPThreads * s) & 7);
+                    if (n >= N) greg[s].x = 0.f;
+                    if (n + 1 >= N) greg[s].y = 0.f;
+                    if (n + 2 >= N) greg[s].z = 0.f;
+                    if (n + 3 >= N) greg[s].w = 0.f;
+                }
+            }
 #pragma unroll
             for (int s = 0; s < S::GSLOTS; ++s) {
                 const int id = p + S::kPThreads * s;
@@ -218,22 +246,25 @@ __global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
             if constexpr (S::kDense) {
 #pragma unroll
                 for (int s = 0; s < S::DUNITS; ++s) {
-                    float* col = ws + wlds[s];
-                    if constexpr (TYPE == kF32) {
+                    // v[j][e]: row j, column e of the unit
+                    float v[4][4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) col[e * WP] = __uint_as_float(wreg[4 * s + e]);
-                    } else {
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t* w = wreg + (4 * s + j) * S::DWPR;
+                        if constexpr (TYPE == kF32) {
 #pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            float lo, hi;
-                            if constexpr (TYPE == kF16)
-                                f16x2(wreg[4 * s + w], lo, hi);
-                            else
-                                bf16x2(wreg[4 * s + w], lo, hi);
-                            col[(2 * w) * WP] = lo;
-                            col[(2 * w + 1) * WP] = hi;
+                            for (int e = 0; e < 4; ++e) v[j][e] = __uint_as_float(w[e]);
+                        } else if constexpr (TYPE == kF16) {
+                            f16x2(w[0], v[j][0], v[j][1]);
+                            f16x2(w[1], v[j][2], v[j][3]);
+                        } else {
+                            bf16x2(w[0], v[j][0], v[j][1]);
+                            bf16x2(w[1], v[j][2], v[j][3]);
                         }
                     }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        *reinterpret_cast<float4*>(ws + wlds[s] + e * WP) = make_float4(v[0][e], v[1][e], v[2][e], v[3][e]);
                 }
             } else if constexpr (TYPE == kQ4_K) {
                 const int c = (p & 7) >> 1;
@@ -280,20 +311,29 @@ __global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
             }
         };
 
-        // Prologue: fill buffer 0 with chunk 0, start loading chunk 1.
-        if (nchunks > 0) {
-            load_chunk(0);
-            store_chunk(0);
-            if (nchunks > 1) load_chunk(BN);
-        }
+        // Chunk j is loaded into slot j % R and written to LDS buffer j % 2.
+        // Prologue: start the loads of chunks 0 .. R - 1, fill buffer 0.
+        using Zero = std::integral_constant<int, 0>;
+        static_for<R>([&](auto i) { load_chunk(i, i * BN); });
+        store_chunk(Zero{}, Zero{}, 0);
         __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) {
-                store_chunk((c & 1) ^ 1);
-                if (c + 2 < nchunks) load_chunk((c + 2) * BN);
-            }
+        // While the consumers contract chunk c: write chunk c + 1 to LDS, start
+        // the loads of chunk c + R into the slot chunk c left, then the
+        // barrier. Whole groups of R chunks run unguarded (a chunk past the end
+        // is loaded and written but never read); the last partial group is
+        // guarded per chunk.
+        auto step = [&](auto i, int c) {
+            constexpr int I = decltype(i)::value;
+            store_chunk(std::integral_constant<int, (I + 1) % R>{}, std::integral_constant<int, (I + 1) & 1>{},
+                        (c + 1) * BN);
+            load_chunk(i, (c + R) * BN);
             __syncthreads();
-        }
+        };
+        int c0 = 0;
+        for (; c0 + R <= nchunks; c0 += R) static_for<R>([&](auto i) { step(i, c0 + decltype(i)::value); });
+        static_for<R>([&](auto i) {
+            if (c0 + decltype(i)::value < nchunks) step(i, c0 + decltype(i)::value);
+        });
         return;
     }
 

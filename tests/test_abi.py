@@ -81,7 +81,8 @@ def test_supported():
 def test_choice():
     assert q.choice(q.Q4_K, 14336, 4096, 16) == q.VARIANT_SKINNY
     assert q.choice(q.Q4_K, 4096, 14336, 4096) == q.VARIANT_WS_128x256
-    assert q.choice(q.Q4_0, 5120, 17408, 2048) in (q.VARIANT_TILE_64x128, q.VARIANT_TILE_64x256)
+    assert q.choice(q.Q4_0, 5120, 17408, 2048) == q.VARIANT_WS_64x128
+    assert q.choice(q.Q4_0, 5120, 17407, 2048) == q.VARIANT_TILE_64x128  # N % 4 != 0: the fallback family
     for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0):
         assert q.choice(wtype, 4096, 4096, 512) in q.VARIANT_NAMES
     for wtype in (q.F32, q.F16, q.BF16):  # dense rows go to the producer/consumer kernel
@@ -97,8 +98,11 @@ def test_variant_applies():
     assert q.variant_applies(q.VARIANT_TILE_128x256, q.Q4_K, 4096, 14336, 4096)
     assert not q.variant_applies(q.VARIANT_TILE_128x128, q.Q4_K, 4096, 14336, 4096)
     assert q.variant_applies(q.VARIANT_WS_128x256, q.Q4_K, 4096, 14336, 4096)
-    assert q.variant_applies(q.VARIANT_WS_128x128, q.F32, 300, 77, 200)      # 1200-byte rows
-    assert not q.variant_applies(q.VARIANT_WS_128x128, q.F16, 301, 77, 200)  # 602-byte rows
+    assert q.variant_applies(q.VARIANT_WS_128x128, q.F32, 300, 76, 200)      # K % 4 == 0
+    assert q.variant_applies(q.VARIANT_WS_128x128, q.F16, 300, 76, 200)
+    assert not q.variant_applies(q.VARIANT_WS_128x128, q.F16, 301, 76, 200)  # K % 4 != 0
+    assert not q.variant_applies(q.VARIANT_WS_128x128, q.F32, 300, 77, 200)  # G rows not 16-byte units
+    assert not q.variant_applies(q.VARIANT_WS_128x256, q.Q4_K, 4096, 14335, 4096)
     assert q.variant_applies(q.VARIANT_TILE_128x128, q.F16, 301, 77, 200)
     assert not q.variant_applies(99, q.F32, 32, 32, 32)
     assert not q.variant_applies(q.VARIANT_TILE_64x64, q.Q4_K, 100, 1, 1)   # bad shape

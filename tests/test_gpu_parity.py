@@ -85,14 +85,16 @@ def check_close(y, acc, ab, label=""):
 # alignment paths: (N % 4 != 0) -> scalar G loads; K chosen so that the W
 # row pitch is 16-, 8-, 4- or only 2-byte aligned.
 SMALL_K = {
-    wl.F32: (300, 256, 301),
-    wl.F16: (301, 264, 296),
-    wl.BF16: (300, 520, 302),
-    wl.Q8_0: (416, 768, 352),
-    wl.Q4_0: (512, 352, 416),
-    wl.Q4_K: (768, 512, 256),
+    wl.F32: (300, 256, 301, 300),
+    wl.F16: (301, 264, 296, 264),
+    wl.BF16: (300, 520, 302, 520),
+    wl.Q8_0: (416, 768, 352, 416),
+    wl.Q4_0: (512, 352, 416, 352),
+    wl.Q4_K: (768, 512, 256, 768),
 }
-SMALL_TN = ((200, 77), (130, 96), (67, 33))
+# (T, N): the last case has N % 4 == 0 (G rows 16-byte aligned, which the
+# producer/consumer kernel needs) with a partial last chunk of 4 rows
+SMALL_TN = ((200, 77), (130, 96), (67, 33), (150, 100))
 
 
 def small_case(wtype, i, seed):
@@ -103,7 +105,7 @@ def small_case(wtype, i, seed):
 # --- decode ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("i", [0, 1, 2])
+@pytest.mark.parametrize("i", [0, 1, 2, 3])
 def test_dequantize_bit_exact(q, wtype, i):
     c = small_case(wtype, i, 100 + i)
     ref = oracle.dequantize(wtype, c["W"], c["K"])
@@ -126,30 +128,39 @@ def test_fused_decode_through_identity_gradient(q, wtype):
     """With T = N and G = I, out_prod(W, I) = decoded W exactly (every other
     term is w * 0); this checks every tile kernel's and the skinny kernel's
     decode without trusting retro_dequantize."""
-    for N, variants in ((48, tile_variants(wtype)), (16, ["skinny"] + tile_variants(wtype))):
-        c = wl.make_case(wtype, N, SMALL_K[wtype][0], N, seed=7)
-        ref = oracle.dequantize(wtype, c["W"], c["K"])
-        c["G"] = np.eye(N, dtype=np.float32)
-        for v in variants:
-            if not applies(q, c, v):
-                continue
-            got = run(q, c, v)
-            assert np.array_equal(got, ref), (v, N)
+    for K in (SMALL_K[wtype][0], SMALL_K[wtype][3]):
+        for N, variants in ((48, tile_variants(wtype)), (16, ["skinny"] + tile_variants(wtype))):
+            c = wl.make_case(wtype, N, K, N, seed=7)
+            ref = oracle.dequantize(wtype, c["W"], c["K"])
+            c["G"] = np.eye(N, dtype=np.float32)
+            for v in variants:
+                if not applies(q, c, v):
+                    continue
+                got = run(q, c, v)
+                assert np.array_equal(got, ref), (v, N, K)
 
 
 # --- contraction ----------------------------------------------------------------
 
+def ws_expected(c):
+    """Whether the producer/consumer variants should take a case: G rows in
+    16-byte units, dense W rows in 4-element units."""
+    dense = c["type"] in (wl.F32, wl.F16, wl.BF16)
+    return c["N"] % 4 == 0 and (not dense or c["K"] % 4 == 0)
+
+
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("i", [0, 1, 2])
+@pytest.mark.parametrize("i", [0, 1, 2, 3])
 def test_tile_variants_match_oracle(q, wtype, i):
     c = small_case(wtype, i, 200 + i)
     _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], c["K"], nthreads=ORACLE_THREADS)
-    ran = 0
+    ran = []
     for v in ["auto"] + tile_variants(wtype):
         if applies(q, c, v):
             check_close(run(q, c, v), acc, ab, v)
-            ran += 1
-    assert ran >= 5
+            ran.append(v)
+    expected = [v for v in tile_variants(wtype) if not v.startswith("ws_") or ws_expected(c)]
+    assert set(expected) <= set(ran), (expected, ran)
 
 
 @pytest.mark.parametrize("wtype", TYPES)
@@ -196,8 +207,9 @@ def test_f32_twin_on_device(q, wtype):
 # --- invariants -----------------------------------------------------------------
 
 @pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q4_0, wl.BF16])
-def test_invariants(q, wtype):
-    c = small_case(wtype, 0, 500)
+@pytest.mark.parametrize("i", [0, 3])
+def test_invariants(q, wtype, i):
+    c = small_case(wtype, i, 500)
     base = run(q, c)
     # every output written (NaN prefill gone), two runs bitwise equal
     assert np.isfinite(base).all()
@@ -232,8 +244,9 @@ def test_zero_size_calls_touch_nothing(q):
     assert q.lib.retro_out_prod(wl.Q4_K, None, None, None, 256, 5, 0, None) == 0
 
 
-def test_no_allocation_during_a_call(q):
-    c = small_case(wl.Q4_K, 0, 600)
+@pytest.mark.parametrize("i", [0, 3])
+def test_no_allocation_during_a_call(q, i):
+    c = small_case(wl.Q4_K, i, 600)
     W, G = dev(c["W"]), dev(c["G"])
     out = torch.empty((c["T"], c["K"]), device="cuda")
     q.out_prod(wl.Q4_K, W, G, c["K"], out=out)  # warm (module load)
