@@ -152,7 +152,9 @@ enum {
     RETRO_VARIANT_WS_128x256 = 7,
     RETRO_VARIANT_WS_64x256 = 8,
     RETRO_VARIANT_WS_128x128 = 9,
-    RETRO_VARIANT_WS_64x128 = 10
+    RETRO_VARIANT_WS_64x128 = 10,
+    RETRO_VARIANT_WS_32x256 = 11,
+    RETRO_VARIANT_WS_32x128 = 12
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the

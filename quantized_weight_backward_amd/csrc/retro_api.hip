@@ -88,6 +88,8 @@ constexpr TileVariant kTiles[] = {
     {RETRO_VARIANT_WS_64x256, 64, 256, 1.04, true},
     {RETRO_VARIANT_WS_128x128, 128, 128, 1.00, true},
     {RETRO_VARIANT_WS_64x128, 64, 128, 1.02, true},
+    {RETRO_VARIANT_WS_32x256, 32, 256, 1.06, true},
+    {RETRO_VARIANT_WS_32x128, 32, 128, 1.04, true},
 };
 
 bool is_dense(int type) { return type == RETRO_F32 || type == RETRO_F16 || type == RETRO_BF16; }
@@ -175,9 +177,9 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     return launch_status();
 }
 
-template <int TYPE, int WA, int WB>
+template <int TYPE, int WA, int WB, int CT>
 int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
-    using S = WsShape<TYPE, WA, WB>;
+    using S = WsShape<TYPE, WA, WB, CT>;
     TileArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.G = G;
@@ -192,7 +194,7 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
     a.tiles_k = int(cdiv(K, S::BK));
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
-    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
 
@@ -225,8 +227,9 @@ int launch_variant(int variant, const void* W, const float* G, float* dst, int64
         case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, st);
         case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, st);
         case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, st);
-        case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4>(W, G, dst, K, N, T, st);
-        case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4, 2>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4, 2>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, st);
         default: break;
     }
     if constexpr (TYPE != kQ4_K) {
@@ -234,8 +237,9 @@ int launch_variant(int variant, const void* W, const float* G, float* dst, int64
             case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, st);
             case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, st);
             case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, st);
-            case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2>(W, G, dst, K, N, T, st);
-            case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2, 2>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2, 2>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_WS_32x128: return launch_ws<TYPE, 1, 1, 1>(W, G, dst, K, N, T, st);
             default: break;
         }
     }

@@ -2,7 +2,7 @@
 //
 // Same contraction and tile mapping as out_prod_tile_kernel, organised so
 // that the matrix pipe never waits on staging:
-//   * 8 waves per workgroup. Waves 0-3 (consumers, 2 x 2 over the tile) only
+//   * 8 waves per workgroup. Waves 0-3 (consumers, CT x 4/CT over the tile) only
 //     read operands from LDS and issue v_mfma_f32_32x32x2_f32. Waves 4-7
 //     (producers) load G and packed W with buffer loads, decode W in
 //     registers and write both into LDS.
@@ -29,14 +29,21 @@
 
 namespace retro {
 
-template <int TYPE, int WA, int WB>
+template <int TYPE, int WA, int WB, int CT>
 struct WsShape {
     using F = Format<TYPE>;
     static constexpr bool kDense = F::kBlock == 1;
     static constexpr int kPThreads = 256;          // producer threads (waves 4-7)
     static constexpr int kThreads = 2 * kPThreads;  // + 4 consumer waves
-    static constexpr int BT = 64 * WA;              // consumer waves 2 x 2, each (32*WA) x (32*WB)
-    static constexpr int BK = 64 * WB;
+    // consumer waves CT x CK, each (32*WA) x (32*WB) outputs
+    static_assert(CT == 1 || CT == 2, "consumer grid 1 x 4 or 2 x 2");
+    static constexpr int CK = 4 / CT;
+    static constexpr int BT = 32 * WA * CT;
+    static constexpr int BK = 32 * WB * CK;
+    // Workgroups per CU the register budget is set for: two for the 32-row
+    // tiles (46 KB of LDS), whose second workgroup fills the first one's
+    // barrier waits; one otherwise.
+    static constexpr int kWgPerCu = BT == 32 ? 2 : 1;
     static constexpr int BN = 32;
     static_assert(BK == 128 || BK == 256, "K tile of 128 or 256 columns");
     static_assert(TYPE != kQ4_K || BK == 256, "Q4_K tiles hold whole super-blocks");
@@ -88,9 +95,9 @@ __device__ __forceinline__ int ws_w_index(int k, int n) {
     return k * WP + (n ^ (((k >> 4) & 7) << 2));
 }
 
-template <int TYPE, int WA, int WB>
-__global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
-    using S = WsShape<TYPE, WA, WB>;
+template <int TYPE, int WA, int WB, int CT>
+__global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void out_prod_ws_kernel(TileArgs args) {
+    using S = WsShape<TYPE, WA, WB, CT>;
     using F = Format<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, WP = S::WP;
 
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_ws_kernel(TileArgs args) {
 
     // ---------------- consumer ----------------
     const int lane = tid & 63;
-    const int wt = wave >> 1, wk = wave & 1;
+    const int wt = wave / S::CK, wk = wave % S::CK;
     const int h = lane >> 5, l32 = lane & 31;
     f32x16 acc[WA][WB];
 #pragma unroll

@@ -31,7 +31,7 @@ ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K]
 ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
-             "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128"]
+             "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128", "ws_32x256", "ws_32x128"]
 
 
 @pytest.fixture(scope="module")
@@ -52,7 +52,7 @@ def variant_id(q, name):
 
 def tile_variants(wtype):
     if wtype == wl.Q4_K:
-        return ["tile_128x256", "tile_64x256", "ws_128x256", "ws_64x256"]
+        return ["tile_128x256", "tile_64x256", "ws_128x256", "ws_64x256", "ws_32x256"]
     return ALL_TILES
 
 
