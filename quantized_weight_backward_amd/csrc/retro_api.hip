@@ -146,6 +146,25 @@ int choose(int type, int64_t K, int64_t N, int64_t T) {
     return best < 0 ? RETRO_E_SHAPE : best;
 }
 
+// Row tiles per group of the tile order. An XCD runs S = 32 CUs x wg_per_cu
+// tiles at once, `height` row tiles by S / height column tiles of its range,
+// so G is fetched about ceil(tiles_k / (S / height)) times and W about
+// ceil(tiles_t / height) times; the height that minimises the sum wins.
+int group_height(int64_t tiles_t, int64_t tiles_k, int wg_per_cu, double g_bytes, double w_bytes) {
+    const int64_t S = 32 * int64_t(wg_per_cu);
+    int best = 1;
+    double best_cost = -1;
+    for (int64_t h = 1; h <= S; h *= 2) {
+        const double cost = g_bytes * double(cdiv(tiles_k, S / h)) + w_bytes * double(cdiv(tiles_t, h));
+        if (best_cost < 0 || cost < best_cost) {
+            best = int(h);
+            best_cost = cost;
+        }
+        if (h >= tiles_t) break;
+    }
+    return best;
+}
+
 // hipGetLastError reports the last error of any runtime call on this thread,
 // so it is cleared right before each launch (clear_last_error) and read right
 // after it (launch_status): the result is this launch's status only.
@@ -171,6 +190,7 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     a.gvec = (N % 4 == 0) ? 1 : 0;
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
+    a.group = group_height(a.tiles_t, a.tiles_k, 2, 4.0 * T * N, double(N) * a.pitch);
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
     hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt), dim3(S::kThreads), 0, st, a);
@@ -192,6 +212,7 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
     a.gvec = (N % 4 == 0) ? 1 : 0;
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
+    a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * a.pitch);
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
     hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);

@@ -55,15 +55,16 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return x * per + (x < rem ? x : rem) + i;
 }
 
-// Logical tile -> (row tile, column tile), in groups of GT row tiles so that
-// neighbours share rows of G and columns of W.
-__device__ __forceinline__ void tile_coords(int b, int tiles_t, int tiles_k, int& tt, int& tk) {
+// Logical tile -> (row tile, column tile), in groups of `height` row tiles
+// (row tile fastest), so that the tiles an XCD runs at once share rows of G
+// and columns of W. The host picks the height that minimises the estimated
+// fetch of G and W for the shape.
+__device__ __forceinline__ void tile_coords(int b, int tiles_t, int tiles_k, int height, int& tt, int& tk) {
     const int lin = xcd_remap(b, tiles_t * tiles_k);
-    constexpr int GT = 8;
-    const int span = GT * tiles_k;
+    const int span = height * tiles_k;
     const int group = lin / span;
-    const int first = group * GT;
-    const int gsize = min(tiles_t - first, GT);
+    const int first = group * height;
+    const int gsize = min(tiles_t - first, height);
     const int in = lin - group * span;
     tt = first + in % gsize;
     tk = in / gsize;
@@ -82,6 +83,7 @@ struct TileArgs {
     int wvec;         // W staging load width (16, 8, 4, 2)
     int gvec;         // 1: G rows take float4 loads (N % 4 == 0)
     int tiles_t, tiles_k;
+    int group;        // row tiles per group of the tile order (tile_coords)
 };
 
 // Column swizzle of a decoded W tile in LDS: XOR column bits 2-4 with
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 
     const int tid = threadIdx.x;
     int tt, tk;
-    tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, tt, tk);
+    tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, args.group, tt, tk);
     const int t0 = tt * BT, k0 = tk * BK;
     const int K = args.K, N = args.N, T = args.T;
     // Byte offset of this tile's k range inside one W row.

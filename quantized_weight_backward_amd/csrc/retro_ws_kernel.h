@@ -52,6 +52,8 @@ struct WsShape {
     static constexpr int G_FLOATS = BT * GP;
     static constexpr int W_FLOATS = BK * WP;
     static constexpr int BUF_FLOATS = G_FLOATS + W_FLOATS;
+    // workgroups that fit on a CU by LDS (160 KB), at most two (16 waves)
+    static constexpr int kResident = (160 * 1024) / (2 * BUF_FLOATS * 4) < 2 ? 1 : 2;
     static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // float4 of G per producer thread
     static_assert(GSLOTS * kPThreads * 4 == BT * BN, "G chunk splits evenly");
     // Dense W: units of 4 rows x 4 consecutive k (16 bytes of F32 or 8 of
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int tt, tk;
-    tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, tt, tk);
+    tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, args.group, tt, tk);
     const int t0 = tt * BT, k0 = tk * BK;
     const int K = args.K, N = args.N, T = args.T;
     const int nchunks = (N + BN - 1) / BN;
