@@ -36,6 +36,11 @@
  * sub-scale/sub-min field. The pages print no Q4_K block; the order used is
  * the GGUF one, and the tests pin the decoder to hand-packed fixtures of that
  * reading and to a full pack bijection, not to values from the pages.
+ *
+ * Parity unpinned against the pages: Q5_K and Q6_K as a whole. The pages name
+ * the K-quant family only through the Q4_K_M files it is used in; these two
+ * layouts are the GGUF ones, and the tests pin them to hand-derived fixtures
+ * and to their structural relations with Q4_K, not to values from the pages.
  */
 #include <math.h>
 #include <pthread.h>
@@ -43,7 +48,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_BF16 = 30 };
+enum { T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_BF16 = 30 };
 
 /* IEEE-754 binary16 -> binary32: 1 sign bit, 5 exponent bits (bias 15), 10
  * fraction bits. Exponent 0: subnormal, value = frac * 2^-24. Exponent 31:
@@ -161,6 +166,69 @@ int oracle_decode_row(int type, const uint8_t *row, int64_t K, float *out) {
             }
         }
         return 0;
+    case T_Q5_K:
+        /* 176-byte super-block of 256 elements: fp16 d, fp16 dmin, the same
+         * 12-byte sub-scale/sub-min field as Q4_K, 32 bytes qh holding each
+         * element's fifth bit, 128 bytes qs of low nibbles. Element e lies
+         * in chunk c = e / 64 at r = e % 64: for r < 32 its low 4 bits are
+         * the low nibble of qs[32c + r], its fifth bit is bit 2c of qh[r],
+         * and it uses sub-block 2c; otherwise the high nibble of
+         * qs[32c + r - 32], bit 2c + 1 of qh[r - 32], sub-block 2c + 1.
+         * value = (d * sc_j) * q - (dmin * m_j) with q in 0..31: each
+         * product exact in F32, one rounding in the subtraction. */
+        if (K % 256) return -1;
+        for (b = 0; b < K / 256; b++) {
+            const uint8_t *blk = row + 176 * b;
+            float d = oracle_half_to_float(rd16(blk));
+            float dmin = oracle_half_to_float(rd16(blk + 2));
+            const uint8_t *s = blk + 4;
+            const uint8_t *qh = blk + 16;
+            const uint8_t *qs = blk + 48;
+            for (int e = 0; e < 256; e++) {
+                int c = e / 64, r = e % 64, q, j, sc, m;
+                if (r < 32) {
+                    q = (qs[32 * c + r] & 15) | (((qh[r] >> (2 * c)) & 1) << 4);
+                    j = 2 * c;
+                } else {
+                    q = (qs[32 * c + r - 32] >> 4) | (((qh[r - 32] >> (2 * c + 1)) & 1) << 4);
+                    j = 2 * c + 1;
+                }
+                q4k_scale_min(s, j, &sc, &m);
+                float a = d * (float)sc;
+                float mm = dmin * (float)m;
+                float v = a * (float)q;
+                out[256 * b + e] = v - mm;
+            }
+        }
+        return 0;
+    case T_Q6_K:
+        /* 210-byte super-block of 256 elements: 128 bytes ql of low nibbles,
+         * 64 bytes qh of 2-bit high parts, 16 signed 8-bit sub-scales (one
+         * per 16 elements), fp16 d last. Element e lies in half h = e / 128,
+         * quarter p = (e % 128) / 32, at l = e % 32: its low 4 bits are the
+         * low (p < 2) or high (p >= 2) nibble of ql[64h + 32(p % 2) + l],
+         * its high 2 bits are bits 2p and 2p + 1 of qh[32h + l], and its
+         * sub-scale is scales[8h + 2p + l / 16]. value = (d * sc) * (q - 32)
+         * with q in 0..63: the odd parts of d, sc and q - 32 have at most
+         * 11, 7 and 5 bits, so the product is exact in F32. */
+        if (K % 256) return -1;
+        for (b = 0; b < K / 256; b++) {
+            const uint8_t *blk = row + 210 * b;
+            const uint8_t *ql = blk;
+            const uint8_t *qh = blk + 128;
+            const int8_t *sc = (const int8_t *)(blk + 192);
+            float d = oracle_half_to_float(rd16(blk + 208));
+            for (int e = 0; e < 256; e++) {
+                int h = e / 128, p = (e % 128) / 32, l = e % 32;
+                int lo = ql[64 * h + 32 * (p % 2) + l];
+                lo = p < 2 ? (lo & 15) : (lo >> 4);
+                int hi = (qh[32 * h + l] >> (2 * p)) & 3;
+                int q = lo | (hi << 4);
+                float a = d * (float)sc[8 * h + 2 * p + l / 16];
+                out[256 * b + e] = a * (float)(q - 32);
+            }
+        }
+        return 0;
     default:
         return -1;
     }
@@ -173,6 +241,8 @@ int64_t oracle_row_bytes(int type, int64_t K) {
     case T_Q8_0: return K % 32 ? -1 : K / 32 * 34;
     case T_Q4_0: return K % 32 ? -1 : K / 32 * 18;
     case T_Q4_K: return K % 256 ? -1 : K / 256 * 144;
+    case T_Q5_K: return K % 256 ? -1 : K / 256 * 176;
+    case T_Q6_K: return K % 256 ? -1 : K / 256 * 210;
     default: return -1;
     }
 }

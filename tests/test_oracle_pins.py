@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads as wl
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K]
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K, wl.Q5_K, wl.Q6_K]
 
 
 def hexbytes(tokens):
@@ -129,6 +129,155 @@ def test_q4_k_non_integer_scales():
         q = int(codes[32 * c + r]) & 15 if r < 32 else int(codes[32 * c + r - 32]) >> 4
         j = 2 * c + (r >= 32)
         assert got[e] == np.float32(2.0 ** -10 * sc[j] * q - 0.5 * m[j]), e
+
+
+def q5_k_superblock(d_bits, dmin_bits, field, qh, qs):
+    blk = np.zeros(176, dtype=np.uint8)
+    blk[0:2] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
+    blk[2:4] = np.array([dmin_bits & 255, dmin_bits >> 8], dtype=np.uint8)
+    blk[4:16] = field
+    blk[16:48] = qh
+    blk[48:176] = qs
+    return blk
+
+
+def q6_k_superblock(d_bits, scales, ql, qh):
+    blk = np.zeros(210, dtype=np.uint8)
+    blk[0:128] = ql
+    blk[128:192] = qh
+    blk[192:208] = np.asarray(scales, dtype=np.int8).view(np.uint8)
+    blk[208:210] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
+    return blk
+
+
+def ramp_codes(n):
+    i = np.arange(n)
+    return (((i * 7 + 3) & 15) | (((i * 5 + 1) & 15) << 4)).astype(np.uint8)
+
+
+def test_q5_k_hand_built_superblock(golden):
+    g4, g5 = golden("q4_k_pack.txt"), golden("q5_k_block.txt")
+    qh = ((np.arange(32) * 13 + 7) & 255).astype(np.uint8)
+    blk = q5_k_superblock(0x3C00, 0x3C00, hexbytes(g4["field_hex"]), qh, ramp_codes(128))
+    got = oracle.dequantize(wl.Q5_K, blk, 256)[0]
+    for item in g5["spot_checks"]:
+        e, v = item.split("=")
+        assert got[int(e)] == float(v), item
+
+
+def test_q5_k_without_fifth_bits_is_q4_k():
+    """qh = 0: a Q5_K block decodes like the Q4_K block with the same scales,
+    field and nibbles (the pinned Q4_K decoder), for random blocks and non-
+    integer scales."""
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        d, dmin = (int(v) for v in rng.integers(0x0400, 0x4400, size=2))
+        field = rng.integers(0, 256, size=12, dtype=np.uint8)
+        qs = rng.integers(0, 256, size=128, dtype=np.uint8)
+        q5 = oracle.dequantize(wl.Q5_K, q5_k_superblock(d, dmin, field, np.zeros(32, np.uint8), qs), 256)[0]
+        q4 = oracle.dequantize(wl.Q4_K, q4_k_superblock(d, dmin, field, qs), 256)[0]
+        assert np.array_equal(q5.view(np.uint32), q4.view(np.uint32))
+
+
+def test_q5_k_each_fifth_bit_moves_one_element_by_16_sub_scales(golden):
+    """With d = dmin = 1 every value is the integer sc_j * q - m_j. Setting
+    one bit of qh adds 16 * sc_j to exactly one element, and the 256 bits
+    reach the 256 elements one to one: bit b of qh[r] belongs to element
+    64 (b // 2) + 32 (b % 2) + r."""
+    g4 = golden("q4_k_pack.txt")
+    field = hexbytes(g4["field_hex"])
+    sc = [int(v) for v in g4["sc"]]
+    qs = ramp_codes(128)
+    base = oracle.dequantize(wl.Q5_K, q5_k_superblock(0x3C00, 0x3C00, field, np.zeros(32, np.uint8), qs), 256)[0]
+    seen = set()
+    for r in range(32):
+        for b in range(8):
+            qh = np.zeros(32, np.uint8)
+            qh[r] = 1 << b
+            got = oracle.dequantize(wl.Q5_K, q5_k_superblock(0x3C00, 0x3C00, field, qh, qs), 256)[0]
+            diff = np.nonzero(got != base)[0]
+            assert len(diff) == 1, (r, b)
+            e = int(diff[0])
+            assert e == 64 * (b // 2) + 32 * (b % 2) + r, (r, b, e)
+            assert got[e] - base[e] == 16 * sc[b], (r, b)
+            seen.add(e)
+    assert seen == set(range(256))
+
+
+def test_q6_k_hand_built_superblock(golden):
+    g = golden("q6_k_block.txt")
+    scales = [int(v) for v in g["scales"]]
+    qh = ((np.arange(64) * 13 + 7) & 255).astype(np.uint8)
+    got = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3C00, scales, ramp_codes(128), qh), 256)[0]
+    for item in g["spot_checks"]:
+        e, v = item.split("=")
+        assert got[int(e)] == float(v), item
+
+
+def test_q6_k_structure():
+    """d = 1, every sub-scale 1, qh = 0: element values are nibble - 32, and
+    the 256 nibbles (low nibbles of ql, then high nibbles, by quarter and
+    half) reach the 256 elements one to one. Then each of the 128 two-bit
+    high parts, set to 1, adds 16 to exactly one element."""
+    ql = np.zeros(128, np.uint8)
+    seen = {}
+    for i in range(128):
+        for hi_nib in (0, 1):
+            ql[:] = 0
+            ql[i] = 0x10 if hi_nib else 0x01
+            got = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3C00, [1] * 16, ql, np.zeros(64, np.uint8)), 256)[0]
+            moved = np.nonzero(got != -32)[0]
+            assert len(moved) == 1 and got[moved[0]] == -31, (i, hi_nib)
+            seen[(i, hi_nib)] = int(moved[0])
+    assert sorted(seen.values()) == list(range(256))
+    # element 128h + 32p + l: nibble of ql[64h + 32(p % 2) + l], high half for p >= 2
+    for (i, hi_nib), e in seen.items():
+        h, p, l = e // 128, (e % 128) // 32, e % 32
+        assert (i, hi_nib) == (64 * h + 32 * (p % 2) + l, int(p >= 2)), (i, hi_nib, e)
+    moved_by_qh = set()
+    for i in range(64):
+        for p in range(4):
+            qh = np.zeros(64, np.uint8)
+            qh[i] = 1 << (2 * p)
+            got = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3C00, [1] * 16, np.zeros(128, np.uint8), qh), 256)[0]
+            moved = np.nonzero(got != -32)[0]
+            assert len(moved) == 1 and got[moved[0]] == -16, (i, p)
+            e = int(moved[0])
+            assert e == 128 * (i // 32) + 32 * p + i % 32, (i, p, e)
+            moved_by_qh.add(e)
+    assert moved_by_qh == set(range(256))
+
+
+def test_q6_k_sub_scale_index_and_sign():
+    """One sub-scale at a time set to -3 (the rest 1): exactly the 16
+    elements 128h + 32p + 16s + 0..15 of sub-scale 8h + 2p + s change, to
+    -3 * (q - 32)."""
+    ql = ramp_codes(128)
+    qh = ((np.arange(64) * 13 + 7) & 255).astype(np.uint8)
+    base = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3C00, [1] * 16, ql, qh), 256)[0]
+    for i in range(16):
+        scales = [1] * 16
+        scales[i] = -3
+        got = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3C00, scales, ql, qh), 256)[0]
+        h, p, s_ = i // 8, (i % 8) // 2, i % 2
+        idx = 128 * h + 32 * p + 16 * s_ + np.arange(16)
+        assert np.array_equal(got[idx], -3 * base[idx])
+        rest = np.setdiff1d(np.arange(256), idx)
+        assert np.array_equal(got[rest], base[rest])
+
+
+def test_q6_k_products_are_exact():
+    """Largest odd parts of d, sub-scale and q - 32 (2047/1024, 127, 31): the
+    oracle's F32 value equals the exact product."""
+    ql = np.full(128, 0xFF, np.uint8)   # low nibbles 15
+    qh = np.full(64, 0x55, np.uint8)    # every 2-bit high part 1 -> q = 31, q - 32 = -1
+    got = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3FFF, [127] * 16, ql, qh), 256)[0]
+    assert np.all(got == np.float32(-(2047 / 1024) * 127))
+    qh = np.zeros(64, np.uint8)         # q = 15 -> q - 32 = -17
+    ql = np.full(128, 0x11, np.uint8)   # q = 1 -> -31
+    got = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3FFF, [127] * 16, ql, qh), 256)[0]
+    assert np.all(got == np.float32(2047 * 127 * -31 / 1024))
+    assert 2047 * 127 * 31 < 2 ** 24
 
 
 @pytest.mark.parametrize("variant", ["same", "shifted"])

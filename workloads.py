@@ -16,6 +16,10 @@ blocks; fp16 fields are little-endian; GGUF block formats):
   Q4_K  144 bytes per 256 elements: fp16 scale, fp16 min-scale, 12 bytes
         holding eight 6-bit sub-scales and eight 6-bit sub-mins, then 128
         bytes of 4-bit codes
+  Q5_K  176 bytes per 256 elements: as Q4_K, with 32 bytes of fifth code
+        bits between the 12-byte field and the 128 bytes of low nibbles
+  Q6_K  210 bytes per 256 elements: 128 bytes of low nibbles, 64 bytes of
+        2-bit high parts, 16 signed 8-bit sub-scales, fp16 scale
 
 Distributions (uniform ranges are [lo, hi) for floats and inclusive for
 integers; N(0, s) takes s as the standard deviation):
@@ -24,6 +28,9 @@ integers; N(0, s) takes s as the standard deviation):
   Q4_0  scale U[1e-3, 1e-2) rounded to fp16, codes U{0..15}
   Q4_K  scale and min-scale U[1e-4, 1e-3) rounded to fp16, sub-scales and
         sub-mins U{0..63}, codes U{0..15}
+  Q5_K  as Q4_K, codes U{0..31}
+  Q6_K  scale U[1e-4, 1e-3) rounded to fp16, sub-scales U{-128..127},
+        codes U{0..63}
   dense W ~ N(0, 0.02) in F32, then rounded to F16 or BF16 (nearest-even)
   G     ~ N(0, sigma) in F32
 
@@ -34,8 +41,10 @@ sub-scale or sub-min, so uniform bytes are uniform 6-bit values for every
 sub-scale and sub-min whatever the bit order of the pack.
 
 Draw order for one case, from numpy Generator(PCG64(seed)): scales (the
-scale, then the Q4_K min-scale), then the Q4_K scale field, then codes (or
-the dense values), then G.
+scale, then the K-quant min-scale), then the sub-scale field, then codes
+(Q5_K: fifth bits, then low nibbles; Q6_K: low nibbles, then high parts) or
+the dense values, then G. Codes of several bits are drawn as uniform bytes
+of their bit fields, which makes every code uniform over its range.
 """
 
 from __future__ import annotations
@@ -43,13 +52,15 @@ from __future__ import annotations
 import numpy as np
 
 # GGUF tensor-type ids
-F32, F16, Q4_0, Q8_0, Q4_K, BF16 = 0, 1, 2, 8, 12, 30
+F32, F16, Q4_0, Q8_0, Q4_K, Q5_K, Q6_K, BF16 = 0, 1, 2, 8, 12, 13, 14, 30
 
-TYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0", Q4_0: "q4_0", Q4_K: "q4_k"}
+TYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0", Q4_0: "q4_0", Q4_K: "q4_k", Q5_K: "q5_k",
+              Q6_K: "q6_k"}
 TYPE_IDS = {v: k for k, v in TYPE_NAMES.items()}
 
 # (elements per block, bytes per block)
-_GEOMETRY = {F32: (1, 4), F16: (1, 2), BF16: (1, 2), Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144)}
+_GEOMETRY = {F32: (1, 4), F16: (1, 2), BF16: (1, 2), Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144),
+             Q5_K: (256, 176), Q6_K: (256, 210)}
 
 
 def block_geometry(wtype: int) -> tuple[int, int]:
@@ -108,6 +119,26 @@ def make_weight(wtype: int, N: int, K: int, rng: np.random.Generator) -> np.ndar
         out[:, :, 2:4] = dmin.view(np.uint8).reshape(N, nb, 2)
         out[:, :, 4:16] = scales
         out[:, :, 16:144] = qs
+    elif wtype == Q5_K:
+        d = _fp16_uniform(rng, 1e-4, 1e-3, (N, nb))
+        dmin = _fp16_uniform(rng, 1e-4, 1e-3, (N, nb))
+        scales = rng.integers(0, 256, size=(N, nb, 12), dtype=np.uint8)
+        qh = rng.integers(0, 256, size=(N, nb, 32), dtype=np.uint8)
+        qs = rng.integers(0, 256, size=(N, nb, 128), dtype=np.uint8)
+        out[:, :, 0:2] = d.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 2:4] = dmin.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 4:16] = scales
+        out[:, :, 16:48] = qh
+        out[:, :, 48:176] = qs
+    elif wtype == Q6_K:
+        d = _fp16_uniform(rng, 1e-4, 1e-3, (N, nb))
+        scales = rng.integers(0, 256, size=(N, nb, 16), dtype=np.uint8)
+        ql = rng.integers(0, 256, size=(N, nb, 128), dtype=np.uint8)
+        qh = rng.integers(0, 256, size=(N, nb, 64), dtype=np.uint8)
+        out[:, :, 0:128] = ql
+        out[:, :, 128:192] = qh
+        out[:, :, 192:208] = scales
+        out[:, :, 208:210] = d.view(np.uint8).reshape(N, nb, 2)
     else:
         raise ValueError(f"unknown weight type {wtype}")
     return out.reshape(N, rb)
