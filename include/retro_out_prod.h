@@ -32,6 +32,17 @@
  *               128 bytes of nibbles (each 64-element chunk c uses 32 bytes:
  *               low nibbles are sub-block 2c, high nibbles sub-block 2c+1);
  *               value (d*sc_j)*q - dmin*m_j
+ *   RETRO_Q5_K  176 bytes / 256 elements: fp16 d, fp16 dmin, the Q4_K 12-byte
+ *               field, 32 bytes qh, 128 bytes of nibbles as Q4_K; element
+ *               r of chunk c (r < 32: low nibble, else high) takes bit 2c
+ *               (2c+1) of qh[r % 32] as its fifth bit; value as Q4_K
+ *   RETRO_Q6_K  210 bytes / 256 elements: 128 bytes of low nibbles, 64 bytes
+ *               of 2-bit high parts, 16 int8 sub-scales, fp16 d; element
+ *               128h + 32p + l: nibble of byte 64h + 32(p%2) + l (high
+ *               nibble for p >= 2), bits 2p..2p+1 of byte 128 + 32h + l,
+ *               sub-scale 8h + 2p + l/16; value (d*sc)*(q-32)
+ * The Q5_K and Q6_K layouts are the GGUF ones: the pages that define this
+ * operation name the K-quant family only through the Q4_K_M files it runs on.
  *
  * Pointers: W, G and dst are device pointers (hipMalloc'd or equivalent) and
  * must be 16-byte aligned. dst must not overlap W or G. stream is a
@@ -63,6 +74,8 @@ enum {
     RETRO_Q4_0 = 2,
     RETRO_Q8_0 = 8,
     RETRO_Q4_K = 12,
+    RETRO_Q5_K = 13,
+    RETRO_Q6_K = 14,
     RETRO_BF16 = 30
 };
 
@@ -85,12 +98,12 @@ enum {
 
 /*
  * dst[t][k] = sum_n W[n][k] * G[t][n] for t < T, k < K.
- *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_K
+ *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_K/Q5_K/Q6_K
  *   W       device, N * retro_row_bytes(type, K) bytes
  *   G       device, T * N floats
  *   dst     device, T * K floats, overwritten
  *   K       elements per W row (a multiple of the block: 32 for Q8_0/Q4_0,
- *           256 for Q4_K, 1 otherwise)
+ *           256 for Q4_K/Q5_K/Q6_K, 1 otherwise)
  *   N       rows of W = the reduction length
  *   T       rows of G and dst
  * T == 0 or K == 0: returns RETRO_OK without touching memory (pointers may
@@ -119,7 +132,8 @@ int retro_dequantize(int type, const void *W, float *out, int64_t K, int64_t N, 
  */
 int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T);
 
-/* Bytes per W row: K/32*34 (Q8_0), K/32*18 (Q4_0), K/256*144 (Q4_K), 4K
+/* Bytes per W row: K/32*34 (Q8_0), K/32*18 (Q4_0), K/256*144 (Q4_K),
+ * K/256*176 (Q5_K), K/256*210 (Q6_K), 4K
  * (F32), 2K (F16, BF16). -1 for an unknown type, a negative K or a K that is
  * not a whole number of blocks. Touches no device. */
 int64_t retro_row_bytes(int type, int64_t K);
@@ -133,7 +147,8 @@ const char *retro_strerror(int code);
  *   RETRO_VARIANT_SKINNY    one pass over W, all of n per workgroup; T <= 16
  *   RETRO_VARIANT_TILE_*    tiled F32-MFMA kernel, tile = rows of T x columns
  *                           of K per workgroup (256-column tiles need K tiles
- *                           that are whole Q4_K super-blocks; Q4_K takes only
+ *                           that are whole K-quant super-blocks; Q4_K, Q5_K and
+ *                           Q6_K take only
  *                           those)
  *   RETRO_VARIANT_WS_*      the same tiles computed by a workgroup whose
  *                           waves are split into MFMA (consumer) and load/

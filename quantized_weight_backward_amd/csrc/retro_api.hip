@@ -44,6 +44,8 @@ bool geometry(int type, Geometry& g) {
         case RETRO_Q8_0: g = {32, 34}; return true;
         case RETRO_Q4_0: g = {32, 18}; return true;
         case RETRO_Q4_K: g = {256, 144}; return true;
+        case RETRO_Q5_K: g = {256, 176}; return true;
+        case RETRO_Q6_K: g = {256, 210}; return true;
         default: return false;
     }
 }
@@ -112,7 +114,8 @@ const TileVariant* find_tile(int variant) {
 // The tiled kernel addresses a tile's BT rows of G and a chunk's 32 rows of
 // W with 32-bit offsets from per-chunk buffer bases.
 bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t T) {
-    if (type == RETRO_Q4_K && v.bk % 256) return false;
+    Geometry geo;
+    if (geometry(type, geo) && geo.block == 256 && v.bk % 256) return false;
     // the producer/consumer kernel loads G rows in 16-byte units and dense W
     // rows in 4-element units
     if (v.ws && (N % 4 || (is_dense(type) && K % 4))) return false;
@@ -253,7 +256,7 @@ int launch_variant(int variant, const void* W, const float* G, float* dst, int64
         case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, st);
         default: break;
     }
-    if constexpr (TYPE != kQ4_K) {
+    if constexpr (!kSuperBlock<TYPE>) {
         switch (variant) {
             case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, st);
             case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, st);
@@ -311,6 +314,8 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         case RETRO_Q8_0: return launch_variant<kQ8_0>(variant, W, G, dst, K, N, T, st);
         case RETRO_Q4_0: return launch_variant<kQ4_0>(variant, W, G, dst, K, N, T, st);
         case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, st);
+        case RETRO_Q5_K: return launch_variant<kQ5_K>(variant, W, G, dst, K, N, T, st);
+        case RETRO_Q6_K: return launch_variant<kQ6_K>(variant, W, G, dst, K, N, T, st);
         default: return RETRO_E_TYPE;
     }
 }
@@ -362,6 +367,8 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
         case RETRO_Q8_0: return launch_dequant<kQ8_0>(W, out, K, N, st);
         case RETRO_Q4_0: return launch_dequant<kQ4_0>(W, out, K, N, st);
         case RETRO_Q4_K: return launch_dequant<kQ4_K>(W, out, K, N, st);
+        case RETRO_Q5_K: return launch_dequant<kQ5_K>(W, out, K, N, st);
+        case RETRO_Q6_K: return launch_dequant<kQ6_K>(W, out, K, N, st);
         default: return RETRO_E_TYPE;
     }
 }

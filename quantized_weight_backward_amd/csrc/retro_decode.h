@@ -5,10 +5,12 @@
 // retro_dequantize covers the arithmetic of all of them.
 //
 // Exactness: a Q8_0/Q4_0 value d*q needs at most 11+8 significant bits, a
-// Q4_K product (d*sc)*q at most 11+6+4 = 21 and dmin*m at most 17, so every
-// product below is exact in float32 and only the Q4_K subtraction rounds
-// (once, to nearest-even). Whether the compiler fuses a*q - b into an FMA
-// therefore changes no bit.
+// Q4_K product (d*sc)*q at most 11+6+4 = 21 (Q5_K: 22) and dmin*m at most 17,
+// so every product below is exact in float32 and only the Q4_K/Q5_K
+// subtraction rounds (once, to nearest-even). A Q6_K value (d*sc)*(q - 32)
+// has odd parts of at most 11, 7 and 5 bits, so it is exact, and so is its
+// form a*q - 32a (a*q needs at most 24 bits). Whether the compiler fuses
+// a*q - b into an FMA therefore changes no bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,7 +19,7 @@
 namespace retro {
 
 // GGUF tensor-type ids.
-enum : int { kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ8_0 = 8, kQ4_K = 12, kBF16 = 30 };
+enum : int { kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ8_0 = 8, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14, kBF16 = 30 };
 
 // kBlock: elements per block; kBytes: bytes per block; kGroup: elements one
 // thread decodes from one 16-byte code load in the tiled kernel.
@@ -28,6 +30,12 @@ template <> struct Format<kBF16> { static constexpr int kBlock = 1,   kBytes = 2
 template <> struct Format<kQ8_0> { static constexpr int kBlock = 32,  kBytes = 34,  kGroup = 16; };
 template <> struct Format<kQ4_0> { static constexpr int kBlock = 32,  kBytes = 18,  kGroup = 32; };
 template <> struct Format<kQ4_K> { static constexpr int kBlock = 256, kBytes = 144, kGroup = 32; };
+template <> struct Format<kQ5_K> { static constexpr int kBlock = 256, kBytes = 176, kGroup = 32; };
+template <> struct Format<kQ6_K> { static constexpr int kBlock = 256, kBytes = 210, kGroup = 32; };
+
+// The K-quant formats: 256-element super-blocks, so a tile of K holds whole
+// super-blocks only when it is 256 columns wide.
+template <int TYPE> constexpr bool kSuperBlock = Format<TYPE>::kBlock == 256;
 
 // IEEE binary16 bits -> float32 (v_cvt_f32_f16; exact, subnormals included).
 __device__ __forceinline__ float half_to_f32(uint32_t bits) {
@@ -111,6 +119,34 @@ __device__ __forceinline__ void q4_k_x4(uint32_t w, bool high, float a, float b,
     const uint32_t m = nibbles(w, high);
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) - b;
+}
+
+// Q5_K: low (high = false) or high nibbles of four qs bytes, plus bit
+// `bit` of the four qh bytes of the same elements as the fifth bit;
+// value a*q - b with a = d*sc_j, b = dmin*m_j (q4_k_coeffs; same field).
+__device__ __forceinline__ void q5_k_x4(uint32_t qs, uint32_t qh, int bit, bool high, float a, float b,
+                                        float out[4]) {
+    const uint32_t fifth = ((qh >> bit) & 0x01010101u) << 4;
+    const uint32_t m = nibbles(qs, high) | fifth;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) - b;
+}
+
+// Q6_K: low or high nibbles of four ql bytes, plus bits 2p, 2p+1 of the four
+// qh bytes of the same elements as bits 4-5 of q; value (d*sc)*(q - 32),
+// computed as a*q + b with a = d*sc and b = -32a (exact, see above).
+__device__ __forceinline__ void q6_k_x4(uint32_t ql, bool high, uint32_t qh, int p, float a, float b,
+                                        float out[4]) {
+    const uint32_t m = nibbles(ql, high) | (((qh >> (2 * p)) & 0x03030303u) << 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) + b;
+}
+
+// Signed 8-bit Q6_K sub-scale `i` (0..3) of a word, times d: (a, b = -32a).
+__device__ __forceinline__ void q6_k_coeffs(uint32_t scales, int i, float d, float& a, float& b) {
+    const int sc = static_cast<int>(static_cast<int8_t>((scales >> (8 * i)) & 0xFFu));
+    a = d * static_cast<float>(sc);
+    b = -32.0f * a;
 }
 
 }  // namespace retro

@@ -95,8 +95,8 @@ struct TileArgs {
 // conflict-free).
 template <int TYPE>
 __device__ __forceinline__ int lds_swizzle(int col) {
-    if constexpr (TYPE == kQ4_K) return col ^ (((col >> 6) & 3) << 2);
-    if constexpr (TYPE == kQ4_0) return col ^ (((col >> 5) & 7) << 2);
+    if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) return col ^ (((col >> 6) & 3) << 2);
+    if constexpr (TYPE == kQ4_0 || TYPE == kQ6_K) return col ^ (((col >> 5) & 7) << 2);
     if constexpr (TYPE == kQ8_0) return col ^ (((col >> 5) & 3) << 2);
     return col;
 }
@@ -316,6 +316,55 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                         q4_k_x4(w[i], true, a1, b1, e);
                         *reinterpret_cast<float4*>(brow + S::swz(hi + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
                     }
+                } else if constexpr (TYPE == kQ5_K) {
+                    // as Q4_K, plus the fifth bits: qh bytes 16h .. 16h + 15
+                    // belong to the same elements as this code unit
+                    const int sb = g >> 3, c = (g >> 1) & 3, h = g & 1;
+                    const uint8_t* blk = raw + 176 * sb;
+                    const uint4 hd = *reinterpret_cast<const uint4*>(blk);
+                    const uint4 qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * h);
+                    const uint4 cw = *reinterpret_cast<const uint4*>(blk + 48 + 32 * c + 16 * h);
+                    float a0, b0, a1, b1;
+                    q4_k_coeffs(hd.x, hd.y, hd.z, hd.w, 2 * c, a0, b0);
+                    q4_k_coeffs(hd.x, hd.y, hd.z, hd.w, 2 * c + 1, a1, b1);
+                    const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+                    const uint32_t hb[4] = {qh.x, qh.y, qh.z, qh.w};
+                    const int lo = 256 * sb + 64 * c + 16 * h, hi = lo + 32;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float e[4];
+                        q5_k_x4(w[i], hb[i], 2 * c, false, a0, b0, e);
+                        *reinterpret_cast<float4*>(brow + S::swz(lo + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
+                        q5_k_x4(w[i], hb[i], 2 * c + 1, true, a1, b1, e);
+                        *reinterpret_cast<float4*>(brow + S::swz(hi + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
+                    }
+                } else if constexpr (TYPE == kQ6_K) {
+                    // group (half hh, l range 8j .. 8j + 7) of super-block sb:
+                    // the elements 128 hh + 32 p + 8j + 0..7 of all four
+                    // quarters p; 2-byte aligned block, read in halfwords
+                    const int sb = g >> 3, hh = (g >> 2) & 1, j = g & 3;
+                    const uint8_t* blk = raw + 210 * sb;
+                    const uint32_t qlw[2][2] = {{lds_word_a2(blk + 64 * hh + 8 * j), lds_word_a2(blk + 64 * hh + 8 * j + 4)},
+                                                {lds_word_a2(blk + 64 * hh + 32 + 8 * j),
+                                                 lds_word_a2(blk + 64 * hh + 32 + 8 * j + 4)}};
+                    const uint32_t qhw[2] = {lds_word_a2(blk + 128 + 32 * hh + 8 * j),
+                                             lds_word_a2(blk + 128 + 32 * hh + 8 * j + 4)};
+                    const uint32_t scw[2] = {lds_word_a2(blk + 192 + 8 * hh), lds_word_a2(blk + 192 + 8 * hh + 4)};
+                    const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk + 208));
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const int si = (j >> 1) + 2 * qq;  // sub-scale 8 hh + si
+                        float a, b;
+                        q6_k_coeffs(scw[si >> 2], si & 3, d, a, b);
+                        const int col = 256 * sb + 128 * hh + 32 * qq + 8 * j;
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            float e[4];
+                            q6_k_x4(qlw[qq & 1][i], qq >= 2, qhw[i], qq, a, b, e);
+                            *reinterpret_cast<float4*>(brow + S::swz(col + 4 * i)) =
+                                make_float4(e[0], e[1], e[2], e[3]);
+                        }
+                    }
                 } else if constexpr (TYPE == kQ4_0) {
                     const uint8_t* blk = raw + 18 * g;
                     const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
@@ -470,7 +519,7 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
         const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + 2 + (r & 15));
         q4_0_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), r >= 16, d, e);
-    } else {  // kQ4_K; K is a multiple of 256, so k < K always
+    } else if constexpr (TYPE == kQ4_K) {  // K is a multiple of 256, so k < K always
         const uint8_t* sbp = row + (k >> 8) * 144;
         const int e256 = k & 255, c = e256 >> 6, r = e256 & 63;
         const bool high = r >= 32;
@@ -479,6 +528,27 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         q4_k_coeffs(hw[0], hw[1], hw[2], hw[3], 2 * c + (high ? 1 : 0), a, b);
         const uint32_t w = *reinterpret_cast<const uint32_t*>(sbp + 16 + 32 * c + (r & 31));
         q4_k_x4(w, high, a, b, e);
+    } else if constexpr (TYPE == kQ5_K) {
+        const uint8_t* sbp = row + (k >> 8) * 176;
+        const int e256 = k & 255, c = e256 >> 6, r = e256 & 63;
+        const bool high = r >= 32;
+        const uint32_t* hw = reinterpret_cast<const uint32_t*>(sbp);
+        float a, b;
+        q4_k_coeffs(hw[0], hw[1], hw[2], hw[3], 2 * c + (high ? 1 : 0), a, b);
+        const uint32_t qh = *reinterpret_cast<const uint32_t*>(sbp + 16 + (r & 31));
+        const uint32_t qs = *reinterpret_cast<const uint32_t*>(sbp + 48 + 32 * c + (r & 31));
+        q5_k_x4(qs, qh, 2 * c + (high ? 1 : 0), high, a, b, e);
+    } else {  // kQ6_K: 2-byte aligned super-blocks
+        const uint8_t* sbp = row + (k >> 8) * 210;
+        const int e256 = k & 255, h = e256 >> 7, p = (e256 >> 5) & 3, l = e256 & 31;
+        const uint16_t* ql = reinterpret_cast<const uint16_t*>(sbp + 64 * h + 32 * (p & 1) + l);
+        const uint16_t* qh = reinterpret_cast<const uint16_t*>(sbp + 128 + 32 * h + l);
+        const int si = 8 * h + 2 * p + (l >> 4);
+        const uint32_t scw = *reinterpret_cast<const uint16_t*>(sbp + 192 + (si & ~1));
+        float a, b;
+        q6_k_coeffs(scw, si & 1, half_to_f32(*reinterpret_cast<const uint16_t*>(sbp + 208)), a, b);
+        q6_k_x4(uint32_t(ql[0]) | (uint32_t(ql[1]) << 16), p >= 2, uint32_t(qh[0]) | (uint32_t(qh[1]) << 16), p, a, b,
+                e);
     }
 }
 
@@ -487,8 +557,8 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
 // (row, block) scale this lane decodes for the whole wave, and 4 G values.
 template <int TYPE>
 struct SkinnyRaw {
-    static constexpr int CW = (TYPE == kF32) ? 4 : (TYPE == kF16 || TYPE == kBF16) ? 2 : 1;
-    static constexpr int HW = (TYPE == kQ4_K) ? 4 : 1;
+    static constexpr int CW = (TYPE == kF32) ? 4 : (TYPE == kF16 || TYPE == kBF16 || TYPE == kQ5_K || TYPE == kQ6_K) ? 2 : 1;
+    static constexpr int HW = (TYPE == kQ4_K || TYPE == kQ5_K) ? 4 : (TYPE == kQ6_K) ? 2 : 1;
     uint32_t code[4][CW];
     uint32_t hdr[HW];
     float g[4];
@@ -498,9 +568,11 @@ struct SkinnyRaw {
 // of everything one lane loads for that group on the fast path; they do not
 // change from group to group, so each group costs one uniform base pointer.
 struct SkinnyOffsets {
-    uint32_t code[4];  // code words of rows 4*(l/16) + s, columns k0 + 4*(l%16) ..
-    uint32_t hdr;      // header of the scale pair this lane decodes
-    uint32_t g;        // G[min(l%16, T-1)][4*(l/16)] (bytes from G + n0)
+    uint32_t code[4];   // code words of rows 4*(l/16) + s, columns k0 + 4*(l%16) ..
+    uint32_t code2[4];  // Q5_K fifth bits / Q6_K high parts of the same elements
+    uint32_t hdr;       // header of the scale pair this lane decodes (Q6_K: its sub-scale pair)
+    uint32_t hdr2;      // Q6_K: the scale d of that row
+    uint32_t g;         // G[min(l%16, T-1)][4*(l/16)] (bytes from G + n0)
 };
 
 // Fast path (K % 4 == 0, N % 4 == 0, whole group inside W). Columns at or
@@ -511,7 +583,7 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
     const int j = lane & 15, rq = lane >> 4;
     const int K = a.K;
     const int kl = min(k0 + 4 * j, K - 4);
-    uint32_t col;
+    uint32_t col, col2 = 0;
     if constexpr (TYPE == kF32) {
         col = 4u * kl;
     } else if constexpr (TYPE == kF16 || TYPE == kBF16) {
@@ -520,18 +592,40 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
         col = (kl >> 5) * 34 + 2 + (kl & 31);
     } else if constexpr (TYPE == kQ4_0) {
         col = (kl >> 5) * 18 + 2 + (kl & 15);
-    } else {
+    } else if constexpr (TYPE == kQ4_K) {
         const int e = kl & 255;
         col = (kl >> 8) * 144 + 16 + 32 * (e >> 6) + (e & 31);
+    } else if constexpr (TYPE == kQ5_K) {
+        const int e = kl & 255;
+        col = (kl >> 8) * 176 + 48 + 32 * (e >> 6) + (e & 31);
+        col2 = (kl >> 8) * 176 + 16 + (e & 31);
+    } else {  // kQ6_K
+        const int e = kl & 255, h = e >> 7, p = (e >> 5) & 3, l = e & 31;
+        col = (kl >> 8) * 210 + 64 * h + 32 * (p & 1) + l;
+        col2 = (kl >> 8) * 210 + 128 + 32 * h + l;
     }
     SkinnyOffsets o;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) o.code[s] = uint32_t((4 * rq + s) * a.pitch) + col;
+    for (int s = 0; s < 4; ++s) {
+        o.code[s] = uint32_t((4 * rq + s) * a.pitch) + col;
+        o.code2[s] = uint32_t((4 * rq + s) * a.pitch) + col2;
+    }
     const int hr = (lane & 31) >> 1, sel = lane & 1;
     uint32_t hcol = 0;
     if constexpr (TYPE == kQ4_K) hcol = (k0 >> 8) * 144;
+    if constexpr (TYPE == kQ5_K) hcol = (k0 >> 8) * 176;
     if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) hcol = (min(k0 + 32 * sel, K - 32) >> 5) * Format<TYPE>::kBytes;
     o.hdr = uint32_t(hr * a.pitch) + hcol;
+    o.hdr2 = 0;
+    if constexpr (TYPE == kQ6_K) {
+        // lane -> (row lane / 4, sub-scale 8h + 2(p0 + w / 2) + w % 2), w = lane % 4,
+        // p0 the slab's first quarter; the halfword holding it, and the row's d
+        const int e0 = k0 & 255, h = e0 >> 7, p0 = (e0 >> 5) & 3, w = lane & 3;
+        const int si = 8 * h + 2 * (p0 + (w >> 1)) + (w & 1);
+        const uint32_t rowb = uint32_t((lane >> 2) * a.pitch) + uint32_t((k0 >> 8) * 210);
+        o.hdr = rowb + 192 + uint32_t(si & ~1);
+        o.hdr2 = rowb + 208;
+    }
     o.g = uint32_t(((long long)min(j, a.T - 1) * a.N + 4 * rq) * 4);
     return o;
 }
@@ -563,13 +657,25 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
             const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s], 0, 0);
             const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s] + 2, 0, 0);
             r.code[s][0] = lo | (hi << 16);
+        } else if constexpr (TYPE == kQ6_K) {
+            // 2-byte aligned super-blocks: low nibbles and high parts in halfwords
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s], 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s] + 2, 0, 0);
+            const uint32_t hlo = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code2[s], 0, 0);
+            const uint32_t hhi = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code2[s] + 2, 0, 0);
+            r.code[s][0] = lo | (hi << 16);
+            r.code[s][1] = hlo | (hhi << 16);
         } else {
             r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
+            if constexpr (TYPE == kQ5_K) r.code[s][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code2[s], 0, 0);
         }
     }
-    if constexpr (TYPE == kQ4_K) {
+    if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) {
         const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wr, o.hdr, 0, 0);
         r.hdr[0] = h.x; r.hdr[1] = h.y; r.hdr[2] = h.z; r.hdr[3] = h.w;
+    } else if constexpr (TYPE == kQ6_K) {
+        r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
+        r.hdr[1] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr2, 0, 0);
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
     } else {
@@ -617,18 +723,39 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
                 const uint16_t* c = reinterpret_cast<const uint16_t*>(row + (kl >> 5) * BYTES + 2 + off);
                 r.code[s][0] = uint32_t(c[0]) | (uint32_t(c[1]) << 16);
             }
-        } else {  // kQ4_K (K % 256 == 0, so kl < K)
+        } else if constexpr (TYPE == kQ4_K) {  // K % 256 == 0, so kl < K
             const int e = kl & 255;
             r.code[s][0] = *reinterpret_cast<const uint32_t*>(row + (kl >> 8) * 144 + 16 + 32 * (e >> 6) + (e & 31));
+        } else if constexpr (TYPE == kQ5_K) {
+            const int e = kl & 255;
+            const uint8_t* sb = row + (kl >> 8) * 176;
+            r.code[s][0] = *reinterpret_cast<const uint32_t*>(sb + 48 + 32 * (e >> 6) + (e & 31));
+            r.code[s][1] = *reinterpret_cast<const uint32_t*>(sb + 16 + (e & 31));
+        } else {  // kQ6_K
+            const int e = kl & 255, h = e >> 7, p = (e >> 5) & 3, l = e & 31;
+            const uint8_t* sb = row + (kl >> 8) * 210;
+            const uint16_t* ql = reinterpret_cast<const uint16_t*>(sb + 64 * h + 32 * (p & 1) + l);
+            const uint16_t* qh = reinterpret_cast<const uint16_t*>(sb + 128 + 32 * h + l);
+            r.code[s][0] = uint32_t(ql[0]) | (uint32_t(ql[1]) << 16);
+            r.code[s][1] = uint32_t(qh[0]) | (uint32_t(qh[1]) << 16);
         }
     }
     const int hr = (lane & 31) >> 1, sel = lane & 1;
     const bool hvalid = n0 + hr < N;
     const uint8_t* hrow = a.W + (long long)(n0 + hr) * a.pitch;
-    if constexpr (TYPE == kQ4_K) {
+    if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) {
         uint4 h = make_uint4(0u, 0u, 0u, 0u);
-        if (hvalid) h = *reinterpret_cast<const uint4*>(hrow + (k0 >> 8) * 144);
+        if (hvalid) h = *reinterpret_cast<const uint4*>(hrow + (k0 >> 8) * Format<TYPE>::kBytes);
         r.hdr[0] = h.x; r.hdr[1] = h.y; r.hdr[2] = h.z; r.hdr[3] = h.w;
+    } else if constexpr (TYPE == kQ6_K) {
+        const int e0 = k0 & 255, h = e0 >> 7, p0 = (e0 >> 5) & 3, w = lane & 3;
+        const int si = 8 * h + 2 * (p0 + (w >> 1)) + (w & 1);
+        r.hdr[0] = r.hdr[1] = 0u;
+        if (n0 + (lane >> 2) < N) {
+            const uint8_t* sb = a.W + (long long)(n0 + (lane >> 2)) * a.pitch + (k0 >> 8) * 210;
+            r.hdr[0] = *reinterpret_cast<const uint16_t*>(sb + 192 + (si & ~1));
+            r.hdr[1] = *reinterpret_cast<const uint16_t*>(sb + 208);
+        }
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
         const int kb = k0 + 32 * sel;
         r.hdr[0] = 0u;
@@ -675,14 +802,27 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
                 q4_0_x4(r.code[s][0], ((4 * j) & 31) >= 16, d, wv[s]);
             }
         }
-    } else {  // kQ4_K: this lane's pair is sub-block 2c + (lane & 1)
+    } else if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) {  // this lane's pair is sub-block 2c + (lane & 1)
         const int c = (k0 & 255) >> 6;
         float am, bm;
         q4_k_coeffs(r.hdr[0], r.hdr[1], r.hdr[2], r.hdr[3], 2 * c + (lane & 1), am, bm);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int src = 2 * (4 * rq + s) + hi;
-            q4_k_x4(r.code[s][0], hi != 0, lane_value(am, src), lane_value(bm, src), wv[s]);
+            if constexpr (TYPE == kQ4_K)
+                q4_k_x4(r.code[s][0], hi != 0, lane_value(am, src), lane_value(bm, src), wv[s]);
+            else
+                q5_k_x4(r.code[s][0], r.code[s][1], 2 * c + hi, hi != 0, lane_value(am, src), lane_value(bm, src),
+                        wv[s]);
+        }
+    } else {  // kQ6_K: this lane's pair is (row lane / 4, sub-scale slot lane % 4)
+        const int e0 = k0 & 255, p = ((e0 >> 5) & 3) + hi, l16 = (j & 7) >> 2;
+        float am, bm;
+        q6_k_coeffs(r.hdr[0], lane & 1, half_to_f32(r.hdr[1]), am, bm);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int src = 4 * (4 * rq + s) + 2 * hi + l16;
+            q6_k_x4(r.code[s][0], p >= 2, r.code[s][1], p, lane_value(am, src), lane_value(bm, src), wv[s]);
         }
     }
 }

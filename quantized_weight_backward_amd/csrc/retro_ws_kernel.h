@@ -46,7 +46,7 @@ struct WsShape {
     static constexpr int kWgPerCu = BT == 32 ? 2 : 1;
     static constexpr int BN = 32;
     static_assert(BK == 128 || BK == 256, "K tile of 128 or 256 columns");
-    static_assert(TYPE != kQ4_K || BK == 256, "Q4_K tiles hold whole super-blocks");
+    static_assert(!kSuperBlock<TYPE> || BK == 256, "K-quant tiles hold whole super-blocks");
     static constexpr int GP = BN + 4;  // floats per t row of G in LDS
     static constexpr int WP = BN + 4;  // floats per k column of W in LDS
     static constexpr int G_FLOATS = BT * GP;
@@ -67,7 +67,11 @@ struct WsShape {
     static constexpr int QSPLIT = (TYPE == kQ8_0 || TYPE == kQ4_0) ? kPThreads / (BN * BK / 32) : 1;
     static constexpr int CB = TYPE == kQ8_0 ? 32 / QSPLIT : 16 / QSPLIT;
     // words of W each producer thread holds between load and decode
-    static constexpr int WWORDS = kDense ? 4 * DWPR * DUNITS : (TYPE == kQ4_K) ? 8 : CB / 4 + 1;
+    static constexpr int WWORDS = kDense ? 4 * DWPR * DUNITS
+                                  : (TYPE == kQ4_K) ? 8
+                                  : (TYPE == kQ5_K) ? 12
+                                  : (TYPE == kQ6_K) ? 9
+                                                    : CB / 4 + 1;
     // Chunks whose loads a producer thread keeps in registers: the chunk
     // being written to LDS plus RING - 1 in flight. Four when a chunk's
     // staging fits in 32 registers (small tiles, whose chunks are short next
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
         // W: byte offset of this thread's block in the chunk, and the LDS
         // float index of the first element it writes in each 16-column group.
         uint32_t woff = 0;
-        int wlds[S::kDense ? S::DUNITS : 2];
+        int wlds[S::kDense ? S::DUNITS : (TYPE == kQ6_K) ? 4 : 2];
         if constexpr (S::kDense) {
             // unit id: rows 4 (id / (BK / 4)) .. + 3, columns 4 (id % (BK / 4)) .. + 3
 #pragma unroll
@@ -144,13 +148,20 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                 const int id = p + S::kPThreads * s, rg = id / (BK / 4), u = id - rg * (BK / 4);
                 wlds[s] = ws_w_index<WP>(4 * u, 4 * rg);
             }
-        } else if constexpr (TYPE == kQ4_K) {
+        } else if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) {
             // code unit p % 8 (16 bytes) of row p / 8: low nibbles are columns
             // 64c + 16h + 0..15, high nibbles 64c + 32 + 16h + 0..15
             const int r = p >> 3, u = p & 7, c = u >> 1, h = u & 1;
             woff = uint32_t(r * args.pitch);
             wlds[0] = ws_w_index<WP>(64 * c + 16 * h, r);
             wlds[1] = ws_w_index<WP>(64 * c + 32 + 16 * h, r);
+        } else if constexpr (TYPE == kQ6_K) {
+            // half hh, l range 8j .. 8j + 7 of row p / 8: columns
+            // 128 hh + 32 qq + 8j + 0..7 of the four quarters qq
+            const int r = p >> 3, hh = (p >> 2) & 1, j = p & 3;
+            woff = uint32_t(r * args.pitch);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) wlds[qq] = ws_w_index<WP>(128 * hh + 32 * qq + 8 * j, r);
         } else {
             // part s of block b of row r: code bytes CB s .. CB s + CB - 1
             const int id = p / S::QSPLIT, s = p - id * S::QSPLIT;
@@ -216,6 +227,30 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                 const u32x4 hd = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
                 wreg[0] = cw.x; wreg[1] = cw.y; wreg[2] = cw.z; wreg[3] = cw.w;
                 wreg[4] = hd.x; wreg[5] = hd.y; wreg[6] = hd.z; wreg[7] = hd.w;
+            } else if constexpr (TYPE == kQ5_K) {
+                // code unit, header, and the 16 fifth-bit bytes of the same elements
+                const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 48 + 16 * (p & 7), 0, 0);
+                const u32x4 hd = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
+                const u32x4 qh = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 16 + 16 * (p & 1), 0, 0);
+                wreg[0] = cw.x; wreg[1] = cw.y; wreg[2] = cw.z; wreg[3] = cw.w;
+                wreg[4] = hd.x; wreg[5] = hd.y; wreg[6] = hd.z; wreg[7] = hd.w;
+                wreg[8] = qh.x; wreg[9] = qh.y; wreg[10] = qh.z; wreg[11] = qh.w;
+            } else if constexpr (TYPE == kQ6_K) {
+                // 2-byte aligned super-blocks, read in halfwords: ql bytes
+                // 64hh + 8j .. (quarters 0, 2) and 64hh + 32 + 8j .. (1, 3),
+                // qh bytes 128 + 32hh + 8j .., the 8 sub-scales of half hh, d
+                const int hh = (p >> 2) & 1, j = p & 3;
+                const uint32_t at[4] = {woff + 64 * hh + 8 * j, woff + 64 * hh + 32 + 8 * j,
+                                        woff + 128 + 32 * hh + 8 * j, woff + 192 + 8 * hh};
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, at[f] + 4 * w, 0, 0);
+                        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, at[f] + 4 * w + 2, 0, 0);
+                        wreg[2 * f + w] = lo | (hi << 16);
+                    }
+                wreg[8] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + 208, 0, 0);
             } else {  // Q8_0, Q4_0: 2-byte aligned blocks, read in halfwords
                 constexpr int CW = S::CB / 4;
                 const uint32_t codes = woff + 2 + S::CB * (p % S::QSPLIT);
@@ -291,6 +326,39 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                     q4_k_x4(wreg[i], true, a1, b1, e);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) hi[(4 * i + j) * WP] = e[j];
+                }
+            } else if constexpr (TYPE == kQ5_K) {
+                const int c = (p & 7) >> 1;
+                float a0, b0, a1, b1;
+                q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c, a0, b0);
+                q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c + 1, a1, b1);
+                float* lo = ws + wlds[0];
+                float* hi = ws + wlds[1];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float e[4];
+                    q5_k_x4(wreg[i], wreg[8 + i], 2 * c, false, a0, b0, e);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) lo[(4 * i + j) * WP] = e[j];
+                    q5_k_x4(wreg[i], wreg[8 + i], 2 * c + 1, true, a1, b1, e);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) hi[(4 * i + j) * WP] = e[j];
+                }
+            } else if constexpr (TYPE == kQ6_K) {
+                const int j = p & 3;
+                const float d = half_to_f32(wreg[8]);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int si = (j >> 1) + 2 * qq;  // sub-scale 8hh + si
+                    float a, b;
+                    q6_k_coeffs(wreg[6 + (si >> 2)], si & 3, d, a, b);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        float e[4];
+                        q6_k_x4(wreg[2 * (qq & 1) + i], qq >= 2, wreg[4 + i], qq, a, b, e);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) ws[wlds[qq] + (4 * i + t) * WP] = e[t];
+                    }
                 }
             } else if constexpr (TYPE == kQ8_0) {
                 constexpr int CW = S::CB / 4;
