@@ -653,18 +653,13 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
             r.code[s][0] = v.x;
             r.code[s][1] = v.y;
         } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
-            // code bytes sit at 2-byte alignment inside these blocks
-            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s], 0, 0);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s] + 2, 0, 0);
-            r.code[s][0] = lo | (hi << 16);
+            // code bytes sit at 2-byte alignment inside these blocks; the
+            // dword load relies on the unaligned buffer access of gfx9-class GPUs
+            r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
         } else if constexpr (TYPE == kQ6_K) {
-            // 2-byte aligned super-blocks: low nibbles and high parts in halfwords
-            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s], 0, 0);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code[s] + 2, 0, 0);
-            const uint32_t hlo = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code2[s], 0, 0);
-            const uint32_t hhi = __builtin_amdgcn_raw_buffer_load_b16(wr, o.code2[s] + 2, 0, 0);
-            r.code[s][0] = lo | (hi << 16);
-            r.code[s][1] = hlo | (hhi << 16);
+            // 2-byte aligned super-blocks (unaligned dword loads, as above)
+            r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
+            r.code[s][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code2[s], 0, 0);
         } else {
             r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
             if constexpr (TYPE == kQ5_K) r.code[s][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code2[s], 0, 0);

@@ -236,30 +236,33 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                 wreg[4] = hd.x; wreg[5] = hd.y; wreg[6] = hd.z; wreg[7] = hd.w;
                 wreg[8] = qh.x; wreg[9] = qh.y; wreg[10] = qh.z; wreg[11] = qh.w;
             } else if constexpr (TYPE == kQ6_K) {
-                // 2-byte aligned super-blocks, read in halfwords: ql bytes
-                // 64hh + 8j .. (quarters 0, 2) and 64hh + 32 + 8j .. (1, 3),
-                // qh bytes 128 + 32hh + 8j .., the 8 sub-scales of half hh, d
+                // ql bytes 64hh + 8j .. (quarters 0, 2) and 64hh + 32 + 8j ..
+                // (1, 3), qh bytes 128 + 32hh + 8j .., the 8 sub-scales of half
+                // hh, d. The super-blocks are only 2-byte aligned; the 8-byte
+                // loads rely on the unaligned buffer access of gfx9-class GPUs.
                 const int hh = (p >> 2) & 1, j = p & 3;
                 const uint32_t at[4] = {woff + 64 * hh + 8 * j, woff + 64 * hh + 32 + 8 * j,
                                         woff + 128 + 32 * hh + 8 * j, woff + 192 + 8 * hh};
 #pragma unroll
-                for (int f = 0; f < 4; ++f)
-#pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, at[f] + 4 * w, 0, 0);
-                        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, at[f] + 4 * w + 2, 0, 0);
-                        wreg[2 * f + w] = lo | (hi << 16);
-                    }
+                for (int f = 0; f < 4; ++f) {
+                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, at[f], 0, 0);
+                    wreg[2 * f] = v.x;
+                    wreg[2 * f + 1] = v.y;
+                }
                 wreg[8] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + 208, 0, 0);
-            } else {  // Q8_0, Q4_0: 2-byte aligned blocks, read in halfwords
+            } else {  // Q8_0, Q4_0: 2-byte aligned blocks (unaligned buffer loads)
                 constexpr int CW = S::CB / 4;
                 const uint32_t codes = woff + 2 + S::CB * (p % S::QSPLIT);
                 wreg[CW] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff, 0, 0);
+                if constexpr (CW == 2) {
+                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, codes, 0, 0);
+                    wreg[0] = v.x; wreg[1] = v.y;
+                } else {
 #pragma unroll
-                for (int w = 0; w < CW; ++w) {
-                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(wr, codes + 4 * w, 0, 0);
-                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(wr, codes + 4 * w + 2, 0, 0);
-                    wreg[w] = lo | (hi << 16);
+                    for (int w = 0; w < CW; w += 4) {
+                        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, codes + 4 * w, 0, 0);
+                        wreg[w] = v.x; wreg[w + 1] = v.y; wreg[w + 2] = v.z; wreg[w + 3] = v.w;
+                    }
                 }
             }
         };
