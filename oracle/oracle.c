@@ -37,10 +37,11 @@
  * the GGUF one, and the tests pin the decoder to hand-packed fixtures of that
  * reading and to a full pack bijection, not to values from the pages.
  *
- * Parity unpinned against the pages: Q5_K and Q6_K as a whole. The pages name
- * the K-quant family only through the Q4_K_M files it is used in; these two
- * layouts are the GGUF ones, and the tests pin them to hand-derived fixtures
- * and to their structural relations with Q4_K, not to values from the pages.
+ * Parity unpinned against the pages: Q2_K, Q3_K, Q5_K and Q6_K as a whole.
+ * The pages name the K-quant family only through the Q4_K_M files it is
+ * used in; these layouts are the GGUF ones, and the tests pin them to
+ * hand-derived fixtures and to structural relations, not to values from the
+ * pages.
  */
 #include <math.h>
 #include <pthread.h>
@@ -48,7 +49,10 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_BF16 = 30 };
+enum {
+    T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8, T_Q2_K = 10, T_Q3_K = 11, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14,
+    T_BF16 = 30
+};
 
 /* IEEE-754 binary16 -> binary32: 1 sign bit, 5 exponent bits (bias 15), 10
  * fraction bits. Exponent 0: subnormal, value = frac * 2^-24. Exponent 31:
@@ -229,6 +233,60 @@ int oracle_decode_row(int type, const uint8_t *row, int64_t K, float *out) {
             }
         }
         return 0;
+    case T_Q2_K:
+        /* 84-byte super-block of 256 elements: 16 bytes of 4-bit sub-scale
+         * (low nibble) / sub-min (high nibble) pairs, 64 bytes qs of 2-bit
+         * codes, fp16 d, fp16 dmin. Element e lies in half h = e / 128,
+         * quarter p = (e % 128) / 32, at l = e % 32: its code is bits 2p and
+         * 2p + 1 of qs[32h + l], its pair is byte 8h + 2p + l / 16.
+         * value = (d * sc) * q - (dmin * m) with q in 0..3: each product
+         * exact in F32, one rounding in the subtraction. */
+        if (K % 256) return -1;
+        for (b = 0; b < K / 256; b++) {
+            const uint8_t *blk = row + 84 * b;
+            const uint8_t *pairs = blk, *qs = blk + 16;
+            float d = oracle_half_to_float(rd16(blk + 80));
+            float dmin = oracle_half_to_float(rd16(blk + 82));
+            for (int e = 0; e < 256; e++) {
+                int h = e / 128, p = (e % 128) / 32, l = e % 32;
+                int q = (qs[32 * h + l] >> (2 * p)) & 3;
+                int pair = pairs[8 * h + 2 * p + l / 16];
+                float a = d * (float)(pair & 15);
+                float mm = dmin * (float)(pair >> 4);
+                float v = a * (float)q;
+                out[256 * b + e] = v - mm;
+            }
+        }
+        return 0;
+    case T_Q3_K:
+        /* 110-byte super-block of 256 elements: 32 bytes hmask, 64 bytes qs
+         * of 2-bit codes, 12 bytes of sixteen 6-bit sub-scales, fp16 d.
+         * Element e lies in half h = e / 128, quarter p = (e % 128) / 32, at
+         * l = e % 32: its low 2 bits are bits 2p, 2p + 1 of qs[32h + l]; bit
+         * 4h + p of hmask[l] set means q = low, clear means q = low - 4 (q in
+         * -4..3); its sub-scale is number 8h + 2p + l / 16. Sub-scale s
+         * (0..15), with i = s % 4 and g = s / 4: low 4 bits are the low
+         * (g < 2) or high (g >= 2) nibble of field byte 4 (g % 2) + i, high 2
+         * bits are bits 2g, 2g + 1 of field byte 8 + i; it counts from -32.
+         * value = (d * (sc - 32)) * q: at most 11 + 6 + 3 bits, exact. */
+        if (K % 256) return -1;
+        for (b = 0; b < K / 256; b++) {
+            const uint8_t *blk = row + 110 * b;
+            const uint8_t *hmask = blk, *qs = blk + 32, *f = blk + 96;
+            float d = oracle_half_to_float(rd16(blk + 108));
+            for (int e = 0; e < 256; e++) {
+                int h = e / 128, p = (e % 128) / 32, l = e % 32;
+                int low = (qs[32 * h + l] >> (2 * p)) & 3;
+                int q = (hmask[l] >> (4 * h + p)) & 1 ? low : low - 4;
+                int s = 8 * h + 2 * p + l / 16, i = s % 4, g = s / 4;
+                int nib = f[4 * (g % 2) + i];
+                nib = g < 2 ? (nib & 15) : (nib >> 4);
+                int sc = nib | (((f[8 + i] >> (2 * g)) & 3) << 4);
+                float a = d * (float)(sc - 32);
+                out[256 * b + e] = a * (float)q;
+            }
+        }
+        return 0;
     default:
         return -1;
     }
@@ -240,6 +298,8 @@ int64_t oracle_row_bytes(int type, int64_t K) {
     case T_F16: case T_BF16: return 2 * K;
     case T_Q8_0: return K % 32 ? -1 : K / 32 * 34;
     case T_Q4_0: return K % 32 ? -1 : K / 32 * 18;
+    case T_Q2_K: return K % 256 ? -1 : K / 256 * 84;
+    case T_Q3_K: return K % 256 ? -1 : K / 256 * 110;
     case T_Q4_K: return K % 256 ? -1 : K / 256 * 144;
     case T_Q5_K: return K % 256 ? -1 : K / 256 * 176;
     case T_Q6_K: return K % 256 ? -1 : K / 256 * 210;

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads as wl
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K, wl.Q5_K, wl.Q6_K]
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K]
 
 
 def hexbytes(tokens):
@@ -278,6 +278,141 @@ def test_q6_k_products_are_exact():
     got = oracle.dequantize(wl.Q6_K, q6_k_superblock(0x3FFF, [127] * 16, ql, qh), 256)[0]
     assert np.all(got == np.float32(2047 * 127 * -31 / 1024))
     assert 2047 * 127 * 31 < 2 ** 24
+
+
+def q2_k_superblock(d_bits, dmin_bits, pairs, qs):
+    blk = np.zeros(84, dtype=np.uint8)
+    blk[0:16] = pairs
+    blk[16:80] = qs
+    blk[80:82] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
+    blk[82:84] = np.array([dmin_bits & 255, dmin_bits >> 8], dtype=np.uint8)
+    return blk
+
+
+def pack_q3_k_field(sc):
+    """Sixteen 6-bit Q3_K sub-scales into the 12-byte field, written for the
+    tests from the layout description (the oracle only unpacks)."""
+    f = [0] * 12
+    for s_, v in enumerate(sc):
+        i, g = s_ % 4, s_ // 4
+        f[4 * (g % 2) + i] |= (v & 15) << (4 * (g // 2))
+        f[8 + i] |= ((v >> 4) & 3) << (2 * g)
+    return np.array(f, dtype=np.uint8)
+
+
+def q3_k_superblock(d_bits, hmask, qs, field):
+    blk = np.zeros(110, dtype=np.uint8)
+    blk[0:32] = hmask
+    blk[32:96] = qs
+    blk[96:108] = field
+    blk[108:110] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
+    return blk
+
+
+def test_q2_k_hand_built_superblock(golden):
+    g = golden("q2_k_block.txt")
+    qs = ((np.arange(64) * 37 + 11) & 255).astype(np.uint8)
+    got = oracle.dequantize(wl.Q2_K, q2_k_superblock(0x3C00, 0x3C00, hexbytes(g["pairs_hex"]), qs), 256)[0]
+    for item in g["spot_checks"]:
+        e, v = item.split("=")
+        assert got[int(e)] == float(v), item
+
+
+def test_q2_k_structure():
+    """d = dmin = 1 and every pair (sc, m) = (1, 0): a code value v in bits
+    2p, 2p + 1 of one qs byte makes exactly one element v, and the 256 (byte,
+    p) positions reach the 256 elements one to one. Then each pair byte, set
+    alone to (sc, m) = (3, 5), changes exactly its 16 elements to 3q - 5."""
+    base_pairs = np.full(16, 0x01, np.uint8)
+    zero = oracle.dequantize(wl.Q2_K, q2_k_superblock(0x3C00, 0x3C00, base_pairs, np.zeros(64, np.uint8)), 256)[0]
+    assert np.all(zero == 0)
+    seen = set()
+    for i in range(64):
+        for p in range(4):
+            for v in (1, 2, 3):
+                qs = np.zeros(64, np.uint8)
+                qs[i] = v << (2 * p)
+                got = oracle.dequantize(wl.Q2_K, q2_k_superblock(0x3C00, 0x3C00, base_pairs, qs), 256)[0]
+                moved = np.nonzero(got)[0]
+                assert len(moved) == 1 and got[moved[0]] == v, (i, p, v)
+            seen.add(int(moved[0]))
+    assert seen == set(range(256))
+    qs = ((np.arange(64) * 37 + 11) & 255).astype(np.uint8)
+    base = oracle.dequantize(wl.Q2_K, q2_k_superblock(0x3C00, 0x3C00, base_pairs, qs), 256)[0]
+    for j in range(16):
+        pairs = base_pairs.copy()
+        pairs[j] = 3 | (5 << 4)
+        got = oracle.dequantize(wl.Q2_K, q2_k_superblock(0x3C00, 0x3C00, pairs, qs), 256)[0]
+        h, p, s_ = j // 8, (j % 8) // 2, j % 2
+        idx = 128 * h + 32 * p + 16 * s_ + np.arange(16)
+        assert np.array_equal(got[idx], 3 * base[idx] - 5)
+        rest = np.setdiff1d(np.arange(256), idx)
+        assert np.array_equal(got[rest], base[rest])
+
+
+def test_q3_k_field_packer_matches_hand_packing(golden):
+    g = golden("q3_k_block.txt")
+    assert np.array_equal(pack_q3_k_field([int(v) for v in g["sc"]]), hexbytes(g["field_hex"]))
+
+
+def test_q3_k_hand_built_superblock(golden):
+    g = golden("q3_k_block.txt")
+    hmask = ((np.arange(32) * 29 + 5) & 255).astype(np.uint8)
+    qs = ((np.arange(64) * 37 + 11) & 255).astype(np.uint8)
+    got = oracle.dequantize(wl.Q3_K, q3_k_superblock(0x3C00, hmask, qs, hexbytes(g["field_hex"])), 256)[0]
+    for item in g["spot_checks"]:
+        e, v = item.split("=")
+        assert got[int(e)] == float(v), item
+
+
+def test_q3_k_sub_scale_bijection_every_value_every_position():
+    """Every 6-bit value at each of the 16 positions, the other 15 positions
+    holding other values: packed (test side), decoded (oracle) with every
+    code 1 (low = 1, mask bit set), so element values are sc - 32."""
+    hmask = np.full(32, 0xFF, np.uint8)
+    qs = np.full(64, 0x55, np.uint8)
+    for pos in range(16):
+        for v in range(64):
+            sc = [(v + 7 * k + 1) % 64 for k in range(16)]
+            sc[pos] = v
+            got = oracle.dequantize(wl.Q3_K, q3_k_superblock(0x3C00, hmask, qs, pack_q3_k_field(sc)), 256)[0]
+            for k in range(16):
+                h, p, s_ = k // 8, (k % 8) // 2, k % 2
+                idx = 128 * h + 32 * p + 16 * s_ + np.arange(16)
+                assert np.all(got[idx] == sc[k] - 32), (pos, v, k)
+
+
+def test_q3_k_mask_bits_and_codes():
+    """Sub-scales all 33 (factor 1), codes 0: every element is -4 with an
+    empty mask. Each mask bit b of hmask[l], set alone, lifts exactly one
+    element to 0: element 128 (b // 4) + 32 (b % 4) + l; each 2-bit code,
+    with the full mask, adds its value to exactly one element."""
+    field = pack_q3_k_field([33] * 16)
+    got = oracle.dequantize(wl.Q3_K, q3_k_superblock(0x3C00, np.zeros(32, np.uint8), np.zeros(64, np.uint8), field),
+                            256)[0]
+    assert np.all(got == -4)
+    seen = set()
+    for l in range(32):
+        for b in range(8):
+            hm = np.zeros(32, np.uint8)
+            hm[l] = 1 << b
+            got = oracle.dequantize(wl.Q3_K, q3_k_superblock(0x3C00, hm, np.zeros(64, np.uint8), field), 256)[0]
+            moved = np.nonzero(got != -4)[0]
+            assert len(moved) == 1 and got[moved[0]] == 0, (l, b)
+            assert moved[0] == 128 * (b // 4) + 32 * (b % 4) + l, (l, b)
+            seen.add(int(moved[0]))
+    assert seen == set(range(256))
+    full = np.full(32, 0xFF, np.uint8)
+    seen = set()
+    for i in range(64):
+        for p in range(4):
+            qs = np.zeros(64, np.uint8)
+            qs[i] = 3 << (2 * p)
+            got = oracle.dequantize(wl.Q3_K, q3_k_superblock(0x3C00, full, qs, field), 256)[0]
+            moved = np.nonzero(got)[0]
+            assert len(moved) == 1 and got[moved[0]] == 3, (i, p)
+            seen.add(int(moved[0]))
+    assert seen == set(range(256))
 
 
 @pytest.mark.parametrize("variant", ["same", "shifted"])

@@ -20,6 +20,10 @@ blocks; fp16 fields are little-endian; GGUF block formats):
         bits between the 12-byte field and the 128 bytes of low nibbles
   Q6_K  210 bytes per 256 elements: 128 bytes of low nibbles, 64 bytes of
         2-bit high parts, 16 signed 8-bit sub-scales, fp16 scale
+  Q2_K  84 bytes per 256 elements: 16 bytes of 4-bit sub-scale/sub-min
+        pairs, 64 bytes of 2-bit codes, fp16 scale, fp16 min-scale
+  Q3_K  110 bytes per 256 elements: 32 bytes of high-bit masks, 64 bytes of
+        2-bit codes, 12 bytes of sixteen 6-bit sub-scales, fp16 scale
 
 Distributions (uniform ranges are [lo, hi) for floats and inclusive for
 integers; N(0, s) takes s as the standard deviation):
@@ -31,6 +35,10 @@ integers; N(0, s) takes s as the standard deviation):
   Q5_K  as Q4_K, codes U{0..31}
   Q6_K  scale U[1e-4, 1e-3) rounded to fp16, sub-scales U{-128..127},
         codes U{0..63}
+  Q2_K  scale and min-scale U[1e-3, 1e-2) rounded to fp16, sub-scales and
+        sub-mins U{0..15}, codes U{0..3}
+  Q3_K  scale U[1e-3, 1e-2) rounded to fp16, sub-scales U{0..63} (-32
+        offset applied in decoding), codes U{-4..3}
   dense W ~ N(0, 0.02) in F32, then rounded to F16 or BF16 (nearest-even)
   G     ~ N(0, sigma) in F32
 
@@ -42,7 +50,8 @@ sub-scale and sub-min whatever the bit order of the pack.
 
 Draw order for one case, from numpy Generator(PCG64(seed)): scales (the
 scale, then the K-quant min-scale), then the sub-scale field, then codes
-(Q5_K: fifth bits, then low nibbles; Q6_K: low nibbles, then high parts) or
+(Q5_K: fifth bits, then low nibbles; Q6_K: low nibbles, then high parts;
+Q2_K: codes after its 16 pair bytes; Q3_K: high-bit masks, then low bits) or
 the dense values, then G. Codes of several bits are drawn as uniform bytes
 of their bit fields, which makes every code uniform over its range.
 """
@@ -52,15 +61,15 @@ from __future__ import annotations
 import numpy as np
 
 # GGUF tensor-type ids
-F32, F16, Q4_0, Q8_0, Q4_K, Q5_K, Q6_K, BF16 = 0, 1, 2, 8, 12, 13, 14, 30
+F32, F16, Q4_0, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16 = 0, 1, 2, 8, 10, 11, 12, 13, 14, 30
 
-TYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0", Q4_0: "q4_0", Q4_K: "q4_k", Q5_K: "q5_k",
-              Q6_K: "q6_k"}
+TYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0", Q4_0: "q4_0", Q2_K: "q2_k", Q3_K: "q3_k",
+              Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k"}
 TYPE_IDS = {v: k for k, v in TYPE_NAMES.items()}
 
 # (elements per block, bytes per block)
 _GEOMETRY = {F32: (1, 4), F16: (1, 2), BF16: (1, 2), Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144),
-             Q5_K: (256, 176), Q6_K: (256, 210)}
+             Q5_K: (256, 176), Q6_K: (256, 210), Q2_K: (256, 84), Q3_K: (256, 110)}
 
 
 def block_geometry(wtype: int) -> tuple[int, int]:
@@ -139,6 +148,24 @@ def make_weight(wtype: int, N: int, K: int, rng: np.random.Generator) -> np.ndar
         out[:, :, 128:192] = qh
         out[:, :, 192:208] = scales
         out[:, :, 208:210] = d.view(np.uint8).reshape(N, nb, 2)
+    elif wtype == Q2_K:
+        d = _fp16_uniform(rng, 1e-3, 1e-2, (N, nb))
+        dmin = _fp16_uniform(rng, 1e-3, 1e-2, (N, nb))
+        pairs = rng.integers(0, 256, size=(N, nb, 16), dtype=np.uint8)
+        qs = rng.integers(0, 256, size=(N, nb, 64), dtype=np.uint8)
+        out[:, :, 0:16] = pairs
+        out[:, :, 16:80] = qs
+        out[:, :, 80:82] = d.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 82:84] = dmin.view(np.uint8).reshape(N, nb, 2)
+    elif wtype == Q3_K:
+        d = _fp16_uniform(rng, 1e-3, 1e-2, (N, nb))
+        field = rng.integers(0, 256, size=(N, nb, 12), dtype=np.uint8)
+        hmask = rng.integers(0, 256, size=(N, nb, 32), dtype=np.uint8)
+        qs = rng.integers(0, 256, size=(N, nb, 64), dtype=np.uint8)
+        out[:, :, 0:32] = hmask
+        out[:, :, 32:96] = qs
+        out[:, :, 96:108] = field
+        out[:, :, 108:110] = d.view(np.uint8).reshape(N, nb, 2)
     else:
         raise ValueError(f"unknown weight type {wtype}")
     return out.reshape(N, rb)
