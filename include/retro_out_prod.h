@@ -41,8 +41,18 @@
  *               128h + 32p + l: nibble of byte 64h + 32(p%2) + l (high
  *               nibble for p >= 2), bits 2p..2p+1 of byte 128 + 32h + l,
  *               sub-scale 8h + 2p + l/16; value (d*sc)*(q-32)
- * The Q5_K and Q6_K layouts are the GGUF ones: the pages that define this
- * operation name the K-quant family only through the Q4_K_M files it runs on.
+ *   RETRO_Q2_K  84 bytes / 256 elements: 16 pair bytes (4-bit sub-scale | 4-bit
+ *               sub-min << 4), 64 bytes of 2-bit codes, fp16 d, fp16 dmin;
+ *               element 128h + 32p + l: bits 2p..2p+1 of byte 16 + 32h + l,
+ *               pair 8h + 2p + l/16; value (d*sc)*q - dmin*m
+ *   RETRO_Q3_K  110 bytes / 256 elements: 32 bytes hmask, 64 bytes of 2-bit
+ *               codes, 12 bytes of sixteen 6-bit sub-scales, fp16 d; element
+ *               128h + 32p + l: bits 2p..2p+1 of byte 32 + 32h + l, minus 4
+ *               unless bit 4h+p of hmask[l] is set, sub-scale 8h + 2p + l/16
+ *               (stored with +32); value (d*(sc-32))*q
+ * The Q2_K, Q3_K, Q5_K and Q6_K layouts are the GGUF ones: the pages that
+ * define this operation name the K-quant family only through the Q4_K_M
+ * files it runs on.
  *
  * Pointers: W, G and dst are device pointers (hipMalloc'd or equivalent) and
  * must be 16-byte aligned. dst must not overlap W or G. stream is a
@@ -73,6 +83,8 @@ enum {
     RETRO_F16 = 1,
     RETRO_Q4_0 = 2,
     RETRO_Q8_0 = 8,
+    RETRO_Q2_K = 10,
+    RETRO_Q3_K = 11,
     RETRO_Q4_K = 12,
     RETRO_Q5_K = 13,
     RETRO_Q6_K = 14,
@@ -98,12 +110,12 @@ enum {
 
 /*
  * dst[t][k] = sum_n W[n][k] * G[t][n] for t < T, k < K.
- *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_K/Q5_K/Q6_K
+ *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q2_K/Q3_K/Q4_K/Q5_K/Q6_K
  *   W       device, N * retro_row_bytes(type, K) bytes
  *   G       device, T * N floats
  *   dst     device, T * K floats, overwritten
  *   K       elements per W row (a multiple of the block: 32 for Q8_0/Q4_0,
- *           256 for Q4_K/Q5_K/Q6_K, 1 otherwise)
+ *           256 for the K-quants Q2_K..Q6_K, 1 otherwise)
  *   N       rows of W = the reduction length
  *   T       rows of G and dst
  * T == 0 or K == 0: returns RETRO_OK without touching memory (pointers may
@@ -132,8 +144,8 @@ int retro_dequantize(int type, const void *W, float *out, int64_t K, int64_t N, 
  */
 int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T);
 
-/* Bytes per W row: K/32*34 (Q8_0), K/32*18 (Q4_0), K/256*144 (Q4_K),
- * K/256*176 (Q5_K), K/256*210 (Q6_K), 4K
+/* Bytes per W row: K/32*34 (Q8_0), K/32*18 (Q4_0), K/256*84 (Q2_K),
+ * K/256*110 (Q3_K), K/256*144 (Q4_K), K/256*176 (Q5_K), K/256*210 (Q6_K), 4K
  * (F32), 2K (F16, BF16). -1 for an unknown type, a negative K or a K that is
  * not a whole number of blocks. Touches no device. */
 int64_t retro_row_bytes(int type, int64_t K);
@@ -147,8 +159,8 @@ const char *retro_strerror(int code);
  *   RETRO_VARIANT_SKINNY    one pass over W, all of n per workgroup; T <= 16
  *   RETRO_VARIANT_TILE_*    tiled F32-MFMA kernel, tile = rows of T x columns
  *                           of K per workgroup (256-column tiles need K tiles
- *                           that are whole K-quant super-blocks; Q4_K, Q5_K and
- *                           Q6_K take only
+ *                           that are whole K-quant super-blocks; the K-quants
+ *                           take only
  *                           those)
  *   RETRO_VARIANT_WS_*      the same tiles computed by a workgroup whose
  *                           waves are split into MFMA (consumer) and load/

@@ -45,6 +45,8 @@ bool geometry(int type, Geometry& g) {
         case RETRO_Q4_0: g = {32, 18}; return true;
         case RETRO_Q4_K: g = {256, 144}; return true;
         case RETRO_Q5_K: g = {256, 176}; return true;
+        case RETRO_Q2_K: g = {256, 84}; return true;
+        case RETRO_Q3_K: g = {256, 110}; return true;
         case RETRO_Q6_K: g = {256, 210}; return true;
         default: return false;
     }
@@ -315,6 +317,8 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         case RETRO_Q4_0: return launch_variant<kQ4_0>(variant, W, G, dst, K, N, T, st);
         case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, st);
         case RETRO_Q5_K: return launch_variant<kQ5_K>(variant, W, G, dst, K, N, T, st);
+        case RETRO_Q2_K: return launch_variant<kQ2_K>(variant, W, G, dst, K, N, T, st);
+        case RETRO_Q3_K: return launch_variant<kQ3_K>(variant, W, G, dst, K, N, T, st);
         case RETRO_Q6_K: return launch_variant<kQ6_K>(variant, W, G, dst, K, N, T, st);
         default: return RETRO_E_TYPE;
     }
@@ -368,6 +372,8 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
         case RETRO_Q4_0: return launch_dequant<kQ4_0>(W, out, K, N, st);
         case RETRO_Q4_K: return launch_dequant<kQ4_K>(W, out, K, N, st);
         case RETRO_Q5_K: return launch_dequant<kQ5_K>(W, out, K, N, st);
+        case RETRO_Q2_K: return launch_dequant<kQ2_K>(W, out, K, N, st);
+        case RETRO_Q3_K: return launch_dequant<kQ3_K>(W, out, K, N, st);
         case RETRO_Q6_K: return launch_dequant<kQ6_K>(W, out, K, N, st);
         default: return RETRO_E_TYPE;
     }

@@ -7,10 +7,13 @@
 // Exactness: a Q8_0/Q4_0 value d*q needs at most 11+8 significant bits, a
 // Q4_K product (d*sc)*q at most 11+6+4 = 21 (Q5_K: 22) and dmin*m at most 17,
 // so every product below is exact in float32 and only the Q4_K/Q5_K
-// subtraction rounds (once, to nearest-even). A Q6_K value (d*sc)*(q - 32)
-// has odd parts of at most 11, 7 and 5 bits, so it is exact, and so is its
-// form a*q - 32a (a*q needs at most 24 bits). Whether the compiler fuses
-// a*q - b into an FMA therefore changes no bit.
+// subtraction rounds (once, to nearest-even); Q2_K (d*sc)*q needs at most
+// 11+4+2 bits and rounds likewise only in its subtraction. A Q6_K value
+// (d*sc)*(q - 32) has odd parts of at most 11, 7 and 5 bits, so it is exact,
+// and so is its form a*q - 32a (a*q needs at most 24 bits); a Q3_K value
+// (d*(sc-32))*q needs at most 11+6+3 bits and its form a*q' - 4a (q' = q+4)
+// is exact too. Whether the compiler fuses a*q - b into an FMA therefore
+// changes no bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,7 +22,9 @@
 namespace retro {
 
 // GGUF tensor-type ids.
-enum : int { kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ8_0 = 8, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14, kBF16 = 30 };
+enum : int {
+    kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ8_0 = 8, kQ2_K = 10, kQ3_K = 11, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14, kBF16 = 30
+};
 
 // kBlock: elements per block; kBytes: bytes per block; kGroup: elements one
 // thread decodes from one 16-byte code load in the tiled kernel.
@@ -32,6 +37,8 @@ template <> struct Format<kQ4_0> { static constexpr int kBlock = 32,  kBytes = 1
 template <> struct Format<kQ4_K> { static constexpr int kBlock = 256, kBytes = 144, kGroup = 32; };
 template <> struct Format<kQ5_K> { static constexpr int kBlock = 256, kBytes = 176, kGroup = 32; };
 template <> struct Format<kQ6_K> { static constexpr int kBlock = 256, kBytes = 210, kGroup = 32; };
+template <> struct Format<kQ2_K> { static constexpr int kBlock = 256, kBytes = 84,  kGroup = 32; };
+template <> struct Format<kQ3_K> { static constexpr int kBlock = 256, kBytes = 110, kGroup = 32; };
 
 // The K-quant formats: 256-element super-blocks, so a tile of K holds whole
 // super-blocks only when it is 256 columns wide.
@@ -147,6 +154,47 @@ __device__ __forceinline__ void q6_k_coeffs(uint32_t scales, int i, float d, flo
     const int sc = static_cast<int>(static_cast<int8_t>((scales >> (8 * i)) & 0xFFu));
     a = d * static_cast<float>(sc);
     b = -32.0f * a;
+}
+
+// Q2_K: the 2-bit codes at bits 2p, 2p+1 of four qs bytes; value a*q - b
+// with a = d*sc, b = dmin*m of the element's pair byte.
+__device__ __forceinline__ void q2_k_x4(uint32_t qs, int p, float a, float b, float out[4]) {
+    const uint32_t m = (qs >> (2 * p)) & 0x03030303u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) - b;
+}
+
+// Q2_K pair byte `i` (0..3) of a word (sub-scale low nibble, sub-min high).
+__device__ __forceinline__ void q2_k_coeffs(uint32_t pairs, int i, float d, float dmin, float& a, float& b) {
+    const uint32_t pr = (pairs >> (8 * i)) & 0xFFu;
+    a = d * static_cast<float>(pr & 15u);
+    b = dmin * static_cast<float>(pr >> 4);
+}
+
+// Q3_K sub-scale s (0..15, stored 0..63) from the 12-byte field given as
+// its little-endian words f0, f1, f2. With i = s % 4, g = s / 4: low 4 bits
+// are the low (g < 2) or high nibble of byte 4 (g % 2) + i, high 2 bits are
+// bits 2g, 2g+1 of byte 8 + i.
+__device__ __forceinline__ uint32_t q3_k_scale(uint32_t f0, uint32_t f1, uint32_t f2, int s) {
+    const int i = s & 3, g = s >> 2;
+    const uint32_t lo = (((g & 1) ? f1 : f0) >> (8 * i + 4 * (g >> 1))) & 15u;
+    return lo | (((f2 >> (8 * i + 2 * g)) & 3u) << 4);
+}
+
+// Q3_K: low 2 bits at bits 2p, 2p+1 of four qs bytes, plus 4 where bit
+// `hbit` of the four hmask bytes is set (q' = q + 4 in 0..7); value
+// a*q' + b with a = d*(sc - 32), b = -4a.
+__device__ __forceinline__ void q3_k_x4(uint32_t qs, uint32_t hm, int p, int hbit, float a, float b,
+                                        float out[4]) {
+    const uint32_t m = ((qs >> (2 * p)) & 0x03030303u) | (((hm >> hbit) & 0x01010101u) << 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) + b;
+}
+
+__device__ __forceinline__ void q3_k_coeffs(uint32_t f0, uint32_t f1, uint32_t f2, int s, float d, float& a,
+                                            float& b) {
+    a = d * static_cast<float>(static_cast<int>(q3_k_scale(f0, f1, f2, s)) - 32);
+    b = -4.0f * a;
 }
 
 }  // namespace retro

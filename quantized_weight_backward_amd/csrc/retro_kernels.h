@@ -96,7 +96,8 @@ struct TileArgs {
 template <int TYPE>
 __device__ __forceinline__ int lds_swizzle(int col) {
     if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) return col ^ (((col >> 6) & 3) << 2);
-    if constexpr (TYPE == kQ4_0 || TYPE == kQ6_K) return col ^ (((col >> 5) & 7) << 2);
+    if constexpr (TYPE == kQ4_0 || TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K)
+        return col ^ (((col >> 5) & 7) << 2);
     if constexpr (TYPE == kQ8_0) return col ^ (((col >> 5) & 3) << 2);
     return col;
 }
@@ -365,6 +366,51 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                                 make_float4(e[0], e[1], e[2], e[3]);
                         }
                     }
+                } else if constexpr (TYPE == kQ2_K || TYPE == kQ3_K) {
+                    // group (half hh, l range 8j .. 8j + 7) of super-block sb:
+                    // elements 128 hh + 32 p + 8j + 0..7 of the four quarters p,
+                    // whose 2-bit codes share the 8 qs bytes 32hh + 8j ..
+                    const int sb = g >> 3, hh = (g >> 2) & 1, j = g & 3;
+                    const uint8_t* blk = raw + Format<TYPE>::kBytes * sb;
+                    constexpr int QS = (TYPE == kQ2_K) ? 16 : 32;
+                    const uint32_t qw[2] = {lds_word_a2(blk + QS + 32 * hh + 8 * j),
+                                            lds_word_a2(blk + QS + 32 * hh + 8 * j + 4)};
+                    uint32_t aux[2] = {0u, 0u}, f0 = 0, f1 = 0, f2 = 0;
+                    float d = 0.f, dmin = 0.f;
+                    if constexpr (TYPE == kQ2_K) {
+                        aux[0] = lds_word_a2(blk + 8 * hh);
+                        aux[1] = lds_word_a2(blk + 8 * hh + 4);
+                        const uint32_t dd = lds_word_a2(blk + 80);
+                        d = half_to_f32(dd & 0xFFFFu);
+                        dmin = half_to_f32(dd >> 16);
+                    } else {
+                        aux[0] = lds_word_a2(blk + 8 * j);  // hmask bytes 8j ..
+                        aux[1] = lds_word_a2(blk + 8 * j + 4);
+                        f0 = lds_word_a2(blk + 96);
+                        f1 = lds_word_a2(blk + 100);
+                        f2 = lds_word_a2(blk + 104);
+                        d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk + 108));
+                    }
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const int si = (j >> 1) + 2 * qq;  // pair / sub-scale 8 hh + si
+                        float a, b;
+                        if constexpr (TYPE == kQ2_K)
+                            q2_k_coeffs(aux[si >> 2], si & 3, d, dmin, a, b);
+                        else
+                            q3_k_coeffs(f0, f1, f2, 8 * hh + si, d, a, b);
+                        const int col = 256 * sb + 128 * hh + 32 * qq + 8 * j;
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            float e[4];
+                            if constexpr (TYPE == kQ2_K)
+                                q2_k_x4(qw[i], qq, a, b, e);
+                            else
+                                q3_k_x4(qw[i], aux[i], qq, 4 * hh + qq, a, b, e);
+                            *reinterpret_cast<float4*>(brow + S::swz(col + 4 * i)) =
+                                make_float4(e[0], e[1], e[2], e[3]);
+                        }
+                    }
                 } else if constexpr (TYPE == kQ4_0) {
                     const uint8_t* blk = raw + 18 * g;
                     const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
@@ -538,6 +584,26 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         const uint32_t qh = *reinterpret_cast<const uint32_t*>(sbp + 16 + (r & 31));
         const uint32_t qs = *reinterpret_cast<const uint32_t*>(sbp + 48 + 32 * c + (r & 31));
         q5_k_x4(qs, qh, 2 * c + (high ? 1 : 0), high, a, b, e);
+    } else if constexpr (TYPE == kQ2_K) {  // 4-byte aligned super-blocks
+        const uint8_t* sbp = row + (k >> 8) * 84;
+        const int e256 = k & 255, h = e256 >> 7, p = (e256 >> 5) & 3, l = e256 & 31;
+        const int pi = 8 * h + 2 * p + (l >> 4);
+        const uint32_t dd = *reinterpret_cast<const uint32_t*>(sbp + 80);
+        float a, b;
+        q2_k_coeffs(*reinterpret_cast<const uint32_t*>(sbp + (pi & ~3)), pi & 3, half_to_f32(dd & 0xFFFFu),
+                    half_to_f32(dd >> 16), a, b);
+        q2_k_x4(*reinterpret_cast<const uint32_t*>(sbp + 16 + 32 * h + l), p, a, b, e);
+    } else if constexpr (TYPE == kQ3_K) {  // 2-byte aligned super-blocks
+        const uint8_t* sbp = row + (k >> 8) * 110;
+        const int e256 = k & 255, h = e256 >> 7, p = (e256 >> 5) & 3, l = e256 & 31;
+        const uint16_t* f = reinterpret_cast<const uint16_t*>(sbp + 96);
+        const uint32_t f0 = f[0] | (uint32_t(f[1]) << 16), f1 = f[2] | (uint32_t(f[3]) << 16),
+                       f2 = f[4] | (uint32_t(f[5]) << 16);
+        float a, b;
+        q3_k_coeffs(f0, f1, f2, 8 * h + 2 * p + (l >> 4), half_to_f32(f[6]), a, b);
+        const uint16_t* qs = reinterpret_cast<const uint16_t*>(sbp + 32 + 32 * h + l);
+        const uint16_t* hm = reinterpret_cast<const uint16_t*>(sbp + l);
+        q3_k_x4(qs[0] | (uint32_t(qs[1]) << 16), hm[0] | (uint32_t(hm[1]) << 16), p, 4 * h + p, a, b, e);
     } else {  // kQ6_K: 2-byte aligned super-blocks
         const uint8_t* sbp = row + (k >> 8) * 210;
         const int e256 = k & 255, h = e256 >> 7, p = (e256 >> 5) & 3, l = e256 & 31;
@@ -557,8 +623,12 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
 // (row, block) scale this lane decodes for the whole wave, and 4 G values.
 template <int TYPE>
 struct SkinnyRaw {
-    static constexpr int CW = (TYPE == kF32) ? 4 : (TYPE == kF16 || TYPE == kBF16 || TYPE == kQ5_K || TYPE == kQ6_K) ? 2 : 1;
-    static constexpr int HW = (TYPE == kQ4_K || TYPE == kQ5_K) ? 4 : (TYPE == kQ6_K) ? 2 : 1;
+    static constexpr int CW = (TYPE == kF32) ? 4
+                              : (TYPE == kF16 || TYPE == kBF16 || TYPE == kQ5_K || TYPE == kQ6_K || TYPE == kQ3_K) ? 2
+                                                                                                            : 1;
+    static constexpr int HW = (TYPE == kQ4_K || TYPE == kQ5_K || TYPE == kQ3_K) ? 4
+                              : (TYPE == kQ6_K || TYPE == kQ2_K)                ? 2
+                                                                                : 1;
     uint32_t code[4][CW];
     uint32_t hdr[HW];
     float g[4];
@@ -570,8 +640,8 @@ struct SkinnyRaw {
 struct SkinnyOffsets {
     uint32_t code[4];   // code words of rows 4*(l/16) + s, columns k0 + 4*(l%16) ..
     uint32_t code2[4];  // Q5_K fifth bits / Q6_K high parts of the same elements
-    uint32_t hdr;       // header of the scale pair this lane decodes (Q6_K: its sub-scale pair)
-    uint32_t hdr2;      // Q6_K: the scale d of that row
+    uint32_t hdr;       // header of the scale pair this lane decodes (Q6_K, Q2_K, Q3_K: see skinny_offsets)
+    uint32_t hdr2;      // Q6_K, Q2_K: the scales of that row
     uint32_t g;         // G[min(l%16, T-1)][4*(l/16)] (bytes from G + n0)
 };
 
@@ -599,10 +669,17 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
         const int e = kl & 255;
         col = (kl >> 8) * 176 + 48 + 32 * (e >> 6) + (e & 31);
         col2 = (kl >> 8) * 176 + 16 + (e & 31);
-    } else {  // kQ6_K
+    } else if constexpr (TYPE == kQ6_K) {
         const int e = kl & 255, h = e >> 7, p = (e >> 5) & 3, l = e & 31;
         col = (kl >> 8) * 210 + 64 * h + 32 * (p & 1) + l;
         col2 = (kl >> 8) * 210 + 128 + 32 * h + l;
+    } else if constexpr (TYPE == kQ2_K) {
+        const int e = kl & 255, h = e >> 7, l = e & 31;
+        col = (kl >> 8) * 84 + 16 + 32 * h + l;
+    } else {  // kQ3_K
+        const int e = kl & 255, h = e >> 7, l = e & 31;
+        col = (kl >> 8) * 110 + 32 + 32 * h + l;
+        col2 = (kl >> 8) * 110 + l;
     }
     SkinnyOffsets o;
 #pragma unroll
@@ -617,14 +694,23 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
     if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) hcol = (min(k0 + 32 * sel, K - 32) >> 5) * Format<TYPE>::kBytes;
     o.hdr = uint32_t(hr * a.pitch) + hcol;
     o.hdr2 = 0;
-    if constexpr (TYPE == kQ6_K) {
-        // lane -> (row lane / 4, sub-scale 8h + 2(p0 + w / 2) + w % 2), w = lane % 4,
-        // p0 the slab's first quarter; the halfword holding it, and the row's d
+    if constexpr (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) {
+        // lane -> (row lane / 4, sub-scale or pair 8h + 2(p0 + w / 2) + w % 2),
+        // w = lane % 4, p0 the slab's first quarter. Q6_K: the halfword holding
+        // that sub-scale and the row's d; Q2_K: the word holding the pair and
+        // the row's d, dmin; Q3_K: the whole sub-scale field with d.
         const int e0 = k0 & 255, h = e0 >> 7, p0 = (e0 >> 5) & 3, w = lane & 3;
         const int si = 8 * h + 2 * (p0 + (w >> 1)) + (w & 1);
-        const uint32_t rowb = uint32_t((lane >> 2) * a.pitch) + uint32_t((k0 >> 8) * 210);
-        o.hdr = rowb + 192 + uint32_t(si & ~1);
-        o.hdr2 = rowb + 208;
+        const uint32_t rowb = uint32_t((lane >> 2) * a.pitch) + uint32_t((k0 >> 8) * Format<TYPE>::kBytes);
+        if constexpr (TYPE == kQ6_K) {
+            o.hdr = rowb + 192 + uint32_t(si & ~1);
+            o.hdr2 = rowb + 208;
+        } else if constexpr (TYPE == kQ2_K) {
+            o.hdr = rowb + uint32_t(si & ~3);
+            o.hdr2 = rowb + 80;
+        } else {
+            o.hdr = rowb + 96;
+        }
     }
     o.g = uint32_t(((long long)min(j, a.T - 1) * a.N + 4 * rq) * 4);
     return o;
@@ -656,7 +742,7 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
             // code bytes sit at 2-byte alignment inside these blocks; the
             // dword load relies on the unaligned buffer access of gfx9-class GPUs
             r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
-        } else if constexpr (TYPE == kQ6_K) {
+        } else if constexpr (TYPE == kQ6_K || TYPE == kQ3_K) {
             // 2-byte aligned super-blocks (unaligned dword loads, as above)
             r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
             r.code[s][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code2[s], 0, 0);
@@ -668,9 +754,19 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
     if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) {
         const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wr, o.hdr, 0, 0);
         r.hdr[0] = h.x; r.hdr[1] = h.y; r.hdr[2] = h.z; r.hdr[3] = h.w;
+    } else if constexpr (TYPE == kQ3_K) {
+        // field bytes 96 .. 107 and d; no load reaches past the block, whose
+        // end may be the end of this group's W range
+        const u32x2 f = __builtin_amdgcn_raw_buffer_load_b64(wr, o.hdr, 0, 0);
+        r.hdr[0] = f.x; r.hdr[1] = f.y;
+        r.hdr[2] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr + 8, 0, 0);
+        r.hdr[3] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr + 12, 0, 0);
     } else if constexpr (TYPE == kQ6_K) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
         r.hdr[1] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr2, 0, 0);
+    } else if constexpr (TYPE == kQ2_K) {
+        r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr, 0, 0);
+        r.hdr[1] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr2, 0, 0);
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
     } else {
@@ -726,6 +822,16 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
             const uint8_t* sb = row + (kl >> 8) * 176;
             r.code[s][0] = *reinterpret_cast<const uint32_t*>(sb + 48 + 32 * (e >> 6) + (e & 31));
             r.code[s][1] = *reinterpret_cast<const uint32_t*>(sb + 16 + (e & 31));
+        } else if constexpr (TYPE == kQ2_K) {
+            const int e = kl & 255, h = e >> 7, l = e & 31;
+            r.code[s][0] = *reinterpret_cast<const uint32_t*>(row + (kl >> 8) * 84 + 16 + 32 * h + l);
+        } else if constexpr (TYPE == kQ3_K) {
+            const int e = kl & 255, h = e >> 7, l = e & 31;
+            const uint8_t* sb = row + (kl >> 8) * 110;
+            const uint16_t* qs = reinterpret_cast<const uint16_t*>(sb + 32 + 32 * h + l);
+            const uint16_t* hm = reinterpret_cast<const uint16_t*>(sb + l);
+            r.code[s][0] = uint32_t(qs[0]) | (uint32_t(qs[1]) << 16);
+            r.code[s][1] = uint32_t(hm[0]) | (uint32_t(hm[1]) << 16);
         } else {  // kQ6_K
             const int e = kl & 255, h = e >> 7, p = (e >> 5) & 3, l = e & 31;
             const uint8_t* sb = row + (kl >> 8) * 210;
@@ -742,14 +848,25 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
         uint4 h = make_uint4(0u, 0u, 0u, 0u);
         if (hvalid) h = *reinterpret_cast<const uint4*>(hrow + (k0 >> 8) * Format<TYPE>::kBytes);
         r.hdr[0] = h.x; r.hdr[1] = h.y; r.hdr[2] = h.z; r.hdr[3] = h.w;
-    } else if constexpr (TYPE == kQ6_K) {
+    } else if constexpr (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) {
         const int e0 = k0 & 255, h = e0 >> 7, p0 = (e0 >> 5) & 3, w = lane & 3;
         const int si = 8 * h + 2 * (p0 + (w >> 1)) + (w & 1);
-        r.hdr[0] = r.hdr[1] = 0u;
+#pragma unroll
+        for (int i = 0; i < SkinnyRaw<TYPE>::HW; ++i) r.hdr[i] = 0u;
         if (n0 + (lane >> 2) < N) {
-            const uint8_t* sb = a.W + (long long)(n0 + (lane >> 2)) * a.pitch + (k0 >> 8) * 210;
-            r.hdr[0] = *reinterpret_cast<const uint16_t*>(sb + 192 + (si & ~1));
-            r.hdr[1] = *reinterpret_cast<const uint16_t*>(sb + 208);
+            const uint8_t* sb = a.W + (long long)(n0 + (lane >> 2)) * a.pitch + (k0 >> 8) * Format<TYPE>::kBytes;
+            if constexpr (TYPE == kQ6_K) {
+                r.hdr[0] = *reinterpret_cast<const uint16_t*>(sb + 192 + (si & ~1));
+                r.hdr[1] = *reinterpret_cast<const uint16_t*>(sb + 208);
+            } else if constexpr (TYPE == kQ2_K) {
+                r.hdr[0] = *reinterpret_cast<const uint32_t*>(sb + (si & ~3));
+                r.hdr[1] = *reinterpret_cast<const uint32_t*>(sb + 80);
+            } else {  // field bytes 96 .. 107 and d at 108 (inside the block)
+                const uint16_t* f = reinterpret_cast<const uint16_t*>(sb + 96);
+#pragma unroll
+                for (int i = 0; i < 3; ++i) r.hdr[i] = uint32_t(f[2 * i]) | (uint32_t(f[2 * i + 1]) << 16);
+                r.hdr[3] = f[6];
+            }
         }
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
         const int kb = k0 + 32 * sel;
@@ -810,14 +927,26 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
                 q5_k_x4(r.code[s][0], r.code[s][1], 2 * c + hi, hi != 0, lane_value(am, src), lane_value(bm, src),
                         wv[s]);
         }
-    } else {  // kQ6_K: this lane's pair is (row lane / 4, sub-scale slot lane % 4)
-        const int e0 = k0 & 255, p = ((e0 >> 5) & 3) + hi, l16 = (j & 7) >> 2;
+    } else {  // Q6_K, Q2_K, Q3_K: this lane's pair is (row lane / 4, sub-scale slot lane % 4)
+        const int e0 = k0 & 255, h = e0 >> 7, p0 = (e0 >> 5) & 3, p = p0 + hi, l16 = (j & 7) >> 2;
+        const int w = lane & 3, si = 8 * h + 2 * (p0 + (w >> 1)) + (w & 1);
         float am, bm;
-        q6_k_coeffs(r.hdr[0], lane & 1, half_to_f32(r.hdr[1]), am, bm);
+        if constexpr (TYPE == kQ6_K)
+            q6_k_coeffs(r.hdr[0], si & 1, half_to_f32(r.hdr[1]), am, bm);
+        else if constexpr (TYPE == kQ2_K)
+            q2_k_coeffs(r.hdr[0], si & 3, half_to_f32(r.hdr[1] & 0xFFFFu), half_to_f32(r.hdr[1] >> 16), am, bm);
+        else
+            q3_k_coeffs(r.hdr[0], r.hdr[1], r.hdr[2], si, half_to_f32(r.hdr[3] & 0xFFFFu), am, bm);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int src = 4 * (4 * rq + s) + 2 * hi + l16;
-            q6_k_x4(r.code[s][0], p >= 2, r.code[s][1], p, lane_value(am, src), lane_value(bm, src), wv[s]);
+            const float a = lane_value(am, src), b = lane_value(bm, src);
+            if constexpr (TYPE == kQ6_K)
+                q6_k_x4(r.code[s][0], p >= 2, r.code[s][1], p, a, b, wv[s]);
+            else if constexpr (TYPE == kQ2_K)
+                q2_k_x4(r.code[s][0], p, a, b, wv[s]);
+            else
+                q3_k_x4(r.code[s][0], r.code[s][1], p, 4 * h + p, a, b, wv[s]);
         }
     }
 }

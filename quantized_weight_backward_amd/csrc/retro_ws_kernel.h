@@ -71,6 +71,8 @@ struct WsShape {
                                   : (TYPE == kQ4_K) ? 8
                                   : (TYPE == kQ5_K) ? 12
                                   : (TYPE == kQ6_K) ? 9
+                                  : (TYPE == kQ2_K) ? 5
+                                  : (TYPE == kQ3_K) ? 8
                                                     : CB / 4 + 1;
     // Chunks whose loads a producer thread keeps in registers: the chunk
     // being written to LDS plus RING - 1 in flight. Four when a chunk's
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
         // W: byte offset of this thread's block in the chunk, and the LDS
         // float index of the first element it writes in each 16-column group.
         uint32_t woff = 0;
-        int wlds[S::kDense ? S::DUNITS : (TYPE == kQ6_K) ? 4 : 2];
+        int wlds[S::kDense ? S::DUNITS : (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) ? 4 : 2];
         if constexpr (S::kDense) {
             // unit id: rows 4 (id / (BK / 4)) .. + 3, columns 4 (id % (BK / 4)) .. + 3
 #pragma unroll
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
             woff = uint32_t(r * args.pitch);
             wlds[0] = ws_w_index<WP>(64 * c + 16 * h, r);
             wlds[1] = ws_w_index<WP>(64 * c + 32 + 16 * h, r);
-        } else if constexpr (TYPE == kQ6_K) {
+        } else if constexpr (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) {
             // half hh, l range 8j .. 8j + 7 of row p / 8: columns
             // 128 hh + 32 qq + 8j + 0..7 of the four quarters qq
             const int r = p >> 3, hh = (p >> 2) & 1, j = p & 3;
@@ -250,6 +252,26 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                     wreg[2 * f + 1] = v.y;
                 }
                 wreg[8] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + 208, 0, 0);
+            } else if constexpr (TYPE == kQ2_K) {
+                // qs bytes 16 + 32hh + 8j .. (the 2-bit codes of all four
+                // quarters), the 8 pair bytes of half hh, d and dmin
+                const int hh = (p >> 2) & 1, j = p & 3;
+                const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 16 + 32 * hh + 8 * j, 0, 0);
+                const u32x2 pr = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 8 * hh, 0, 0);
+                wreg[0] = c.x; wreg[1] = c.y; wreg[2] = pr.x; wreg[3] = pr.y;
+                wreg[4] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 80, 0, 0);
+            } else if constexpr (TYPE == kQ3_K) {
+                // qs bytes 32 + 32hh + 8j .., hmask bytes 8j .., the 12-byte
+                // sub-scale field and d (bytes 96 .. 109; no load reaches past
+                // the block, whose end may be the end of W)
+                const int hh = (p >> 2) & 1, j = p & 3;
+                const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 32 + 32 * hh + 8 * j, 0, 0);
+                const u32x2 hm = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 8 * j, 0, 0);
+                const u32x2 f = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 96, 0, 0);
+                wreg[0] = c.x; wreg[1] = c.y; wreg[2] = hm.x; wreg[3] = hm.y;
+                wreg[4] = f.x; wreg[5] = f.y;
+                wreg[6] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 104, 0, 0);
+                wreg[7] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + 108, 0, 0);
             } else {  // Q8_0, Q4_0: 2-byte aligned blocks (unaligned buffer loads)
                 constexpr int CW = S::CB / 4;
                 const uint32_t codes = woff + 2 + S::CB * (p % S::QSPLIT);
@@ -359,6 +381,34 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                     for (int i = 0; i < 2; ++i) {
                         float e[4];
                         q6_k_x4(wreg[2 * (qq & 1) + i], qq >= 2, wreg[4 + i], qq, a, b, e);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) ws[wlds[qq] + (4 * i + t) * WP] = e[t];
+                    }
+                }
+            } else if constexpr (TYPE == kQ2_K || TYPE == kQ3_K) {
+                const int hh = (p >> 2) & 1, j = p & 3;
+                float d, dmin = 0.f;
+                if constexpr (TYPE == kQ2_K) {
+                    d = half_to_f32(wreg[4] & 0xFFFFu);
+                    dmin = half_to_f32(wreg[4] >> 16);
+                } else {
+                    d = half_to_f32(wreg[7] & 0xFFFFu);
+                }
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int si = (j >> 1) + 2 * qq;  // pair / sub-scale 8hh + si
+                    float a, b;
+                    if constexpr (TYPE == kQ2_K)
+                        q2_k_coeffs(wreg[2 + (si >> 2)], si & 3, d, dmin, a, b);
+                    else
+                        q3_k_coeffs(wreg[4], wreg[5], wreg[6], 8 * hh + si, d, a, b);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        float e[4];
+                        if constexpr (TYPE == kQ2_K)
+                            q2_k_x4(wreg[i], qq, a, b, e);
+                        else
+                            q3_k_x4(wreg[i], wreg[2 + i], qq, 4 * hh + qq, a, b, e);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) ws[wlds[qq] + (4 * i + t) * WP] = e[t];
                     }

@@ -37,6 +37,7 @@ def test_enum_values_match_header():
     text = open(HEADER).read()
     for name, value in [("RETRO_F32", q.F32), ("RETRO_F16", q.F16), ("RETRO_Q4_0", q.Q4_0), ("RETRO_Q8_0", q.Q8_0),
                         ("RETRO_Q4_K", q.Q4_K), ("RETRO_Q5_K", q.Q5_K), ("RETRO_Q6_K", q.Q6_K),
+                        ("RETRO_Q2_K", q.Q2_K), ("RETRO_Q3_K", q.Q3_K),
                         ("RETRO_BF16", q.BF16), ("RETRO_E_TYPE", q.E_TYPE),
                         ("RETRO_E_SHAPE", q.E_SHAPE), ("RETRO_E_NULL", q.E_NULL), ("RETRO_E_ALIGN", q.E_ALIGN),
                         ("RETRO_E_ALIAS", q.E_ALIAS), ("RETRO_E_HIP", q.E_HIP), ("RETRO_E_VARIANT", q.E_VARIANT),
@@ -47,7 +48,8 @@ def test_enum_values_match_header():
         assert m and int(m.group(1)) == value, name
 
 
-@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K, wl.Q5_K, wl.Q6_K])
+@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K,
+                                   wl.Q6_K])
 def test_row_bytes_matches_the_format(wtype):
     blk, nbytes = wl.block_geometry(wtype)
     for nblocks in (0, 1, 3, 16, 56):
@@ -65,6 +67,8 @@ def test_row_bytes_of_the_workloads():
     assert q.row_bytes(q.F16, 4096) == 8192
     assert q.row_bytes(q.Q5_K, 4096) == 2816
     assert q.row_bytes(q.Q6_K, 14336) == 11760
+    assert q.row_bytes(q.Q2_K, 4096) == 1344
+    assert q.row_bytes(q.Q3_K, 4096) == 1760
     assert q.row_bytes(99, 256) == -1
 
 
@@ -92,7 +96,7 @@ def test_choice():
         assert q.VARIANT_NAMES[q.choice(wtype, 4096, 4096, 512)].startswith("ws_")
     assert q.choice(q.F16, 301, 77, 200) == q.VARIANT_TILE_64x64  # 602-byte rows: no 16-byte units
     assert q.choice(q.Q4_K, 100, 1, 1) == q.E_SHAPE
-    for wtype in (q.Q5_K, q.Q6_K):  # K-quants: 256-column tiles, as Q4_K
+    for wtype in (q.Q2_K, q.Q3_K, q.Q5_K, q.Q6_K):  # K-quants: 256-column tiles, as Q4_K
         assert q.choice(wtype, 4096, 14336, 4096) == q.VARIANT_WS_128x256
         assert q.choice(wtype, 14336, 4096, 16) == q.VARIANT_SKINNY
         assert not q.variant_applies(q.VARIANT_WS_64x128, wtype, 4096, 14336, 4096)

@@ -29,7 +29,8 @@ REL_MAX = 1e-5
 REL_TIGHT = 2e-6
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_K, wl.Q5_K, wl.Q6_K]
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K]
+KQUANTS = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
 ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
              "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128", "ws_32x256", "ws_32x128"]
 
@@ -51,7 +52,7 @@ def variant_id(q, name):
 
 
 def tile_variants(wtype):
-    if wtype in (wl.Q4_K, wl.Q5_K, wl.Q6_K):
+    if wtype in KQUANTS:
         return ["tile_128x256", "tile_64x256", "ws_128x256", "ws_64x256", "ws_32x256"]
     return ALL_TILES
 
@@ -93,6 +94,8 @@ SMALL_K = {
     wl.Q4_K: (768, 512, 256, 768),
     wl.Q5_K: (512, 768, 256, 512),
     wl.Q6_K: (768, 256, 512, 768),
+    wl.Q2_K: (512, 768, 256, 768),
+    wl.Q3_K: (768, 512, 256, 512),
 }
 # (T, N): the last case has N % 4 == 0 (G rows 16-byte aligned, which the
 # producer/consumer kernel needs) with a partial last chunk of 4 rows
@@ -108,8 +111,9 @@ def small_case(wtype, i, seed):
 
 def same_bits_zeros_equal(a, b):
     """Bit-identical floats, except that +0 and -0 count as equal: the Q6_K
-    kernels form (d*sc)*(q - 32) as a*q - 32a, which is +0 where the plain
-    product is -0 (negative d*sc, q = 32); every non-zero value is exact."""
+    and Q3_K kernels form (d*sc)*(q - c) as a*q - c*a, which is +0 where the
+    plain product is -0 (negative d*sc, q = c); every non-zero value is
+    exact."""
     a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
     return a.shape == b.shape and bool(np.all((a.view(np.uint32) == b.view(np.uint32)) | ((a == 0) & (b == 0))))
 
@@ -181,7 +185,7 @@ def test_skinny_matches_oracle(q, wtype, T, N):
     assert q.choice(wtype, c["K"], N, T) == q.VARIANT_SKINNY
     check_close(run(q, c, "skinny"), acc, ab, "skinny")
     check_close(run(q, c, "auto"), acc, ab, "auto")
-    small_tile = "tile_64x256" if wtype in (wl.Q4_K, wl.Q5_K, wl.Q6_K) else "tile_64x64"
+    small_tile = "tile_64x256" if wtype in KQUANTS else "tile_64x64"
     check_close(run(q, c, small_tile), acc, ab, "tile at small T")
     for v in tile_variants(wtype):
         if v.startswith("ws_") and applies(q, c, v):
@@ -195,7 +199,7 @@ def test_q8_0_tiny_workload(q):
     check_close(y, acc, ab)
 
 
-@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q4_0, wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.F16, wl.BF16])
+@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q4_0, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.F16, wl.BF16])
 def test_f32_twin_on_device(q, wtype):
     """out_prod(Qx, W) and out_prod(F32, dequant(W)) run the same tile on
     identical B operands, so they agree bit for bit."""
@@ -216,7 +220,7 @@ def test_f32_twin_on_device(q, wtype):
 
 # --- invariants -----------------------------------------------------------------
 
-@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.Q4_0, wl.BF16])
+@pytest.mark.parametrize("wtype", [wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.Q4_0, wl.BF16])
 @pytest.mark.parametrize("i", [0, 3])
 def test_invariants(q, wtype, i):
     c = small_case(wtype, i, 500)
@@ -318,6 +322,10 @@ FULL = [
     ("q6_k_n14336_k4096_t4096", None),
     ("q5_k_n4096_k14336_t16", None),
     ("q6_k_n4096_k14336_t16", None),
+    ("q2_k_n14336_k4096_t4096", None),
+    ("q3_k_n14336_k4096_t4096", None),
+    ("q2_k_n4096_k14336_t16", None),
+    ("q3_k_n4096_k14336_t16", None),
 ]
 
 
@@ -343,7 +351,8 @@ def test_full_size_sampled_rows(q, name, wtype):
 
 
 @pytest.mark.parametrize("name", ["q4_0_n17408_k5120_t2048", "q4_k_n14336_k4096_t4096", "q4_k_n4096_k14336_t16",
-                                  "q5_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096", "q6_k_n4096_k14336_t16"])
+                                  "q5_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096", "q6_k_n4096_k14336_t16",
+                                  "q2_k_n14336_k4096_t4096", "q3_k_n14336_k4096_t4096", "q3_k_n4096_k14336_t16"])
 def test_full_size_decode_through_identity(q, name):
     """Full-size W through the benchmarked kernel with G = I (T = N): the
     output is the decoded W, bit for bit."""

@@ -197,12 +197,17 @@ WORKLOADS = {
     "q4_0_n17408_k5120_t2048": dict(type=Q4_0, N=17408, K=5120, T=2048, seed=1003, g_sigma=1e-2),
     "q4_k_n14336_k4096_t4096": dict(type=Q4_K, N=14336, K=4096, T=4096, seed=1004, g_sigma=1.0),
     "q4_k_n4096_k14336_t16": dict(type=Q4_K, N=4096, K=14336, T=16, seed=1005, g_sigma=1.0),
-    # The same two Q4_K shapes in the other K-quants of a Q4_K_M file (Q5_K
-    # and Q6_K tensors sit beside the Q4_K ones), with their own seeds.
+    # The same two Q4_K shapes in the other K-quants (a Q4_K_M file puts
+    # Q5_K and Q6_K tensors beside the Q4_K ones; Q2_K and Q3_K make the
+    # smaller K-quant mixes), with their own seeds.
     "q5_k_n14336_k4096_t4096": dict(type=Q5_K, N=14336, K=4096, T=4096, seed=1006, g_sigma=1.0),
     "q6_k_n14336_k4096_t4096": dict(type=Q6_K, N=14336, K=4096, T=4096, seed=1007, g_sigma=1.0),
     "q5_k_n4096_k14336_t16": dict(type=Q5_K, N=4096, K=14336, T=16, seed=1008, g_sigma=1.0),
     "q6_k_n4096_k14336_t16": dict(type=Q6_K, N=4096, K=14336, T=16, seed=1009, g_sigma=1.0),
+    "q2_k_n14336_k4096_t4096": dict(type=Q2_K, N=14336, K=4096, T=4096, seed=1010, g_sigma=1.0),
+    "q3_k_n14336_k4096_t4096": dict(type=Q3_K, N=14336, K=4096, T=4096, seed=1011, g_sigma=1.0),
+    "q2_k_n4096_k14336_t16": dict(type=Q2_K, N=4096, K=14336, T=16, seed=1012, g_sigma=1.0),
+    "q3_k_n4096_k14336_t16": dict(type=Q3_K, N=4096, K=14336, T=16, seed=1013, g_sigma=1.0),
 }
 
 
