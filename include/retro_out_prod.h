@@ -165,8 +165,9 @@ const char *retro_strerror(int code);
  *   RETRO_VARIANT_WS_*      the same tiles computed by a workgroup whose
  *                           waves are split into MFMA (consumer) and load/
  *                           decode (producer) roles over double-buffered LDS;
- *                           needs N % 4 == 0 (and K % 4 == 0 for F32, F16,
- *                           BF16); the TILE_* kernel takes the other shapes
+ *                           needs G rows in 16-byte units (ldg % 4 == 0;
+ *                           ldg = N when contiguous) and K % 4 == 0 for F32,
+ *                           F16, BF16; the TILE_* kernel takes the others
  */
 enum {
     RETRO_VARIANT_AUTO = 0,
@@ -189,6 +190,33 @@ enum {
 int retro_out_prod_variant(int variant, int type, const void *W, const float *G, float *dst,
                            int64_t K, int64_t N, int64_t T, void *stream);
 
+/*
+ * retro_out_prod on row-strided operands: W row n starts at byte n * ldw, G
+ * row t at float t * ldg, dst row t at float t * ldd (elements within a row
+ * stay contiguous). This takes views of larger tensors: a slice of G's
+ * columns or rows, a block of dst's columns, W rows with padding between them.
+ * With ldw = retro_row_bytes(type, K), ldg = N and ldd = K it is
+ * retro_out_prod. This generalises the contiguous src1 and dst that the
+ * llama.cpp PR #3 ("cuda: out_prod accepts a quantized src0") admits
+ * (section "What") to strided ones.
+ *   ldw  >= retro_row_bytes(type, K)   bytes
+ *   ldg  >= N                          floats
+ *   ldd  >= K                          floats
+ * Errors as retro_out_prod, plus RETRO_E_SHAPE for a stride shorter than its
+ * row or a span beyond the size limits. Only the elements of dst's T x K
+ * block are written; the bytes between its rows are left as they are.
+ * RETRO_E_ALIAS compares the address ranges the operands span (first to last
+ * element), so interleaved views of one tensor count as overlapping.
+ */
+int retro_out_prod_strided(int type, const void *W, int64_t ldw, const float *G, int64_t ldg, float *dst,
+                           int64_t ldd, int64_t K, int64_t N, int64_t T, void *stream);
+
+/* retro_out_prod_strided with a forced kernel variant (RETRO_E_VARIANT when
+ * it does not apply). */
+int retro_out_prod_strided_variant(int variant, int type, const void *W, int64_t ldw, const float *G,
+                                   int64_t ldg, float *dst, int64_t ldd, int64_t K, int64_t N, int64_t T,
+                                   void *stream);
+
 /* The variant retro_out_prod would run for this type and shape, or a
  * negative error code (as retro_out_prod_supported would refuse). Touches no
  * device. */
@@ -197,6 +225,10 @@ int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T);
 /* 1 if retro_out_prod_variant(variant, type, ..., K, N, T) with valid buffers
  * would run, 0 otherwise. Touches no device. */
 int retro_out_prod_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T);
+
+/* The same for retro_out_prod_strided_variant with strides ldw, ldg, ldd. */
+int retro_out_prod_strided_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, int64_t ldw,
+                                           int64_t ldg, int64_t ldd);
 
 #ifdef __cplusplus
 }

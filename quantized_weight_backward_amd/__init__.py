@@ -55,8 +55,9 @@ VARIANT_NAMES = {
 LIB_PATH = _build.LIB_PATH
 
 # The exported symbols, as declared in include/retro_out_prod.h.
-EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_dequantize", "retro_out_prod_supported",
-           "retro_out_prod_choice", "retro_out_prod_variant_applies", "retro_row_bytes", "retro_strerror")
+EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided", "retro_out_prod_strided_variant",
+           "retro_dequantize", "retro_out_prod_supported", "retro_out_prod_choice", "retro_out_prod_variant_applies",
+           "retro_out_prod_strided_variant_applies", "retro_row_bytes", "retro_strerror")
 
 
 def _load() -> ctypes.CDLL:
@@ -70,6 +71,12 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp]
     lib.retro_out_prod_variant.restype = i32
     lib.retro_out_prod_variant.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, vp]
+    lib.retro_out_prod_strided.restype = i32
+    lib.retro_out_prod_strided.argtypes = [i32, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+    lib.retro_out_prod_strided_variant.restype = i32
+    lib.retro_out_prod_strided_variant.argtypes = [i32, i32, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+    lib.retro_out_prod_strided_variant_applies.restype = i32
+    lib.retro_out_prod_strided_variant_applies.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64]
     lib.retro_dequantize.restype = i32
     lib.retro_dequantize.argtypes = [i32, vp, vp, i64, i64, vp]
     lib.retro_out_prod_supported.restype = i32
@@ -128,39 +135,66 @@ def _ptr(t) -> int | None:
     return None if t is None else int(t.data_ptr())
 
 
-def _device_tensor(t, name):
+def _device_tensor(t, name, contiguous=True):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _row_stride(t, name) -> int:
+    """Elements between rows of a 2-D view whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D view with contiguous rows")
+    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
 
 
 def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, stream=None):
     """dst = out_prod(W, G): W packed bytes (N rows), G float32 T x N, dst float32 T x K.
 
-    W is any contiguous device tensor holding N * row_bytes(wtype, K) bytes.
-    Runs asynchronously on `stream` (default: torch's current stream).
+    W is a contiguous device tensor of N * row_bytes(wtype, K) bytes, or a
+    2-D uint8 view of N rows whose first row_bytes bytes hold a W row; G and
+    out are 2-D float32 views whose rows are contiguous (their row strides
+    may exceed N and K). Runs asynchronously on `stream` (default: torch's
+    current stream).
     """
-    _device_tensor(W, "W")
-    _device_tensor(G, "G")
+    _device_tensor(W, "W", contiguous=False)
+    _device_tensor(G, "G", contiguous=False)
     if G.dtype != torch.float32 or G.dim() != 2:
         raise ValueError("G must be a 2-D float32 tensor (T x N)")
     T, N = G.shape
     rb = row_bytes(wtype, K)
     if rb < 0:
         _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
-    if W.numel() * W.element_size() != N * rb:
-        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
+    if W.is_contiguous():
+        if W.numel() * W.element_size() != N * rb:
+            raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
+        ldw = rb
+    else:
+        if W.dtype != torch.uint8 or W.shape[0] != N or W.shape[1] < rb:
+            raise ValueError(f"a strided W must be a uint8 view of N rows of at least {rb} bytes")
+        ldw = _row_stride(W, "W")
+    ldg = _row_stride(G, "G")
     if out is None:
         out = torch.empty((T, K), dtype=torch.float32, device=G.device)
     else:
-        _device_tensor(out, "out")
+        _device_tensor(out, "out", contiguous=False)
         if out.dtype != torch.float32 or tuple(out.shape) != (T, K):
             raise ValueError("out must be float32 T x K")
-    _check(lib.retro_out_prod_variant(int(variant), int(wtype), _ptr(W), _ptr(G), _ptr(out), int(K), int(N),
-                                      int(T), _stream_handle(stream)))
+    ldd = _row_stride(out, "out")
+    if (ldw, ldg, ldd) == (rb, N, K):
+        _check(lib.retro_out_prod_variant(int(variant), int(wtype), _ptr(W), _ptr(G), _ptr(out), int(K), int(N),
+                                          int(T), _stream_handle(stream)))
+    else:
+        _check(lib.retro_out_prod_strided_variant(int(variant), int(wtype), _ptr(W), ldw, _ptr(G), ldg, _ptr(out),
+                                                  ldd, int(K), int(N), int(T), _stream_handle(stream)))
     return out
+
+
+def variant_applies_strided(variant: int, wtype: int, K: int, N: int, T: int, ldw: int, ldg: int, ldd: int) -> bool:
+    return lib.retro_out_prod_strided_variant_applies(int(variant), int(wtype), int(K), int(N), int(T), int(ldw),
+                                                      int(ldg), int(ldd)) == 1
 
 
 def dequantize(wtype: int, W, K: int, N: int, out=None, stream=None):

@@ -76,6 +76,25 @@ int check_shape(int type, int64_t K, int64_t N, int64_t T) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Row strides of the three operands.
+struct Strides {
+    int64_t ldw;  // bytes between consecutive W rows (>= the row's bytes)
+    int64_t ldg;  // floats between consecutive G rows (>= N)
+    int64_t ldd;  // floats between consecutive dst rows (>= K)
+};
+
+Strides contiguous(int type, int64_t K, int64_t N) { return {row_bytes_of(type, K), N, K}; }
+
+// Strides no shorter than the rows, and spans within the size limits (the
+// shape itself already checked).
+int check_strides(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    if (s.ldw < row_bytes_of(type, K) || s.ldg < N || s.ldd < K) return RETRO_E_SHAPE;
+    if (!product_below(N, s.ldw, kByteLimit) || !product_below(T, s.ldg, kCountLimit) ||
+        !product_below(T, s.ldd, kCountLimit))
+        return RETRO_E_SHAPE;
+    return RETRO_OK;
+}
+
 struct TileVariant {
     int id, bt, bk;
     double penalty;  // relative cost per output of the smaller tiles
@@ -102,7 +121,7 @@ bool is_dense(int type) { return type == RETRO_F32 || type == RETRO_F16 || type 
 // for every type on MI355X (Q4_K 0.84 vs 0.74 of the F32 peak at T = 4096,
 // Q4_0 0.76 vs 0.66, Q8_0 0.73 vs 0.67, dense T = 512 0.61-0.68 vs 0.50),
 // so it is preferred; the single-role kernel is the fallback for the shapes
-// it does not take (N % 4 != 0, or a dense K % 4 != 0).
+// it does not take (G rows not in 16-byte units, or a dense K % 4 != 0).
 bool prefers_ws(int) { return true; }
 constexpr double kOtherFamily = 1.3;
 
@@ -115,31 +134,34 @@ const TileVariant* find_tile(int variant) {
 
 // The tiled kernel addresses a tile's BT rows of G and a chunk's 32 rows of
 // W with 32-bit offsets from per-chunk buffer bases.
-bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t T) {
+bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     Geometry geo;
     if (geometry(type, geo) && geo.block == 256 && v.bk % 256) return false;
     // the producer/consumer kernel loads G rows in 16-byte units and dense W
     // rows in 4-element units
-    if (v.ws && (N % 4 || (is_dense(type) && K % 4))) return false;
-    return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit && int64_t(v.bt) * N * 4 < (int64_t(1) << 31) &&
-           33 * row_bytes_of(type, K) < (int64_t(1) << 31);
+    if (v.ws && (s.ldg % 4 || (is_dense(type) && K % 4))) return false;
+    (void)N;
+    return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit && int64_t(v.bt) * s.ldg * 4 < (int64_t(1) << 31) &&
+           33 * s.ldw < (int64_t(1) << 31);
 }
 
 // The skinny kernel addresses one 16-row group of W, and the 16 rows of G
 // it reads, through buffer descriptors whose sizes are signed 32-bit.
-bool skinny_applies(int type, int64_t K, int64_t N, int64_t T) {
-    return T <= 16 && cdiv(K, 64) < kGridLimit && 16 * row_bytes_of(type, K) < (int64_t(1) << 31) &&
-           16 * N * 4 < (int64_t(1) << 31);
+bool skinny_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    (void)type;
+    (void)N;
+    return T <= 16 && cdiv(K, 64) < kGridLimit && 16 * s.ldw < (int64_t(1) << 31) &&
+           16 * s.ldg * 4 < (int64_t(1) << 31);
 }
 
 // Pick the tile that minimises (tiles per CU, rounded up) x tile area x
 // relative cost: the rounding is the wave quantisation over 256 CUs.
-int choose(int type, int64_t K, int64_t N, int64_t T) {
-    if (skinny_applies(type, K, N, T)) return RETRO_VARIANT_SKINNY;
+int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    if (skinny_applies(type, K, N, T, s)) return RETRO_VARIANT_SKINNY;
     int best = -1;
     double best_cost = 0;
     for (const auto& v : kTiles) {
-        if (!tile_applies(v, type, K, N, T)) continue;
+        if (!tile_applies(v, type, K, N, T, s)) continue;
         const double weight = v.penalty * (v.ws == prefers_ws(type) ? 1.0 : kOtherFamily);
         const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk);
         const double cost = double(cdiv(nt, kNumCUs)) * v.bt * v.bk * weight;
@@ -177,7 +199,8 @@ void clear_last_error() { (void)hipGetLastError(); }
 int launch_status() { return hipGetLastError() == hipSuccess ? RETRO_OK : RETRO_E_HIP; }
 
 template <int TYPE, int WA, int WB, int WGT, int WGK>
-int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+                hipStream_t st) {
     using S = TileShape<TYPE, WA, WB, WGT, WGK>;
     TileArgs a;
     a.W = static_cast<const uint8_t*>(W);
@@ -186,16 +209,18 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     a.K = int(K);
     a.N = int(N);
     a.T = int(T);
-    a.pitch = row_bytes_of(TYPE, K);
+    a.pitch = s.ldw;
+    a.ldg = s.ldg;
+    a.ldd = s.ldd;
     // Widest staging load that the row pitch and the tile span are both
     // multiples of (the base pointer is 16-byte aligned).
     int wvec = 16;
     while (wvec > 2 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0)) wvec >>= 1;
     a.wvec = wvec;
-    a.gvec = (N % 4 == 0) ? 1 : 0;
+    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
-    a.group = group_height(a.tiles_t, a.tiles_k, 2, 4.0 * T * N, double(N) * a.pitch);
+    a.group = group_height(a.tiles_t, a.tiles_k, 2, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
     hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt), dim3(S::kThreads), 0, st, a);
@@ -203,7 +228,8 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
 }
 
 template <int TYPE, int WA, int WB, int CT>
-int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+              hipStream_t st) {
     using S = WsShape<TYPE, WA, WB, CT>;
     TileArgs a;
     a.W = static_cast<const uint8_t*>(W);
@@ -212,12 +238,14 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
     a.K = int(K);
     a.N = int(N);
     a.T = int(T);
-    a.pitch = row_bytes_of(TYPE, K);
+    a.pitch = s.ldw;
+    a.ldg = s.ldg;
+    a.ldd = s.ldd;
     a.wvec = 16;
-    a.gvec = (N % 4 == 0) ? 1 : 0;
+    a.gvec = 1;
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
-    a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * a.pitch);
+    a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
     hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);
@@ -225,7 +253,8 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
 }
 
 template <int TYPE>
-int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+                  hipStream_t st) {
     constexpr int kWaves = RETRO_SKINNY_WAVES;
     SkinnyArgs a;
     a.W = static_cast<const uint8_t*>(W);
@@ -234,9 +263,11 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     a.K = int(K);
     a.N = int(N);
     a.T = int(T);
-    a.pitch = row_bytes_of(TYPE, K);
+    a.pitch = s.ldw;
+    a.ldg = s.ldg;
+    a.ldd = s.ldd;
     a.wide = (K % 4 == 0) ? 1 : 0;
-    a.gvec = (N % 4 == 0) ? 1 : 0;
+    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
     const dim3 grid(unsigned(cdiv(K, 64))), block(kWaves * 64);
     clear_last_error();
     if (a.wide && a.gvec)
@@ -248,24 +279,24 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
 
 template <int TYPE>
 int launch_variant(int variant, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
-                   hipStream_t st) {
+                   const Strides& s, hipStream_t st) {
     switch (variant) {
-        case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, st);
-        case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, st);
-        case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, st);
-        case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4, 2>(W, G, dst, K, N, T, st);
-        case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4, 2>(W, G, dst, K, N, T, st);
-        case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, st);
+        case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, s, st);
         default: break;
     }
     if constexpr (!kSuperBlock<TYPE>) {
         switch (variant) {
-            case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, st);
-            case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, st);
-            case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, st);
-            case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2, 2>(W, G, dst, K, N, T, st);
-            case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2, 2>(W, G, dst, K, N, T, st);
-            case RETRO_VARIANT_WS_32x128: return launch_ws<TYPE, 1, 1, 1>(W, G, dst, K, N, T, st);
+            case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS_32x128: return launch_ws<TYPE, 1, 1, 1>(W, G, dst, K, N, T, s, st);
             default: break;
         }
     }
@@ -280,46 +311,47 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
     return pa < pb + uint64_t(nb) && pb < pa + uint64_t(na);
 }
 
-// Whether a forced variant takes this type and shape (shape already checked).
-bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
-    if (variant == RETRO_VARIANT_AUTO) return choose(type, K, N, T) > 0;
-    if (variant == RETRO_VARIANT_SKINNY) return skinny_applies(type, K, N, T);
+// Whether a forced variant takes this type, shape and strides (all already
+// checked).
+bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    if (variant == RETRO_VARIANT_AUTO) return choose(type, K, N, T, s) > 0;
+    if (variant == RETRO_VARIANT_SKINNY) return skinny_applies(type, K, N, T, s);
     const TileVariant* tv = find_tile(variant);
-    return tv && tile_applies(*tv, type, K, N, T);
+    return tv && tile_applies(*tv, type, K, N, T, s);
 }
 
 int out_prod_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
-                  int64_t T, void* stream) {
-    const int rc = check_shape(type, K, N, T);
+                  int64_t T, const Strides& s, void* stream) {
+    int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    rc = check_strides(type, K, N, T, s);
     if (rc != RETRO_OK) return rc;
     if (T == 0 || K == 0) return RETRO_OK;
-    const int64_t w_bytes = N * row_bytes_of(type, K);
-    const int64_t g_bytes = T * N * 4;
-    const int64_t d_bytes = T * K * 4;
+    // bytes each operand spans
+    const int64_t w_bytes = N > 0 ? (N - 1) * s.ldw + row_bytes_of(type, K) : 0;
+    const int64_t g_bytes = N > 0 ? ((T - 1) * s.ldg + N) * 4 : 0;
+    const int64_t d_bytes = ((T - 1) * s.ldd + K) * 4;
     if (!dst || (N > 0 && (!W || !G))) return RETRO_E_NULL;
     if (!aligned16(dst) || (N > 0 && (!aligned16(W) || !aligned16(G)))) return RETRO_E_ALIGN;
     if (overlap(dst, d_bytes, W, w_bytes) || overlap(dst, d_bytes, G, g_bytes)) return RETRO_E_ALIAS;
     if (variant == RETRO_VARIANT_AUTO) {
-        variant = choose(type, K, N, T);
+        variant = choose(type, K, N, T, s);
         if (variant < 0) return variant;
-    } else if (variant == RETRO_VARIANT_SKINNY) {
-        if (!skinny_applies(type, K, N, T)) return RETRO_E_VARIANT;
-    } else {
-        const TileVariant* tv = find_tile(variant);
-        if (!tv || !tile_applies(*tv, type, K, N, T)) return RETRO_E_VARIANT;
+    } else if (!variant_applies(variant, type, K, N, T, s)) {
+        return RETRO_E_VARIANT;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (type) {
-        case RETRO_F32: return launch_variant<kF32>(variant, W, G, dst, K, N, T, st);
-        case RETRO_F16: return launch_variant<kF16>(variant, W, G, dst, K, N, T, st);
-        case RETRO_BF16: return launch_variant<kBF16>(variant, W, G, dst, K, N, T, st);
-        case RETRO_Q8_0: return launch_variant<kQ8_0>(variant, W, G, dst, K, N, T, st);
-        case RETRO_Q4_0: return launch_variant<kQ4_0>(variant, W, G, dst, K, N, T, st);
-        case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, st);
-        case RETRO_Q5_K: return launch_variant<kQ5_K>(variant, W, G, dst, K, N, T, st);
-        case RETRO_Q2_K: return launch_variant<kQ2_K>(variant, W, G, dst, K, N, T, st);
-        case RETRO_Q3_K: return launch_variant<kQ3_K>(variant, W, G, dst, K, N, T, st);
-        case RETRO_Q6_K: return launch_variant<kQ6_K>(variant, W, G, dst, K, N, T, st);
+        case RETRO_F32: return launch_variant<kF32>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_F16: return launch_variant<kF16>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_BF16: return launch_variant<kBF16>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q8_0: return launch_variant<kQ8_0>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q4_0: return launch_variant<kQ4_0>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q5_K: return launch_variant<kQ5_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q2_K: return launch_variant<kQ2_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q3_K: return launch_variant<kQ3_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q6_K: return launch_variant<kQ6_K>(variant, W, G, dst, K, N, T, s, st);
         default: return RETRO_E_TYPE;
     }
 }
@@ -346,12 +378,23 @@ extern "C" {
 
 int retro_out_prod(int type, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
                    void* stream) {
-    return out_prod_impl(RETRO_VARIANT_AUTO, type, W, G, dst, K, N, T, stream);
+    return out_prod_impl(RETRO_VARIANT_AUTO, type, W, G, dst, K, N, T, contiguous(type, K, N), stream);
 }
 
 int retro_out_prod_variant(int variant, int type, const void* W, const float* G, float* dst, int64_t K,
                            int64_t N, int64_t T, void* stream) {
-    return out_prod_impl(variant, type, W, G, dst, K, N, T, stream);
+    return out_prod_impl(variant, type, W, G, dst, K, N, T, contiguous(type, K, N), stream);
+}
+
+int retro_out_prod_strided(int type, const void* W, int64_t ldw, const float* G, int64_t ldg, float* dst,
+                           int64_t ldd, int64_t K, int64_t N, int64_t T, void* stream) {
+    return out_prod_impl(RETRO_VARIANT_AUTO, type, W, G, dst, K, N, T, Strides{ldw, ldg, ldd}, stream);
+}
+
+int retro_out_prod_strided_variant(int variant, int type, const void* W, int64_t ldw, const float* G,
+                                   int64_t ldg, float* dst, int64_t ldd, int64_t K, int64_t N, int64_t T,
+                                   void* stream) {
+    return out_prod_impl(variant, type, W, G, dst, K, N, T, Strides{ldw, ldg, ldd}, stream);
 }
 
 int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, void* stream) {
@@ -382,19 +425,26 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
 int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T) {
     if (check_shape(type, K, N, T) != RETRO_OK) return 0;
     if (T == 0 || K == 0) return 1;
-    return choose(type, K, N, T) > 0 ? 1 : 0;
+    return choose(type, K, N, T, contiguous(type, K, N)) > 0 ? 1 : 0;
 }
 
 int retro_out_prod_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
+    return retro_out_prod_strided_variant_applies(variant, type, K, N, T, row_bytes_of(type, K), N, K);
+}
+
+int retro_out_prod_strided_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, int64_t ldw,
+                                           int64_t ldg, int64_t ldd) {
     if (check_shape(type, K, N, T) != RETRO_OK) return 0;
+    const Strides s{ldw, ldg, ldd};
+    if (check_strides(type, K, N, T, s) != RETRO_OK) return 0;
     if (T == 0 || K == 0) return 1;
-    return variant_applies(variant, type, K, N, T) ? 1 : 0;
+    return variant_applies(variant, type, K, N, T, s) ? 1 : 0;
 }
 
 int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T) {
     const int rc = check_shape(type, K, N, T);
     if (rc != RETRO_OK) return rc;
-    return choose(type, K, N, T);
+    return choose(type, K, N, T, contiguous(type, K, N));
 }
 
 int64_t retro_row_bytes(int type, int64_t K) { return row_bytes_of(type, K); }

@@ -79,11 +79,13 @@ struct TileArgs {
     const float* G;
     float* dst;
     int K, N, T;
-    long long pitch;  // bytes per W row
+    long long pitch;  // bytes between consecutive W rows
     int wvec;         // W staging load width (16, 8, 4, 2)
     int gvec;         // 1: G rows take float4 loads (N % 4 == 0)
     int tiles_t, tiles_k;
     int group;        // row tiles per group of the tile order (tile_coords)
+    long long ldg;    // floats between consecutive G rows (>= N)
+    long long ldd;    // floats between consecutive dst rows (>= K)
 };
 
 // Column swizzle of a decoded W tile in LDS: XOR column bits 2-4 with
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 #pragma unroll
     for (int s = 0; s < S::GSLOTS; ++s) {
         const int id = tid + S::kThreads * s;
-        goff[s] = uint32_t(((id >> 3) * N + 4 * (id & 7)) * 4);
+        goff[s] = uint32_t(((id >> 3) * args.ldg + 4 * (id & 7)) * 4);
     }
 #pragma unroll
     for (int s = 0; s < S::WSLOTS; ++s) {
@@ -176,8 +178,10 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
         const int r = id / S::UPR, u = id - r * S::UPR;
         woff[s] = uint32_t(r * args.pitch + 16 * u);
     }
-    const long long g_end = (long long)T * N;         // elements of G
-    const long long w_end = (long long)N * args.pitch;  // bytes of W
+    const long long g_end = (long long)(T - 1) * args.ldg + N;  // elements spanned by G
+    // bytes spanned by W: rows are `pitch` apart, the last one ends after
+    // its K / block blocks
+    const long long w_end = N > 0 ? (long long)(N - 1) * args.pitch + (long long)(K / F::kBlock) * F::kBytes : 0;
 
     // Global -> registers for the chunk of W rows [n0, n0 + 32). Both loads go
     // through buffer descriptors based at the chunk's first element, so rows
@@ -187,9 +191,9 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
     // (possible only in the last chunk) are zeroed explicitly.
     auto load_chunk = [&](int n0) {
         n0 = __builtin_amdgcn_readfirstlane(n0);
-        const long long gb = (long long)t0 * N + n0;
+        const long long gb = (long long)t0 * args.ldg + n0;
         const __amdgpu_buffer_rsrc_t gr =
-            buffer_rsrc(args.G + gb, uint32_t(min(4 * (g_end - gb), (long long)0x7FFFFFFF)));
+            buffer_rsrc(args.G + gb, uint32_t(max(0ll, min(4 * (g_end - gb), (long long)0x7FFFFFFF))));
 #pragma unroll
         for (int s = 0; s < S::GSLOTS; ++s) {
             if (args.gvec) {
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
         }
         const long long wb = (long long)n0 * args.pitch + kb0;
         const __amdgpu_buffer_rsrc_t wr =
-            buffer_rsrc(args.W + wb, uint32_t(min(w_end - wb, (long long)0x7FFFFFFF)));
+            buffer_rsrc(args.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
 #pragma unroll
         for (int s = 0; s < S::WSLOTS; ++s) {
             if (S::WUNITS % S::kThreads != 0 && tid + S::kThreads * s >= S::WUNITS) continue;
@@ -499,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int t = t0 + wt * 32 * WA + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (t < T && k < K) args.dst[(long long)t * K + k] = acc[a][b][v];
+                if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = acc[a][b][v];
             }
         }
 }
@@ -513,7 +517,9 @@ struct SkinnyArgs {
     const float* G;
     float* dst;
     int K, N, T;
-    long long pitch;
+    long long pitch;  // bytes between consecutive W rows
+    long long ldg;    // floats between consecutive G rows (>= N)
+    long long ldd;    // floats between consecutive dst rows (>= K)
     int wide;  // 1: W rows allow the widest load of 4 consecutive elements
     int gvec;  // 1: G rows take float4 loads
 };
@@ -712,7 +718,7 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
             o.hdr = rowb + 96;
         }
     }
-    o.g = uint32_t(((long long)min(j, a.T - 1) * a.N + 4 * rq) * 4);
+    o.g = uint32_t(((long long)min(j, a.T - 1) * a.ldg + 4 * rq) * 4);
     return o;
 }
 
@@ -725,7 +731,7 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
     // per-lane offset from them.
     n0 = __builtin_amdgcn_readfirstlane(n0);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.W + (long long)n0 * a.pitch, uint32_t(16 * a.pitch));
-    const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(a.G + n0, uint32_t(4 * ((long long)(a.T - 1) * a.N + 16)));
+    const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(a.G + n0, uint32_t(4 * ((long long)(a.T - 1) * a.ldg + 16)));
     const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(gr, o.g, 0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) r.g[q] = __uint_as_float(gv[q]);
@@ -785,7 +791,7 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
 #pragma unroll
     for (int s = 0; s < 4; ++s) r.g[s] = 0.f;
     if (j < a.T) {
-        const float* gp = a.G + (long long)j * N + nq;
+        const float* gp = a.G + (long long)j * a.ldg + nq;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             if (nq + s < N) r.g[s] = gp[s];
@@ -1044,7 +1050,7 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
         float sum = part[o];
 #pragma unroll
         for (int w = 1; w < NWAVES; ++w) sum += part[w * 16 * KS + o];
-        if (tr < T && k0 + kk < K) args.dst[(long long)tr * K + k0 + kk] = sum;
+        if (tr < T && k0 + kk < K) args.dst[(long long)tr * args.ldd + k0 + kk] = sum;
     }
 }
 

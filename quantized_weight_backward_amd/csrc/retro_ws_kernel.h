@@ -137,7 +137,7 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
 #pragma unroll
         for (int s = 0; s < S::GSLOTS; ++s) {
             const int id = p + S::kPThreads * s;
-            goff[s] = uint32_t(((id >> 3) * N + 4 * (id & 7)) * 4);
+            goff[s] = uint32_t(((id >> 3) * args.ldg + 4 * (id & 7)) * 4);
         }
         // W: byte offset of this thread's block in the chunk, and the LDS
         // float index of the first element it writes in each 16-column group.
@@ -179,8 +179,11 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                 wlds[1] = ws_w_index<WP>(32 * b + 16, r) + S::CB * s * WP;
             }
         }
-        const long long g_end = (long long)T * N;
-        const long long w_end = (long long)N * args.pitch;
+        const long long g_end = (long long)(T - 1) * args.ldg + N;  // elements spanned by G
+        // bytes spanned by W: rows are `pitch` apart, the last one ends after
+        // its K / block blocks
+        const long long w_end =
+            N > 0 ? (long long)(N - 1) * args.pitch + (long long)(K / F::kBlock) * F::kBytes : 0;
 
         // Loads of chunk rows [n0, n0 + 32) into registers, issued the same way
         // for every chunk (no branch), so that the loads of later chunks stay
@@ -190,12 +193,12 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
         // at or past N in the last chunk (the next t row's values) are zeroed
         // when the chunk is written to LDS. Columns past K in the last k tile
         // read bytes of the next row (or zero) and only reach outputs that are
-        // not stored. G rows are 16-byte aligned (N % 4 == 0).
+        // not stored. G rows are 16-byte aligned (ldg % 4 == 0).
         auto load_chunk = [&](auto slot, int n0) {
             float4(&greg)[S::GSLOTS] = gring[decltype(slot)::value];
             uint32_t(&wreg)[S::WWORDS] = wring[decltype(slot)::value];
             n0 = __builtin_amdgcn_readfirstlane(n0);
-            const long long gb = (long long)t0 * N + n0;
+            const long long gb = (long long)t0 * args.ldg + n0;
             const __amdgpu_buffer_rsrc_t gr =
                 buffer_rsrc(args.G + gb, uint32_t(max(0ll, min(4 * (g_end - gb), (long long)0x7FFFFFFF))));
 #pragma unroll
@@ -542,7 +545,7 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int t = t0 + wt * 32 * WA + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (t < T && k < K) args.dst[(long long)t * K + k] = acc[a][b][v];
+                if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = acc[a][b][v];
             }
         }
 }

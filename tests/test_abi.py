@@ -122,6 +122,20 @@ def test_variant_applies():
         assert q.variant_applies(v, q.Q8_0, 0, 5, 5)                        # empty output
 
 
+def test_strided_variant_applies():
+    rb = q.row_bytes(q.Q4_0, 512)
+    assert q.variant_applies_strided(q.VARIANT_WS_64x128, q.Q4_0, 512, 77, 200, rb, 80, 512)    # G rows 16-byte units
+    assert not q.variant_applies_strided(q.VARIANT_WS_64x128, q.Q4_0, 512, 77, 200, rb, 77, 512)
+    assert q.variant_applies_strided(q.VARIANT_TILE_64x128, q.Q4_0, 512, 77, 200, rb, 77, 512)
+    assert not q.variant_applies_strided(q.VARIANT_TILE_64x128, q.Q4_0, 512, 77, 200, rb, 76, 512)  # ldg < N
+    assert not q.variant_applies_strided(q.VARIANT_TILE_64x128, q.Q4_0, 512, 77, 200, rb - 1, 80, 512)
+    assert q.variant_applies_strided(q.VARIANT_SKINNY, q.Q4_0, 512, 77, 16, rb + 100, 1000, 600)
+    # contiguous strides: the same answers as the contiguous query
+    for v in q.VARIANT_NAMES:
+        assert q.variant_applies_strided(v, q.Q4_K, 768, 96, 130, q.row_bytes(q.Q4_K, 768), 96, 768) == \
+            q.variant_applies(v, q.Q4_K, 768, 96, 130)
+
+
 def test_strerror_covers_every_code():
     for code in (q.OK, q.E_TYPE, q.E_SHAPE, q.E_NULL, q.E_ALIGN, q.E_ALIAS, q.E_HIP, q.E_VARIANT):
         s = q.strerror(code)
@@ -158,6 +172,18 @@ def test_validation_errors_before_any_device_work():
                                       None) == q.E_VARIANT
     assert lib.retro_out_prod_variant(q.VARIANT_TILE_128x128, q.Q4_K, 0x100000, 0x200000, 0x300000, 256, 4, 64,
                                       None) == q.E_VARIANT
+    # strides: each at least its row, valid strides behave as retro_out_prod
+    st = lib.retro_out_prod_strided
+    assert st(q.F32, 0x100000, 15, 0x200000, 4, 0x300000, 4, 4, 4, 4, None) == q.E_SHAPE  # ldw < row bytes
+    assert st(q.F32, 0x100000, 16, 0x200000, 3, 0x300000, 4, 4, 4, 4, None) == q.E_SHAPE  # ldg < N
+    assert st(q.F32, 0x100000, 16, 0x200000, 4, 0x300000, 3, 4, 4, 4, None) == q.E_SHAPE  # ldd < K
+    assert st(q.F32, 0x100000, 1 << 60, 0x200000, 4, 0x300000, 4, 4, 4, 4, None) == q.E_SHAPE  # W span too large
+    assert st(q.F32, None, 0, None, 5, None, 0, 0, 5, 5, None) == q.OK                  # empty output
+    assert st(q.F32, 0x100000, 16, 0x200008, 8, 0x300000, 4, 4, 4, 4, None) == q.E_ALIGN
+    # dst rows 100 floats apart span (3 * 100 + 4) * 4 bytes from 0x100000: they reach W at 0x100400
+    assert st(q.F32, 0x100400, 16, 0x200000, 4, 0x100000, 100, 4, 4, 4, None) == q.E_ALIAS
+    assert lib.retro_out_prod_strided_variant(42, q.F32, 0x100000, 16, 0x200000, 4, 0x300000, 4, 4, 4, 4,
+                                              None) == q.E_VARIANT
     # dequantize
     assert lib.retro_dequantize(99, None, None, 32, 1, None) == q.E_TYPE
     assert lib.retro_dequantize(q.Q4_K, None, None, 32, 1, None) == q.E_SHAPE

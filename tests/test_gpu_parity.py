@@ -308,6 +308,49 @@ def test_runs_on_the_given_stream(q):
     check_close(out.cpu().numpy(), acc, ab)
 
 
+# --- strided operands --------------------------------------------------------------
+
+STRIDED = [(wl.Q4_K, 768, 96, 130), (wl.Q4_0, 512, 77, 200), (wl.F16, 264, 100, 150), (wl.Q6_K, 512, 60, 70),
+           (wl.Q8_0, 416, 33, 16), (wl.Q2_K, 256, 40, 9)]
+
+
+@pytest.mark.parametrize("wtype,K,N,T", STRIDED)
+@pytest.mark.parametrize("gpad", [4, 3])
+def test_strided_operands_match_oracle(q, wtype, K, N, T, gpad):
+    """G as a column slice of a wider buffer (row stride N + gpad + 4, first
+    column 4), dst as a column block of a wider buffer, W rows padded by 48
+    bytes: every kernel that takes the strides matches the oracle on the
+    contiguous data, and the rest of dst's buffer keeps its sentinel."""
+    c = wl.make_case(wtype, N, K, T, seed=900 + N)
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
+    rb = wl.row_bytes(wtype, K)
+    wbig = torch.zeros((N, rb + 48), dtype=torch.uint8, device="cuda")
+    wbig[:, :rb] = dev(c["W"])
+    W = wbig[:, :rb]
+    ldg = N + gpad + 4
+    gbig = torch.full((T, ldg), float("nan"), device="cuda")
+    gbig[:, 4:4 + N] = dev(c["G"])
+    G = gbig[:, 4:4 + N]
+    ldd = K + 12
+    ran = []
+    for v in ["auto", "skinny"] + tile_variants(wtype):
+        if v != "auto" and not q.variant_applies_strided(variant_id(q, v), wtype, K, N, T, rb + 48, ldg, ldd):
+            continue
+        dbig = torch.full((T, ldd), 7.0, device="cuda")
+        out = dbig[:, 8:8 + K]
+        q.out_prod(wtype, W, G, K, out=out, variant=variant_id(q, v) if v != "auto" else 0)
+        torch.cuda.synchronize()
+        check_close(out.cpu().numpy(), acc, ab, f"strided {v}")
+        rest = dbig.clone()
+        rest[:, 8:8 + K] = 7.0
+        assert bool((rest == 7.0).all()), v
+        ran.append(v)
+    families = {v.split("_")[0] for v in ran if v != "auto"}
+    assert ("skinny" in families) == (T <= 16), ran
+    if T > 16:
+        assert "tile" in families and (("ws" in families) == (ldg % 4 == 0)), ran
+
+
 # --- full-size workloads ----------------------------------------------------------
 
 FULL = [
