@@ -37,6 +37,10 @@
  * the GGUF one, and the tests pin the decoder to hand-packed fixtures of that
  * reading and to a full pack bijection, not to values from the pages.
  *
+ * Parity unpinned against the pages: the layouts of Q4_1, Q5_0 and Q5_1 (the
+ * PR's commit message lists them among the swept types but prints no block),
+ * the GGUF ones, pinned to hand-derived fixtures.
+ *
  * Parity unpinned against the pages: Q2_K, Q3_K, Q5_K and Q6_K as a whole.
  * The pages name the K-quant family only through the Q4_K_M files it is
  * used in; these layouts are the GGUF ones, and the tests pin them to
@@ -50,8 +54,8 @@
 #include <string.h>
 
 enum {
-    T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8, T_Q2_K = 10, T_Q3_K = 11, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14,
-    T_BF16 = 30
+    T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q4_1 = 3, T_Q5_0 = 6, T_Q5_1 = 7, T_Q8_0 = 8, T_Q2_K = 10, T_Q3_K = 11,
+    T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_BF16 = 30
 };
 
 /* IEEE-754 binary16 -> binary32: 1 sign bit, 5 exponent bits (bias 15), 10
@@ -138,6 +142,43 @@ int oracle_decode_row(int type, const uint8_t *row, int64_t K, float *out) {
             }
         }
         return 0;
+    case T_Q4_1:
+    case T_Q5_0:
+    case T_Q5_1: {
+        /* 32-element blocks with an fp16 scale d, codes as in Q4_0 (element
+         * j < 16 is the low nibble of code byte j, element j + 16 its high
+         * nibble), and:
+         *   Q4_1 (20 bytes): d, fp16 offset m, 16 code bytes; value d*q + m
+         *   Q5_0 (22 bytes): d, 4 bytes qh, 16 code bytes; bit j of qh (a
+         *     little-endian 32-bit word) is element j's fifth bit; value
+         *     d*(q - 16)
+         *   Q5_1 (24 bytes): d, m, qh, 16 code bytes; value d*q + m
+         * d*q is exact in F32; the sum with m rounds once. */
+        const int bytes = type == T_Q4_1 ? 20 : type == T_Q5_0 ? 22 : 24;
+        const int has_m = type != T_Q5_0, has_qh = type != T_Q4_1;
+        if (K % 32) return -1;
+        for (b = 0; b < K / 32; b++) {
+            const uint8_t *blk = row + bytes * b;
+            float d = oracle_half_to_float(rd16(blk));
+            float m = has_m ? oracle_half_to_float(rd16(blk + 2)) : 0.0f;
+            const uint8_t *qhp = blk + (has_m ? 4 : 2);
+            uint32_t qh = has_qh ? (uint32_t)qhp[0] | (uint32_t)qhp[1] << 8 | (uint32_t)qhp[2] << 16 |
+                                       (uint32_t)qhp[3] << 24
+                                 : 0;
+            const uint8_t *qs = blk + bytes - 16;
+            for (int j = 0; j < 32; j++) {
+                int nib = j < 16 ? (qs[j] & 15) : (qs[j - 16] >> 4);
+                int q = nib | (int)((qh >> j) & 1) << 4;
+                if (type == T_Q5_0) {
+                    out[32 * b + j] = d * (float)(q - 16);
+                } else {
+                    float v = d * (float)q;
+                    out[32 * b + j] = v + m;
+                }
+            }
+        }
+        return 0;
+    }
     case T_Q4_K:
         /* 144-byte super-block of 256 elements: fp16 d, fp16 dmin, 12 bytes
          * of sub-scales/sub-mins, 128 code bytes. Element e lies in 64-wide
@@ -298,6 +339,9 @@ int64_t oracle_row_bytes(int type, int64_t K) {
     case T_F16: case T_BF16: return 2 * K;
     case T_Q8_0: return K % 32 ? -1 : K / 32 * 34;
     case T_Q4_0: return K % 32 ? -1 : K / 32 * 18;
+    case T_Q4_1: return K % 32 ? -1 : K / 32 * 20;
+    case T_Q5_0: return K % 32 ? -1 : K / 32 * 22;
+    case T_Q5_1: return K % 32 ? -1 : K / 32 * 24;
     case T_Q2_K: return K % 256 ? -1 : K / 256 * 84;
     case T_Q3_K: return K % 256 ? -1 : K / 256 * 110;
     case T_Q4_K: return K % 256 ? -1 : K / 256 * 144;

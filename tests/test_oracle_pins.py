@@ -15,7 +15,8 @@ import torch
 import oracle
 import workloads as wl
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K]
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K,
+         wl.Q6_K]
 
 
 def hexbytes(tokens):
@@ -129,6 +130,38 @@ def test_q4_k_non_integer_scales():
         q = int(codes[32 * c + r]) & 15 if r < 32 else int(codes[32 * c + r - 32]) >> 4
         j = 2 * c + (r >= 32)
         assert got[e] == np.float32(2.0 ** -10 * sc[j] * q - 0.5 * m[j]), e
+
+
+@pytest.mark.parametrize("name,wtype", [("q4_1_a", wl.Q4_1), ("q4_1_b", wl.Q4_1), ("q5_0_a", wl.Q5_0),
+                                        ("q5_0_b", wl.Q5_0), ("q5_1_a", wl.Q5_1)])
+def test_q4_1_q5_hand_built_blocks(golden, name, wtype):
+    g = golden("q4_1_q5_blocks.txt")
+    got = oracle.dequantize(wtype, hexbytes(g[name + "_hex"]), 32)[0]
+    for item in g[name + "_expected"]:
+        e, v = item.split("=")
+        assert got[int(e)] == float(v), (name, item)
+
+
+def test_q5_0_fifth_bits_one_to_one():
+    """d = 1, all nibbles 0, qh = 1 << b: exactly element b becomes 0 (q = 16),
+    the others stay -16; Q5_1 with m = 0 and the same bytes gives 16 there and
+    0 elsewhere, and Q4_1 with qh's bytes removed matches Q5_1 with qh = 0."""
+    for b in range(32):
+        qh = (1 << b).to_bytes(4, "little")
+        blk = np.frombuffer(bytes([0x00, 0x3C]) + qh + bytes(16), dtype=np.uint8)
+        got = oracle.dequantize(wl.Q5_0, blk, 32)[0]
+        assert got[b] == 0 and np.all(np.delete(got, b) == -16), b
+        blk1 = np.frombuffer(bytes([0x00, 0x3C, 0x00, 0x00]) + qh + bytes(16), dtype=np.uint8)
+        got1 = oracle.dequantize(wl.Q5_1, blk1, 32)[0]
+        assert got1[b] == 16 and np.all(np.delete(got1, b) == 0), b
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        d, m = (int(v) for v in rng.integers(0x0400, 0x4400, size=2))
+        codes = rng.integers(0, 256, size=16, dtype=np.uint8).tobytes()
+        head = bytes([d & 255, d >> 8, m & 255, m >> 8])
+        a = oracle.dequantize(wl.Q5_1, np.frombuffer(head + bytes(4) + codes, np.uint8), 32)[0]
+        b_ = oracle.dequantize(wl.Q4_1, np.frombuffer(head + codes, np.uint8), 32)[0]
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
 
 
 def q5_k_superblock(d_bits, dmin_bits, field, qh, qs):

@@ -16,7 +16,8 @@ def test_deterministic_and_seed_sensitive():
     assert not np.array_equal(a["W"], c["W"])
 
 
-@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
+@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K,
+                                   wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
 def test_shapes(wtype):
     blk, nbytes = wl.block_geometry(wtype)
     K = 2 * max(blk, 32)
