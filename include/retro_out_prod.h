@@ -27,6 +27,13 @@
  *   RETRO_Q4_0  18 bytes / 32 elements: fp16 d, 16 bytes of nibbles; element
  *               j<16 = low nibble of byte j, j+16 = its high nibble;
  *               value d*(q-8)
+ *   RETRO_Q4_1  20 bytes / 32 elements: fp16 d, fp16 m, nibbles as Q4_0;
+ *               value d*q + m
+ *   RETRO_Q5_0  22 bytes / 32 elements: fp16 d, 32-bit qh (little-endian),
+ *               nibbles as Q4_0; bit j of qh is element j's fifth bit;
+ *               value d*(q-16)
+ *   RETRO_Q5_1  24 bytes / 32 elements: fp16 d, fp16 m, qh, nibbles as
+ *               Q5_0; value d*q + m
  *   RETRO_Q4_K  144 bytes / 256 elements: fp16 d, fp16 dmin, 12 bytes of
  *               eight 6-bit sub-scales sc_j and sub-mins m_j (GGUF packing),
  *               128 bytes of nibbles (each 64-element chunk c uses 32 bytes:
@@ -50,9 +57,10 @@
  *               128h + 32p + l: bits 2p..2p+1 of byte 32 + 32h + l, minus 4
  *               unless bit 4h+p of hmask[l] is set, sub-scale 8h + 2p + l/16
  *               (stored with +32); value (d*(sc-32))*q
- * The Q2_K, Q3_K, Q5_K and Q6_K layouts are the GGUF ones: the pages that
- * define this operation name the K-quant family only through the Q4_K_M
- * files it runs on.
+ * The Q4_1, Q5_0, Q5_1, Q2_K, Q3_K, Q5_K and Q6_K layouts are the GGUF ones:
+ * the pages that define this operation name them only as members of the
+ * quantized types it admits (and the K-quant family through the Q4_K_M files
+ * it runs on).
  *
  * Pointers: W, G and dst are device pointers (hipMalloc'd or equivalent) and
  * must be 16-byte aligned. dst must not overlap W or G. stream is a
@@ -82,6 +90,9 @@ enum {
     RETRO_F32 = 0,
     RETRO_F16 = 1,
     RETRO_Q4_0 = 2,
+    RETRO_Q4_1 = 3,
+    RETRO_Q5_0 = 6,
+    RETRO_Q5_1 = 7,
     RETRO_Q8_0 = 8,
     RETRO_Q2_K = 10,
     RETRO_Q3_K = 11,
@@ -110,7 +121,7 @@ enum {
 
 /*
  * dst[t][k] = sum_n W[n][k] * G[t][n] for t < T, k < K.
- *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q2_K/Q3_K/Q4_K/Q5_K/Q6_K
+ *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_1/Q5_0/Q5_1/Q2_K/Q3_K/Q4_K/Q5_K/Q6_K
  *   W       device, N * retro_row_bytes(type, K) bytes
  *   G       device, T * N floats
  *   dst     device, T * K floats, overwritten
@@ -202,6 +213,10 @@ int retro_out_prod_variant(int variant, int type, const void *W, const float *G,
  *   ldw  >= retro_row_bytes(type, K)   bytes
  *   ldg  >= N                          floats
  *   ldd  >= K                          floats
+ * ldw must also be a multiple of the largest power of two (at most 16) that
+ * divides the type's block bytes (F32: 4; F16, BF16, Q8_0, Q4_0, Q5_0, Q3_K,
+ * Q6_K: 2; Q4_1, Q2_K: 4; Q5_1: 8; Q4_K, Q5_K: 16), so that each row is as
+ * aligned as the blocks of a contiguous row; otherwise RETRO_E_ALIGN.
  * Errors as retro_out_prod, plus RETRO_E_SHAPE for a stride shorter than its
  * row or a span beyond the size limits. Only the elements of dst's T x K
  * block are written; the bytes between its rows are left as they are.

@@ -43,6 +43,9 @@ bool geometry(int type, Geometry& g) {
         case RETRO_BF16: g = {1, 2}; return true;
         case RETRO_Q8_0: g = {32, 34}; return true;
         case RETRO_Q4_0: g = {32, 18}; return true;
+        case RETRO_Q4_1: g = {32, 20}; return true;
+        case RETRO_Q5_0: g = {32, 22}; return true;
+        case RETRO_Q5_1: g = {32, 24}; return true;
         case RETRO_Q4_K: g = {256, 144}; return true;
         case RETRO_Q5_K: g = {256, 176}; return true;
         case RETRO_Q2_K: g = {256, 84}; return true;
@@ -87,11 +90,23 @@ Strides contiguous(int type, int64_t K, int64_t N) { return {row_bytes_of(type, 
 
 // Strides no shorter than the rows, and spans within the size limits (the
 // shape itself already checked).
+// Alignment of a block within a contiguous row: the largest power of two
+// (at most 16) that divides the block's bytes. The kernels' loads assume it.
+int64_t block_alignment(int type) {
+    Geometry g;
+    if (!geometry(type, g)) return 1;
+    int64_t a = 1;
+    while (a < 16 && g.bytes % (2 * a) == 0) a *= 2;
+    return a;
+}
+
 int check_strides(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     if (s.ldw < row_bytes_of(type, K) || s.ldg < N || s.ldd < K) return RETRO_E_SHAPE;
     if (!product_below(N, s.ldw, kByteLimit) || !product_below(T, s.ldg, kCountLimit) ||
         !product_below(T, s.ldd, kCountLimit))
         return RETRO_E_SHAPE;
+    // every row starts as aligned as a block of a contiguous row
+    if (s.ldw % block_alignment(type)) return RETRO_E_ALIGN;
     return RETRO_OK;
 }
 
@@ -347,6 +362,9 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         case RETRO_BF16: return launch_variant<kBF16>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q8_0: return launch_variant<kQ8_0>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q4_0: return launch_variant<kQ4_0>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q4_1: return launch_variant<kQ4_1>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q5_0: return launch_variant<kQ5_0>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q5_1: return launch_variant<kQ5_1>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q5_K: return launch_variant<kQ5_K>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q2_K: return launch_variant<kQ2_K>(variant, W, G, dst, K, N, T, s, st);
@@ -413,6 +431,9 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
         case RETRO_BF16: return launch_dequant<kBF16>(W, out, K, N, st);
         case RETRO_Q8_0: return launch_dequant<kQ8_0>(W, out, K, N, st);
         case RETRO_Q4_0: return launch_dequant<kQ4_0>(W, out, K, N, st);
+        case RETRO_Q4_1: return launch_dequant<kQ4_1>(W, out, K, N, st);
+        case RETRO_Q5_0: return launch_dequant<kQ5_0>(W, out, K, N, st);
+        case RETRO_Q5_1: return launch_dequant<kQ5_1>(W, out, K, N, st);
         case RETRO_Q4_K: return launch_dequant<kQ4_K>(W, out, K, N, st);
         case RETRO_Q5_K: return launch_dequant<kQ5_K>(W, out, K, N, st);
         case RETRO_Q2_K: return launch_dequant<kQ2_K>(W, out, K, N, st);
@@ -455,7 +476,7 @@ const char* retro_strerror(int code) {
         case RETRO_E_TYPE: return "unknown or unsupported weight type";
         case RETRO_E_SHAPE: return "bad shape: negative size, K not a whole number of blocks, or size over the limits";
         case RETRO_E_NULL: return "NULL buffer";
-        case RETRO_E_ALIGN: return "W, G and dst must be 16-byte aligned";
+        case RETRO_E_ALIGN: return "W, G and dst must be 16-byte aligned, and W rows as aligned as its blocks";
         case RETRO_E_ALIAS: return "dst overlaps W or G";
         case RETRO_E_HIP: return "HIP launch error";
         case RETRO_E_VARIANT: return "kernel variant unknown or not applicable to this type and shape";

@@ -4,7 +4,8 @@
 // bytes into float32 through the primitives below, so one bit-exact check of
 // retro_dequantize covers the arithmetic of all of them.
 //
-// Exactness: a Q8_0/Q4_0 value d*q needs at most 11+8 significant bits, a
+// Exactness: a Q8_0/Q4_0/Q5_0 value d*q needs at most 11+8 significant bits
+// (Q4_1/Q5_1 add the offset m with one rounding), a
 // Q4_K product (d*sc)*q at most 11+6+4 = 21 (Q5_K: 22) and dmin*m at most 17,
 // so every product below is exact in float32 and only the Q4_K/Q5_K
 // subtraction rounds (once, to nearest-even); Q2_K (d*sc)*q needs at most
@@ -23,7 +24,8 @@ namespace retro {
 
 // GGUF tensor-type ids.
 enum : int {
-    kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ8_0 = 8, kQ2_K = 10, kQ3_K = 11, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14, kBF16 = 30
+    kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ4_1 = 3, kQ5_0 = 6, kQ5_1 = 7, kQ8_0 = 8, kQ2_K = 10, kQ3_K = 11, kQ4_K = 12,
+    kQ5_K = 13, kQ6_K = 14, kBF16 = 30
 };
 
 // kBlock: elements per block; kBytes: bytes per block; kGroup: elements one
@@ -34,6 +36,18 @@ template <> struct Format<kF16>  { static constexpr int kBlock = 1,   kBytes = 2
 template <> struct Format<kBF16> { static constexpr int kBlock = 1,   kBytes = 2,   kGroup = 8;  };
 template <> struct Format<kQ8_0> { static constexpr int kBlock = 32,  kBytes = 34,  kGroup = 16; };
 template <> struct Format<kQ4_0> { static constexpr int kBlock = 32,  kBytes = 18,  kGroup = 32; };
+template <> struct Format<kQ4_1> { static constexpr int kBlock = 32,  kBytes = 20,  kGroup = 32; };
+template <> struct Format<kQ5_0> { static constexpr int kBlock = 32,  kBytes = 22,  kGroup = 32; };
+template <> struct Format<kQ5_1> { static constexpr int kBlock = 32,  kBytes = 24,  kGroup = 32; };
+
+// The 32-element nibble formats: element j < 16 is the low nibble of code
+// byte j, element j + 16 its high nibble, after a header of kHeader bytes
+// (fp16 d; Q4_1/Q5_1 an fp16 offset m; Q5_0/Q5_1 a 32-bit word of fifth
+// bits, bit j for element j).
+template <int TYPE> constexpr bool kNibble32 = TYPE == kQ4_0 || TYPE == kQ4_1 || TYPE == kQ5_0 || TYPE == kQ5_1;
+template <int TYPE> constexpr bool kHasOffset = TYPE == kQ4_1 || TYPE == kQ5_1;
+template <int TYPE> constexpr bool kHasFifth = TYPE == kQ5_0 || TYPE == kQ5_1;
+template <int TYPE> constexpr int kHeader = Format<TYPE>::kBytes - 16;
 template <> struct Format<kQ4_K> { static constexpr int kBlock = 256, kBytes = 144, kGroup = 32; };
 template <> struct Format<kQ5_K> { static constexpr int kBlock = 256, kBytes = 176, kGroup = 32; };
 template <> struct Format<kQ6_K> { static constexpr int kBlock = 256, kBytes = 210, kGroup = 32; };
@@ -83,15 +97,38 @@ __device__ __forceinline__ uint32_t nibbles(uint32_t w, bool high) {
     return m;
 }
 
-// Q4_0: from four code bytes take the low (high = false) or high nibbles;
-// value d * (q - 8).
-__device__ __forceinline__ void q4_0_x4(uint32_t w, bool high, float d, float out[4]) {
-    const uint32_t m = nibbles(w, high);
+// Bits first .. first + 3 of a 32-bit fifth-bit word, as bit 4 of the four
+// bytes of a word (a multiply by 0x00204081 places bit i at bit 8i).
+__device__ __forceinline__ uint32_t fifth_bits(uint32_t qh, int first) {
+    return ((((qh >> first) & 15u) * 0x00204081u) & 0x01010101u) << 4;
+}
+
+// Q4_1 / Q5_0 / Q5_1: the low or high nibbles of four code bytes, plus the
+// fifth bits `fifth` (fifth_bits; 0 for Q4_1); value d*q + m, where m is the
+// block's offset (Q5_0: m = -16d, exact, since d*(q - 16) = d*q - 16d).
+__device__ __forceinline__ void q4_1_x4(uint32_t w, bool high, uint32_t fifth, float d, float m, float out[4]) {
+    const uint32_t q = nibbles(w, high) | fifth;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = static_cast<int>((m >> (8 * i)) & 0xFFu);
-        out[i] = d * static_cast<float>(q - 8);
-    }
+    for (int i = 0; i < 4; ++i) out[i] = d * static_cast<float>((q >> (8 * i)) & 0xFFu) + m;
+}
+
+// Scale d, offset m and fifth-bit word qh of a 32-element nibble block whose
+// first 8 bytes are the words h0, h1 (Q4_0: m = -8d; Q5_0: m = -16d; both
+// exact, so d*q + m is the block's value d*(q - 8) or d*(q - 16) with at
+// most a different sign of zero).
+template <int TYPE>
+__device__ __forceinline__ void nibble32_header(uint32_t h0, uint32_t h1, float& d, float& m, uint32_t& qh) {
+    d = half_to_f32(h0 & 0xFFFFu);
+    if constexpr (kHasOffset<TYPE>)
+        m = half_to_f32(h0 >> 16);
+    else
+        m = (TYPE == kQ4_0 ? -8.0f : -16.0f) * d;
+    if constexpr (TYPE == kQ5_0)
+        qh = (h0 >> 16) | (h1 << 16);
+    else if constexpr (TYPE == kQ5_1)
+        qh = h1;
+    else
+        qh = 0u;
 }
 
 // Q4_K sub-scale and sub-min j (0..7) from the 12-byte field, given as its

@@ -98,7 +98,7 @@ struct TileArgs {
 template <int TYPE>
 __device__ __forceinline__ int lds_swizzle(int col) {
     if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) return col ^ (((col >> 6) & 3) << 2);
-    if constexpr (TYPE == kQ4_0 || TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K)
+    if constexpr (kNibble32<TYPE> || TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K)
         return col ^ (((col >> 5) & 7) << 2);
     if constexpr (TYPE == kQ8_0) return col ^ (((col >> 5) & 3) << 2);
     return col;
@@ -415,17 +415,19 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                                 make_float4(e[0], e[1], e[2], e[3]);
                         }
                     }
-                } else if constexpr (TYPE == kQ4_0) {
-                    const uint8_t* blk = raw + 18 * g;
-                    const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+                } else if constexpr (kNibble32<TYPE>) {
+                    const uint8_t* blk = raw + Format<TYPE>::kBytes * g;
+                    float d, m;
+                    uint32_t qh;
+                    nibble32_header<TYPE>(lds_word_a2(blk), lds_word_a2(blk + 4), d, m, qh);
                     const int lo = 32 * g;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t w = lds_word_a2(blk + 2 + 4 * i);
+                        const uint32_t w = lds_word_a2(blk + kHeader<TYPE> + 4 * i);
                         float e[4];
-                        q4_0_x4(w, false, d, e);
+                        q4_1_x4(w, false, fifth_bits(qh, 4 * i), d, m, e);
                         *reinterpret_cast<float4*>(brow + S::swz(lo + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
-                        q4_0_x4(w, true, d, e);
+                        q4_1_x4(w, true, fifth_bits(qh, 16 + 4 * i), d, m, e);
                         *reinterpret_cast<float4*>(brow + S::swz(lo + 16 + 4 * i)) =
                             make_float4(e[0], e[1], e[2], e[3]);
                     }
@@ -564,13 +566,17 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
         const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + 2 + r);
         q8_0_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), d, e);
-    } else if constexpr (TYPE == kQ4_0) {
+    } else if constexpr (kNibble32<TYPE>) {  // 2-byte aligned blocks
         if (k >= K) { e[0] = e[1] = e[2] = e[3] = 0.f; return; }
-        const uint8_t* blk = row + (k >> 5) * 18;
+        const uint8_t* blk = row + (k >> 5) * Format<TYPE>::kBytes;
         const int r = k & 31;
-        const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
-        const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + 2 + (r & 15));
-        q4_0_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), r >= 16, d, e);
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(blk);
+        float d, m;
+        uint32_t qh;
+        nibble32_header<TYPE>(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16), d,
+                              m, qh);
+        const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + kHeader<TYPE> + (r & 15));
+        q4_1_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), r >= 16, fifth_bits(qh, r), d, m, e);
     } else if constexpr (TYPE == kQ4_K) {  // K is a multiple of 256, so k < K always
         const uint8_t* sbp = row + (k >> 8) * 144;
         const int e256 = k & 255, c = e256 >> 6, r = e256 & 63;
@@ -632,9 +638,9 @@ struct SkinnyRaw {
     static constexpr int CW = (TYPE == kF32) ? 4
                               : (TYPE == kF16 || TYPE == kBF16 || TYPE == kQ5_K || TYPE == kQ6_K || TYPE == kQ3_K) ? 2
                                                                                                             : 1;
-    static constexpr int HW = (TYPE == kQ4_K || TYPE == kQ5_K || TYPE == kQ3_K) ? 4
-                              : (TYPE == kQ6_K || TYPE == kQ2_K)                ? 2
-                                                                                : 1;
+    static constexpr int HW = (TYPE == kQ4_K || TYPE == kQ5_K || TYPE == kQ3_K)    ? 4
+                              : (TYPE == kQ6_K || TYPE == kQ2_K || kHasFifth<TYPE>) ? 2
+                                                                                   : 1;
     uint32_t code[4][CW];
     uint32_t hdr[HW];
     float g[4];
@@ -666,8 +672,8 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
         col = 2u * kl;
     } else if constexpr (TYPE == kQ8_0) {
         col = (kl >> 5) * 34 + 2 + (kl & 31);
-    } else if constexpr (TYPE == kQ4_0) {
-        col = (kl >> 5) * 18 + 2 + (kl & 15);
+    } else if constexpr (kNibble32<TYPE>) {
+        col = (kl >> 5) * Format<TYPE>::kBytes + kHeader<TYPE> + (kl & 15);
     } else if constexpr (TYPE == kQ4_K) {
         const int e = kl & 255;
         col = (kl >> 8) * 144 + 16 + 32 * (e >> 6) + (e & 31);
@@ -697,7 +703,8 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
     uint32_t hcol = 0;
     if constexpr (TYPE == kQ4_K) hcol = (k0 >> 8) * 144;
     if constexpr (TYPE == kQ5_K) hcol = (k0 >> 8) * 176;
-    if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) hcol = (min(k0 + 32 * sel, K - 32) >> 5) * Format<TYPE>::kBytes;
+    if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>)
+        hcol = (min(k0 + 32 * sel, K - 32) >> 5) * Format<TYPE>::kBytes;
     o.hdr = uint32_t(hr * a.pitch) + hcol;
     o.hdr2 = 0;
     if constexpr (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) {
@@ -744,7 +751,7 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
             const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, o.code[s], 0, 0);
             r.code[s][0] = v.x;
             r.code[s][1] = v.y;
-        } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+        } else if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>) {
             // code bytes sit at 2-byte alignment inside these blocks; the
             // dword load relies on the unaligned buffer access of gfx9-class GPUs
             r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
@@ -773,6 +780,12 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
     } else if constexpr (TYPE == kQ2_K) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr, 0, 0);
         r.hdr[1] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr2, 0, 0);
+    } else if constexpr (kHasFifth<TYPE>) {  // d, m, qh: the first 8 bytes of a 22- or 24-byte block
+        const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(wr, o.hdr, 0, 0);
+        r.hdr[0] = h.x;
+        r.hdr[1] = h.y;
+    } else if constexpr (TYPE == kQ4_1) {
+        r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr, 0, 0);
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
     } else {
@@ -813,11 +826,11 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
             if (kl + 1 < K) r.code[s][0] |= uint32_t(p[1]) << 16;
             if (kl + 2 < K) r.code[s][1] |= p[2];
             if (kl + 3 < K) r.code[s][1] |= uint32_t(p[3]) << 16;
-        } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+        } else if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>) {
             if (kl < K) {
                 constexpr int BYTES = Format<TYPE>::kBytes;
-                const int off = (TYPE == kQ8_0) ? (kl & 31) : (kl & 15);
-                const uint16_t* c = reinterpret_cast<const uint16_t*>(row + (kl >> 5) * BYTES + 2 + off);
+                const int off = (TYPE == kQ8_0) ? 2 + (kl & 31) : kHeader<TYPE> + (kl & 15);
+                const uint16_t* c = reinterpret_cast<const uint16_t*>(row + (kl >> 5) * BYTES + off);
                 r.code[s][0] = uint32_t(c[0]) | (uint32_t(c[1]) << 16);
             }
         } else if constexpr (TYPE == kQ4_K) {  // K % 256 == 0, so kl < K
@@ -874,10 +887,17 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
                 r.hdr[3] = f[6];
             }
         }
-    } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+    } else if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>) {
+        // the header halfwords (d; m; qh), none past the header
+        constexpr int HH = TYPE == kQ8_0 ? 1 : (kHeader<TYPE> / 2 < 4 ? kHeader<TYPE> / 2 : 4);
         const int kb = k0 + 32 * sel;
-        r.hdr[0] = 0u;
-        if (hvalid && kb < K) r.hdr[0] = *reinterpret_cast<const uint16_t*>(hrow + (kb >> 5) * Format<TYPE>::kBytes);
+#pragma unroll
+        for (int i = 0; i < SkinnyRaw<TYPE>::HW; ++i) r.hdr[i] = 0u;
+        if (hvalid && kb < K) {
+            const uint16_t* h = reinterpret_cast<const uint16_t*>(hrow + (kb >> 5) * Format<TYPE>::kBytes);
+#pragma unroll
+            for (int i = 0; i < HH; ++i) r.hdr[i >> 1] |= uint32_t(h[i]) << (16 * (i & 1));
+        }
     } else {
         r.hdr[0] = 0u;
     }
@@ -909,16 +929,31 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
             bf16x2(r.code[s][0], wv[s][0], wv[s][1]);
             bf16x2(r.code[s][1], wv[s][2], wv[s][3]);
         }
-    } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
+    } else if constexpr (TYPE == kQ8_0) {
         const float dmine = half_to_f32(r.hdr[0]);
 #pragma unroll
+        for (int s = 0; s < 4; ++s) q8_0_x4(r.code[s][0], lane_value(dmine, 2 * (4 * rq + s) + hi), wv[s]);
+    } else if constexpr (kNibble32<TYPE>) {
+        // this lane decodes the header of (row (lane % 32) / 2, block lane % 2)
+        float dmine, mmine;
+        uint32_t qhmine;
+        if constexpr (kHasFifth<TYPE>)
+            nibble32_header<TYPE>(r.hdr[0], r.hdr[1], dmine, mmine, qhmine);
+        else
+            nibble32_header<TYPE>(r.hdr[0], 0u, dmine, mmine, qhmine);
+        const int e = (4 * j) & 31;  // element of the block this lane's 4 columns start at
+#pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const float d = lane_value(dmine, 2 * (4 * rq + s) + hi);
-            if constexpr (TYPE == kQ8_0) {
-                q8_0_x4(r.code[s][0], d, wv[s]);
-            } else {
-                q4_0_x4(r.code[s][0], ((4 * j) & 31) >= 16, d, wv[s]);
-            }
+            const int src = 2 * (4 * rq + s) + hi;
+            const float d = lane_value(dmine, src);
+            float m;
+            if constexpr (kHasOffset<TYPE>)
+                m = lane_value(mmine, src);
+            else
+                m = (TYPE == kQ4_0 ? -8.0f : -16.0f) * d;
+            uint32_t qh = 0u;
+            if constexpr (kHasFifth<TYPE>) qh = uint32_t(__builtin_amdgcn_ds_bpermute(src << 2, int(qhmine)));
+            q4_1_x4(r.code[s][0], e >= 16, fifth_bits(qh, e), d, m, wv[s]);
         }
     } else if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) {  // this lane's pair is sub-block 2c + (lane & 1)
         const int c = (k0 & 255) >> 6;

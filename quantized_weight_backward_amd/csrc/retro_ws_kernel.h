@@ -62,9 +62,9 @@ struct WsShape {
     static constexpr int DWPR = F::kBytes;
     static constexpr int DUNITS = kDense ? (BN / 4) * (BK / 4) / kPThreads : 0;
     static_assert(!kDense || DUNITS * kPThreads * 16 == BN * BK, "dense chunk splits evenly");
-    // Q8_0 / Q4_0: a 32-element block is split over QSPLIT producer threads,
-    // each holding CB code bytes of it.
-    static constexpr int QSPLIT = (TYPE == kQ8_0 || TYPE == kQ4_0) ? kPThreads / (BN * BK / 32) : 1;
+    // Q8_0 and the 32-element nibble blocks: a block is split over QSPLIT
+    // producer threads, each holding CB code bytes of it.
+    static constexpr int QSPLIT = (TYPE == kQ8_0 || kNibble32<TYPE>) ? kPThreads / (BN * BK / 32) : 1;
     static constexpr int CB = TYPE == kQ8_0 ? 32 / QSPLIT : 16 / QSPLIT;
     // words of W each producer thread holds between load and decode
     static constexpr int WWORDS = kDense ? 4 * DWPR * DUNITS
@@ -73,6 +73,7 @@ struct WsShape {
                                   : (TYPE == kQ6_K) ? 9
                                   : (TYPE == kQ2_K) ? 5
                                   : (TYPE == kQ3_K) ? 8
+                                  : kHasFifth<TYPE> ? CB / 4 + 2
                                                     : CB / 4 + 1;
     // Chunks whose loads a producer thread keeps in registers: the chunk
     // being written to LDS plus RING - 1 in flight. Four when a chunk's
@@ -275,10 +276,21 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
                 wreg[4] = f.x; wreg[5] = f.y;
                 wreg[6] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 104, 0, 0);
                 wreg[7] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + 108, 0, 0);
-            } else {  // Q8_0, Q4_0: 2-byte aligned blocks (unaligned buffer loads)
+            } else {  // Q8_0, nibble blocks: 2-byte aligned blocks (unaligned buffer loads)
                 constexpr int CW = S::CB / 4;
-                const uint32_t codes = woff + 2 + S::CB * (p % S::QSPLIT);
-                wreg[CW] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff, 0, 0);
+                constexpr int HDR = TYPE == kQ8_0 ? 2 : kHeader<TYPE>;
+                const uint32_t codes = woff + HDR + S::CB * (p % S::QSPLIT);
+                // header: d (and m), or its first 8 bytes (d, m, qh) for the
+                // fifth-bit blocks, which are 22 or 24 bytes long
+                if constexpr (kHasFifth<TYPE>) {
+                    const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(wr, woff, 0, 0);
+                    wreg[CW] = h.x;
+                    wreg[CW + 1] = h.y;
+                } else if constexpr (TYPE == kQ4_1) {
+                    wreg[CW] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff, 0, 0);
+                } else {
+                    wreg[CW] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff, 0, 0);
+                }
                 if constexpr (CW == 2) {
                     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, codes, 0, 0);
                     wreg[0] = v.x; wreg[1] = v.y;
@@ -428,16 +440,22 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
 #pragma unroll
                     for (int j = 0; j < 4; ++j) col[j * WP] = e[j];
                 }
-            } else {  // Q4_0
+            } else {  // 32-element nibble blocks: code bytes CB s .. of the block
                 constexpr int CW = S::CB / 4;
-                const float d = half_to_f32(wreg[CW]);
+                float d, m;
+                uint32_t qh;
+                if constexpr (kHasFifth<TYPE>)
+                    nibble32_header<TYPE>(wreg[CW], wreg[CW + 1], d, m, qh);
+                else
+                    nibble32_header<TYPE>(wreg[CW], 0u, d, m, qh);
+                const int first = S::CB * (p % S::QSPLIT);
 #pragma unroll
                 for (int w = 0; w < CW; ++w) {
                     float e[4];
-                    q4_0_x4(wreg[w], false, d, e);
+                    q4_1_x4(wreg[w], false, fifth_bits(qh, first + 4 * w), d, m, e);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) ws[wlds[0] + (4 * w + j) * WP] = e[j];
-                    q4_0_x4(wreg[w], true, d, e);
+                    q4_1_x4(wreg[w], true, fifth_bits(qh, 16 + first + 4 * w), d, m, e);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) ws[wlds[1] + (4 * w + j) * WP] = e[j];
                 }

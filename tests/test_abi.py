@@ -37,7 +37,8 @@ def test_enum_values_match_header():
     text = open(HEADER).read()
     for name, value in [("RETRO_F32", q.F32), ("RETRO_F16", q.F16), ("RETRO_Q4_0", q.Q4_0), ("RETRO_Q8_0", q.Q8_0),
                         ("RETRO_Q4_K", q.Q4_K), ("RETRO_Q5_K", q.Q5_K), ("RETRO_Q6_K", q.Q6_K),
-                        ("RETRO_Q2_K", q.Q2_K), ("RETRO_Q3_K", q.Q3_K),
+                        ("RETRO_Q2_K", q.Q2_K), ("RETRO_Q3_K", q.Q3_K), ("RETRO_Q4_1", q.Q4_1),
+                        ("RETRO_Q5_0", q.Q5_0), ("RETRO_Q5_1", q.Q5_1),
                         ("RETRO_BF16", q.BF16), ("RETRO_E_TYPE", q.E_TYPE),
                         ("RETRO_E_SHAPE", q.E_SHAPE), ("RETRO_E_NULL", q.E_NULL), ("RETRO_E_ALIGN", q.E_ALIGN),
                         ("RETRO_E_ALIAS", q.E_ALIAS), ("RETRO_E_HIP", q.E_HIP), ("RETRO_E_VARIANT", q.E_VARIANT),
@@ -48,8 +49,8 @@ def test_enum_values_match_header():
         assert m and int(m.group(1)) == value, name
 
 
-@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K,
-                                   wl.Q6_K])
+@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K,
+                                   wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
 def test_row_bytes_matches_the_format(wtype):
     blk, nbytes = wl.block_geometry(wtype)
     for nblocks in (0, 1, 3, 16, 56):
@@ -69,6 +70,9 @@ def test_row_bytes_of_the_workloads():
     assert q.row_bytes(q.Q6_K, 14336) == 11760
     assert q.row_bytes(q.Q2_K, 4096) == 1344
     assert q.row_bytes(q.Q3_K, 4096) == 1760
+    assert q.row_bytes(q.Q4_1, 5120) == 3200
+    assert q.row_bytes(q.Q5_0, 5120) == 3520
+    assert q.row_bytes(q.Q5_1, 5120) == 3840
     assert q.row_bytes(99, 256) == -1
 
 
@@ -90,8 +94,12 @@ def test_choice():
     assert q.choice(q.Q4_K, 4096, 14336, 4096) == q.VARIANT_WS_128x256
     assert q.choice(q.Q4_0, 5120, 17408, 2048) == q.VARIANT_WS_64x128
     assert q.choice(q.Q4_0, 5120, 17407, 2048) == q.VARIANT_TILE_64x128  # N % 4 != 0: the fallback family
-    for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0):
+    for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0, q.Q4_1, q.Q5_0, q.Q5_1):
         assert q.choice(wtype, 4096, 4096, 512) in q.VARIANT_NAMES
+    for wtype in (q.Q4_1, q.Q5_0, q.Q5_1):  # the 32-element blocks, as Q4_0
+        assert q.choice(wtype, 5120, 17408, 2048) == q.VARIANT_WS_64x128
+        assert q.choice(wtype, 5120, 4096, 16) == q.VARIANT_SKINNY
+        assert q.choice(wtype, 48, 1, 1) == q.E_SHAPE
     for wtype in (q.F32, q.F16, q.BF16):  # dense rows go to the producer/consumer kernel
         assert q.VARIANT_NAMES[q.choice(wtype, 4096, 4096, 512)].startswith("ws_")
     assert q.choice(q.F16, 301, 77, 200) == q.VARIANT_TILE_64x64  # 602-byte rows: no 16-byte units
@@ -130,6 +138,13 @@ def test_strided_variant_applies():
     assert not q.variant_applies_strided(q.VARIANT_TILE_64x128, q.Q4_0, 512, 77, 200, rb, 76, 512)  # ldg < N
     assert not q.variant_applies_strided(q.VARIANT_TILE_64x128, q.Q4_0, 512, 77, 200, rb - 1, 80, 512)
     assert q.variant_applies_strided(q.VARIANT_SKINNY, q.Q4_0, 512, 77, 16, rb + 100, 1000, 600)
+    # W rows must keep the alignment of a contiguous row's blocks
+    assert not q.variant_applies_strided(q.VARIANT_SKINNY, q.Q4_0, 512, 77, 16, rb + 101, 1000, 600)
+    assert not q.variant_applies_strided(q.VARIANT_SKINNY, q.Q4_K, 256, 8, 16, 144 + 8, 8, 256)
+    assert q.variant_applies_strided(q.VARIANT_SKINNY, q.Q4_K, 256, 8, 16, 144 + 16, 8, 256)
+    assert not q.variant_applies_strided(q.VARIANT_SKINNY, q.F32, 64, 8, 16, 258, 8, 64)
+    assert q.variant_applies_strided(q.VARIANT_SKINNY, q.Q5_1, 64, 8, 16, 56, 8, 64)
+    assert not q.variant_applies_strided(q.VARIANT_SKINNY, q.Q5_1, 64, 8, 16, 52, 8, 64)
     # contiguous strides: the same answers as the contiguous query
     for v in q.VARIANT_NAMES:
         assert q.variant_applies_strided(v, q.Q4_K, 768, 96, 130, q.row_bytes(q.Q4_K, 768), 96, 768) == \
@@ -180,6 +195,8 @@ def test_validation_errors_before_any_device_work():
     assert st(q.F32, 0x100000, 1 << 60, 0x200000, 4, 0x300000, 4, 4, 4, 4, None) == q.E_SHAPE  # W span too large
     assert st(q.F32, None, 0, None, 5, None, 0, 0, 5, 5, None) == q.OK                  # empty output
     assert st(q.F32, 0x100000, 16, 0x200008, 8, 0x300000, 4, 4, 4, 4, None) == q.E_ALIGN
+    assert st(q.F32, 0x100000, 18, 0x200000, 4, 0x300000, 4, 4, 4, 4, None) == q.E_ALIGN  # ldw % 4 != 0
+    assert st(q.Q4_0, 0x100000, 19, 0x200000, 4, 0x300000, 32, 32, 4, 4, None) == q.E_ALIGN  # ldw odd
     # dst rows 100 floats apart span (3 * 100 + 4) * 4 bytes from 0x100000: they reach W at 0x100400
     assert st(q.F32, 0x100400, 16, 0x200000, 4, 0x100000, 100, 4, 4, 4, None) == q.E_ALIAS
     assert lib.retro_out_prod_strided_variant(42, q.F32, 0x100000, 16, 0x200000, 4, 0x300000, 4, 4, 4, 4,

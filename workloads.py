@@ -228,6 +228,10 @@ WORKLOADS = {
     "q3_k_n14336_k4096_t4096": dict(type=Q3_K, N=14336, K=4096, T=4096, seed=1011, g_sigma=1.0),
     "q2_k_n4096_k14336_t16": dict(type=Q2_K, N=4096, K=14336, T=16, seed=1012, g_sigma=1.0),
     "q3_k_n4096_k14336_t16": dict(type=Q3_K, N=4096, K=14336, T=16, seed=1013, g_sigma=1.0),
+    # The Q4_0 shape in the other 32-element block types, with their own seeds.
+    "q4_1_n17408_k5120_t2048": dict(type=Q4_1, N=17408, K=5120, T=2048, seed=1014, g_sigma=1e-2),
+    "q5_0_n17408_k5120_t2048": dict(type=Q5_0, N=17408, K=5120, T=2048, seed=1015, g_sigma=1e-2),
+    "q5_1_n17408_k5120_t2048": dict(type=Q5_1, N=17408, K=5120, T=2048, seed=1016, g_sigma=1e-2),
 }
 
 
