@@ -204,7 +204,7 @@ def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
 
 
 def kernel_family(variant: str) -> str:
-    return {"ws": "out_prod_ws_kernel", "tile": "out_prod_tile_kernel"}.get(variant.split("_")[0],
+    return {"ws": "out_prod_ws_kernel", "tile": "out_prod_tile_kernel"}.get(variant.split("_")[0].rstrip("2"),
                                                                          "out_prod_skinny_kernel")
 
 

@@ -179,6 +179,11 @@ const char *retro_strerror(int code);
  *                           needs G rows in 16-byte units (ldg % 4 == 0;
  *                           ldg = N when contiguous) and K % 4 == 0 for F32,
  *                           F16, BF16; the TILE_* kernel takes the others
+ *   RETRO_VARIANT_WS2_64x128  WS_64x128 with two pipelines in one
+ *                           workgroup (even and odd 32-row chunks of W,
+ *                           partial sums added in LDS in that order): two
+ *                           MFMA waves per SIMD for shapes with about one
+ *                           tile per CU
  */
 enum {
     RETRO_VARIANT_AUTO = 0,
@@ -193,7 +198,8 @@ enum {
     RETRO_VARIANT_WS_128x128 = 9,
     RETRO_VARIANT_WS_64x128 = 10,
     RETRO_VARIANT_WS_32x256 = 11,
-    RETRO_VARIANT_WS_32x128 = 12
+    RETRO_VARIANT_WS_32x128 = 12,
+    RETRO_VARIANT_WS2_64x128 = 13
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the

@@ -128,6 +128,8 @@ constexpr TileVariant kTiles[] = {
     {RETRO_VARIANT_WS_64x128, 64, 128, 1.02, true},
     {RETRO_VARIANT_WS_32x256, 32, 256, 1.06, true},
     {RETRO_VARIANT_WS_32x128, 32, 128, 1.04, true},
+    // taken only through the rule at the end of choose()
+    {RETRO_VARIANT_WS2_64x128, 64, 128, 1.50, true},
 };
 
 bool is_dense(int type) { return type == RETRO_F32 || type == RETRO_F16 || type == RETRO_BF16; }
@@ -155,7 +157,8 @@ bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t 
     // the producer/consumer kernel loads G rows in 16-byte units and dense W
     // rows in 4-element units
     if (v.ws && (s.ldg % 4 || (is_dense(type) && K % 4))) return false;
-    (void)N;
+    // chunk offsets run up to a few hundred rows past N in 32-bit arithmetic
+    if (N >= kDimLimit - 4096) return false;
     return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit && int64_t(v.bt) * s.ldg * 4 < (int64_t(1) << 31) &&
            33 * s.ldw < (int64_t(1) << 31);
 }
@@ -185,6 +188,13 @@ int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
             best_cost = cost;
         }
     }
+    // 64 x 128 tiles in two pipelines per workgroup beat one pipeline per
+    // workgroup when a CU gets at most one tile (one pipeline then leaves a
+    // single MFMA wave per SIMD), and for F32 rows at any tile count
+    // (measured: 0.64-0.70 vs 0.58-0.65 of the F32 peak at one tile per CU;
+    // 0.75 vs 0.71 for F32 with several).
+    if (best == RETRO_VARIANT_WS_64x128 && (type == RETRO_F32 || cdiv(T, 64) * cdiv(K, 128) <= kNumCUs))
+        best = RETRO_VARIANT_WS2_64x128;
     return best < 0 ? RETRO_E_SHAPE : best;
 }
 
@@ -242,10 +252,10 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     return launch_status();
 }
 
-template <int TYPE, int WA, int WB, int CT>
+template <int TYPE, int WA, int WB, int CT, int NG = 1>
 int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
               hipStream_t st) {
-    using S = WsShape<TYPE, WA, WB, CT>;
+    using S = WsShape<TYPE, WA, WB, CT, NG>;
     TileArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.G = G;
@@ -263,7 +273,7 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
     a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
-    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG>), dim3(nt), dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
 
@@ -311,6 +321,7 @@ int launch_variant(int variant, const void* W, const float* G, float* dst, int64
             case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, s, st);
             case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2, 2>(W, G, dst, K, N, T, s, st);
             case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS2_64x128: return launch_ws<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, s, st);
             case RETRO_VARIANT_WS_32x128: return launch_ws<TYPE, 1, 1, 1>(W, G, dst, K, N, T, s, st);
             default: break;
         }

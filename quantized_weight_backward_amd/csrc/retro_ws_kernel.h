@@ -10,6 +10,11 @@
 //     chunk c from buffer c % 2, the producers fill buffer (c + 1) % 2 with
 //     chunk c + 1, whose loads they issued one chunk earlier. One workgroup
 //     barrier per 32-row chunk.
+//   * With NG = 2 the workgroup holds two such pipelines (16 waves) over the
+//     same output tile, one for the even and one for the odd chunks, sharing
+//     the barriers; their partial sums are added in LDS at the end. Each SIMD
+//     then holds two consumer waves, whose MFMAs fill each other's waits, for
+//     shapes with too few tiles for two workgroups per CU.
 //   * Both operands are read as 16-byte vectors. G is kept t-major (a row of
 //     32 reduction values per t) and decoded W k-major (a column of 32
 //     reduction values per k), and MFMA step r of phase q contracts rows
@@ -29,12 +34,13 @@
 
 namespace retro {
 
-template <int TYPE, int WA, int WB, int CT>
+template <int TYPE, int WA, int WB, int CT, int NG = 1>
 struct WsShape {
     using F = Format<TYPE>;
     static constexpr bool kDense = F::kBlock == 1;
-    static constexpr int kPThreads = 256;          // producer threads (waves 4-7)
-    static constexpr int kThreads = 2 * kPThreads;  // + 4 consumer waves
+    static_assert(NG == 1 || NG == 2, "one or two pipelines");
+    static constexpr int kPThreads = 256;               // producer threads of one pipeline (4 waves)
+    static constexpr int kThreads = 2 * kPThreads * NG;  // + 4 consumer waves per pipeline
     // consumer waves CT x CK, each (32*WA) x (32*WB) outputs
     static_assert(CT == 1 || CT == 2, "consumer grid 1 x 4 or 2 x 2");
     static constexpr int CK = 4 / CT;
@@ -43,7 +49,7 @@ struct WsShape {
     // Workgroups per CU the register budget is set for: two for the 32-row
     // tiles (46 KB of LDS), whose second workgroup fills the first one's
     // barrier waits; one otherwise.
-    static constexpr int kWgPerCu = BT == 32 ? 2 : 1;
+    static constexpr int kWgPerCu = (BT == 32 && NG == 1) ? 2 : 1;
     static constexpr int BN = 32;
     static_assert(BK == 128 || BK == 256, "K tile of 128 or 256 columns");
     static_assert(!kSuperBlock<TYPE> || BK == 256, "K-quant tiles hold whole super-blocks");
@@ -53,7 +59,7 @@ struct WsShape {
     static constexpr int W_FLOATS = BK * WP;
     static constexpr int BUF_FLOATS = G_FLOATS + W_FLOATS;
     // workgroups that fit on a CU by LDS (160 KB), at most two (16 waves)
-    static constexpr int kResident = (160 * 1024) / (2 * BUF_FLOATS * 4) < 2 ? 1 : 2;
+    static constexpr int kResident = (NG == 2 || (160 * 1024) / (2 * BUF_FLOATS * 4) < 2) ? 1 : 2;
     static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // float4 of G per producer thread
     static_assert(GSLOTS * kPThreads * 4 == BT * BN, "G chunk splits evenly");
     // Dense W: units of 4 rows x 4 consecutive k (16 bytes of F32 or 8 of
@@ -104,13 +110,14 @@ __device__ __forceinline__ int ws_w_index(int k, int n) {
     return k * WP + (n ^ (((k >> 4) & 7) << 2));
 }
 
-template <int TYPE, int WA, int WB, int CT>
-__global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void out_prod_ws_kernel(TileArgs args) {
-    using S = WsShape<TYPE, WA, WB, CT>;
+template <int TYPE, int WA, int WB, int CT, int NG>
+__global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)) void out_prod_ws_kernel(
+    TileArgs args) {
+    using S = WsShape<TYPE, WA, WB, CT, NG>;
     using F = Format<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, WP = S::WP;
 
-    __shared__ __attribute__((aligned(16))) float lds[2 * S::BUF_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds_all[2 * NG * S::BUF_FLOATS];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,15 +125,20 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
     tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, args.group, tt, tk);
     const int t0 = tt * BT, k0 = tk * BK;
     const int K = args.K, N = args.N, T = args.T;
-    const int nchunks = (N + BN - 1) / BN;
+    // pipeline g takes chunks g, g + NG, g + 2 NG, ...: nloc of them each (a
+    // chunk past the last one reads and contracts zeros)
+    const int nloc = ((N + BN - 1) / BN + NG - 1) / NG;
 
     // The two roles run separate loops with the same barrier sequence (one
     // after the prologue, one per chunk): the role test is uniform per wave,
     // and keeping the loops apart keeps the consumers' accumulators and the
     // producers' staging registers from being allocated side by side.
-    if (wave >= 4) {
+    if (wave >= 4 * NG) {
         // ---------------- producer ----------------
-        const int p = tid - S::kPThreads;
+        const int pg = (tid - NG * S::kPThreads) >> 8;  // pipeline
+        const int p = (tid - NG * S::kPThreads) & (S::kPThreads - 1);
+        float* const lds = lds_all + pg * 2 * S::BUF_FLOATS;
+        auto chunk_n0 = [&](int c) { return (pg + NG * c) * BN; };
         const long long kb0 = (long long)(k0 / F::kBlock) * F::kBytes;
         constexpr int R = S::RING;
         float4 gring[R][S::GSLOTS];
@@ -465,8 +477,8 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
         // Chunk j is loaded into slot j % R and written to LDS buffer j % 2.
         // Prologue: start the loads of chunks 0 .. R - 1, fill buffer 0.
         using Zero = std::integral_constant<int, 0>;
-        static_for<R>([&](auto i) { load_chunk(i, i * BN); });
-        store_chunk(Zero{}, Zero{}, 0);
+        static_for<R>([&](auto i) { load_chunk(i, chunk_n0(i)); });
+        store_chunk(Zero{}, Zero{}, chunk_n0(0));
         __syncthreads();
         // While the consumers contract chunk c: write chunk c + 1 to LDS, start
         // the loads of chunk c + R into the slot chunk c left, then the
@@ -476,21 +488,27 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
         auto step = [&](auto i, int c) {
             constexpr int I = decltype(i)::value;
             store_chunk(std::integral_constant<int, (I + 1) % R>{}, std::integral_constant<int, (I + 1) & 1>{},
-                        (c + 1) * BN);
-            load_chunk(i, (c + R) * BN);
+                        chunk_n0(c + 1));
+            load_chunk(i, chunk_n0(c + R));
             __syncthreads();
         };
         int c0 = 0;
-        for (; c0 + R <= nchunks; c0 += R) static_for<R>([&](auto i) { step(i, c0 + decltype(i)::value); });
+        for (; c0 + R <= nloc; c0 += R) static_for<R>([&](auto i) { step(i, c0 + decltype(i)::value); });
         static_for<R>([&](auto i) {
-            if (c0 + decltype(i)::value < nchunks) step(i, c0 + decltype(i)::value);
+            if (c0 + decltype(i)::value < nloc) step(i, c0 + decltype(i)::value);
         });
+        if constexpr (NG == 2) {  // the two barriers of the consumers' reduction
+            __syncthreads();
+            __syncthreads();
+        }
         return;
     }
 
     // ---------------- consumer ----------------
     const int lane = tid & 63;
-    const int wt = wave / S::CK, wk = wave % S::CK;
+    const int cg = wave >> 2, cw = wave & 3;  // pipeline, wave within it
+    const int wt = cw / S::CK, wk = cw % S::CK;
+    const float* const lds = lds_all + cg * 2 * S::BUF_FLOATS;
     const int h = lane >> 5, l32 = lane & 31;
     f32x16 acc[WA][WB];
 #pragma unroll
@@ -548,9 +566,33 @@ __global__ __launch_bounds__(512, (WsShape<TYPE, WA, WB, CT>::kWgPerCu)) void ou
     using Buf1 = std::integral_constant<int, 1>;
     __syncthreads();
     read_phase(Buf0{}, 0, a0, b0);
-    for (int c = 0; c < nchunks; c += 2) {
+    for (int c = 0; c < nloc; c += 2) {
         chunk(Buf0{});
-        if (c + 1 < nchunks) chunk(Buf1{});
+        if (c + 1 < nloc) chunk(Buf1{});
+    }
+    if constexpr (NG == 2) {
+        // pipeline 1's sums -> LDS (register r of lane l of wave w at
+        // r * 256 + 64 w + l), added to pipeline 0's in that fixed order
+        constexpr int NR = WA * WB * 16;
+        static_assert(NR * 256 <= 2 * NG * S::BUF_FLOATS, "reduction fits in LDS");
+        __syncthreads();
+        float* red = lds_all + 64 * cw + lane;
+        if (cg == 1) {
+#pragma unroll
+            for (int a = 0; a < WA; ++a)
+#pragma unroll
+                for (int b = 0; b < WB; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) red[((a * WB + b) * 16 + v) * 256] = acc[a][b][v];
+        }
+        __syncthreads();
+        if (cg == 1) return;
+#pragma unroll
+        for (int a = 0; a < WA; ++a)
+#pragma unroll
+            for (int b = 0; b < WB; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[a][b][v] += red[((a * WB + b) * 16 + v) * 256];
     }
 
     // D layout of v_mfma_f32_32x32x2f32: lane l, register v holds

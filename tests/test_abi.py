@@ -101,7 +101,11 @@ def test_choice():
         assert q.choice(wtype, 5120, 4096, 16) == q.VARIANT_SKINNY
         assert q.choice(wtype, 48, 1, 1) == q.E_SHAPE
     for wtype in (q.F32, q.F16, q.BF16):  # dense rows go to the producer/consumer kernel
-        assert q.VARIANT_NAMES[q.choice(wtype, 4096, 4096, 512)].startswith("ws_")
+        assert q.VARIANT_NAMES[q.choice(wtype, 4096, 4096, 512)].startswith("ws")
+    # one 64 x 128 tile per CU (or F32 rows): two pipelines per workgroup
+    for wtype in (q.F32, q.F16, q.BF16, q.Q4_0, q.Q8_0):
+        assert q.choice(wtype, 4096, 4096, 512) == q.VARIANT_WS2_64x128
+    assert q.choice(q.F32, 5120, 17408, 2048) == q.VARIANT_WS2_64x128
     assert q.choice(q.F16, 301, 77, 200) == q.VARIANT_TILE_64x64  # 602-byte rows: no 16-byte units
     assert q.choice(q.Q4_K, 100, 1, 1) == q.E_SHAPE
     for wtype in (q.Q2_K, q.Q3_K, q.Q5_K, q.Q6_K):  # K-quants: 256-column tiles, as Q4_K
