@@ -238,6 +238,40 @@ int retro_out_prod_strided_variant(int variant, int type, const void *W, int64_t
                                    int64_t ldg, float *dst, int64_t ldd, int64_t K, int64_t N, int64_t T,
                                    void *stream);
 
+/*
+ * Batched retro_out_prod_strided over two outer dimensions, with the weight
+ * broadcast over batches: for i3 < ne3, i2 < ne2
+ *
+ *     dst[i3][i2] = out_prod(W[i3 / (ne3 / ne03)][i2 / (ne2 / ne02)], G[i3][i2])
+ *
+ * This is ggml's OUT_PROD over dimensions 2 and 3, whose source operand may
+ * have fewer matrices than the gradient (the broadcast ratios that the
+ * llama.cpp PR #3 "cuda: out_prod accepts a quantized src0" carries through
+ * its cuBLAS paths; the test table of its section "Measured" names the
+ * broadcast cases). Each matrix is laid out as in retro_out_prod_strided;
+ * matrix (i2, i3) of W starts i2 * sw2 + i3 * sw3 bytes after W, of G and
+ * dst i2 * sg2 + i3 * sg3 and i2 * sd2 + i3 * sd3 floats after G and dst.
+ *   ne02, ne03 >= 1 divide ne2, ne3 >= 0; ne2, ne3 and ne2 * ne3 <= 65535
+ *   strides >= 0; sw2, sw3 multiples of 16 bytes, sg*, sd* multiples of 4
+ *     floats (RETRO_E_ALIGN otherwise), so every matrix is 16-byte aligned
+ *   the dst matrices must not overlap: sd2 spans at least one dst matrix and
+ *     sd3 at least ne2 of them (RETRO_E_ALIAS otherwise); W and G may
+ *     overlap themselves freely
+ * ne2 * ne3 = 0 is a no-op. Errors as retro_out_prod_strided; RETRO_E_ALIAS
+ * compares the whole spans of all batches.
+ */
+int retro_out_prod_batched(int type, const void *W, int64_t ldw, int64_t sw2, int64_t sw3, const float *G,
+                           int64_t ldg, int64_t sg2, int64_t sg3, float *dst, int64_t ldd, int64_t sd2, int64_t sd3,
+                           int64_t K, int64_t N, int64_t T, int64_t ne02, int64_t ne03, int64_t ne2, int64_t ne3,
+                           void *stream);
+
+/* retro_out_prod_batched with a forced kernel variant (RETRO_E_VARIANT when
+ * it does not apply to one matrix). */
+int retro_out_prod_batched_variant(int variant, int type, const void *W, int64_t ldw, int64_t sw2, int64_t sw3,
+                                   const float *G, int64_t ldg, int64_t sg2, int64_t sg3, float *dst, int64_t ldd,
+                                   int64_t sd2, int64_t sd3, int64_t K, int64_t N, int64_t T, int64_t ne02,
+                                   int64_t ne03, int64_t ne2, int64_t ne3, void *stream);
+
 /* The variant retro_out_prod would run for this type and shape, or a
  * negative error code (as retro_out_prod_supported would refuse). Touches no
  * device. */

@@ -60,7 +60,8 @@ LIB_PATH = _build.LIB_PATH
 # The exported symbols, as declared in include/retro_out_prod.h.
 EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided", "retro_out_prod_strided_variant",
            "retro_dequantize", "retro_out_prod_supported", "retro_out_prod_choice", "retro_out_prod_variant_applies",
-           "retro_out_prod_strided_variant_applies", "retro_row_bytes", "retro_strerror")
+           "retro_out_prod_strided_variant_applies", "retro_out_prod_batched", "retro_out_prod_batched_variant",
+           "retro_row_bytes", "retro_strerror")
 
 
 def _load() -> ctypes.CDLL:
@@ -78,6 +79,12 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod_strided.argtypes = [i32, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
     lib.retro_out_prod_strided_variant.restype = i32
     lib.retro_out_prod_strided_variant.argtypes = [i32, i32, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+    lib.retro_out_prod_batched.restype = i32
+    lib.retro_out_prod_batched.argtypes = [i32, vp, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64, i64,
+                                           i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.retro_out_prod_batched_variant.restype = i32
+    lib.retro_out_prod_batched_variant.argtypes = [i32, i32, vp, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64,
+                                                   i64, i64, i64, i64, i64, i64, i64, i64, vp]
     lib.retro_out_prod_strided_variant_applies.restype = i32
     lib.retro_out_prod_strided_variant_applies.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64]
     lib.retro_dequantize.restype = i32
@@ -192,6 +199,56 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
     else:
         _check(lib.retro_out_prod_strided_variant(int(variant), int(wtype), _ptr(W), ldw, _ptr(G), ldg, _ptr(out),
                                                   ldd, int(K), int(N), int(T), _stream_handle(stream)))
+    return out
+
+
+def _as4(t):
+    while t.dim() < 4:
+        t = t.unsqueeze(0)
+    return t
+
+
+def _matrix_strides(t, rows, name):
+    """(row stride, stride of dim 1, stride of dim 0) in elements of a 4-D
+    view with contiguous rows; strides of size-1 dimensions read as 0 and
+    a single row's stride as its length."""
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
+    ld = int(t.stride(2)) if t.shape[2] > 1 else rows
+    return ld, (int(t.stride(1)) if t.shape[1] > 1 else 0), (int(t.stride(0)) if t.shape[0] > 1 else 0)
+
+
+def out_prod_batched(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, stream=None):
+    """Batched out_prod over two outer dimensions with W broadcast (see
+    retro_out_prod_batched): W uint8 [ne03, ne02, N, >= row_bytes],
+    G float32 [ne3, ne2, T, N], out float32 [ne3, ne2, T, K] (leading
+    dimensions may be left out; ne03 divides ne3 and ne02 divides ne2).
+    Rows are contiguous; rows and matrices may be any distance apart."""
+    _device_tensor(W, "W", contiguous=False)
+    _device_tensor(G, "G", contiguous=False)
+    if G.dtype != torch.float32 or not 2 <= G.dim() <= 4 or W.dtype != torch.uint8 or not 2 <= W.dim() <= 4:
+        raise ValueError("W must be a 2-4-D uint8 tensor and G a 2-4-D float32 tensor")
+    W4, G4 = _as4(W), _as4(G)
+    ne03, ne02, N, wcols = W4.shape
+    ne3, ne2, T, n_g = G4.shape
+    rb = row_bytes(wtype, K)
+    if rb < 0:
+        _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
+    if n_g != N or wcols < rb:
+        raise ValueError(f"W must hold N = {n_g} rows of at least {rb} bytes per matrix")
+    if out is None:
+        out = torch.empty(tuple(G.shape[:-2]) + (T, K), dtype=torch.float32, device=G.device)
+    else:
+        _device_tensor(out, "out", contiguous=False)
+        if out.dtype != torch.float32 or tuple(out.shape) != tuple(G.shape[:-2]) + (T, K):
+            raise ValueError("out must be float32 with G's leading dimensions and T x K matrices")
+    D4 = _as4(out)
+    ldw, sw2, sw3 = _matrix_strides(W4, rb, "W")
+    ldg, sg2, sg3 = _matrix_strides(G4, N, "G")
+    ldd, sd2, sd3 = _matrix_strides(D4, K, "out")
+    _check(lib.retro_out_prod_batched_variant(int(variant), int(wtype), _ptr(W), ldw, sw2, sw3, _ptr(G), ldg, sg2,
+                                              sg3, _ptr(out), ldd, sd2, sd3, int(K), int(N), int(T), int(ne02),
+                                              int(ne03), int(ne2), int(ne3), _stream_handle(stream)))
     return out
 
 

@@ -79,12 +79,21 @@ int check_shape(int type, int64_t K, int64_t N, int64_t T) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Row strides of the three operands.
+// Layout of the three operands: row strides, and the batches over two outer
+// dimensions (ne2 x ne3 products; W has ne02 x ne03 matrices, each serving
+// ne2 / ne02 x ne3 / ne03 consecutive batches).
 struct Strides {
     int64_t ldw;  // bytes between consecutive W rows (>= the row's bytes)
     int64_t ldg;  // floats between consecutive G rows (>= N)
     int64_t ldd;  // floats between consecutive dst rows (>= K)
+    int64_t ne02 = 1, ne03 = 1, ne2 = 1, ne3 = 1;
+    int64_t sw2 = 0, sw3 = 0;  // bytes between W matrices
+    int64_t sg2 = 0, sg3 = 0;  // floats between G matrices
+    int64_t sd2 = 0, sd3 = 0;  // floats between dst matrices
+    int64_t batches() const { return ne2 * ne3; }
 };
+
+constexpr int64_t kBatchLimit = 65535;  // workgroups along the grid's second dimension
 
 Strides contiguous(int type, int64_t K, int64_t N) { return {row_bytes_of(type, K), N, K}; }
 
@@ -107,6 +116,15 @@ int check_strides(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
         return RETRO_E_SHAPE;
     // every row starts as aligned as a block of a contiguous row
     if (s.ldw % block_alignment(type)) return RETRO_E_ALIGN;
+    // batches: W's counts divide the others', strides non-negative, spans
+    // within the limits, every matrix starting as aligned as a single one
+    if (s.ne02 < 1 || s.ne03 < 1 || s.ne2 < 0 || s.ne3 < 0 || s.ne2 % s.ne02 || s.ne3 % s.ne03)
+        return RETRO_E_SHAPE;
+    if (s.ne2 > kBatchLimit || s.ne3 > kBatchLimit || s.batches() > kBatchLimit) return RETRO_E_SHAPE;
+    const int64_t st[6] = {s.sw2, s.sw3, s.sg2, s.sg3, s.sd2, s.sd3};
+    for (int64_t v : st)
+        if (v < 0 || v >= kCountLimit / kBatchLimit) return RETRO_E_SHAPE;
+    if (s.sw2 % 16 || s.sw3 % 16 || s.sg2 % 4 || s.sg3 % 4 || s.sd2 % 4 || s.sd3 % 4) return RETRO_E_ALIGN;
     return RETRO_OK;
 }
 
@@ -181,7 +199,7 @@ int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     for (const auto& v : kTiles) {
         if (!tile_applies(v, type, K, N, T, s)) continue;
         const double weight = v.penalty * (v.ws == prefers_ws(type) ? 1.0 : kOtherFamily);
-        const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk);
+        const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk) * s.batches();
         const double cost = double(cdiv(nt, kNumCUs)) * v.bt * v.bk * weight;
         if (best < 0 || cost < best_cost) {
             best = v.id;
@@ -193,7 +211,8 @@ int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     // single MFMA wave per SIMD), and for F32 rows at any tile count
     // (measured: 0.64-0.70 vs 0.58-0.65 of the F32 peak at one tile per CU;
     // 0.75 vs 0.71 for F32 with several).
-    if (best == RETRO_VARIANT_WS_64x128 && (type == RETRO_F32 || cdiv(T, 64) * cdiv(K, 128) <= kNumCUs))
+    if (best == RETRO_VARIANT_WS_64x128 &&
+        (type == RETRO_F32 || cdiv(T, 64) * cdiv(K, 128) * s.batches() <= kNumCUs))
         best = RETRO_VARIANT_WS2_64x128;
     return best < 0 ? RETRO_E_SHAPE : best;
 }
@@ -223,6 +242,20 @@ int group_height(int64_t tiles_t, int64_t tiles_k, int wg_per_cu, double g_bytes
 void clear_last_error() { (void)hipGetLastError(); }
 int launch_status() { return hipGetLastError() == hipSuccess ? RETRO_OK : RETRO_E_HIP; }
 
+BatchArgs batch_args(const Strides& s) {
+    BatchArgs b;
+    b.ne2 = int(s.ne2);
+    b.r2 = int(s.ne2 / s.ne02);
+    b.r3 = int(s.ne3 / s.ne03);
+    b.w2 = s.sw2;
+    b.w3 = s.sw3;
+    b.g2 = s.sg2;
+    b.g3 = s.sg3;
+    b.d2 = s.sd2;
+    b.d3 = s.sd3;
+    return b;
+}
+
 template <int TYPE, int WA, int WB, int WGT, int WGK>
 int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
                 hipStream_t st) {
@@ -237,18 +270,23 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     a.pitch = s.ldw;
     a.ldg = s.ldg;
     a.ldd = s.ldd;
-    // Widest staging load that the row pitch and the tile span are both
-    // multiples of (the base pointer is 16-byte aligned).
+    // Widest staging load that the row pitch, the tile span and the row's
+    // bytes are all multiples of (the base pointer is 16-byte aligned): then
+    // no load straddles the end of W, where a buffer load reads zero for the
+    // whole word.
+    const int64_t rbytes = row_bytes_of(TYPE, K);
     int wvec = 16;
-    while (wvec > 2 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0)) wvec >>= 1;
+    while (wvec > 2 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0 || (rbytes % wvec) != 0)) wvec >>= 1;
     a.wvec = wvec;
     a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
     a.group = group_height(a.tiles_t, a.tiles_k, 2, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
+    a.batch = batch_args(s);
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
-    hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt, unsigned(s.batches())),
+                       dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
 
@@ -271,9 +309,11 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
     a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
+    a.batch = batch_args(s);
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
-    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG>), dim3(nt, unsigned(s.batches())),
+                       dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
 
@@ -293,7 +333,8 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     a.ldd = s.ldd;
     a.wide = (K % 4 == 0) ? 1 : 0;
     a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
-    const dim3 grid(unsigned(cdiv(K, 64))), block(kWaves * 64);
+    a.batch = batch_args(s);
+    const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches())), block(kWaves * 64);
     clear_last_error();
     if (a.wide && a.gvec)
         hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true>), grid, block, 0, st, a);
@@ -352,14 +393,21 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
     if (rc != RETRO_OK) return rc;
     rc = check_strides(type, K, N, T, s);
     if (rc != RETRO_OK) return rc;
-    if (T == 0 || K == 0) return RETRO_OK;
-    // bytes each operand spans
+    if (T == 0 || K == 0 || s.batches() == 0) return RETRO_OK;
+    // bytes each operand spans: one matrix, then all batches
     const int64_t w_bytes = N > 0 ? (N - 1) * s.ldw + row_bytes_of(type, K) : 0;
     const int64_t g_bytes = N > 0 ? ((T - 1) * s.ldg + N) * 4 : 0;
     const int64_t d_bytes = ((T - 1) * s.ldd + K) * 4;
+    const int64_t w_all = N > 0 ? (s.ne03 - 1) * s.sw3 + (s.ne02 - 1) * s.sw2 + w_bytes : 0;
+    const int64_t g_all = N > 0 ? ((s.ne3 - 1) * s.sg3 + (s.ne2 - 1) * s.sg2) * 4 + g_bytes : 0;
+    const int64_t d_all = ((s.ne3 - 1) * s.sd3 + (s.ne2 - 1) * s.sd2) * 4 + d_bytes;
     if (!dst || (N > 0 && (!W || !G))) return RETRO_E_NULL;
     if (!aligned16(dst) || (N > 0 && (!aligned16(W) || !aligned16(G)))) return RETRO_E_ALIGN;
-    if (overlap(dst, d_bytes, W, w_bytes) || overlap(dst, d_bytes, G, g_bytes)) return RETRO_E_ALIAS;
+    if (overlap(dst, d_all, W, w_all) || overlap(dst, d_all, G, g_all)) return RETRO_E_ALIAS;
+    // the dst matrices must not overlap one another: batch i2 after i2 - 1,
+    // batch i3 after the whole of i3 - 1
+    if ((s.ne2 > 1 && s.sd2 * 4 < d_bytes) || (s.ne3 > 1 && s.sd3 * 4 < (s.ne2 - 1) * s.sd2 * 4 + d_bytes))
+        return RETRO_E_ALIAS;
     if (variant == RETRO_VARIANT_AUTO) {
         variant = choose(type, K, N, T, s);
         if (variant < 0) return variant;
@@ -424,6 +472,32 @@ int retro_out_prod_strided_variant(int variant, int type, const void* W, int64_t
                                    int64_t ldg, float* dst, int64_t ldd, int64_t K, int64_t N, int64_t T,
                                    void* stream) {
     return out_prod_impl(variant, type, W, G, dst, K, N, T, Strides{ldw, ldg, ldd}, stream);
+}
+
+int retro_out_prod_batched_variant(int variant, int type, const void* W, int64_t ldw, int64_t sw2, int64_t sw3,
+                                   const float* G, int64_t ldg, int64_t sg2, int64_t sg3, float* dst, int64_t ldd,
+                                   int64_t sd2, int64_t sd3, int64_t K, int64_t N, int64_t T, int64_t ne02,
+                                   int64_t ne03, int64_t ne2, int64_t ne3, void* stream) {
+    Strides s{ldw, ldg, ldd};
+    s.ne02 = ne02;
+    s.ne03 = ne03;
+    s.ne2 = ne2;
+    s.ne3 = ne3;
+    s.sw2 = sw2;
+    s.sw3 = sw3;
+    s.sg2 = sg2;
+    s.sg3 = sg3;
+    s.sd2 = sd2;
+    s.sd3 = sd3;
+    return out_prod_impl(variant, type, W, G, dst, K, N, T, s, stream);
+}
+
+int retro_out_prod_batched(int type, const void* W, int64_t ldw, int64_t sw2, int64_t sw3, const float* G,
+                           int64_t ldg, int64_t sg2, int64_t sg3, float* dst, int64_t ldd, int64_t sd2, int64_t sd3,
+                           int64_t K, int64_t N, int64_t T, int64_t ne02, int64_t ne03, int64_t ne2, int64_t ne3,
+                           void* stream) {
+    return retro_out_prod_batched_variant(RETRO_VARIANT_AUTO, type, W, ldw, sw2, sw3, G, ldg, sg2, sg3, dst, ldd,
+                                          sd2, sd3, K, N, T, ne02, ne03, ne2, ne3, stream);
 }
 
 int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, void* stream) {

@@ -74,6 +74,25 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_t, int tiles_k, int
 // Tiled kernel
 // ---------------------------------------------------------------------------
 
+// Batches over two outer dimensions (i2 < ne2, i3 < ne3 with ne2 * ne3 =
+// gridDim.y): batch (i2, i3) reads W matrix (i2 / r2, i3 / r3), which
+// broadcasts one W matrix over r2 x r3 batches, and G and dst matrix (i2, i3).
+// Matrices are w2 / w3 bytes (W) and g2 / g3, d2 / d3 floats (G, dst) apart.
+struct BatchArgs {
+    int ne2, r2, r3;
+    long long w2, w3, g2, g3, d2, d3;
+};
+
+// Moves the three base pointers to this workgroup's batch (blockIdx.y).
+template <typename Args>
+__device__ __forceinline__ void enter_batch(Args& a) {
+    const int b = blockIdx.y;
+    const int i2 = b % a.batch.ne2, i3 = b / a.batch.ne2;
+    a.W += (long long)(i3 / a.batch.r3) * a.batch.w3 + (long long)(i2 / a.batch.r2) * a.batch.w2;
+    a.G += (long long)i3 * a.batch.g3 + (long long)i2 * a.batch.g2;
+    a.dst += (long long)i3 * a.batch.d3 + (long long)i2 * a.batch.d2;
+}
+
 struct TileArgs {
     const uint8_t* W;
     const float* G;
@@ -86,6 +105,7 @@ struct TileArgs {
     int group;        // row tiles per group of the tile order (tile_coords)
     long long ldg;    // floats between consecutive G rows (>= N)
     long long ldd;    // floats between consecutive dst rows (>= K)
+    BatchArgs batch;
 };
 
 // Column swizzle of a decoded W tile in LDS: XOR column bits 2-4 with
@@ -151,6 +171,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
     __shared__ __attribute__((aligned(16))) float Bs[BN * BP];
     __shared__ __attribute__((aligned(16))) uint8_t Raw[S::kStaged ? S::LDS_RAW : 16];
 
+    enter_batch(args);
     const int tid = threadIdx.x;
     int tt, tk;
     tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, args.group, tt, tk);
@@ -524,6 +545,7 @@ struct SkinnyArgs {
     long long ldd;    // floats between consecutive dst rows (>= K)
     int wide;  // 1: W rows allow the widest load of 4 consecutive elements
     int gvec;  // 1: G rows take float4 loads
+    BatchArgs batch;
 };
 
 // Four consecutive elements k, k+1, k+2, k+3 (k a multiple of 4) of W row
@@ -1006,6 +1028,7 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
     constexpr int KS = 64;  // dst columns per workgroup
     __shared__ __attribute__((aligned(16))) float part[NWAVES * 16 * KS];
 
+    enter_batch(args);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int K = args.K, N = args.N, T = args.T;

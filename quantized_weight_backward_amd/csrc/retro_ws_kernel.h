@@ -119,6 +119,7 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
 
     __shared__ __attribute__((aligned(16))) float lds_all[2 * NG * S::BUF_FLOATS];
 
+    enter_batch(args);
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int tt, tk;

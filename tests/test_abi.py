@@ -155,6 +155,27 @@ def test_strided_variant_applies():
             q.variant_applies(v, q.Q4_K, 768, 96, 130)
 
 
+def test_batched_validation():
+    b = q.lib.retro_out_prod_batched
+    # (type, W, ldw, sw2, sw3, G, ldg, sg2, sg3, dst, ldd, sd2, sd3, K, N, T, ne02, ne03, ne2, ne3, stream)
+    W, G, D = 0x100000, 0x200000, 0x300000
+    ok = dict(sw=(64, 128), sg=(16, 32), sd=(16, 32), ne=(1, 1, 2, 2))
+
+    def call(sw=ok["sw"], sg=ok["sg"], sd=ok["sd"], ne=ok["ne"], w=W, g=G, d=D):
+        return b(q.F32, w, 16, sw[0], sw[1], g, 4, sg[0], sg[1], d, 4, sd[0], sd[1], 4, 4, 4, *ne, None)
+    assert call(ne=(2, 1, 3, 2)) == q.E_SHAPE           # ne02 does not divide ne2
+    assert call(ne=(0, 1, 2, 2)) == q.E_SHAPE           # no W matrix
+    assert call(ne=(1, 1, 300, 300)) == q.E_SHAPE       # beyond 65535 batches
+    assert call(sg=(-16, 32)) == q.E_SHAPE              # negative stride
+    assert call(sw=(8, 128)) == q.E_ALIGN               # W matrices not 16-byte aligned
+    assert call(sd=(18, 36)) == q.E_ALIGN
+    assert call(sd=(8, 32)) == q.E_ALIAS                # dst matrices (16 floats) overlap along i2
+    assert call(sd=(16, 16)) == q.E_ALIAS               # ... and along i3
+    assert call(d=0x100010) == q.E_ALIAS                # dst over W
+    assert call(ne=(1, 1, 0, 2), w=None, g=None, d=None) == q.OK   # no batches: a no-op
+    assert call(w=None) == q.E_NULL
+
+
 def test_strerror_covers_every_code():
     for code in (q.OK, q.E_TYPE, q.E_SHAPE, q.E_NULL, q.E_ALIGN, q.E_ALIAS, q.E_HIP, q.E_VARIANT):
         s = q.strerror(code)

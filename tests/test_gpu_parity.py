@@ -320,16 +320,19 @@ STRIDED = [(wl.Q4_K, 768, 96, 130), (wl.Q4_0, 512, 77, 200), (wl.F16, 264, 100, 
 
 
 @pytest.mark.parametrize("wtype,K,N,T", STRIDED)
-@pytest.mark.parametrize("gpad", [4, 3])
-def test_strided_operands_match_oracle(q, wtype, K, N, T, gpad):
+@pytest.mark.parametrize("gpad,wpad", [(4, "48"), (3, "48"), (4, "to16")])
+def test_strided_operands_match_oracle(q, wtype, K, N, T, gpad, wpad):
     """G as a column slice of a wider buffer (row stride N + gpad + 4, first
     column 4), dst as a column block of a wider buffer, W rows padded by 48
-    bytes: every kernel that takes the strides matches the oracle on the
-    contiguous data, and the rest of dst's buffer keeps its sentinel."""
+    bytes or up to a multiple of 16 (a row pitch wider loads fit while the
+    rows themselves end off that grid): every kernel that takes the strides
+    matches the oracle on the contiguous data, and the rest of dst's buffer
+    keeps its sentinel."""
     c = wl.make_case(wtype, N, K, T, seed=900 + N)
     _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
     rb = wl.row_bytes(wtype, K)
-    wbig = torch.zeros((N, rb + 48), dtype=torch.uint8, device="cuda")
+    ldw = rb + 48 if wpad == "48" else (rb + 15) // 16 * 16
+    wbig = torch.zeros((N, ldw), dtype=torch.uint8, device="cuda")
     wbig[:, :rb] = dev(c["W"])
     W = wbig[:, :rb]
     ldg = N + gpad + 4
@@ -339,7 +342,7 @@ def test_strided_operands_match_oracle(q, wtype, K, N, T, gpad):
     ldd = K + 12
     ran = []
     for v in ["auto", "skinny"] + tile_variants(wtype):
-        if v != "auto" and not q.variant_applies_strided(variant_id(q, v), wtype, K, N, T, rb + 48, ldg, ldd):
+        if v != "auto" and not q.variant_applies_strided(variant_id(q, v), wtype, K, N, T, ldw, ldg, ldd):
             continue
         dbig = torch.full((T, ldd), 7.0, device="cuda")
         out = dbig[:, 8:8 + K]
@@ -354,6 +357,60 @@ def test_strided_operands_match_oracle(q, wtype, K, N, T, gpad):
     assert ("skinny" in families) == (T <= 16), ran
     if T > 16:
         assert "tile" in families and (("ws" in families) == (ldg % 4 == 0)), ran
+
+
+# --- batches over two outer dimensions, with W broadcast ------------------------------
+
+BATCHED = [(wl.Q4_K, 512, 64, 40, ["auto", "ws_64x256", "tile_64x256"]),
+           (wl.Q5_0, 352, 48, 12, ["auto", "skinny", "tile_64x64"]),
+           (wl.BF16, 264, 40, 70, ["auto", "ws_32x128", "ws2_64x128", "tile_128x128"])]
+
+
+@pytest.mark.parametrize("wtype,K,N,T,variants", BATCHED)
+def test_batched_broadcast_matches_oracle(q, wtype, K, N, T, variants):
+    """dst[i3][i2] = out_prod(W[i3 / 2][i2 / 2], G[i3][i2]) over 2 x 4 batches
+    with 1 x 2 W matrices; W rows padded to 16-byte multiples, G a permuted
+    view (its i3 batches closer than its i2 ones), dst matrices with gaps.
+    Every batch matches the oracle on its own pair of matrices, and the
+    gaps of dst keep their sentinel."""
+    ne03, ne02, ne3, ne2 = 1, 2, 2, 4
+    rb = wl.row_bytes(wtype, K)
+    ldw = (rb + 15) // 16 * 16
+    cases = [wl.make_case(wtype, N, K, T, seed=1200 + i) for i in range(ne03 * ne02)]
+    wbig = torch.zeros((ne03, ne02, N, ldw), dtype=torch.uint8, device="cuda")
+    for i, c in enumerate(cases):
+        wbig[i // ne02, i % ne02, :, :rb] = dev(c["W"])
+    rng = np.random.default_rng(77)
+    g_host = rng.standard_normal((ne2, ne3, T, N)).astype(np.float32)
+    G = dev(g_host).permute(1, 0, 2, 3)              # [ne3, ne2, T, N], not contiguous
+    for v in variants:
+        if v != "auto" and not q.variant_applies(variant_id(q, v), wtype, K, N, T):
+            continue
+        dbig = torch.full((ne3, ne2, T + 1, K + 4), 7.0, device="cuda")
+        out = dbig[:, :, :T, :K]
+        q.out_prod_batched(wtype, wbig, G, K, out=out, variant=variant_id(q, v) if v != "auto" else 0)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for i3 in range(ne3):
+            for i2 in range(ne2):
+                c = cases[(i3 // (ne3 // ne03)) * ne02 + i2 // (ne2 // ne02)]
+                _, acc, ab = oracle.out_prod(wtype, c["W"], g_host[i2, i3], K)
+                check_close(got[i3, i2], acc, ab, f"batch {i3},{i2} {v}")
+        rest = dbig.clone()
+        rest[:, :, :T, :K] = 7.0
+        assert bool((rest == 7.0).all()), v
+
+
+def test_batched_empty_and_single(q):
+    """No batches is a no-op; one batch equals retro_out_prod."""
+    c = wl.make_case(wl.Q4_0, 33, 256, 20, seed=5)
+    W, G = dev(c["W"]).view(33, -1), dev(c["G"])
+    ref = run(q, c)
+    one = q.out_prod_batched(wl.Q4_0, W, G, 256)
+    torch.cuda.synchronize()
+    assert np.array_equal(one.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    empty = torch.zeros((0, 20, 256), device="cuda")
+    q.out_prod_batched(wl.Q4_0, W, G.unsqueeze(0)[:0], 256, out=empty)
 
 
 # --- full-size workloads ----------------------------------------------------------
