@@ -41,6 +41,11 @@
  * PR's commit message lists them among the swept types but prints no block),
  * the GGUF ones, pinned to hand-derived fixtures.
  *
+ * Parity unpinned against the pages: MXFP4. The PR's type sweep names it
+ * and prints no block; the element and scale encodings are those of the OCP
+ * Microscaling (MX) specification (E2M1 elements, an E8M0 shared scale), in
+ * the GGUF block order, pinned to hand-derived fixtures.
+ *
  * Parity unpinned against the pages: Q2_K, Q3_K, Q5_K and Q6_K as a whole.
  * The pages name the K-quant family only through the Q4_K_M files it is
  * used in; these layouts are the GGUF ones, and the tests pin them to
@@ -55,8 +60,17 @@
 
 enum {
     T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q4_1 = 3, T_Q5_0 = 6, T_Q5_1 = 7, T_Q8_0 = 8, T_Q2_K = 10, T_Q3_K = 11,
-    T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_BF16 = 30
+    T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_BF16 = 30, T_MXFP4 = 39
 };
+
+/* An E2M1 code (bit 3 sign, bits 2..1 exponent, bit 0 mantissa; exponent
+ * bias 1, no infinities or NaNs): exponent field 0 is the subnormal range,
+ * value m/2, otherwise (1 + m/2) * 2^(E - 1). */
+static double e2m1_value(int code) {
+    const int E = (code >> 1) & 3, m = code & 1;
+    const double mag = E == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, E - 1);
+    return (code & 8) ? -mag : mag;
+}
 
 /* IEEE-754 binary16 -> binary32: 1 sign bit, 5 exponent bits (bias 15), 10
  * fraction bits. Exponent 0: subnormal, value = frac * 2^-24. Exponent 31:
@@ -179,6 +193,22 @@ int oracle_decode_row(int type, const uint8_t *row, int64_t K, float *out) {
         }
         return 0;
     }
+    case T_MXFP4:
+        /* 17-byte block of 32 elements: an E8M0 scale byte e (the scale is
+         * 2^(e - 127); e = 255 is NaN), then 16 code bytes. Element j < 16
+         * is the low nibble of code byte j, element j + 16 its high nibble.
+         * value = e2m1(code) * scale, formed exactly in double and rounded
+         * once to F32 (exact unless it overflows). */
+        if (K % 32) return -1;
+        for (b = 0; b < K / 32; b++) {
+            const uint8_t *blk = row + 17 * b;
+            const double scale = blk[0] == 255 ? NAN : ldexp(1.0, (int)blk[0] - 127);
+            for (int j = 0; j < 16; j++) {
+                out[32 * b + j] = (float)(e2m1_value(blk[1 + j] & 15) * scale);
+                out[32 * b + j + 16] = (float)(e2m1_value(blk[1 + j] >> 4) * scale);
+            }
+        }
+        return 0;
     case T_Q4_K:
         /* 144-byte super-block of 256 elements: fp16 d, fp16 dmin, 12 bytes
          * of sub-scales/sub-mins, 128 code bytes. Element e lies in 64-wide
@@ -347,6 +377,7 @@ int64_t oracle_row_bytes(int type, int64_t K) {
     case T_Q4_K: return K % 256 ? -1 : K / 256 * 144;
     case T_Q5_K: return K % 256 ? -1 : K / 256 * 176;
     case T_Q6_K: return K % 256 ? -1 : K / 256 * 210;
+    case T_MXFP4: return K % 32 ? -1 : K / 32 * 17;
     default: return -1;
     }
 }

@@ -15,8 +15,8 @@ import torch
 import oracle
 import workloads as wl
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K,
-         wl.Q6_K]
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K,
+         wl.Q5_K, wl.Q6_K]
 
 
 def hexbytes(tokens):
@@ -140,6 +140,46 @@ def test_q4_1_q5_hand_built_blocks(golden, name, wtype):
     for item in g[name + "_expected"]:
         e, v = item.split("=")
         assert got[int(e)] == float(v), (name, item)
+
+
+def _fixture_value(v):
+    return float.fromhex(v) if "p" in v else float(v)
+
+
+@pytest.mark.parametrize("name", ["mx_a", "mx_b", "mx_c", "mx_d", "mx_e"])
+def test_mxfp4_hand_built_blocks(golden, name):
+    g = golden("mxfp4_blocks.txt")
+    got = oracle.dequantize(wl.MXFP4, hexbytes(g[name + "_hex"]), 32)[0]
+    for item in g[name + "_expected"]:
+        e, v = item.split("=")
+        want = np.float32(_fixture_value(v))
+        if np.isnan(want):
+            assert np.isnan(got[int(e)]), (name, item)
+        else:
+            assert got[int(e)] == want and np.signbit(got[int(e)]) == np.signbit(want), (name, item)
+
+
+def test_mxfp4_structure():
+    """Every code byte under several scales: a nibble decodes the same in
+    either half of a byte, the sign bit negates (zero included), the eight
+    magnitudes rise strictly from 0, and one more in the scale byte doubles
+    every value."""
+    blocks = np.zeros((16, 17), dtype=np.uint8)
+    blocks[:, 1:] = np.arange(256, dtype=np.uint8).reshape(16, 16)   # code byte j of block i is 16 i + j
+    vals = {}
+    idx = np.arange(256)
+    for e in (100, 101, 127, 200):
+        blocks[:, 0] = e
+        v = oracle.dequantize(wl.MXFP4, blocks, 32)
+        lo, hi = v[:, :16].reshape(-1), v[:, 16:].reshape(-1)   # nibble values of byte b
+        for a, b in ((lo, lo[idx & 15]), (hi, lo[idx >> 4])):
+            assert np.array_equal(a, b) and np.array_equal(np.signbit(a), np.signbit(b))
+        assert lo[0] == 0 and np.all(np.diff(lo[:8]) > 0)
+        for c in range(8):
+            assert lo[c | 8] == -lo[c] and np.signbit(lo[c | 8]) and not np.signbit(lo[c])
+        vals[e] = v
+    assert np.array_equal(vals[101], 2 * vals[100])
+    assert np.array_equal(vals[127][0, :8], np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32))
 
 
 def test_q5_0_fifth_bits_one_to_one():
@@ -582,6 +622,8 @@ def test_row_bytes():
     assert oracle.row_bytes(wl.Q4_K, 14336) == 8064
     assert oracle.row_bytes(wl.F16, 4096) == 8192
     assert oracle.row_bytes(wl.F32, 4096) == 16384
+    assert oracle.row_bytes(wl.MXFP4, 5120) == 2720
+    assert oracle.row_bytes(wl.MXFP4, 48) == -1
     assert oracle.row_bytes(wl.Q4_K, 100) == -1
     assert oracle.row_bytes(99, 32) == -1
 

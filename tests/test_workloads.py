@@ -16,14 +16,22 @@ def test_deterministic_and_seed_sensitive():
     assert not np.array_equal(a["W"], c["W"])
 
 
-@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K,
-                                   wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
+@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4,
+                                   wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
 def test_shapes(wtype):
     blk, nbytes = wl.block_geometry(wtype)
     K = 2 * max(blk, 32)
     c = wl.make_case(wtype, 5, K, 3, seed=1)
     assert c["W"].dtype == np.uint8 and c["W"].shape == (5, K // blk * nbytes)
     assert c["G"].dtype == np.float32 and c["G"].shape == (3, 5)
+
+
+def test_mxfp4_scales_and_codes():
+    c = wl.make_case(wl.MXFP4, 64, 1024, 1, seed=2)
+    blk = c["W"].reshape(64, 32, 17)
+    assert blk[:, :, 0].min() == 117 and blk[:, :, 0].max() == 120
+    nib = np.concatenate([blk[:, :, 1:] & 15, blk[:, :, 1:] >> 4])
+    assert set(np.unique(nib)) == set(range(16))
 
 
 def test_q8_0_codes_and_scales():
