@@ -34,6 +34,10 @@
  *               value d*(q-16)
  *   RETRO_Q5_1  24 bytes / 32 elements: fp16 d, fp16 m, qh, nibbles as
  *               Q5_0; value d*q + m
+ *   RETRO_MXFP4 17 bytes / 32 elements: E8M0 scale byte e, 16 bytes of
+ *               E2M1 codes in the Q4_0 nibble order (OCP Microscaling:
+ *               sign, 2-bit exponent, 1-bit mantissa); value
+ *               e2m1(q) * 2^(e-127), e = 255 NaN; blocks only byte-aligned
  *   RETRO_Q4_K  144 bytes / 256 elements: fp16 d, fp16 dmin, 12 bytes of
  *               eight 6-bit sub-scales sc_j and sub-mins m_j (GGUF packing),
  *               128 bytes of nibbles (each 64-element chunk c uses 32 bytes:
@@ -57,7 +61,7 @@
  *               128h + 32p + l: bits 2p..2p+1 of byte 32 + 32h + l, minus 4
  *               unless bit 4h+p of hmask[l] is set, sub-scale 8h + 2p + l/16
  *               (stored with +32); value (d*(sc-32))*q
- * The Q4_1, Q5_0, Q5_1, Q2_K, Q3_K, Q5_K and Q6_K layouts are the GGUF ones:
+ * The Q4_1, Q5_0, Q5_1, MXFP4, Q2_K, Q3_K, Q5_K and Q6_K layouts are the GGUF ones:
  * the pages that define this operation name them only as members of the
  * quantized types it admits (and the K-quant family through the Q4_K_M files
  * it runs on).
@@ -99,7 +103,8 @@ enum {
     RETRO_Q4_K = 12,
     RETRO_Q5_K = 13,
     RETRO_Q6_K = 14,
-    RETRO_BF16 = 30
+    RETRO_BF16 = 30,
+    RETRO_MXFP4 = 39
 };
 
 /* Error codes. */
@@ -121,7 +126,7 @@ enum {
 
 /*
  * dst[t][k] = sum_n W[n][k] * G[t][n] for t < T, k < K.
- *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_1/Q5_0/Q5_1/Q2_K/Q3_K/Q4_K/Q5_K/Q6_K
+ *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_1/Q5_0/Q5_1/MXFP4/Q2_K/Q3_K/Q4_K/Q5_K/Q6_K
  *   W       device, N * retro_row_bytes(type, K) bytes
  *   G       device, T * N floats
  *   dst     device, T * K floats, overwritten
@@ -221,7 +226,7 @@ int retro_out_prod_variant(int variant, int type, const void *W, const float *G,
  *   ldd  >= K                          floats
  * ldw must also be a multiple of the largest power of two (at most 16) that
  * divides the type's block bytes (F32: 4; F16, BF16, Q8_0, Q4_0, Q5_0, Q3_K,
- * Q6_K: 2; Q4_1, Q2_K: 4; Q5_1: 8; Q4_K, Q5_K: 16), so that each row is as
+ * Q6_K: 2; Q4_1, Q2_K: 4; Q5_1: 8; Q4_K, Q5_K: 16; MXFP4: 1), so that each row is as
  * aligned as the blocks of a contiguous row; otherwise RETRO_E_ALIGN.
  * Errors as retro_out_prod, plus RETRO_E_SHAPE for a stride shorter than its
  * row or a span beyond the size limits. Only the elements of dst's T x K

@@ -46,6 +46,7 @@ bool geometry(int type, Geometry& g) {
         case RETRO_Q4_1: g = {32, 20}; return true;
         case RETRO_Q5_0: g = {32, 22}; return true;
         case RETRO_Q5_1: g = {32, 24}; return true;
+        case RETRO_MXFP4: g = {32, 17}; return true;
         case RETRO_Q4_K: g = {256, 144}; return true;
         case RETRO_Q5_K: g = {256, 176}; return true;
         case RETRO_Q2_K: g = {256, 84}; return true;
@@ -276,7 +277,7 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     // whole word.
     const int64_t rbytes = row_bytes_of(TYPE, K);
     int wvec = 16;
-    while (wvec > 2 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0 || (rbytes % wvec) != 0)) wvec >>= 1;
+    while (wvec > 1 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0 || (rbytes % wvec) != 0)) wvec >>= 1;
     a.wvec = wvec;
     a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
     a.tiles_t = int(cdiv(T, S::BT));
@@ -424,6 +425,7 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         case RETRO_Q4_1: return launch_variant<kQ4_1>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q5_0: return launch_variant<kQ5_0>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q5_1: return launch_variant<kQ5_1>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_MXFP4: return launch_variant<kMXFP4>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q5_K: return launch_variant<kQ5_K>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q2_K: return launch_variant<kQ2_K>(variant, W, G, dst, K, N, T, s, st);
@@ -519,6 +521,7 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
         case RETRO_Q4_1: return launch_dequant<kQ4_1>(W, out, K, N, st);
         case RETRO_Q5_0: return launch_dequant<kQ5_0>(W, out, K, N, st);
         case RETRO_Q5_1: return launch_dequant<kQ5_1>(W, out, K, N, st);
+        case RETRO_MXFP4: return launch_dequant<kMXFP4>(W, out, K, N, st);
         case RETRO_Q4_K: return launch_dequant<kQ4_K>(W, out, K, N, st);
         case RETRO_Q5_K: return launch_dequant<kQ5_K>(W, out, K, N, st);
         case RETRO_Q2_K: return launch_dequant<kQ2_K>(W, out, K, N, st);

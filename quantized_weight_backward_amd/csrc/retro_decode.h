@@ -14,7 +14,9 @@
 // and so is its form a*q - 32a (a*q needs at most 24 bits); a Q3_K value
 // (d*(sc-32))*q needs at most 11+6+3 bits and its form a*q' - 4a (q' = q+4)
 // is exact too. Whether the compiler fuses a*q - b into an FMA therefore
-// changes no bit.
+// changes no bit. An MXFP4 value, an E2M1 code times a power of two, is
+// formed by the hardware's scaled FP4 conversion, which returns that product
+// rounded once (exact unless it overflows; NaN for the NaN scale).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,7 +27,7 @@ namespace retro {
 // GGUF tensor-type ids.
 enum : int {
     kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ4_1 = 3, kQ5_0 = 6, kQ5_1 = 7, kQ8_0 = 8, kQ2_K = 10, kQ3_K = 11, kQ4_K = 12,
-    kQ5_K = 13, kQ6_K = 14, kBF16 = 30
+    kQ5_K = 13, kQ6_K = 14, kBF16 = 30, kMXFP4 = 39
 };
 
 // kBlock: elements per block; kBytes: bytes per block; kGroup: elements one
@@ -39,6 +41,7 @@ template <> struct Format<kQ4_0> { static constexpr int kBlock = 32,  kBytes = 1
 template <> struct Format<kQ4_1> { static constexpr int kBlock = 32,  kBytes = 20,  kGroup = 32; };
 template <> struct Format<kQ5_0> { static constexpr int kBlock = 32,  kBytes = 22,  kGroup = 32; };
 template <> struct Format<kQ5_1> { static constexpr int kBlock = 32,  kBytes = 24,  kGroup = 32; };
+template <> struct Format<kMXFP4> { static constexpr int kBlock = 32, kBytes = 17,  kGroup = 32; };
 
 // The 32-element nibble formats: element j < 16 is the low nibble of code
 // byte j, element j + 16 its high nibble, after a header of kHeader bytes
@@ -48,6 +51,9 @@ template <int TYPE> constexpr bool kNibble32 = TYPE == kQ4_0 || TYPE == kQ4_1 ||
 template <int TYPE> constexpr bool kHasOffset = TYPE == kQ4_1 || TYPE == kQ5_1;
 template <int TYPE> constexpr bool kHasFifth = TYPE == kQ5_0 || TYPE == kQ5_1;
 template <int TYPE> constexpr int kHeader = Format<TYPE>::kBytes - 16;
+// MXFP4 shares that code layout (after a one-byte E8M0 scale) but not the
+// arithmetic.
+template <int TYPE> constexpr bool kNibbleLayout = kNibble32<TYPE> || TYPE == kMXFP4;
 template <> struct Format<kQ4_K> { static constexpr int kBlock = 256, kBytes = 144, kGroup = 32; };
 template <> struct Format<kQ5_K> { static constexpr int kBlock = 256, kBytes = 176, kGroup = 32; };
 template <> struct Format<kQ6_K> { static constexpr int kBlock = 256, kBytes = 210, kGroup = 32; };
@@ -110,6 +116,37 @@ __device__ __forceinline__ void q4_1_x4(uint32_t w, bool high, uint32_t fifth, f
     const uint32_t q = nibbles(w, high) | fifth;
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = d * static_cast<float>((q >> (8 * i)) & 0xFFu) + m;
+}
+
+// MXFP4 scale from its E8M0 byte: 2^(e - 127) as float32 (e = 0 is the
+// subnormal 2^-127, e = 255 NaN).
+__device__ __forceinline__ float mx_scale(uint32_t e) {
+    e &= 0xFFu;
+    const uint32_t bits = e == 0u ? 0x00400000u : e == 255u ? 0x7FC00000u : (e << 23);
+    return __uint_as_float(bits);
+}
+
+// MXFP4: the low (lo) and high (hi) nibbles of the four code bytes of w,
+// each an E2M1 value times the scale s: one conversion per byte, which
+// returns (low nibble, high nibble) of the selected byte.
+__device__ __forceinline__ void mxfp4_x8(uint32_t w, float s, float lo[4], float hi[4]) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
+    const f2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
+    const f2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
+    const f2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
+    lo[0] = a.x; hi[0] = a.y;
+    lo[1] = b.x; hi[1] = b.y;
+    lo[2] = c.x; hi[2] = c.y;
+    lo[3] = d.x; hi[3] = d.y;
+}
+
+// MXFP4: the low (high = false) or high nibbles of four code bytes.
+__device__ __forceinline__ void mxfp4_x4(uint32_t w, bool high, float s, float out[4]) {
+    float lo[4], hi[4];
+    mxfp4_x8(w, s, lo, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = high ? hi[i] : lo[i];
 }
 
 // Scale d, offset m and fifth-bit word qh of a 32-element nibble block whose

@@ -38,6 +38,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Four bytes starting at any LDS address: the two aligned words around
+// them, funnel-shifted (reads at most 4 bytes past the last one).
+__device__ __forceinline__ uint32_t lds_word_a1(const uint8_t* p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
+    return __builtin_amdgcn_alignbyte(q[1], q[0], uint32_t(a & 3));
+}
+
 // Four code bytes starting at a 2-byte aligned LDS address.
 __device__ __forceinline__ uint32_t lds_word_a2(const uint8_t* p) {
     const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
@@ -118,7 +126,7 @@ struct TileArgs {
 template <int TYPE>
 __device__ __forceinline__ int lds_swizzle(int col) {
     if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) return col ^ (((col >> 6) & 3) << 2);
-    if constexpr (kNibble32<TYPE> || TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K)
+    if constexpr (kNibbleLayout<TYPE> || TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K)
         return col ^ (((col >> 5) & 7) << 2);
     if constexpr (TYPE == kQ8_0) return col ^ (((col >> 5) & 3) << 2);
     return col;
@@ -239,8 +247,8 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
             }
         }
         const long long wb = (long long)n0 * args.pitch + kb0;
-        const __amdgpu_buffer_rsrc_t wr =
-            buffer_rsrc(args.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
+        const uint32_t wrange = uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF)));
+        const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(args.W + wb, wrange);
 #pragma unroll
         for (int s = 0; s < S::WSLOTS; ++s) {
             if (S::WUNITS % S::kThreads != 0 && tid + S::kThreads * s >= S::WUNITS) continue;
@@ -253,6 +261,20 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                 const u32x2 x0 = __builtin_amdgcn_raw_buffer_load_b64(wr, o, 0, 0);
                 const u32x2 x1 = __builtin_amdgcn_raw_buffer_load_b64(wr, o + 8, 0, 0);
                 v = make_uint4(x0.x, x0.y, x1.x, x1.y);
+            } else if (args.wvec == 1) {
+                // rows of odd length: whole units inside W take one unaligned
+                // load, the unit reaching past its end takes bytes (a word
+                // straddling the end of a buffer range reads as zero)
+                if (o + 16 <= wrange) {
+                    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 0);
+                    v = make_uint4(x.x, x.y, x.z, x.w);
+                } else {
+                    uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        w4[q >> 2] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(wr, o + q, 0, 0)) << (8 * (q & 3));
+                    v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                }
             } else if (args.wvec == 4) {
                 v = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(wr, o, 0, 0),
                                __builtin_amdgcn_raw_buffer_load_b32(wr, o + 4, 0, 0),
@@ -452,6 +474,18 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                         *reinterpret_cast<float4*>(brow + S::swz(lo + 16 + 4 * i)) =
                             make_float4(e[0], e[1], e[2], e[3]);
                     }
+                } else if constexpr (TYPE == kMXFP4) {  // 17-byte blocks: any byte alignment
+                    const uint8_t* blk = raw + 17 * g;
+                    const float sc = mx_scale(blk[0]);
+                    const int lo = 32 * g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float el[4], eh[4];
+                        mxfp4_x8(lds_word_a1(blk + 1 + 4 * i), sc, el, eh);
+                        *reinterpret_cast<float4*>(brow + S::swz(lo + 4 * i)) = make_float4(el[0], el[1], el[2], el[3]);
+                        *reinterpret_cast<float4*>(brow + S::swz(lo + 16 + 4 * i)) =
+                            make_float4(eh[0], eh[1], eh[2], eh[3]);
+                    }
                 } else if constexpr (TYPE == kQ8_0) {
                     const int b = g >> 1, h = g & 1;
                     const uint8_t* blk = raw + 34 * b;
@@ -588,6 +622,13 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
         const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + 2 + r);
         q8_0_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), d, e);
+    } else if constexpr (TYPE == kMXFP4) {  // 17-byte blocks: read bytewise
+        if (k >= K) { e[0] = e[1] = e[2] = e[3] = 0.f; return; }
+        const uint8_t* blk = row + (k >> 5) * 17;
+        const int r = k & 31;
+        const uint8_t* c = blk + 1 + (r & 15);
+        const uint32_t w = uint32_t(c[0]) | (uint32_t(c[1]) << 8) | (uint32_t(c[2]) << 16) | (uint32_t(c[3]) << 24);
+        mxfp4_x4(w, r >= 16, mx_scale(blk[0]), e);
     } else if constexpr (kNibble32<TYPE>) {  // 2-byte aligned blocks
         if (k >= K) { e[0] = e[1] = e[2] = e[3] = 0.f; return; }
         const uint8_t* blk = row + (k >> 5) * Format<TYPE>::kBytes;
@@ -694,7 +735,7 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
         col = 2u * kl;
     } else if constexpr (TYPE == kQ8_0) {
         col = (kl >> 5) * 34 + 2 + (kl & 31);
-    } else if constexpr (kNibble32<TYPE>) {
+    } else if constexpr (kNibbleLayout<TYPE>) {
         col = (kl >> 5) * Format<TYPE>::kBytes + kHeader<TYPE> + (kl & 15);
     } else if constexpr (TYPE == kQ4_K) {
         const int e = kl & 255;
@@ -725,7 +766,7 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
     uint32_t hcol = 0;
     if constexpr (TYPE == kQ4_K) hcol = (k0 >> 8) * 144;
     if constexpr (TYPE == kQ5_K) hcol = (k0 >> 8) * 176;
-    if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>)
+    if constexpr (TYPE == kQ8_0 || kNibbleLayout<TYPE>)
         hcol = (min(k0 + 32 * sel, K - 32) >> 5) * Format<TYPE>::kBytes;
     o.hdr = uint32_t(hr * a.pitch) + hcol;
     o.hdr2 = 0;
@@ -773,8 +814,8 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
             const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, o.code[s], 0, 0);
             r.code[s][0] = v.x;
             r.code[s][1] = v.y;
-        } else if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>) {
-            // code bytes sit at 2-byte alignment inside these blocks; the
+        } else if constexpr (TYPE == kQ8_0 || kNibbleLayout<TYPE>) {
+            // code bytes sit at 2-byte (MXFP4: any) alignment inside these blocks; the
             // dword load relies on the unaligned buffer access of gfx9-class GPUs
             r.code[s][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.code[s], 0, 0);
         } else if constexpr (TYPE == kQ6_K || TYPE == kQ3_K) {
@@ -810,6 +851,8 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr, 0, 0);
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
+    } else if constexpr (TYPE == kMXFP4) {
+        r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b8(wr, o.hdr, 0, 0);
     } else {
         r.hdr[0] = 0u;
     }
@@ -848,6 +891,11 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
             if (kl + 1 < K) r.code[s][0] |= uint32_t(p[1]) << 16;
             if (kl + 2 < K) r.code[s][1] |= p[2];
             if (kl + 3 < K) r.code[s][1] |= uint32_t(p[3]) << 16;
+        } else if constexpr (TYPE == kMXFP4) {
+            if (kl < K) {
+                const uint8_t* c = row + (kl >> 5) * 17 + 1 + (kl & 15);
+                r.code[s][0] = uint32_t(c[0]) | (uint32_t(c[1]) << 8) | (uint32_t(c[2]) << 16) | (uint32_t(c[3]) << 24);
+            }
         } else if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>) {
             if (kl < K) {
                 constexpr int BYTES = Format<TYPE>::kBytes;
@@ -909,6 +957,10 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
                 r.hdr[3] = f[6];
             }
         }
+    } else if constexpr (TYPE == kMXFP4) {
+        const int kb = k0 + 32 * sel;
+        r.hdr[0] = 0u;
+        if (hvalid && kb < K) r.hdr[0] = hrow[(kb >> 5) * 17];
     } else if constexpr (TYPE == kQ8_0 || kNibble32<TYPE>) {
         // the header halfwords (d; m; qh), none past the header
         constexpr int HH = TYPE == kQ8_0 ? 1 : (kHeader<TYPE> / 2 < 4 ? kHeader<TYPE> / 2 : 4);
@@ -955,6 +1007,12 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
         const float dmine = half_to_f32(r.hdr[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) q8_0_x4(r.code[s][0], lane_value(dmine, 2 * (4 * rq + s) + hi), wv[s]);
+    } else if constexpr (TYPE == kMXFP4) {
+        // this lane decodes the scale of (row (lane % 32) / 2, block lane % 2)
+        const float smine = mx_scale(r.hdr[0]);
+        const int e = (4 * j) & 31;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mxfp4_x4(r.code[s][0], e >= 16, lane_value(smine, 2 * (4 * rq + s) + hi), wv[s]);
     } else if constexpr (kNibble32<TYPE>) {
         // this lane decodes the header of (row (lane % 32) / 2, block lane % 2)
         float dmine, mmine;

@@ -70,7 +70,7 @@ struct WsShape {
     static_assert(!kDense || DUNITS * kPThreads * 16 == BN * BK, "dense chunk splits evenly");
     // Q8_0 and the 32-element nibble blocks: a block is split over QSPLIT
     // producer threads, each holding CB code bytes of it.
-    static constexpr int QSPLIT = (TYPE == kQ8_0 || kNibble32<TYPE>) ? kPThreads / (BN * BK / 32) : 1;
+    static constexpr int QSPLIT = (TYPE == kQ8_0 || kNibbleLayout<TYPE>) ? kPThreads / (BN * BK / 32) : 1;
     static constexpr int CB = TYPE == kQ8_0 ? 32 / QSPLIT : 16 / QSPLIT;
     // words of W each producer thread holds between load and decode
     static constexpr int WWORDS = kDense ? 4 * DWPR * DUNITS
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
                 wreg[4] = f.x; wreg[5] = f.y;
                 wreg[6] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 104, 0, 0);
                 wreg[7] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + 108, 0, 0);
-            } else {  // Q8_0, nibble blocks: 2-byte aligned blocks (unaligned buffer loads)
+            } else {  // Q8_0, nibble blocks: 2-byte (MXFP4: any) aligned blocks (unaligned buffer loads)
                 constexpr int CW = S::CB / 4;
                 constexpr int HDR = TYPE == kQ8_0 ? 2 : kHeader<TYPE>;
                 const uint32_t codes = woff + HDR + S::CB * (p % S::QSPLIT);
@@ -301,6 +301,8 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
                     wreg[CW + 1] = h.y;
                 } else if constexpr (TYPE == kQ4_1) {
                     wreg[CW] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff, 0, 0);
+                } else if constexpr (TYPE == kMXFP4) {
+                    wreg[CW] = __builtin_amdgcn_raw_buffer_load_b8(wr, woff, 0, 0);
                 } else {
                     wreg[CW] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff, 0, 0);
                 }
@@ -452,6 +454,19 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
                     float* col = (4 * w < 16) ? ws + wlds[0] + (4 * w) * WP : ws + wlds[1] + (4 * w - 16) * WP;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) col[j * WP] = e[j];
+                }
+            } else if constexpr (TYPE == kMXFP4) {  // code bytes CB s .. of the block
+                constexpr int CW = S::CB / 4;
+                const float sc = mx_scale(wreg[CW]);
+#pragma unroll
+                for (int w = 0; w < CW; ++w) {
+                    float el[4], eh[4];
+                    mxfp4_x8(wreg[w], sc, el, eh);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ws[wlds[0] + (4 * w + j) * WP] = el[j];
+                        ws[wlds[1] + (4 * w + j) * WP] = eh[j];
+                    }
                 }
             } else {  // 32-element nibble blocks: code bytes CB s .. of the block
                 constexpr int CW = S::CB / 4;

@@ -38,7 +38,7 @@ def test_enum_values_match_header():
     for name, value in [("RETRO_F32", q.F32), ("RETRO_F16", q.F16), ("RETRO_Q4_0", q.Q4_0), ("RETRO_Q8_0", q.Q8_0),
                         ("RETRO_Q4_K", q.Q4_K), ("RETRO_Q5_K", q.Q5_K), ("RETRO_Q6_K", q.Q6_K),
                         ("RETRO_Q2_K", q.Q2_K), ("RETRO_Q3_K", q.Q3_K), ("RETRO_Q4_1", q.Q4_1),
-                        ("RETRO_Q5_0", q.Q5_0), ("RETRO_Q5_1", q.Q5_1),
+                        ("RETRO_Q5_0", q.Q5_0), ("RETRO_Q5_1", q.Q5_1), ("RETRO_MXFP4", q.MXFP4),
                         ("RETRO_BF16", q.BF16), ("RETRO_E_TYPE", q.E_TYPE),
                         ("RETRO_E_SHAPE", q.E_SHAPE), ("RETRO_E_NULL", q.E_NULL), ("RETRO_E_ALIGN", q.E_ALIGN),
                         ("RETRO_E_ALIAS", q.E_ALIAS), ("RETRO_E_HIP", q.E_HIP), ("RETRO_E_VARIANT", q.E_VARIANT),
@@ -49,8 +49,8 @@ def test_enum_values_match_header():
         assert m and int(m.group(1)) == value, name
 
 
-@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K,
-                                   wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
+@pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4,
+                                   wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
 def test_row_bytes_matches_the_format(wtype):
     blk, nbytes = wl.block_geometry(wtype)
     for nblocks in (0, 1, 3, 16, 56):
@@ -73,6 +73,7 @@ def test_row_bytes_of_the_workloads():
     assert q.row_bytes(q.Q4_1, 5120) == 3200
     assert q.row_bytes(q.Q5_0, 5120) == 3520
     assert q.row_bytes(q.Q5_1, 5120) == 3840
+    assert q.row_bytes(q.MXFP4, 5120) == 2720
     assert q.row_bytes(99, 256) == -1
 
 
@@ -96,7 +97,7 @@ def test_choice():
     assert q.choice(q.Q4_0, 5120, 17407, 2048) == q.VARIANT_TILE_64x128  # N % 4 != 0: the fallback family
     for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0, q.Q4_1, q.Q5_0, q.Q5_1):
         assert q.choice(wtype, 4096, 4096, 512) in q.VARIANT_NAMES
-    for wtype in (q.Q4_1, q.Q5_0, q.Q5_1):  # the 32-element blocks, as Q4_0
+    for wtype in (q.Q4_1, q.Q5_0, q.Q5_1, q.MXFP4):  # the 32-element blocks, as Q4_0
         assert q.choice(wtype, 5120, 17408, 2048) == q.VARIANT_WS_64x128
         assert q.choice(wtype, 5120, 4096, 16) == q.VARIANT_SKINNY
         assert q.choice(wtype, 48, 1, 1) == q.E_SHAPE

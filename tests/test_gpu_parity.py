@@ -29,8 +29,8 @@ REL_MAX = 1e-5
 REL_TIGHT = 2e-6
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K, wl.Q3_K, wl.Q4_K,
-         wl.Q5_K, wl.Q6_K]
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K,
+         wl.Q4_K, wl.Q5_K, wl.Q6_K]
 KQUANTS = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
 ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
              "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128", "ws_32x256", "ws_32x128", "ws2_64x128"]
@@ -95,6 +95,7 @@ SMALL_K = {
     wl.Q4_1: (512, 352, 192, 416),
     wl.Q5_0: (352, 416, 128, 352),
     wl.Q5_1: (512, 352, 416, 256),
+    wl.MXFP4: (352, 416, 512, 128),   # 187-, 221-byte rows: odd pitches
     wl.Q4_K: (768, 512, 256, 768),
     wl.Q5_K: (512, 768, 256, 512),
     wl.Q6_K: (768, 256, 512, 768),
@@ -203,8 +204,8 @@ def test_q8_0_tiny_workload(q):
     check_close(y, acc, ab)
 
 
-@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K,
-                                   wl.Q6_K, wl.F16, wl.BF16])
+@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K,
+                                   wl.Q5_K, wl.Q6_K, wl.F16, wl.BF16])
 def test_f32_twin_on_device(q, wtype):
     """out_prod(Qx, W) and out_prod(F32, dequant(W)) run the same tile on
     identical B operands, so they agree bit for bit."""
@@ -225,7 +226,7 @@ def test_f32_twin_on_device(q, wtype):
 
 # --- invariants -----------------------------------------------------------------
 
-@pytest.mark.parametrize("wtype", [wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.Q4_0, wl.Q5_1, wl.BF16])
+@pytest.mark.parametrize("wtype", [wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.Q4_0, wl.Q5_1, wl.MXFP4, wl.BF16])
 @pytest.mark.parametrize("i", [0, 3])
 def test_invariants(q, wtype, i):
     c = small_case(wtype, i, 500)
@@ -316,7 +317,8 @@ def test_runs_on_the_given_stream(q):
 # --- strided operands --------------------------------------------------------------
 
 STRIDED = [(wl.Q4_K, 768, 96, 130), (wl.Q4_0, 512, 77, 200), (wl.F16, 264, 100, 150), (wl.Q6_K, 512, 60, 70),
-           (wl.Q8_0, 416, 33, 16), (wl.Q2_K, 256, 40, 9), (wl.Q5_0, 352, 52, 90), (wl.Q5_1, 256, 44, 12)]
+           (wl.Q8_0, 416, 33, 16), (wl.Q2_K, 256, 40, 9), (wl.Q5_0, 352, 52, 90), (wl.Q5_1, 256, 44, 12),
+           (wl.MXFP4, 352, 40, 70)]
 
 
 @pytest.mark.parametrize("wtype,K,N,T", STRIDED)
@@ -434,6 +436,7 @@ FULL = [
     ("q4_1_n17408_k5120_t2048", None),
     ("q5_0_n17408_k5120_t2048", None),
     ("q5_1_n17408_k5120_t2048", None),
+    ("mxfp4_n17408_k5120_t2048", None),
 ]
 
 
@@ -461,7 +464,7 @@ def test_full_size_sampled_rows(q, name, wtype):
 @pytest.mark.parametrize("name", ["q4_0_n17408_k5120_t2048", "q4_k_n14336_k4096_t4096", "q4_k_n4096_k14336_t16",
                                   "q5_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096", "q6_k_n4096_k14336_t16",
                                   "q2_k_n14336_k4096_t4096", "q3_k_n14336_k4096_t4096", "q3_k_n4096_k14336_t16",
-                                  "q5_0_n17408_k5120_t2048"])
+                                  "q5_0_n17408_k5120_t2048", "mxfp4_n17408_k5120_t2048"])
 def test_full_size_decode_through_identity(q, name):
     """Full-size W through the benchmarked kernel with G = I (T = N): the
     output is the decoded W, bit for bit."""
