@@ -62,6 +62,8 @@ def _load():
         lib.oracle_out_prod.restype = ctypes.c_int
         lib.oracle_out_prod.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp,
                                         ctypes.c_int]
+        lib.oracle_mul_mat.restype = ctypes.c_int
+        lib.oracle_mul_mat.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -130,6 +132,35 @@ def out_prod(wtype: int, W: np.ndarray, G: np.ndarray, K: int, rows=None, nthrea
     if rc != 0:
         raise ValueError("oracle_out_prod failed")
     return dst, acc, abssum
+
+
+def mul_mat(wtype: int, W: np.ndarray, X: np.ndarray, K: int, rows=None, nthreads: int = 1):
+    """y = mul_mat(W, x): y[t][n] = sum_k W[n][k] x[t][k] (X float32 T x K).
+
+    Returns (y F32, acc float64, abssum float64), each len(rows) x N.
+    """
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim != 2 or X.shape[1] != K:
+        raise ValueError("X must be T x K")
+    T = X.shape[0]
+    rb = row_bytes(wtype, K)
+    if rb <= 0 or W.size % rb:
+        raise ValueError("W does not hold whole rows of the given type and K")
+    N = W.size // rb
+    if rows is None:
+        nrows, rows_arr, rows_ptr = T, None, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rows_ptr = rows_arr.size, _ptr(rows_arr)
+    y = np.empty((nrows, N), dtype=np.float32)
+    acc = np.empty((nrows, N), dtype=np.float64)
+    abssum = np.empty((nrows, N), dtype=np.float64)
+    rc = _load().oracle_mul_mat(wtype, _ptr(W), _ptr(X), K, N, T, rows_ptr, nrows, _ptr(y), _ptr(acc),
+                                _ptr(abssum), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_mul_mat failed")
+    return y, acc, abssum
 
 
 def errors(y: np.ndarray, acc: np.ndarray, abssum: np.ndarray) -> dict:

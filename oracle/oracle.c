@@ -482,3 +482,74 @@ int oracle_out_prod(int type, const uint8_t *W, const float *G, int64_t K, int64
     free(own_rows);
     return 0;
 }
+
+/* mul_mat, the forward of the layer whose input gradient out_prod computes
+ * (the PR's commit message: the backward of mul_mat(W, x) with respect to x
+ * is out_prod(W, grad^T)): y[t][n] = sum_k W[n][k] * x[t][k], with W[n][k]
+ * the decoded value, for the nrows selected t rows (rows == NULL selects
+ * t = 0 .. nrows-1). Products and sums in double, k increasing; acc gets the
+ * sums, abssum the sums of |W[n][k] * x[t][k]|, y their F32 rounding, each
+ * nrows x N. */
+typedef struct {
+    const float *w, *X;
+    const int64_t *rows;
+    int64_t nrows, K, N;
+    float *y;
+    double *acc, *abssum;
+    int tid, nthreads;
+} mm_job_t;
+
+static void *mm_worker(void *arg) {
+    const mm_job_t *j = (const mm_job_t *)arg;
+    for (int64_t i = j->tid; i < j->nrows; i += j->nthreads) {
+        const float *x = j->X + j->rows[i] * j->K;
+        for (int64_t n = 0; n < j->N; n++) {
+            const float *wn = j->w + n * j->K;
+            double a = 0.0, s = 0.0;
+            for (int64_t k = 0; k < j->K; k++) {
+                double p = (double)wn[k] * (double)x[k];
+                a += p;
+                s += fabs(p);
+            }
+            j->acc[i * j->N + n] = a;
+            j->abssum[i * j->N + n] = s;
+            j->y[i * j->N + n] = (float)a;
+        }
+    }
+    return NULL;
+}
+
+int oracle_mul_mat(int type, const uint8_t *W, const float *X, int64_t K, int64_t N, int64_t T,
+                   const int64_t *rows, int64_t nrows, float *y, double *acc, double *abssum, int nthreads) {
+    if (oracle_row_bytes(type, K) < 0 || K < 0 || N < 0 || T < 0 || nrows < 0) return -1;
+    if (N == 0 || nrows == 0) return 0;
+    int64_t *own_rows = NULL;
+    if (!rows) {
+        if (nrows > T) return -1;
+        own_rows = (int64_t *)malloc((size_t)nrows * sizeof(int64_t));
+        if (!own_rows) return -1;
+        for (int64_t i = 0; i < nrows; i++) own_rows[i] = i;
+        rows = own_rows;
+    }
+    for (int64_t i = 0; i < nrows; i++)
+        if (rows[i] < 0 || rows[i] >= T) { free(own_rows); return -1; }
+    float *w = (float *)malloc((size_t)N * (size_t)(K > 0 ? K : 1) * sizeof(float));
+    if (!w) { free(own_rows); return -1; }
+    if (oracle_dequantize(type, W, K, N, w)) { free(w); free(own_rows); return -1; }
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    mm_job_t jobs[256];
+    pthread_t th[256];
+    for (int t = 0; t < nthreads; t++) jobs[t] = (mm_job_t){w, X, rows, nrows, K, N, y, acc, abssum, t, nthreads};
+    int started = 0;
+    for (int t = 1; t < nthreads; t++) {
+        if (pthread_create(&th[t], NULL, mm_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    for (int t = started + 1; t < nthreads; t++) mm_worker(&jobs[t]);
+    mm_worker(&jobs[0]);
+    for (int t = 1; t <= started; t++) pthread_join(th[t], NULL);
+    free(w);
+    free(own_rows);
+    return 0;
+}

@@ -607,6 +607,64 @@ def test_special_cases():
     assert np.array_equal(d, oracle.dequantize(wl.Q4_0, c["W"], c["K"]))
 
 
+# --- mul_mat (the forward) ----------------------------------------------------
+
+@pytest.mark.parametrize("wtype", TYPES)
+def test_mul_mat_matches_numpy_and_torch(wtype):
+    """y = x W^T with the decoded W: numpy float64 matmul and torch's
+    float64 linear layer agree with the oracle's double sums."""
+    K = 2 * max(wl.block_geometry(wtype)[0], 32)
+    c = wl.make_case(wtype, 7, K, 5, seed=31)
+    x = np.random.default_rng(3).standard_normal((5, K)).astype(np.float32)
+    w = oracle.dequantize(wtype, c["W"], K).astype(np.float64)
+    y, acc, ab = oracle.mul_mat(wtype, c["W"], x, K)
+    ref = x.astype(np.float64) @ w.T
+    assert np.allclose(acc, ref, rtol=1e-12, atol=1e-12)
+    lin = torch.nn.functional.linear(torch.from_numpy(x).double(), torch.from_numpy(w)).numpy()
+    assert np.allclose(acc, lin, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(y, acc.astype(np.float32))
+    assert np.allclose(ab, np.abs(x.astype(np.float64)) @ np.abs(w).T, rtol=1e-12, atol=1e-12)
+
+
+def test_mul_mat_brute_force_reverse_order():
+    c = wl.make_case(wl.Q4_K, 3, 256, 2, seed=8)
+    x = np.random.default_rng(4).standard_normal((2, 256)).astype(np.float32)
+    w = oracle.dequantize(wl.Q4_K, c["W"], 256)
+    _, acc, _ = oracle.mul_mat(wl.Q4_K, c["W"], x, 256)
+    for t in range(2):
+        for n in range(3):
+            s = 0.0
+            for k in reversed(range(256)):
+                s += float(w[n, k]) * float(x[t, k])
+            assert abs(s - acc[t, n]) <= 1e-12 * max(1.0, abs(s))
+
+
+@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q6_K, wl.MXFP4, wl.BF16])
+def test_mul_mat_and_out_prod_are_adjoint(wtype):
+    """<G, mul_mat(W, x)> = <out_prod(W, G), x>: the two oracle functions
+    contract the same W along its two different directions."""
+    K = 2 * max(wl.block_geometry(wtype)[0], 32)
+    c = wl.make_case(wtype, 9, K, 4, seed=12)
+    x = np.random.default_rng(5).standard_normal((4, K)).astype(np.float32)
+    _, y, _ = oracle.mul_mat(wtype, c["W"], x, K)
+    _, d, _ = oracle.out_prod(wtype, c["W"], c["G"], K)
+    lhs = float((c["G"].astype(np.float64) * y).sum())
+    rhs = float((d * x.astype(np.float64)).sum())
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
+
+
+def test_mul_mat_f32_twin_and_row_subset():
+    c = wl.make_case(wl.Q5_K, 6, 512, 9, seed=14)
+    x = np.random.default_rng(6).standard_normal((9, 512)).astype(np.float32)
+    w32 = oracle.dequantize(wl.Q5_K, c["W"], 512)
+    a, _, _ = oracle.mul_mat(wl.Q5_K, c["W"], x, 512)
+    b, _, _ = oracle.mul_mat(wl.F32, w32.view(np.uint8), x, 512)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    rows = np.array([8, 0, 3])
+    s, _, _ = oracle.mul_mat(wl.Q5_K, c["W"], x, 512, rows=rows, nthreads=3)
+    assert np.array_equal(s, a[rows])
+
+
 def test_row_subset_and_threads_change_nothing():
     c = small_case(wl.Q4_K, T=21, N=40, nblk=2, seed=16)
     full, acc, ab = oracle.out_prod(wl.Q4_K, c["W"], c["G"], c["K"])
