@@ -184,6 +184,8 @@ const char *retro_strerror(int code);
  *                           needs G rows in 16-byte units (ldg % 4 == 0;
  *                           ldg = N when contiguous) and K % 4 == 0 for F32,
  *                           F16, BF16; the TILE_* kernel takes the others
+ *   RETRO_VARIANT_SIMPLE    retro_mul_mat only: one thread per output, for
+ *                           the shapes the tiled kernel refuses
  *   RETRO_VARIANT_WS2_64x128  WS_64x128 with two pipelines in one
  *                           workgroup (even and odd 32-row chunks of W,
  *                           partial sums added in LDS in that order): two
@@ -204,7 +206,8 @@ enum {
     RETRO_VARIANT_WS_64x128 = 10,
     RETRO_VARIANT_WS_32x256 = 11,
     RETRO_VARIANT_WS_32x128 = 12,
-    RETRO_VARIANT_WS2_64x128 = 13
+    RETRO_VARIANT_WS2_64x128 = 13,
+    RETRO_VARIANT_SIMPLE = 15
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the
@@ -289,6 +292,38 @@ int retro_out_prod_variant_applies(int variant, int type, int64_t K, int64_t N, 
 /* The same for retro_out_prod_strided_variant with strides ldw, ldg, ldd. */
 int retro_out_prod_strided_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, int64_t ldw,
                                            int64_t ldg, int64_t ldd);
+
+/*
+ * mul_mat, the forward of the layer whose input gradient retro_out_prod
+ * computes (the llama.cpp PR #3 "cuda: out_prod accepts a quantized src0",
+ * commit message: the backward of mul_mat(W, x) with respect to x is
+ * out_prod(W, grad^T)), through the same packed W:
+ *
+ *     Y[t][n] = sum_{k=0}^{K-1} W[n][k] * X[t][k]        t < T, n < N
+ *
+ *   W  N rows of retro_row_bytes(type, K) bytes, as for retro_out_prod
+ *   X  T x K float32, row-major contiguous
+ *   Y  T x N float32, row-major contiguous, overwritten (K = 0 writes zeros)
+ * Pointers, alignment, aliasing, errors and execution as retro_out_prod.
+ * Variants: RETRO_VARIANT_WS_128x128 / _64x128 / _32x128 (tiles of T x N;
+ * need K % 4 == 0 for F32/F16/BF16), RETRO_VARIANT_SKINNY (T <= 16: one
+ * workgroup per 16 rows of W over all of k) and RETRO_VARIANT_SIMPLE.
+ */
+int retro_mul_mat(int type, const void *W, const float *X, float *Y, int64_t K, int64_t N, int64_t T,
+                  void *stream);
+
+/* retro_mul_mat with a forced kernel variant (RETRO_E_VARIANT when it does
+ * not apply). */
+int retro_mul_mat_variant(int variant, int type, const void *W, const float *X, float *Y, int64_t K, int64_t N,
+                          int64_t T, void *stream);
+
+/* The variant retro_mul_mat would run, or a negative error code. Touches no
+ * device. */
+int retro_mul_mat_choice(int type, int64_t K, int64_t N, int64_t T);
+
+/* 1 if retro_mul_mat_variant(variant, type, ..., K, N, T) with valid buffers
+ * would run, 0 otherwise. Touches no device. */
+int retro_mul_mat_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T);
 
 #ifdef __cplusplus
 }

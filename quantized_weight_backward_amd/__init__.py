@@ -47,12 +47,13 @@ VARIANT_WS_64x128 = 10
 VARIANT_WS_32x256 = 11
 VARIANT_WS_32x128 = 12
 VARIANT_WS2_64x128 = 13
+VARIANT_SIMPLE = 15
 VARIANT_NAMES = {
     VARIANT_SKINNY: "skinny", VARIANT_TILE_128x128: "tile_128x128", VARIANT_TILE_128x256: "tile_128x256",
     VARIANT_TILE_64x128: "tile_64x128", VARIANT_TILE_64x64: "tile_64x64", VARIANT_TILE_64x256: "tile_64x256",
     VARIANT_WS_128x256: "ws_128x256", VARIANT_WS_64x256: "ws_64x256", VARIANT_WS_128x128: "ws_128x128",
     VARIANT_WS_64x128: "ws_64x128", VARIANT_WS_32x256: "ws_32x256", VARIANT_WS_32x128: "ws_32x128",
-    VARIANT_WS2_64x128: "ws2_64x128",
+    VARIANT_WS2_64x128: "ws2_64x128", VARIANT_SIMPLE: "simple",
 }
 
 LIB_PATH = _build.LIB_PATH
@@ -61,6 +62,7 @@ LIB_PATH = _build.LIB_PATH
 EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided", "retro_out_prod_strided_variant",
            "retro_dequantize", "retro_out_prod_supported", "retro_out_prod_choice", "retro_out_prod_variant_applies",
            "retro_out_prod_strided_variant_applies", "retro_out_prod_batched", "retro_out_prod_batched_variant",
+           "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
            "retro_row_bytes", "retro_strerror")
 
 
@@ -85,6 +87,14 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod_batched_variant.restype = i32
     lib.retro_out_prod_batched_variant.argtypes = [i32, i32, vp, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64,
                                                    i64, i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.retro_mul_mat.restype = i32
+    lib.retro_mul_mat.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp]
+    lib.retro_mul_mat_variant.restype = i32
+    lib.retro_mul_mat_variant.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, vp]
+    lib.retro_mul_mat_choice.restype = i32
+    lib.retro_mul_mat_choice.argtypes = [i32, i64, i64, i64]
+    lib.retro_mul_mat_variant_applies.restype = i32
+    lib.retro_mul_mat_variant_applies.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_out_prod_strided_variant_applies.restype = i32
     lib.retro_out_prod_strided_variant_applies.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64]
     lib.retro_dequantize.restype = i32
@@ -255,6 +265,44 @@ def out_prod_batched(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_
 def variant_applies_strided(variant: int, wtype: int, K: int, N: int, T: int, ldw: int, ldg: int, ldd: int) -> bool:
     return lib.retro_out_prod_strided_variant_applies(int(variant), int(wtype), int(K), int(N), int(T), int(ldw),
                                                       int(ldg), int(ldd)) == 1
+
+
+def mul_mat(wtype: int, W, X, N: int | None = None, out=None, variant: int = VARIANT_AUTO, stream=None):
+    """Y = mul_mat(W, X), the forward Y[t][n] = sum_k W[n][k] X[t][k]: X a
+    contiguous float32 T x K device tensor, W contiguous packed bytes of N
+    rows (N taken from W's size unless given), Y float32 T x N."""
+    _device_tensor(W, "W")
+    _device_tensor(X, "X")
+    if X.dtype != torch.float32 or X.dim() != 2:
+        raise ValueError("X must be a contiguous 2-D float32 tensor (T x K)")
+    T, K = X.shape
+    rb = row_bytes(wtype, K)
+    if rb < 0:
+        _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
+    nbytes = W.numel() * W.element_size()
+    if N is None:
+        if rb == 0:
+            raise ValueError("N must be given when K = 0")
+        N = nbytes // rb
+    if nbytes != N * rb:
+        raise ValueError(f"W holds {nbytes} bytes, expected N*row_bytes = {N * rb}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=X.device)
+    else:
+        _device_tensor(out, "out")
+        if out.dtype != torch.float32 or tuple(out.shape) != (T, N):
+            raise ValueError("out must be contiguous float32 T x N")
+    _check(lib.retro_mul_mat_variant(int(variant), int(wtype), _ptr(W), _ptr(X), _ptr(out), int(K), int(N), int(T),
+                                     _stream_handle(stream)))
+    return out
+
+
+def mul_mat_choice(wtype: int, K: int, N: int, T: int) -> int:
+    return int(lib.retro_mul_mat_choice(int(wtype), int(K), int(N), int(T)))
+
+
+def mul_mat_variant_applies(variant: int, wtype: int, K: int, N: int, T: int) -> bool:
+    return lib.retro_mul_mat_variant_applies(int(variant), int(wtype), int(K), int(N), int(T)) == 1
 
 
 def dequantize(wtype: int, W, K: int, N: int, out=None, stream=None):

@@ -13,6 +13,7 @@
 
 #include "retro_kernels.h"
 #include "retro_ws_kernel.h"
+#include "retro_mm_kernel.h"
 #include "retro_out_prod.h"
 
 namespace {
@@ -451,9 +452,187 @@ int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t 
     return launch_status();
 }
 
+// ---------------------------------------------------------------------------
+// mul_mat
+// ---------------------------------------------------------------------------
+
+struct MmTile {
+    int id, bt, bn;
+    double penalty;
+};
+
+constexpr MmTile kMmTiles[] = {
+    {RETRO_VARIANT_WS_128x128, 128, 128, 1.00},
+    {RETRO_VARIANT_WS_64x128, 64, 128, 1.02},
+    {RETRO_VARIANT_WS_32x128, 32, 128, 1.04},
+};
+
+// The tiled kernel loads x rows in 16-byte units and addresses a tile's W
+// rows and x rows with 32-bit offsets.
+bool mm_tile_applies(const MmTile& v, int type, int64_t K, int64_t N, int64_t T) {
+    (void)N;
+    if (is_dense(type) && K % 4) return false;
+    return cdiv(T, v.bt) * cdiv(N, v.bn) < kGridLimit && int64_t(v.bn) * row_bytes_of(type, K) < (int64_t(1) << 31) &&
+           int64_t(v.bt) * K * 4 < (int64_t(1) << 31);
+}
+
+bool mm_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
+    if (variant == RETRO_VARIANT_SIMPLE) return cdiv(T * N, 256) < kGridLimit;
+    if (variant == RETRO_VARIANT_SKINNY) return T <= 16 && cdiv(N, 16) < kGridLimit;
+    for (const auto& v : kMmTiles)
+        if (v.id == variant) return mm_tile_applies(v, type, K, N, T);
+    return false;
+}
+
+int mm_choose(int type, int64_t K, int64_t N, int64_t T) {
+    if (mm_variant_applies(RETRO_VARIANT_SKINNY, type, K, N, T)) return RETRO_VARIANT_SKINNY;
+    int best = -1;
+    double best_cost = 0;
+    for (const auto& v : kMmTiles) {
+        if (!mm_tile_applies(v, type, K, N, T)) continue;
+        const double cost = double(cdiv(cdiv(T, v.bt) * cdiv(N, v.bn), kNumCUs)) * v.bt * v.bn * v.penalty;
+        if (best < 0 || cost < best_cost) {
+            best = v.id;
+            best_cost = cost;
+        }
+    }
+    if (best < 0 && mm_variant_applies(RETRO_VARIANT_SIMPLE, type, K, N, T)) best = RETRO_VARIANT_SIMPLE;
+    return best < 0 ? RETRO_E_SHAPE : best;
+}
+
+template <int TYPE, int WA, int WB, int CT>
+int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+    using S = MmShape<TYPE, WA, WB, CT>;
+    MmArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.X = X;
+    a.Y = Y;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.ldx = K;
+    a.ldy = N;
+    a.tiles_t = int(cdiv(T, S::BT));
+    a.tiles_n = int(cdiv(N, S::BK));
+    a.group = group_height(a.tiles_t, a.tiles_n, S::kResident, 4.0 * T * K, double(N) * a.pitch);
+    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_n);
+    clear_last_error();
+    hipLaunchKernelGGL((mul_mat_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE>
+int launch_mm_simple(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+    MmSimpleArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.X = X;
+    a.Y = Y;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.ldx = K;
+    a.ldy = N;
+    a.wide = (K % 4 == 0) ? 1 : 0;
+    clear_last_error();
+    hipLaunchKernelGGL((mul_mat_simple_kernel<TYPE>), dim3(unsigned(cdiv(T * N, 256))), dim3(256), 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE>
+int launch_mm_skinny(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+    MmSimpleArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.X = X;
+    a.Y = Y;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.ldx = K;
+    a.ldy = N;
+    a.wide = (K % 4 == 0) ? 1 : 0;
+    clear_last_error();
+    hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE>), dim3(unsigned(cdiv(N, 16))), dim3(1024), 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE>
+int launch_mm_variant(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                      hipStream_t st) {
+    switch (variant) {
+        case RETRO_VARIANT_WS_128x128: return launch_mm<TYPE, 2, 2, 2>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_WS_64x128: return launch_mm<TYPE, 1, 2, 2>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_WS_32x128: return launch_mm<TYPE, 1, 1, 1>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_SIMPLE: return launch_mm_simple<TYPE>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_SKINNY: return launch_mm_skinny<TYPE>(W, X, Y, K, N, T, st);
+        default: return RETRO_E_VARIANT;
+    }
+}
+
+int mul_mat_impl(int variant, int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                 void* stream) {
+    int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    if (T == 0 || N == 0) return RETRO_OK;
+    const int64_t w_bytes = N * row_bytes_of(type, K);
+    const int64_t x_bytes = T * K * 4;
+    const int64_t y_bytes = T * N * 4;
+    if (!Y || (K > 0 && (!W || !X))) return RETRO_E_NULL;
+    if (!aligned16(Y) || (K > 0 && (!aligned16(W) || !aligned16(X)))) return RETRO_E_ALIGN;
+    if (overlap(Y, y_bytes, W, w_bytes) || overlap(Y, y_bytes, X, x_bytes)) return RETRO_E_ALIAS;
+    if (variant == RETRO_VARIANT_AUTO) {
+        variant = mm_choose(type, K, N, T);
+        if (variant < 0) return variant;
+    } else if (!mm_variant_applies(variant, type, K, N, T)) {
+        return RETRO_E_VARIANT;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (type) {
+        case RETRO_F32: return launch_mm_variant<kF32>(variant, W, X, Y, K, N, T, st);
+        case RETRO_F16: return launch_mm_variant<kF16>(variant, W, X, Y, K, N, T, st);
+        case RETRO_BF16: return launch_mm_variant<kBF16>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q8_0: return launch_mm_variant<kQ8_0>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q4_0: return launch_mm_variant<kQ4_0>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q4_1: return launch_mm_variant<kQ4_1>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q5_0: return launch_mm_variant<kQ5_0>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q5_1: return launch_mm_variant<kQ5_1>(variant, W, X, Y, K, N, T, st);
+        case RETRO_MXFP4: return launch_mm_variant<kMXFP4>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q4_K: return launch_mm_variant<kQ4_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q5_K: return launch_mm_variant<kQ5_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q2_K: return launch_mm_variant<kQ2_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q3_K: return launch_mm_variant<kQ3_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q6_K: return launch_mm_variant<kQ6_K>(variant, W, X, Y, K, N, T, st);
+        default: return RETRO_E_TYPE;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+int retro_mul_mat(int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                  void* stream) {
+    return mul_mat_impl(RETRO_VARIANT_AUTO, type, W, X, Y, K, N, T, stream);
+}
+
+int retro_mul_mat_variant(int variant, int type, const void* W, const float* X, float* Y, int64_t K, int64_t N,
+                          int64_t T, void* stream) {
+    return mul_mat_impl(variant, type, W, X, Y, K, N, T, stream);
+}
+
+int retro_mul_mat_choice(int type, int64_t K, int64_t N, int64_t T) {
+    const int rc = check_shape(type, K, N, T);
+    return rc != RETRO_OK ? rc : mm_choose(type, K, N, T);
+}
+
+int retro_mul_mat_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
+    if (check_shape(type, K, N, T) != RETRO_OK) return 0;
+    if (T == 0 || N == 0) return 1;
+    if (variant == RETRO_VARIANT_AUTO) return mm_choose(type, K, N, T) > 0 ? 1 : 0;
+    return mm_variant_applies(variant, type, K, N, T) ? 1 : 0;
+}
 
 int retro_out_prod(int type, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
                    void* stream) {

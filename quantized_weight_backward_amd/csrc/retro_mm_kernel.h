@@ -1,0 +1,417 @@
+// retro_mm_kernel.h - mul_mat, the forward y = x W^T of the layer whose
+// input gradient OUT_PROD computes, through the same resident packed weight.
+//
+//     y[t][n] = sum_k W[n][k] * x[t][k]
+//
+// The reduction now runs along k, the direction the blocks are packed in,
+// and the outputs are the rows of W. The kernel keeps the producer/consumer
+// pipeline of out_prod_ws_kernel and its consumer waves unchanged (they see
+// a t-major operand and a column-major operand of 32 reduction values per
+// chunk, whatever the two indices mean); only the producers differ: per
+// chunk of 32 k values they load x like G, and for each of the tile's W
+// rows decode 32 consecutive elements of that row - one 32-element block,
+// or one 32-element part of a 256-element super-block - writing each row's
+// values as one column of the LDS operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "retro_ws_kernel.h"
+
+namespace retro {
+
+struct MmArgs {
+    const uint8_t* W;
+    const float* X;
+    float* Y;
+    int K, N, T;
+    long long pitch;  // bytes between consecutive W rows
+    long long ldx;    // floats between consecutive x rows (a multiple of 4)
+    long long ldy;    // floats between consecutive y rows (>= N)
+    int tiles_t, tiles_n, group;
+};
+
+// Loads and decode of 16 consecutive elements k .. k + 15 (k % 16 == 0) of
+// one W row that starts at byte `ro` of buffer `wr`. All loads stay inside
+// the row's blocks (dense rows: inside the row for k < K, and K % 4 == 0),
+// so none straddles the end of W; rows at or past N read as zero.
+template <int TYPE>
+struct MmCodec;
+
+template <>
+struct MmCodec<kF32> {
+    static constexpr int WORDS = 16;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, ro + 4u * k + 16u * i, 0, 0);
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int, float (&e)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[i] = __uint_as_float(w[i]);
+    }
+};
+
+template <int TYPE>
+struct MmCodecHalf {
+    static constexpr int WORDS = 8;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, ro + 2u * k + 16u * i, 0, 0);
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int, float (&e)[16]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (TYPE == kF16)
+                f16x2(w[i], e[2 * i], e[2 * i + 1]);
+            else
+                bf16x2(w[i], e[2 * i], e[2 * i + 1]);
+        }
+    }
+};
+template <> struct MmCodec<kF16> : MmCodecHalf<kF16> {};
+template <> struct MmCodec<kBF16> : MmCodecHalf<kBF16> {};
+
+template <>
+struct MmCodec<kQ8_0> {
+    static constexpr int WORDS = 5;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+        const uint32_t blk = ro + 34u * uint32_t(k >> 5);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, blk + 2u + 16u * ((k >> 4) & 1), 0, 0);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        w[4] = __builtin_amdgcn_raw_buffer_load_b16(wr, blk, 0, 0);
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int, float (&e)[16]) {
+        const float d = half_to_f32(w[4] & 0xFFFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q8_0_x4(w[i], d, e + 4 * i);
+    }
+};
+
+// The 32-element nibble blocks and MXFP4: element j < 16 is the low nibble
+// of code byte j, element j + 16 its high nibble.
+template <int TYPE>
+struct MmCodecNibble {
+    static constexpr int HW = kHasFifth<TYPE> ? 2 : 1;
+    static constexpr int WORDS = 4 + HW;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+        const uint32_t blk = ro + uint32_t(Format<TYPE>::kBytes) * uint32_t(k >> 5);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, blk + kHeader<TYPE>, 0, 0);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        if constexpr (kHasFifth<TYPE>) {
+            const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(wr, blk, 0, 0);
+            w[4] = h.x;
+            w[5] = h.y;
+        } else if constexpr (TYPE == kQ4_1) {
+            w[4] = __builtin_amdgcn_raw_buffer_load_b32(wr, blk, 0, 0);
+        } else if constexpr (TYPE == kMXFP4) {
+            w[4] = __builtin_amdgcn_raw_buffer_load_b8(wr, blk, 0, 0);
+        } else {
+            w[4] = __builtin_amdgcn_raw_buffer_load_b16(wr, blk, 0, 0);
+        }
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int k, float (&e)[16]) {
+        const bool high = ((k >> 4) & 1) != 0;  // elements 16 .. 31 of the block
+        if constexpr (TYPE == kMXFP4) {
+            const float s = mx_scale(w[4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mxfp4_x4(w[i], high, s, e + 4 * i);
+        } else {
+            float d, m;
+            uint32_t qh;
+            if constexpr (kHasFifth<TYPE>)
+                nibble32_header<TYPE>(w[4], w[5], d, m, qh);
+            else
+                nibble32_header<TYPE>(w[4], 0u, d, m, qh);
+            const int first = high ? 16 : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q4_1_x4(w[i], high, fifth_bits(qh, first + 4 * i), d, m, e + 4 * i);
+        }
+    }
+};
+template <> struct MmCodec<kQ4_0> : MmCodecNibble<kQ4_0> {};
+template <> struct MmCodec<kQ4_1> : MmCodecNibble<kQ4_1> {};
+template <> struct MmCodec<kQ5_0> : MmCodecNibble<kQ5_0> {};
+template <> struct MmCodec<kQ5_1> : MmCodecNibble<kQ5_1> {};
+template <> struct MmCodec<kMXFP4> : MmCodecNibble<kMXFP4> {};
+
+// Q4_K / Q5_K: element e of a super-block lies in 64-element chunk c = e / 64
+// at r = e % 64; its code is the low (r < 32) or high nibble of code byte
+// 32c + r % 32, and it uses sub-block 2c + (r >= 32).
+template <int TYPE>
+struct MmCodecK45 {
+    static constexpr bool kQ5 = TYPE == kQ5_K;
+    static constexpr int WORDS = kQ5 ? 12 : 8;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+        const uint32_t sb = ro + uint32_t(Format<TYPE>::kBytes) * uint32_t(k >> 8);
+        const int e = k & 255, c = e >> 6, l = e & 31;
+        const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(wr, sb + (kQ5 ? 48u : 16u) + 32u * c + l, 0, 0);
+        const u32x4 hd = __builtin_amdgcn_raw_buffer_load_b128(wr, sb, 0, 0);
+        w[0] = cw.x; w[1] = cw.y; w[2] = cw.z; w[3] = cw.w;
+        w[4] = hd.x; w[5] = hd.y; w[6] = hd.z; w[7] = hd.w;
+        if constexpr (kQ5) {
+            const u32x4 qh = __builtin_amdgcn_raw_buffer_load_b128(wr, sb + 16u + l, 0, 0);
+            w[8] = qh.x; w[9] = qh.y; w[10] = qh.z; w[11] = qh.w;
+        }
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int k, float (&e)[16]) {
+        const int r = k & 63, c = (k & 255) >> 6;
+        const bool high = r >= 32;
+        const int j = 2 * c + (high ? 1 : 0);
+        float a, b;
+        q4_k_coeffs(w[4], w[5], w[6], w[7], j, a, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (kQ5)
+                q5_k_x4(w[i], w[8 + i], j, high, a, b, e + 4 * i);
+            else
+                q4_k_x4(w[i], high, a, b, e + 4 * i);
+        }
+    }
+};
+template <> struct MmCodec<kQ4_K> : MmCodecK45<kQ4_K> {};
+template <> struct MmCodec<kQ5_K> : MmCodecK45<kQ5_K> {};
+
+// Q6_K, Q2_K, Q3_K: element e = 128 h + 32 p + l of a super-block, with
+// sub-scale (Q2_K: pair) 8 h + 2 p + l / 16.
+template <>
+struct MmCodec<kQ6_K> {
+    static constexpr int WORDS = 10;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+        const uint32_t sb = ro + 210u * uint32_t(k >> 8);
+        const int e = k & 255, h = e >> 7, p = (e >> 5) & 3, l = e & 31, si = 8 * h + 2 * p + (l >> 4);
+        const u32x4 ql = __builtin_amdgcn_raw_buffer_load_b128(wr, sb + 64u * h + 32u * (p & 1) + l, 0, 0);
+        const u32x4 qh = __builtin_amdgcn_raw_buffer_load_b128(wr, sb + 128u + 32u * h + l, 0, 0);
+        w[0] = ql.x; w[1] = ql.y; w[2] = ql.z; w[3] = ql.w;
+        w[4] = qh.x; w[5] = qh.y; w[6] = qh.z; w[7] = qh.w;
+        w[8] = __builtin_amdgcn_raw_buffer_load_b32(wr, sb + 192u + uint32_t(si & ~3), 0, 0);
+        w[9] = __builtin_amdgcn_raw_buffer_load_b16(wr, sb + 208u, 0, 0);
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int k, float (&e)[16]) {
+        const int el = k & 255, h = el >> 7, p = (el >> 5) & 3, si = 8 * h + 2 * p + ((el & 31) >> 4);
+        float a, b;
+        q6_k_coeffs(w[8], si & 3, half_to_f32(w[9] & 0xFFFFu), a, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q6_k_x4(w[i], p >= 2, w[4 + i], p, a, b, e + 4 * i);
+    }
+};
+
+template <>
+struct MmCodec<kQ2_K> {
+    static constexpr int WORDS = 6;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+        const uint32_t sb = ro + 84u * uint32_t(k >> 8);
+        const int e = k & 255, h = e >> 7, p = (e >> 5) & 3, l = e & 31, pi = 8 * h + 2 * p + (l >> 4);
+        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(wr, sb + 16u + 32u * h + l, 0, 0);
+        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+        w[4] = __builtin_amdgcn_raw_buffer_load_b32(wr, sb + uint32_t(pi & ~3), 0, 0);
+        w[5] = __builtin_amdgcn_raw_buffer_load_b32(wr, sb + 80u, 0, 0);
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int k, float (&e)[16]) {
+        const int el = k & 255, h = el >> 7, p = (el >> 5) & 3, pi = 8 * h + 2 * p + ((el & 31) >> 4);
+        float a, b;
+        q2_k_coeffs(w[4], pi & 3, half_to_f32(w[5] & 0xFFFFu), half_to_f32(w[5] >> 16), a, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q2_k_x4(w[i], p, a, b, e + 4 * i);
+    }
+};
+
+template <>
+struct MmCodec<kQ3_K> {
+    static constexpr int WORDS = 12;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+        const uint32_t sb = ro + 110u * uint32_t(k >> 8);
+        const int e = k & 255, h = e >> 7, l = e & 31;
+        const u32x4 qs = __builtin_amdgcn_raw_buffer_load_b128(wr, sb + 32u + 32u * h + l, 0, 0);
+        const u32x4 hm = __builtin_amdgcn_raw_buffer_load_b128(wr, sb + l, 0, 0);
+        const u32x2 f = __builtin_amdgcn_raw_buffer_load_b64(wr, sb + 96u, 0, 0);
+        w[0] = qs.x; w[1] = qs.y; w[2] = qs.z; w[3] = qs.w;
+        w[4] = hm.x; w[5] = hm.y; w[6] = hm.z; w[7] = hm.w;
+        w[8] = f.x; w[9] = f.y;
+        // field bytes 104 .. 107 and d at 108; nothing past the block
+        w[10] = __builtin_amdgcn_raw_buffer_load_b32(wr, sb + 104u, 0, 0);
+        w[11] = __builtin_amdgcn_raw_buffer_load_b16(wr, sb + 108u, 0, 0);
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int k, float (&e)[16]) {
+        const int el = k & 255, h = el >> 7, p = (el >> 5) & 3, si = 8 * h + 2 * p + ((el & 31) >> 4);
+        float a, b;
+        q3_k_coeffs(w[8], w[9], w[10], si, half_to_f32(w[11] & 0xFFFFu), a, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q3_k_x4(w[i], w[4 + i], p, 4 * h + p, a, b, e + 4 * i);
+    }
+};
+
+template <int TYPE, int WA, int WB, int CT>
+struct MmShape {
+    using F = Format<TYPE>;
+    static constexpr bool kDense = F::kBlock == 1;
+    static constexpr int kPThreads = 256;
+    static constexpr int kThreads = 2 * kPThreads;
+    static_assert(CT == 1 || CT == 2, "consumer grid 1 x 4 or 2 x 2");
+    static constexpr int CK = 4 / CT;
+    static constexpr int BT = 32 * WA * CT;  // rows of x per tile
+    static constexpr int BK = 32 * WB * CK;  // rows of W (outputs) per tile
+    static constexpr int kWgPerCu = BT == 32 ? 2 : 1;
+    static constexpr int BN = 32;  // k values per chunk
+    static constexpr int GP = BN + 4;
+    static constexpr int WP = BN + 4;
+    static constexpr int G_FLOATS = BT * GP;
+    static constexpr int W_FLOATS = BK * WP;
+    static constexpr int BUF_FLOATS = G_FLOATS + W_FLOATS;
+    static constexpr int kResident = (160 * 1024) / (2 * BUF_FLOATS * 4) < 2 ? 1 : 2;
+    static constexpr int GSLOTS = BT * BN / 4 / kPThreads;
+    static_assert(GSLOTS * kPThreads * 4 == BT * BN, "x chunk splits evenly");
+    // units of 16 elements of one W row per producer thread and chunk
+    static constexpr int UNITS = BK * BN / 16 / kPThreads;
+    static_assert(UNITS * kPThreads * 16 == BK * BN, "W chunk splits evenly");
+    static constexpr int WWORDS = UNITS * MmCodec<TYPE>::WORDS;
+    static constexpr int SLOT_REGS = 4 * GSLOTS + WWORDS;
+    static constexpr int RING = SLOT_REGS <= 32 ? 4 : 2;
+};
+
+template <int TYPE, int WA, int WB, int CT>
+__global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWgPerCu)) void mul_mat_ws_kernel(MmArgs args) {
+    using S = MmShape<TYPE, WA, WB, CT>;
+    using C = MmCodec<TYPE>;
+    constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, WP = S::WP;
+
+    __shared__ __attribute__((aligned(16))) float lds_all[2 * S::BUF_FLOATS];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tt, tn;
+    tile_coords(blockIdx.x, args.tiles_t, args.tiles_n, args.group, tt, tn);
+    const int t0 = tt * BT, n0 = tn * BK;
+    const int K = args.K, N = args.N, T = args.T;
+    const int nloc = (K + BN - 1) / BN;
+
+    if (wave >= 4) {
+        // ---------------- producer ----------------
+        const int p = tid - S::kPThreads;
+        float* const lds = lds_all;
+        constexpr int R = S::RING;
+        float4 gring[R][S::GSLOTS];
+        uint32_t wring[R][S::WWORDS];
+        // x: slot s is t row id / 8, columns 4 (id % 8) .. + 3 of the chunk
+        uint32_t goff[S::GSLOTS];
+#pragma unroll
+        for (int s = 0; s < S::GSLOTS; ++s) {
+            const int id = p + S::kPThreads * s;
+            goff[s] = uint32_t(((id >> 3) * args.ldx + 4 * (id & 7)) * 4);
+        }
+        // W: unit u is row id / 2 of the tile, elements 16 (id % 2) .. + 15
+        // of the chunk, written as that row's column of the LDS operand
+        uint32_t wro[S::UNITS];
+        int wlds[S::UNITS][4], wk[S::UNITS];
+#pragma unroll
+        for (int u = 0; u < S::UNITS; ++u) {
+            const int id = p + S::kPThreads * u, r = id >> 1, h = id & 1;
+            wro[u] = uint32_t(r * args.pitch);
+            wk[u] = 16 * h;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) wlds[u][g] = ws_w_index<WP>(r, 16 * h + 4 * g);
+        }
+        const long long x_end = (long long)(T - 1) * args.ldx + K;  // elements spanned by x
+        const long long wb = (long long)n0 * args.pitch;
+        const long long w_end =
+            (long long)(N - 1) * args.pitch + (long long)(K / S::F::kBlock) * S::F::kBytes;
+        const __amdgpu_buffer_rsrc_t wr =
+            buffer_rsrc(args.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
+
+        // Chunk c covers k = 32 c .. 32 c + 31. Loads are issued the same way
+        // for every chunk; x columns at or past K (the next row's values, or
+        // a chunk past the last) are zeroed when written to LDS, and so are
+        // the W values there (for dense rows they are the next row's; a
+        // chunk past the last is never contracted).
+        auto load_chunk = [&](auto slot, int c) {
+            float4(&greg)[S::GSLOTS] = gring[decltype(slot)::value];
+            uint32_t(&wreg)[S::WWORDS] = wring[decltype(slot)::value];
+            const int k0 = __builtin_amdgcn_readfirstlane(c * BN);
+            const long long xb = (long long)t0 * args.ldx + k0;
+            const __amdgpu_buffer_rsrc_t xr =
+                buffer_rsrc(args.X + xb, uint32_t(max(0ll, min(4 * (x_end - xb), (long long)0x7FFFFFFF))));
+#pragma unroll
+            for (int s = 0; s < S::GSLOTS; ++s) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, goff[s], 0, 0);
+                greg[s] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                      __uint_as_float(v.w));
+            }
+            // a chunk past the last one reads the last chunk again (its
+            // values are never used); no load leaves the row
+            const int kc = max(0, min(k0, (nloc - 1) * BN));
+#pragma unroll
+            for (int u = 0; u < S::UNITS; ++u) {
+                uint32_t(&w)[C::WORDS] = *reinterpret_cast<uint32_t(*)[C::WORDS]>(wreg + u * C::WORDS);
+                C::fetch(wr, wro[u], kc + wk[u], w);
+            }
+        };
+
+        auto store_chunk = [&](auto slot, auto buf, int c) {
+            float4(&greg)[S::GSLOTS] = gring[decltype(slot)::value];
+            const uint32_t(&wreg)[S::WWORDS] = wring[decltype(slot)::value];
+            float* gs = lds + decltype(buf)::value * S::BUF_FLOATS;
+            float* ws = gs + S::G_FLOATS;
+            const int k0 = c * BN;
+            if (k0 + BN > K) {
+#pragma unroll
+                for (int s = 0; s < S::GSLOTS; ++s) {
+                    const int k = k0 + 4 * ((p + S::kPThreads * s) & 7);
+                    if (k >= K) greg[s].x = 0.f;
+                    if (k + 1 >= K) greg[s].y = 0.f;
+                    if (k + 2 >= K) greg[s].z = 0.f;
+                    if (k + 3 >= K) greg[s].w = 0.f;
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < S::GSLOTS; ++s) {
+                const int id = p + S::kPThreads * s;
+                *reinterpret_cast<float4*>(gs + (id >> 3) * GP + 4 * (id & 7)) = greg[s];
+            }
+            const int kc = max(0, min(k0, (nloc - 1) * BN));
+#pragma unroll
+            for (int u = 0; u < S::UNITS; ++u) {
+                const uint32_t(&w)[C::WORDS] = *reinterpret_cast<const uint32_t(*)[C::WORDS]>(wreg + u * C::WORDS);
+                float e[16];
+                C::decode(w, kc + wk[u], e);
+                if (k0 + BN > K) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (k0 + wk[u] + i >= K) e[i] = 0.f;
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<float4*>(ws + wlds[u][g]) =
+                        make_float4(e[4 * g], e[4 * g + 1], e[4 * g + 2], e[4 * g + 3]);
+            }
+        };
+
+        using Zero = std::integral_constant<int, 0>;
+        static_for<R>([&](auto i) { load_chunk(i, i); });
+        store_chunk(Zero{}, Zero{}, 0);
+        __syncthreads();
+        auto step = [&](auto i, int c) {
+            constexpr int I = decltype(i)::value;
+            store_chunk(std::integral_constant<int, (I + 1) % R>{}, std::integral_constant<int, (I + 1) & 1>{},
+                        c + 1);
+            load_chunk(i, c + R);
+            __syncthreads();
+        };
+        int c0 = 0;
+        for (; c0 + R <= nloc; c0 += R) static_for<R>([&](auto i) { step(i, c0 + decltype(i)::value); });
+        static_for<R>([&](auto i) {
+            if (c0 + decltype(i)::value < nloc) step(i, c0 + decltype(i)::value);
+        });
+        return;
+    }
+
+    // ---------------- consumer ----------------
+    ws_consume<S, WA, WB, 1>(lds_all, tid, wave, nloc, t0, n0, T, N, args.Y, args.ldy);
+}
+
+}  // namespace retro

@@ -110,6 +110,120 @@ __device__ __forceinline__ int ws_w_index(int k, int n) {
     return k * WP + (n ^ (((k >> 4) & 7) << 2));
 }
 
+// Consumer waves 0 .. 4 NG - 1 of a producer/consumer tile kernel: contract
+// the nloc chunks its pipeline's producers publish in LDS (shape S: BT x BK
+// outputs, chunks of 32 reduction values; G-side operand t-major with pitch
+// GP, W-side operand k-major through ws_w_index) and store the BT x BK tile
+// at rows t0.., columns c0.. of dst (rows < T and columns < ncols only).
+template <typename S, int WA, int WB, int NG>
+__device__ __forceinline__ void ws_consume(float* lds_all, int tid, int wave, int nloc, int t0, int c0, int T,
+                                           int ncols, float* dst, long long ldd) {
+    const int lane = tid & 63;
+    const int cg = wave >> 2, cw = wave & 3;  // pipeline, wave within it
+    const int wt = cw / S::CK, wk = cw % S::CK;
+    const float* const lds = lds_all + cg * 2 * S::BUF_FLOATS;
+    constexpr int GP = S::GP, WP = S::WP;
+    const int h = lane >> 5, l32 = lane & 31;
+    f32x16 acc[WA][WB];
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+    // Phase q reads G[t][8q + 4h .. + 3] for the lane's t rows and
+    // W[8q + 4h .. + 3][k] for its k columns; the W index depends on q
+    // through the group permutation, so it is kept per phase.
+    const float* gbase = lds + (wt * 32 * WA + l32) * GP + 4 * h;
+    int widx[4][WB];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+            widx[q][b] = S::G_FLOATS + ws_w_index<WP>(wk * 32 * WB + 32 * b + l32, 8 * q + 4 * h);
+
+    auto read_phase = [&](auto buf_tag, int q, f32x4 (&av)[WA], f32x4 (&bv)[WB]) {
+        constexpr int off = decltype(buf_tag)::value * S::BUF_FLOATS;
+#pragma unroll
+        for (int a = 0; a < WA; ++a) av[a] = *reinterpret_cast<const f32x4*>(gbase + off + 32 * a * GP + 8 * q);
+#pragma unroll
+        for (int b = 0; b < WB; ++b) bv[b] = *reinterpret_cast<const f32x4*>(lds + off + widx[q][b]);
+    };
+    auto mfma_phase = [&](const f32x4 (&av)[WA], const f32x4 (&bv)[WB]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int a = 0; a < WA; ++a)
+#pragma unroll
+                for (int b = 0; b < WB; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][r], bv[b][r], acc[a][b], 0, 0, 0);
+    };
+    // One chunk from buffer BUF. Phase q + 1 is read while phase q's MFMAs
+    // run; phase 0 of the next chunk (buffer 1 - BUF) is read right after the
+    // barrier that publishes it, ahead of this chunk's last MFMAs. After the
+    // last chunk that read sees a stale buffer and its values are unused.
+    f32x4 a0[WA], a1[WA], b0[WB], b1[WB];
+    auto chunk = [&](auto buf_tag) {
+        using Next = std::integral_constant<int, 1 - decltype(buf_tag)::value>;
+        read_phase(buf_tag, 1, a1, b1);
+        mfma_phase(a0, b0);
+        read_phase(buf_tag, 2, a0, b0);
+        mfma_phase(a1, b1);
+        read_phase(buf_tag, 3, a1, b1);
+        mfma_phase(a0, b0);
+        __syncthreads();
+        read_phase(Next{}, 0, a0, b0);
+        mfma_phase(a1, b1);
+    };
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
+    __syncthreads();
+    read_phase(Buf0{}, 0, a0, b0);
+    for (int c = 0; c < nloc; c += 2) {
+        chunk(Buf0{});
+        if (c + 1 < nloc) chunk(Buf1{});
+    }
+    if constexpr (NG == 2) {
+        // pipeline 1's sums -> LDS (register r of lane l of wave w at
+        // r * 256 + 64 w + l), added to pipeline 0's in that fixed order
+        constexpr int NR = WA * WB * 16;
+        static_assert(NR * 256 <= 2 * NG * S::BUF_FLOATS, "reduction fits in LDS");
+        __syncthreads();
+        float* red = lds_all + 64 * cw + lane;
+        if (cg == 1) {
+#pragma unroll
+            for (int a = 0; a < WA; ++a)
+#pragma unroll
+                for (int b = 0; b < WB; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) red[((a * WB + b) * 16 + v) * 256] = acc[a][b][v];
+        }
+        __syncthreads();
+        if (cg == 1) return;
+#pragma unroll
+        for (int a = 0; a < WA; ++a)
+#pragma unroll
+            for (int b = 0; b < WB; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[a][b][v] += red[((a * WB + b) * 16 + v) * 256];
+    }
+
+    // D layout of v_mfma_f32_32x32x2f32: lane l, register v holds
+    // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+        for (int b = 0; b < WB; ++b) {
+            const int k = c0 + wk * 32 * WB + 32 * b + l32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + wt * 32 * WA + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (t < T && k < ncols) dst[(long long)t * ldd + k] = acc[a][b][v];
+            }
+        }
+}
+
 template <int TYPE, int WA, int WB, int CT, int NG>
 __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)) void out_prod_ws_kernel(
     TileArgs args) {
@@ -521,109 +635,7 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
     }
 
     // ---------------- consumer ----------------
-    const int lane = tid & 63;
-    const int cg = wave >> 2, cw = wave & 3;  // pipeline, wave within it
-    const int wt = cw / S::CK, wk = cw % S::CK;
-    const float* const lds = lds_all + cg * 2 * S::BUF_FLOATS;
-    const int h = lane >> 5, l32 = lane & 31;
-    f32x16 acc[WA][WB];
-#pragma unroll
-    for (int a = 0; a < WA; ++a)
-#pragma unroll
-        for (int b = 0; b < WB; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-
-    // Phase q reads G[t][8q + 4h .. + 3] for the lane's t rows and
-    // W[8q + 4h .. + 3][k] for its k columns; the W index depends on q
-    // through the group permutation, so it is kept per phase.
-    const float* gbase = lds + (wt * 32 * WA + l32) * GP + 4 * h;
-    int widx[4][WB];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int b = 0; b < WB; ++b)
-            widx[q][b] = S::G_FLOATS + ws_w_index<WP>(wk * 32 * WB + 32 * b + l32, 8 * q + 4 * h);
-
-    auto read_phase = [&](auto buf_tag, int q, f32x4 (&av)[WA], f32x4 (&bv)[WB]) {
-        constexpr int off = decltype(buf_tag)::value * S::BUF_FLOATS;
-#pragma unroll
-        for (int a = 0; a < WA; ++a) av[a] = *reinterpret_cast<const f32x4*>(gbase + off + 32 * a * GP + 8 * q);
-#pragma unroll
-        for (int b = 0; b < WB; ++b) bv[b] = *reinterpret_cast<const f32x4*>(lds + off + widx[q][b]);
-    };
-    auto mfma_phase = [&](const f32x4 (&av)[WA], const f32x4 (&bv)[WB]) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int a = 0; a < WA; ++a)
-#pragma unroll
-                for (int b = 0; b < WB; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][r], bv[b][r], acc[a][b], 0, 0, 0);
-    };
-    // One chunk from buffer BUF. Phase q + 1 is read while phase q's MFMAs
-    // run; phase 0 of the next chunk (buffer 1 - BUF) is read right after the
-    // barrier that publishes it, ahead of this chunk's last MFMAs. After the
-    // last chunk that read sees a stale buffer and its values are unused.
-    f32x4 a0[WA], a1[WA], b0[WB], b1[WB];
-    auto chunk = [&](auto buf_tag) {
-        using Next = std::integral_constant<int, 1 - decltype(buf_tag)::value>;
-        read_phase(buf_tag, 1, a1, b1);
-        mfma_phase(a0, b0);
-        read_phase(buf_tag, 2, a0, b0);
-        mfma_phase(a1, b1);
-        read_phase(buf_tag, 3, a1, b1);
-        mfma_phase(a0, b0);
-        __syncthreads();
-        read_phase(Next{}, 0, a0, b0);
-        mfma_phase(a1, b1);
-    };
-    using Buf0 = std::integral_constant<int, 0>;
-    using Buf1 = std::integral_constant<int, 1>;
-    __syncthreads();
-    read_phase(Buf0{}, 0, a0, b0);
-    for (int c = 0; c < nloc; c += 2) {
-        chunk(Buf0{});
-        if (c + 1 < nloc) chunk(Buf1{});
-    }
-    if constexpr (NG == 2) {
-        // pipeline 1's sums -> LDS (register r of lane l of wave w at
-        // r * 256 + 64 w + l), added to pipeline 0's in that fixed order
-        constexpr int NR = WA * WB * 16;
-        static_assert(NR * 256 <= 2 * NG * S::BUF_FLOATS, "reduction fits in LDS");
-        __syncthreads();
-        float* red = lds_all + 64 * cw + lane;
-        if (cg == 1) {
-#pragma unroll
-            for (int a = 0; a < WA; ++a)
-#pragma unroll
-                for (int b = 0; b < WB; ++b)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) red[((a * WB + b) * 16 + v) * 256] = acc[a][b][v];
-        }
-        __syncthreads();
-        if (cg == 1) return;
-#pragma unroll
-        for (int a = 0; a < WA; ++a)
-#pragma unroll
-            for (int b = 0; b < WB; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[a][b][v] += red[((a * WB + b) * 16 + v) * 256];
-    }
-
-    // D layout of v_mfma_f32_32x32x2f32: lane l, register v holds
-    // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
-#pragma unroll
-    for (int a = 0; a < WA; ++a)
-#pragma unroll
-        for (int b = 0; b < WB; ++b) {
-            const int k = k0 + wk * 32 * WB + 32 * b + l32;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int t = t0 + wt * 32 * WA + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = acc[a][b][v];
-            }
-        }
+    ws_consume<S, WA, WB, NG>(lds_all, tid, wave, nloc, t0, k0, T, K, args.dst, args.ldd);
 }
 
 }  // namespace retro

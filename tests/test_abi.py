@@ -177,6 +177,28 @@ def test_batched_validation():
     assert call(w=None) == q.E_NULL
 
 
+def test_mul_mat_validation_and_choice():
+    mm = q.lib.retro_mul_mat
+    # (type, W, X, Y, K, N, T, stream)
+    assert mm(99, None, None, None, 32, 1, 1, None) == q.E_TYPE
+    assert mm(q.Q4_K, None, None, None, 128, 1, 1, None) == q.E_SHAPE
+    assert mm(q.F32, None, None, None, 4, 0, 4, None) == q.OK            # no outputs
+    assert mm(q.F32, None, None, None, 4, 4, 4, None) == q.E_NULL
+    assert mm(q.F32, 0x100004, 0x200000, 0x300000, 4, 4, 4, None) == q.E_ALIGN
+    assert mm(q.F32, 0x100000, 0x200000, 0x100020, 4, 4, 4, None) == q.E_ALIAS   # Y over W
+    assert q.lib.retro_mul_mat_variant(q.VARIANT_WS_128x256, q.F32, 0x100000, 0x200000, 0x300000, 4, 4, 4,
+                                       None) == q.E_VARIANT
+    assert q.mul_mat_choice(q.Q4_K, 4096, 14336, 4096) == q.VARIANT_WS_128x128
+    assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 16) == q.VARIANT_SKINNY
+    assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 17) == q.VARIANT_WS_32x128
+    assert q.mul_mat_choice(q.F16, 301, 64, 100) == q.VARIANT_SIMPLE      # x rows not in 16-byte units
+    assert q.mul_mat_choice(q.F16, 301, 64, 9) == q.VARIANT_SKINNY
+    assert not q.mul_mat_variant_applies(q.VARIANT_WS_64x128, q.F16, 301, 64, 100)
+    assert q.mul_mat_variant_applies(q.VARIANT_SIMPLE, q.F16, 301, 64, 100)
+    for wtype in (q.Q8_0, q.Q4_0, q.MXFP4, q.Q2_K, q.Q6_K, q.BF16):
+        assert q.mul_mat_choice(wtype, 4096, 4096, 512) in (q.VARIANT_WS_128x128, q.VARIANT_WS_64x128)
+
+
 def test_strerror_covers_every_code():
     for code in (q.OK, q.E_TYPE, q.E_SHAPE, q.E_NULL, q.E_ALIGN, q.E_ALIAS, q.E_HIP, q.E_VARIANT):
         s = q.strerror(code)

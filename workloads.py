@@ -205,6 +205,12 @@ def make_grad(T: int, N: int, sigma: float, rng: np.random.Generator) -> np.ndar
     return g
 
 
+def make_input(T: int, K: int, seed: int, sigma: float = 1.0) -> np.ndarray:
+    """The input x of the forward mul_mat: T x K float32, N(0, sigma), from
+    its own generator (seed) so that it does not disturb a case's draws."""
+    return make_grad(T, K, sigma, np.random.default_rng(seed))
+
+
 def make_case(wtype: int, N: int, K: int, T: int, seed: int, g_sigma: float = 1.0) -> dict:
     """One seeded (W, G) pair in the draw order stated in the module docstring."""
     rng = np.random.Generator(np.random.PCG64(seed))
