@@ -307,7 +307,8 @@ int retro_out_prod_strided_variant_applies(int variant, int type, int64_t K, int
  * Pointers, alignment, aliasing, errors and execution as retro_out_prod.
  * Variants: RETRO_VARIANT_WS_128x128 / _64x128 / _32x128 (tiles of T x N;
  * need K % 4 == 0 for F32/F16/BF16), RETRO_VARIANT_SKINNY (T <= 16: one
- * workgroup per 16 rows of W over all of k) and RETRO_VARIANT_SIMPLE.
+ * workgroup per 16 rows of W over all of k; the same condition on K) and
+ * RETRO_VARIANT_SIMPLE (any shape).
  */
 int retro_mul_mat(int type, const void *W, const float *X, float *Y, int64_t K, int64_t N, int64_t T,
                   void *stream);

@@ -478,7 +478,9 @@ bool mm_tile_applies(const MmTile& v, int type, int64_t K, int64_t N, int64_t T)
 
 bool mm_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
     if (variant == RETRO_VARIANT_SIMPLE) return cdiv(T * N, 256) < kGridLimit;
-    if (variant == RETRO_VARIANT_SKINNY) return T <= 16 && cdiv(N, 16) < kGridLimit;
+    if (variant == RETRO_VARIANT_SKINNY)  // 16 rows of W and of x addressed with 32-bit offsets
+        return T <= 16 && cdiv(N, 16) < kGridLimit && !(is_dense(type) && K % 4) &&
+               16 * row_bytes_of(type, K) < (int64_t(1) << 31) && 16 * K * 4 < (int64_t(1) << 31);
     for (const auto& v : kMmTiles)
         if (v.id == variant) return mm_tile_applies(v, type, K, N, T);
     return false;

@@ -1233,48 +1233,4 @@ __global__ __launch_bounds__(256) void mul_mat_simple_kernel(MmSimpleArgs a) {
     a.Y[(long long)t * a.ldy + n] = acc;
 }
 
-// mul_mat for T <= 16: one workgroup (16 waves) per 16 rows of W, all of k,
-// v_mfma_f32_16x16x4_f32 with M = t, N = W row, K = 4 steps of k. Step s of
-// a 16-column group g uses column 16 g + 4 (l / 16) + s for lane l, so a
-// lane decodes 4 consecutive elements of its row and reads 4 consecutive
-// x values as one float4. Groups go to waves in turn; the partial sums are
-// added over waves in increasing wave order in LDS (deterministic).
-template <int TYPE>
-__global__ __launch_bounds__(1024) void mul_mat_skinny_kernel(MmSimpleArgs a) {
-    constexpr int NW = 16;
-    __shared__ __attribute__((aligned(16))) float part[NW * 256];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n0 = blockIdx.x * 16;
-    const int j = lane & 15, kk = lane >> 4;
-    const int K = a.K;
-    const uint8_t* row = a.W + (long long)min(n0 + j, a.N - 1) * a.pitch;  // rows past N: unused outputs
-    const bool trow = j < a.T;
-    const float* x = a.X + (long long)(trow ? j : 0) * a.ldx;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int groups = (K + 15) / 16;
-#pragma unroll 4
-    for (int g = wave; g < groups; g += NW) {
-        const int k = 16 * g + 4 * kk;
-        float e[4];
-        skinny_load4<TYPE>(row, k, K, a.wide, e);
-        float xv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xv[i] = (trow && k + i < K) ? x[k + i] : 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s], e[s], acc, 0, 0, 0);
-    }
-    // D layout: lane l, register v holds t = 4 (l / 16) + v, row n0 + l % 16
-#pragma unroll
-    for (int v = 0; v < 4; ++v) part[wave * 256 + (4 * kk + v) * 16 + j] = acc[v];
-    __syncthreads();
-    if (tid < 256) {
-        const int t = tid >> 4, nn = tid & 15;
-        float sum = part[tid];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) sum += part[w * 256 + tid];
-        if (t < a.T && n0 + nn < a.N) a.Y[(long long)t * a.ldy + n0 + nn] = sum;
-    }
-}
-
 }  // namespace retro

@@ -414,4 +414,93 @@ __global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWgPerCu)) void mu
     ws_consume<S, WA, WB, 1>(lds_all, tid, wave, nloc, t0, n0, T, N, args.Y, args.ldy);
 }
 
+// mul_mat for T <= 16: one workgroup (16 waves) per 16 rows of W over all
+// of k, v_mfma_f32_16x16x4_f32 with M = t, N = W row, K = 4 steps of k.
+// Iteration g of a wave covers k = 64 g .. 64 g + 63: lane l decodes the 16
+// elements 64 g + 16 (l / 16) .. + 15 of row n0 + l % 16 (one MmCodec unit,
+// one header decode) and reads the same 16 x values of row t = l % 16, and
+// round r, step s of the 16 MFMAs uses element 4 r + s. The next
+// iteration's loads are issued before the current one is decoded. Partial
+// sums are added over waves in increasing wave order in LDS.
+template <int TYPE>
+__global__ __launch_bounds__(1024) void mul_mat_skinny_kernel(MmSimpleArgs a) {
+    using C = MmCodec<TYPE>;
+    using F = Format<TYPE>;
+    constexpr int NW = 16;
+    __shared__ __attribute__((aligned(16))) float part[NW * 256];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * 16;
+    const int j = lane & 15, kk = lane >> 4;
+    const int K = a.K;
+    // W rows n0 .. n0 + 15 (rows at or past N read as zero); x rows t (t at
+    // or past T read as zero: x rows are K floats apart)
+    const long long wb = (long long)n0 * a.pitch;
+    const long long w_end = (long long)(a.N - 1) * a.pitch + (long long)(K / F::kBlock) * F::kBytes;
+    const __amdgpu_buffer_rsrc_t wr =
+        buffer_rsrc(a.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
+    const long long x_end = (long long)(a.T - 1) * a.ldx + K;
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.X, uint32_t(max(0ll, min(4 * x_end, (long long)0x7FFFFFFF))));
+    const uint32_t ro = uint32_t(j * a.pitch);
+    const uint32_t xo = uint32_t(j * a.ldx * 4);
+    const int groups = (K + 63) / 64;
+
+    uint32_t wraw[2][C::WORDS];
+    u32x4 xraw[2][4];
+    // Loads of group g into slot S: always issued (a group past the last
+    // reads bytes it never uses), so that they stay in flight.
+    auto fetch = [&](auto slot, int g) {
+        constexpr int S = decltype(slot)::value;
+        const int k = 64 * g + 16 * kk;
+        C::fetch(wr, ro, k, wraw[S]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xraw[S][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 4u * k + 16u * i, 0, 0);
+    };
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](auto slot, int g) {
+        constexpr int S = decltype(slot)::value;
+        const int k = 64 * g + 16 * kk;
+        float e[16], xv[16];
+        C::decode(wraw[S], k, e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xv[4 * i] = __uint_as_float(xraw[S][i].x);
+            xv[4 * i + 1] = __uint_as_float(xraw[S][i].y);
+            xv[4 * i + 2] = __uint_as_float(xraw[S][i].z);
+            xv[4 * i + 3] = __uint_as_float(xraw[S][i].w);
+        }
+        if (k + 16 > K) {  // elements at or past K: zero on both sides
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (k + i >= K) e[i] = xv[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i], e[i], acc, 0, 0, 0);
+    };
+    using Slot0 = std::integral_constant<int, 0>;
+    using Slot1 = std::integral_constant<int, 1>;
+    int g = wave;
+    if (g < groups) {
+        fetch(Slot0{}, g);
+        for (; g < groups; g += 2 * NW) {
+            fetch(Slot1{}, g + NW);
+            compute(Slot0{}, g);
+            if (g + NW >= groups) break;
+            fetch(Slot0{}, g + 2 * NW);
+            compute(Slot1{}, g + NW);
+        }
+    }
+    // D layout: lane l, register v holds t = 4 (l / 16) + v, row n0 + l % 16
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[wave * 256 + (4 * kk + v) * 16 + j] = acc[v];
+    __syncthreads();
+    if (tid < 256) {
+        const int t = tid >> 4, nn = tid & 15;
+        float sum = part[tid];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) sum += part[w * 256 + tid];
+        if (t < a.T && n0 + nn < a.N) a.Y[(long long)t * a.ldy + n0 + nn] = sum;
+    }
+}
+
 }  // namespace retro

@@ -192,7 +192,8 @@ def test_mul_mat_validation_and_choice():
     assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 16) == q.VARIANT_SKINNY
     assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 17) == q.VARIANT_WS_32x128
     assert q.mul_mat_choice(q.F16, 301, 64, 100) == q.VARIANT_SIMPLE      # x rows not in 16-byte units
-    assert q.mul_mat_choice(q.F16, 301, 64, 9) == q.VARIANT_SKINNY
+    assert q.mul_mat_choice(q.F16, 301, 64, 9) == q.VARIANT_SIMPLE
+    assert q.mul_mat_choice(q.F16, 300, 64, 9) == q.VARIANT_SKINNY
     assert not q.mul_mat_variant_applies(q.VARIANT_WS_64x128, q.F16, 301, 64, 100)
     assert q.mul_mat_variant_applies(q.VARIANT_SIMPLE, q.F16, 301, 64, 100)
     for wtype in (q.Q8_0, q.Q4_0, q.MXFP4, q.Q2_K, q.Q6_K, q.BF16):
