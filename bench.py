@@ -32,6 +32,8 @@ LARGE = "q4_k_n14336_k4096_t4096"
 SKINNY = "q4_k_n4096_k14336_t16"
 PROFILES = os.path.join(REPO, "profiles")
 KERNEL_SOURCES = ["quantized_weight_backward_amd/csrc/retro_kernels.h",
+                  "quantized_weight_backward_amd/csrc/retro_unit.hip",
+                  "quantized_weight_backward_amd/csrc/retro_host.h",
                   "quantized_weight_backward_amd/csrc/retro_ws_kernel.h",
                   "quantized_weight_backward_amd/csrc/retro_decode.h",
                   "quantized_weight_backward_amd/csrc/retro_api.hip"]

@@ -1,6 +1,6 @@
 // retro_api.hip - the C ABI declared in include/retro_out_prod.h: argument
-// validation, kernel choice and launch. Host code only; the kernels live in
-// retro_kernels.h.
+// validation and kernel choice. Host code only: the launches of each weight
+// type are in its own object built from retro_unit.hip.
 //
 // The entry points follow the OUT_PROD admission rule of llama.cpp PR #3
 // ("cuda: out_prod accepts a quantized src0", section "What": any contiguous
@@ -11,57 +11,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "retro_kernels.h"
-#include "retro_ws_kernel.h"
-#include "retro_mm_kernel.h"
+#include "retro_host.h"
 #include "retro_out_prod.h"
 
 namespace {
 
-using namespace retro;
-
-constexpr int kNumCUs = 256;  // MI355X
-
-// Waves per skinny workgroup (each CU runs one skinny workgroup at the
-// benchmarked shapes, so this sets the waves per SIMD available to hide
-// memory latency).
-#ifndef RETRO_SKINNY_WAVES
-#define RETRO_SKINNY_WAVES 16
-#endif
-constexpr int64_t kDimLimit = int64_t(1) << 31;
-constexpr int64_t kByteLimit = int64_t(1) << 62;
-constexpr int64_t kCountLimit = int64_t(1) << 60;  // float counts: 4 * count < 2^62
-constexpr int64_t kGridLimit = int64_t(1) << 30;
-
-struct Geometry {
-    int block, bytes;
-};
-
-bool geometry(int type, Geometry& g) {
-    switch (type) {
-        case RETRO_F32: g = {1, 4}; return true;
-        case RETRO_F16: g = {1, 2}; return true;
-        case RETRO_BF16: g = {1, 2}; return true;
-        case RETRO_Q8_0: g = {32, 34}; return true;
-        case RETRO_Q4_0: g = {32, 18}; return true;
-        case RETRO_Q4_1: g = {32, 20}; return true;
-        case RETRO_Q5_0: g = {32, 22}; return true;
-        case RETRO_Q5_1: g = {32, 24}; return true;
-        case RETRO_MXFP4: g = {32, 17}; return true;
-        case RETRO_Q4_K: g = {256, 144}; return true;
-        case RETRO_Q5_K: g = {256, 176}; return true;
-        case RETRO_Q2_K: g = {256, 84}; return true;
-        case RETRO_Q3_K: g = {256, 110}; return true;
-        case RETRO_Q6_K: g = {256, 210}; return true;
-        default: return false;
-    }
-}
-
-int64_t row_bytes_of(int type, int64_t K) {
-    Geometry g;
-    if (!geometry(type, g) || K < 0 || K % g.block) return -1;
-    return K / g.block * g.bytes;
-}
+using namespace retro::host;
 
 // a * b < limit for non-negative a, b.
 bool product_below(int64_t a, int64_t b, int64_t limit) { return a == 0 || b < limit / a; }
@@ -78,24 +33,6 @@ int check_shape(int type, int64_t K, int64_t N, int64_t T) {
         return RETRO_E_SHAPE;
     return RETRO_OK;
 }
-
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Layout of the three operands: row strides, and the batches over two outer
-// dimensions (ne2 x ne3 products; W has ne02 x ne03 matrices, each serving
-// ne2 / ne02 x ne3 / ne03 consecutive batches).
-struct Strides {
-    int64_t ldw;  // bytes between consecutive W rows (>= the row's bytes)
-    int64_t ldg;  // floats between consecutive G rows (>= N)
-    int64_t ldd;  // floats between consecutive dst rows (>= K)
-    int64_t ne02 = 1, ne03 = 1, ne2 = 1, ne3 = 1;
-    int64_t sw2 = 0, sw3 = 0;  // bytes between W matrices
-    int64_t sg2 = 0, sg3 = 0;  // floats between G matrices
-    int64_t sd2 = 0, sd3 = 0;  // floats between dst matrices
-    int64_t batches() const { return ne2 * ne3; }
-};
-
-constexpr int64_t kBatchLimit = 65535;  // workgroups along the grid's second dimension
 
 Strides contiguous(int type, int64_t K, int64_t N) { return {row_bytes_of(type, K), N, K}; }
 
@@ -219,159 +156,6 @@ int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     return best < 0 ? RETRO_E_SHAPE : best;
 }
 
-// Row tiles per group of the tile order. An XCD runs S = 32 CUs x wg_per_cu
-// tiles at once, `height` row tiles by S / height column tiles of its range,
-// so G is fetched about ceil(tiles_k / (S / height)) times and W about
-// ceil(tiles_t / height) times; the height that minimises the sum wins.
-int group_height(int64_t tiles_t, int64_t tiles_k, int wg_per_cu, double g_bytes, double w_bytes) {
-    const int64_t S = 32 * int64_t(wg_per_cu);
-    int best = 1;
-    double best_cost = -1;
-    for (int64_t h = 1; h <= S; h *= 2) {
-        const double cost = g_bytes * double(cdiv(tiles_k, S / h)) + w_bytes * double(cdiv(tiles_t, h));
-        if (best_cost < 0 || cost < best_cost) {
-            best = int(h);
-            best_cost = cost;
-        }
-        if (h >= tiles_t) break;
-    }
-    return best;
-}
-
-// hipGetLastError reports the last error of any runtime call on this thread,
-// so it is cleared right before each launch (clear_last_error) and read right
-// after it (launch_status): the result is this launch's status only.
-void clear_last_error() { (void)hipGetLastError(); }
-int launch_status() { return hipGetLastError() == hipSuccess ? RETRO_OK : RETRO_E_HIP; }
-
-BatchArgs batch_args(const Strides& s) {
-    BatchArgs b;
-    b.ne2 = int(s.ne2);
-    b.r2 = int(s.ne2 / s.ne02);
-    b.r3 = int(s.ne3 / s.ne03);
-    b.w2 = s.sw2;
-    b.w3 = s.sw3;
-    b.g2 = s.sg2;
-    b.g3 = s.sg3;
-    b.d2 = s.sd2;
-    b.d3 = s.sd3;
-    return b;
-}
-
-template <int TYPE, int WA, int WB, int WGT, int WGK>
-int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
-                hipStream_t st) {
-    using S = TileShape<TYPE, WA, WB, WGT, WGK>;
-    TileArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.G = G;
-    a.dst = dst;
-    a.K = int(K);
-    a.N = int(N);
-    a.T = int(T);
-    a.pitch = s.ldw;
-    a.ldg = s.ldg;
-    a.ldd = s.ldd;
-    // Widest staging load that the row pitch, the tile span and the row's
-    // bytes are all multiples of (the base pointer is 16-byte aligned): then
-    // no load straddles the end of W, where a buffer load reads zero for the
-    // whole word.
-    const int64_t rbytes = row_bytes_of(TYPE, K);
-    int wvec = 16;
-    while (wvec > 1 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0 || (rbytes % wvec) != 0)) wvec >>= 1;
-    a.wvec = wvec;
-    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
-    a.tiles_t = int(cdiv(T, S::BT));
-    a.tiles_k = int(cdiv(K, S::BK));
-    a.group = group_height(a.tiles_t, a.tiles_k, 2, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
-    a.batch = batch_args(s);
-    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
-    clear_last_error();
-    hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt, unsigned(s.batches())),
-                       dim3(S::kThreads), 0, st, a);
-    return launch_status();
-}
-
-template <int TYPE, int WA, int WB, int CT, int NG = 1>
-int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
-              hipStream_t st) {
-    using S = WsShape<TYPE, WA, WB, CT, NG>;
-    TileArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.G = G;
-    a.dst = dst;
-    a.K = int(K);
-    a.N = int(N);
-    a.T = int(T);
-    a.pitch = s.ldw;
-    a.ldg = s.ldg;
-    a.ldd = s.ldd;
-    a.wvec = 16;
-    a.gvec = 1;
-    a.tiles_t = int(cdiv(T, S::BT));
-    a.tiles_k = int(cdiv(K, S::BK));
-    a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
-    a.batch = batch_args(s);
-    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
-    clear_last_error();
-    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG>), dim3(nt, unsigned(s.batches())),
-                       dim3(S::kThreads), 0, st, a);
-    return launch_status();
-}
-
-template <int TYPE>
-int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
-                  hipStream_t st) {
-    constexpr int kWaves = RETRO_SKINNY_WAVES;
-    SkinnyArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.G = G;
-    a.dst = dst;
-    a.K = int(K);
-    a.N = int(N);
-    a.T = int(T);
-    a.pitch = s.ldw;
-    a.ldg = s.ldg;
-    a.ldd = s.ldd;
-    a.wide = (K % 4 == 0) ? 1 : 0;
-    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
-    a.batch = batch_args(s);
-    const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches())), block(kWaves * 64);
-    clear_last_error();
-    if (a.wide && a.gvec)
-        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false>), grid, block, 0, st, a);
-    return launch_status();
-}
-
-template <int TYPE>
-int launch_variant(int variant, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
-                   const Strides& s, hipStream_t st) {
-    switch (variant) {
-        case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, st);
-        case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, s, st);
-        case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, s, st);
-        case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4, 2>(W, G, dst, K, N, T, s, st);
-        case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4, 2>(W, G, dst, K, N, T, s, st);
-        case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, s, st);
-        default: break;
-    }
-    if constexpr (!kSuperBlock<TYPE>) {
-        switch (variant) {
-            case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, s, st);
-            case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, s, st);
-            case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, s, st);
-            case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2, 2>(W, G, dst, K, N, T, s, st);
-            case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2, 2>(W, G, dst, K, N, T, s, st);
-            case RETRO_VARIANT_WS2_64x128: return launch_ws<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, s, st);
-            case RETRO_VARIANT_WS_32x128: return launch_ws<TYPE, 1, 1, 1>(W, G, dst, K, N, T, s, st);
-            default: break;
-        }
-    }
-    return RETRO_E_VARIANT;
-}
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -418,38 +202,22 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (type) {
-        case RETRO_F32: return launch_variant<kF32>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_F16: return launch_variant<kF16>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_BF16: return launch_variant<kBF16>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q8_0: return launch_variant<kQ8_0>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q4_0: return launch_variant<kQ4_0>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q4_1: return launch_variant<kQ4_1>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q5_0: return launch_variant<kQ5_0>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q5_1: return launch_variant<kQ5_1>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_MXFP4: return launch_variant<kMXFP4>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q4_K: return launch_variant<kQ4_K>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q5_K: return launch_variant<kQ5_K>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q2_K: return launch_variant<kQ2_K>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q3_K: return launch_variant<kQ3_K>(variant, W, G, dst, K, N, T, s, st);
-        case RETRO_Q6_K: return launch_variant<kQ6_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_F32: return launch_out_prod<RETRO_F32>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_F16: return launch_out_prod<RETRO_F16>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_BF16: return launch_out_prod<RETRO_BF16>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q8_0: return launch_out_prod<RETRO_Q8_0>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q4_0: return launch_out_prod<RETRO_Q4_0>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q4_1: return launch_out_prod<RETRO_Q4_1>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q5_0: return launch_out_prod<RETRO_Q5_0>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q5_1: return launch_out_prod<RETRO_Q5_1>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_MXFP4: return launch_out_prod<RETRO_MXFP4>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q4_K: return launch_out_prod<RETRO_Q4_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q5_K: return launch_out_prod<RETRO_Q5_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q2_K: return launch_out_prod<RETRO_Q2_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q3_K: return launch_out_prod<RETRO_Q3_K>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_Q6_K: return launch_out_prod<RETRO_Q6_K>(variant, W, G, dst, K, N, T, s, st);
         default: return RETRO_E_TYPE;
     }
-}
-
-template <int TYPE>
-int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t st) {
-    DequantArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.out = out;
-    a.K = int(K);
-    a.N = int(N);
-    a.pitch = row_bytes_of(TYPE, K);
-    a.wide = (K % 4 == 0) ? 1 : 0;
-    a.gpr = int(cdiv(K, 4));
-    a.groups = N * int64_t(a.gpr);
-    clear_last_error();
-    hipLaunchKernelGGL((dequant_kernel<TYPE>), dim3(unsigned(cdiv(a.groups, 256))), dim3(256), 0, st, a);
-    return launch_status();
 }
 
 // ---------------------------------------------------------------------------
@@ -502,77 +270,6 @@ int mm_choose(int type, int64_t K, int64_t N, int64_t T) {
     return best < 0 ? RETRO_E_SHAPE : best;
 }
 
-template <int TYPE, int WA, int WB, int CT>
-int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
-    using S = MmShape<TYPE, WA, WB, CT>;
-    MmArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.X = X;
-    a.Y = Y;
-    a.K = int(K);
-    a.N = int(N);
-    a.T = int(T);
-    a.pitch = row_bytes_of(TYPE, K);
-    a.ldx = K;
-    a.ldy = N;
-    a.tiles_t = int(cdiv(T, S::BT));
-    a.tiles_n = int(cdiv(N, S::BK));
-    a.group = group_height(a.tiles_t, a.tiles_n, S::kResident, 4.0 * T * K, double(N) * a.pitch);
-    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_n);
-    clear_last_error();
-    hipLaunchKernelGGL((mul_mat_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);
-    return launch_status();
-}
-
-template <int TYPE>
-int launch_mm_simple(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
-    MmSimpleArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.X = X;
-    a.Y = Y;
-    a.K = int(K);
-    a.N = int(N);
-    a.T = int(T);
-    a.pitch = row_bytes_of(TYPE, K);
-    a.ldx = K;
-    a.ldy = N;
-    a.wide = (K % 4 == 0) ? 1 : 0;
-    clear_last_error();
-    hipLaunchKernelGGL((mul_mat_simple_kernel<TYPE>), dim3(unsigned(cdiv(T * N, 256))), dim3(256), 0, st, a);
-    return launch_status();
-}
-
-template <int TYPE>
-int launch_mm_skinny(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
-    MmSimpleArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.X = X;
-    a.Y = Y;
-    a.K = int(K);
-    a.N = int(N);
-    a.T = int(T);
-    a.pitch = row_bytes_of(TYPE, K);
-    a.ldx = K;
-    a.ldy = N;
-    a.wide = (K % 4 == 0) ? 1 : 0;
-    clear_last_error();
-    hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE>), dim3(unsigned(cdiv(N, 16))), dim3(1024), 0, st, a);
-    return launch_status();
-}
-
-template <int TYPE>
-int launch_mm_variant(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
-                      hipStream_t st) {
-    switch (variant) {
-        case RETRO_VARIANT_WS_128x128: return launch_mm<TYPE, 2, 2, 2>(W, X, Y, K, N, T, st);
-        case RETRO_VARIANT_WS_64x128: return launch_mm<TYPE, 1, 2, 2>(W, X, Y, K, N, T, st);
-        case RETRO_VARIANT_WS_32x128: return launch_mm<TYPE, 1, 1, 1>(W, X, Y, K, N, T, st);
-        case RETRO_VARIANT_SIMPLE: return launch_mm_simple<TYPE>(W, X, Y, K, N, T, st);
-        case RETRO_VARIANT_SKINNY: return launch_mm_skinny<TYPE>(W, X, Y, K, N, T, st);
-        default: return RETRO_E_VARIANT;
-    }
-}
-
 int mul_mat_impl(int variant, int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
                  void* stream) {
     int rc = check_shape(type, K, N, T);
@@ -592,20 +289,20 @@ int mul_mat_impl(int variant, int type, const void* W, const float* X, float* Y,
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (type) {
-        case RETRO_F32: return launch_mm_variant<kF32>(variant, W, X, Y, K, N, T, st);
-        case RETRO_F16: return launch_mm_variant<kF16>(variant, W, X, Y, K, N, T, st);
-        case RETRO_BF16: return launch_mm_variant<kBF16>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q8_0: return launch_mm_variant<kQ8_0>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q4_0: return launch_mm_variant<kQ4_0>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q4_1: return launch_mm_variant<kQ4_1>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q5_0: return launch_mm_variant<kQ5_0>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q5_1: return launch_mm_variant<kQ5_1>(variant, W, X, Y, K, N, T, st);
-        case RETRO_MXFP4: return launch_mm_variant<kMXFP4>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q4_K: return launch_mm_variant<kQ4_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q5_K: return launch_mm_variant<kQ5_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q2_K: return launch_mm_variant<kQ2_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q3_K: return launch_mm_variant<kQ3_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q6_K: return launch_mm_variant<kQ6_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_F32: return launch_mul_mat<RETRO_F32>(variant, W, X, Y, K, N, T, st);
+        case RETRO_F16: return launch_mul_mat<RETRO_F16>(variant, W, X, Y, K, N, T, st);
+        case RETRO_BF16: return launch_mul_mat<RETRO_BF16>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q8_0: return launch_mul_mat<RETRO_Q8_0>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q4_0: return launch_mul_mat<RETRO_Q4_0>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q4_1: return launch_mul_mat<RETRO_Q4_1>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q5_0: return launch_mul_mat<RETRO_Q5_0>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q5_1: return launch_mul_mat<RETRO_Q5_1>(variant, W, X, Y, K, N, T, st);
+        case RETRO_MXFP4: return launch_mul_mat<RETRO_MXFP4>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q4_K: return launch_mul_mat<RETRO_Q4_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q5_K: return launch_mul_mat<RETRO_Q5_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q2_K: return launch_mul_mat<RETRO_Q2_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q3_K: return launch_mul_mat<RETRO_Q3_K>(variant, W, X, Y, K, N, T, st);
+        case RETRO_Q6_K: return launch_mul_mat<RETRO_Q6_K>(variant, W, X, Y, K, N, T, st);
         default: return RETRO_E_TYPE;
     }
 }
@@ -694,20 +391,20 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
     if (overlap(out, N * K * 4, W, N * row_bytes_of(type, K))) return RETRO_E_ALIAS;
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (type) {
-        case RETRO_F32: return launch_dequant<kF32>(W, out, K, N, st);
-        case RETRO_F16: return launch_dequant<kF16>(W, out, K, N, st);
-        case RETRO_BF16: return launch_dequant<kBF16>(W, out, K, N, st);
-        case RETRO_Q8_0: return launch_dequant<kQ8_0>(W, out, K, N, st);
-        case RETRO_Q4_0: return launch_dequant<kQ4_0>(W, out, K, N, st);
-        case RETRO_Q4_1: return launch_dequant<kQ4_1>(W, out, K, N, st);
-        case RETRO_Q5_0: return launch_dequant<kQ5_0>(W, out, K, N, st);
-        case RETRO_Q5_1: return launch_dequant<kQ5_1>(W, out, K, N, st);
-        case RETRO_MXFP4: return launch_dequant<kMXFP4>(W, out, K, N, st);
-        case RETRO_Q4_K: return launch_dequant<kQ4_K>(W, out, K, N, st);
-        case RETRO_Q5_K: return launch_dequant<kQ5_K>(W, out, K, N, st);
-        case RETRO_Q2_K: return launch_dequant<kQ2_K>(W, out, K, N, st);
-        case RETRO_Q3_K: return launch_dequant<kQ3_K>(W, out, K, N, st);
-        case RETRO_Q6_K: return launch_dequant<kQ6_K>(W, out, K, N, st);
+        case RETRO_F32: return launch_dequant<RETRO_F32>(W, out, K, N, st);
+        case RETRO_F16: return launch_dequant<RETRO_F16>(W, out, K, N, st);
+        case RETRO_BF16: return launch_dequant<RETRO_BF16>(W, out, K, N, st);
+        case RETRO_Q8_0: return launch_dequant<RETRO_Q8_0>(W, out, K, N, st);
+        case RETRO_Q4_0: return launch_dequant<RETRO_Q4_0>(W, out, K, N, st);
+        case RETRO_Q4_1: return launch_dequant<RETRO_Q4_1>(W, out, K, N, st);
+        case RETRO_Q5_0: return launch_dequant<RETRO_Q5_0>(W, out, K, N, st);
+        case RETRO_Q5_1: return launch_dequant<RETRO_Q5_1>(W, out, K, N, st);
+        case RETRO_MXFP4: return launch_dequant<RETRO_MXFP4>(W, out, K, N, st);
+        case RETRO_Q4_K: return launch_dequant<RETRO_Q4_K>(W, out, K, N, st);
+        case RETRO_Q5_K: return launch_dequant<RETRO_Q5_K>(W, out, K, N, st);
+        case RETRO_Q2_K: return launch_dequant<RETRO_Q2_K>(W, out, K, N, st);
+        case RETRO_Q3_K: return launch_dequant<RETRO_Q3_K>(W, out, K, N, st);
+        case RETRO_Q6_K: return launch_dequant<RETRO_Q6_K>(W, out, K, N, st);
         default: return RETRO_E_TYPE;
     }
 }

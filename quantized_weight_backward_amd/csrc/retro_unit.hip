@@ -1,0 +1,249 @@
+// retro_unit.hip - the kernels and launches of one weight type, chosen at
+// compile time with -DRETRO_UNIT_TYPE=<GGUF type id>. The library links one
+// such object per type; retro_api.hip validates arguments, picks the variant
+// and calls the entry points declared in retro_host.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "retro_host.h"
+#include "retro_kernels.h"
+#include "retro_mm_kernel.h"
+#include "retro_ws_kernel.h"
+
+#ifndef RETRO_UNIT_TYPE
+#error "RETRO_UNIT_TYPE (a GGUF weight type id) must be defined"
+#endif
+
+// Waves per skinny workgroup (each CU runs one skinny workgroup at the
+// benchmarked shapes, so this sets the waves per SIMD available to hide
+// memory latency).
+#ifndef RETRO_SKINNY_WAVES
+#define RETRO_SKINNY_WAVES 16
+#endif
+
+namespace retro {
+namespace host {
+
+static_assert(kF32 == RETRO_F32 && kF16 == RETRO_F16 && kBF16 == RETRO_BF16 && kQ8_0 == RETRO_Q8_0 &&
+                  kQ4_0 == RETRO_Q4_0 && kQ4_1 == RETRO_Q4_1 && kQ5_0 == RETRO_Q5_0 && kQ5_1 == RETRO_Q5_1 &&
+                  kMXFP4 == RETRO_MXFP4 && kQ2_K == RETRO_Q2_K && kQ3_K == RETRO_Q3_K && kQ4_K == RETRO_Q4_K &&
+                  kQ5_K == RETRO_Q5_K && kQ6_K == RETRO_Q6_K,
+              "device and ABI type ids agree");
+
+namespace {
+
+BatchArgs batch_args(const Strides& s) {
+    BatchArgs b;
+    b.ne2 = int(s.ne2);
+    b.r2 = int(s.ne2 / s.ne02);
+    b.r3 = int(s.ne3 / s.ne03);
+    b.w2 = s.sw2;
+    b.w3 = s.sw3;
+    b.g2 = s.sg2;
+    b.g3 = s.sg3;
+    b.d2 = s.sd2;
+    b.d3 = s.sd3;
+    return b;
+}
+
+template <int TYPE, int WA, int WB, int WGT, int WGK>
+int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+                hipStream_t st) {
+    using S = TileShape<TYPE, WA, WB, WGT, WGK>;
+    TileArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.G = G;
+    a.dst = dst;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = s.ldw;
+    a.ldg = s.ldg;
+    a.ldd = s.ldd;
+    // Widest staging load that the row pitch, the tile span and the row's
+    // bytes are all multiples of (the base pointer is 16-byte aligned): then
+    // no load straddles the end of W, where a buffer load reads zero for the
+    // whole word.
+    const int64_t rbytes = row_bytes_of(TYPE, K);
+    int wvec = 16;
+    while (wvec > 1 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0 || (rbytes % wvec) != 0)) wvec >>= 1;
+    a.wvec = wvec;
+    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
+    a.tiles_t = int(cdiv(T, S::BT));
+    a.tiles_k = int(cdiv(K, S::BK));
+    a.group = group_height(a.tiles_t, a.tiles_k, 2, 4.0 * T * N, double(N) * rbytes);
+    a.batch = batch_args(s);
+    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
+    clear_last_error();
+    hipLaunchKernelGGL((out_prod_tile_kernel<TYPE, WA, WB, WGT, WGK>), dim3(nt, unsigned(s.batches())),
+                       dim3(S::kThreads), 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE, int WA, int WB, int CT, int NG = 1>
+int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+              hipStream_t st) {
+    using S = WsShape<TYPE, WA, WB, CT, NG>;
+    TileArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.G = G;
+    a.dst = dst;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = s.ldw;
+    a.ldg = s.ldg;
+    a.ldd = s.ldd;
+    a.wvec = 16;
+    a.gvec = 1;
+    a.tiles_t = int(cdiv(T, S::BT));
+    a.tiles_k = int(cdiv(K, S::BK));
+    a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
+    a.batch = batch_args(s);
+    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
+    clear_last_error();
+    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG>), dim3(nt, unsigned(s.batches())),
+                       dim3(S::kThreads), 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE>
+int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+                  hipStream_t st) {
+    constexpr int kWaves = RETRO_SKINNY_WAVES;
+    SkinnyArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.G = G;
+    a.dst = dst;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = s.ldw;
+    a.ldg = s.ldg;
+    a.ldd = s.ldd;
+    a.wide = (K % 4 == 0) ? 1 : 0;
+    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
+    a.batch = batch_args(s);
+    const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches())), block(kWaves * 64);
+    clear_last_error();
+    if (a.wide && a.gvec)
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false>), grid, block, 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE, int WA, int WB, int CT>
+int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+    using S = MmShape<TYPE, WA, WB, CT>;
+    MmArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.X = X;
+    a.Y = Y;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.ldx = K;
+    a.ldy = N;
+    a.tiles_t = int(cdiv(T, S::BT));
+    a.tiles_n = int(cdiv(N, S::BK));
+    a.group = group_height(a.tiles_t, a.tiles_n, S::kResident, 4.0 * T * K, double(N) * a.pitch);
+    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_n);
+    clear_last_error();
+    hipLaunchKernelGGL((mul_mat_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    return launch_status();
+}
+
+MmSimpleArgs mm_simple_args(int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T) {
+    MmSimpleArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.X = X;
+    a.Y = Y;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = row_bytes_of(type, K);
+    a.ldx = K;
+    a.ldy = N;
+    a.wide = (K % 4 == 0) ? 1 : 0;
+    return a;
+}
+
+}  // namespace
+
+template <int TYPE>
+int launch_out_prod(int variant, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                    const Strides& s, hipStream_t st) {
+    switch (variant) {
+        case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, s, st);
+        default: break;
+    }
+    if constexpr (!kSuperBlock<TYPE>) {
+        switch (variant) {
+            case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_TILE_64x128: return launch_tile<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_TILE_64x64: return launch_tile<TYPE, 1, 1, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS_128x128: return launch_ws<TYPE, 2, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS_64x128: return launch_ws<TYPE, 1, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS2_64x128: return launch_ws<TYPE, 1, 2, 2, 2>(W, G, dst, K, N, T, s, st);
+            case RETRO_VARIANT_WS_32x128: return launch_ws<TYPE, 1, 1, 1>(W, G, dst, K, N, T, s, st);
+            default: break;
+        }
+    }
+    return RETRO_E_VARIANT;
+}
+
+template <int TYPE>
+int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                   hipStream_t st) {
+    switch (variant) {
+        case RETRO_VARIANT_WS_128x128: return launch_mm<TYPE, 2, 2, 2>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_WS_64x128: return launch_mm<TYPE, 1, 2, 2>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_WS_32x128: return launch_mm<TYPE, 1, 1, 1>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_SIMPLE: {
+            const MmSimpleArgs a = mm_simple_args(TYPE, W, X, Y, K, N, T);
+            clear_last_error();
+            hipLaunchKernelGGL((mul_mat_simple_kernel<TYPE>), dim3(unsigned(cdiv(T * N, 256))), dim3(256), 0, st,
+                               a);
+            return launch_status();
+        }
+        case RETRO_VARIANT_SKINNY: {
+            const MmSimpleArgs a = mm_simple_args(TYPE, W, X, Y, K, N, T);
+            clear_last_error();
+            hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE>), dim3(unsigned(cdiv(N, 16))), dim3(1024), 0, st, a);
+            return launch_status();
+        }
+        default: return RETRO_E_VARIANT;
+    }
+}
+
+template <int TYPE>
+int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t st) {
+    DequantArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.out = out;
+    a.K = int(K);
+    a.N = int(N);
+    a.pitch = row_bytes_of(TYPE, K);
+    a.wide = (K % 4 == 0) ? 1 : 0;
+    a.gpr = int(cdiv(K, 4));
+    a.groups = N * int64_t(a.gpr);
+    clear_last_error();
+    hipLaunchKernelGGL((dequant_kernel<TYPE>), dim3(unsigned(cdiv(a.groups, 256))), dim3(256), 0, st, a);
+    return launch_status();
+}
+
+template int launch_out_prod<RETRO_UNIT_TYPE>(int, const void*, const float*, float*, int64_t, int64_t, int64_t,
+                                              const Strides&, hipStream_t);
+template int launch_mul_mat<RETRO_UNIT_TYPE>(int, const void*, const float*, float*, int64_t, int64_t, int64_t,
+                                             hipStream_t);
+template int launch_dequant<RETRO_UNIT_TYPE>(const void*, float*, int64_t, int64_t, hipStream_t);
+
+}  // namespace host
+}  // namespace retro
