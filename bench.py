@@ -77,7 +77,7 @@ PROFILE_COMMANDS = {
                        "python3 bench.py --copy-probe-mib 1024",
 }
 KERNELS = {  # summary tag -> (kernel-name prefix in rocprofv3 output, workload, variant)
-    f"ws_{LARGE}": ("void retro::out_prod_ws_kernel<12, 2, 4, 2, 1>", LARGE, "ws_128x256"),
+    f"ws_{LARGE}": ("void retro::out_prod_ws_kernel<12, 2, 4, 2, 1, false>", LARGE, "ws_128x256"),
     f"skinny_{SKINNY}": ("void retro::out_prod_skinny_kernel<12, 16, true>", SKINNY, "skinny"),
 }
 LARGE_TAG, SKINNY_TAG = f"ws_{LARGE}", f"skinny_{SKINNY}"

@@ -181,9 +181,10 @@ const char *retro_strerror(int code);
  *   RETRO_VARIANT_WS_*      the same tiles computed by a workgroup whose
  *                           waves are split into MFMA (consumer) and load/
  *                           decode (producer) roles over double-buffered LDS;
- *                           needs G rows in 16-byte units (ldg % 4 == 0;
- *                           ldg = N when contiguous) and K % 4 == 0 for F32,
- *                           F16, BF16; the TILE_* kernel takes the others
+ *                           needs G rows (or, stored t-fastest, columns) in
+ *                           16-byte units (ldg % 4 == 0; ldg = N when
+ *                           contiguous) and K % 4 == 0 for F32, F16, BF16;
+ *                           the TILE_* kernel takes the others
  *   RETRO_VARIANT_SIMPLE    retro_mul_mat only: one thread per output, for
  *                           the shapes the tiled kernel refuses
  *   RETRO_VARIANT_WS2_64x128  WS_64x128 with two pipelines in one
@@ -279,6 +280,51 @@ int retro_out_prod_batched_variant(int variant, int type, const void *W, int64_t
                                    const float *G, int64_t ldg, int64_t sg2, int64_t sg3, float *dst, int64_t ldd,
                                    int64_t sd2, int64_t sd3, int64_t K, int64_t N, int64_t T, int64_t ne02,
                                    int64_t ne03, int64_t ne2, int64_t ne3, void *stream);
+
+/*
+ * The most general form: retro_out_prod_batched with G in either
+ * orientation. Element G[t][n] of matrix (i2, i3) is the float at
+ *
+ *     G + i2 * sg2 + i3 * sg3 + t * sgt + n * sgn
+ *
+ * with one of the two element strides equal to 1:
+ *   sgn == 1           G rows contiguous (the gradient as ggml's mul_mat
+ *                      writes it, which out_prod reads through grad^T, a
+ *                      transposed view - llama.cpp PR #3 "cuda: out_prod
+ *                      accepts a quantized src0", commit message); sgt >= N.
+ *                      This is retro_out_prod_batched with ldg = sgt.
+ *   sgt == 1, sgn > 1  G stored t-fastest (a contiguous src1 of ggml's
+ *                      OUT_PROD: each of the N columns of G holds its T
+ *                      values side by side); sgn >= T.
+ * Anything else is RETRO_E_SHAPE. A stride of a dimension of size 1 is never
+ * used: pass a value that satisfies the rule (for T = 1 with contiguous rows,
+ * sgt = N). The producer/consumer kernels (RETRO_VARIANT_WS*) need sgt (rows)
+ * or sgn (t-fastest) to be a multiple of 4; the single-role tile kernels and
+ * the skinny kernel take any stride. All other arguments, limits and errors
+ * as retro_out_prod_batched; RETRO_E_ALIAS compares the span from G's first
+ * to its last element ((N - 1) * sgn + T floats per matrix when t-fastest).
+ */
+int retro_out_prod_views(int type, const void *W, int64_t ldw, int64_t sw2, int64_t sw3, const float *G, int64_t sgt,
+                         int64_t sgn, int64_t sg2, int64_t sg3, float *dst, int64_t ldd, int64_t sd2, int64_t sd3,
+                         int64_t K, int64_t N, int64_t T, int64_t ne02, int64_t ne03, int64_t ne2, int64_t ne3,
+                         void *stream);
+
+/* retro_out_prod_views with a forced kernel variant (RETRO_E_VARIANT when it
+ * does not apply to one matrix). */
+int retro_out_prod_views_variant(int variant, int type, const void *W, int64_t ldw, int64_t sw2, int64_t sw3,
+                                 const float *G, int64_t sgt, int64_t sgn, int64_t sg2, int64_t sg3, float *dst,
+                                 int64_t ldd, int64_t sd2, int64_t sd3, int64_t K, int64_t N, int64_t T, int64_t ne02,
+                                 int64_t ne03, int64_t ne2, int64_t ne3, void *stream);
+
+/* 1 if retro_out_prod_views_variant(variant, ...) with these strides and valid
+ * buffers would run, 0 otherwise. Touches no device. */
+int retro_out_prod_views_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, int64_t ldw,
+                                         int64_t sgt, int64_t sgn, int64_t ldd);
+
+/* The variant retro_out_prod_views would run for ne2 x ne3 matrices of this
+ * type, shape and strides, or a negative error code. Touches no device. */
+int retro_out_prod_views_choice(int type, int64_t K, int64_t N, int64_t T, int64_t ldw, int64_t sgt, int64_t sgn,
+                                int64_t ldd, int64_t ne2, int64_t ne3);
 
 /* The variant retro_out_prod would run for this type and shape, or a
  * negative error code (as retro_out_prod_supported would refuse). Touches no

@@ -62,6 +62,8 @@ LIB_PATH = _build.LIB_PATH
 EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided", "retro_out_prod_strided_variant",
            "retro_dequantize", "retro_out_prod_supported", "retro_out_prod_choice", "retro_out_prod_variant_applies",
            "retro_out_prod_strided_variant_applies", "retro_out_prod_batched", "retro_out_prod_batched_variant",
+           "retro_out_prod_views", "retro_out_prod_views_variant", "retro_out_prod_views_variant_applies",
+           "retro_out_prod_views_choice",
            "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
            "retro_row_bytes", "retro_strerror")
 
@@ -87,6 +89,16 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod_batched_variant.restype = i32
     lib.retro_out_prod_batched_variant.argtypes = [i32, i32, vp, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64,
                                                    i64, i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.retro_out_prod_views.restype = i32
+    lib.retro_out_prod_views.argtypes = [i32, vp, i64, i64, i64, vp, i64, i64, i64, i64, vp, i64, i64, i64,
+                                         i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.retro_out_prod_views_variant.restype = i32
+    lib.retro_out_prod_views_variant.argtypes = [i32, i32, vp, i64, i64, i64, vp, i64, i64, i64, i64, vp, i64, i64,
+                                                 i64, i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.retro_out_prod_views_variant_applies.restype = i32
+    lib.retro_out_prod_views_variant_applies.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, i64]
+    lib.retro_out_prod_views_choice.restype = i32
+    lib.retro_out_prod_views_choice.argtypes = [i32, i64, i64, i64, i64, i64, i64, i64, i64, i64]
     lib.retro_mul_mat.restype = i32
     lib.retro_mul_mat.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp]
     lib.retro_mul_mat_variant.restype = i32
@@ -174,10 +186,12 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
     """dst = out_prod(W, G): W packed bytes (N rows), G float32 T x N, dst float32 T x K.
 
     W is a contiguous device tensor of N * row_bytes(wtype, K) bytes, or a
-    2-D uint8 view of N rows whose first row_bytes bytes hold a W row; G and
-    out are 2-D float32 views whose rows are contiguous (their row strides
-    may exceed N and K). Runs asynchronously on `stream` (default: torch's
-    current stream).
+    2-D uint8 view of N rows whose first row_bytes bytes hold a W row; out is
+    a 2-D float32 view whose rows are contiguous (its row stride may exceed
+    K); G is a 2-D float32 view whose rows are contiguous, or whose columns
+    are (G stored t-fastest, such as the transpose of a contiguous N x T
+    tensor). Runs asynchronously on `stream` (default: torch's current
+    stream).
     """
     _device_tensor(W, "W", contiguous=False)
     _device_tensor(G, "G", contiguous=False)
@@ -195,7 +209,7 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
         if W.dtype != torch.uint8 or W.shape[0] != N or W.shape[1] < rb:
             raise ValueError(f"a strided W must be a uint8 view of N rows of at least {rb} bytes")
         ldw = _row_stride(W, "W")
-    ldg = _row_stride(G, "G")
+    sgt, sgn = _g_strides(G.unsqueeze(0).unsqueeze(0))
     if out is None:
         out = torch.empty((T, K), dtype=torch.float32, device=G.device)
     else:
@@ -203,12 +217,16 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
         if out.dtype != torch.float32 or tuple(out.shape) != (T, K):
             raise ValueError("out must be float32 T x K")
     ldd = _row_stride(out, "out")
-    if (ldw, ldg, ldd) == (rb, N, K):
+    if (ldw, sgt, sgn, ldd) == (rb, N, 1, K):
         _check(lib.retro_out_prod_variant(int(variant), int(wtype), _ptr(W), _ptr(G), _ptr(out), int(K), int(N),
                                           int(T), _stream_handle(stream)))
-    else:
-        _check(lib.retro_out_prod_strided_variant(int(variant), int(wtype), _ptr(W), ldw, _ptr(G), ldg, _ptr(out),
+    elif sgn == 1:
+        _check(lib.retro_out_prod_strided_variant(int(variant), int(wtype), _ptr(W), ldw, _ptr(G), sgt, _ptr(out),
                                                   ldd, int(K), int(N), int(T), _stream_handle(stream)))
+    else:
+        _check(lib.retro_out_prod_views_variant(int(variant), int(wtype), _ptr(W), ldw, 0, 0, _ptr(G), sgt, sgn, 0,
+                                                0, _ptr(out), ldd, 0, 0, int(K), int(N), int(T), 1, 1, 1, 1,
+                                                _stream_handle(stream)))
     return out
 
 
@@ -228,12 +246,26 @@ def _matrix_strides(t, rows, name):
     return ld, (int(t.stride(1)) if t.shape[1] > 1 else 0), (int(t.stride(0)) if t.shape[0] > 1 else 0)
 
 
+def _g_strides(G4):
+    """(sgt, sgn): element strides of the T x N matrices of a 4-D G view
+    whose rows or columns are contiguous. The stride of a dimension of size
+    1 is never used and is reported so that the layout rule holds."""
+    T, N = int(G4.shape[2]), int(G4.shape[3])
+    st, sn = int(G4.stride(2)), int(G4.stride(3))
+    if N <= 1 or sn == 1:
+        return (st if T > 1 else max(N, 1)), 1
+    if T <= 1 or st == 1:
+        return 1, sn
+    raise ValueError("G must have contiguous rows or contiguous columns")
+
+
 def out_prod_batched(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, stream=None):
     """Batched out_prod over two outer dimensions with W broadcast (see
     retro_out_prod_batched): W uint8 [ne03, ne02, N, >= row_bytes],
     G float32 [ne3, ne2, T, N], out float32 [ne3, ne2, T, K] (leading
     dimensions may be left out; ne03 divides ne3 and ne02 divides ne2).
-    Rows are contiguous; rows and matrices may be any distance apart."""
+    Rows of W and out are contiguous; G's rows or its columns are (see
+    out_prod); rows and matrices may be any distance apart."""
     _device_tensor(W, "W", contiguous=False)
     _device_tensor(G, "G", contiguous=False)
     if G.dtype != torch.float32 or not 2 <= G.dim() <= 4 or W.dtype != torch.uint8 or not 2 <= W.dim() <= 4:
@@ -254,17 +286,31 @@ def out_prod_batched(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_
             raise ValueError("out must be float32 with G's leading dimensions and T x K matrices")
     D4 = _as4(out)
     ldw, sw2, sw3 = _matrix_strides(W4, rb, "W")
-    ldg, sg2, sg3 = _matrix_strides(G4, N, "G")
+    sgt, sgn = _g_strides(G4)
+    sg2 = int(G4.stride(1)) if G4.shape[1] > 1 else 0
+    sg3 = int(G4.stride(0)) if G4.shape[0] > 1 else 0
     ldd, sd2, sd3 = _matrix_strides(D4, K, "out")
-    _check(lib.retro_out_prod_batched_variant(int(variant), int(wtype), _ptr(W), ldw, sw2, sw3, _ptr(G), ldg, sg2,
-                                              sg3, _ptr(out), ldd, sd2, sd3, int(K), int(N), int(T), int(ne02),
-                                              int(ne03), int(ne2), int(ne3), _stream_handle(stream)))
+    _check(lib.retro_out_prod_views_variant(int(variant), int(wtype), _ptr(W), ldw, sw2, sw3, _ptr(G), sgt, sgn, sg2,
+                                            sg3, _ptr(out), ldd, sd2, sd3, int(K), int(N), int(T), int(ne02),
+                                            int(ne03), int(ne2), int(ne3), _stream_handle(stream)))
     return out
 
 
 def variant_applies_strided(variant: int, wtype: int, K: int, N: int, T: int, ldw: int, ldg: int, ldd: int) -> bool:
     return lib.retro_out_prod_strided_variant_applies(int(variant), int(wtype), int(K), int(N), int(T), int(ldw),
                                                       int(ldg), int(ldd)) == 1
+
+
+def variant_applies_views(variant: int, wtype: int, K: int, N: int, T: int, ldw: int, sgt: int, sgn: int,
+                          ldd: int) -> bool:
+    return lib.retro_out_prod_views_variant_applies(int(variant), int(wtype), int(K), int(N), int(T), int(ldw),
+                                                    int(sgt), int(sgn), int(ldd)) == 1
+
+
+def choice_views(wtype: int, K: int, N: int, T: int, ldw: int, sgt: int, sgn: int, ldd: int, ne2: int = 1,
+                 ne3: int = 1) -> int:
+    return int(lib.retro_out_prod_views_choice(int(wtype), int(K), int(N), int(T), int(ldw), int(sgt), int(sgn),
+                                               int(ldd), int(ne2), int(ne3)))
 
 
 def mul_mat(wtype: int, W, X, N: int | None = None, out=None, variant: int = VARIANT_AUTO, stream=None):

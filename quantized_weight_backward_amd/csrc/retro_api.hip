@@ -49,8 +49,10 @@ int64_t block_alignment(int type) {
 }
 
 int check_strides(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    if (s.ldw < row_bytes_of(type, K) || s.ldg < N || s.ldd < K) return RETRO_E_SHAPE;
-    if (!product_below(N, s.ldw, kByteLimit) || !product_below(T, s.ldg, kCountLimit) ||
+    // G rows (or, stored t-fastest, columns) no shorter than they are long
+    const int64_t g_len = s.gcols ? T : N, g_count = s.gcols ? N : T;
+    if (s.ldw < row_bytes_of(type, K) || s.ldg < g_len || s.ldd < K) return RETRO_E_SHAPE;
+    if (!product_below(N, s.ldw, kByteLimit) || !product_below(g_count, s.ldg, kCountLimit) ||
         !product_below(T, s.ldd, kCountLimit))
         return RETRO_E_SHAPE;
     // every row starts as aligned as a block of a contiguous row
@@ -106,8 +108,9 @@ const TileVariant* find_tile(int variant) {
     return nullptr;
 }
 
-// The tiled kernel addresses a tile's BT rows of G and a chunk's 32 rows of
-// W with 32-bit offsets from per-chunk buffer bases.
+// The tiled kernel addresses a tile's BT rows of G (with G stored t-fastest:
+// a chunk's 32 columns) and a chunk's 32 rows of W with 32-bit offsets from
+// per-chunk buffer bases.
 bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     Geometry geo;
     if (geometry(type, geo) && geo.block == 256 && v.bk % 256) return false;
@@ -116,12 +119,14 @@ bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t 
     if (v.ws && (s.ldg % 4 || (is_dense(type) && K % 4))) return false;
     // chunk offsets run up to a few hundred rows past N in 32-bit arithmetic
     if (N >= kDimLimit - 4096) return false;
-    return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit && int64_t(v.bt) * s.ldg * 4 < (int64_t(1) << 31) &&
+    const int64_t g_span = s.gcols ? 32 * s.ldg + v.bt : int64_t(v.bt) * s.ldg;
+    return cdiv(T, v.bt) * cdiv(K, v.bk) < kGridLimit && g_span * 4 < (int64_t(1) << 31) &&
            33 * s.ldw < (int64_t(1) << 31);
 }
 
 // The skinny kernel addresses one 16-row group of W, and the 16 rows of G
-// it reads, through buffer descriptors whose sizes are signed 32-bit.
+// it reads (16 columns, when G is stored t-fastest: at most 16 ldg floats),
+// through buffer descriptors whose sizes are signed 32-bit.
 bool skinny_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     (void)type;
     (void)N;
@@ -173,6 +178,23 @@ bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, con
     return tv && tile_applies(*tv, type, K, N, T, s);
 }
 
+// G's layout from its two element strides: G[t][n] at t * sgt + n * sgn,
+// with one of them 1 (rows contiguous: sgn = 1; columns contiguous, G stored
+// t-fastest: sgt = 1, sgn > 1).
+bool g_layout(int64_t sgt, int64_t sgn, Strides& s) {
+    if (sgn == 1) {
+        s.ldg = sgt;
+        s.gcols = false;
+        return true;
+    }
+    if (sgt == 1) {
+        s.ldg = sgn;
+        s.gcols = true;
+        return true;
+    }
+    return false;
+}
+
 int out_prod_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
                   int64_t T, const Strides& s, void* stream) {
     int rc = check_shape(type, K, N, T);
@@ -182,7 +204,7 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
     if (T == 0 || K == 0 || s.batches() == 0) return RETRO_OK;
     // bytes each operand spans: one matrix, then all batches
     const int64_t w_bytes = N > 0 ? (N - 1) * s.ldw + row_bytes_of(type, K) : 0;
-    const int64_t g_bytes = N > 0 ? ((T - 1) * s.ldg + N) * 4 : 0;
+    const int64_t g_bytes = N > 0 ? (s.gcols ? (N - 1) * s.ldg + T : (T - 1) * s.ldg + N) * 4 : 0;
     const int64_t d_bytes = ((T - 1) * s.ldd + K) * 4;
     const int64_t w_all = N > 0 ? (s.ne03 - 1) * s.sw3 + (s.ne02 - 1) * s.sw2 + w_bytes : 0;
     const int64_t g_all = N > 0 ? ((s.ne3 - 1) * s.sg3 + (s.ne2 - 1) * s.sg2) * 4 + g_bytes : 0;
@@ -354,11 +376,12 @@ int retro_out_prod_strided_variant(int variant, int type, const void* W, int64_t
     return out_prod_impl(variant, type, W, G, dst, K, N, T, Strides{ldw, ldg, ldd}, stream);
 }
 
-int retro_out_prod_batched_variant(int variant, int type, const void* W, int64_t ldw, int64_t sw2, int64_t sw3,
-                                   const float* G, int64_t ldg, int64_t sg2, int64_t sg3, float* dst, int64_t ldd,
-                                   int64_t sd2, int64_t sd3, int64_t K, int64_t N, int64_t T, int64_t ne02,
-                                   int64_t ne03, int64_t ne2, int64_t ne3, void* stream) {
-    Strides s{ldw, ldg, ldd};
+int retro_out_prod_views_variant(int variant, int type, const void* W, int64_t ldw, int64_t sw2, int64_t sw3,
+                                 const float* G, int64_t sgt, int64_t sgn, int64_t sg2, int64_t sg3, float* dst,
+                                 int64_t ldd, int64_t sd2, int64_t sd3, int64_t K, int64_t N, int64_t T, int64_t ne02,
+                                 int64_t ne03, int64_t ne2, int64_t ne3, void* stream) {
+    Strides s{ldw, 0, ldd};
+    if (!g_layout(sgt, sgn, s)) return RETRO_E_SHAPE;
     s.ne02 = ne02;
     s.ne03 = ne03;
     s.ne2 = ne2;
@@ -370,6 +393,22 @@ int retro_out_prod_batched_variant(int variant, int type, const void* W, int64_t
     s.sd2 = sd2;
     s.sd3 = sd3;
     return out_prod_impl(variant, type, W, G, dst, K, N, T, s, stream);
+}
+
+int retro_out_prod_views(int type, const void* W, int64_t ldw, int64_t sw2, int64_t sw3, const float* G, int64_t sgt,
+                         int64_t sgn, int64_t sg2, int64_t sg3, float* dst, int64_t ldd, int64_t sd2, int64_t sd3,
+                         int64_t K, int64_t N, int64_t T, int64_t ne02, int64_t ne03, int64_t ne2, int64_t ne3,
+                         void* stream) {
+    return retro_out_prod_views_variant(RETRO_VARIANT_AUTO, type, W, ldw, sw2, sw3, G, sgt, sgn, sg2, sg3, dst, ldd,
+                                        sd2, sd3, K, N, T, ne02, ne03, ne2, ne3, stream);
+}
+
+int retro_out_prod_batched_variant(int variant, int type, const void* W, int64_t ldw, int64_t sw2, int64_t sw3,
+                                   const float* G, int64_t ldg, int64_t sg2, int64_t sg3, float* dst, int64_t ldd,
+                                   int64_t sd2, int64_t sd3, int64_t K, int64_t N, int64_t T, int64_t ne02,
+                                   int64_t ne03, int64_t ne2, int64_t ne3, void* stream) {
+    return retro_out_prod_views_variant(variant, type, W, ldw, sw2, sw3, G, ldg, 1, sg2, sg3, dst, ldd, sd2, sd3, K,
+                                        N, T, ne02, ne03, ne2, ne3, stream);
 }
 
 int retro_out_prod_batched(int type, const void* W, int64_t ldw, int64_t sw2, int64_t sw3, const float* G,
@@ -426,6 +465,27 @@ int retro_out_prod_strided_variant_applies(int variant, int type, int64_t K, int
     if (check_strides(type, K, N, T, s) != RETRO_OK) return 0;
     if (T == 0 || K == 0) return 1;
     return variant_applies(variant, type, K, N, T, s) ? 1 : 0;
+}
+
+int retro_out_prod_views_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, int64_t ldw,
+                                         int64_t sgt, int64_t sgn, int64_t ldd) {
+    if (check_shape(type, K, N, T) != RETRO_OK) return 0;
+    Strides s{ldw, 0, ldd};
+    if (!g_layout(sgt, sgn, s) || check_strides(type, K, N, T, s) != RETRO_OK) return 0;
+    if (T == 0 || K == 0) return 1;
+    return variant_applies(variant, type, K, N, T, s) ? 1 : 0;
+}
+
+int retro_out_prod_views_choice(int type, int64_t K, int64_t N, int64_t T, int64_t ldw, int64_t sgt, int64_t sgn,
+                                int64_t ldd, int64_t ne2, int64_t ne3) {
+    int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    Strides s{ldw, 0, ldd};
+    if (!g_layout(sgt, sgn, s)) return RETRO_E_SHAPE;
+    s.ne2 = ne2;
+    s.ne3 = ne3;
+    rc = check_strides(type, K, N, T, s);
+    return rc != RETRO_OK ? rc : choose(type, K, N, T, s);
 }
 
 int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T) {

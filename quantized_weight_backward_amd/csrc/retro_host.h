@@ -56,8 +56,9 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ne2 / ne02 x ne3 / ne03 consecutive batches).
 struct Strides {
     int64_t ldw;  // bytes between consecutive W rows (>= the row's bytes)
-    int64_t ldg;  // floats between consecutive G rows (>= N)
+    int64_t ldg;  // G[t][n] at float t * ldg + n (ldg >= N), or n * ldg + t when gcols (ldg >= T)
     int64_t ldd;  // floats between consecutive dst rows (>= K)
+    bool gcols = false;  // G stored t-fastest: its columns are contiguous
     int64_t ne02 = 1, ne03 = 1, ne2 = 1, ne3 = 1;
     int64_t sw2 = 0, sw3 = 0;  // bytes between W matrices
     int64_t sg2 = 0, sg3 = 0;  // floats between G matrices

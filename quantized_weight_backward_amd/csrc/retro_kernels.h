@@ -108,10 +108,11 @@ struct TileArgs {
     int K, N, T;
     long long pitch;  // bytes between consecutive W rows
     int wvec;         // W staging load width (16, 8, 4, 2)
-    int gvec;         // 1: G rows take float4 loads (N % 4 == 0)
+    int gvec;         // 1: G rows take float4 loads (ldg % 4 == 0, not gcols)
+    int gcols;        // 1: G is stored t-fastest (the columns of G are contiguous)
     int tiles_t, tiles_k;
     int group;        // row tiles per group of the tile order (tile_coords)
-    long long ldg;    // floats between consecutive G rows (>= N)
+    long long ldg;    // G[t][n] at t * ldg + n (ldg >= N), or at n * ldg + t when gcols (ldg >= T)
     long long ldd;    // floats between consecutive dst rows (>= K)
     BatchArgs batch;
 };
@@ -193,13 +194,15 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 
     // Byte offsets of this thread's staging loads from the chunk's buffer
     // bases (the same for every chunk and tile): G slot s covers tile row
-    // r = id / 8, columns 4*(id % 8) .. +3 of the chunk; W slot s covers
-    // 16-byte unit u of tile row r.
+    // r = id / 8, columns 4*(id % 8) .. +3 of the chunk (the four elements
+    // gstep bytes apart); W slot s covers 16-byte unit u of tile row r.
     uint32_t goff[S::GSLOTS], woff[S::WSLOTS];
+    const uint32_t gstep = args.gcols ? uint32_t(4 * args.ldg) : 4u;
 #pragma unroll
     for (int s = 0; s < S::GSLOTS; ++s) {
         const int id = tid + S::kThreads * s;
-        goff[s] = uint32_t(((id >> 3) * args.ldg + 4 * (id & 7)) * 4);
+        const long long r = id >> 3, c = 4 * (id & 7);
+        goff[s] = uint32_t((args.gcols ? c * args.ldg + r : r * args.ldg + c) * 4);
     }
 #pragma unroll
     for (int s = 0; s < S::WSLOTS; ++s) {
@@ -207,20 +210,23 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
         const int r = id / S::UPR, u = id - r * S::UPR;
         woff[s] = uint32_t(r * args.pitch + 16 * u);
     }
-    const long long g_end = (long long)(T - 1) * args.ldg + N;  // elements spanned by G
+    // elements spanned by G
+    const long long g_end = args.gcols ? (long long)(N - 1) * args.ldg + T : (long long)(T - 1) * args.ldg + N;
     // bytes spanned by W: rows are `pitch` apart, the last one ends after
     // its K / block blocks
     const long long w_end = N > 0 ? (long long)(N - 1) * args.pitch + (long long)(K / F::kBlock) * F::kBytes : 0;
 
     // Global -> registers for the chunk of W rows [n0, n0 + 32). Both loads go
-    // through buffer descriptors based at the chunk's first element, so rows
-    // past the end of G (t >= T) and of W (n >= N) read as zero in hardware.
+    // through buffer descriptors based at the chunk's first element, so what
+    // lies past the end of G and of W (n >= N) reads as zero in hardware.
     // Bytes of a row past this tile's K range belong to the next row: they
-    // only feed dst columns >= K, which are never stored. G columns >= N
-    // (possible only in the last chunk) are zeroed explicitly.
+    // only feed dst columns >= K, which are never stored; G rows t >= T (other
+    // values when G is stored t-fastest) only feed dst rows that are never
+    // stored. G columns >= N (possible only in the last chunk) are zeroed
+    // explicitly.
     auto load_chunk = [&](int n0) {
         n0 = __builtin_amdgcn_readfirstlane(n0);
-        const long long gb = (long long)t0 * args.ldg + n0;
+        const long long gb = args.gcols ? (long long)n0 * args.ldg + t0 : (long long)t0 * args.ldg + n0;
         const __amdgpu_buffer_rsrc_t gr =
             buffer_rsrc(args.G + gb, uint32_t(max(0ll, min(4 * (g_end - gb), (long long)0x7FFFFFFF))));
 #pragma unroll
@@ -231,9 +237,9 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                                       __uint_as_float(v.w));
             } else {
                 greg[s].x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s], 0, 0));
-                greg[s].y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 4, 0, 0));
-                greg[s].z = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 8, 0, 0));
-                greg[s].w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 12, 0, 0));
+                greg[s].y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + gstep, 0, 0));
+                greg[s].z = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 2 * gstep, 0, 0));
+                greg[s].w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, goff[s] + 3 * gstep, 0, 0));
             }
         }
         if (n0 + BN > N) {
@@ -575,10 +581,11 @@ struct SkinnyArgs {
     float* dst;
     int K, N, T;
     long long pitch;  // bytes between consecutive W rows
-    long long ldg;    // floats between consecutive G rows (>= N)
+    long long ldg;    // G[t][n] at t * ldg + n (ldg >= N), or at n * ldg + t when gcols (ldg >= T)
     long long ldd;    // floats between consecutive dst rows (>= K)
-    int wide;  // 1: W rows allow the widest load of 4 consecutive elements
-    int gvec;  // 1: G rows take float4 loads
+    int wide;   // 1: W rows allow the widest load of 4 consecutive elements
+    int gvec;   // 1: the fast path's G loads are aligned (G rows take float4 loads, or gcols)
+    int gcols;  // 1: G is stored t-fastest (the columns of G are contiguous)
     BatchArgs batch;
 };
 
@@ -717,12 +724,13 @@ struct SkinnyOffsets {
     uint32_t code2[4];  // Q5_K fifth bits / Q6_K high parts of the same elements
     uint32_t hdr;       // header of the scale pair this lane decodes (Q6_K, Q2_K, Q3_K: see skinny_offsets)
     uint32_t hdr2;      // Q6_K, Q2_K: the scales of that row
-    uint32_t g;         // G[min(l%16, T-1)][4*(l/16)] (bytes from G + n0)
+    uint32_t g;         // G[min(l%16, T-1)][n0 + 4*(l/16)] (bytes from G[0][n0])
 };
 
-// Fast path (K % 4 == 0, N % 4 == 0, whole group inside W). Columns at or
-// beyond K and rows of G at or beyond T are clamped to valid addresses: they
-// only feed dst columns and rows that are never stored.
+// Fast path (K % 4 == 0, G rows 16-byte aligned or G stored t-fastest,
+// whole group inside W). Columns at or beyond K and rows of G at or beyond T
+// are clamped to valid addresses: they only feed dst columns and rows that
+// are never stored.
 template <int TYPE>
 __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int k0, int lane) {
     const int j = lane & 15, rq = lane >> 4;
@@ -788,7 +796,8 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
             o.hdr = rowb + 96;
         }
     }
-    o.g = uint32_t(((long long)min(j, a.T - 1) * a.ldg + 4 * rq) * 4);
+    const long long gt = min(j, a.T - 1);
+    o.g = uint32_t((a.gcols ? 4 * rq * a.ldg + gt : gt * a.ldg + 4 * rq) * 4);
     return o;
 }
 
@@ -801,10 +810,21 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
     // per-lane offset from them.
     n0 = __builtin_amdgcn_readfirstlane(n0);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.W + (long long)n0 * a.pitch, uint32_t(16 * a.pitch));
-    const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(a.G + n0, uint32_t(4 * ((long long)(a.T - 1) * a.ldg + 16)));
-    const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(gr, o.g, 0, 0);
+    if (a.gcols) {
+        // G[t][n0 + 4(l/16) + q]: four words ldg apart (the 16 columns n0 ..
+        // n0 + 15 span 15 ldg + T floats)
+        const __amdgpu_buffer_rsrc_t gr =
+            buffer_rsrc(a.G + (long long)n0 * a.ldg, uint32_t(4 * (15 * a.ldg + a.T)));
+        const uint32_t step = uint32_t(4 * a.ldg);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r.g[q] = __uint_as_float(gv[q]);
+        for (int q = 0; q < 4; ++q)
+            r.g[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, o.g + q * step, 0, 0));
+    } else {
+        const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(a.G + n0, uint32_t(4 * ((long long)(a.T - 1) * a.ldg + 16)));
+        const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(gr, o.g, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.g[q] = __uint_as_float(gv[q]);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         if constexpr (TYPE == kF32) {
@@ -869,10 +889,12 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
 #pragma unroll
     for (int s = 0; s < 4; ++s) r.g[s] = 0.f;
     if (j < a.T) {
-        const float* gp = a.G + (long long)j * a.ldg + nq;
+        // G[j][nq + s]
+        const long long gs = a.gcols ? a.ldg : 1;
+        const float* gp = a.G + (a.gcols ? (long long)nq * a.ldg + j : (long long)j * a.ldg + nq);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            if (nq + s < N) r.g[s] = gp[s];
+            if (nq + s < N) r.g[s] = gp[s * gs];
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {

@@ -68,7 +68,8 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     int wvec = 16;
     while (wvec > 1 && ((a.pitch % wvec) != 0 || (S::SPAN % wvec) != 0 || (rbytes % wvec) != 0)) wvec >>= 1;
     a.wvec = wvec;
-    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
+    a.gvec = (!s.gcols && s.ldg % 4 == 0) ? 1 : 0;
+    a.gcols = s.gcols ? 1 : 0;
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
     a.group = group_height(a.tiles_t, a.tiles_k, 2, 4.0 * T * N, double(N) * rbytes);
@@ -96,14 +97,18 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
     a.ldd = s.ldd;
     a.wvec = 16;
     a.gvec = 1;
+    a.gcols = s.gcols ? 1 : 0;  // the kernel takes the layout as a template argument
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_k = int(cdiv(K, S::BK));
     a.group = group_height(a.tiles_t, a.tiles_k, S::kResident, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
     a.batch = batch_args(s);
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
     clear_last_error();
-    hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG>), dim3(nt, unsigned(s.batches())),
-                       dim3(S::kThreads), 0, st, a);
+    const dim3 grid(nt, unsigned(s.batches()));
+    if (s.gcols)
+        hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG, true>), grid, dim3(S::kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG, false>), grid, dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
 
@@ -122,7 +127,8 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     a.ldg = s.ldg;
     a.ldd = s.ldd;
     a.wide = (K % 4 == 0) ? 1 : 0;
-    a.gvec = (s.ldg % 4 == 0) ? 1 : 0;
+    a.gvec = (s.gcols || s.ldg % 4 == 0) ? 1 : 0;
+    a.gcols = s.gcols ? 1 : 0;
     a.batch = batch_args(s);
     const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches())), block(kWaves * 64);
     clear_last_error();

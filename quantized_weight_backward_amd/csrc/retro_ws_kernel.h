@@ -224,7 +224,9 @@ __device__ __forceinline__ void ws_consume(float* lds_all, int tid, int wave, in
         }
 }
 
-template <int TYPE, int WA, int WB, int CT, int NG>
+// GCOLS: G stored t-fastest (args.ldg floats between its columns); the
+// consumers see the same LDS contents either way.
+template <int TYPE, int WA, int WB, int CT, int NG, bool GCOLS>
 __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)) void out_prod_ws_kernel(
     TileArgs args) {
     using S = WsShape<TYPE, WA, WB, CT, NG>;
@@ -260,12 +262,18 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
         uint32_t wring[R][S::WWORDS];
         // Byte offsets of this thread's G loads from the chunk's base (the
         // same for every chunk): slot s is t row id / 8, columns
-        // 4 (id % 8) .. + 3.
+        // 4 (id % 8) .. + 3. With G stored t-fastest the thread holds a block
+        // of GSLOTS columns by 4 t rows instead: slot s is column
+        // GSLOTS (p % CG) + s, t rows 4 (p / CG) .. + 3 (CG = 32 / GSLOTS
+        // column groups), so that each t row of the block is one LDS store.
+        constexpr int CG = BN / S::GSLOTS;
+        static_assert(CG * (BT / 4) == S::kPThreads, "column blocks cover the G chunk");
         uint32_t goff[S::GSLOTS];
 #pragma unroll
         for (int s = 0; s < S::GSLOTS; ++s) {
             const int id = p + S::kPThreads * s;
-            goff[s] = uint32_t(((id >> 3) * args.ldg + 4 * (id & 7)) * 4);
+            goff[s] = GCOLS ? uint32_t(((S::GSLOTS * (p % CG) + s) * args.ldg + 4 * (p / CG)) * 4)
+                            : uint32_t(((id >> 3) * args.ldg + 4 * (id & 7)) * 4);
         }
         // W: byte offset of this thread's block in the chunk, and the LDS
         // float index of the first element it writes in each 16-column group.
@@ -307,7 +315,9 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
                 wlds[1] = ws_w_index<WP>(32 * b + 16, r) + S::CB * s * WP;
             }
         }
-        const long long g_end = (long long)(T - 1) * args.ldg + N;  // elements spanned by G
+        // elements spanned by G
+        const long long g_end =
+            GCOLS ? (long long)(N - 1) * args.ldg + T : (long long)(T - 1) * args.ldg + N;
         // bytes spanned by W: rows are `pitch` apart, the last one ends after
         // its K / block blocks
         const long long w_end =
@@ -320,13 +330,14 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
         // chunk past the last one reads zeros or rows it never uses. G columns
         // at or past N in the last chunk (the next t row's values) are zeroed
         // when the chunk is written to LDS. Columns past K in the last k tile
-        // read bytes of the next row (or zero) and only reach outputs that are
-        // not stored. G rows are 16-byte aligned (ldg % 4 == 0).
+        // read bytes of the next row (or zero), and G rows past T (other values
+        // when G is stored t-fastest) are read too: both only reach outputs
+        // that are not stored. ldg % 4 == 0, so the G loads are 16-byte aligned.
         auto load_chunk = [&](auto slot, int n0) {
             float4(&greg)[S::GSLOTS] = gring[decltype(slot)::value];
             uint32_t(&wreg)[S::WWORDS] = wring[decltype(slot)::value];
             n0 = __builtin_amdgcn_readfirstlane(n0);
-            const long long gb = (long long)t0 * args.ldg + n0;
+            const long long gb = GCOLS ? (long long)n0 * args.ldg + t0 : (long long)t0 * args.ldg + n0;
             const __amdgpu_buffer_rsrc_t gr =
                 buffer_rsrc(args.G + gb, uint32_t(max(0ll, min(4 * (g_end - gb), (long long)0x7FFFFFFF))));
 #pragma unroll
@@ -441,20 +452,45 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
             const uint32_t(&wreg)[S::WWORDS] = wring[decltype(slot)::value];
             float* gs = lds + decltype(buf)::value * S::BUF_FLOATS;
             float* ws = gs + S::G_FLOATS;
-            if (n0 + BN > N) {
+            if constexpr (GCOLS) {
+                // the thread's block, transposed: t row j of it is element j
+                // of every slot, stored as one vector of GSLOTS columns
+                constexpr int GS = S::GSLOTS;
+                const int c0 = GS * (p % CG);
+                if (n0 + BN > N) {
+#pragma unroll
+                    for (int s = 0; s < GS; ++s)
+                        if (n0 + c0 + s >= N) greg[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                auto elem = [](const float4& v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; };
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float* row = gs + (4 * (p / CG) + j) * GP + c0;
+                    if constexpr (GS == 4) {
+                        *reinterpret_cast<float4*>(row) =
+                            make_float4(elem(greg[0], j), elem(greg[1], j), elem(greg[2], j), elem(greg[3], j));
+                    } else if constexpr (GS == 2) {
+                        *reinterpret_cast<float2*>(row) = make_float2(elem(greg[0], j), elem(greg[1], j));
+                    } else {
+                        row[0] = elem(greg[0], j);
+                    }
+                }
+            } else {
+                if (n0 + BN > N) {
+#pragma unroll
+                    for (int s = 0; s < S::GSLOTS; ++s) {
+                        const int n = n0 + 4 * ((p + S::kPThreads * s) & 7);
+                        if (n >= N) greg[s].x = 0.f;
+                        if (n + 1 >= N) greg[s].y = 0.f;
+                        if (n + 2 >= N) greg[s].z = 0.f;
+                        if (n + 3 >= N) greg[s].w = 0.f;
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < S::GSLOTS; ++s) {
-                    const int n = n0 + 4 * ((p + S::kPThreads * s) & 7);
-                    if (n >= N) greg[s].x = 0.f;
-                    if (n + 1 >= N) greg[s].y = 0.f;
-                    if (n + 2 >= N) greg[s].z = 0.f;
-                    if (n + 3 >= N) greg[s].w = 0.f;
+                    const int id = p + S::kPThreads * s;
+                    *reinterpret_cast<float4*>(gs + (id >> 3) * GP + 4 * (id & 7)) = greg[s];
                 }
-            }
-#pragma unroll
-            for (int s = 0; s < S::GSLOTS; ++s) {
-                const int id = p + S::kPThreads * s;
-                *reinterpret_cast<float4*>(gs + (id >> 3) * GP + 4 * (id & 7)) = greg[s];
             }
             if constexpr (S::kDense) {
 #pragma unroll

@@ -177,6 +177,42 @@ def test_batched_validation():
     assert call(w=None) == q.E_NULL
 
 
+def test_views_validation_and_choice():
+    v = q.lib.retro_out_prod_views
+    # (type, W, ldw, sw2, sw3, G, sgt, sgn, sg2, sg3, dst, ldd, sd2, sd3, K, N, T, ne02, ne03, ne2, ne3, stream)
+    W, G, D = 0x100000, 0x200000, 0x300000
+
+    def call(sgt, sgn, K=8, N=6, T=5, g=G, d=D):
+        return v(q.F32, W, 4 * K, 0, 0, g, sgt, sgn, 0, 0, d, K, 0, 0, K, N, T, 1, 1, 1, 1, None)
+    assert call(6, 2) == q.E_SHAPE                       # neither stride is 1
+    assert call(5, 1) == q.E_SHAPE                       # rows shorter than N
+    assert call(1, 4) == q.E_SHAPE                       # columns shorter than T
+    assert call(1, 5, g=0x200004) == q.E_ALIGN
+    # G stored t-fastest spans (N - 1) * sgn + T floats: 4 * 30 = 120 bytes
+    assert call(1, 5, d=G + 112) == q.E_ALIAS
+
+    assert call(1, 5, d=G + 128, T=0) == q.OK              # no rows: a no-op
+    assert call(1, 5, g=None) == q.E_NULL
+    # the same contract through the query functions
+    assert q.variant_applies_views(q.VARIANT_WS_64x128, q.Q4_0, 512, 64, 100, 288, 1, 100, 512)
+    assert not q.variant_applies_views(q.VARIANT_WS_64x128, q.Q4_0, 512, 64, 100, 288, 1, 101, 512)
+    assert q.variant_applies_views(q.VARIANT_TILE_64x128, q.Q4_0, 512, 64, 100, 288, 1, 101, 512)
+    assert q.variant_applies_views(q.VARIANT_SKINNY, q.Q4_0, 512, 64, 16, 288, 1, 17, 512)
+    assert not q.variant_applies_views(q.VARIANT_SKINNY, q.Q4_0, 512, 64, 16, 288, 1, 15, 512)
+    # G stored t-fastest takes the same kernels as rows at the benchmarked shapes
+    rb = q.row_bytes(q.Q4_K, 4096)
+    assert q.choice_views(q.Q4_K, 4096, 14336, 4096, rb, 1, 4096, 4096) == q.choice(q.Q4_K, 4096, 14336, 4096)
+    assert q.choice_views(q.Q4_K, 14336, 4096, 16, q.row_bytes(q.Q4_K, 14336), 1, 16, 14336) == q.VARIANT_SKINNY
+    # a column stride off the 16-byte grid leaves the single-role tiles
+    assert q.choice_views(q.Q4_0, 4096, 4096, 1000, q.row_bytes(q.Q4_0, 4096), 1, 1001, 4096) in (
+        q.VARIANT_TILE_128x256, q.VARIANT_TILE_128x128, q.VARIANT_TILE_64x256, q.VARIANT_TILE_64x128,
+        q.VARIANT_TILE_64x64)
+    # rows: the strided entry point's rule
+    assert q.choice_views(q.Q4_0, 4096, 4096, 1000, q.row_bytes(q.Q4_0, 4096), 4096, 1, 4096) == q.choice(
+        q.Q4_0, 4096, 4096, 1000)
+    assert q.choice_views(q.Q4_0, 4096, 4096, 1000, q.row_bytes(q.Q4_0, 4096), 3, 3, 4096) == q.E_SHAPE
+
+
 def test_mul_mat_validation_and_choice():
     mm = q.lib.retro_mul_mat
     # (type, W, X, Y, K, N, T, stream)

@@ -361,6 +361,64 @@ def test_strided_operands_match_oracle(q, wtype, K, N, T, gpad, wpad):
         assert "tile" in families and (("ws" in families) == (ldg % 4 == 0)), ran
 
 
+# --- G stored t-fastest (its columns contiguous) -------------------------------------
+
+def g_columns(g, ldg):
+    """A T x N view of g whose columns are contiguous: the transpose of an
+    N x ldg buffer holding g^T in its first T columns and NaN after them."""
+    T, N = g.shape
+    big = torch.full((N, ldg), float("nan"), device="cuda")
+    big[:, :T] = dev(np.ascontiguousarray(g.T))
+    return big[:, :T].t()
+
+
+GCOLS = [(wl.Q4_K, 768, 96, 130), (wl.Q4_0, 512, 77, 200), (wl.F16, 264, 100, 150), (wl.F32, 301, 64, 70),
+         (wl.Q6_K, 512, 60, 70), (wl.Q8_0, 416, 33, 16), (wl.Q2_K, 256, 40, 9), (wl.Q5_1, 256, 44, 12),
+         (wl.MXFP4, 352, 40, 70), (wl.Q3_K, 512, 35, 100), (wl.BF16, 520, 50, 5), (wl.Q5_K, 256, 37, 67),
+         (wl.Q4_1, 192, 64, 33), (wl.Q5_0, 352, 29, 16)]
+
+
+@pytest.mark.parametrize("wtype,K,N,T", GCOLS)
+@pytest.mark.parametrize("pad", ["none", "one", "to4"])
+def test_g_columns_match_rows_and_oracle(q, wtype, K, N, T, pad):
+    """G stored t-fastest (the transpose of an N x ldg buffer, NaN past its
+    T values per column; ldg = T, T + 1, or a multiple of 4 past T): every
+    kernel that takes the layout matches the oracle on the same G, and is
+    bit-identical to the same kernel on G stored by rows (both layouts give
+    the kernels the same values in the same order)."""
+    c = wl.make_case(wtype, N, K, T, seed=1300 + N)
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
+    ldg = {"none": T, "one": T + 1, "to4": (T + 7) // 4 * 4}[pad]
+    rb = wl.row_bytes(wtype, K)
+    W, Gc = dev(c["W"]), g_columns(c["G"], ldg)
+    assert Gc.stride() == (1, ldg)
+    # G by rows, with the row stride rounded up to 4 floats (a layout every
+    # kernel takes)
+    gbig = torch.full((T, (N + 3) // 4 * 4), float("nan"), device="cuda")
+    gbig[:, :N] = dev(c["G"])
+    Gr = gbig[:, :N]
+    ran = []
+    for v in ["auto", "skinny"] + tile_variants(wtype):
+        vid = 0 if v == "auto" else variant_id(q, v)
+        if v != "auto" and not q.variant_applies_views(vid, wtype, K, N, T, rb, 1, ldg, K):
+            continue
+        out = torch.full((T, K), float("nan"), device="cuda")
+        q.out_prod(wtype, W, Gc, K, out=out, variant=vid)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        check_close(got, acc, ab, f"g columns {v}")
+        if v != "auto":
+            ref = q.out_prod(wtype, W, Gr, K, variant=vid)
+            torch.cuda.synchronize()
+            assert np.array_equal(got.view(np.uint32), ref.cpu().numpy().view(np.uint32)), v
+        ran.append(v)
+    families = {v.split("_")[0].rstrip("2") for v in ran if v != "auto"}
+    assert ("skinny" in families) == (T <= 16), ran
+    dense_odd = wtype in (wl.F32, wl.F16, wl.BF16) and K % 4 != 0
+    if T > 16:
+        assert "tile" in families and (("ws" in families) == (ldg % 4 == 0 and not dense_odd)), ran
+
+
 # --- batches over two outer dimensions, with W broadcast ------------------------------
 
 BATCHED = [(wl.Q4_K, 512, 64, 40, ["auto", "ws_64x256", "tile_64x256"]),
@@ -369,12 +427,13 @@ BATCHED = [(wl.Q4_K, 512, 64, 40, ["auto", "ws_64x256", "tile_64x256"]),
 
 
 @pytest.mark.parametrize("wtype,K,N,T,variants", BATCHED)
-def test_batched_broadcast_matches_oracle(q, wtype, K, N, T, variants):
+@pytest.mark.parametrize("layout", ["rows", "columns"])
+def test_batched_broadcast_matches_oracle(q, wtype, K, N, T, variants, layout):
     """dst[i3][i2] = out_prod(W[i3 / 2][i2 / 2], G[i3][i2]) over 2 x 4 batches
     with 1 x 2 W matrices; W rows padded to 16-byte multiples, G a permuted
-    view (its i3 batches closer than its i2 ones), dst matrices with gaps.
-    Every batch matches the oracle on its own pair of matrices, and the
-    gaps of dst keep their sentinel."""
+    view (its i3 batches closer than its i2 ones; each matrix stored by rows
+    or t-fastest), dst matrices with gaps. Every batch matches the oracle on
+    its own pair of matrices, and the gaps of dst keep their sentinel."""
     ne03, ne02, ne3, ne2 = 1, 2, 2, 4
     rb = wl.row_bytes(wtype, K)
     ldw = (rb + 15) // 16 * 16
@@ -384,9 +443,14 @@ def test_batched_broadcast_matches_oracle(q, wtype, K, N, T, variants):
         wbig[i // ne02, i % ne02, :, :rb] = dev(c["W"])
     rng = np.random.default_rng(77)
     g_host = rng.standard_normal((ne2, ne3, T, N)).astype(np.float32)
-    G = dev(g_host).permute(1, 0, 2, 3)              # [ne3, ne2, T, N], not contiguous
+    if layout == "rows":
+        G = dev(g_host).permute(1, 0, 2, 3)              # [ne3, ne2, T, N], not contiguous
+    else:
+        G = dev(np.ascontiguousarray(g_host.transpose(0, 1, 3, 2))).permute(1, 0, 3, 2)
+        assert G.stride(2) == 1
+    sgt, sgn = (N, 1) if layout == "rows" else (1, T)
     for v in variants:
-        if v != "auto" and not q.variant_applies(variant_id(q, v), wtype, K, N, T):
+        if v != "auto" and not q.variant_applies_views(variant_id(q, v), wtype, K, N, T, ldw, sgt, sgn, K):
             continue
         dbig = torch.full((ne3, ne2, T + 1, K + 4), 7.0, device="cuda")
         out = dbig[:, :, :T, :K]
@@ -459,6 +523,27 @@ def test_full_size_sampled_rows(q, name, wtype):
     y = out[torch.from_numpy(rows).cuda()].cpu().numpy()
     e = check_close(y, acc, ab, name)
     print(f"{name} {wl.TYPE_NAMES[c['type']]}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
+
+
+@pytest.mark.parametrize("name,wtype", [("q4_k_n14336_k4096_t4096", None), ("q4_k_n4096_k14336_t16", None),
+                                        ("q4_0_n17408_k5120_t2048", None), ("dense_n4096_k4096_t512", wl.BF16)])
+def test_full_size_g_columns(q, name, wtype):
+    """The benchmarked shapes with G stored t-fastest (the transpose of a
+    contiguous N x T tensor, as ggml's OUT_PROD gets a contiguous src1): the
+    same kernel is chosen and the whole output is bit-identical to the one
+    from G stored by rows."""
+    c = wl.workload(name, wtype)
+    K, N, T = c["K"], c["N"], c["T"]
+    rb = wl.row_bytes(c["type"], K)
+    assert q.choice_views(c["type"], K, N, T, rb, 1, T, K) == q.choice(c["type"], K, N, T)
+    W, Gr = dev(c["W"]), dev(c["G"])
+    Gc = Gr.t().contiguous().t()
+    a = q.out_prod(c["type"], W, Gr, K)
+    b = q.out_prod(c["type"], W, Gc, K)
+    torch.cuda.synchronize()
+    assert torch.isfinite(b).all().item()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    del Gc
 
 
 @pytest.mark.parametrize("name", ["q4_0_n17408_k5120_t2048", "q4_k_n14336_k4096_t4096", "q4_k_n4096_k14336_t16",
