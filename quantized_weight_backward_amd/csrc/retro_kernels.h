@@ -210,8 +210,10 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
         const int r = id / S::UPR, u = id - r * S::UPR;
         woff[s] = uint32_t(r * args.pitch + 16 * u);
     }
-    // elements spanned by G
-    const long long g_end = args.gcols ? (long long)(N - 1) * args.ldg + T : (long long)(T - 1) * args.ldg + N;
+    // elements spanned by G (none when N = 0: G is empty and its pointer may
+    // be null)
+    const long long g_end =
+        N == 0 ? 0 : args.gcols ? (long long)(N - 1) * args.ldg + T : (long long)(T - 1) * args.ldg + N;
     // bytes spanned by W: rows are `pitch` apart, the last one ends after
     // its K / block blocks
     const long long w_end = N > 0 ? (long long)(N - 1) * args.pitch + (long long)(K / F::kBlock) * F::kBytes : 0;

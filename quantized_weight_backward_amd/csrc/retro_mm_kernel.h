@@ -317,7 +317,7 @@ __global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWgPerCu)) void mu
 #pragma unroll
             for (int g = 0; g < 4; ++g) wlds[u][g] = ws_w_index<WP>(r, 16 * h + 4 * g);
         }
-        const long long x_end = (long long)(T - 1) * args.ldx + K;  // elements spanned by x
+        const long long x_end = K == 0 ? 0 : (long long)(T - 1) * args.ldx + K;  // elements spanned by x
         const long long wb = (long long)n0 * args.pitch;
         const long long w_end =
             (long long)(N - 1) * args.pitch + (long long)(K / S::F::kBlock) * S::F::kBytes;
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(1024) void mul_mat_skinny_kernel(MmSimpleArgs a) {
     const long long w_end = (long long)(a.N - 1) * a.pitch + (long long)(K / F::kBlock) * F::kBytes;
     const __amdgpu_buffer_rsrc_t wr =
         buffer_rsrc(a.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
-    const long long x_end = (long long)(a.T - 1) * a.ldx + K;
+    const long long x_end = K == 0 ? 0 : (long long)(a.T - 1) * a.ldx + K;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.X, uint32_t(max(0ll, min(4 * x_end, (long long)0x7FFFFFFF))));
     const uint32_t ro = uint32_t(j * a.pitch);
     const uint32_t xo = uint32_t(j * a.ldx * 4);

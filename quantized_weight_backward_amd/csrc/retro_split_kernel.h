@@ -1,0 +1,393 @@
+// retro_split_kernel.h - Q4_K OUT_PROD on bf16 MFMA with exact operands
+// ("exact split"): a variant that trades the F32-input MFMA for the bf16
+// matrix rate, keeping every product exact and every sum in F32.
+//
+// A Q4_K element of row n, sub-block j of a super-block is
+// d*sc_j*q - dmin*m_j (q a nibble, sc_j and m_j 6-bit integers, d and dmin
+// fp16). Over one super-block of columns the contraction splits as
+//
+//   dst[t][k] = sum_n (G[t][n]*d[n]) * v[n][k]  -  sum_n (G[t][n]*dmin[n]) * m_j(k)[n]
+//
+// with v = sc_j*q an integer below 1024. Each factor is made exact in bf16:
+//   * v = hi + lo with hi = v & ~3 (at most 8 significant bits) and lo = v & 3;
+//   * m_j, at most 6 bits, as it is;
+//   * A = fl(G*d) and E = fl(G*dmin), single F32 roundings, each cut into
+//     three bf16 parts (the top 8, the next 8 and the last 8 significant
+//     bits: A = A0 + A1 + A2 exactly).
+// The main term is then six bf16 MFMAs (A0, A1, A2 times hi and lo), the
+// min term three (E0, E1, E2 times m). Products of bf16 values are exact;
+// the matrix core adds them in F32 arithmetic (measured on gfx950: it keeps
+// about F32 precision relative to the largest product of one instruction and
+// truncates). Against the F32-input path the result differs by the two
+// roundings of A and E and by that addition, all at F32 level.
+//
+// Organisation as in out_prod_ws_kernel (8 waves: 4 consumers in a 2 x 2
+// grid over a 128 x 256 tile, 4 producers; G and the decoded W double
+// buffered in LDS, one barrier per 32-row chunk). The producers write G
+// (F32), d and dmin per row, hi and lo of v (bf16, k-major with the 32 rows
+// of a column contiguous) and m (bf16); the consumers form the A and E parts
+// in registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "retro_ws_kernel.h"
+
+namespace retro {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct SplitShape {
+    static constexpr int kPThreads = 256;
+    static constexpr int kThreads = 512;
+    static constexpr int BT = 128, BK = 256, BN = 32;
+    static constexpr int GP = BN + 4;          // floats per t row of G
+    static constexpr int G_FLOATS = BT * GP;   // 4608
+    static constexpr int D_OFF = G_FLOATS;     // d of the chunk's 32 rows
+    static constexpr int DM_OFF = D_OFF + BN;  // dmin
+    // bf16 operands, counted in floats (two bf16 each)
+    static constexpr int B_OFF = DM_OFF + BN;             // hi, lo: 2 x BK columns x 32 rows
+    static constexpr int B_PART = BK * BN / 2;            // floats per part
+    static constexpr int M_OFF = B_OFF + 2 * B_PART;      // m: 16 columns x 32 rows (8 used)
+    static constexpr int BUF_FLOATS = M_OFF + 16 * BN / 2;
+    static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // 4
+};
+
+// Float offset, inside a part of the bf16 W operand, of the 8-byte group
+// holding rows 4 r4 .. 4 r4 + 3 of column col. A column's 32 rows are four
+// 16-byte units; unit u sits at position u ^ ((col >> 2) & 3), so that the
+// 16 columns a quarter wave reads hit distinct banks.
+__device__ __forceinline__ int split_b_index(int col, int r4) {
+    return col * 16 + 4 * ((r4 >> 1) ^ ((col >> 2) & 3)) + 2 * (r4 & 1);
+}
+
+// The bf16 bits of an exactly representable float (its upper half).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// x (8 floats) -> three bf16x8 parts with x = p0 + p1 + p2 exactly: p0 keeps
+// the top 16 bits of x (sign, exponent, 7 fraction bits), p1 the same of the
+// remainder, p2 the last remainder (at most 8 significant bits).
+__device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& p1, bf16x8& p2) {
+    uint32_t w0[4], w1[4], w2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float h[2], m[2], r[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float v = x[2 * i + e];
+            h[e] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+            const float r1 = v - h[e];
+            m[e] = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+            r[e] = r1 - m[e];
+        }
+        w0[i] = bf16_pair(h[0], h[1]);
+        w1[i] = bf16_pair(m[0], m[1]);
+        w2[i] = bf16_pair(r[0], r[1]);
+    }
+    p0 = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w0[2], w0[3]});
+    p1 = __builtin_bit_cast(bf16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
+    p2 = __builtin_bit_cast(bf16x8, u32x4{w2[0], w2[1], w2[2], w2[3]});
+}
+
+template <int TYPE>
+__global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
+    static_assert(TYPE == kQ4_K, "exact split is built for Q4_K");
+    using S = SplitShape;
+    using F = Format<TYPE>;
+    constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP;
+
+    __shared__ __attribute__((aligned(16))) float lds[2 * S::BUF_FLOATS];
+
+    enter_batch(args);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tt, tk;
+    tile_coords(blockIdx.x, args.tiles_t, args.tiles_k, args.group, tt, tk);
+    const int t0 = tt * BT, k0 = tk * BK;
+    const int K = args.K, N = args.N, T = args.T;
+    const int nloc = (N + BN - 1) / BN;
+
+    if (wave >= 4) {
+        // ---------------- producer ----------------
+        const int p = tid - S::kPThreads;
+        // the m operand's unused columns 8..15 hold zeros
+        if (p < 2 * 8 * BN / 2) {
+            const int b = p / (8 * BN / 2), o = p % (8 * BN / 2);
+            lds[b * S::BUF_FLOATS + S::M_OFF + 8 * BN / 2 + o] = 0.f;
+        }
+        const long long kb0 = (long long)(k0 / F::kBlock) * F::kBytes;
+        // G: slot s is t row id / 8, columns 4 (id % 8) .. + 3 (id = p + 256 s)
+        uint32_t goff[S::GSLOTS];
+#pragma unroll
+        for (int s = 0; s < S::GSLOTS; ++s) {
+            const int id = p + S::kPThreads * s;
+            goff[s] = uint32_t(((id >> 3) * args.ldg + 4 * (id & 7)) * 4);
+        }
+        // W: rows 4 r4 .. 4 r4 + 3 of the chunk, code word w of each (bytes
+        // 16 + 4w .. of the super-block: low nibbles are columns
+        // 64 (w / 8) + 4 (w % 8) + 0..3 of sub-block 2 (w / 8), high nibbles
+        // the same plus 32, of sub-block 2 (w / 8) + 1)
+        const int r4 = p >> 5, w = p & 31;
+        uint32_t roff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) roff[i] = uint32_t((4 * r4 + i) * args.pitch);
+        // elements spanned by G (none when N = 0: G is empty and its pointer
+        // may be null)
+        const long long g_end = N == 0 ? 0 : (long long)(T - 1) * args.ldg + N;
+        const long long w_end =
+            N > 0 ? (long long)(N - 1) * args.pitch + (long long)(K / F::kBlock) * F::kBytes : 0;
+
+        constexpr int R = 2;
+        float4 gring[R][S::GSLOTS];
+        uint32_t hring[R][4][4];  // per row: d | dmin << 16, the three scale words
+        uint32_t cring[R][4];     // per row: the code word
+
+        auto load_chunk = [&](auto slot, int n0) __attribute__((always_inline)) {
+            constexpr int I = decltype(slot)::value;
+            n0 = __builtin_amdgcn_readfirstlane(n0);
+            const long long gb = (long long)t0 * args.ldg + n0;
+            const __amdgpu_buffer_rsrc_t gr =
+                buffer_rsrc(args.G + gb, uint32_t(max(0ll, min(4 * (g_end - gb), (long long)0x7FFFFFFF))));
+#pragma unroll
+            for (int s = 0; s < S::GSLOTS; ++s) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, goff[s], 0, 0);
+                gring[I][s] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                          __uint_as_float(v.w));
+            }
+            const long long wb = (long long)n0 * args.pitch + kb0;
+            const __amdgpu_buffer_rsrc_t wr =
+                buffer_rsrc(args.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wr, roff[i], 0, 0);
+                hring[I][i][0] = h.x;
+                hring[I][i][1] = h.y;
+                hring[I][i][2] = h.z;
+                hring[I][i][3] = h.w;
+                cring[I][i] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 16 + 4 * w, 0, 0);
+            }
+        };
+
+        auto store_chunk = [&](auto slot, auto buf, int n0) __attribute__((always_inline)) {
+            constexpr int I = decltype(slot)::value;
+            float* const base = lds + decltype(buf)::value * S::BUF_FLOATS;
+            // G rows as loaded; columns at or past N (the next row's values in
+            // the last chunk) zeroed
+            if (n0 + BN > N) {
+#pragma unroll
+                for (int s = 0; s < S::GSLOTS; ++s) {
+                    const int n = n0 + 4 * ((p + S::kPThreads * s) & 7);
+                    if (n >= N) gring[I][s].x = 0.f;
+                    if (n + 1 >= N) gring[I][s].y = 0.f;
+                    if (n + 2 >= N) gring[I][s].z = 0.f;
+                    if (n + 3 >= N) gring[I][s].w = 0.f;
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < S::GSLOTS; ++s) {
+                const int id = p + S::kPThreads * s;
+                *reinterpret_cast<float4*>(base + (id >> 3) * GP + 4 * (id & 7)) = gring[I][s];
+            }
+            // d, dmin (words w = 8, 9) and m_w (w < 8) of the four rows
+            if (w == 8 || w == 9) {
+                float4 v;
+                v.x = half_to_f32(w == 8 ? (hring[I][0][0] & 0xFFFFu) : (hring[I][0][0] >> 16));
+                v.y = half_to_f32(w == 8 ? (hring[I][1][0] & 0xFFFFu) : (hring[I][1][0] >> 16));
+                v.z = half_to_f32(w == 8 ? (hring[I][2][0] & 0xFFFFu) : (hring[I][2][0] >> 16));
+                v.w = half_to_f32(w == 8 ? (hring[I][3][0] & 0xFFFFu) : (hring[I][3][0] >> 16));
+                *reinterpret_cast<float4*>(base + (w == 8 ? S::D_OFF : S::DM_OFF) + 4 * r4) = v;
+            } else if (w < 8) {
+                float m[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t sc, mm;
+                    q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], w, sc, mm);
+                    m[i] = static_cast<float>(mm);
+                }
+                // column w, rows 4 r4 .. + 3 (plain k-major, 16 floats per column)
+                *reinterpret_cast<uint2*>(base + S::M_OFF + w * 16 + 2 * r4) =
+                    make_uint2(bf16_pair(m[0], m[1]), bf16_pair(m[2], m[3]));
+            }
+            // v = sc * q of 8 columns x 4 rows, split into hi and lo
+            const int c = w >> 3, j0 = 4 * (w & 7);
+            uint32_t sc_lo[4], sc_hi[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t mm;
+                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c, sc_lo[i], mm);
+                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c + 1, sc_hi[i], mm);
+            }
+            float* const hi_part = base + S::B_OFF;
+            float* const lo_part = hi_part + S::B_PART;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    float vh[4], vl[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t q = (cring[I][i] >> (8 * b + 4 * half)) & 15u;
+                        const uint32_t v = (half ? sc_hi[i] : sc_lo[i]) * q;
+                        vh[i] = static_cast<float>(v & ~3u);
+                        vl[i] = static_cast<float>(v & 3u);
+                    }
+                    const int col = 64 * c + 32 * half + j0 + b;
+                    const int o = split_b_index(col, r4);
+                    *reinterpret_cast<uint2*>(hi_part + o) = make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
+                    *reinterpret_cast<uint2*>(lo_part + o) = make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                }
+            }
+        };
+
+        using Zero = std::integral_constant<int, 0>;
+        static_for<R>([&](auto i) { load_chunk(i, decltype(i)::value * BN); });
+        store_chunk(Zero{}, Zero{}, 0);
+        __syncthreads();
+        auto step = [&](auto i, int c) __attribute__((always_inline)) {
+            constexpr int I = decltype(i)::value;
+            store_chunk(std::integral_constant<int, (I + 1) % R>{}, std::integral_constant<int, (I + 1) & 1>{},
+                        (c + 1) * BN);
+            load_chunk(i, (c + R) * BN);
+            __syncthreads();
+        };
+        int c0 = 0;
+        for (; c0 + R <= nloc; c0 += R) static_for<R>([&](auto i) { step(i, c0 + decltype(i)::value); });
+        static_for<R>([&](auto i) {
+            if (c0 + decltype(i)::value < nloc) step(i, c0 + decltype(i)::value);
+        });
+        __syncthreads();  // the consumers' exchange of the min term
+        return;
+    }
+
+    // ---------------- consumer ----------------
+    const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int wt = wave >> 1, wk = wave & 1;
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+    f32x4 accm[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) accm[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // B operand offsets (floats) of the lane's columns, per k-step s
+    int boff[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int col = 128 * wk + 32 * b + l32;
+            boff[s][b] = S::B_OFF + col * 16 + 4 * ((2 * s + h) ^ ((col >> 2) & 3));
+        }
+
+    auto contract = [&](const float* base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int n = 16 * s + 8 * h;
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n + 4);
+            bf16x8 ap[2][3];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const float* g = base + (64 * wt + 32 * a + l32) * GP + n;
+                const f32x4 g0 = *reinterpret_cast<const f32x4*>(g);
+                const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + 4);
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = g0[e] * d0[e];
+                    x[4 + e] = g1[e] * d1[e];
+                }
+                split3(x, ap[a][0], ap[a][1], ap[a][2]);
+            }
+            bf16x8 bp[4][2];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    bp[b][q] = *reinterpret_cast<const bf16x8*>(base + boff[s][b] + q * S::B_PART);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pa = 0; pa < 3; ++pa)
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[a][pa], bp[b][q], acc[a][b], 0,
+                                                                                0, 0);
+        }
+        // min term: t rows 64 wt + 16 (2 wk + a) + l % 16, all 32 rows n of
+        // the chunk (n = 8 (l / 16) + 0..7), columns j = l % 16 (8 used)
+        {
+            const int n = 8 * (lane >> 4);
+            const f32x4 m0 = *reinterpret_cast<const f32x4*>(base + S::DM_OFF + n);
+            const f32x4 m1 = *reinterpret_cast<const f32x4*>(base + S::DM_OFF + n + 4);
+            const bf16x8 mb = *reinterpret_cast<const bf16x8*>(base + S::M_OFF + (lane & 15) * 16 + 4 * (lane >> 4));
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const float* g = base + (64 * wt + 16 * (2 * wk + a) + (lane & 15)) * GP + n;
+                const f32x4 g0 = *reinterpret_cast<const f32x4*>(g);
+                const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + 4);
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = g0[e] * m0[e];
+                    x[4 + e] = g1[e] * m1[e];
+                }
+                bf16x8 ep[3];
+                split3(x, ep[0], ep[1], ep[2]);
+#pragma unroll
+                for (int pa = 0; pa < 3; ++pa)
+                    accm[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ep[pa], mb, accm[a], 0, 0, 0);
+            }
+        }
+    };
+
+    __syncthreads();
+    for (int c = 0; c < nloc; c += 2) {
+        contract(lds);
+        __syncthreads();
+        if (c + 1 < nloc) {
+            contract(lds + S::BUF_FLOATS);
+            __syncthreads();
+        }
+    }
+
+    // the min term of tile rows 0..127, columns (sub-blocks) 0..7, through LDS
+    // (D layout of the 16 x 16 product: lane l, register i holds row
+    // 4 (l / 16) + i, column l % 16)
+    float* const mins = lds;
+    if ((lane & 15) < 8) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mins[(64 * wt + 16 * (2 * wk + a) + 4 * (lane >> 4) + i) * 8 + (lane & 15)] = accm[a][i];
+    }
+    __syncthreads();
+    // D layout of the 32 x 32 product: lane l, register v holds row
+    // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int k = k0 + 128 * wk + 32 * b + l32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int tl = 64 * wt + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int t = t0 + tl;
+                if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = acc[a][b][v] - mins[tl * 8 + 4 * wk + b];
+            }
+        }
+}
+
+}  // namespace retro

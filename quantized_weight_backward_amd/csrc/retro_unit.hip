@@ -8,6 +8,7 @@
 #include "retro_host.h"
 #include "retro_kernels.h"
 #include "retro_mm_kernel.h"
+#include "retro_split_kernel.h"
 #include "retro_ws_kernel.h"
 
 #ifndef RETRO_UNIT_TYPE
@@ -113,6 +114,33 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
 }
 
 template <int TYPE>
+int launch_split(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+                 hipStream_t st) {
+    using S = SplitShape;
+    TileArgs a;
+    a.W = static_cast<const uint8_t*>(W);
+    a.G = G;
+    a.dst = dst;
+    a.K = int(K);
+    a.N = int(N);
+    a.T = int(T);
+    a.pitch = s.ldw;
+    a.ldg = s.ldg;
+    a.ldd = s.ldd;
+    a.wvec = 16;
+    a.gvec = 1;
+    a.gcols = 0;
+    a.tiles_t = int(cdiv(T, S::BT));
+    a.tiles_k = int(cdiv(K, S::BK));
+    a.group = group_height(a.tiles_t, a.tiles_k, 1, 4.0 * T * N, double(N) * row_bytes_of(TYPE, K));
+    a.batch = batch_args(s);
+    const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_k);
+    clear_last_error();
+    hipLaunchKernelGGL((out_prod_split_kernel<TYPE>), dim3(nt, unsigned(s.batches())), dim3(S::kThreads), 0, st, a);
+    return launch_status();
+}
+
+template <int TYPE>
 int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
                   hipStream_t st) {
     constexpr int kWaves = RETRO_SKINNY_WAVES;
@@ -190,6 +218,8 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
         case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, s, st);
         default: break;
     }
+    if constexpr (TYPE == kQ4_K)
+        if (variant == RETRO_VARIANT_SPLIT_128x256) return launch_split<TYPE>(W, G, dst, K, N, T, s, st);
     if constexpr (!kSuperBlock<TYPE>) {
         switch (variant) {
             case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, s, st);

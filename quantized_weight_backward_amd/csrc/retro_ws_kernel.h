@@ -315,9 +315,10 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
                 wlds[1] = ws_w_index<WP>(32 * b + 16, r) + S::CB * s * WP;
             }
         }
-        // elements spanned by G
+        // elements spanned by G (none when N = 0: G is empty and its pointer
+        // may be null)
         const long long g_end =
-            GCOLS ? (long long)(N - 1) * args.ldg + T : (long long)(T - 1) * args.ldg + N;
+            N == 0 ? 0 : GCOLS ? (long long)(N - 1) * args.ldg + T : (long long)(T - 1) * args.ldg + N;
         // bytes spanned by W: rows are `pitch` apart, the last one ends after
         // its K / block blocks
         const long long w_end =

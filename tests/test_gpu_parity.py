@@ -256,6 +256,25 @@ def test_empty_reduction_fills_zeros(q, wtype):
         assert np.array_equal(y, np.zeros((T, K), np.float32))
 
 
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q4_0, wl.F32, wl.MXFP4])
+def test_empty_reduction_with_a_row_stride(q, wtype):
+    """N = 0 with G an empty view whose row stride is not 0 (torch hands over
+    a null pointer for it): every kernel that takes the shape writes zeros and
+    reads nothing of G or W."""
+    K = SMALL_K[wtype][0]
+    W = torch.zeros(0, dtype=torch.uint8, device="cuda")
+    for T in (7, 100):
+        G = torch.zeros((T, 8), device="cuda")[:, :0]
+        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype == wl.Q4_K else []):
+            vid = 0 if v == "auto" else variant_id(q, v)
+            if v != "auto" and not q.variant_applies_strided(vid, wtype, K, 0, T, wl.row_bytes(wtype, K), 8, K):
+                continue
+            out = torch.full((T, K), float("nan"), device="cuda")
+            q.out_prod(wtype, W, G, K, out=out, variant=vid)
+            torch.cuda.synchronize()
+            assert not out.any() and not out.isnan().any(), v
+
+
 def test_zero_size_calls_touch_nothing(q):
     out = torch.full((0, 256), 1.0, device="cuda")
     q.out_prod(wl.Q4_K, torch.zeros(0, dtype=torch.uint8, device="cuda"),
@@ -417,6 +436,75 @@ def test_g_columns_match_rows_and_oracle(q, wtype, K, N, T, pad):
     dense_odd = wtype in (wl.F32, wl.F16, wl.BF16) and K % 4 != 0
     if T > 16:
         assert "tile" in families and (("ws" in families) == (ldg % 4 == 0 and not dense_odd)), ran
+
+
+# --- exact split on bf16 MFMA (Q4_K, opt-in) -----------------------------------------
+
+SPLIT_SHAPES = [(200, 76, 768), (130, 96, 512), (67, 36, 256), (150, 100, 768), (5, 40, 256), (129, 300, 512)]
+
+
+@pytest.mark.parametrize("T,N,K", SPLIT_SHAPES)
+def test_split_matches_oracle(q, T, N, K):
+    """The exact-split variant against the oracle at the same bars as the
+    F32-input kernels, plus: deterministic, and exactly linear in G (G * 2
+    doubles every output bit for bit: the parts of fl(2 G d) are twice those
+    of fl(G d), and the matrix core's truncation scales with them)."""
+    c = wl.make_case(wl.Q4_K, N, K, T, seed=1400 + T)
+    assert q.variant_applies(q.VARIANT_SPLIT_128x256, wl.Q4_K, K, N, T)
+    _, acc, ab = oracle.out_prod(wl.Q4_K, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
+    y = run(q, c, "split_128x256")
+    e = check_close(y, acc, ab, "split")
+    assert np.array_equal(run(q, c, "split_128x256", prefill=1e30).view(np.uint32), y.view(np.uint32))
+    two = run(q, dict(c, G=c["G"] * np.float32(2)), "split_128x256")
+    assert np.array_equal(two, 2 * y)
+    print(f"split T={T} N={N} K={K}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
+
+
+def test_split_strided_batched_and_empty(q):
+    """Strided G and dst, batches with W broadcast, and N = 0 (the empty sum)."""
+    K, N, T = 512, 70, 90
+    cases = [wl.make_case(wl.Q4_K, N, K, T, seed=1500 + i) for i in range(2)]
+    rb = wl.row_bytes(wl.Q4_K, K)
+    W = torch.stack([dev(c["W"]).view(N, rb) for c in cases])          # [2, N, rb]
+    g_host = np.stack([c["G"] for c in cases] * 2)                      # 4 batches, W i2 // 2
+    gbig = torch.full((4, T, N + 6), float("nan"), device="cuda")
+    gbig[:, :, 4:4 + N] = dev(g_host)
+    G = gbig[:, :, 4:4 + N]
+    dbig = torch.full((4, T, K + 8), 7.0, device="cuda")
+    out = dbig[:, :, 4:4 + K]
+    # W [1, 2, N, rb] broadcast over G [1, 4, T, N]: batch i2 takes W matrix i2 // 2
+    q.out_prod_batched(wl.Q4_K, W.unsqueeze(0), G.unsqueeze(0), K, out=out.unsqueeze(0),
+                       variant=q.VARIANT_SPLIT_128x256)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i in range(4):
+        c = cases[i // 2]
+        _, acc, ab = oracle.out_prod(wl.Q4_K, c["W"], g_host[i], K)
+        check_close(got[i], acc, ab, f"split batch {i}")
+    rest = dbig.clone()
+    rest[:, :, 4:4 + K] = 7.0
+    assert bool((rest == 7.0).all())
+    # N = 0
+    g0 = torch.zeros((9, 4), device="cuda")[:, :0]  # row stride 4: 16-byte rows, as the variant needs
+    empty = q.out_prod(wl.Q4_K, torch.zeros(0, dtype=torch.uint8, device="cuda"), g0, 256,
+                       variant=q.VARIANT_SPLIT_128x256)
+    torch.cuda.synchronize()
+    assert not empty.any()
+
+
+def test_split_full_size_sampled_rows(q):
+    """The large Q4_K workload through the exact-split kernel, on sampled
+    rows the oracle computes one by one."""
+    c = wl.workload("q4_k_n14336_k4096_t4096")
+    W, G = dev(c["W"]), dev(c["G"])
+    out = q.out_prod(c["type"], W, G, c["K"], variant=q.VARIANT_SPLIT_128x256)
+    again = q.out_prod(c["type"], W, G, c["K"], variant=q.VARIANT_SPLIT_128x256)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.equal(out, again)
+    rows = np.unique(np.concatenate([[0, c["T"] - 1], np.random.default_rng(8).integers(0, c["T"], size=14)]))
+    _, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"], rows=rows, nthreads=ORACLE_THREADS)
+    e = check_close(out[torch.from_numpy(rows).cuda()].cpu().numpy(), acc, ab, "split full")
+    print(f"split q4_k_n14336_k4096_t4096: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
 
 
 # --- batches over two outer dimensions, with W broadcast ------------------------------
