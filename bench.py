@@ -28,10 +28,12 @@ sys.path.insert(0, REPO)
 
 PEAK_F32_TFLOPS = 157.3  # MI355X dense MFMA F32
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 LARGE = "q4_k_n14336_k4096_t4096"
 SKINNY = "q4_k_n4096_k14336_t16"
 PROFILES = os.path.join(REPO, "profiles")
 KERNEL_SOURCES = ["quantized_weight_backward_amd/csrc/retro_kernels.h",
+                  "quantized_weight_backward_amd/csrc/retro_split_kernel.h",
                   "quantized_weight_backward_amd/csrc/retro_unit.hip",
                   "quantized_weight_backward_amd/csrc/retro_host.h",
                   "quantized_weight_backward_amd/csrc/retro_ws_kernel.h",
@@ -303,6 +305,34 @@ def main() -> int:
     ms_per_step = wall / args.steps * 1e3
     value = (fl_large + fl_skinny) / (wall / args.steps) / 1e12
 
+    # The exact-split variant (bf16 MFMA on exact operand parts; opt-in, never
+    # chosen automatically) on the large workload, timed after the step loop.
+    split = None
+    if q.variant_applies(q.VARIANT_SPLIT_128x256, q.Q4_K, large["K"], large["N"], large["T"]):
+        for _ in range(2):
+            q.out_prod(q.Q4_K, Wl, Gl, large["K"], out=Dl, variant=q.VARIANT_SPLIT_128x256)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in sev:
+            e[0].record(stream)
+            q.out_prod(q.Q4_K, Wl, Gl, large["K"], out=Dl, variant=q.VARIANT_SPLIT_128x256)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        t_split = np.array([e[0].elapsed_time(e[1]) for e in sev]) * 1e-3
+        # MFMA work issued per launch: per 128 x 256 tile and 32-row chunk,
+        # 384 bf16 32x32x16 products (32768 FLOP each) and 24 16x16x32 ones
+        # (16384 FLOP) for the min term
+        tiles = -(-large["T"] // 128) * -(-large["K"] // 256)
+        chunks = -(-large["N"] // 32)
+        issued = tiles * chunks * (384 * 32768 + 24 * 16384)
+        avg_split = float(t_split.mean())
+        split = {"kernel": "out_prod_split_kernel (split_128x256)", "avg_launch_ms": round(avg_split * 1e3, 4),
+                 "min_launch_ms": round(float(t_split.min()) * 1e3, 4),
+                 "tflops": round(fl_large / avg_split / 1e12, 3),
+                 "f32_mfma_roof_frac": round(fl_large / avg_split / 1e12 / PEAK_F32_TFLOPS, 4),
+                 "bf16_flops_issued_per_launch": issued,
+                 "bf16_mfma_frac": round(issued / avg_split / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "speedup_vs_f32_kernel": round(avg_large / avg_split, 3)}
+
     skinny_tflops = fl_skinny / avg_skinny / 1e12
     skinny_gbs = wbytes / avg_skinny / 1e9
     t_roof = max(wbytes / (PEAK_HBM_GBS * 1e9), fl_skinny / (PEAK_F32_TFLOPS * 1e12))
@@ -339,6 +369,7 @@ def main() -> int:
                    "f32_mfma_frac": round(skinny_tflops / PEAK_F32_TFLOPS, 4),
                    "binding_roof_frac": round(t_roof / avg_skinny, 4),
                    "weight_bytes": wbytes},
+        "exact_split": split,
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
