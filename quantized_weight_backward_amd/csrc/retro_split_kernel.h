@@ -9,7 +9,8 @@
 //   dst[t][k] = sum_n (G[t][n]*d[n]) * v[n][k]  -  sum_n (G[t][n]*dmin[n]) * m_j(k)[n]
 //
 // with v = sc_j*q an integer below 1024. Each factor is made exact in bf16:
-//   * v = hi + lo with hi = v & ~3 (at most 8 significant bits) and lo = v & 3;
+//   * v = hi + lo with hi its top 8 significant bits and lo the rest (at most
+//     2 bits, as v < 1024);
 //   * m_j, at most 6 bits, as it is;
 //   * A = fl(G*d) and E = fl(G*dmin), single F32 roundings, each cut into
 //     three bf16 parts (the top 8, the next 8 and the last 8 significant
@@ -21,8 +22,8 @@
 // truncates). Against the F32-input path the result differs by the two
 // roundings of A and E and by that addition, all at F32 level.
 //
-// Organisation as in out_prod_ws_kernel (8 waves: 4 consumers in a 2 x 2
-// grid over a 128 x 256 tile, 4 producers; G and the decoded W double
+// Organisation as in out_prod_ws_kernel (8 waves: 4 consumers, each 32 rows
+// by all 256 columns of a 128 x 256 tile, 4 producers; G and the decoded W double
 // buffered in LDS, one barrier per 32-row chunk). The producers write G
 // (F32), d and dmin per row, hi and lo of v (bf16, k-major with the 32 rows
 // of a column contiguous) and m (bf16); the consumers form the A and E parts
@@ -213,28 +214,35 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                 *reinterpret_cast<uint2*>(base + S::M_OFF + w * 16 + 2 * r4) =
                     make_uint2(bf16_pair(m[0], m[1]), bf16_pair(m[2], m[3]));
             }
-            // v = sc * q of 8 columns x 4 rows, split into hi and lo
+            // v = sc * q of 8 columns x 4 rows (exact in F32, below 1024), split
+            // as hi = its top 8 significant bits and lo = v - hi (at most 2
+            // bits), both exact in bf16
             const int c = w >> 3, j0 = 4 * (w & 7);
-            uint32_t sc_lo[4], sc_hi[4];
+            float sc_lo[4], sc_hi[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                uint32_t mm;
-                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c, sc_lo[i], mm);
-                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c + 1, sc_hi[i], mm);
+                uint32_t sl, sh, mm;
+                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c, sl, mm);
+                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c + 1, sh, mm);
+                sc_lo[i] = static_cast<float>(sl);
+                sc_hi[i] = static_cast<float>(sh);
             }
             float* const hi_part = base + S::B_OFF;
             float* const lo_part = hi_part + S::B_PART;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
+                for (int beta = 0; beta < 4; ++beta) {
+                    // byte b of the code words; rotated by lane so that the 16
+                    // lanes of a quarter wave write distinct banks
+                    const int b = (beta + (w >> 2)) & 3;
                     float vh[4], vl[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t q = (cring[I][i] >> (8 * b + 4 * half)) & 15u;
-                        const uint32_t v = (half ? sc_hi[i] : sc_lo[i]) * q;
-                        vh[i] = static_cast<float>(v & ~3u);
-                        vl[i] = static_cast<float>(v & 3u);
+                        const float q = static_cast<float>((cring[I][i] >> (8 * b + 4 * half)) & 15u);
+                        const float v = q * (half ? sc_hi[i] : sc_lo[i]);
+                        vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+                        vl[i] = v - vh[i];
                     }
                     const int col = 64 * c + 32 * half + j0 + b;
                     const int o = split_b_index(col, r4);
@@ -265,26 +273,25 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
     }
 
     // ---------------- consumer ----------------
+    // wave w: tile rows 32 w .. 32 w + 31, all 256 columns (8 blocks of 32)
     const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-    const int wt = wave >> 1, wk = wave & 1;
-    f32x16 acc[2][4];
+    const int wt = wave;
+    f32x16 acc[8];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 8; ++b)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
     f32x4 accm[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) accm[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // B operand offsets (floats) of the lane's columns, per k-step s
-    int boff[2][4];
+    int boff[2][8];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int col = 128 * wk + 32 * b + l32;
+        for (int b = 0; b < 8; ++b) {
+            const int col = 32 * b + l32;
             boff[s][b] = S::B_OFF + col * 16 + 4 * ((2 * s + h) ^ ((col >> 2) & 3));
         }
 
@@ -292,12 +299,11 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int n = 16 * s + 8 * h;
-            const f32x4 d0 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n);
-            const f32x4 d1 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n + 4);
-            bf16x8 ap[2][3];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const float* g = base + (64 * wt + 32 * a + l32) * GP + n;
+            bf16x8 ap[3];
+            {
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n + 4);
+                const float* g = base + (32 * wt + l32) * GP + n;
                 const f32x4 g0 = *reinterpret_cast<const f32x4*>(g);
                 const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + 4);
                 float x[8];
@@ -306,27 +312,29 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     x[e] = g0[e] * d0[e];
                     x[4 + e] = g1[e] * d1[e];
                 }
-                split3(x, ap[a][0], ap[a][1], ap[a][2]);
+                split3(x, ap[0], ap[1], ap[2]);
             }
-            bf16x8 bp[4][2];
+            // the 8 column blocks in two halves of 4 (operands of one half live)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int half = 0; half < 2; ++half) {
+                bf16x8 bp[4][2];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        bp[b][q] = *reinterpret_cast<const bf16x8*>(base + boff[s][4 * half + b] + q * S::B_PART);
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    bp[b][q] = *reinterpret_cast<const bf16x8*>(base + boff[s][b] + q * S::B_PART);
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int pa = 0; pa < 3; ++pa)
-#pragma unroll
-                    for (int a = 0; a < 2; ++a)
+                    for (int pa = 0; pa < 3; ++pa)
 #pragma unroll
                         for (int b = 0; b < 4; ++b)
-                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[a][pa], bp[b][q], acc[a][b], 0,
-                                                                                0, 0);
+                            acc[4 * half + b] =
+                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[pa], bp[b][q], acc[4 * half + b], 0, 0, 0);
+            }
         }
-        // min term: t rows 64 wt + 16 (2 wk + a) + l % 16, all 32 rows n of
-        // the chunk (n = 8 (l / 16) + 0..7), columns j = l % 16 (8 used)
+        // min term: t rows 32 wt + 16 a + l % 16, all 32 rows n of the chunk
+        // (n = 8 (l / 16) + 0..7), columns j = l % 16 (8 used)
         {
             const int n = 8 * (lane >> 4);
             const f32x4 m0 = *reinterpret_cast<const f32x4*>(base + S::DM_OFF + n);
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
             const bf16x8 mb = *reinterpret_cast<const bf16x8*>(base + S::M_OFF + (lane & 15) * 16 + 4 * (lane >> 4));
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-                const float* g = base + (64 * wt + 16 * (2 * wk + a) + (lane & 15)) * GP + n;
+                const float* g = base + (32 * wt + 16 * a + (lane & 15)) * GP + n;
                 const f32x4 g0 = *reinterpret_cast<const f32x4*>(g);
                 const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + 4);
                 float x[8];
@@ -362,32 +370,29 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         }
     }
 
-    // the min term of tile rows 0..127, columns (sub-blocks) 0..7, through LDS
+    // the min term of the wave's rows, columns (sub-blocks) 0..7, through LDS
     // (D layout of the 16 x 16 product: lane l, register i holds row
-    // 4 (l / 16) + i, column l % 16)
-    float* const mins = lds;
+    // 4 (l / 16) + i, column l % 16); each wave reads back its own rows
+    float* const mins = lds + 32 * 8 * wt;
     if ((lane & 15) < 8) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                mins[(64 * wt + 16 * (2 * wk + a) + 4 * (lane >> 4) + i) * 8 + (lane & 15)] = accm[a][i];
+            for (int i = 0; i < 4; ++i) mins[(16 * a + 4 * (lane >> 4) + i) * 8 + (lane & 15)] = accm[a][i];
     }
     __syncthreads();
     // D layout of the 32 x 32 product: lane l, register v holds row
     // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 8; ++b) {
+        const int k = k0 + 32 * b + l32;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int k = k0 + 128 * wk + 32 * b + l32;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int tl = 64 * wt + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-                const int t = t0 + tl;
-                if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = acc[a][b][v] - mins[tl * 8 + 4 * wk + b];
-            }
+        for (int v = 0; v < 16; ++v) {
+            const int tl = 8 * (v >> 2) + 4 * h + (v & 3);
+            const int t = t0 + 32 * wt + tl;
+            if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = acc[b][v] - mins[tl * 8 + b];
         }
+    }
 }
 
 }  // namespace retro
