@@ -81,6 +81,7 @@ PROFILE_COMMANDS = {
 KERNELS = {  # summary tag -> (kernel-name prefix in rocprofv3 output, workload, variant)
     f"ws_{LARGE}": ("void retro::out_prod_ws_kernel<12, 2, 4, 2, 1, false>", LARGE, "ws_128x256"),
     f"skinny_{SKINNY}": ("void retro::out_prod_skinny_kernel<12, 16, true>", SKINNY, "skinny"),
+    f"split_{LARGE}": ("void retro::out_prod_split_kernel<12>", LARGE, "split_128x256"),
 }
 LARGE_TAG, SKINNY_TAG = f"ws_{LARGE}", f"skinny_{SKINNY}"
 
@@ -325,7 +326,8 @@ def main() -> int:
         chunks = -(-large["N"] // 32)
         issued = tiles * chunks * (384 * 32768 + 24 * 16384)
         avg_split = float(t_split.mean())
-        split = {"kernel": "out_prod_split_kernel (split_128x256)", "avg_launch_ms": round(avg_split * 1e3, 4),
+        split = {"kernel": "out_prod_split_kernel (split_128x256)", "traffic": read_traffic(f"split_{LARGE}"),
+                 "avg_launch_ms": round(avg_split * 1e3, 4),
                  "min_launch_ms": round(float(t_split.min()) * 1e3, 4),
                  "tflops": round(fl_large / avg_split / 1e12, 3),
                  "f32_mfma_roof_frac": round(fl_large / avg_split / 1e12 / PEAK_F32_TFLOPS, 4),
