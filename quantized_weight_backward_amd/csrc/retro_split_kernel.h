@@ -97,7 +97,8 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& 
 
 template <int TYPE>
 __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
-    static_assert(TYPE == kQ4_K, "exact split is built for Q4_K");
+    static_assert(TYPE == kQ4_K || TYPE == kQ6_K, "exact split is built for Q4_K and Q6_K");
+    constexpr bool kMin = TYPE == kQ4_K;  // Q6_K values have no min term
     using S = SplitShape;
     using F = Format<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP;
@@ -133,6 +134,9 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         // 16 + 4w .. of the super-block: low nibbles are columns
         // 64 (w / 8) + 4 (w % 8) + 0..3 of sub-block 2 (w / 8), high nibbles
         // the same plus 32, of sub-block 2 (w / 8) + 1)
+        // Q6_K instead: half h = w / 16 of the super-block, elements
+        // l = 2 (w % 16) + e (e = 0, 1) of its four quarters qq: columns
+        // 128 h + 32 qq + l
         const int r4 = p >> 5, w = p & 31;
         uint32_t roff[4];
 #pragma unroll
@@ -145,8 +149,9 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
 
         constexpr int R = 2;
         float4 gring[R][S::GSLOTS];
-        uint32_t hring[R][4][4];  // per row: d | dmin << 16, the three scale words
-        uint32_t cring[R][4];     // per row: the code word
+        uint32_t hring[R][4][4];  // Q4_K, per row: d | dmin << 16, the three scale words
+        uint32_t cring[R][4];     // Q4_K, per row: the code word
+        uint32_t q6ring[R][4][6];  // Q6_K, per row: ql bytes (quarters 0, 2), (1, 3), qh bytes, 8 scales, d
 
         auto load_chunk = [&](auto slot, int n0) __attribute__((always_inline)) {
             constexpr int I = decltype(slot)::value;
@@ -163,14 +168,30 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
             const long long wb = (long long)n0 * args.pitch + kb0;
             const __amdgpu_buffer_rsrc_t wr =
                 buffer_rsrc(args.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
+            if constexpr (TYPE == kQ4_K) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wr, roff[i], 0, 0);
-                hring[I][i][0] = h.x;
-                hring[I][i][1] = h.y;
-                hring[I][i][2] = h.z;
-                hring[I][i][3] = h.w;
-                cring[I][i] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 16 + 4 * w, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wr, roff[i], 0, 0);
+                    hring[I][i][0] = h.x;
+                    hring[I][i][1] = h.y;
+                    hring[I][i][2] = h.z;
+                    hring[I][i][3] = h.w;
+                    cring[I][i] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 16 + 4 * w, 0, 0);
+                }
+            } else {
+                // super-blocks are 2-byte aligned; the 8-byte load of the
+                // scales relies on the unaligned buffer access of gfx9-class GPUs
+                const uint32_t hb = 64 * (w >> 4), lb = 2 * (w & 15);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    q6ring[I][i][0] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + hb + lb, 0, 0);
+                    q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + hb + 32 + lb, 0, 0);
+                    q6ring[I][i][2] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + 128 + hb / 2 + lb, 0, 0);
+                    const u32x2 sc = __builtin_amdgcn_raw_buffer_load_b64(wr, roff[i] + 192 + hb / 8, 0, 0);
+                    q6ring[I][i][3] = sc.x;
+                    q6ring[I][i][4] = sc.y;
+                    q6ring[I][i][5] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + 208, 0, 0);
+                }
             }
         };
 
@@ -194,60 +215,100 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                 const int id = p + S::kPThreads * s;
                 *reinterpret_cast<float4*>(base + (id >> 3) * GP + 4 * (id & 7)) = gring[I][s];
             }
-            // d, dmin (words w = 8, 9) and m_w (w < 8) of the four rows
-            if (w == 8 || w == 9) {
-                float4 v;
-                v.x = half_to_f32(w == 8 ? (hring[I][0][0] & 0xFFFFu) : (hring[I][0][0] >> 16));
-                v.y = half_to_f32(w == 8 ? (hring[I][1][0] & 0xFFFFu) : (hring[I][1][0] >> 16));
-                v.z = half_to_f32(w == 8 ? (hring[I][2][0] & 0xFFFFu) : (hring[I][2][0] >> 16));
-                v.w = half_to_f32(w == 8 ? (hring[I][3][0] & 0xFFFFu) : (hring[I][3][0] >> 16));
-                *reinterpret_cast<float4*>(base + (w == 8 ? S::D_OFF : S::DM_OFF) + 4 * r4) = v;
-            } else if (w < 8) {
-                float m[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint32_t sc, mm;
-                    q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], w, sc, mm);
-                    m[i] = static_cast<float>(mm);
-                }
-                // column w, rows 4 r4 .. + 3 (plain k-major, 16 floats per column)
-                *reinterpret_cast<uint2*>(base + S::M_OFF + w * 16 + 2 * r4) =
-                    make_uint2(bf16_pair(m[0], m[1]), bf16_pair(m[2], m[3]));
-            }
-            // v = sc * q of 8 columns x 4 rows (exact in F32, below 1024), split
-            // as hi = its top 8 significant bits and lo = v - hi (at most 2
-            // bits), both exact in bf16
-            const int c = w >> 3, j0 = 4 * (w & 7);
-            float sc_lo[4], sc_hi[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t sl, sh, mm;
-                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c, sl, mm);
-                q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c + 1, sh, mm);
-                sc_lo[i] = static_cast<float>(sl);
-                sc_hi[i] = static_cast<float>(sh);
-            }
-            float* const hi_part = base + S::B_OFF;
-            float* const lo_part = hi_part + S::B_PART;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-#pragma unroll
-                for (int beta = 0; beta < 4; ++beta) {
-                    // byte b of the code words; rotated by lane so that the 16
-                    // lanes of a quarter wave write distinct banks
-                    const int b = (beta + (w >> 2)) & 3;
-                    float vh[4], vl[4];
-#pragma unroll
+            if constexpr (TYPE == kQ4_K) {
+                // d, dmin (words w = 8, 9) and m_w (w < 8) of the four rows
+                if (w == 8 || w == 9) {
+                    float4 v;
+                    v.x = half_to_f32(w == 8 ? (hring[I][0][0] & 0xFFFFu) : (hring[I][0][0] >> 16));
+                    v.y = half_to_f32(w == 8 ? (hring[I][1][0] & 0xFFFFu) : (hring[I][1][0] >> 16));
+                    v.z = half_to_f32(w == 8 ? (hring[I][2][0] & 0xFFFFu) : (hring[I][2][0] >> 16));
+                    v.w = half_to_f32(w == 8 ? (hring[I][3][0] & 0xFFFFu) : (hring[I][3][0] >> 16));
+                    *reinterpret_cast<float4*>(base + (w == 8 ? S::D_OFF : S::DM_OFF) + 4 * r4) = v;
+                } else if (w < 8) {
+                    float m[4];
+    #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float q = static_cast<float>((cring[I][i] >> (8 * b + 4 * half)) & 15u);
-                        const float v = q * (half ? sc_hi[i] : sc_lo[i]);
-                        vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
-                        vl[i] = v - vh[i];
+                        uint32_t sc, mm;
+                        q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], w, sc, mm);
+                        m[i] = static_cast<float>(mm);
                     }
-                    const int col = 64 * c + 32 * half + j0 + b;
-                    const int o = split_b_index(col, r4);
-                    *reinterpret_cast<uint2*>(hi_part + o) = make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
-                    *reinterpret_cast<uint2*>(lo_part + o) = make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                    // column w, rows 4 r4 .. + 3 (plain k-major, 16 floats per column)
+                    *reinterpret_cast<uint2*>(base + S::M_OFF + w * 16 + 2 * r4) =
+                        make_uint2(bf16_pair(m[0], m[1]), bf16_pair(m[2], m[3]));
+                }
+                // v = sc * q of 8 columns x 4 rows (exact in F32, below 1024), split
+                // as hi = its top 8 significant bits and lo = v - hi (at most 2
+                // bits), both exact in bf16
+                const int c = w >> 3, j0 = 4 * (w & 7);
+                float sc_lo[4], sc_hi[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t sl, sh, mm;
+                    q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c, sl, mm);
+                    q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c + 1, sh, mm);
+                    sc_lo[i] = static_cast<float>(sl);
+                    sc_hi[i] = static_cast<float>(sh);
+                }
+                float* const hi_part = base + S::B_OFF;
+                float* const lo_part = hi_part + S::B_PART;
+    #pragma unroll
+                for (int half = 0; half < 2; ++half) {
+    #pragma unroll
+                    for (int beta = 0; beta < 4; ++beta) {
+                        // byte b of the code words; rotated by lane so that the 16
+                        // lanes of a quarter wave write distinct banks
+                        const int b = (beta + (w >> 2)) & 3;
+                        float vh[4], vl[4];
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float q = static_cast<float>((cring[I][i] >> (8 * b + 4 * half)) & 15u);
+                            const float v = q * (half ? sc_hi[i] : sc_lo[i]);
+                            vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+                            vl[i] = v - vh[i];
+                        }
+                        const int col = 64 * c + 32 * half + j0 + b;
+                        const int o = split_b_index(col, r4);
+                        *reinterpret_cast<uint2*>(hi_part + o) = make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
+                        *reinterpret_cast<uint2*>(lo_part + o) = make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                    }
+                }
+            } else {
+                // d of the four rows (word w = 8)
+                if (w == 8)
+                    *reinterpret_cast<float4*>(base + S::D_OFF + 4 * r4) =
+                        make_float4(half_to_f32(q6ring[I][0][5]), half_to_f32(q6ring[I][1][5]),
+                                    half_to_f32(q6ring[I][2][5]), half_to_f32(q6ring[I][3][5]));
+                // v = sc * (q - 32) of 8 columns x 4 rows (|v| <= 4096, exact in
+                // F32), split as hi = its top 8 significant bits and lo = v - hi
+                // (at most 5 bits), both exact in bf16. Element l = 2 (w % 16) + e
+                // of quarter qq: ql byte l of quarter pair qq % 2 (high nibble for
+                // qq >= 2), bits 2 qq .. of qh byte l, scale 2 qq + l / 16.
+                const int h = w >> 4, jl = w & 15;
+                float* const hi_part = base + S::B_OFF;
+                float* const lo_part = hi_part + S::B_PART;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        float vh[4], vl[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t ql = q6ring[I][i][qq & 1] >> (8 * e + 4 * (qq >> 1));
+                            const uint32_t qh = q6ring[I][i][2] >> (8 * e + 2 * qq);
+                            const int q = int((ql & 15u) | ((qh & 3u) << 4)) - 32;
+                            const int si = 2 * qq + (jl >> 3);  // scale byte within the half's 8
+                            const int sc = int(int8_t((q6ring[I][i][3 + (si >> 2)] >> (8 * (si & 3))) & 0xFFu));
+                            const float v = static_cast<float>(sc * q);
+                            vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+                            vl[i] = v - vh[i];
+                        }
+                        const int col = 128 * h + 32 * qq + 2 * jl + e;
+                        const int o = split_b_index(col, r4);
+                        *reinterpret_cast<uint2*>(hi_part + o) =
+                            make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
+                        *reinterpret_cast<uint2*>(lo_part + o) =
+                            make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                    }
                 }
             }
         };
@@ -335,7 +396,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         }
         // min term: t rows 32 wt + 16 a + l % 16, all 32 rows n of the chunk
         // (n = 8 (l / 16) + 0..7), columns j = l % 16 (8 used)
-        {
+        if constexpr (kMin) {
             const int n = 8 * (lane >> 4);
             const f32x4 m0 = *reinterpret_cast<const f32x4*>(base + S::DM_OFF + n);
             const f32x4 m1 = *reinterpret_cast<const f32x4*>(base + S::DM_OFF + n + 4);
@@ -374,7 +435,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
     // (D layout of the 16 x 16 product: lane l, register i holds row
     // 4 (l / 16) + i, column l % 16); each wave reads back its own rows
     float* const mins = lds + 32 * 8 * wt;
-    if ((lane & 15) < 8) {
+    if (kMin && (lane & 15) < 8) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -390,7 +451,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         for (int v = 0; v < 16; ++v) {
             const int tl = 8 * (v >> 2) + 4 * h + (v & 3);
             const int t = t0 + 32 * wt + tl;
-            if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = acc[b][v] - mins[tl * 8 + b];
+            if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = kMin ? acc[b][v] - mins[tl * 8 + b] : acc[b][v];
         }
     }
 }

@@ -218,9 +218,8 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
         case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, s, st);
         default: break;
     }
-    if constexpr (TYPE == kQ4_K) {
+    if constexpr (TYPE == kQ4_K || TYPE == kQ6_K)
         if (variant == RETRO_VARIANT_SPLIT_128x256) return launch_split<TYPE>(W, G, dst, K, N, T, s, st);
-    }
     if constexpr (!kSuperBlock<TYPE>) {
         switch (variant) {
             case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, s, st);

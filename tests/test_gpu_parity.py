@@ -265,7 +265,8 @@ def test_empty_reduction_with_a_row_stride(q, wtype):
     W = torch.zeros(0, dtype=torch.uint8, device="cuda")
     for T in (7, 100):
         G = torch.zeros((T, 8), device="cuda")[:, :0]
-        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype == wl.Q4_K else []):
+        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype in (wl.Q4_K, wl.Q6_K)
+                                                              else []):
             vid = 0 if v == "auto" else variant_id(q, v)
             if v != "auto" and not q.variant_applies_strided(vid, wtype, K, 0, T, wl.row_bytes(wtype, K), 8, K):
                 continue
@@ -444,20 +445,21 @@ SPLIT_SHAPES = [(200, 76, 768), (130, 96, 512), (67, 36, 256), (150, 100, 768), 
 
 
 @pytest.mark.parametrize("T,N,K", SPLIT_SHAPES)
-def test_split_matches_oracle(q, T, N, K):
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q6_K])
+def test_split_matches_oracle(q, T, N, K, wtype):
     """The exact-split variant against the oracle at the same bars as the
     F32-input kernels, plus: deterministic, and exactly linear in G (G * 2
     doubles every output bit for bit: the parts of fl(2 G d) are twice those
     of fl(G d), and the matrix core's truncation scales with them)."""
-    c = wl.make_case(wl.Q4_K, N, K, T, seed=1400 + T)
-    assert q.variant_applies(q.VARIANT_SPLIT_128x256, wl.Q4_K, K, N, T)
-    _, acc, ab = oracle.out_prod(wl.Q4_K, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
+    c = wl.make_case(wtype, N, K, T, seed=1400 + T)
+    assert q.variant_applies(q.VARIANT_SPLIT_128x256, wtype, K, N, T)
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
     y = run(q, c, "split_128x256")
     e = check_close(y, acc, ab, "split")
     assert np.array_equal(run(q, c, "split_128x256", prefill=1e30).view(np.uint32), y.view(np.uint32))
     two = run(q, dict(c, G=c["G"] * np.float32(2)), "split_128x256")
     assert np.array_equal(two, 2 * y)
-    print(f"split T={T} N={N} K={K}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
+    print(f"split {wl.TYPE_NAMES[wtype]} T={T} N={N} K={K}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
 
 
 def test_split_strided_batched_and_empty(q):
@@ -492,10 +494,11 @@ def test_split_strided_batched_and_empty(q):
     assert not empty.any()
 
 
-def test_split_full_size_sampled_rows(q):
-    """The large Q4_K workload through the exact-split kernel, on sampled
-    rows the oracle computes one by one."""
-    c = wl.workload("q4_k_n14336_k4096_t4096")
+@pytest.mark.parametrize("name", ["q4_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096"])
+def test_split_full_size_sampled_rows(q, name):
+    """The large Q4_K and Q6_K workloads through the exact-split kernel, on
+    sampled rows the oracle computes one by one."""
+    c = wl.workload(name)
     W, G = dev(c["W"]), dev(c["G"])
     out = q.out_prod(c["type"], W, G, c["K"], variant=q.VARIANT_SPLIT_128x256)
     again = q.out_prod(c["type"], W, G, c["K"], variant=q.VARIANT_SPLIT_128x256)
@@ -504,7 +507,7 @@ def test_split_full_size_sampled_rows(q):
     rows = np.unique(np.concatenate([[0, c["T"] - 1], np.random.default_rng(8).integers(0, c["T"], size=14)]))
     _, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"], rows=rows, nthreads=ORACLE_THREADS)
     e = check_close(out[torch.from_numpy(rows).cuda()].cpu().numpy(), acc, ab, "split full")
-    print(f"split q4_k_n14336_k4096_t4096: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
+    print(f"split {name}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
 
 
 # --- batches over two outer dimensions, with W broadcast ------------------------------
