@@ -192,12 +192,13 @@ const char *retro_strerror(int code);
  *                           partial sums added in LDS in that order): two
  *                           MFMA waves per SIMD for shapes with about one
  *                           tile per CU
- *   RETRO_VARIANT_SPLIT_128x256  Q4_K and Q6_K only, never chosen
+ *   RETRO_VARIANT_SPLIT_128x256  Q4_K, Q5_K and Q6_K only, never chosen
  *                           automatically: the 128 x 256 producer/consumer
  *                           tile on bf16 MFMA with exact operands. Per
  *                           super-block the sum is taken as
- *                           sum_n fl(G*d) * v minus (Q4_K) sum_n fl(G*dmin) * m,
- *                           v = sc*q (Q4_K) or sc*(q - 32) (Q6_K), every
+ *                           sum_n fl(G*d) * v minus (Q4_K, Q5_K)
+ *                           sum_n fl(G*dmin) * m, v = sc*q or sc*(q - 32)
+ *                           (Q6_K), every
  *                           factor cut into bf16 parts that add up to it
  *                           exactly, so every product is exact and every sum
  *                           is F32; the result differs from the F32-input

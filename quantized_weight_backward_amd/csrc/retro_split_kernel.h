@@ -97,8 +97,10 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& 
 
 template <int TYPE>
 __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
-    static_assert(TYPE == kQ4_K || TYPE == kQ6_K, "exact split is built for Q4_K and Q6_K");
-    constexpr bool kMin = TYPE == kQ4_K;  // Q6_K values have no min term
+    static_assert(TYPE == kQ4_K || TYPE == kQ5_K || TYPE == kQ6_K, "exact split is built for Q4_K, Q5_K, Q6_K");
+    constexpr bool kMin = TYPE != kQ6_K;  // Q6_K values have no min term
+    constexpr bool kQ45 = TYPE == kQ4_K || TYPE == kQ5_K;
+    constexpr uint32_t kCodes = TYPE == kQ5_K ? 48 : 16;  // first code byte of a super-block
     using S = SplitShape;
     using F = Format<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP;
@@ -149,8 +151,9 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
 
         constexpr int R = 2;
         float4 gring[R][S::GSLOTS];
-        uint32_t hring[R][4][4];  // Q4_K, per row: d | dmin << 16, the three scale words
-        uint32_t cring[R][4];     // Q4_K, per row: the code word
+        uint32_t hring[R][4][4];  // Q4_K, Q5_K, per row: d | dmin << 16, the three scale words
+        uint32_t cring[R][4];     // Q4_K, Q5_K, per row: the code word
+        uint32_t fring[R][4];     // Q5_K, per row: the fifth-bit bytes of the code word's elements
         uint32_t q6ring[R][4][6];  // Q6_K, per row: ql bytes (quarters 0, 2), (1, 3), qh bytes, 8 scales, d
 
         auto load_chunk = [&](auto slot, int n0) __attribute__((always_inline)) {
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
             const long long wb = (long long)n0 * args.pitch + kb0;
             const __amdgpu_buffer_rsrc_t wr =
                 buffer_rsrc(args.W + wb, uint32_t(max(0ll, min(w_end - wb, (long long)0x7FFFFFFF))));
-            if constexpr (TYPE == kQ4_K) {
+            if constexpr (kQ45) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wr, roff[i], 0, 0);
@@ -176,7 +179,10 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     hring[I][i][1] = h.y;
                     hring[I][i][2] = h.z;
                     hring[I][i][3] = h.w;
-                    cring[I][i] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 16 + 4 * w, 0, 0);
+                    cring[I][i] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + kCodes + 4 * w, 0, 0);
+                    // qh bytes 4 (w % 8) .. + 3 hold the fifth bits of the word's bytes
+                    if constexpr (TYPE == kQ5_K)
+                        fring[I][i] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 16 + 4 * (w & 7), 0, 0);
                 }
             } else {
                 // super-blocks are 2-byte aligned; the 8-byte load of the
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                 const int id = p + S::kPThreads * s;
                 *reinterpret_cast<float4*>(base + (id >> 3) * GP + 4 * (id & 7)) = gring[I][s];
             }
-            if constexpr (TYPE == kQ4_K) {
+            if constexpr (kQ45) {
                 // d, dmin (words w = 8, 9) and m_w (w < 8) of the four rows
                 if (w == 8 || w == 9) {
                     float4 v;
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     *reinterpret_cast<float4*>(base + (w == 8 ? S::D_OFF : S::DM_OFF) + 4 * r4) = v;
                 } else if (w < 8) {
                     float m[4];
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         uint32_t sc, mm;
                         q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], w, sc, mm);
@@ -236,12 +242,12 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     *reinterpret_cast<uint2*>(base + S::M_OFF + w * 16 + 2 * r4) =
                         make_uint2(bf16_pair(m[0], m[1]), bf16_pair(m[2], m[3]));
                 }
-                // v = sc * q of 8 columns x 4 rows (exact in F32, below 1024), split
-                // as hi = its top 8 significant bits and lo = v - hi (at most 2
-                // bits), both exact in bf16
+                // v = sc * q of 8 columns x 4 rows (exact in F32: below 1024 for
+                // Q4_K, 2048 for Q5_K), split as hi = its top 8 significant bits
+                // and lo = v - hi (at most 3 bits), both exact in bf16
                 const int c = w >> 3, j0 = 4 * (w & 7);
                 float sc_lo[4], sc_hi[4];
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     uint32_t sl, sh, mm;
                     q4_k_scale_min(hring[I][i][1], hring[I][i][2], hring[I][i][3], 2 * c, sl, mm);
@@ -251,17 +257,20 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                 }
                 float* const hi_part = base + S::B_OFF;
                 float* const lo_part = hi_part + S::B_PART;
-    #pragma unroll
+#pragma unroll
                 for (int half = 0; half < 2; ++half) {
-    #pragma unroll
+#pragma unroll
                     for (int beta = 0; beta < 4; ++beta) {
                         // byte b of the code words; rotated by lane so that the 16
                         // lanes of a quarter wave write distinct banks
                         const int b = (beta + (w >> 2)) & 3;
                         float vh[4], vl[4];
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float q = static_cast<float>((cring[I][i] >> (8 * b + 4 * half)) & 15u);
+                            uint32_t qi = (cring[I][i] >> (8 * b + 4 * half)) & 15u;
+                        if constexpr (TYPE == kQ5_K)  // bit 2c (low nibbles) or 2c + 1 (high) of qh byte
+                            qi |= ((fring[I][i] >> (8 * b + 2 * c + half)) & 1u) << 4;
+                        const float q = static_cast<float>(qi);
                             const float v = q * (half ? sc_hi[i] : sc_lo[i]);
                             vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
                             vl[i] = v - vh[i];

@@ -265,7 +265,7 @@ def test_empty_reduction_with_a_row_stride(q, wtype):
     W = torch.zeros(0, dtype=torch.uint8, device="cuda")
     for T in (7, 100):
         G = torch.zeros((T, 8), device="cuda")[:, :0]
-        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype in (wl.Q4_K, wl.Q6_K)
+        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype in (wl.Q4_K, wl.Q5_K, wl.Q6_K)
                                                               else []):
             vid = 0 if v == "auto" else variant_id(q, v)
             if v != "auto" and not q.variant_applies_strided(vid, wtype, K, 0, T, wl.row_bytes(wtype, K), 8, K):
@@ -445,7 +445,7 @@ SPLIT_SHAPES = [(200, 76, 768), (130, 96, 512), (67, 36, 256), (150, 100, 768), 
 
 
 @pytest.mark.parametrize("T,N,K", SPLIT_SHAPES)
-@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q6_K])
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q5_K, wl.Q6_K])
 def test_split_matches_oracle(q, T, N, K, wtype):
     """The exact-split variant against the oracle at the same bars as the
     F32-input kernels, plus: deterministic, and exactly linear in G (G * 2
@@ -494,7 +494,7 @@ def test_split_strided_batched_and_empty(q):
     assert not empty.any()
 
 
-@pytest.mark.parametrize("name", ["q4_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096"])
+@pytest.mark.parametrize("name", ["q4_k_n14336_k4096_t4096", "q5_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096"])
 def test_split_full_size_sampled_rows(q, name):
     """The large Q4_K and Q6_K workloads through the exact-split kernel, on
     sampled rows the oracle computes one by one."""
