@@ -192,19 +192,20 @@ const char *retro_strerror(int code);
  *                           partial sums added in LDS in that order): two
  *                           MFMA waves per SIMD for shapes with about one
  *                           tile per CU
- *   RETRO_VARIANT_SPLIT_128x256  Q4_K, Q5_K and Q6_K only, never chosen
- *                           automatically: the 128 x 256 producer/consumer
- *                           tile on bf16 MFMA with exact operands. Per
- *                           super-block the sum is taken as
- *                           sum_n fl(G*d) * v minus (Q4_K, Q5_K)
- *                           sum_n fl(G*dmin) * m, v = sc*q or sc*(q - 32)
- *                           (Q6_K), every
+ *   RETRO_VARIANT_SPLIT_128x256  the K-quants (Q2_K .. Q6_K) only, never
+ *                           chosen automatically: the 128 x 256 producer/
+ *                           consumer tile on bf16 MFMA with exact operands.
+ *                           Per super-block the sum is taken as
+ *                           sum_n fl(G*d) * v minus (Q2_K, Q4_K, Q5_K)
+ *                           sum_n fl(G*dmin) * m, v the integer product of
+ *                           sub-block scale and code (sc*q, sc*(q - 32) for
+ *                           Q6_K, (sc - 32)*q for Q3_K), every
  *                           factor cut into bf16 parts that add up to it
  *                           exactly, so every product is exact and every sum
  *                           is F32; the result differs from the F32-input
  *                           kernels by the roundings of G*d (and G*dmin) and
  *                           by the matrix core's F32 addition (it truncates).
- *                           Within the same error bars (tests), about 1.8x
+ *                           Within the same error bars (tests), 1.7x to 2.7x
  *                           the rate. G by rows with ldg % 4 == 0.
  */
 enum {

@@ -177,8 +177,8 @@ bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, con
     if (variant == RETRO_VARIANT_SPLIT_128x256) {
         // the 128 x 256 producer/consumer tile's limits, for G by rows
         constexpr TileVariant tile{RETRO_VARIANT_SPLIT_128x256, 128, 256, 1.0, true};
-        return (type == RETRO_Q4_K || type == RETRO_Q5_K || type == RETRO_Q6_K) && !s.gcols &&
-               tile_applies(tile, type, K, N, T, s);
+        Geometry g;
+        return geometry(type, g) && g.block == 256 && !s.gcols && tile_applies(tile, type, K, N, T, s);
     }
     const TileVariant* tv = find_tile(variant);
     return tv && tile_applies(*tv, type, K, N, T, s);

@@ -1,6 +1,10 @@
-// retro_split_kernel.h - Q4_K OUT_PROD on bf16 MFMA with exact operands
+// retro_split_kernel.h - K-quant OUT_PROD on bf16 MFMA with exact operands
 // ("exact split"): a variant that trades the F32-input MFMA for the bf16
-// matrix rate, keeping every product exact and every sum in F32.
+// matrix rate, keeping every product exact and every sum in F32. Written out
+// below for Q4_K; Q5_K adds a fifth code bit (v < 2048), Q6_K has
+// v = sc*(q - 32) and no min term, Q2_K has v = sc*q <= 45 (one bf16 part) and
+// 16 sub-blocks of mins, Q3_K has v = (sc - 32)*q' with |v| <= 128 (one part)
+// and no min term.
 //
 // A Q4_K element of row n, sub-block j of a super-block is
 // d*sc_j*q - dmin*m_j (q a nibble, sc_j and m_j 6-bit integers, d and dmin
@@ -52,7 +56,7 @@ struct SplitShape {
     // bf16 operands, counted in floats (two bf16 each)
     static constexpr int B_OFF = DM_OFF + BN;             // hi, lo: 2 x BK columns x 32 rows
     static constexpr int B_PART = BK * BN / 2;            // floats per part
-    static constexpr int M_OFF = B_OFF + 2 * B_PART;      // m: 16 columns x 32 rows (8 used)
+    static constexpr int M_OFF = B_OFF + 2 * B_PART;      // m: 16 columns x 32 rows (8 used but for Q2_K)
     static constexpr int BUF_FLOATS = M_OFF + 16 * BN / 2;
     static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // 4
 };
@@ -97,8 +101,13 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& 
 
 template <int TYPE>
 __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
-    static_assert(TYPE == kQ4_K || TYPE == kQ5_K || TYPE == kQ6_K, "exact split is built for Q4_K, Q5_K, Q6_K");
-    constexpr bool kMin = TYPE != kQ6_K;  // Q6_K values have no min term
+    static_assert(kSuperBlock<TYPE>, "exact split is built for the K-quants");
+    // sub-blocks of the min term per super-block (Q3_K and Q6_K values have none)
+    constexpr int kMinCols = (TYPE == kQ4_K || TYPE == kQ5_K) ? 8 : TYPE == kQ2_K ? 16 : 0;
+    constexpr bool kMin = kMinCols > 0;
+    // bf16 parts of v: two for Q4_K, Q5_K (v < 2048) and Q6_K (|v| <= 4096),
+    // one for Q2_K (v <= 45) and Q3_K (|v| <= 128)
+    constexpr int kBParts = (TYPE == kQ2_K || TYPE == kQ3_K) ? 1 : 2;
     constexpr bool kQ45 = TYPE == kQ4_K || TYPE == kQ5_K;
     constexpr uint32_t kCodes = TYPE == kQ5_K ? 48 : 16;  // first code byte of a super-block
     using S = SplitShape;
@@ -119,8 +128,9 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
     if (wave >= 4) {
         // ---------------- producer ----------------
         const int p = tid - S::kPThreads;
-        // the m operand's unused columns 8..15 hold zeros
-        if (p < 2 * 8 * BN / 2) {
+        // the m operand's unused columns 8..15 hold zeros (Q4_K, Q5_K; Q2_K
+        // writes all 16 with each chunk)
+        if (kMinCols == 8 && p < 2 * 8 * BN / 2) {
             const int b = p / (8 * BN / 2), o = p % (8 * BN / 2);
             lds[b * S::BUF_FLOATS + S::M_OFF + 8 * BN / 2 + o] = 0.f;
         }
@@ -154,7 +164,10 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         uint32_t hring[R][4][4];  // Q4_K, Q5_K, per row: d | dmin << 16, the three scale words
         uint32_t cring[R][4];     // Q4_K, Q5_K, per row: the code word
         uint32_t fring[R][4];     // Q5_K, per row: the fifth-bit bytes of the code word's elements
-        uint32_t q6ring[R][4][6];  // Q6_K, per row: ql bytes (quarters 0, 2), (1, 3), qh bytes, 8 scales, d
+        // Q6_K, per row: ql bytes (quarters 0, 2), (1, 3), qh bytes, 8 scales, d;
+        // Q2_K: qs bytes, the 16 pair bytes, d | dmin << 16;
+        // Q3_K: hmask bytes, qs bytes, the 12-byte scale field, d
+        uint32_t q6ring[R][4][6];
 
         auto load_chunk = [&](auto slot, int n0) __attribute__((always_inline)) {
             constexpr int I = decltype(slot)::value;
@@ -184,7 +197,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     if constexpr (TYPE == kQ5_K)
                         fring[I][i] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 16 + 4 * (w & 7), 0, 0);
                 }
-            } else {
+            } else if constexpr (TYPE == kQ6_K) {
                 // super-blocks are 2-byte aligned; the 8-byte load of the
                 // scales relies on the unaligned buffer access of gfx9-class GPUs
                 const uint32_t hb = 64 * (w >> 4), lb = 2 * (w & 15);
@@ -197,6 +210,37 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     q6ring[I][i][3] = sc.x;
                     q6ring[I][i][4] = sc.y;
                     q6ring[I][i][5] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + 208, 0, 0);
+                }
+            } else if constexpr (TYPE == kQ2_K) {
+                // 84-byte super-blocks: 16 pair bytes, 64 code bytes, d, dmin.
+                // The lane's elements use pair bytes 8 h + w % 16 / 8 + 2 qq
+                // (qq = 0..3): the 8 bytes from 8 h, shifted so that these are
+                // bytes 0, 2, 4, 6; its sub-min is the high nibble of pair byte w.
+                const uint32_t lb = 32 * (w >> 4) + 2 * (w & 15);
+                const uint32_t sh = 8 * ((w >> 3) & 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    q6ring[I][i][0] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + 16 + lb, 0, 0);
+                    const u32x2 pr = __builtin_amdgcn_raw_buffer_load_b64(wr, roff[i] + 8 * (w >> 4), 0, 0);
+                    const uint64_t p64 = ((uint64_t(pr.y) << 32) | pr.x) >> sh;
+                    q6ring[I][i][1] = uint32_t(p64);
+                    q6ring[I][i][2] = uint32_t(p64 >> 32);
+                    q6ring[I][i][3] = __builtin_amdgcn_raw_buffer_load_b8(wr, roff[i] + (w & 15), 0, 0);
+                    q6ring[I][i][5] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 80, 0, 0);
+                }
+            } else {
+                // 110-byte super-blocks: 32 hmask bytes, 64 code bytes, the
+                // 12-byte scale field, d (no load reaches past the block)
+                const uint32_t lb = 2 * (w & 15);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    q6ring[I][i][0] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + lb, 0, 0);
+                    q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + 32 + 32 * (w >> 4) + lb, 0, 0);
+                    const u32x2 f = __builtin_amdgcn_raw_buffer_load_b64(wr, roff[i] + 96, 0, 0);
+                    q6ring[I][i][2] = f.x;
+                    q6ring[I][i][3] = f.y;
+                    q6ring[I][i][4] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 104, 0, 0);
+                    q6ring[I][i][5] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + 108, 0, 0);
                 }
             }
         };
@@ -281,7 +325,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                         *reinterpret_cast<uint2*>(lo_part + o) = make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
                     }
                 }
-            } else {
+            } else if constexpr (TYPE == kQ6_K) {
                 // d of the four rows (word w = 8)
                 if (w == 8)
                     *reinterpret_cast<float4*>(base + S::D_OFF + 4 * r4) =
@@ -317,6 +361,61 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                             make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
                         *reinterpret_cast<uint2*>(lo_part + o) =
                             make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                    }
+                }
+            } else {
+                // Q2_K and Q3_K: one bf16 part. Element l = 2 (w % 16) + e of
+                // quarter qq of half h = w / 16: code bits 2 qq .. of code byte
+                // 32 h + l, sub-scale 8 h + 2 qq + l / 16 (and, for Q3_K, bit
+                // 4 h + qq of hmask byte l).
+                const int h = w >> 4, jl = w & 15;
+                if (w == 8 || (TYPE == kQ2_K && w == 9)) {
+                    float4 v;
+                    if constexpr (TYPE == kQ2_K) {
+                        const int sh = w == 8 ? 0 : 16;
+                        v = make_float4(half_to_f32((q6ring[I][0][5] >> sh) & 0xFFFFu),
+                                        half_to_f32((q6ring[I][1][5] >> sh) & 0xFFFFu),
+                                        half_to_f32((q6ring[I][2][5] >> sh) & 0xFFFFu),
+                                        half_to_f32((q6ring[I][3][5] >> sh) & 0xFFFFu));
+                    } else {
+                        v = make_float4(half_to_f32(q6ring[I][0][5]), half_to_f32(q6ring[I][1][5]),
+                                        half_to_f32(q6ring[I][2][5]), half_to_f32(q6ring[I][3][5]));
+                    }
+                    *reinterpret_cast<float4*>(base + (w == 8 ? S::D_OFF : S::DM_OFF) + 4 * r4) = v;
+                }
+                if constexpr (TYPE == kQ2_K) {
+                    // sub-min m_w (high nibble of pair byte w) of the four rows
+                    if (w < 16) {
+                        float m[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) m[i] = static_cast<float>((q6ring[I][i][3] >> 4) & 15u);
+                        *reinterpret_cast<uint2*>(base + S::M_OFF + w * 16 + 2 * r4) =
+                            make_uint2(bf16_pair(m[0], m[1]), bf16_pair(m[2], m[3]));
+                    }
+                }
+                float* const hi_part = base + S::B_OFF;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        float v[4];
+                        const int si = 8 * h + 2 * qq + (jl >> 3);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (TYPE == kQ2_K) {
+                                const uint32_t q = (q6ring[I][i][0] >> (8 * e + 2 * qq)) & 3u;
+                                const uint32_t sc = (q6ring[I][i][1 + (qq >> 1)] >> (16 * (qq & 1))) & 15u;
+                                v[i] = static_cast<float>(sc * q);
+                            } else {
+                                const int q = int((q6ring[I][i][1] >> (8 * e + 2 * qq)) & 3u) - 4 +
+                                              4 * int((q6ring[I][i][0] >> (8 * e + 4 * h + qq)) & 1u);
+                                const int sc = int(q3_k_scale(q6ring[I][i][2], q6ring[I][i][3], q6ring[I][i][4], si)) - 32;
+                                v[i] = static_cast<float>(sc * q);
+                            }
+                        }
+                        const int col = 128 * h + 32 * qq + 2 * jl + e;
+                        *reinterpret_cast<uint2*>(hi_part + split_b_index(col, r4)) =
+                            make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
                     }
                 }
             }
@@ -387,14 +486,14 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
             // the 8 column blocks in two halves of 4 (operands of one half live)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                bf16x8 bp[4][2];
+                bf16x8 bp[4][kBParts];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
 #pragma unroll
-                    for (int q = 0; q < 2; ++q)
+                    for (int q = 0; q < kBParts; ++q)
                         bp[b][q] = *reinterpret_cast<const bf16x8*>(base + boff[s][4 * half + b] + q * S::B_PART);
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < kBParts; ++q)
 #pragma unroll
                     for (int pa = 0; pa < 3; ++pa)
 #pragma unroll
@@ -404,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
             }
         }
         // min term: t rows 32 wt + 16 a + l % 16, all 32 rows n of the chunk
-        // (n = 8 (l / 16) + 0..7), columns j = l % 16 (8 used)
+        // (n = 8 (l / 16) + 0..7), columns j = l % 16 (kMinCols used)
         if constexpr (kMin) {
             const int n = 8 * (lane >> 4);
             const f32x4 m0 = *reinterpret_cast<const f32x4*>(base + S::DM_OFF + n);
@@ -440,27 +539,29 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         }
     }
 
-    // the min term of the wave's rows, columns (sub-blocks) 0..7, through LDS
-    // (D layout of the 16 x 16 product: lane l, register i holds row
-    // 4 (l / 16) + i, column l % 16); each wave reads back its own rows
-    float* const mins = lds + 32 * 8 * wt;
-    if (kMin && (lane & 15) < 8) {
+    // the min term of the wave's rows, columns (sub-blocks) 0 .. kMinCols - 1,
+    // through LDS (D layout of the 16 x 16 product: lane l, register i holds
+    // row 4 (l / 16) + i, column l % 16); each wave reads back its own rows
+    float* const mins = lds + 32 * 16 * wt;
+    if (kMin && (lane & 15) < kMinCols) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mins[(16 * a + 4 * (lane >> 4) + i) * 8 + (lane & 15)] = accm[a][i];
+            for (int i = 0; i < 4; ++i) mins[(16 * a + 4 * (lane >> 4) + i) * 16 + (lane & 15)] = accm[a][i];
     }
     __syncthreads();
     // D layout of the 32 x 32 product: lane l, register v holds row
-    // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
+    // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32. Column block b is
+    // sub-block b (32 columns) or, for Q2_K, sub-blocks 2b and 2b + 1.
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         const int k = k0 + 32 * b + l32;
+        const int j = kMinCols == 16 ? 2 * b + (l32 >> 4) : b;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int tl = 8 * (v >> 2) + 4 * h + (v & 3);
             const int t = t0 + 32 * wt + tl;
-            if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = kMin ? acc[b][v] - mins[tl * 8 + b] : acc[b][v];
+            if (t < T && k < K) args.dst[(long long)t * args.ldd + k] = kMin ? acc[b][v] - mins[tl * 16 + j] : acc[b][v];
         }
     }
 }

@@ -218,7 +218,7 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
         case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, s, st);
         default: break;
     }
-    if constexpr (TYPE == kQ4_K || TYPE == kQ5_K || TYPE == kQ6_K)
+    if constexpr (kSuperBlock<TYPE>)
         if (variant == RETRO_VARIANT_SPLIT_128x256) return launch_split<TYPE>(W, G, dst, K, N, T, s, st);
     if constexpr (!kSuperBlock<TYPE>) {
         switch (variant) {

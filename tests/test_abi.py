@@ -214,14 +214,16 @@ def test_views_validation_and_choice():
 
 
 def test_split_variant_applies():
-    """The exact-split variant takes Q4_K, Q5_K and Q6_K with G by rows in 16-byte
-    units, and nothing else; it is never the automatic choice."""
+    """The exact-split variant takes the five K-quant types with G by rows in
+    16-byte units, and nothing else; it is never the automatic choice."""
     v = q.VARIANT_SPLIT_128x256
     assert q.variant_applies(v, q.Q4_K, 4096, 14336, 4096)
     assert q.variant_applies(v, q.Q4_K, 256, 36, 5)
     assert not q.variant_applies(v, q.Q4_K, 256, 33, 5)           # G rows of 33 floats
-    assert q.variant_applies(v, q.Q5_K, 4096, 14336, 4096) and q.variant_applies(v, q.Q6_K, 4096, 14336, 4096)
-    for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0, q.Q2_K, q.Q3_K, q.MXFP4):
+    for wtype in (q.Q2_K, q.Q3_K, q.Q5_K, q.Q6_K):
+        assert q.variant_applies(v, wtype, 4096, 14336, 4096)
+        assert not q.variant_applies(v, wtype, 256, 33, 5)
+    for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0, q.Q4_1, q.Q5_0, q.Q5_1, q.MXFP4):
         assert not q.variant_applies(v, wtype, 4096, 4096, 512)
     rb = q.row_bytes(q.Q4_K, 512)
     assert not q.variant_applies_views(v, q.Q4_K, 512, 64, 100, rb, 1, 100, 512)   # G stored t-fastest

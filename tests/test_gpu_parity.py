@@ -256,7 +256,7 @@ def test_empty_reduction_fills_zeros(q, wtype):
         assert np.array_equal(y, np.zeros((T, K), np.float32))
 
 
-@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q4_0, wl.F32, wl.MXFP4])
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q2_K, wl.Q3_K, wl.Q4_0, wl.F32, wl.MXFP4])
 def test_empty_reduction_with_a_row_stride(q, wtype):
     """N = 0 with G an empty view whose row stride is not 0 (torch hands over
     a null pointer for it): every kernel that takes the shape writes zeros and
@@ -265,8 +265,7 @@ def test_empty_reduction_with_a_row_stride(q, wtype):
     W = torch.zeros(0, dtype=torch.uint8, device="cuda")
     for T in (7, 100):
         G = torch.zeros((T, 8), device="cuda")[:, :0]
-        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype in (wl.Q4_K, wl.Q5_K, wl.Q6_K)
-                                                              else []):
+        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype in SPLIT_TYPES else []):
             vid = 0 if v == "auto" else variant_id(q, v)
             if v != "auto" and not q.variant_applies_strided(vid, wtype, K, 0, T, wl.row_bytes(wtype, K), 8, K):
                 continue
@@ -439,13 +438,14 @@ def test_g_columns_match_rows_and_oracle(q, wtype, K, N, T, pad):
         assert "tile" in families and (("ws" in families) == (ldg % 4 == 0 and not dense_odd)), ran
 
 
-# --- exact split on bf16 MFMA (Q4_K, opt-in) -----------------------------------------
+# --- exact split on bf16 MFMA (K-quants, opt-in) -------------------------------------
 
+SPLIT_TYPES = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
 SPLIT_SHAPES = [(200, 76, 768), (130, 96, 512), (67, 36, 256), (150, 100, 768), (5, 40, 256), (129, 300, 512)]
 
 
 @pytest.mark.parametrize("T,N,K", SPLIT_SHAPES)
-@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q5_K, wl.Q6_K])
+@pytest.mark.parametrize("wtype", SPLIT_TYPES)
 def test_split_matches_oracle(q, T, N, K, wtype):
     """The exact-split variant against the oracle at the same bars as the
     F32-input kernels, plus: deterministic, and exactly linear in G (G * 2
@@ -494,10 +494,11 @@ def test_split_strided_batched_and_empty(q):
     assert not empty.any()
 
 
-@pytest.mark.parametrize("name", ["q4_k_n14336_k4096_t4096", "q5_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096"])
+@pytest.mark.parametrize("name", ["q2_k_n14336_k4096_t4096", "q3_k_n14336_k4096_t4096", "q4_k_n14336_k4096_t4096",
+                                  "q5_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096"])
 def test_split_full_size_sampled_rows(q, name):
-    """The large Q4_K and Q6_K workloads through the exact-split kernel, on
-    sampled rows the oracle computes one by one."""
+    """The large K-quant workloads through the exact-split kernel, on sampled
+    rows the oracle computes one by one."""
     c = wl.workload(name)
     W, G = dev(c["W"]), dev(c["G"])
     out = q.out_prod(c["type"], W, G, c["K"], variant=q.VARIANT_SPLIT_128x256)
