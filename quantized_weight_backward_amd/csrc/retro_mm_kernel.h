@@ -418,16 +418,22 @@ __global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWgPerCu)) void mu
 // of k, v_mfma_f32_16x16x4_f32 with M = t, N = W row, K = 4 steps of k.
 // Iteration g of a wave covers k = 64 g .. 64 g + 63: lane l decodes the 16
 // elements 64 g + 16 (l / 16) .. + 15 of row n0 + l % 16 (one MmCodec unit,
-// one header decode) and reads the same 16 x values of row t = l % 16, and
-// round r, step s of the 16 MFMAs uses element 4 r + s. The next
-// iteration's loads are issued before the current one is decoded. Partial
-// sums are added over waves in increasing wave order in LDS.
+// one header decode) and takes the same 16 x values of row t = l % 16, and
+// round r, step s of the 16 MFMAs uses element 4 r + s. x goes through a
+// tile of the wave's own in LDS: loaded with 16 lanes per 256-byte row
+// segment (the MFMA layout would give each lane its own 64-byte region and
+// keep the address unit busy four times as long), then read back in the
+// MFMA layout. The next iteration's loads are issued before the current one
+// is decoded. Partial sums are added over waves in increasing wave order in
+// LDS.
 template <int TYPE>
 __global__ __launch_bounds__(1024) void mul_mat_skinny_kernel(MmSimpleArgs a) {
     using C = MmCodec<TYPE>;
     using F = Format<TYPE>;
     constexpr int NW = 16;
+    constexpr int XP = 68;  // floats per t row of a wave's x tile (64 + 4: conflict-free reads)
     __shared__ __attribute__((aligned(16))) float part[NW * 256];
+    __shared__ __attribute__((aligned(16))) float xtile[NW * 16 * XP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = blockIdx.x * 16;
@@ -442,7 +448,12 @@ __global__ __launch_bounds__(1024) void mul_mat_skinny_kernel(MmSimpleArgs a) {
     const long long x_end = K == 0 ? 0 : (long long)(a.T - 1) * a.ldx + K;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.X, uint32_t(max(0ll, min(4 * x_end, (long long)0x7FFFFFFF))));
     const uint32_t ro = uint32_t(j * a.pitch);
-    const uint32_t xo = uint32_t(j * a.ldx * 4);
+    // x load i of an iteration: row 4 i + l / 16, floats 4 (l % 16) .. + 3
+    // of the iteration's 64
+    uint32_t xo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xo[i] = uint32_t(((4 * i + kk) * a.ldx + 4 * j) * 4);
+    float* const xt = xtile + wave * 16 * XP;
     const int groups = (K + 63) / 64;
 
     uint32_t wraw[2][C::WORDS];
@@ -454,21 +465,32 @@ __global__ __launch_bounds__(1024) void mul_mat_skinny_kernel(MmSimpleArgs a) {
         const int k = 64 * g + 16 * kk;
         C::fetch(wr, ro, k, wraw[S]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xraw[S][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 4u * k + 16u * i, 0, 0);
+        for (int i = 0; i < 4; ++i) xraw[S][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i] + 256u * g, 0, 0);
     };
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](auto slot, int g) {
         constexpr int S = decltype(slot)::value;
         const int k = 64 * g + 16 * kk;
         float e[16], xv[16];
-        C::decode(wraw[S], k, e);
+        // the x tile through LDS; the fences keep the wave's LDS accesses in
+        // program order (the previous iteration's reads before these writes,
+        // these writes before the reads below)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xt + (4 * i + kk) * XP + 4 * j) = xraw[S][i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            xv[4 * i] = __uint_as_float(xraw[S][i].x);
-            xv[4 * i + 1] = __uint_as_float(xraw[S][i].y);
-            xv[4 * i + 2] = __uint_as_float(xraw[S][i].z);
-            xv[4 * i + 3] = __uint_as_float(xraw[S][i].w);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(xt + j * XP + 16 * kk + 4 * i);
+            xv[4 * i] = v[0];
+            xv[4 * i + 1] = v[1];
+            xv[4 * i + 2] = v[2];
+            xv[4 * i + 3] = v[3];
         }
+        C::decode(wraw[S], k, e);
         if (k + 16 > K) {  // elements at or past K: zero on both sides
 #pragma unroll
             for (int i = 0; i < 16; ++i)
