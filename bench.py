@@ -335,6 +335,35 @@ def main() -> int:
                  "bf16_mfma_frac": round(issued / avg_split / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "speedup_vs_f32_kernel": round(avg_large / avg_split, 3)}
 
+    # Measured ceilings on this GPU, timed after the rest: MFMA-only loops
+    # (no memory traffic) for the F32-input and bf16 instructions, and a
+    # 16-byte device copy of 1 GiB (2 GiB over HBM).
+    def timed(launch, reps=5):
+        launch()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in ev:
+            e[0].record(stream)
+            launch()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+
+    sink = q.probe_sink(dev)
+    f32_fl = q.probe_mfma(q.PROBE_MFMA_F32, sink, 4096)
+    mfma_f32 = f32_fl / timed(lambda: q.probe_mfma(q.PROBE_MFMA_F32, sink, 4096)) / 1e12
+    bf16_fl = q.probe_mfma(q.PROBE_MFMA_BF16, sink, 4096)
+    mfma_bf16 = bf16_fl / timed(lambda: q.probe_mfma(q.PROBE_MFMA_BF16, sink, 4096)) / 1e12
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    copy_gbs = 2.0 * csrc.numel() * 4 / timed(lambda: q.probe_copy(csrc, cdst)) / 1e9
+    del csrc, cdst, sink
+    ceilings = {"kind": "measured on this GPU: MFMA-only loops (no memory), 16-byte copy of 1 GiB",
+                "mfma_f32_tflops": round(mfma_f32, 2), "mfma_bf16_tflops": round(mfma_bf16, 1),
+                "copy_gbs": round(copy_gbs, 1),
+                "mfma_f32_clock_ghz": round(mfma_f32 / PEAK_F32_TFLOPS * 2.4, 3)}
+    if split is not None:
+        split["bf16_mfma_frac_of_measured"] = round(split["bf16_flops_issued_per_launch"] / avg_split / 1e12 / mfma_bf16, 4)
+
     skinny_tflops = fl_skinny / avg_skinny / 1e12
     skinny_gbs = wbytes / avg_skinny / 1e9
     t_roof = max(wbytes / (PEAK_HBM_GBS * 1e9), fl_skinny / (PEAK_F32_TFLOPS * 1e12))
@@ -359,6 +388,7 @@ def main() -> int:
                               "kernel": q.VARIANT_NAMES[v_skinny], "w_copies_rotated": n_rot}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 4),
+                     "frac_of_measured": round(achieved / mfma_f32, 4),
                      "traffic": traffic,
                      "kernel": f"{kernel_family(q.VARIANT_NAMES[v_large])} ({q.VARIANT_NAMES[v_large]})",
                      "avg_launch_ms": round(avg_large * 1e3, 4), "min_launch_ms": round(float(t_large.min()) * 1e3, 4),
@@ -369,9 +399,12 @@ def main() -> int:
                    "tflops": round(skinny_tflops, 3), "weight_gbs": round(skinny_gbs, 1),
                    "hbm_frac": round(skinny_gbs / PEAK_HBM_GBS, 4),
                    "f32_mfma_frac": round(skinny_tflops / PEAK_F32_TFLOPS, 4),
+                   "f32_mfma_frac_of_measured": round(skinny_tflops / mfma_f32, 4),
+                   "hbm_frac_of_measured_copy": round(skinny_gbs / copy_gbs, 4),
                    "binding_roof_frac": round(t_roof / avg_skinny, 4),
                    "weight_bytes": wbytes},
         "exact_split": split,
+        "ceilings": ceilings,
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -59,14 +59,19 @@ VARIANT_NAMES = {
 
 LIB_PATH = _build.LIB_PATH
 
-# The exported symbols, as declared in include/retro_out_prod.h.
+# The exported symbols, as declared in include/retro_out_prod.h and
+# include/retro_probe.h.
 EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided", "retro_out_prod_strided_variant",
            "retro_dequantize", "retro_out_prod_supported", "retro_out_prod_choice", "retro_out_prod_variant_applies",
            "retro_out_prod_strided_variant_applies", "retro_out_prod_batched", "retro_out_prod_batched_variant",
            "retro_out_prod_views", "retro_out_prod_views_variant", "retro_out_prod_views_variant_applies",
            "retro_out_prod_views_choice",
            "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
-           "retro_row_bytes", "retro_strerror")
+           "retro_row_bytes", "retro_strerror",
+           "retro_probe_sink_floats", "retro_probe_mfma", "retro_probe_copy")
+
+PROBE_MFMA_F32 = 0
+PROBE_MFMA_BF16 = 1
 
 
 def _load() -> ctypes.CDLL:
@@ -120,6 +125,12 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod_variant_applies.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_row_bytes.restype = i64
     lib.retro_row_bytes.argtypes = [i32, i64]
+    lib.retro_probe_sink_floats.restype = i64
+    lib.retro_probe_sink_floats.argtypes = []
+    lib.retro_probe_mfma.restype = i32
+    lib.retro_probe_mfma.argtypes = [i32, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
+    lib.retro_probe_copy.restype = i32
+    lib.retro_probe_copy.argtypes = [vp, vp, i64, vp]
     lib.retro_strerror.restype = ctypes.c_char_p
     lib.retro_strerror.argtypes = [i32]
     return lib
@@ -350,6 +361,33 @@ def mul_mat_choice(wtype: int, K: int, N: int, T: int) -> int:
 
 def mul_mat_variant_applies(variant: int, wtype: int, K: int, N: int, T: int) -> bool:
     return lib.retro_mul_mat_variant_applies(int(variant), int(wtype), int(K), int(N), int(T)) == 1
+
+
+def probe_sink(device=None):
+    """A float32 device buffer of the size the matrix-core probe writes."""
+    return torch.empty(int(lib.retro_probe_sink_floats()), dtype=torch.float32, device=device or "cuda")
+
+
+def probe_mfma(kind: int, sink, iterations: int, stream=None) -> float:
+    """Enqueue the matrix-core probe (PROBE_MFMA_F32 or PROBE_MFMA_BF16);
+    returns the FLOPs of the launch."""
+    _device_tensor(sink, "sink")
+    if sink.dtype != torch.float32 or sink.numel() < int(lib.retro_probe_sink_floats()):
+        raise ValueError("sink must be a float32 buffer of retro_probe_sink_floats() elements")
+    flops = ctypes.c_double(0.0)
+    _check(lib.retro_probe_mfma(int(kind), _ptr(sink), int(iterations), ctypes.byref(flops), _stream_handle(stream)))
+    return flops.value
+
+
+def probe_copy(src, dst, stream=None) -> None:
+    """Enqueue the copy probe: dst = src, two contiguous device tensors of the
+    same number of bytes (a multiple of 16)."""
+    _device_tensor(src, "src")
+    _device_tensor(dst, "dst")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _check(lib.retro_probe_copy(_ptr(src), _ptr(dst), n, _stream_handle(stream)))
 
 
 def dequantize(wtype: int, W, K: int, N: int, out=None, stream=None):

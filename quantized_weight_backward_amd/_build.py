@@ -2,8 +2,8 @@
 
 The kernels of each weight type are compiled into an object of their own
 (retro_unit.hip with -DRETRO_UNIT_TYPE=<type id>) and the C ABI into another
-(retro_api.hip); the objects are built in parallel and linked into one
-shared library.
+(retro_api.hip), the measured-ceiling probes into a third (retro_probe.hip);
+the objects are built in parallel and linked into one shared library.
 """
 
 from __future__ import annotations
@@ -21,6 +21,7 @@ LIB_NAME = "libretro_out_prod.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 API_SOURCE = os.path.join(CSRC, "retro_api.hip")
 UNIT_SOURCE = os.path.join(CSRC, "retro_unit.hip")
+PROBE_SOURCE = os.path.join(CSRC, "retro_probe.hip")
 # GGUF ids of the weight types, one kernel object each
 UNIT_TYPES = {"f32": 0, "f16": 1, "q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q2_k": 10, "q3_k": 11,
               "q4_k": 12, "q5_k": 13, "q6_k": 14, "bf16": 30, "mxfp4": 39}
@@ -46,7 +47,7 @@ def hipcc() -> str:
 
 def _jobs() -> int:
     limit = int(os.environ.get("MAX_JOBS", "16") or 16)
-    return max(1, min(limit, os.cpu_count() or 1, len(UNIT_TYPES) + 1))
+    return max(1, min(limit, os.cpu_count() or 1, len(UNIT_TYPES) + 2))
 
 
 def _run(cmd: list[str]) -> str:
@@ -61,7 +62,8 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source into LIB_PATH (always recompiles)."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     base = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c"]
-    jobs = [(os.path.join(OBJ_DIR, "retro_api.o"), [API_SOURCE])]
+    jobs = [(os.path.join(OBJ_DIR, "retro_api.o"), [API_SOURCE]),
+            (os.path.join(OBJ_DIR, "retro_probe.o"), [PROBE_SOURCE])]
     for name, tid in UNIT_TYPES.items():
         jobs.append((os.path.join(OBJ_DIR, f"retro_unit_{name}.o"), [f"-DRETRO_UNIT_TYPE={tid}", UNIT_SOURCE]))
     with ThreadPoolExecutor(max_workers=_jobs()) as pool:

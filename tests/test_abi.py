@@ -2,6 +2,7 @@
 declares, and every validation path returns its error before touching a
 device."""
 
+import glob
 import os
 import re
 
@@ -13,12 +14,15 @@ from conftest import REPO
 q = pytest.importorskip("quantized_weight_backward_amd")  # raises if the library is missing
 
 HEADER = os.path.join(REPO, "include", "retro_out_prod.h")
+HEADERS = sorted(glob.glob(os.path.join(REPO, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(retro_\w+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(retro_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_is_the_in_tree_build():
@@ -319,3 +323,22 @@ def test_python_binding_rejects_host_tensors():
 
     with pytest.raises(ValueError):
         q.out_prod(q.F32, torch.zeros(16, dtype=torch.uint8), torch.zeros(1, 4), 1)
+
+
+def test_probe_validation():
+    """The measured-ceiling probes refuse bad arguments before any launch."""
+    mfma, copy = q.lib.retro_probe_mfma, q.lib.retro_probe_copy
+    assert q.lib.retro_probe_sink_floats() == 2048 * 256
+    # (kind, sink, iterations, flops, stream)
+    assert mfma(2, 0x100000, 10, None, None) == q.E_TYPE
+    assert mfma(q.PROBE_MFMA_F32, 0x100000, 0, None, None) == q.E_SHAPE
+    assert mfma(q.PROBE_MFMA_BF16, 0x100000, (1 << 20) + 1, None, None) == q.E_SHAPE
+    assert mfma(q.PROBE_MFMA_F32, None, 10, None, None) == q.E_NULL
+    assert mfma(q.PROBE_MFMA_F32, 0x100002, 10, None, None) == q.E_ALIGN
+    # (src, dst, bytes, stream)
+    assert copy(0x100000, 0x200000, -16, None) == q.E_SHAPE
+    assert copy(0x100000, 0x200000, 24, None) == q.E_SHAPE
+    assert copy(None, None, 0, None) == q.OK
+    assert copy(None, 0x200000, 16, None) == q.E_NULL
+    assert copy(0x100008, 0x200000, 16, None) == q.E_ALIGN
+    assert copy(0x100000, 0x100010, 64, None) == q.E_ALIAS
