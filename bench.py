@@ -203,7 +203,14 @@ def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
     oracle.out_prod(case["type"], case["W"], case["G"], K, rows=rows, nthreads=cores)
     secs = time.perf_counter() - t0
     flops = 2.0 * N * K * nrows
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "host_cpu": model, "host_threads": os.cpu_count(),
             "sample": f"{nrows} of {case['T']} t rows of {LARGE} (full decode of W included), "
                       f"{secs:.1f} s"}
 
