@@ -207,6 +207,15 @@ const char *retro_strerror(int code);
  *                           by the matrix core's F32 addition (it truncates).
  *                           Within the same error bars (tests), 1.7x to 2.7x
  *                           the rate. G by rows with ldg % 4 == 0.
+ *   RETRO_VARIANT_SPLIT_128x128  the same form on a 128 x 128 tile for Q4_0,
+ *                           Q5_0, MXFP4, BF16 and F16, never chosen
+ *                           automatically: the decoded weight v (d (q - 8),
+ *                           d (q - 16), the E2M1 value times its scale, or
+ *                           the weight itself) is exact in F32 with at most
+ *                           16 significant bits, so it is cut into one bf16
+ *                           part (BF16, MXFP4) or two, and G itself into
+ *                           three. G by rows with ldg % 4 == 0; BF16 and F16
+ *                           rows 16-byte aligned (row pitch % 16 == 0).
  */
 enum {
     RETRO_VARIANT_AUTO = 0,
@@ -224,7 +233,8 @@ enum {
     RETRO_VARIANT_WS_32x128 = 12,
     RETRO_VARIANT_WS2_64x128 = 13,
     RETRO_VARIANT_SIMPLE = 15,
-    RETRO_VARIANT_SPLIT_128x256 = 16
+    RETRO_VARIANT_SPLIT_128x256 = 16,
+    RETRO_VARIANT_SPLIT_128x128 = 17
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the

@@ -180,6 +180,14 @@ bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, con
         Geometry g;
         return geometry(type, g) && g.block == 256 && !s.gcols && tile_applies(tile, type, K, N, T, s);
     }
+    if (variant == RETRO_VARIANT_SPLIT_128x128) {
+        // the 128 x 128 tile of the 32-element block types and the 16-bit
+        // dense types, G by rows; dense rows are read in 16-byte units
+        constexpr TileVariant tile{RETRO_VARIANT_SPLIT_128x128, 128, 128, 1.0, true};
+        const bool typed = type == RETRO_Q4_0 || type == RETRO_Q5_0 || type == RETRO_MXFP4 ||
+                           type == RETRO_BF16 || type == RETRO_F16;
+        return typed && !s.gcols && (!is_dense(type) || s.ldw % 16 == 0) && tile_applies(tile, type, K, N, T, s);
+    }
     const TileVariant* tv = find_tile(variant);
     return tv && tile_applies(*tv, type, K, N, T, s);
 }

@@ -4,7 +4,8 @@
 // below for Q4_K; Q5_K adds a fifth code bit (v < 2048), Q6_K has
 // v = sc*(q - 32) and no min term, Q2_K has v = sc*q <= 45 (one bf16 part) and
 // 16 sub-blocks of mins, Q3_K has v = (sc - 32)*q' with |v| <= 128 (one part)
-// and no min term.
+// and no min term. For Q4_0, Q5_0, MXFP4, BF16 and F16 v is the decoded weight
+// itself (at most 16 significant bits), A = G, on a 128-column tile.
 //
 // A Q4_K element of row n, sub-block j of a super-block is
 // d*sc_j*q - dmin*m_j (q a nibble, sc_j and m_j 6-bit integers, d and dmin
@@ -45,10 +46,19 @@ namespace retro {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// The weight types the exact split takes, and its tile width: whole
+// super-blocks (256 columns) for the K-quants, 128 columns (four 32-element
+// blocks, or dense columns) for the others.
+template <int TYPE>
+constexpr bool kSplitNarrow = TYPE == kQ4_0 || TYPE == kQ5_0 || TYPE == kMXFP4 || TYPE == kBF16 || TYPE == kF16;
+template <int TYPE>
+constexpr int kSplitBK = kSuperBlock<TYPE> ? 256 : 128;
+
+template <int BK_>
 struct SplitShape {
     static constexpr int kPThreads = 256;
     static constexpr int kThreads = 512;
-    static constexpr int BT = 128, BK = 256, BN = 32;
+    static constexpr int BT = 128, BK = BK_, BN = 32;
     static constexpr int GP = BN + 4;          // floats per t row of G
     static constexpr int G_FLOATS = BT * GP;   // 4608
     static constexpr int D_OFF = G_FLOATS;     // d of the chunk's 32 rows
@@ -101,18 +111,24 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& 
 
 template <int TYPE>
 __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
-    static_assert(kSuperBlock<TYPE>, "exact split is built for the K-quants");
+    static_assert(kSuperBlock<TYPE> || kSplitNarrow<TYPE>, "no exact split for this type");
+    constexpr bool kKQ = kSuperBlock<TYPE>;
     // sub-blocks of the min term per super-block (Q3_K and Q6_K values have none)
     constexpr int kMinCols = (TYPE == kQ4_K || TYPE == kQ5_K) ? 8 : TYPE == kQ2_K ? 16 : 0;
     constexpr bool kMin = kMinCols > 0;
     // bf16 parts of v: two for Q4_K, Q5_K (v < 2048) and Q6_K (|v| <= 4096),
-    // one for Q2_K (v <= 45) and Q3_K (|v| <= 128)
-    constexpr int kBParts = (TYPE == kQ2_K || TYPE == kQ3_K) ? 1 : 2;
+    // one for Q2_K (v <= 45) and Q3_K (|v| <= 128). For the other types v is
+    // the weight itself: one part for BF16 and MXFP4 (at most 2 significant
+    // bits), two for F16 (11), Q4_0 (d (q - 8): 15) and Q5_0 (d (q - 16): 16).
+    constexpr int kBParts = (TYPE == kQ2_K || TYPE == kQ3_K || TYPE == kBF16 || TYPE == kMXFP4) ? 1 : 2;
+    // the K-quants take A = fl(G d) per super-block; the others A = G
+    constexpr bool kScaleA = kKQ;
     constexpr bool kQ45 = TYPE == kQ4_K || TYPE == kQ5_K;
     constexpr uint32_t kCodes = TYPE == kQ5_K ? 48 : 16;  // first code byte of a super-block
-    using S = SplitShape;
+    using S = SplitShape<kSplitBK<TYPE>>;
     using F = Format<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP;
+    constexpr int NB = BK / 32;  // 32-column blocks of the tile
 
     __shared__ __attribute__((aligned(16))) float lds[2 * S::BUF_FLOATS];
 
@@ -148,8 +164,13 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         // the same plus 32, of sub-block 2 (w / 8) + 1)
         // Q6_K instead: half h = w / 16 of the super-block, elements
         // l = 2 (w % 16) + e (e = 0, 1) of its four quarters qq: columns
-        // 128 h + 32 qq + l
-        const int r4 = p >> 5, w = p & 31;
+        // 128 h + 32 qq + l.
+        // The 128-column types: threads p < 128 only (waves 4 and 5), rows
+        // 4 r4 .. + 3 with r4 = p / 16, and w = p % 16: code word w % 4 of
+        // block w / 4 (columns 32 (w / 4) + 4 (w % 4) + 0..3 and the same
+        // plus 16), or dense columns 8 w .. 8 w + 7.
+        const int r4 = kKQ ? p >> 5 : (p >> 4) & 7, w = kKQ ? p & 31 : p & 15;
+        const bool wact = kKQ || p < 128;  // uniform per wave
         uint32_t roff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) roff[i] = uint32_t((4 * r4 + i) * args.pitch);
@@ -166,7 +187,9 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         uint32_t fring[R][4];     // Q5_K, per row: the fifth-bit bytes of the code word's elements
         // Q6_K, per row: ql bytes (quarters 0, 2), (1, 3), qh bytes, 8 scales, d;
         // Q2_K: qs bytes, the 16 pair bytes, d | dmin << 16;
-        // Q3_K: hmask bytes, qs bytes, the 12-byte scale field, d
+        // Q3_K: hmask bytes, qs bytes, the 12-byte scale field, d;
+        // Q4_0, Q5_0, MXFP4: the code word, d or the scale byte, the fifth
+        // bits; BF16, F16: the row's 8 columns
         uint32_t q6ring[R][4][6];
 
         auto load_chunk = [&](auto slot, int n0) __attribute__((always_inline)) {
@@ -228,7 +251,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     q6ring[I][i][3] = __builtin_amdgcn_raw_buffer_load_b8(wr, roff[i] + (w & 15), 0, 0);
                     q6ring[I][i][5] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 80, 0, 0);
                 }
-            } else {
+            } else if constexpr (TYPE == kQ3_K) {
                 // 110-byte super-blocks: 32 hmask bytes, 64 code bytes, the
                 // 12-byte scale field, d (no load reaches past the block)
                 const uint32_t lb = 2 * (w & 15);
@@ -241,6 +264,38 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                     q6ring[I][i][3] = f.y;
                     q6ring[I][i][4] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + 104, 0, 0);
                     q6ring[I][i][5] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + 108, 0, 0);
+                }
+            } else if constexpr (kNibbleLayout<TYPE>) {
+                // Q4_0 (18-byte blocks: d, 16 code bytes), Q5_0 (22 bytes: d,
+                // the 4 fifth-bit bytes, 16 code bytes), MXFP4 (17 bytes: the
+                // scale byte, 16 code bytes): 2- or 1-byte aligned blocks,
+                // read with unaligned buffer loads. Per row: the code word,
+                // d (or the scale byte), the fifth bits.
+                if (wact) {
+                    const uint32_t blk = uint32_t(F::kBytes) * uint32_t(w >> 2);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        q6ring[I][i][0] =
+                            __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + blk + kHeader<TYPE> + 4 * (w & 3), 0, 0);
+                        if constexpr (TYPE == kMXFP4)
+                            q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b8(wr, roff[i] + blk, 0, 0);
+                        else
+                            q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + blk, 0, 0);
+                        if constexpr (TYPE == kQ5_0)
+                            q6ring[I][i][2] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + blk + 2, 0, 0);
+                    }
+                }
+            } else {
+                // BF16, F16: columns 8 w .. 8 w + 7 of each row, one 16-byte load
+                if (wact) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, roff[i] + 16 * w, 0, 0);
+                        q6ring[I][i][0] = v.x;
+                        q6ring[I][i][1] = v.y;
+                        q6ring[I][i][2] = v.z;
+                        q6ring[I][i][3] = v.w;
+                    }
                 }
             }
         };
@@ -363,7 +418,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                             make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
                     }
                 }
-            } else {
+            } else if constexpr (TYPE == kQ2_K || TYPE == kQ3_K) {
                 // Q2_K and Q3_K: one bf16 part. Element l = 2 (w % 16) + e of
                 // quarter qq of half h = w / 16: code bits 2 qq .. of code byte
                 // 32 h + l, sub-scale 8 h + 2 qq + l / 16 (and, for Q3_K, bit
@@ -418,6 +473,88 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                             make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
                     }
                 }
+            } else if constexpr (kNibbleLayout<TYPE>) {
+                // v = d (q - 8) (Q4_0), d (q - 16) (Q5_0, q with its fifth bit)
+                // or the E2M1 value times the scale (MXFP4), exact in F32;
+                // byte e of the code word holds elements 4 (w % 4) + e (low
+                // nibble) and that plus 16 (high nibble) of block w / 4
+                if (wact) {
+                    const int blk = w >> 2, wb = w & 3;
+                    float* const hi_part = base + S::B_OFF;
+                    float* const lo_part = hi_part + S::B_PART;
+                    float lo[4][4], hv[4][4];  // [row][byte]: low- and high-nibble values
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t cw = q6ring[I][i][0];
+                        if constexpr (TYPE == kMXFP4) {
+                            mxfp4_x8(cw, mx_scale(q6ring[I][i][1]), lo[i], hv[i]);
+                        } else {
+                            const float d = half_to_f32(q6ring[I][i][1] & 0xFFFFu);
+                            constexpr int kOff = TYPE == kQ5_0 ? 16 : 8;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                int ql = int((cw >> (8 * e)) & 15u), qhi = int((cw >> (8 * e + 4)) & 15u);
+                                if constexpr (TYPE == kQ5_0) {
+                                    const uint32_t qh = q6ring[I][i][2];
+                                    ql |= int((qh >> (4 * wb + e)) & 1u) << 4;
+                                    qhi |= int((qh >> (16 + 4 * wb + e)) & 1u) << 4;
+                                }
+                                lo[i][e] = d * static_cast<float>(ql - kOff);
+                                hv[i][e] = d * static_cast<float>(qhi - kOff);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float vh[4], vl[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = half ? hv[i][e] : lo[i][e];
+                                vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+                                vl[i] = v - vh[i];
+                            }
+                            const int o = split_b_index(32 * blk + 16 * half + 4 * wb + e, r4);
+                            *reinterpret_cast<uint2*>(hi_part + o) =
+                                make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
+                            if constexpr (kBParts == 2)
+                                *reinterpret_cast<uint2*>(lo_part + o) =
+                                    make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                        }
+                    }
+                }
+            } else {
+                // BF16: the weights are the bf16 operand (halfword e % 2 of
+                // word e / 2 of each row); F16: exact in F32, split as hi =
+                // its top 8 significant bits and lo = the rest (at most 3)
+                if (wact) {
+                    float* const hi_part = base + S::B_OFF;
+                    float* const lo_part = hi_part + S::B_PART;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int o = split_b_index(8 * w + e, r4);
+                        const int wd = e >> 1;
+                        if constexpr (TYPE == kBF16) {
+                            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                            *reinterpret_cast<uint2*>(hi_part + o) =
+                                make_uint2(__builtin_amdgcn_perm(q6ring[I][1][wd], q6ring[I][0][wd], sel),
+                                           __builtin_amdgcn_perm(q6ring[I][3][wd], q6ring[I][2][wd], sel));
+                        } else {
+                            float vh[4], vl[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = half_to_f32((q6ring[I][i][wd] >> (16 * (e & 1))) & 0xFFFFu);
+                                vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+                                vl[i] = v - vh[i];
+                            }
+                            *reinterpret_cast<uint2*>(hi_part + o) =
+                                make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
+                            *reinterpret_cast<uint2*>(lo_part + o) =
+                                make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                        }
+                    }
+                }
             }
         };
 
@@ -442,12 +579,12 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
     }
 
     // ---------------- consumer ----------------
-    // wave w: tile rows 32 w .. 32 w + 31, all 256 columns (8 blocks of 32)
+    // wave w: tile rows 32 w .. 32 w + 31, all BK columns (NB blocks of 32)
     const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int wt = wave;
-    f32x16 acc[8];
+    f32x16 acc[NB];
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
     f32x4 accm[2];
@@ -455,11 +592,11 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
     for (int a = 0; a < 2; ++a) accm[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // B operand offsets (floats) of the lane's columns, per k-step s
-    int boff[2][8];
+    int boff[2][NB];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < NB; ++b) {
             const int col = 32 * b + l32;
             boff[s][b] = S::B_OFF + col * 16 + 4 * ((2 * s + h) ^ ((col >> 2) & 3));
         }
@@ -470,22 +607,29 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
             const int n = 16 * s + 8 * h;
             bf16x8 ap[3];
             {
-                const f32x4 d0 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n);
-                const f32x4 d1 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n + 4);
                 const float* g = base + (32 * wt + l32) * GP + n;
                 const f32x4 g0 = *reinterpret_cast<const f32x4*>(g);
                 const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + 4);
                 float x[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    x[e] = g0[e] * d0[e];
-                    x[4 + e] = g1[e] * d1[e];
+                    x[e] = g0[e];
+                    x[4 + e] = g1[e];
+                }
+                if constexpr (kScaleA) {
+                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(base + S::D_OFF + n + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] *= d0[e];
+                        x[4 + e] *= d1[e];
+                    }
                 }
                 split3(x, ap[0], ap[1], ap[2]);
             }
-            // the 8 column blocks in two halves of 4 (operands of one half live)
+            // the column blocks in groups of 4 (operands of one group live)
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
+            for (int half = 0; half < NB / 4; ++half) {
                 bf16x8 bp[4][kBParts];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
@@ -554,7 +698,7 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
     // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32. Column block b is
     // sub-block b (32 columns) or, for Q2_K, sub-blocks 2b and 2b + 1.
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < NB; ++b) {
         const int k = k0 + 32 * b + l32;
         const int j = kMinCols == 16 ? 2 * b + (l32 >> 4) : b;
 #pragma unroll

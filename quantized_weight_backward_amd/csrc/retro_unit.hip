@@ -116,7 +116,7 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
 template <int TYPE>
 int launch_split(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
                  hipStream_t st) {
-    using S = SplitShape;
+    using S = SplitShape<kSplitBK<TYPE>>;
     TileArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.G = G;
@@ -220,6 +220,8 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
     }
     if constexpr (kSuperBlock<TYPE>)
         if (variant == RETRO_VARIANT_SPLIT_128x256) return launch_split<TYPE>(W, G, dst, K, N, T, s, st);
+    if constexpr (kSplitNarrow<TYPE>)
+        if (variant == RETRO_VARIANT_SPLIT_128x128) return launch_split<TYPE>(W, G, dst, K, N, T, s, st);
     if constexpr (!kSuperBlock<TYPE>) {
         switch (variant) {
             case RETRO_VARIANT_TILE_128x128: return launch_tile<TYPE, 2, 2, 2, 2>(W, G, dst, K, N, T, s, st);

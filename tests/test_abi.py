@@ -234,6 +234,21 @@ def test_split_variant_applies():
     assert q.variant_applies_views(v, q.Q4_K, 512, 64, 100, rb, 68, 1, 512)
     for T in (1, 16, 17, 4096):
         assert q.choice(q.Q4_K, 4096, 14336, T) != v
+    # the 128-column tile: the 32-element block types with an exact decoded
+    # value of at most 16 bits, and the 16-bit dense types with 16-byte rows
+    v2 = q.VARIANT_SPLIT_128x128
+    for wtype in (q.Q4_0, q.Q5_0, q.MXFP4, q.BF16, q.F16):
+        assert q.variant_applies(v2, wtype, 5120, 17408, 2048)
+        assert q.variant_applies(v2, wtype, 352, 64, 140)            # partial last tile
+        assert not q.variant_applies(v2, wtype, 5120, 33, 2048)      # G rows of 33 floats
+        assert q.choice(wtype, 5120, 17408, 2048) != v2
+    for wtype in (q.F32, q.Q8_0, q.Q4_1, q.Q5_1, q.Q4_K, q.Q6_K):
+        assert not q.variant_applies(v2, wtype, 4096, 4096, 512)
+    for wtype in (q.Q4_0, q.BF16):
+        assert not q.variant_applies(v, wtype, 4096, 4096, 512)
+    rb = q.row_bytes(q.BF16, 64)
+    assert q.variant_applies_views(v2, q.BF16, 64, 64, 100, rb, 68, 1, 64)
+    assert not q.variant_applies_views(v2, q.BF16, 64, 64, 100, rb + 8, 68, 1, 64)  # rows 8-byte aligned
 
 
 def test_mul_mat_validation_and_choice():

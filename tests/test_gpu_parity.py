@@ -265,7 +265,7 @@ def test_empty_reduction_with_a_row_stride(q, wtype):
     W = torch.zeros(0, dtype=torch.uint8, device="cuda")
     for T in (7, 100):
         G = torch.zeros((T, 8), device="cuda")[:, :0]
-        for v in ["auto", "skinny"] + tile_variants(wtype) + (["split_128x256"] if wtype in SPLIT_TYPES else []):
+        for v in ["auto", "skinny"] + tile_variants(wtype) + ([SPLIT_VARIANT[wtype]] if wtype in SPLIT_VARIANT else []):
             vid = 0 if v == "auto" else variant_id(q, v)
             if v != "auto" and not q.variant_applies_strided(vid, wtype, K, 0, T, wl.row_bytes(wtype, K), 8, K):
                 continue
@@ -440,24 +440,33 @@ def test_g_columns_match_rows_and_oracle(q, wtype, K, N, T, pad):
 
 # --- exact split on bf16 MFMA (K-quants, opt-in) -------------------------------------
 
-SPLIT_TYPES = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
+# the exact-split variant of each type it takes: 256-column tiles for the
+# K-quants, 128-column tiles for the 32-element block types and 16-bit dense
+SPLIT_VARIANT = {**{t: "split_128x256" for t in (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)},
+                 **{t: "split_128x128" for t in (wl.Q4_0, wl.Q5_0, wl.MXFP4, wl.BF16, wl.F16)}}
+SPLIT_TYPES = tuple(SPLIT_VARIANT)
 SPLIT_SHAPES = [(200, 76, 768), (130, 96, 512), (67, 36, 256), (150, 100, 768), (5, 40, 256), (129, 300, 512)]
+# 128-column tiles: K a whole number of blocks but not of tiles (a partial last tile)
+NARROW_SHAPES = [(140, 64, 352), (33, 100, 160)]
 
 
-@pytest.mark.parametrize("T,N,K", SPLIT_SHAPES)
+@pytest.mark.parametrize("T,N,K", SPLIT_SHAPES + NARROW_SHAPES)
 @pytest.mark.parametrize("wtype", SPLIT_TYPES)
 def test_split_matches_oracle(q, T, N, K, wtype):
     """The exact-split variant against the oracle at the same bars as the
     F32-input kernels, plus: deterministic, and exactly linear in G (G * 2
     doubles every output bit for bit: the parts of fl(2 G d) are twice those
     of fl(G d), and the matrix core's truncation scales with them)."""
+    variant = SPLIT_VARIANT[wtype]
+    if K % 256 and variant == "split_128x256":
+        pytest.skip("K-quant rows are whole super-blocks")
     c = wl.make_case(wtype, N, K, T, seed=1400 + T)
-    assert q.variant_applies(q.VARIANT_SPLIT_128x256, wtype, K, N, T)
+    assert q.variant_applies(variant_id(q, variant), wtype, K, N, T)
     _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
-    y = run(q, c, "split_128x256")
+    y = run(q, c, variant)
     e = check_close(y, acc, ab, "split")
-    assert np.array_equal(run(q, c, "split_128x256", prefill=1e30).view(np.uint32), y.view(np.uint32))
-    two = run(q, dict(c, G=c["G"] * np.float32(2)), "split_128x256")
+    assert np.array_equal(run(q, c, variant, prefill=1e30).view(np.uint32), y.view(np.uint32))
+    two = run(q, dict(c, G=c["G"] * np.float32(2)), variant)
     assert np.array_equal(two, 2 * y)
     print(f"split {wl.TYPE_NAMES[wtype]} T={T} N={N} K={K}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
 
@@ -494,15 +503,18 @@ def test_split_strided_batched_and_empty(q):
     assert not empty.any()
 
 
-@pytest.mark.parametrize("name", ["q2_k_n14336_k4096_t4096", "q3_k_n14336_k4096_t4096", "q4_k_n14336_k4096_t4096",
-                                  "q5_k_n14336_k4096_t4096", "q6_k_n14336_k4096_t4096"])
-def test_split_full_size_sampled_rows(q, name):
-    """The large K-quant workloads through the exact-split kernel, on sampled
-    rows the oracle computes one by one."""
-    c = wl.workload(name)
+@pytest.mark.parametrize("name,wtype", [(n, None) for n in (
+    "q2_k_n14336_k4096_t4096", "q3_k_n14336_k4096_t4096", "q4_k_n14336_k4096_t4096", "q5_k_n14336_k4096_t4096",
+    "q6_k_n14336_k4096_t4096", "q4_0_n17408_k5120_t2048", "q5_0_n17408_k5120_t2048", "mxfp4_n17408_k5120_t2048")] +
+    [("dense_n4096_k4096_t512", wl.BF16), ("dense_n4096_k4096_t512", wl.F16)])
+def test_split_full_size_sampled_rows(q, name, wtype):
+    """The large workloads of every type the exact split takes, through it,
+    on sampled rows the oracle computes one by one."""
+    c = wl.workload(name, wtype)
+    v = variant_id(q, SPLIT_VARIANT[c["type"]])
     W, G = dev(c["W"]), dev(c["G"])
-    out = q.out_prod(c["type"], W, G, c["K"], variant=q.VARIANT_SPLIT_128x256)
-    again = q.out_prod(c["type"], W, G, c["K"], variant=q.VARIANT_SPLIT_128x256)
+    out = q.out_prod(c["type"], W, G, c["K"], variant=v)
+    again = q.out_prod(c["type"], W, G, c["K"], variant=v)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all().item() and torch.equal(out, again)
     rows = np.unique(np.concatenate([[0, c["T"] - 1], np.random.default_rng(8).integers(0, c["T"], size=14)]))
