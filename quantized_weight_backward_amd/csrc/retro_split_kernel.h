@@ -165,12 +165,10 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
         // Q6_K instead: half h = w / 16 of the super-block, elements
         // l = 2 (w % 16) + e (e = 0, 1) of its four quarters qq: columns
         // 128 h + 32 qq + l.
-        // The 128-column types: threads p < 128 only (waves 4 and 5), rows
-        // 4 r4 .. + 3 with r4 = p / 16, and w = p % 16: code word w % 4 of
-        // block w / 4 (columns 32 (w / 4) + 4 (w % 4) + 0..3 and the same
-        // plus 16), or dense columns 8 w .. 8 w + 7.
-        const int r4 = kKQ ? p >> 5 : (p >> 4) & 7, w = kKQ ? p & 31 : p & 15;
-        const bool wact = kKQ || p < 128;  // uniform per wave
+        // The 128-column types: slot w = 2 u + f, the low (f = 0) or high
+        // (f = 1) nibbles of code word u % 4 of block u / 4 (columns
+        // 32 (u / 4) + 16 f + 4 (u % 4) + 0..3), or dense columns 4 w .. + 3.
+        const int r4 = p >> 5, w = p & 31;
         uint32_t roff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) roff[i] = uint32_t((4 * r4 + i) * args.pitch);
@@ -271,31 +269,26 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
                 // scale byte, 16 code bytes): 2- or 1-byte aligned blocks,
                 // read with unaligned buffer loads. Per row: the code word,
                 // d (or the scale byte), the fifth bits.
-                if (wact) {
-                    const uint32_t blk = uint32_t(F::kBytes) * uint32_t(w >> 2);
+                const int u = w >> 1;
+                const uint32_t blk = uint32_t(F::kBytes) * uint32_t(u >> 2);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        q6ring[I][i][0] =
-                            __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + blk + kHeader<TYPE> + 4 * (w & 3), 0, 0);
-                        if constexpr (TYPE == kMXFP4)
-                            q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b8(wr, roff[i] + blk, 0, 0);
-                        else
-                            q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + blk, 0, 0);
-                        if constexpr (TYPE == kQ5_0)
-                            q6ring[I][i][2] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + blk + 2, 0, 0);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    q6ring[I][i][0] =
+                        __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + blk + kHeader<TYPE> + 4 * (u & 3), 0, 0);
+                    if constexpr (TYPE == kMXFP4)
+                        q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b8(wr, roff[i] + blk, 0, 0);
+                    else
+                        q6ring[I][i][1] = __builtin_amdgcn_raw_buffer_load_b16(wr, roff[i] + blk, 0, 0);
+                    if constexpr (TYPE == kQ5_0)
+                        q6ring[I][i][2] = __builtin_amdgcn_raw_buffer_load_b32(wr, roff[i] + blk + 2, 0, 0);
                 }
             } else {
-                // BF16, F16: columns 8 w .. 8 w + 7 of each row, one 16-byte load
-                if (wact) {
+                // BF16, F16: columns 4 w .. 4 w + 3 of each row, one 8-byte load
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, roff[i] + 16 * w, 0, 0);
-                        q6ring[I][i][0] = v.x;
-                        q6ring[I][i][1] = v.y;
-                        q6ring[I][i][2] = v.z;
-                        q6ring[I][i][3] = v.w;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, roff[i] + 8 * w, 0, 0);
+                    q6ring[I][i][0] = v.x;
+                    q6ring[I][i][1] = v.y;
                 }
             }
         };
@@ -476,83 +469,70 @@ __global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
             } else if constexpr (kNibbleLayout<TYPE>) {
                 // v = d (q - 8) (Q4_0), d (q - 16) (Q5_0, q with its fifth bit)
                 // or the E2M1 value times the scale (MXFP4), exact in F32;
-                // byte e of the code word holds elements 4 (w % 4) + e (low
-                // nibble) and that plus 16 (high nibble) of block w / 4
-                if (wact) {
-                    const int blk = w >> 2, wb = w & 3;
-                    float* const hi_part = base + S::B_OFF;
-                    float* const lo_part = hi_part + S::B_PART;
-                    float lo[4][4], hv[4][4];  // [row][byte]: low- and high-nibble values
+                // byte e of the code word holds element 4 (u % 4) + e (low
+                // nibble) or that plus 16 (high nibble) of block u / 4
+                const int u = w >> 1, f = w & 1, blk = u >> 2, wb = u & 3;
+                float* const hi_part = base + S::B_OFF;
+                float* const lo_part = hi_part + S::B_PART;
+                float val[4][4];  // [row][byte]: the value of this thread's nibble
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t cw = q6ring[I][i][0];
-                        if constexpr (TYPE == kMXFP4) {
-                            mxfp4_x8(cw, mx_scale(q6ring[I][i][1]), lo[i], hv[i]);
-                        } else {
-                            const float d = half_to_f32(q6ring[I][i][1] & 0xFFFFu);
-                            constexpr int kOff = TYPE == kQ5_0 ? 16 : 8;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                int ql = int((cw >> (8 * e)) & 15u), qhi = int((cw >> (8 * e + 4)) & 15u);
-                                if constexpr (TYPE == kQ5_0) {
-                                    const uint32_t qh = q6ring[I][i][2];
-                                    ql |= int((qh >> (4 * wb + e)) & 1u) << 4;
-                                    qhi |= int((qh >> (16 + 4 * wb + e)) & 1u) << 4;
-                                }
-                                lo[i][e] = d * static_cast<float>(ql - kOff);
-                                hv[i][e] = d * static_cast<float>(qhi - kOff);
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t cw = q6ring[I][i][0] >> (4 * f);  // the thread's nibbles in the low halves
+                    if constexpr (TYPE == kMXFP4) {
+                        float unused[4];
+                        mxfp4_x8(cw, mx_scale(q6ring[I][i][1]), val[i], unused);
+                    } else {
+                        const float d = half_to_f32(q6ring[I][i][1] & 0xFFFFu);
+                        constexpr int kOff = TYPE == kQ5_0 ? 16 : 8;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            float vh[4], vl[4];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float v = half ? hv[i][e] : lo[i][e];
-                                vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
-                                vl[i] = v - vh[i];
-                            }
-                            const int o = split_b_index(32 * blk + 16 * half + 4 * wb + e, r4);
-                            *reinterpret_cast<uint2*>(hi_part + o) =
-                                make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
-                            if constexpr (kBParts == 2)
-                                *reinterpret_cast<uint2*>(lo_part + o) =
-                                    make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                            int q = int((cw >> (8 * e)) & 15u);
+                            if constexpr (TYPE == kQ5_0) q |= int((q6ring[I][i][2] >> (16 * f + 4 * wb + e)) & 1u) << 4;
+                            val[i][e] = d * static_cast<float>(q - kOff);
                         }
                     }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float vh[4], vl[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        vh[i] = __uint_as_float(__float_as_uint(val[i][e]) & 0xFFFF0000u);
+                        vl[i] = val[i][e] - vh[i];
+                    }
+                    const int o = split_b_index(32 * blk + 16 * f + 4 * wb + e, r4);
+                    *reinterpret_cast<uint2*>(hi_part + o) = make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
+                    if constexpr (kBParts == 2)
+                        *reinterpret_cast<uint2*>(lo_part + o) =
+                            make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
                 }
             } else {
                 // BF16: the weights are the bf16 operand (halfword e % 2 of
                 // word e / 2 of each row); F16: exact in F32, split as hi =
                 // its top 8 significant bits and lo = the rest (at most 3)
-                if (wact) {
-                    float* const hi_part = base + S::B_OFF;
-                    float* const lo_part = hi_part + S::B_PART;
+                float* const hi_part = base + S::B_OFF;
+                float* const lo_part = hi_part + S::B_PART;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int o = split_b_index(8 * w + e, r4);
-                        const int wd = e >> 1;
-                        if constexpr (TYPE == kBF16) {
-                            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                            *reinterpret_cast<uint2*>(hi_part + o) =
-                                make_uint2(__builtin_amdgcn_perm(q6ring[I][1][wd], q6ring[I][0][wd], sel),
-                                           __builtin_amdgcn_perm(q6ring[I][3][wd], q6ring[I][2][wd], sel));
-                        } else {
-                            float vh[4], vl[4];
+                for (int e = 0; e < 4; ++e) {
+                    const int o = split_b_index(4 * w + e, r4);
+                    const int wd = e >> 1;
+                    if constexpr (TYPE == kBF16) {
+                        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                        *reinterpret_cast<uint2*>(hi_part + o) =
+                            make_uint2(__builtin_amdgcn_perm(q6ring[I][1][wd], q6ring[I][0][wd], sel),
+                                       __builtin_amdgcn_perm(q6ring[I][3][wd], q6ring[I][2][wd], sel));
+                    } else {
+                        float vh[4], vl[4];
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float v = half_to_f32((q6ring[I][i][wd] >> (16 * (e & 1))) & 0xFFFFu);
-                                vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
-                                vl[i] = v - vh[i];
-                            }
-                            *reinterpret_cast<uint2*>(hi_part + o) =
-                                make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
-                            *reinterpret_cast<uint2*>(lo_part + o) =
-                                make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
+                        for (int i = 0; i < 4; ++i) {
+                            const float v = half_to_f32((q6ring[I][i][wd] >> (16 * (e & 1))) & 0xFFFFu);
+                            vh[i] = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+                            vl[i] = v - vh[i];
                         }
+                        *reinterpret_cast<uint2*>(hi_part + o) =
+                            make_uint2(bf16_pair(vh[0], vh[1]), bf16_pair(vh[2], vh[3]));
+                        *reinterpret_cast<uint2*>(lo_part + o) =
+                            make_uint2(bf16_pair(vl[0], vl[1]), bf16_pair(vl[2], vl[3]));
                     }
                 }
             }
