@@ -42,10 +42,15 @@ KERNEL_SOURCES = ["quantized_weight_backward_amd/csrc/retro_kernels.h",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so
+    that an edit of a comment does not void the recorded counters."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(REPO, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(REPO, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

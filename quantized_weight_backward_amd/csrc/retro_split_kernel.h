@@ -1,5 +1,5 @@
-// retro_split_kernel.h - K-quant OUT_PROD on bf16 MFMA with exact operands
-// ("exact split"): a variant that trades the F32-input MFMA for the bf16
+// retro_split_kernel.h - OUT_PROD on bf16 MFMA with exact operands ("exact
+// split"): a variant that trades the F32-input MFMA for the bf16
 // matrix rate, keeping every product exact and every sum in F32. Written out
 // below for Q4_K; Q5_K adds a fifth code bit (v < 2048), Q6_K has
 // v = sc*(q - 32) and no min term, Q2_K has v = sc*q <= 45 (one bf16 part) and
@@ -28,11 +28,11 @@
 // roundings of A and E and by that addition, all at F32 level.
 //
 // Organisation as in out_prod_ws_kernel (8 waves: 4 consumers, each 32 rows
-// by all 256 columns of a 128 x 256 tile, 4 producers; G and the decoded W double
-// buffered in LDS, one barrier per 32-row chunk). The producers write G
-// (F32), d and dmin per row, hi and lo of v (bf16, k-major with the 32 rows
-// of a column contiguous) and m (bf16); the consumers form the A and E parts
-// in registers.
+// by all BK columns of a 128 x BK tile, BK = 256 for the K-quants and 128 for
+// the others; 4 producers; G and the decoded W double buffered in LDS, one
+// barrier per 32-row chunk). The producers write G (F32), d and dmin per row,
+// the parts of v (bf16, k-major with the 32 rows of a column contiguous) and
+// m (bf16); the consumers form the A and E parts in registers.
 #pragma once
 
 #include <hip/hip_runtime.h>
