@@ -471,11 +471,13 @@ def test_split_matches_oracle(q, T, N, K, wtype):
     print(f"split {wl.TYPE_NAMES[wtype]} T={T} N={N} K={K}: nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
 
 
-def test_split_strided_batched_and_empty(q):
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q4_0, wl.MXFP4, wl.BF16])
+def test_split_strided_batched_and_empty(q, wtype):
     """Strided G and dst, batches with W broadcast, and N = 0 (the empty sum)."""
+    variant = variant_id(q, SPLIT_VARIANT[wtype])
     K, N, T = 512, 70, 90
-    cases = [wl.make_case(wl.Q4_K, N, K, T, seed=1500 + i) for i in range(2)]
-    rb = wl.row_bytes(wl.Q4_K, K)
+    cases = [wl.make_case(wtype, N, K, T, seed=1500 + i) for i in range(2)]
+    rb = wl.row_bytes(wtype, K)
     W = torch.stack([dev(c["W"]).view(N, rb) for c in cases])          # [2, N, rb]
     g_host = np.stack([c["G"] for c in cases] * 2)                      # 4 batches, W i2 // 2
     gbig = torch.full((4, T, N + 6), float("nan"), device="cuda")
@@ -484,21 +486,19 @@ def test_split_strided_batched_and_empty(q):
     dbig = torch.full((4, T, K + 8), 7.0, device="cuda")
     out = dbig[:, :, 4:4 + K]
     # W [1, 2, N, rb] broadcast over G [1, 4, T, N]: batch i2 takes W matrix i2 // 2
-    q.out_prod_batched(wl.Q4_K, W.unsqueeze(0), G.unsqueeze(0), K, out=out.unsqueeze(0),
-                       variant=q.VARIANT_SPLIT_128x256)
+    q.out_prod_batched(wtype, W.unsqueeze(0), G.unsqueeze(0), K, out=out.unsqueeze(0), variant=variant)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     for i in range(4):
         c = cases[i // 2]
-        _, acc, ab = oracle.out_prod(wl.Q4_K, c["W"], g_host[i], K)
+        _, acc, ab = oracle.out_prod(wtype, c["W"], g_host[i], K)
         check_close(got[i], acc, ab, f"split batch {i}")
     rest = dbig.clone()
     rest[:, :, 4:4 + K] = 7.0
     assert bool((rest == 7.0).all())
     # N = 0
     g0 = torch.zeros((9, 4), device="cuda")[:, :0]  # row stride 4: 16-byte rows, as the variant needs
-    empty = q.out_prod(wl.Q4_K, torch.zeros(0, dtype=torch.uint8, device="cuda"), g0, 256,
-                       variant=q.VARIANT_SPLIT_128x256)
+    empty = q.out_prod(wtype, torch.zeros(0, dtype=torch.uint8, device="cuda"), g0, 256, variant=variant)
     torch.cuda.synchronize()
     assert not empty.any()
 
