@@ -220,6 +220,19 @@ def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
                       f"{secs:.1f} s"}
 
 
+def cpu_baseline_skinny(case: dict) -> dict:
+    """The CPU oracle on one host thread over the whole T = 16 workload (all
+    16 t rows, full decode of W)."""
+    import oracle
+
+    t0 = time.perf_counter()
+    oracle.out_prod(case["type"], case["W"], case["G"], case["K"], nthreads=1)
+    secs = time.perf_counter() - t0
+    flops = 2.0 * case["T"] * case["N"] * case["K"]
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {case['T']} t rows of {SKINNY} (full decode of W included), {secs:.2f} s"}
+
+
 def kernel_family(variant: str) -> str:
     return {"ws": "out_prod_ws_kernel", "tile": "out_prod_tile_kernel"}.get(variant.split("_")[0].rstrip("2"),
                                                                          "out_prod_skinny_kernel")
@@ -422,6 +435,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(large)
+        out["cpu_baseline_skinny"] = cpu_baseline_skinny(skinny)
     print(json.dumps(out), flush=True)
     return 0
 
