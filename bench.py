@@ -89,6 +89,27 @@ KERNELS = {  # summary tag -> (kernel-name prefix in rocprofv3 output, workload,
     f"split_{LARGE}": ("void retro::out_prod_split_kernel<12>", LARGE, "split_128x256"),
 }
 LARGE_TAG, SKINNY_TAG = f"ws_{LARGE}", f"skinny_{SKINNY}"
+# Kernel traces of single cases outside the benchmark step (opt-in variants,
+# the forward), each from its own run of `bench.py --profile-case`:
+# summary tag -> (workload, dense weight type or "", op, variant, kernel-name prefix)
+CASE_TRACES = {
+    "split128_mxfp4_n17408_k5120_t2048": ("mxfp4_n17408_k5120_t2048", "", "out_prod", "split_128x128",
+                                          "void retro::out_prod_split_kernel<39>"),
+    "split128_q4_0_n17408_k5120_t2048": ("q4_0_n17408_k5120_t2048", "", "out_prod", "split_128x128",
+                                         "void retro::out_prod_split_kernel<2>"),
+    "split128_bf16_n4096_k4096_t512": ("dense_n4096_k4096_t512", "bf16", "out_prod", "split_128x128",
+                                       "void retro::out_prod_split_kernel<30>"),
+    "mulmat_skinny_q4_k_n4096_k14336_t16": ("q4_k_n4096_k14336_t16", "", "mul_mat", "skinny",
+                                            "void retro::mul_mat_skinny_kernel<12>"),
+}
+
+
+def case_trace_command(tag: str, run_dir: str) -> str:
+    workload, wtype, op, variant, _ = CASE_TRACES[tag]
+    out = os.path.relpath(run_dir, REPO).rstrip("/")
+    dense = f" --wtype {wtype}" if wtype else ""
+    return (f"rocprofv3 --kernel-trace --stats -f csv -d {out}/trace_{tag} -o run -- python3 bench.py "
+            f"--profile-case {workload}{dense} --op {op} --variant {variant} --launches 10")
 
 
 def _mean_counter(path: str, prefix: str) -> tuple[float, int]:
@@ -119,6 +140,21 @@ def summarize(run_dir: str) -> None:
     f_scale = copy_bytes / (f_copy * 1024)
     w_scale = copy_bytes / (w_copy * 1024)
     src = kernel_source_hash()
+    for tag, (workload, wtype, op, variant, prefix) in CASE_TRACES.items():
+        path = os.path.join(run_dir, f"trace_{tag}", "run_kernel_stats.csv")
+        if not os.path.exists(path):
+            continue
+        row = next(r for r in csv.DictReader(open(path)) if r["Name"].startswith(prefix))
+        lines = [f"# {tag}: rocprofv3 kernel trace", "",
+                 f"Command (repository root): `{case_trace_command(tag, run_dir)}`", "",
+                 f"Kernel: `{row['Name']}` ({op}, workload {workload}{' ' + wtype if wtype else ''}, "
+                 f"variant {variant})", "",
+                 "| calls | average (us) | min (us) | max (us) |", "|---|---|---|---|",
+                 f"| {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | {float(row['MinNs']) / 1e3:.2f} | "
+                 f"{float(row['MaxNs']) / 1e3:.2f} |", "",
+                 f"kernel source_sha256: {src}", ""]
+        open(os.path.join(PROFILES, f"{tag}_trace.md"), "w").write("\n".join(lines))
+        print(f"{tag}: avg {float(row['AverageNs']) / 1e3:.2f} us")
     for tag, (prefix, workload, _) in KERNELS.items():
         row = next(r for r in stats if r["Name"].startswith(prefix))
         lines = [f"# {tag}: rocprofv3 kernel trace", "",
@@ -246,6 +282,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this size (counter calibration)")
+    ap.add_argument("--profile-case", metavar="WORKLOAD", default=None,
+                    help="only run one workload LAUNCHES times (for a kernel trace) and exit")
+    ap.add_argument("--wtype", default="", help="with --profile-case: f32, f16 or bf16 for the dense workload")
+    ap.add_argument("--op", choices=("out_prod", "mul_mat"), default="out_prod")
+    ap.add_argument("--variant", default="auto", help="with --profile-case: a variant name, or auto")
+    ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--summarize", metavar="RUN_DIR", default=None,
                     help="write profiles/*.md from rocprofv3 output under RUN_DIR and exit (no GPU)")
     args = ap.parse_args()
@@ -276,6 +318,33 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return 0
+
+    if args.profile_case:
+        wtype = {"f32": q.F32, "f16": q.F16, "bf16": q.BF16}.get(args.wtype) if args.wtype else None
+        c = wl.workload(args.profile_case, wtype)
+        vid = 0 if args.variant == "auto" else {v: k for k, v in q.VARIANT_NAMES.items()}[args.variant]
+        W = torch.from_numpy(c["W"]).to(dev)
+        if args.op == "out_prod":
+            G = torch.from_numpy(c["G"]).to(dev)
+            out = torch.empty((c["T"], c["K"]), dtype=torch.float32, device=dev)
+            call = lambda: q.out_prod(c["type"], W, G, c["K"], out=out, variant=vid)
+        else:
+            X = torch.randn((c["T"], c["K"]), device=dev)
+            out = torch.empty((c["T"], c["N"]), dtype=torch.float32, device=dev)
+            call = lambda: q.mul_mat(c["type"], W, X, out=out, variant=vid)
+        for _ in range(2):
+            call()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.launches)]
+        for e in ev:
+            e[0].record()
+            call()
+            e[1].record()
+        torch.cuda.synchronize()
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        print(json.dumps({"profile_case": args.profile_case, "wtype": args.wtype, "op": args.op,
+                          "variant": args.variant, "launches": args.launches,
+                          "median_us": round(float(np.median(ms)) * 1e3, 2)}))
         return 0
 
     print("bench: generating inputs", file=sys.stderr, flush=True)
