@@ -175,14 +175,13 @@ __device__ __forceinline__ void nibble32_header(uint32_t h0, uint32_t h1, float&
 //         m  = high nibble of byte j+4 | (top 2 bits of byte j) << 4.
 __device__ __forceinline__ void q4_k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j,
                                                uint32_t& sc, uint32_t& m) {
-    if (j < 4) {
-        sc = (s0 >> (8 * j)) & 63u;
-        m = (s1 >> (8 * j)) & 63u;
-    } else {
-        const int i = j - 4;
-        sc = ((s2 >> (8 * i)) & 15u) | (((s0 >> (8 * i + 6)) & 3u) << 4);
-        m = ((s2 >> (8 * i + 4)) & 15u) | (((s1 >> (8 * i + 6)) & 3u) << 4);
-    }
+    // both forms from byte j % 4 of each word, then a select (no branch: j
+    // differs between lanes)
+    const uint32_t sh = 8u * uint32_t(j & 3);
+    const uint32_t b0 = (s0 >> sh) & 0xFFu, b1 = (s1 >> sh) & 0xFFu, b2 = (s2 >> sh) & 0xFFu;
+    const bool low = j < 4;
+    sc = low ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
+    m = low ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
 }
 
 // Q4_K sub-block j of a super-block whose first 16 bytes are the words
