@@ -147,6 +147,10 @@ int retro_out_prod(int type, const void *W, const float *G, float *dst, int64_t 
  * 16-byte aligned, must not overlap W). The conversion the PR's converters
  * perform (section "What": dequantize through the converters mul_mat
  * already uses), exposed so that decoded values can be checked bit for bit.
+ * Every value is the format's formula above evaluated in IEEE float32 in the
+ * order written there, bit for bit: the sign of a zero, subnormal scales and
+ * results, infinities (a scale of +-inf gives +-inf, or NaN where the formula
+ * meets inf*0 or inf-inf) and NaN included; NaN payloads are unspecified.
  * The fused kernels of retro_out_prod decode with the same device functions.
  * K == 0 or N == 0: RETRO_OK, nothing touched.
  */
@@ -160,13 +164,19 @@ int retro_dequantize(int type, const void *W, float *out, int64_t K, int64_t N, 
  */
 int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T);
 
-/* Bytes per W row: K/32*34 (Q8_0), K/32*18 (Q4_0), K/256*84 (Q2_K),
- * K/256*110 (Q3_K), K/256*144 (Q4_K), K/256*176 (Q5_K), K/256*210 (Q6_K), 4K
- * (F32), 2K (F16, BF16). -1 for an unknown type, a negative K or a K that is
- * not a whole number of blocks. Touches no device. */
+/* Bytes per W row, from the block formats above (the PR's OUT_PROD reads
+ * src0 as whole rows of blocks, section "What"): K/32*34 (Q8_0), K/32*18
+ * (Q4_0), K/32*20 (Q4_1), K/32*22 (Q5_0), K/32*24 (Q5_1), K/32*17 (MXFP4),
+ * K/256*84 (Q2_K), K/256*110 (Q3_K), K/256*144 (Q4_K), K/256*176 (Q5_K),
+ * K/256*210 (Q6_K), 4K (F32), 2K (F16, BF16). -1 for an unknown type, a
+ * negative K or a K that is not a whole number of blocks. Touches no
+ * device. */
 int64_t retro_row_bytes(int type, int64_t K);
 
-/* A static, NUL-terminated description of an error code (never NULL). */
+/* A static, NUL-terminated description of an error code (never NULL): an
+ * unsupported call is reported, never run elsewhere (where the Retrograd
+ * CUDA status page's runtime falls back to the CPU, section "What works on
+ * the GPU"). */
 const char *retro_strerror(int code);
 
 /*
@@ -216,6 +226,9 @@ const char *retro_strerror(int code);
  *                           part (BF16, MXFP4) or two, and G itself into
  *                           three. G by rows with ldg % 4 == 0; BF16 and F16
  *                           rows 16-byte aligned (row pitch % 16 == 0).
+ *   Both SPLIT variants take finite weights and gradients: an infinite weight
+ *   meets the zero parts of the other operand (inf * 0) and gives NaN where
+ *   the F32-input kernels give +-inf. Subnormal values are exact.
  */
 enum {
     RETRO_VARIANT_AUTO = 0,

@@ -4,19 +4,21 @@
 // bytes into float32 through the primitives below, so one bit-exact check of
 // retro_dequantize covers the arithmetic of all of them.
 //
-// Exactness: a Q8_0/Q4_0/Q5_0 value d*q needs at most 11+8 significant bits
-// (Q4_1/Q5_1 add the offset m with one rounding), a
-// Q4_K product (d*sc)*q at most 11+6+4 = 21 (Q5_K: 22) and dmin*m at most 17,
-// so every product below is exact in float32 and only the Q4_K/Q5_K
-// subtraction rounds (once, to nearest-even); Q2_K (d*sc)*q needs at most
-// 11+4+2 bits and rounds likewise only in its subtraction. A Q6_K value
-// (d*sc)*(q - 32) has odd parts of at most 11, 7 and 5 bits, so it is exact,
-// and so is its form a*q - 32a (a*q needs at most 24 bits); a Q3_K value
-// (d*(sc-32))*q needs at most 11+6+3 bits and its form a*q' - 4a (q' = q+4)
-// is exact too. Whether the compiler fuses a*q - b into an FMA therefore
-// changes no bit. An MXFP4 value, an E2M1 code times a power of two, is
-// formed by the hardware's scaled FP4 conversion, which returns that product
-// rounded once (exact unless it overflows; NaN for the NaN scale).
+// Exactness: a Q8_0/Q4_0/Q5_0 value d*(q - c) needs at most 11+8 significant
+// bits (Q4_1/Q5_1 add the offset m with one rounding), a Q4_K product
+// (d*sc)*q at most 11+6+4 = 21 (Q5_K: 22) and dmin*m at most 17, so every
+// product below is exact in float32 and only the Q4_K/Q5_K subtraction rounds
+// (once, to nearest-even); Q2_K (d*sc)*q needs at most 11+4+2 bits and rounds
+// likewise only in its subtraction. A Q6_K value (d*sc)*(q - 32) and a Q3_K
+// value (d*(sc - 32))*(q - 4) are exact. The formats that subtract a constant
+// from the code (Q4_0, Q5_0, Q6_K, Q3_K) are decoded as scale times (q - c)
+// in that order, never as scale*q - scale*c: the two agree on every finite
+// value, but only the first gives the sign of a zero and an infinite scale's
+// +-inf as the formats' own formulas do. Whether the compiler fuses a*q - b
+// into an FMA changes no bit. An MXFP4 value, an E2M1 code times a power of
+// two, is formed by the hardware's scaled FP4 conversion, which returns that
+// product rounded once (exact unless it overflows to inf, subnormal scales
+// and results included; NaN for the NaN scale).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -109,9 +111,39 @@ __device__ __forceinline__ uint32_t fifth_bits(uint32_t qh, int first) {
     return ((((qh >> first) & 15u) * 0x00204081u) & 0x01010101u) << 4;
 }
 
-// Q4_1 / Q5_0 / Q5_1: the low or high nibbles of four code bytes, plus the
-// fifth bits `fifth` (fifth_bits; 0 for Q4_1); value d*q + m, where m is the
-// block's offset (Q5_0: m = -16d, exact, since d*(q - 16) = d*q - 16d).
+// Four signed codes held in the top bits of the four bytes of `top`: byte i
+// is (q_i - c) * 2^s as a signed 8-bit integer (the code's value q_i XOR c,
+// c = 2^(b-1) for a b-bit code, placed at bits 8-b .. 7). Each element is
+// one signed-byte conversion (exact) times as = a * 2^-s (exact: a power of
+// two times a scale far above the subnormal range), so the result is
+// a * (q_i - c) rounded once, which is exact.
+__device__ __forceinline__ void signed_top_x4(uint32_t top, float as, float out[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = static_cast<float>(static_cast<int8_t>((top >> (8 * i)) & 0xFFu)) * as;
+}
+
+// The fifth bits first .. first + 3 of a 32-bit word, inverted, as bit 7 of
+// the four bytes of a word (q XOR 16 for a 5-bit code).
+__device__ __forceinline__ uint32_t fifth_bits_top(uint32_t qh, int first) {
+    return (((((qh >> first) & 15u) * 0x00204081u) & 0x01010101u) << 7) ^ 0x80808080u;
+}
+
+// Q4_0: the low (high = false) or high nibbles of four code bytes, value
+// d*(q - 8) = float(16*(q - 8)) * (d/16); ds = d/16.
+__device__ __forceinline__ void q4_0_x4(uint32_t w, bool high, float ds, float out[4]) {
+    const uint32_t x = w ^ 0x88888888u;  // every nibble q -> q XOR 8
+    signed_top_x4((high ? x : (x << 4)) & 0xF0F0F0F0u, ds, out);
+}
+
+// Q5_0: the low or high nibbles of four code bytes plus their fifth bits
+// `qh` bits first .. first + 3, value d*(q - 16) = float(8*(q - 16)) * (d/8);
+// ds = d/8.
+__device__ __forceinline__ void q5_0_x4(uint32_t w, bool high, uint32_t qh, int first, float ds, float out[4]) {
+    signed_top_x4(((high ? (w >> 1) : (w << 3)) & 0x78787878u) | fifth_bits_top(qh, first), ds, out);
+}
+
+// Q4_1 / Q5_1: the low or high nibbles of four code bytes, plus the fifth
+// bits `fifth` (fifth_bits; 0 for Q4_1); value d*q + m, m the block's offset.
 __device__ __forceinline__ void q4_1_x4(uint32_t w, bool high, uint32_t fifth, float d, float m, float out[4]) {
     const uint32_t q = nibbles(w, high) | fifth;
 #pragma unroll
@@ -149,23 +181,39 @@ __device__ __forceinline__ void mxfp4_x4(uint32_t w, bool high, float s, float o
     for (int i = 0; i < 4; ++i) out[i] = high ? hi[i] : lo[i];
 }
 
-// Scale d, offset m and fifth-bit word qh of a 32-element nibble block whose
-// first 8 bytes are the words h0, h1 (Q4_0: m = -8d; Q5_0: m = -16d; both
-// exact, so d*q + m is the block's value d*(q - 8) or d*(q - 16) with at
-// most a different sign of zero).
+// Scale, offset m and fifth-bit word qh of a 32-element nibble block whose
+// first 8 bytes are the words h0, h1. Q4_1/Q5_1: d and the offset m
+// (value d*q + m). Q4_0 and Q5_0 have no offset (m = 0) and give their scale
+// d as d/16 and d/8, the factor of q4_0_x4 and q5_0_x4.
 template <int TYPE>
 __device__ __forceinline__ void nibble32_header(uint32_t h0, uint32_t h1, float& d, float& m, uint32_t& qh) {
     d = half_to_f32(h0 & 0xFFFFu);
     if constexpr (kHasOffset<TYPE>)
         m = half_to_f32(h0 >> 16);
     else
-        m = (TYPE == kQ4_0 ? -8.0f : -16.0f) * d;
+        m = 0.0f;
+    if constexpr (TYPE == kQ4_0) d *= 0.0625f;
+    if constexpr (TYPE == kQ5_0) d *= 0.125f;
     if constexpr (TYPE == kQ5_0)
         qh = (h0 >> 16) | (h1 << 16);
     else if constexpr (TYPE == kQ5_1)
         qh = h1;
     else
         qh = 0u;
+}
+
+// Elements first .. first + 3 (first % 4 == 0; the low nibbles of the code
+// word w for first < 16, its high nibbles otherwise) of a 32-element nibble
+// block with header values d, m, qh from nibble32_header.
+template <int TYPE>
+__device__ __forceinline__ void nibble32_x4(uint32_t w, uint32_t qh, int first, float d, float m, float out[4]) {
+    const bool high = first >= 16;
+    if constexpr (TYPE == kQ4_0)
+        q4_0_x4(w, high, d, out);
+    else if constexpr (TYPE == kQ5_0)
+        q5_0_x4(w, high, qh, first, d, out);
+    else
+        q4_1_x4(w, high, fifth_bits(qh, first), d, m, out);
 }
 
 // Q4_K sub-scale and sub-min j (0..7) from the 12-byte field, given as its
@@ -213,20 +261,21 @@ __device__ __forceinline__ void q5_k_x4(uint32_t qs, uint32_t qh, int bit, bool 
 }
 
 // Q6_K: low or high nibbles of four ql bytes, plus bits 2p, 2p+1 of the four
-// qh bytes of the same elements as bits 4-5 of q; value (d*sc)*(q - 32),
-// computed as a*q + b with a = d*sc and b = -32a (exact, see above).
-__device__ __forceinline__ void q6_k_x4(uint32_t ql, bool high, uint32_t qh, int p, float a, float b,
-                                        float out[4]) {
-    const uint32_t m = nibbles(ql, high) | (((qh >> (2 * p)) & 0x03030303u) << 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) + b;
+// qh bytes of the same elements as bits 4-5 of q; value (d*sc)*(q - 32) =
+// float(4*(q - 32)) * as with as = d*sc/4 (q6_k_coeffs).
+__device__ __forceinline__ void q6_k_x4(uint32_t ql, bool high, uint32_t qh, int p, float as, float out[4]) {
+    // q XOR 32 at bits 2..7: the nibble at bits 2-5, the two high bits at 6-7
+    // with the upper one inverted
+    const uint32_t lo4 = (high ? (ql >> 2) : (ql << 2)) & 0x3C3C3C3Cu;
+    const uint32_t hi2 = (((qh >> (2 * p)) << 6) & 0xC0C0C0C0u) ^ 0x80808080u;
+    signed_top_x4(lo4 | hi2, as, out);
 }
 
-// Signed 8-bit Q6_K sub-scale `i` (0..3) of a word, times d: (a, b = -32a).
-__device__ __forceinline__ void q6_k_coeffs(uint32_t scales, int i, float d, float& a, float& b) {
+// Signed 8-bit Q6_K sub-scale `i` (0..3) of a word, times d, over 4:
+// as = d*sc/4 (exact), the factor of q6_k_x4.
+__device__ __forceinline__ void q6_k_coeffs(uint32_t scales, int i, float d, float& as) {
     const int sc = static_cast<int>(static_cast<int8_t>((scales >> (8 * i)) & 0xFFu));
-    a = d * static_cast<float>(sc);
-    b = -32.0f * a;
+    as = d * static_cast<float>(sc) * 0.25f;
 }
 
 // Q2_K: the 2-bit codes at bits 2p, 2p+1 of four qs bytes; value a*q - b
@@ -256,18 +305,17 @@ __device__ __forceinline__ uint32_t q3_k_scale(uint32_t f0, uint32_t f1, uint32_
 
 // Q3_K: low 2 bits at bits 2p, 2p+1 of four qs bytes, plus 4 where bit
 // `hbit` of the four hmask bytes is set (q' = q + 4 in 0..7); value
-// a*q' + b with a = d*(sc - 32), b = -4a.
-__device__ __forceinline__ void q3_k_x4(uint32_t qs, uint32_t hm, int p, int hbit, float a, float b,
-                                        float out[4]) {
-    const uint32_t m = ((qs >> (2 * p)) & 0x03030303u) | (((hm >> hbit) & 0x01010101u) << 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) + b;
+// (d*(sc - 32))*(q' - 4) = float(32*(q' - 4)) * as with as = d*(sc - 32)/32
+// (q3_k_coeffs).
+__device__ __forceinline__ void q3_k_x4(uint32_t qs, uint32_t hm, int p, int hbit, float as, float out[4]) {
+    // q' XOR 4 at bits 5..7: the low bits at 5-6, the mask bit inverted at 7
+    const uint32_t lo2 = ((qs >> (2 * p)) & 0x03030303u) << 5;
+    const uint32_t hi1 = (((hm >> hbit) & 0x01010101u) << 7) ^ 0x80808080u;
+    signed_top_x4(lo2 | hi1, as, out);
 }
 
-__device__ __forceinline__ void q3_k_coeffs(uint32_t f0, uint32_t f1, uint32_t f2, int s, float d, float& a,
-                                            float& b) {
-    a = d * static_cast<float>(static_cast<int>(q3_k_scale(f0, f1, f2, s)) - 32);
-    b = -4.0f * a;
+__device__ __forceinline__ void q3_k_coeffs(uint32_t f0, uint32_t f1, uint32_t f2, int s, float d, float& as) {
+    as = d * static_cast<float>(static_cast<int>(q3_k_scale(f0, f1, f2, s)) - 32) * 0.03125f;
 }
 
 }  // namespace retro

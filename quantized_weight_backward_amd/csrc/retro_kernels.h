@@ -410,13 +410,13 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) {
                         const int si = (j >> 1) + 2 * qq;  // sub-scale 8 hh + si
-                        float a, b;
-                        q6_k_coeffs(scw[si >> 2], si & 3, d, a, b);
+                        float a;
+                        q6_k_coeffs(scw[si >> 2], si & 3, d, a);
                         const int col = 256 * sb + 128 * hh + 32 * qq + 8 * j;
 #pragma unroll
                         for (int i = 0; i < 2; ++i) {
                             float e[4];
-                            q6_k_x4(qlw[qq & 1][i], qq >= 2, qhw[i], qq, a, b, e);
+                            q6_k_x4(qlw[qq & 1][i], qq >= 2, qhw[i], qq, a, e);
                             *reinterpret_cast<float4*>(brow + S::swz(col + 4 * i)) =
                                 make_float4(e[0], e[1], e[2], e[3]);
                         }
@@ -449,11 +449,11 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) {
                         const int si = (j >> 1) + 2 * qq;  // pair / sub-scale 8 hh + si
-                        float a, b;
+                        float a, b = 0.f;
                         if constexpr (TYPE == kQ2_K)
                             q2_k_coeffs(aux[si >> 2], si & 3, d, dmin, a, b);
                         else
-                            q3_k_coeffs(f0, f1, f2, 8 * hh + si, d, a, b);
+                            q3_k_coeffs(f0, f1, f2, 8 * hh + si, d, a);
                         const int col = 256 * sb + 128 * hh + 32 * qq + 8 * j;
 #pragma unroll
                         for (int i = 0; i < 2; ++i) {
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                             if constexpr (TYPE == kQ2_K)
                                 q2_k_x4(qw[i], qq, a, b, e);
                             else
-                                q3_k_x4(qw[i], aux[i], qq, 4 * hh + qq, a, b, e);
+                                q3_k_x4(qw[i], aux[i], qq, 4 * hh + qq, a, e);
                             *reinterpret_cast<float4*>(brow + S::swz(col + 4 * i)) =
                                 make_float4(e[0], e[1], e[2], e[3]);
                         }
@@ -476,9 +476,9 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t w = lds_word_a2(blk + kHeader<TYPE> + 4 * i);
                         float e[4];
-                        q4_1_x4(w, false, fifth_bits(qh, 4 * i), d, m, e);
+                        nibble32_x4<TYPE>(w, qh, 4 * i, d, m, e);
                         *reinterpret_cast<float4*>(brow + S::swz(lo + 4 * i)) = make_float4(e[0], e[1], e[2], e[3]);
-                        q4_1_x4(w, true, fifth_bits(qh, 16 + 4 * i), d, m, e);
+                        nibble32_x4<TYPE>(w, qh, 16 + 4 * i, d, m, e);
                         *reinterpret_cast<float4*>(brow + S::swz(lo + 16 + 4 * i)) =
                             make_float4(e[0], e[1], e[2], e[3]);
                     }
@@ -648,7 +648,7 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         nibble32_header<TYPE>(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16), d,
                               m, qh);
         const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + kHeader<TYPE> + (r & 15));
-        q4_1_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), r >= 16, fifth_bits(qh, r), d, m, e);
+        nibble32_x4<TYPE>(uint32_t(c[0]) | (uint32_t(c[1]) << 16), qh, r, d, m, e);
     } else if constexpr (TYPE == kQ4_K) {  // K is a multiple of 256, so k < K always
         const uint8_t* sbp = row + (k >> 8) * 144;
         const int e256 = k & 255, c = e256 >> 6, r = e256 & 63;
@@ -683,11 +683,11 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         const uint16_t* f = reinterpret_cast<const uint16_t*>(sbp + 96);
         const uint32_t f0 = f[0] | (uint32_t(f[1]) << 16), f1 = f[2] | (uint32_t(f[3]) << 16),
                        f2 = f[4] | (uint32_t(f[5]) << 16);
-        float a, b;
-        q3_k_coeffs(f0, f1, f2, 8 * h + 2 * p + (l >> 4), half_to_f32(f[6]), a, b);
+        float a;
+        q3_k_coeffs(f0, f1, f2, 8 * h + 2 * p + (l >> 4), half_to_f32(f[6]), a);
         const uint16_t* qs = reinterpret_cast<const uint16_t*>(sbp + 32 + 32 * h + l);
         const uint16_t* hm = reinterpret_cast<const uint16_t*>(sbp + l);
-        q3_k_x4(qs[0] | (uint32_t(qs[1]) << 16), hm[0] | (uint32_t(hm[1]) << 16), p, 4 * h + p, a, b, e);
+        q3_k_x4(qs[0] | (uint32_t(qs[1]) << 16), hm[0] | (uint32_t(hm[1]) << 16), p, 4 * h + p, a, e);
     } else {  // kQ6_K: 2-byte aligned super-blocks
         const uint8_t* sbp = row + (k >> 8) * 210;
         const int e256 = k & 255, h = e256 >> 7, p = (e256 >> 5) & 3, l = e256 & 31;
@@ -695,10 +695,9 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         const uint16_t* qh = reinterpret_cast<const uint16_t*>(sbp + 128 + 32 * h + l);
         const int si = 8 * h + 2 * p + (l >> 4);
         const uint32_t scw = *reinterpret_cast<const uint16_t*>(sbp + 192 + (si & ~1));
-        float a, b;
-        q6_k_coeffs(scw, si & 1, half_to_f32(*reinterpret_cast<const uint16_t*>(sbp + 208)), a, b);
-        q6_k_x4(uint32_t(ql[0]) | (uint32_t(ql[1]) << 16), p >= 2, uint32_t(qh[0]) | (uint32_t(qh[1]) << 16), p, a, b,
-                e);
+        float a;
+        q6_k_coeffs(scw, si & 1, half_to_f32(*reinterpret_cast<const uint16_t*>(sbp + 208)), a);
+        q6_k_x4(uint32_t(ql[0]) | (uint32_t(ql[1]) << 16), p >= 2, uint32_t(qh[0]) | (uint32_t(qh[1]) << 16), p, a, e);
     }
 }
 
@@ -1050,14 +1049,11 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
         for (int s = 0; s < 4; ++s) {
             const int src = 2 * (4 * rq + s) + hi;
             const float d = lane_value(dmine, src);
-            float m;
-            if constexpr (kHasOffset<TYPE>)
-                m = lane_value(mmine, src);
-            else
-                m = (TYPE == kQ4_0 ? -8.0f : -16.0f) * d;
+            float m = 0.f;
+            if constexpr (kHasOffset<TYPE>) m = lane_value(mmine, src);
             uint32_t qh = 0u;
             if constexpr (kHasFifth<TYPE>) qh = uint32_t(__builtin_amdgcn_ds_bpermute(src << 2, int(qhmine)));
-            q4_1_x4(r.code[s][0], e >= 16, fifth_bits(qh, e), d, m, wv[s]);
+            nibble32_x4<TYPE>(r.code[s][0], qh, e, d, m, wv[s]);
         }
     } else if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) {  // this lane's pair is sub-block 2c + (lane & 1)
         const int c = (k0 & 255) >> 6;
@@ -1075,23 +1071,23 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
     } else {  // Q6_K, Q2_K, Q3_K: this lane's pair is (row lane / 4, sub-scale slot lane % 4)
         const int e0 = k0 & 255, h = e0 >> 7, p0 = (e0 >> 5) & 3, p = p0 + hi, l16 = (j & 7) >> 2;
         const int w = lane & 3, si = 8 * h + 2 * (p0 + (w >> 1)) + (w & 1);
-        float am, bm;
+        float am, bm = 0.f;
         if constexpr (TYPE == kQ6_K)
-            q6_k_coeffs(r.hdr[0], si & 1, half_to_f32(r.hdr[1]), am, bm);
+            q6_k_coeffs(r.hdr[0], si & 1, half_to_f32(r.hdr[1]), am);
         else if constexpr (TYPE == kQ2_K)
             q2_k_coeffs(r.hdr[0], si & 3, half_to_f32(r.hdr[1] & 0xFFFFu), half_to_f32(r.hdr[1] >> 16), am, bm);
         else
-            q3_k_coeffs(r.hdr[0], r.hdr[1], r.hdr[2], si, half_to_f32(r.hdr[3] & 0xFFFFu), am, bm);
+            q3_k_coeffs(r.hdr[0], r.hdr[1], r.hdr[2], si, half_to_f32(r.hdr[3] & 0xFFFFu), am);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int src = 4 * (4 * rq + s) + 2 * hi + l16;
-            const float a = lane_value(am, src), b = lane_value(bm, src);
+            const float a = lane_value(am, src);
             if constexpr (TYPE == kQ6_K)
-                q6_k_x4(r.code[s][0], p >= 2, r.code[s][1], p, a, b, wv[s]);
+                q6_k_x4(r.code[s][0], p >= 2, r.code[s][1], p, a, wv[s]);
             else if constexpr (TYPE == kQ2_K)
-                q2_k_x4(r.code[s][0], p, a, b, wv[s]);
+                q2_k_x4(r.code[s][0], p, a, lane_value(bm, src), wv[s]);
             else
-                q3_k_x4(r.code[s][0], r.code[s][1], p, 4 * h + p, a, b, wv[s]);
+                q3_k_x4(r.code[s][0], r.code[s][1], p, 4 * h + p, a, wv[s]);
         }
     }
 }

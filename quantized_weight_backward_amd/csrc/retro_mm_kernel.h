@@ -131,7 +131,7 @@ struct MmCodecNibble {
                 nibble32_header<TYPE>(w[4], 0u, d, m, qh);
             const int first = high ? 16 : 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q4_1_x4(w[i], high, fifth_bits(qh, first + 4 * i), d, m, e + 4 * i);
+            for (int i = 0; i < 4; ++i) nibble32_x4<TYPE>(w[i], qh, first + 4 * i, d, m, e + 4 * i);
         }
     }
 };
@@ -195,10 +195,10 @@ struct MmCodec<kQ6_K> {
     }
     __device__ static void decode(const uint32_t (&w)[WORDS], int k, float (&e)[16]) {
         const int el = k & 255, h = el >> 7, p = (el >> 5) & 3, si = 8 * h + 2 * p + ((el & 31) >> 4);
-        float a, b;
-        q6_k_coeffs(w[8], si & 3, half_to_f32(w[9] & 0xFFFFu), a, b);
+        float a;
+        q6_k_coeffs(w[8], si & 3, half_to_f32(w[9] & 0xFFFFu), a);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q6_k_x4(w[i], p >= 2, w[4 + i], p, a, b, e + 4 * i);
+        for (int i = 0; i < 4; ++i) q6_k_x4(w[i], p >= 2, w[4 + i], p, a, e + 4 * i);
     }
 };
 
@@ -240,10 +240,10 @@ struct MmCodec<kQ3_K> {
     }
     __device__ static void decode(const uint32_t (&w)[WORDS], int k, float (&e)[16]) {
         const int el = k & 255, h = el >> 7, p = (el >> 5) & 3, si = 8 * h + 2 * p + ((el & 31) >> 4);
-        float a, b;
-        q3_k_coeffs(w[8], w[9], w[10], si, half_to_f32(w[11] & 0xFFFFu), a, b);
+        float a;
+        q3_k_coeffs(w[8], w[9], w[10], si, half_to_f32(w[11] & 0xFFFFu), a);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q3_k_x4(w[i], w[4 + i], p, 4 * h + p, a, b, e + 4 * i);
+        for (int i = 0; i < 4; ++i) q3_k_x4(w[i], w[4 + i], p, 4 * h + p, a, e + 4 * i);
     }
 };
 

@@ -556,12 +556,12 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
                     const int si = (j >> 1) + 2 * qq;  // sub-scale 8hh + si
-                    float a, b;
-                    q6_k_coeffs(wreg[6 + (si >> 2)], si & 3, d, a, b);
+                    float a;
+                    q6_k_coeffs(wreg[6 + (si >> 2)], si & 3, d, a);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         float e[4];
-                        q6_k_x4(wreg[2 * (qq & 1) + i], qq >= 2, wreg[4 + i], qq, a, b, e);
+                        q6_k_x4(wreg[2 * (qq & 1) + i], qq >= 2, wreg[4 + i], qq, a, e);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) ws[wlds[qq] + (4 * i + t) * WP] = e[t];
                     }
@@ -578,18 +578,18 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
                     const int si = (j >> 1) + 2 * qq;  // pair / sub-scale 8hh + si
-                    float a, b;
+                    float a, b = 0.f;
                     if constexpr (TYPE == kQ2_K)
                         q2_k_coeffs(wreg[2 + (si >> 2)], si & 3, d, dmin, a, b);
                     else
-                        q3_k_coeffs(wreg[4], wreg[5], wreg[6], 8 * hh + si, d, a, b);
+                        q3_k_coeffs(wreg[4], wreg[5], wreg[6], 8 * hh + si, d, a);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         float e[4];
                         if constexpr (TYPE == kQ2_K)
                             q2_k_x4(wreg[i], qq, a, b, e);
                         else
-                            q3_k_x4(wreg[i], wreg[2 + i], qq, 4 * hh + qq, a, b, e);
+                            q3_k_x4(wreg[i], wreg[2 + i], qq, 4 * hh + qq, a, e);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) ws[wlds[qq] + (4 * i + t) * WP] = e[t];
                     }
@@ -631,10 +631,10 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
 #pragma unroll
                 for (int w = 0; w < CW; ++w) {
                     float e[4];
-                    q4_1_x4(wreg[w], false, fifth_bits(qh, first + 4 * w), d, m, e);
+                    nibble32_x4<TYPE>(wreg[w], qh, first + 4 * w, d, m, e);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) ws[wlds[0] + (4 * w + j) * WP] = e[j];
-                    q4_1_x4(wreg[w], true, fifth_bits(qh, 16 + first + 4 * w), d, m, e);
+                    nibble32_x4<TYPE>(wreg[w], qh, 16 + first + 4 * w, d, m, e);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) ws[wlds[1] + (4 * w + j) * WP] = e[j];
                 }

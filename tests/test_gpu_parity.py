@@ -114,13 +114,11 @@ def small_case(wtype, i, seed):
 
 # --- decode ---------------------------------------------------------------------
 
-def same_bits_zeros_equal(a, b):
-    """Bit-identical floats, except that +0 and -0 count as equal: the Q6_K,
-    Q3_K, Q4_0 and Q5_0 kernels form a*(q - c) as a*q - c*a, which is +0
-    where the plain product is -0 (negative a, q = c); every non-zero value
-    is exact."""
+def same_bits(a, b):
+    """Bit-identical floats, the sign of every zero included (the decoders
+    form a*(q - c) in that order, as the formats define it)."""
     a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
-    return a.shape == b.shape and bool(np.all((a.view(np.uint32) == b.view(np.uint32)) | ((a == 0) & (b == 0))))
+    return a.shape == b.shape and bool(np.all(a.view(np.uint32) == b.view(np.uint32)))
 
 
 @pytest.mark.parametrize("wtype", TYPES)
@@ -129,7 +127,7 @@ def test_dequantize_bit_exact(q, wtype, i):
     c = small_case(wtype, i, 100 + i)
     ref = oracle.dequantize(wtype, c["W"], c["K"])
     got = q.dequantize(wtype, dev(c["W"]), c["K"], c["N"]).cpu().numpy()
-    assert same_bits_zeros_equal(got, ref)
+    assert same_bits(got, ref)
 
 
 def test_dequantize_hand_built_blocks(q, golden):
@@ -585,7 +583,9 @@ def test_batched_empty_and_single(q):
 
 # --- full-size workloads ----------------------------------------------------------
 
-FULL = [
+# The five benchmarked workloads (the dense one in its three storage types):
+# every output is compared with the oracle.
+FIVE = [
     ("q8_0_n128_k256_t64", None),
     ("dense_n4096_k4096_t512", wl.F32),
     ("dense_n4096_k4096_t512", wl.F16),
@@ -593,6 +593,9 @@ FULL = [
     ("q4_0_n17408_k5120_t2048", None),
     ("q4_k_n14336_k4096_t4096", None),
     ("q4_k_n4096_k14336_t16", None),
+]
+# The other types at the same shapes: sampled rows.
+FULL = [
     ("q5_k_n14336_k4096_t4096", None),
     ("q6_k_n14336_k4096_t4096", None),
     ("q5_k_n4096_k14336_t16", None),
@@ -608,11 +611,32 @@ FULL = [
 ]
 
 
+@pytest.mark.parametrize("name,wtype", FIVE)
+def test_full_size_whole_output(q, name, wtype):
+    """The launch configuration the benchmark times, every output compared
+    with the oracle element by element (NMSE over the whole output, the
+    relative error of each output), then determinism of a second call."""
+    c = wl.workload(name, wtype)
+    print(f"{name} {wl.TYPE_NAMES[c['type']]}: kernel {q.VARIANT_NAMES[q.choice(c['type'], c['K'], c['N'], c['T'])]}",
+          flush=True)
+    W, G = dev(c["W"]), dev(c["G"])
+    out = torch.full((c["T"], c["K"]), float("nan"), device="cuda")
+    q.out_prod(c["type"], W, G, c["K"], out=out)
+    again = q.out_prod(c["type"], W, G, c["K"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    y = out.cpu().numpy()
+    del W, G, out, again
+    _, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"], nthreads=ORACLE_THREADS)
+    e = check_close(y, acc, ab, name)
+    print(f"{name} {wl.TYPE_NAMES[c['type']]}: {y.size} outputs, nmse={e['nmse']:.3e} max_rel={e['max_rel']:.3e}")
+
+
 @pytest.mark.parametrize("name,wtype", FULL)
 def test_full_size_sampled_rows(q, name, wtype):
-    """The launch configuration the benchmark times, checked on sampled t
-    rows that the oracle computes one by one (first, last and random rows),
-    plus whole-output properties: all finite, deterministic."""
+    """The other types at the benchmarked shapes, checked on sampled t rows
+    that the oracle computes one by one (first, last and random rows), plus
+    whole-output properties: all finite, deterministic."""
     c = wl.workload(name, wtype)
     W, G = dev(c["W"]), dev(c["G"])
     out = torch.full((c["T"], c["K"]), float("nan"), device="cuda")

@@ -14,13 +14,14 @@ import torch
 
 import oracle
 import workloads as wl
+from blocks import (hexbytes, pack_q3_k_field, pack_q4_k_field, q2_k_superblock, q3_k_superblock,
+                    q4_k_superblock, q5_k_superblock, q6_k_superblock, ramp_codes)
+from blocks import fixture_value as _fixture_value
 
 TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K,
          wl.Q5_K, wl.Q6_K]
 
 
-def hexbytes(tokens):
-    return np.array([int(t, 16) for t in tokens], dtype=np.uint8)
 
 
 # --- element decoders -------------------------------------------------------
@@ -70,23 +71,8 @@ def test_hand_built_blocks(golden, fixture, wtype):
         assert np.array_equal(np.signbit(got), np.signbit(expected)), name
 
 
-def pack_q4_k_field(sc, m):
-    """GGUF Q4_K sub-scale/sub-min packing, written for the tests (the oracle only unpacks)."""
-    s = [0] * 12
-    for j in range(4):
-        s[j] = (sc[j] & 63) | ((sc[j + 4] >> 4) << 6)
-        s[j + 4] = (m[j] & 63) | ((m[j + 4] >> 4) << 6)
-        s[j + 8] = (sc[j + 4] & 15) | ((m[j + 4] & 15) << 4)
-    return np.array(s, dtype=np.uint8)
 
 
-def q4_k_superblock(d_bits, dmin_bits, field, codes):
-    blk = np.zeros(144, dtype=np.uint8)
-    blk[0:2] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
-    blk[2:4] = np.array([dmin_bits & 255, dmin_bits >> 8], dtype=np.uint8)
-    blk[4:16] = field
-    blk[16:144] = codes
-    return blk
 
 
 def test_q4_k_field_packer_matches_hand_packing(golden):
@@ -142,8 +128,6 @@ def test_q4_1_q5_hand_built_blocks(golden, name, wtype):
         assert got[int(e)] == float(v), (name, item)
 
 
-def _fixture_value(v):
-    return float.fromhex(v) if "p" in v else float(v)
 
 
 @pytest.mark.parametrize("name", ["mx_a", "mx_b", "mx_c", "mx_d", "mx_e"])
@@ -204,28 +188,10 @@ def test_q5_0_fifth_bits_one_to_one():
         assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
 
 
-def q5_k_superblock(d_bits, dmin_bits, field, qh, qs):
-    blk = np.zeros(176, dtype=np.uint8)
-    blk[0:2] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
-    blk[2:4] = np.array([dmin_bits & 255, dmin_bits >> 8], dtype=np.uint8)
-    blk[4:16] = field
-    blk[16:48] = qh
-    blk[48:176] = qs
-    return blk
 
 
-def q6_k_superblock(d_bits, scales, ql, qh):
-    blk = np.zeros(210, dtype=np.uint8)
-    blk[0:128] = ql
-    blk[128:192] = qh
-    blk[192:208] = np.asarray(scales, dtype=np.int8).view(np.uint8)
-    blk[208:210] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
-    return blk
 
 
-def ramp_codes(n):
-    i = np.arange(n)
-    return (((i * 7 + 3) & 15) | (((i * 5 + 1) & 15) << 4)).astype(np.uint8)
 
 
 def test_q5_k_hand_built_superblock(golden):
@@ -353,33 +319,10 @@ def test_q6_k_products_are_exact():
     assert 2047 * 127 * 31 < 2 ** 24
 
 
-def q2_k_superblock(d_bits, dmin_bits, pairs, qs):
-    blk = np.zeros(84, dtype=np.uint8)
-    blk[0:16] = pairs
-    blk[16:80] = qs
-    blk[80:82] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
-    blk[82:84] = np.array([dmin_bits & 255, dmin_bits >> 8], dtype=np.uint8)
-    return blk
 
 
-def pack_q3_k_field(sc):
-    """Sixteen 6-bit Q3_K sub-scales into the 12-byte field, written for the
-    tests from the layout description (the oracle only unpacks)."""
-    f = [0] * 12
-    for s_, v in enumerate(sc):
-        i, g = s_ % 4, s_ // 4
-        f[4 * (g % 2) + i] |= (v & 15) << (4 * (g // 2))
-        f[8 + i] |= ((v >> 4) & 3) << (2 * g)
-    return np.array(f, dtype=np.uint8)
 
 
-def q3_k_superblock(d_bits, hmask, qs, field):
-    blk = np.zeros(110, dtype=np.uint8)
-    blk[0:32] = hmask
-    blk[32:96] = qs
-    blk[96:108] = field
-    blk[108:110] = np.array([d_bits & 255, d_bits >> 8], dtype=np.uint8)
-    return blk
 
 
 def test_q2_k_hand_built_superblock(golden):
@@ -698,3 +641,25 @@ def test_error_metrics_flag_a_planted_precision_loss():
     eb = oracle.errors(bad, acc, ab)
     assert eg["nmse"] < 1e-10 and eg["max_rel"] < 2e-6
     assert eb["max_rel"] > 2e-6
+
+
+def test_golden_block_reader_matches_every_fixture(golden):
+    """The block list the device tests read (tests/blocks.py) holds every
+    fixture file, and the oracle decodes each of its blocks to the fixture's
+    values, signs included."""
+    import os
+
+    from blocks import golden_blocks
+
+    blocks = golden_blocks(golden)
+    files = {label.split(":")[0] for label, *_ in blocks}
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    assert files == {f for f in os.listdir(here) if f.endswith(".txt")}
+    for label, wtype, K, raw, expected in blocks:
+        got = oracle.dequantize(wtype, raw, K)[0]
+        for e, v in expected.items():
+            want = np.float32(v)
+            if np.isnan(want):
+                assert np.isnan(got[e]), (label, e)
+            else:
+                assert got[e] == want and np.signbit(got[e]) == np.signbit(want), (label, e)
