@@ -10,12 +10,19 @@ with a 14336-wide MLP:
 Inputs are seeded synthetic data (workloads.py) resident in HBM before the
 timed region. value = whole-step F32 TFLOP/s (2*T*N*K per call).
 
+After the step loop the same process times every benchmarked workload at
+the kernel retro_out_prod chooses for it (the tiny Q8_0 case, the dense
+4096 x 4096 weight in F32, F16 and BF16, Q4_0 17408 x 5120, and the two
+Q4_K shapes), each as back-to-back launches between two HIP events, and
+reports them under "workloads".
+
 Prints ONE JSON line. --gpus N > 1 is refused: the path runs on one GPU.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -31,6 +38,20 @@ PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 LARGE = "q4_k_n14336_k4096_t4096"
 SKINNY = "q4_k_n4096_k14336_t16"
+# Every benchmarked workload: (workload, dense storage type or "").
+WORKLOADS = [
+    ("q8_0_n128_k256_t64", ""),
+    ("dense_n4096_k4096_t512", "f32"),
+    ("dense_n4096_k4096_t512", "f16"),
+    ("dense_n4096_k4096_t512", "bf16"),
+    ("q4_0_n17408_k5120_t2048", ""),
+    (LARGE, ""),
+    (SKINNY, ""),
+]
+# W copies rotated between launches of a workload whose weight could stay
+# in the 256 MB Infinity Cache across launches and is read at the HBM rate
+# (the small-T shape; the others are bound by the matrix rate)
+ROTATE = {SKINNY: 12}
 PROFILES = os.path.join(REPO, "profiles")
 KERNEL_SOURCES = ["quantized_weight_backward_amd/csrc/retro_kernels.h",
                   "quantized_weight_backward_amd/csrc/retro_split_kernel.h",
@@ -39,6 +60,7 @@ KERNEL_SOURCES = ["quantized_weight_backward_amd/csrc/retro_kernels.h",
                   "quantized_weight_backward_amd/csrc/retro_ws_kernel.h",
                   "quantized_weight_backward_amd/csrc/retro_decode.h",
                   "quantized_weight_backward_amd/csrc/retro_api.hip"]
+TYPE_IDS = {"q8_0": 8, "q4_0": 2, "q4_k": 12, "f32": 0, "f16": 1, "bf16": 30, "mxfp4": 39}
 
 
 def kernel_source_hash() -> str:
@@ -54,42 +76,70 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(tag: str):
-    """HBM bytes per launch from a committed counter summary, or None when
-    the summary is missing or the kernels changed since it was taken."""
+def workload_tag(workload: str, dense: str) -> str:
+    """dense_n4096_k4096_t512 + f16 -> f16_n4096_k4096_t512; others unchanged."""
+    return workload.replace("dense", dense) if dense else workload
+
+
+def kernel_family(variant: str) -> str:
+    head = variant.split("_")[0]
+    return {"ws": "out_prod_ws_kernel", "ws2": "out_prod_ws_kernel", "tile": "out_prod_tile_kernel",
+            "split": "out_prod_split_kernel"}.get(head, "out_prod_skinny_kernel")
+
+
+def kernel_prefix(variant: str, wtype: int) -> str:
+    """Start of the demangled kernel name rocprofv3 reports for a variant
+    and weight type (unique within one benchmark run: each type runs one
+    variant of each kernel family)."""
+    return f"void retro::{kernel_family(variant)}<{wtype},"
+
+
+def read_profile_value(tag: str, key: str):
+    """A value recorded in profiles/<tag>_traffic.md, or None when the
+    summary is missing or the kernels changed since it was taken."""
     path = os.path.join(PROFILES, f"{tag}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     src = re.search(r"source_sha256:\s*(\w+)", text)
-    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    val = re.search(key + r":\s*([0-9.eE+]+)", text)
     if not src or not val or src.group(1) != kernel_source_hash():
         return None
     return float(val.group(1))
 
 
+def read_traffic(tag: str):
+    return read_profile_value(tag, "hbm_bytes_per_launch")
+
+
+BENCH_PROFILE_ARGS = "--steps 20 --warmup 3 --reps 20 --no-cpu-baseline"
+COUNTER_ARGS = "--steps 3 --warmup 1 --reps 3 --no-cpu-baseline"
+PROFILE_WARMUP = 3  # launches of each kernel dropped from a trace summary (the bench's warm-up)
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d {out}/prof_trace -o run -- "
-             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+             f"python3 bench.py {BENCH_PROFILE_ARGS}",
     "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/pmc_FETCH_SIZE -o run -- "
-                  "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+                  f"python3 bench.py {COUNTER_ARGS}",
     "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/pmc_WRITE_SIZE -o run -- "
-                  "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+                  f"python3 bench.py {COUNTER_ARGS}",
     "mfma": "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES "
             "GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS -f csv "
-            "-d {out}/pmc_mfma -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+            f"-d {{out}}/pmc_mfma -o run -- python3 bench.py {COUNTER_ARGS}",
+    "waits": "rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_INSTS_SALU "
+             f"SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_MISC -f csv -d {{out}}/pmc_waits -o run -- python3 bench.py "
+             f"{COUNTER_ARGS}",
+    "tcc_req": "rocprofv3 --pmc TCC_EA0_RDREQ TCC_EA0_RDREQ_32B TCC_EA0_RDREQ_64B TCC_EA0_RDREQ_128B -f csv "
+               f"-d {{out}}/pmc_tcc_req -o run -- python3 bench.py {COUNTER_ARGS}",
+    "tcc_hit": "rocprofv3 --pmc TCC_HIT TCC_MISS TCC_EA0_RDREQ_DRAM -f csv "
+               f"-d {{out}}/pmc_tcc_hit -o run -- python3 bench.py {COUNTER_ARGS}",
     "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/pmc_copy_FETCH_SIZE -o run -- "
                        "python3 bench.py --copy-probe-mib 1024",
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/pmc_copy_WRITE_SIZE -o run -- "
                        "python3 bench.py --copy-probe-mib 1024",
 }
-KERNELS = {  # summary tag -> (kernel-name prefix in rocprofv3 output, workload, variant)
-    f"ws_{LARGE}": ("void retro::out_prod_ws_kernel<12, 2, 4, 2, 1, false>", LARGE, "ws_128x256"),
-    f"skinny_{SKINNY}": ("void retro::out_prod_skinny_kernel<12, 16, true>", SKINNY, "skinny"),
-    f"split_{LARGE}": ("void retro::out_prod_split_kernel<12>", LARGE, "split_128x256"),
-}
-LARGE_TAG, SKINNY_TAG = f"ws_{LARGE}", f"skinny_{SKINNY}"
-# Kernel traces of single cases outside the benchmark step (opt-in variants,
+# Counter passes summarised per kernel (each a rocprofv3 run of its own).
+COUNTER_PASSES = ("mfma", "waits", "tcc_req", "tcc_hit")
+# Kernel traces of single cases outside the benchmark run (opt-in variants,
 # the forward), each from its own run of `bench.py --profile-case`:
 # summary tag -> (workload, dense weight type or "", op, variant, kernel-name prefix)
 CASE_TRACES = {
@@ -102,6 +152,7 @@ CASE_TRACES = {
     "mulmat_skinny_q4_k_n4096_k14336_t16": ("q4_k_n4096_k14336_t16", "", "mul_mat", "skinny",
                                             "void retro::mul_mat_skinny_kernel<12>"),
 }
+CASE_WARMUP = 2  # launches --profile-case makes before its timed ones
 
 
 def case_trace_command(tag: str, run_dir: str) -> str:
@@ -112,63 +163,108 @@ def case_trace_command(tag: str, run_dir: str) -> str:
             f"--profile-case {workload}{dense} --op {op} --variant {variant} --launches 10")
 
 
-def _mean_counter(path: str, prefix: str) -> tuple[float, int]:
-    import csv
-
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if r["Kernel_Name"].startswith(prefix)]
-    return (sum(vals) / len(vals) if vals else float("nan")), len(vals)
-
-
 def profile_command(name: str, run_dir: str) -> str:
     """The rocprofv3 command of PROFILE_COMMANDS[name] writing under run_dir."""
     return PROFILE_COMMANDS[name].format(out=os.path.relpath(run_dir, REPO).rstrip("/"))
 
 
+def _find_csv(run_dir: str, sub: str, suffix: str) -> str | None:
+    """rocprofv3 writes <out>/<host>/<pid>_... or <out>/run_<suffix>; find it."""
+    base = os.path.join(run_dir, sub)
+    for root, _, files in os.walk(base):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+def steady_dispatches(trace_csv: str, prefix: str, drop: int) -> tuple[str, list[float]]:
+    """Durations (ns) of the dispatches of the one kernel whose name starts
+    with prefix, in launch order, without the first `drop` (warm-up)."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if r["Kernel_Name"].startswith(prefix)]
+    names = {r["Kernel_Name"] for r in rows}
+    if len(names) != 1:
+        raise RuntimeError(f"{prefix}: expected one kernel, found {sorted(names)}")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+    return names.pop(), durs[drop:]
+
+
+def _counter_means(path: str, prefix: str, drop: int = 1) -> dict:
+    """Per-dispatch counter values of one kernel (the first `drop`
+    dispatches, warm-up, excluded), averaged per counter."""
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Kernel_Name"].startswith(prefix):
+            per.setdefault(r["Counter_Name"], {}).setdefault(int(r["Dispatch_Id"]), 0.0)
+            per[r["Counter_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    out = {}
+    for name, by_dispatch in per.items():
+        vals = [by_dispatch[d] for d in sorted(by_dispatch)][drop:] or list(by_dispatch.values())
+        out[name] = (sum(vals) / len(vals), len(vals))
+    return out
+
+
+def _copy_scale(run_dir: str, sub: str, counter: str) -> tuple[float, float]:
+    path = _find_csv(run_dir, sub, "counter_collection.csv")
+    vals = _counter_means(path, "__amd_rocclr_copyBuffer", drop=0)
+    kib = vals[counter][0]
+    return kib, (1024 << 20) / (kib * 1024)
+
+
+def _stats_row(name: str, durs: list[float]) -> list[str]:
+    us = [d / 1e3 for d in durs]
+    mean = sum(us) / len(us)
+    med = sorted(us)[len(us) // 2]
+    return [f"Kernel: `{name}`", "",
+            "| steady-state launches | mean (us) | median (us) | min (us) | max (us) |", "|---|---|---|---|---|",
+            f"| {len(us)} | {mean:.2f} | {med:.2f} | {min(us):.2f} | {max(us):.2f} |", ""]
+
+
 def summarize(run_dir: str) -> None:
     """Write profiles/<tag>_trace.md, <tag>_traffic.md and <tag>_counters.md
-    from rocprofv3 output under run_dir (the commands in PROFILE_COMMANDS with
-    {out} = run_dir, run from the repository root)."""
-    import csv
+    for every benchmarked workload's kernel, from rocprofv3 output under
+    run_dir (the commands in PROFILE_COMMANDS with {out} = run_dir, run from
+    the repository root). Trace figures are over steady-state dispatches only
+    (each kernel's first PROFILE_WARMUP launches dropped)."""
+    import quantized_weight_backward_amd as q
+    import workloads as wl
 
     os.makedirs(PROFILES, exist_ok=True)
-    stats = list(csv.DictReader(open(os.path.join(run_dir, "prof_trace", "run_kernel_stats.csv"))))
-    copy_bytes = 1024 << 20
-    f_copy, _ = _mean_counter(os.path.join(run_dir, "pmc_copy_FETCH_SIZE", "run_counter_collection.csv"),
-                              "__amd_rocclr_copyBuffer")
-    w_copy, _ = _mean_counter(os.path.join(run_dir, "pmc_copy_WRITE_SIZE", "run_counter_collection.csv"),
-                              "__amd_rocclr_copyBuffer")
-    f_scale = copy_bytes / (f_copy * 1024)
-    w_scale = copy_bytes / (w_copy * 1024)
     src = kernel_source_hash()
-    for tag, (workload, wtype, op, variant, prefix) in CASE_TRACES.items():
-        path = os.path.join(run_dir, f"trace_{tag}", "run_kernel_stats.csv")
-        if not os.path.exists(path):
-            continue
-        row = next(r for r in csv.DictReader(open(path)) if r["Name"].startswith(prefix))
-        lines = [f"# {tag}: rocprofv3 kernel trace", "",
-                 f"Command (repository root): `{case_trace_command(tag, run_dir)}`", "",
-                 f"Kernel: `{row['Name']}` ({op}, workload {workload}{' ' + wtype if wtype else ''}, "
-                 f"variant {variant})", "",
-                 "| calls | average (us) | min (us) | max (us) |", "|---|---|---|---|",
-                 f"| {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | {float(row['MinNs']) / 1e3:.2f} | "
-                 f"{float(row['MaxNs']) / 1e3:.2f} |", "",
-                 f"kernel source_sha256: {src}", ""]
-        open(os.path.join(PROFILES, f"{tag}_trace.md"), "w").write("\n".join(lines))
-        print(f"{tag}: avg {float(row['AverageNs']) / 1e3:.2f} us")
-    for tag, (prefix, workload, _) in KERNELS.items():
-        row = next(r for r in stats if r["Name"].startswith(prefix))
+    trace_csv = _find_csv(run_dir, "prof_trace", "kernel_trace.csv")
+    f_copy, f_scale = _copy_scale(run_dir, "pmc_copy_FETCH_SIZE", "FETCH_SIZE")
+    w_copy, w_scale = _copy_scale(run_dir, "pmc_copy_WRITE_SIZE", "WRITE_SIZE")
+    fetch_csv = _find_csv(run_dir, "pmc_FETCH_SIZE", "counter_collection.csv")
+    write_csv = _find_csv(run_dir, "pmc_WRITE_SIZE", "counter_collection.csv")
+    for workload, dense in WORKLOADS:
+        c = wl.WORKLOADS[workload]
+        wtype = TYPE_IDS[dense] if dense else c["type"]
+        variant = q.VARIANT_NAMES[q.choice(wtype, c["K"], c["N"], c["T"])]
+        prefix = kernel_prefix(variant, wtype)
+        tag = f"{variant}_{workload_tag(workload, dense)}"
+        name, durs = steady_dispatches(trace_csv, prefix, PROFILE_WARMUP)
+        flops = 2.0 * c["T"] * c["N"] * c["K"]
+        mean_s = sum(durs) / len(durs) / 1e9
         lines = [f"# {tag}: rocprofv3 kernel trace", "",
                  f"Command (repository root): `{profile_command('trace', run_dir)}`", "",
-                 f"Kernel: `{row['Name']}` (workload {workload})", "",
-                 "| calls | average (us) | min (us) | max (us) | share of GPU time |",
-                 "|---|---|---|---|---|",
-                 f"| {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | {float(row['MinNs']) / 1e3:.2f} | "
-                 f"{float(row['MaxNs']) / 1e3:.2f} | {float(row['Percentage']):.2f}% |", "",
-                 f"kernel source_sha256: {src}", ""]
+                 f"Workload {workload_tag(workload, dense)}, the kernel retro_out_prod chooses ({variant}). "
+                 f"The first {PROFILE_WARMUP} launches of the kernel (the benchmark's warm-up) are left out.", "",
+                 *_stats_row(name, durs),
+                 f"F32 TFLOP/s at the mean: {flops / mean_s / 1e12:.2f} "
+                 f"(2*T*N*K = {flops:.6g}); fraction of the 157.3 TFLOP/s F32 peak: "
+                 f"{flops / mean_s / 1e12 / PEAK_F32_TFLOPS:.4f}", ""]
+        if workload == SKINNY:
+            wbytes = c["N"] * wl.row_bytes(wtype, c["K"])
+            t_roof = max(wbytes / (PEAK_HBM_GBS * 1e9), flops / (PEAK_F32_TFLOPS * 1e12))
+            lines += [f"Weight GB/s at the mean: {wbytes / mean_s / 1e9:.1f}; fraction of the binding roof "
+                      f"(max of weight bytes / 8 TB/s and FLOPs / 157.3 TFLOP/s = {t_roof * 1e6:.2f} us): "
+                      f"{t_roof / mean_s:.4f}", ""]
+        lines += [f"kernel source_sha256: {src}", ""]
         open(os.path.join(PROFILES, f"{tag}_trace.md"), "w").write("\n".join(lines))
-        fetch, nf = _mean_counter(os.path.join(run_dir, "pmc_FETCH_SIZE", "run_counter_collection.csv"), prefix)
-        write, nw = _mean_counter(os.path.join(run_dir, "pmc_WRITE_SIZE", "run_counter_collection.csv"), prefix)
-        hbm = fetch * 1024 * f_scale + write * 1024 * w_scale
+        fetch = _counter_means(fetch_csv, prefix)["FETCH_SIZE"]
+        write = _counter_means(write_csv, prefix)["WRITE_SIZE"]
+        hbm = fetch[0] * 1024 * f_scale + write[0] * 1024 * w_scale
         lines = [f"# {tag}: HBM traffic per launch (rocprofv3 counters)", "",
                  "Commands (repository root):", "",
                  *[f"- `{profile_command(k, run_dir)}`" for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE",
@@ -177,33 +273,41 @@ def summarize(run_dir: str) -> None:
                  f"read FETCH_SIZE = {f_copy:.1f} KiB and WRITE_SIZE = {w_copy:.1f} KiB per copy launch, so "
                  f"FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}.", "",
                  "| counter | KiB per launch (mean) | launches | scaled bytes |", "|---|---|---|---|",
-                 f"| FETCH_SIZE | {fetch:.1f} | {nf} | {fetch * 1024 * f_scale:.4g} |",
-                 f"| WRITE_SIZE | {write:.1f} | {nw} | {write * 1024 * w_scale:.4g} |", "",
+                 f"| FETCH_SIZE | {fetch[0]:.1f} | {fetch[1]} | {fetch[0] * 1024 * f_scale:.4g} |",
+                 f"| WRITE_SIZE | {write[0]:.1f} | {write[1]} | {write[0] * 1024 * w_scale:.4g} |", "",
                  f"hbm_bytes_per_launch: {hbm:.6g}",
                  f"source_sha256: {src}", ""]
         open(os.path.join(PROFILES, f"{tag}_traffic.md"), "w").write("\n".join(lines))
-        mfma_csv = os.path.join(run_dir, "pmc_mfma", "run_counter_collection.csv")
-        if os.path.exists(mfma_csv):
-            write_counter_summary(tag, prefix, workload, mfma_csv, src, profile_command("mfma", run_dir))
-        print(f"{tag}: avg {float(row['AverageNs']) / 1e3:.2f} us, traffic {hbm / 1e6:.1f} MB per launch")
+        write_counter_summary(tag, prefix, c, run_dir, src)
+        print(f"{tag}: mean {sum(durs) / len(durs) / 1e3:.2f} us over {len(durs)}, traffic {hbm / 1e6:.1f} MB")
+    for tag, (workload, dense, op, variant, prefix) in CASE_TRACES.items():
+        path = _find_csv(run_dir, f"trace_{tag}", "kernel_trace.csv")
+        if not path:
+            continue
+        name, durs = steady_dispatches(path, prefix, CASE_WARMUP)
+        lines = [f"# {tag}: rocprofv3 kernel trace", "",
+                 f"Command (repository root): `{case_trace_command(tag, run_dir)}`", "",
+                 f"{op}, workload {workload_tag(workload, dense)}, variant {variant}; the first {CASE_WARMUP} "
+                 "launches (warm-up) are left out.", "",
+                 *_stats_row(name, durs), f"kernel source_sha256: {src}", ""]
+        open(os.path.join(PROFILES, f"{tag}_trace.md"), "w").write("\n".join(lines))
+        print(f"{tag}: mean {sum(durs) / len(durs) / 1e3:.2f} us")
 
 
-def write_counter_summary(tag: str, prefix: str, workload: str, path: str, src: str, command: str) -> None:
-    """profiles/<tag>_counters.md: per-launch means of the MFMA pass, with
-    the checks of the F32 MFMA work against 2*T*N*K (one MOP = 512 FLOPs)."""
-    import csv
-
-    import workloads as wl
-
-    per = {}
-    for r in csv.DictReader(open(path)):
-        if r["Kernel_Name"].startswith(prefix):
-            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    mean = {k: sum(v) / len(v) for k, v in per.items()}
-    case = wl.WORKLOADS[workload]
+def write_counter_summary(tag: str, prefix: str, case: dict, run_dir: str, src: str) -> None:
+    """profiles/<tag>_counters.md: per-launch means of the counter passes,
+    with the F32 MFMA work checked against 2*T*N*K (one MOP = 512 FLOPs)."""
+    mean, commands = {}, []
+    for p in COUNTER_PASSES:
+        path = _find_csv(run_dir, f"pmc_{p}", "counter_collection.csv")
+        if path:
+            mean.update({k: v[0] for k, v in _counter_means(path, prefix).items()})
+            commands.append(profile_command(p, run_dir))
+    if not mean:
+        return
     flops = 2.0 * case["T"] * case["N"] * case["K"]
-    lines = [f"# {tag}: MFMA and LDS counters per launch (rocprofv3)", "",
-             f"Command (repository root): `{command}`", "",
+    lines = [f"# {tag}: counters per launch (rocprofv3)", "", "Commands (repository root), one pass each:", "",
+             *[f"- `{c}`" for c in commands], "",
              "| counter | mean per launch |", "|---|---|",
              *[f"| {k} | {v:.6g} |" for k, v in sorted(mean.items())], ""]
     mops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_F32")
@@ -220,8 +324,29 @@ def write_counter_summary(tag: str, prefix: str, workload: str, path: str, src: 
     if valu and cu:
         lines += [f"VALU instructions per SIMD per busy cycle = SQ_INSTS_VALU / (4 * SQ_BUSY_CU_CYCLES) = "
                   f"{valu / (4 * cu):.4f} (a wave64 VALU instruction occupies a SIMD for about 4 cycles)", ""]
+    wcyc, wany = mean.get("SQ_WAVE_CYCLES"), mean.get("SQ_WAIT_ANY")
+    if wcyc and wany:
+        lines += [f"Waves waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES) = {wany / wcyc:.4f}", ""]
+    req = mean.get("TCC_EA0_RDREQ_sum") or mean.get("TCC_EA0_RDREQ")
+    if req:
+        b32 = mean.get("TCC_EA0_RDREQ_32B_sum") or mean.get("TCC_EA0_RDREQ_32B") or 0.0
+        b64 = mean.get("TCC_EA0_RDREQ_64B_sum") or mean.get("TCC_EA0_RDREQ_64B") or 0.0
+        b128 = mean.get("TCC_EA0_RDREQ_128B_sum") or mean.get("TCC_EA0_RDREQ_128B") or 0.0
+        lines += [f"L2-to-memory read requests: {req:.6g} (32 B: {b32:.6g}, 64 B: {b64:.6g}, 128 B: {b128:.6g}); "
+                  f"bytes by size {32 * b32 + 64 * b64 + 128 * b128:.6g}", ""]
+    hit, miss = mean.get("TCC_HIT_sum") or mean.get("TCC_HIT"), mean.get("TCC_MISS_sum") or mean.get("TCC_MISS")
+    if hit is not None and miss:
+        lines += [f"L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS) = {hit / (hit + miss):.4f}", ""]
     lines += [f"source_sha256: {src}", ""]
     open(os.path.join(PROFILES, f"{tag}_counters.md"), "w").write("\n".join(lines))
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        return ""
 
 
 def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
@@ -244,14 +369,8 @@ def cpu_baseline(case: dict, target_s: float = 20.0) -> dict:
     oracle.out_prod(case["type"], case["W"], case["G"], K, rows=rows, nthreads=cores)
     secs = time.perf_counter() - t0
     flops = 2.0 * N * K * nrows
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
-    except OSError:
-        pass
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "host_cpu": model, "host_threads": os.cpu_count(),
+            "host_cpu": host_cpu(), "host_threads": os.cpu_count(),
             "sample": f"{nrows} of {case['T']} t rows of {LARGE} (full decode of W included), "
                       f"{secs:.1f} s"}
 
@@ -269,16 +388,12 @@ def cpu_baseline_skinny(case: dict) -> dict:
             "sample": f"all {case['T']} t rows of {SKINNY} (full decode of W included), {secs:.2f} s"}
 
 
-def kernel_family(variant: str) -> str:
-    return {"ws": "out_prod_ws_kernel", "tile": "out_prod_tile_kernel"}.get(variant.split("_")[0].rstrip("2"),
-                                                                         "out_prod_skinny_kernel")
-
-
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=20, help="back-to-back launches per workload timed after the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this size (counter calibration)")
@@ -309,6 +424,7 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs cuda:0"
     dev = torch.device("cuda:0")
+    ids = {v: k for k, v in q.VARIANT_NAMES.items()}
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -323,7 +439,7 @@ def main() -> int:
     if args.profile_case:
         wtype = {"f32": q.F32, "f16": q.F16, "bf16": q.BF16}.get(args.wtype) if args.wtype else None
         c = wl.workload(args.profile_case, wtype)
-        vid = 0 if args.variant == "auto" else {v: k for k, v in q.VARIANT_NAMES.items()}[args.variant]
+        vid = 0 if args.variant == "auto" else ids[args.variant]
         W = torch.from_numpy(c["W"]).to(dev)
         if args.op == "out_prod":
             G = torch.from_numpy(c["G"]).to(dev)
@@ -333,7 +449,7 @@ def main() -> int:
             X = torch.randn((c["T"], c["K"]), device=dev)
             out = torch.empty((c["T"], c["N"]), dtype=torch.float32, device=dev)
             call = lambda: q.mul_mat(c["type"], W, X, out=out, variant=vid)
-        for _ in range(2):
+        for _ in range(CASE_WARMUP):
             call()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.launches)]
         for e in ev:
@@ -355,7 +471,7 @@ def main() -> int:
     Dl = torch.empty((large["T"], large["K"]), dtype=torch.float32, device=dev)
     # several copies of the skinny W (33 MB each) so that consecutive calls
     # cannot be served from the 256 MB Infinity Cache
-    n_rot = 12
+    n_rot = ROTATE[SKINNY]
     Ws = [torch.from_numpy(skinny["W"]).to(dev) for _ in range(n_rot)]
     Gs = torch.from_numpy(skinny["G"]).to(dev)
     Ds = torch.empty((skinny["T"], skinny["K"]), dtype=torch.float32, device=dev)
@@ -375,6 +491,7 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
+    print("bench: timing the step", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -394,11 +511,69 @@ def main() -> int:
     fl_skinny = 2.0 * skinny["T"] * skinny["N"] * skinny["K"]
     wbytes = float(skinny["W"].nbytes)
     avg_large = float(t_large.mean())
-    avg_skinny = float(t_skinny.mean())
     achieved = fl_large / avg_large / 1e12
-    traffic = read_traffic(LARGE_TAG) if q.VARIANT_NAMES[v_large] == KERNELS[LARGE_TAG][2] else None
     ms_per_step = wall / args.steps * 1e3
     value = (fl_large + fl_skinny) / (wall / args.steps) / 1e12
+    large_tag = f"{q.VARIANT_NAMES[v_large]}_{LARGE}"
+    skinny_tag = f"{q.VARIANT_NAMES[v_skinny]}_{SKINNY}"
+
+    def back_to_back(call, reps):
+        """Mean launch time (s) of `reps` launches enqueued back to back
+        between two HIP events on the launch stream. A spin of about a
+        millisecond goes first, so that the host has queued every launch
+        before the first event completes and host launch overhead cannot
+        leave the GPU idle between them."""
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(2_000_000)
+        b0.record(stream)
+        for i in range(reps):
+            call(i)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) * 1e-3 / reps
+
+    # The small-T kernel on its own: launch pairs inside the step include the
+    # events' own overhead (a few us against a ~25 us kernel), so its figures
+    # come from launches back to back on rotated W copies.
+    avg_skinny = back_to_back(lambda i: q.out_prod(q.Q4_K, Ws[i % n_rot], Gs, skinny["K"], out=Ds),
+                              max(args.reps, 2 * n_rot))
+
+    # Every benchmarked workload at the kernel retro_out_prod chooses.
+    print("bench: timing every workload", file=sys.stderr, flush=True)
+    per_workload = []
+    for workload, dense in WORKLOADS:
+        if workload == LARGE:
+            c, W_list, G, D = large, [Wl], Gl, Dl
+        elif workload == SKINNY:
+            c, W_list, G, D = skinny, Ws, Gs, Ds
+        else:
+            c = wl.workload(workload, TYPE_IDS[dense] if dense else None)
+            W_list = [torch.from_numpy(c["W"]).to(dev) for _ in range(ROTATE.get(workload, 1))]
+            G = torch.from_numpy(c["G"]).to(dev)
+            D = torch.empty((c["T"], c["K"]), dtype=torch.float32, device=dev)
+        wtype, K, N, T = c["type"], c["K"], c["N"], c["T"]
+        variant = q.VARIANT_NAMES[q.choice(wtype, K, N, T)]
+        call = lambda i: q.out_prod(wtype, W_list[i % len(W_list)], G, K, out=D)  # noqa: E731
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        reps = max(args.reps, 2 * len(W_list))
+        sec = back_to_back(call, reps)
+        flops = 2.0 * T * N * K
+        wb = float(c["W"].nbytes)
+        t_roof = max(wb / (PEAK_HBM_GBS * 1e9), flops / (PEAK_F32_TFLOPS * 1e12))
+        tag = f"{variant}_{workload_tag(workload, dense)}"
+        per_workload.append({
+            "workload": workload_tag(workload, dense), "weight_type": wl.TYPE_NAMES[wtype], "kernel": variant,
+            "launches": reps, "avg_launch_us": round(sec * 1e6, 3), "tflops": round(flops / sec / 1e12, 3),
+            "f32_mfma_frac": round(flops / sec / 1e12 / PEAK_F32_TFLOPS, 4),
+            "weight_gbs": round(wb / sec / 1e9, 1), "hbm_frac_weights": round(wb / sec / 1e9 / PEAK_HBM_GBS, 4),
+            "binding_roof": "f32_mfma" if flops / (PEAK_F32_TFLOPS * 1e12) >= wb / (PEAK_HBM_GBS * 1e9) else "hbm",
+            "binding_roof_frac": round(t_roof / sec, 4), "traffic": read_traffic(tag),
+            "w_copies_rotated": len(W_list)})
+        if workload not in (LARGE, SKINNY):
+            del W_list, G, D
+            torch.cuda.empty_cache()
 
     # The exact-split variant (bf16 MFMA on exact operand parts; opt-in, never
     # chosen automatically) on the large workload, timed after the step loop.
@@ -420,7 +595,8 @@ def main() -> int:
         chunks = -(-large["N"] // 32)
         issued = tiles * chunks * (384 * 32768 + 24 * 16384)
         avg_split = float(t_split.mean())
-        split = {"kernel": "out_prod_split_kernel (split_128x256)", "traffic": read_traffic(f"split_{LARGE}"),
+        split = {"kernel": "out_prod_split_kernel (split_128x256)",
+                 "traffic": read_traffic(f"split_128x256_{LARGE}"),
                  "avg_launch_ms": round(avg_split * 1e3, 4),
                  "min_launch_ms": round(float(t_split.min()) * 1e3, 4),
                  "tflops": round(fl_large / avg_split / 1e12, 3),
@@ -457,6 +633,8 @@ def main() -> int:
                 "mfma_f32_clock_ghz": round(mfma_f32 / PEAK_F32_TFLOPS * 2.4, 3)}
     if split is not None:
         split["bf16_mfma_frac_of_measured"] = round(split["bf16_flops_issued_per_launch"] / avg_split / 1e12 / mfma_bf16, 4)
+    for entry in per_workload:
+        entry["f32_mfma_frac_of_measured"] = round(entry["tflops"] / mfma_f32, 4)
 
     skinny_tflops = fl_skinny / avg_skinny / 1e12
     skinny_gbs = wbytes / avg_skinny / 1e9
@@ -483,13 +661,14 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 4),
                      "frac_of_measured": round(achieved / mfma_f32, 4),
-                     "traffic": traffic,
+                     "traffic": read_traffic(large_tag),
                      "kernel": f"{kernel_family(q.VARIANT_NAMES[v_large])} ({q.VARIANT_NAMES[v_large]})",
                      "avg_launch_ms": round(avg_large * 1e3, 4), "min_launch_ms": round(float(t_large.min()) * 1e3, 4),
                      "flops_per_launch": fl_large},
-        "skinny": {"kernel": "out_prod_skinny_kernel", "traffic": read_traffic(SKINNY_TAG),
+        "skinny": {"kernel": f"{kernel_family(q.VARIANT_NAMES[v_skinny])} ({q.VARIANT_NAMES[v_skinny]})",
+                   "traffic": read_traffic(skinny_tag),
                    "avg_launch_us": round(avg_skinny * 1e6, 3),
-                   "min_launch_us": round(float(t_skinny.min()) * 1e6, 3),
+                   "avg_launch_us_event_pairs": round(float(t_skinny.mean()) * 1e6, 3),
                    "tflops": round(skinny_tflops, 3), "weight_gbs": round(skinny_gbs, 1),
                    "hbm_frac": round(skinny_gbs / PEAK_HBM_GBS, 4),
                    "f32_mfma_frac": round(skinny_tflops / PEAK_F32_TFLOPS, 4),
@@ -497,6 +676,7 @@ def main() -> int:
                    "hbm_frac_of_measured_copy": round(skinny_gbs / copy_gbs, 4),
                    "binding_roof_frac": round(t_roof / avg_skinny, 4),
                    "weight_bytes": wbytes},
+        "workloads": per_workload,
         "exact_split": split,
         "ceilings": ceilings,
         "kernel_source": kernel_source_hash(),
