@@ -25,6 +25,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F32, F16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16 = 0, 1, 2, 3, 6, 7, 8, 10, 11, 12, 13, 14, 30
 MXFP4 = 39
+NVFP4 = 40
 
 _lib = None
 

@@ -46,6 +46,16 @@
  * Microscaling (MX) specification (E2M1 elements, an E8M0 shared scale), in
  * the GGUF block order, pinned to hand-derived fixtures.
  *
+ * Parity unpinned against the pages: NVFP4. The PR's type sweep names it and
+ * prints no block. The element and scale encodings are those of NVIDIA's
+ * NVFP4 format (E2M1 elements, one FP8 E4M3 scale per 16 elements; the
+ * per-tensor F32 scale of that format is not part of a block and is taken
+ * as 1). The block layout is this library's reading: 64 elements in 36
+ * bytes, the four sub-block scales first, then 8 code bytes per sub-block in
+ * the nibble order MXFP4 uses within its block. Pinned to hand-derived
+ * fixtures, to the E4M3 decode of an independent library and to the pinned
+ * E2M1 decode of MXFP4.
+ *
  * Parity unpinned against the pages: Q2_K, Q3_K, Q5_K and Q6_K as a whole.
  * The pages name the K-quant family only through the Q4_K_M files it is
  * used in; these layouts are the GGUF ones, and the tests pin them to
@@ -60,7 +70,7 @@
 
 enum {
     T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q4_1 = 3, T_Q5_0 = 6, T_Q5_1 = 7, T_Q8_0 = 8, T_Q2_K = 10, T_Q3_K = 11,
-    T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_BF16 = 30, T_MXFP4 = 39
+    T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_BF16 = 30, T_MXFP4 = 39, T_NVFP4 = 40
 };
 
 /* An E2M1 code (bit 3 sign, bits 2..1 exponent, bit 0 mantissa; exponent
@@ -70,6 +80,18 @@ static double e2m1_value(int code) {
     const int E = (code >> 1) & 3, m = code & 1;
     const double mag = E == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, E - 1);
     return (code & 8) ? -mag : mag;
+}
+
+/* An FP8 E4M3 byte (the OCP 8-bit floating-point format E4M3, which NVFP4
+ * uses for its block scales): bit 7 sign, bits 6..3 exponent E (bias 7),
+ * bits 2..0 mantissa m. E = 0 is the subnormal range, value m/8 * 2^-6;
+ * otherwise (1 + m/8) * 2^(E - 7). There are no infinities: E = 15 with
+ * m = 7 is NaN (both signs), so the largest value is 1.75 * 2^8 = 448. */
+static double e4m3_value(int byte) {
+    const int E = (byte >> 3) & 15, m = byte & 7;
+    if (E == 15 && m == 7) return NAN;
+    const double mag = E == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, E - 10);
+    return (byte & 0x80) ? -mag : mag;
 }
 
 /* IEEE-754 binary16 -> binary32: 1 sign bit, 5 exponent bits (bias 15), 10
@@ -206,6 +228,26 @@ int oracle_decode_row(int type, const uint8_t *row, int64_t K, float *out) {
             for (int j = 0; j < 16; j++) {
                 out[32 * b + j] = (float)(e2m1_value(blk[1 + j] & 15) * scale);
                 out[32 * b + j + 16] = (float)(e2m1_value(blk[1 + j] >> 4) * scale);
+            }
+        }
+        return 0;
+    case T_NVFP4:
+        /* 36-byte block of 64 elements: four E4M3 scale bytes, scale s for
+         * the 16 elements 16s .. 16s + 15, then 32 code bytes, 8 per
+         * sub-block: element 16s + i (i < 8) is the low nibble of code byte
+         * 8s + i, element 16s + 8 + i its high nibble. value = e2m1(code) *
+         * scale_s, exact in double (at most 2 + 4 significant bits) and
+         * rounded once to F32, which is exact in range. */
+        if (K % 64) return -1;
+        for (b = 0; b < K / 64; b++) {
+            const uint8_t *blk = row + 36 * b;
+            for (int sb = 0; sb < 4; sb++) {
+                const double scale = e4m3_value(blk[sb]);
+                for (int i = 0; i < 8; i++) {
+                    const int c = blk[4 + 8 * sb + i];
+                    out[64 * b + 16 * sb + i] = (float)(e2m1_value(c & 15) * scale);
+                    out[64 * b + 16 * sb + 8 + i] = (float)(e2m1_value(c >> 4) * scale);
+                }
             }
         }
         return 0;
@@ -378,6 +420,7 @@ int64_t oracle_row_bytes(int type, int64_t K) {
     case T_Q5_K: return K % 256 ? -1 : K / 256 * 176;
     case T_Q6_K: return K % 256 ? -1 : K / 256 * 210;
     case T_MXFP4: return K % 32 ? -1 : K / 32 * 17;
+    case T_NVFP4: return K % 64 ? -1 : K / 64 * 36;
     default: return -1;
     }
 }

@@ -142,6 +142,10 @@ def golden_blocks(read):
     for name in ("mx_a", "mx_b", "mx_c", "mx_d", "mx_e"):
         out.append((f"mxfp4_blocks.txt:{name}", wl.MXFP4, 32, hexbytes(g[name + "_hex"]),
                     spot(g[name + "_expected"])))
+    g = read("nvfp4_blocks.txt")
+    for name in ("nv_a", "nv_b", "nv_c"):
+        out.append((f"nvfp4_blocks.txt:{name}", wl.NVFP4, 64, hexbytes(g[name + "_hex"]),
+                    spot(g[name + "_expected"])))
     g4 = read("q4_k_pack.txt")
     field = hexbytes(g4["field_hex"])
     out.append(("q4_k_pack.txt", wl.Q4_K, 256, q4_k_superblock(0x3C00, 0x3C00, field, ramp_codes(128)),

@@ -18,8 +18,8 @@ from blocks import (hexbytes, pack_q3_k_field, pack_q4_k_field, q2_k_superblock,
                     q4_k_superblock, q5_k_superblock, q6_k_superblock, ramp_codes)
 from blocks import fixture_value as _fixture_value
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K,
-         wl.Q5_K, wl.Q6_K]
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.NVFP4, wl.Q2_K, wl.Q3_K,
+         wl.Q4_K, wl.Q5_K, wl.Q6_K]
 
 
 
@@ -141,6 +141,58 @@ def test_mxfp4_hand_built_blocks(golden, name):
             assert np.isnan(got[int(e)]), (name, item)
         else:
             assert got[int(e)] == want and np.signbit(got[int(e)]) == np.signbit(want), (name, item)
+
+
+@pytest.mark.parametrize("name", ["nv_a", "nv_b", "nv_c"])
+def test_nvfp4_hand_built_blocks(golden, name):
+    g = golden("nvfp4_blocks.txt")
+    got = oracle.dequantize(wl.NVFP4, hexbytes(g[name + "_hex"]), 64)[0]
+    for item in g[name + "_expected"]:
+        e, v = item.split("=")
+        want = np.float32(_fixture_value(v))
+        if np.isnan(want):
+            assert np.isnan(got[int(e)]), (name, item)
+        else:
+            assert got[int(e)] == want and np.signbit(got[int(e)]) == np.signbit(want), (name, item)
+
+
+def test_nvfp4_scale_is_fp8_e4m3_of_an_independent_library():
+    """Every one of the 256 scale bytes, under codes of value 1 (nibble 2):
+    the decoded elements are the scale itself, which must be torch's
+    float8_e4m3fn value of the byte (NaN for 0x7F and 0xFF, subnormals for
+    exponent 0, signs and zeros included)."""
+    blk = np.zeros((64, 36), dtype=np.uint8)
+    blk[:, 0:4] = np.arange(256, dtype=np.uint8).reshape(64, 4)  # scale byte 4 i + s of block i
+    blk[:, 4:] = 0x22
+    got = oracle.dequantize(wl.NVFP4, blk, 64).reshape(64, 4, 16)
+    ref = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy().reshape(64, 4)
+    for i in range(16):
+        col = got[:, :, i]
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(col), nan)
+        assert np.array_equal(col[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_nvfp4_codes_are_the_pinned_e2m1():
+    """Under scale 1 (E4M3 0x38) every code byte decodes, nibble for nibble,
+    to the values MXFP4 gives the same byte under scale 1 (E8M0 127): the
+    E2M1 decode pinned above. Element 16s + i takes the low nibble of code
+    byte 8s + i and element 16s + 8 + i its high nibble."""
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)  # 8 NVFP4 blocks of 32 code bytes
+    nv = np.zeros((8, 36), dtype=np.uint8)
+    nv[:, 0:4] = 0x38
+    nv[:, 4:] = codes
+    got = oracle.dequantize(wl.NVFP4, nv, 64).reshape(8, 4, 2, 8)  # block, sub-block, half, i
+    mx = np.zeros((16, 17), dtype=np.uint8)
+    mx[:, 0] = 127
+    mx[:, 1:] = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    ref = oracle.dequantize(wl.MXFP4, mx, 32)  # row r: byte 16 r + j -> lo at j, hi at j + 16
+    lo_of = ref[:, :16].reshape(-1)
+    hi_of = ref[:, 16:].reshape(-1)
+    b = codes.reshape(8, 4, 8)  # the byte under (block, sub-block, i)
+    for half, table in ((0, lo_of), (1, hi_of)):
+        want = table[b]
+        assert np.array_equal(got[:, :, half, :].view(np.uint32), want.view(np.uint32)), half
 
 
 def test_mxfp4_structure():
@@ -625,6 +677,8 @@ def test_row_bytes():
     assert oracle.row_bytes(wl.F32, 4096) == 16384
     assert oracle.row_bytes(wl.MXFP4, 5120) == 2720
     assert oracle.row_bytes(wl.MXFP4, 48) == -1
+    assert oracle.row_bytes(wl.NVFP4, 5120) == 2880
+    assert oracle.row_bytes(wl.NVFP4, 96) == -1
     assert oracle.row_bytes(wl.Q4_K, 100) == -1
     assert oracle.row_bytes(99, 32) == -1
 

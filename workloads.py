@@ -20,6 +20,8 @@ blocks; fp16 fields are little-endian; GGUF block formats):
         bits, 16 bytes of 4-bit codes
   MXFP4 17 bytes per 32 elements: an E8M0 scale byte, then 16 bytes of
         E2M1 codes
+  NVFP4 36 bytes per 64 elements: four FP8 E4M3 scale bytes (one per 16
+        elements), then 32 bytes of E2M1 codes
   Q4_K  144 bytes per 256 elements: fp16 scale, fp16 min-scale, 12 bytes
         holding eight 6-bit sub-scales and eight 6-bit sub-mins, then 128
         bytes of 4-bit codes
@@ -41,6 +43,8 @@ integers; N(0, s) takes s as the standard deviation):
         codes U{0..15} / U{0..31}
   Q5_0  scale U[1e-3, 1e-2) rounded to fp16, codes U{0..31}
   MXFP4 scale byte U{117..120} (scales 2^-10 .. 2^-7), codes U{0..15}
+  NVFP4 scale bytes U{0x08..0x37} (positive normal E4M3 values 2^-6 ..
+        1.875 * 2^-1), codes U{0..15}
   Q4_K  scale and min-scale U[1e-4, 1e-3) rounded to fp16, sub-scales and
         sub-mins U{0..63}, codes U{0..15}
   Q5_K  as Q4_K, codes U{0..31}
@@ -74,15 +78,17 @@ import numpy as np
 # GGUF tensor-type ids
 F32, F16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16 = 0, 1, 2, 3, 6, 7, 8, 10, 11, 12, 13, 14, 30
 MXFP4 = 39
+NVFP4 = 40  # this library's id for it (the pages give no number)
 
 TYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", Q8_0: "q8_0", Q4_0: "q4_0", Q4_1: "q4_1", Q5_0: "q5_0",
-              Q5_1: "q5_1", MXFP4: "mxfp4", Q2_K: "q2_k", Q3_K: "q3_k", Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k"}
+              Q5_1: "q5_1", MXFP4: "mxfp4", NVFP4: "nvfp4", Q2_K: "q2_k", Q3_K: "q3_k", Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k"}
 TYPE_IDS = {v: k for k, v in TYPE_NAMES.items()}
 
 # (elements per block, bytes per block)
 _GEOMETRY = {F32: (1, 4), F16: (1, 2), BF16: (1, 2), Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144),
              Q5_K: (256, 176), Q6_K: (256, 210), Q2_K: (256, 84), Q3_K: (256, 110), Q4_1: (32, 20),
-             Q5_0: (32, 22), Q5_1: (32, 24), MXFP4: (32, 17)}
+             Q5_0: (32, 22), Q5_1: (32, 24), MXFP4: (32, 17),
+             NVFP4: (64, 36)}
 
 
 def block_geometry(wtype: int) -> tuple[int, int]:
@@ -146,6 +152,9 @@ def make_weight(wtype: int, N: int, K: int, rng: np.random.Generator) -> np.ndar
     elif wtype == MXFP4:
         out[:, :, 0] = rng.integers(117, 121, size=(N, nb), dtype=np.uint8)
         out[:, :, 1:17] = rng.integers(0, 256, size=(N, nb, 16), dtype=np.uint8)
+    elif wtype == NVFP4:
+        out[:, :, 0:4] = rng.integers(0x08, 0x38, size=(N, nb, 4), dtype=np.uint8)
+        out[:, :, 4:36] = rng.integers(0, 256, size=(N, nb, 32), dtype=np.uint8)
     elif wtype == Q4_K:
         d = _fp16_uniform(rng, 1e-4, 1e-3, (N, nb))
         dmin = _fp16_uniform(rng, 1e-4, 1e-3, (N, nb))
@@ -246,6 +255,8 @@ WORKLOADS = {
     "q5_0_n17408_k5120_t2048": dict(type=Q5_0, N=17408, K=5120, T=2048, seed=1015, g_sigma=1e-2),
     "q5_1_n17408_k5120_t2048": dict(type=Q5_1, N=17408, K=5120, T=2048, seed=1016, g_sigma=1e-2),
     "mxfp4_n17408_k5120_t2048": dict(type=MXFP4, N=17408, K=5120, T=2048, seed=1017, g_sigma=1e-2),
+    "nvfp4_n17408_k5120_t2048": dict(type=NVFP4, N=17408, K=5120, T=2048, seed=1018, g_sigma=1e-2),
+    "nvfp4_n4096_k14336_t16": dict(type=NVFP4, N=4096, K=14336, T=16, seed=1019, g_sigma=1.0),
 }
 
 
