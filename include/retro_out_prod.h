@@ -38,6 +38,15 @@
  *               E2M1 codes in the Q4_0 nibble order (OCP Microscaling:
  *               sign, 2-bit exponent, 1-bit mantissa); value
  *               e2m1(q) * 2^(e-127), e = 255 NaN; blocks only byte-aligned
+ *   RETRO_NVFP4 36 bytes / 64 elements: four FP8 E4M3 scale bytes (one per
+ *               16-element sub-block: sign, 4-bit exponent with bias 7,
+ *               3-bit mantissa; subnormals m * 2^-9, 0x7F/0xFF NaN), then 32
+ *               bytes of E2M1 codes, 8 per sub-block: element 16s + i (i < 8)
+ *               = low nibble of code byte 8s + i, 16s + 8 + i its high
+ *               nibble; value e2m1(q) * scale_s. NVIDIA's NVFP4 element and
+ *               scale encodings; the block layout is this library's reading
+ *               (the format's per-tensor F32 scale lies outside the blocks:
+ *               a caller applies it to G or dst)
  *   RETRO_Q4_K  144 bytes / 256 elements: fp16 d, fp16 dmin, 12 bytes of
  *               eight 6-bit sub-scales sc_j and sub-mins m_j (GGUF packing),
  *               128 bytes of nibbles (each 64-element chunk c uses 32 bytes:
@@ -104,7 +113,8 @@ enum {
     RETRO_Q5_K = 13,
     RETRO_Q6_K = 14,
     RETRO_BF16 = 30,
-    RETRO_MXFP4 = 39
+    RETRO_MXFP4 = 39,
+    RETRO_NVFP4 = 40
 };
 
 /* Error codes. */
@@ -126,12 +136,13 @@ enum {
 
 /*
  * dst[t][k] = sum_n W[n][k] * G[t][n] for t < T, k < K.
- *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_1/Q5_0/Q5_1/MXFP4/Q2_K/Q3_K/Q4_K/Q5_K/Q6_K
+ *   type    one of RETRO_F32/F16/BF16/Q8_0/Q4_0/Q4_1/Q5_0/Q5_1/MXFP4/NVFP4/Q2_K/Q3_K/Q4_K/Q5_K/Q6_K
  *   W       device, N * retro_row_bytes(type, K) bytes
  *   G       device, T * N floats
  *   dst     device, T * K floats, overwritten
- *   K       elements per W row (a multiple of the block: 32 for Q8_0/Q4_0,
- *           256 for the K-quants Q2_K..Q6_K, 1 otherwise)
+ *   K       elements per W row (a multiple of the block: 32 for Q8_0, Q4_0,
+ *           Q4_1, Q5_0, Q5_1 and MXFP4, 64 for NVFP4, 256 for the K-quants
+ *           Q2_K..Q6_K, 1 otherwise)
  *   N       rows of W = the reduction length
  *   T       rows of G and dst
  * T == 0 or K == 0: returns RETRO_OK without touching memory (pointers may
@@ -167,7 +178,7 @@ int retro_out_prod_supported(int type, int64_t K, int64_t N, int64_t T);
 /* Bytes per W row, from the block formats above (the PR's OUT_PROD reads
  * src0 as whole rows of blocks, section "What"): K/32*34 (Q8_0), K/32*18
  * (Q4_0), K/32*20 (Q4_1), K/32*22 (Q5_0), K/32*24 (Q5_1), K/32*17 (MXFP4),
- * K/256*84 (Q2_K), K/256*110 (Q3_K), K/256*144 (Q4_K), K/256*176 (Q5_K),
+ * K/64*36 (NVFP4), K/256*84 (Q2_K), K/256*110 (Q3_K), K/256*144 (Q4_K), K/256*176 (Q5_K),
  * K/256*210 (Q6_K), 4K (F32), 2K (F16, BF16). -1 for an unknown type, a
  * negative K or a K that is not a whole number of blocks. Touches no
  * device. */

@@ -26,9 +26,9 @@ import torch  # noqa: F401
 from . import _build
 
 F32, F16, Q4_0, Q4_1, Q5_0, Q5_1, Q8_0 = 0, 1, 2, 3, 6, 7, 8
-Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16, MXFP4 = 10, 11, 12, 13, 14, 30, 39
+Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, BF16, MXFP4, NVFP4 = 10, 11, 12, 13, 14, 30, 39, 40
 TYPES = {"f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0,
-         "q5_1": Q5_1, "mxfp4": MXFP4, "q2_k": Q2_K, "q3_k": Q3_K, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+         "q5_1": Q5_1, "mxfp4": MXFP4, "nvfp4": NVFP4, "q2_k": Q2_K, "q3_k": Q3_K, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 
 OK = 0
 E_TYPE, E_SHAPE, E_NULL, E_ALIGN, E_ALIAS, E_HIP, E_VARIANT = -1, -2, -3, -4, -5, -6, -7

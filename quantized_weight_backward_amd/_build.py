@@ -24,7 +24,8 @@ UNIT_SOURCE = os.path.join(CSRC, "retro_unit.hip")
 PROBE_SOURCE = os.path.join(CSRC, "retro_probe.hip")
 # GGUF ids of the weight types, one kernel object each
 UNIT_TYPES = {"f32": 0, "f16": 1, "q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8, "q2_k": 10, "q3_k": 11,
-              "q4_k": 12, "q5_k": 13, "q6_k": 14, "bf16": 30, "mxfp4": 39}
+              "q4_k": 12, "q5_k": 13, "q6_k": 14, "bf16": 30, "mxfp4": 39,
+              "nvfp4": 40}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

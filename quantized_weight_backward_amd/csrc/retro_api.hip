@@ -247,6 +247,7 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         case RETRO_Q5_0: return launch_out_prod<RETRO_Q5_0>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q5_1: return launch_out_prod<RETRO_Q5_1>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_MXFP4: return launch_out_prod<RETRO_MXFP4>(variant, W, G, dst, K, N, T, s, st);
+        case RETRO_NVFP4: return launch_out_prod<RETRO_NVFP4>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q4_K: return launch_out_prod<RETRO_Q4_K>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q5_K: return launch_out_prod<RETRO_Q5_K>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_Q2_K: return launch_out_prod<RETRO_Q2_K>(variant, W, G, dst, K, N, T, s, st);
@@ -334,6 +335,7 @@ int mul_mat_impl(int variant, int type, const void* W, const float* X, float* Y,
         case RETRO_Q5_0: return launch_mul_mat<RETRO_Q5_0>(variant, W, X, Y, K, N, T, st);
         case RETRO_Q5_1: return launch_mul_mat<RETRO_Q5_1>(variant, W, X, Y, K, N, T, st);
         case RETRO_MXFP4: return launch_mul_mat<RETRO_MXFP4>(variant, W, X, Y, K, N, T, st);
+        case RETRO_NVFP4: return launch_mul_mat<RETRO_NVFP4>(variant, W, X, Y, K, N, T, st);
         case RETRO_Q4_K: return launch_mul_mat<RETRO_Q4_K>(variant, W, X, Y, K, N, T, st);
         case RETRO_Q5_K: return launch_mul_mat<RETRO_Q5_K>(variant, W, X, Y, K, N, T, st);
         case RETRO_Q2_K: return launch_mul_mat<RETRO_Q2_K>(variant, W, X, Y, K, N, T, st);
@@ -453,6 +455,7 @@ int retro_dequantize(int type, const void* W, float* out, int64_t K, int64_t N, 
         case RETRO_Q5_0: return launch_dequant<RETRO_Q5_0>(W, out, K, N, st);
         case RETRO_Q5_1: return launch_dequant<RETRO_Q5_1>(W, out, K, N, st);
         case RETRO_MXFP4: return launch_dequant<RETRO_MXFP4>(W, out, K, N, st);
+        case RETRO_NVFP4: return launch_dequant<RETRO_NVFP4>(W, out, K, N, st);
         case RETRO_Q4_K: return launch_dequant<RETRO_Q4_K>(W, out, K, N, st);
         case RETRO_Q5_K: return launch_dequant<RETRO_Q5_K>(W, out, K, N, st);
         case RETRO_Q2_K: return launch_dequant<RETRO_Q2_K>(W, out, K, N, st);

@@ -29,7 +29,7 @@ namespace retro {
 // GGUF tensor-type ids.
 enum : int {
     kF32 = 0, kF16 = 1, kQ4_0 = 2, kQ4_1 = 3, kQ5_0 = 6, kQ5_1 = 7, kQ8_0 = 8, kQ2_K = 10, kQ3_K = 11, kQ4_K = 12,
-    kQ5_K = 13, kQ6_K = 14, kBF16 = 30, kMXFP4 = 39
+    kQ5_K = 13, kQ6_K = 14, kBF16 = 30, kMXFP4 = 39, kNVFP4 = 40
 };
 
 // kBlock: elements per block; kBytes: bytes per block; kGroup: elements one
@@ -44,6 +44,11 @@ template <> struct Format<kQ4_1> { static constexpr int kBlock = 32,  kBytes = 2
 template <> struct Format<kQ5_0> { static constexpr int kBlock = 32,  kBytes = 22,  kGroup = 32; };
 template <> struct Format<kQ5_1> { static constexpr int kBlock = 32,  kBytes = 24,  kGroup = 32; };
 template <> struct Format<kMXFP4> { static constexpr int kBlock = 32, kBytes = 17,  kGroup = 32; };
+// NVFP4: 64 elements in 36 bytes, four FP8 E4M3 sub-block scales then 32
+// code bytes; sub-block s (elements 16s .. 16s + 15) takes code bytes
+// 8s .. 8s + 7, element 16s + i (i < 8) the low nibble of byte 8s + i and
+// element 16s + 8 + i its high nibble.
+template <> struct Format<kNVFP4> { static constexpr int kBlock = 64, kBytes = 36,  kGroup = 32; };
 
 // The 32-element nibble formats: element j < 16 is the low nibble of code
 // byte j, element j + 16 its high nibble, after a header of kHeader bytes
@@ -171,6 +176,42 @@ __device__ __forceinline__ void mxfp4_x8(uint32_t w, float s, float lo[4], float
     lo[1] = b.x; hi[1] = b.y;
     lo[2] = c.x; hi[2] = c.y;
     lo[3] = d.x; hi[3] = d.y;
+}
+
+// FP8 E4M3 byte -> float32, exactly (the NVFP4 sub-block scale): sign bit
+// 7, exponent bits 6..3 (bias 7), mantissa bits 2..0; exponent 0 is the
+// subnormal range m * 2^-9; exponent 15 with mantissa 7 is NaN (the format
+// has no infinities). Branch-free: the normal pattern is built in the
+// float32 fields (exponent + 120, mantissa at the top of the fraction).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    const float sub = static_cast<float>(m) * 0x1p-9f;
+    float mag = e == 0u ? sub : normal;
+    mag = (b & 0x7Fu) == 0x7Fu ? __uint_as_float(0x7FC00000u) : mag;
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// NVFP4: the low (lo) and high (hi) nibbles of four code bytes of one
+// sub-block, E2M1 values (the hardware conversion at scale 1, exact) times
+// the sub-block scale s (exact: at most 2 + 4 significant bits, far from the
+// subnormal range; NaN for the NaN scale).
+__device__ __forceinline__ void nvfp4_x8(uint32_t w, float s, float lo[4], float hi[4]) {
+    float l[4], h[4];
+    mxfp4_x8(w, 1.0f, l, h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = l[i] * s;
+        hi[i] = h[i] * s;
+    }
+}
+
+// NVFP4: the low (high = false) or high nibbles of four code bytes.
+__device__ __forceinline__ void nvfp4_x4(uint32_t w, bool high, float s, float out[4]) {
+    float lo[4], hi[4];
+    nvfp4_x8(w, s, lo, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = high ? hi[i] : lo[i];
 }
 
 // MXFP4: the low (high = false) or high nibbles of four code bytes.

@@ -34,6 +34,7 @@ inline bool geometry(int type, Geometry& g) {
         case RETRO_Q5_0: g = {32, 22}; return true;
         case RETRO_Q5_1: g = {32, 24}; return true;
         case RETRO_MXFP4: g = {32, 17}; return true;
+        case RETRO_NVFP4: g = {64, 36}; return true;
         case RETRO_Q4_K: g = {256, 144}; return true;
         case RETRO_Q5_K: g = {256, 176}; return true;
         case RETRO_Q2_K: g = {256, 84}; return true;

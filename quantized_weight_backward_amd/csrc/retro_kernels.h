@@ -127,7 +127,7 @@ struct TileArgs {
 template <int TYPE>
 __device__ __forceinline__ int lds_swizzle(int col) {
     if constexpr (TYPE == kQ4_K || TYPE == kQ5_K) return col ^ (((col >> 6) & 3) << 2);
-    if constexpr (kNibbleLayout<TYPE> || TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K)
+    if constexpr (kNibbleLayout<TYPE> || TYPE == kNVFP4 || TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K)
         return col ^ (((col >> 5) & 7) << 2);
     if constexpr (TYPE == kQ8_0) return col ^ (((col >> 5) & 3) << 2);
     return col;
@@ -494,6 +494,25 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
                         *reinterpret_cast<float4*>(brow + S::swz(lo + 16 + 4 * i)) =
                             make_float4(eh[0], eh[1], eh[2], eh[3]);
                     }
+                } else if constexpr (TYPE == kNVFP4) {  // 36-byte blocks, 4-byte aligned
+                    // group g: sub-blocks 2h and 2h + 1 of block b
+                    const int b = g >> 1, h = g & 1;
+                    const uint8_t* blk = raw + 36 * b;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int sb = 2 * h + q;
+                        const float sc = e4m3_to_f32(blk[sb]);
+                        const int out = 64 * b + 16 * sb;
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            float el[4], eh[4];
+                            nvfp4_x8(*reinterpret_cast<const uint32_t*>(blk + 4 + 8 * sb + 4 * i), sc, el, eh);
+                            *reinterpret_cast<float4*>(brow + S::swz(out + 4 * i)) =
+                                make_float4(el[0], el[1], el[2], el[3]);
+                            *reinterpret_cast<float4*>(brow + S::swz(out + 8 + 4 * i)) =
+                                make_float4(eh[0], eh[1], eh[2], eh[3]);
+                        }
+                    }
                 } else if constexpr (TYPE == kQ8_0) {
                     const int b = g >> 1, h = g & 1;
                     const uint8_t* blk = raw + 34 * b;
@@ -631,6 +650,11 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
         const float d = half_to_f32(*reinterpret_cast<const uint16_t*>(blk));
         const uint16_t* c = reinterpret_cast<const uint16_t*>(blk + 2 + r);
         q8_0_x4(uint32_t(c[0]) | (uint32_t(c[1]) << 16), d, e);
+    } else if constexpr (TYPE == kNVFP4) {  // K is a multiple of 64, so k < K always
+        const uint8_t* blk = row + (k >> 6) * 36;
+        const int r = k & 63, sb = r >> 4, i = r & 15;
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(blk + 4 + 8 * sb + (i & 7));
+        nvfp4_x4(w, i >= 8, e4m3_to_f32(blk[sb]), e);
     } else if constexpr (TYPE == kMXFP4) {  // 17-byte blocks: read bytewise
         if (k >= K) { e[0] = e[1] = e[2] = e[3] = 0.f; return; }
         const uint8_t* blk = row + (k >> 5) * 17;
@@ -746,6 +770,9 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
         col = (kl >> 5) * 34 + 2 + (kl & 31);
     } else if constexpr (kNibbleLayout<TYPE>) {
         col = (kl >> 5) * Format<TYPE>::kBytes + kHeader<TYPE> + (kl & 15);
+    } else if constexpr (TYPE == kNVFP4) {
+        const int e = kl & 63;
+        col = (kl >> 6) * 36 + 4 + 8 * (e >> 4) + (e & 7);
     } else if constexpr (TYPE == kQ4_K) {
         const int e = kl & 255;
         col = (kl >> 8) * 144 + 16 + 32 * (e >> 6) + (e & 31);
@@ -779,6 +806,8 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
         hcol = (min(k0 + 32 * sel, K - 32) >> 5) * Format<TYPE>::kBytes;
     o.hdr = uint32_t(hr * a.pitch) + hcol;
     o.hdr2 = 0;
+    if constexpr (TYPE == kNVFP4)  // the scale byte of (row lane / 4, sub-block lane % 4)
+        o.hdr = uint32_t((lane >> 2) * a.pitch) + uint32_t((k0 >> 6) * 36 + (lane & 3));
     if constexpr (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) {
         // lane -> (row lane / 4, sub-scale or pair 8h + 2(p0 + w / 2) + w % 2),
         // w = lane % 4, p0 the slab's first quarter. Q6_K: the halfword holding
@@ -872,7 +901,7 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b32(wr, o.hdr, 0, 0);
     } else if constexpr (TYPE == kQ8_0 || TYPE == kQ4_0) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b16(wr, o.hdr, 0, 0);
-    } else if constexpr (TYPE == kMXFP4) {
+    } else if constexpr (TYPE == kMXFP4 || TYPE == kNVFP4) {
         r.hdr[0] = __builtin_amdgcn_raw_buffer_load_b8(wr, o.hdr, 0, 0);
     } else {
         r.hdr[0] = 0u;
@@ -914,6 +943,9 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
             if (kl + 1 < K) r.code[s][0] |= uint32_t(p[1]) << 16;
             if (kl + 2 < K) r.code[s][1] |= p[2];
             if (kl + 3 < K) r.code[s][1] |= uint32_t(p[3]) << 16;
+        } else if constexpr (TYPE == kNVFP4) {  // K % 64 == 0, so kl < K
+            const int e = kl & 63;
+            r.code[s][0] = *reinterpret_cast<const uint32_t*>(row + (kl >> 6) * 36 + 4 + 8 * (e >> 4) + (e & 7));
         } else if constexpr (TYPE == kMXFP4) {
             if (kl < K) {
                 const uint8_t* c = row + (kl >> 5) * 17 + 1 + (kl & 15);
@@ -980,6 +1012,9 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
                 r.hdr[3] = f[6];
             }
         }
+    } else if constexpr (TYPE == kNVFP4) {
+        r.hdr[0] = 0u;
+        if (n0 + (lane >> 2) < N) r.hdr[0] = a.W[(long long)(n0 + (lane >> 2)) * a.pitch + (k0 >> 6) * 36 + (lane & 3)];
     } else if constexpr (TYPE == kMXFP4) {
         const int kb = k0 + 32 * sel;
         r.hdr[0] = 0u;
@@ -1036,6 +1071,14 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
         const int e = (4 * j) & 31;
 #pragma unroll
         for (int s = 0; s < 4; ++s) mxfp4_x4(r.code[s][0], e >= 16, lane_value(smine, 2 * (4 * rq + s) + hi), wv[s]);
+    } else if constexpr (TYPE == kNVFP4) {
+        // this lane decodes the scale of (row lane / 4, sub-block lane % 4);
+        // its own 4 columns 4j .. 4j + 3 lie in sub-block j / 4, the high
+        // nibbles for j % 4 >= 2
+        const float smine = e4m3_to_f32(r.hdr[0]);
+        const bool high = (j & 2) != 0;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) nvfp4_x4(r.code[s][0], high, lane_value(smine, 4 * (4 * rq + s) + (j >> 2)), wv[s]);
     } else if constexpr (kNibble32<TYPE>) {
         // this lane decodes the header of (row (lane % 32) / 2, block lane % 2)
         float dmine, mmine;

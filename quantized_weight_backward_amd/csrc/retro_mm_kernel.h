@@ -141,6 +141,34 @@ template <> struct MmCodec<kQ5_0> : MmCodecNibble<kQ5_0> {};
 template <> struct MmCodec<kQ5_1> : MmCodecNibble<kQ5_1> {};
 template <> struct MmCodec<kMXFP4> : MmCodecNibble<kMXFP4> {};
 
+// NVFP4: a 16-element unit is one sub-block: its 8 code bytes (low nibbles
+// are elements 0 .. 7, high nibbles 8 .. 15) and its E4M3 scale byte.
+template <>
+struct MmCodec<kNVFP4> {
+    static constexpr int WORDS = 3;
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t wr, uint32_t ro, int k, uint32_t (&w)[WORDS]) {
+        const uint32_t blk = ro + 36u * uint32_t(k >> 6);
+        const uint32_t sb = uint32_t((k & 63) >> 4);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, blk + 4u + 8u * sb, 0, 0);
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = __builtin_amdgcn_raw_buffer_load_b8(wr, blk + sb, 0, 0);
+    }
+    __device__ static void decode(const uint32_t (&w)[WORDS], int, float (&e)[16]) {
+        const float s = e4m3_to_f32(w[2]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            float lo[4], hi[4];
+            nvfp4_x8(w[i], s, lo, hi);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                e[4 * i + j] = lo[j];
+                e[8 + 4 * i + j] = hi[j];
+            }
+        }
+    }
+};
+
 // Q4_K / Q5_K: element e of a super-block lies in 64-element chunk c = e / 64
 // at r = e % 64; its code is the low (r < 32) or high nibble of code byte
 // 32c + r % 32, and it uses sub-block 2c + (r >= 32).

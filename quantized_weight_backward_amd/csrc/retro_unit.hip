@@ -27,7 +27,7 @@ namespace host {
 
 static_assert(kF32 == RETRO_F32 && kF16 == RETRO_F16 && kBF16 == RETRO_BF16 && kQ8_0 == RETRO_Q8_0 &&
                   kQ4_0 == RETRO_Q4_0 && kQ4_1 == RETRO_Q4_1 && kQ5_0 == RETRO_Q5_0 && kQ5_1 == RETRO_Q5_1 &&
-                  kMXFP4 == RETRO_MXFP4 && kQ2_K == RETRO_Q2_K && kQ3_K == RETRO_Q3_K && kQ4_K == RETRO_Q4_K &&
+                  kMXFP4 == RETRO_MXFP4 && kNVFP4 == RETRO_NVFP4 && kQ2_K == RETRO_Q2_K && kQ3_K == RETRO_Q3_K && kQ4_K == RETRO_Q4_K &&
                   kQ5_K == RETRO_Q5_K && kQ6_K == RETRO_Q6_K,
               "device and ABI type ids agree");
 

@@ -72,6 +72,9 @@ struct WsShape {
     // producer threads, each holding CB code bytes of it.
     static constexpr int QSPLIT = (TYPE == kQ8_0 || kNibbleLayout<TYPE>) ? kPThreads / (BN * BK / 32) : 1;
     static constexpr int CB = TYPE == kQ8_0 ? 32 / QSPLIT : 16 / QSPLIT;
+    // NVFP4: each producer thread takes NV_SB consecutive 16-element
+    // sub-blocks of one row (8 threads per row of the chunk).
+    static constexpr int NV_SB = BK / 128;
     // words of W each producer thread holds between load and decode
     static constexpr int WWORDS = kDense ? 4 * DWPR * DUNITS
                                   : (TYPE == kQ4_K) ? 8
@@ -79,6 +82,7 @@ struct WsShape {
                                   : (TYPE == kQ6_K) ? 9
                                   : (TYPE == kQ2_K) ? 5
                                   : (TYPE == kQ3_K) ? 8
+                                  : (TYPE == kNVFP4) ? 2 * NV_SB + 1
                                   : kHasFifth<TYPE> ? CB / 4 + 2
                                                     : CB / 4 + 1;
     // Chunks whose loads a producer thread keeps in registers: the chunk
@@ -300,6 +304,13 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
             woff = uint32_t(r * args.pitch);
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) wlds[qq] = ws_w_index<WP>(128 * hh + 32 * qq + 8 * j, r);
+        } else if constexpr (TYPE == kNVFP4) {
+            // sub-blocks NV_SB u .. NV_SB u + NV_SB - 1 of row p / 8 (u = p % 8):
+            // columns 16 NV_SB u .., one 16-column group each
+            const int r = p >> 3, col = 16 * S::NV_SB * (p & 7);
+            woff = uint32_t(r * args.pitch + (col >> 6) * 36);
+#pragma unroll
+            for (int i = 0; i < S::NV_SB; ++i) wlds[i] = ws_w_index<WP>(col + 16 * i, r);
         } else {
             // part s of block b of row r: code bytes CB s .. CB s + CB - 1
             const int id = p / S::QSPLIT, s = p - id * S::QSPLIT;
@@ -415,6 +426,19 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
                 wreg[4] = f.x; wreg[5] = f.y;
                 wreg[6] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 104, 0, 0);
                 wreg[7] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + 108, 0, 0);
+            } else if constexpr (TYPE == kNVFP4) {
+                // the code bytes of the thread's sub-blocks (8 each) and their
+                // scale bytes; 36-byte blocks are 4-byte aligned
+                const int sb0 = (S::NV_SB * (p & 7)) & 3;
+                if constexpr (S::NV_SB == 1) {
+                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 4 + 8 * sb0, 0, 0);
+                    wreg[0] = v.x; wreg[1] = v.y;
+                    wreg[2] = __builtin_amdgcn_raw_buffer_load_b8(wr, woff + sb0, 0, 0);
+                } else {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 4 + 8 * sb0, 0, 0);
+                    wreg[0] = v.x; wreg[1] = v.y; wreg[2] = v.z; wreg[3] = v.w;
+                    wreg[4] = __builtin_amdgcn_raw_buffer_load_b16(wr, woff + sb0, 0, 0);
+                }
             } else {  // Q8_0, nibble blocks: 2-byte (MXFP4: any) aligned blocks (unaligned buffer loads)
                 constexpr int CW = S::CB / 4;
                 constexpr int HDR = TYPE == kQ8_0 ? 2 : kHeader<TYPE>;
@@ -605,6 +629,23 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)
                     float* col = (4 * w < 16) ? ws + wlds[0] + (4 * w) * WP : ws + wlds[1] + (4 * w - 16) * WP;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) col[j * WP] = e[j];
+                }
+            } else if constexpr (TYPE == kNVFP4) {
+                // sub-block i: words 2i, 2i + 1 hold its 8 code bytes; low
+                // nibbles are its columns 0 .. 7, high nibbles 8 .. 15
+#pragma unroll
+                for (int i = 0; i < S::NV_SB; ++i) {
+                    const float sc = e4m3_to_f32((wreg[2 * S::NV_SB] >> (8 * i)) & 0xFFu);
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        float el[4], eh[4];
+                        nvfp4_x8(wreg[2 * i + w], sc, el, eh);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            ws[wlds[i] + (4 * w + j) * WP] = el[j];
+                            ws[wlds[i] + (8 + 4 * w + j) * WP] = eh[j];
+                        }
+                    }
                 }
             } else if constexpr (TYPE == kMXFP4) {  // code bytes CB s .. of the block
                 constexpr int CW = S::CB / 4;

@@ -54,7 +54,7 @@ def test_enum_values_match_header():
 
 
 @pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4,
-                                   wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
+                                   wl.NVFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
 def test_row_bytes_matches_the_format(wtype):
     blk, nbytes = wl.block_geometry(wtype)
     for nblocks in (0, 1, 3, 16, 56):
@@ -73,6 +73,7 @@ def test_row_bytes_of_the_workloads():
     assert q.row_bytes(q.Q5_K, 4096) == 2816
     assert q.row_bytes(q.Q6_K, 14336) == 11760
     assert q.row_bytes(q.Q2_K, 4096) == 1344
+    assert q.row_bytes(q.NVFP4, 5120) == 2880
     assert q.row_bytes(q.Q3_K, 4096) == 1760
     assert q.row_bytes(q.Q4_1, 5120) == 3200
     assert q.row_bytes(q.Q5_0, 5120) == 3520

@@ -35,7 +35,7 @@ from blocks import golden_blocks
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K,
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.NVFP4, wl.Q2_K, wl.Q3_K,
          wl.Q4_K, wl.Q5_K, wl.Q6_K]
 KQUANTS = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
 OUT_PROD_VARIANTS = ["skinny", "tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
@@ -51,7 +51,7 @@ HALF_FIELDS = {
     wl.Q2_K: (80, 82), wl.Q3_K: (108,), wl.Q4_K: (0, 2), wl.Q5_K: (0, 2), wl.Q6_K: (208,),
 }
 BLOCK = {wl.Q8_0: (32, 34), wl.Q4_0: (32, 18), wl.Q4_1: (32, 20), wl.Q5_0: (32, 22), wl.Q5_1: (32, 24),
-         wl.MXFP4: (32, 17), wl.Q2_K: (256, 84), wl.Q3_K: (256, 110), wl.Q4_K: (256, 144), wl.Q5_K: (256, 176),
+         wl.MXFP4: (32, 17), wl.NVFP4: (64, 36), wl.Q2_K: (256, 84), wl.Q3_K: (256, 110), wl.Q4_K: (256, 144), wl.Q5_K: (256, 176),
          wl.Q6_K: (256, 210)}
 # binary16 patterns at the ends of the format: the smallest and largest
 # subnormals (both signs), zeros, the largest normal, infinities, NaNs
@@ -273,6 +273,28 @@ def test_mxfp4_normal_scale_ends_through_split(q):
     out = q.out_prod(wl.MXFP4, W, G, K, variant=ids["split_128x128"])
     torch.cuda.synchronize()
     assert_decode(out.cpu().numpy()[0], want, "mxfp4 split_128x128")
+
+
+def nvfp4_scale_row():
+    """Every E4M3 scale byte (the four scales of a block take four of them)
+    over code bytes that run through all 256 values: 64 blocks."""
+    blocks = np.zeros((64, 36), dtype=np.uint8)
+    blocks[:, 0:4] = np.arange(256, dtype=np.uint8).reshape(64, 4)
+    blocks[:, 4:] = (np.arange(64 * 32) * 37 % 256).astype(np.uint8).reshape(64, 32)
+    return blocks.reshape(-1), 64 * 64
+
+
+def test_nvfp4_every_scale_byte(q):
+    """NVFP4 with every E4M3 scale byte (zeros of either sign, subnormals, the
+    largest, NaN) and every code: the device decode equals the oracle's E2M1
+    times the E4M3 scale, in retro_dequantize and in every kernel."""
+    row, K = nvfp4_scale_row()
+    want = oracle.dequantize(wl.NVFP4, row, K)[0]
+    assert np.isnan(want).any() and ((want != 0) & (np.abs(want) < 2.0 ** -6)).any()
+    got = q.dequantize(wl.NVFP4, dev(row), K, 1).cpu().numpy()[0]
+    assert_decode(got, want, "nvfp4 dequantize", signed_zeros=True)
+    checked = through_every_kernel(q, wl.NVFP4, row, K, "nvfp4", split=False)
+    assert "skinny" in checked and "ws_128x256" in checked and "tile_64x64" in checked, checked
 
 
 @pytest.mark.parametrize("wtype", [wl.F16, wl.BF16])

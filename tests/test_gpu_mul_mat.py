@@ -19,13 +19,13 @@ REL_MAX = 1e-5
 REL_TIGHT = 2e-6
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K,
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.NVFP4, wl.Q2_K, wl.Q3_K,
          wl.Q4_K, wl.Q5_K, wl.Q6_K]
 VARIANTS = ["auto", "ws_128x128", "ws_64x128", "ws_32x128", "skinny", "simple"]
 # K per type: several 32-column chunks and, for the K-quants, several
 # super-blocks; dense K not a multiple of 32 (a partial last chunk)
 K_OF = {wl.F32: 300, wl.F16: 264, wl.BF16: 520, wl.Q8_0: 416, wl.Q4_0: 352, wl.Q4_1: 192, wl.Q5_0: 416,
-        wl.Q5_1: 352, wl.MXFP4: 352, wl.Q2_K: 512, wl.Q3_K: 768, wl.Q4_K: 768, wl.Q5_K: 512, wl.Q6_K: 768}
+        wl.Q5_1: 352, wl.MXFP4: 352, wl.NVFP4: 320, wl.Q2_K: 512, wl.Q3_K: 768, wl.Q4_K: 768, wl.Q5_K: 512, wl.Q6_K: 768}
 # (T, N): ragged in both, one below the 32-row tile, one spanning several tiles
 SHAPES = [(200, 77), (20, 130), (67, 256), (16, 100), (5, 33)]
 
@@ -81,7 +81,7 @@ def test_mul_mat_matches_oracle(q, wtype, shape):
     assert ("skinny" in ran) == (T <= 16), ran
 
 
-@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q6_K, wl.MXFP4, wl.Q5_1, wl.BF16])
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q6_K, wl.MXFP4, wl.NVFP4, wl.Q5_1, wl.BF16])
 def test_mul_mat_f32_twin_on_device(q, wtype):
     """The same tile on identical decoded values: bit-identical to the F32
     weight holding them."""

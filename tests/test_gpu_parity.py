@@ -29,7 +29,7 @@ REL_MAX = 1e-5
 REL_TIGHT = 2e-6
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
-TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K,
+TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.NVFP4, wl.Q2_K, wl.Q3_K,
          wl.Q4_K, wl.Q5_K, wl.Q6_K]
 KQUANTS = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
 ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
@@ -96,6 +96,7 @@ SMALL_K = {
     wl.Q5_0: (352, 416, 128, 352),
     wl.Q5_1: (512, 352, 416, 256),
     wl.MXFP4: (352, 416, 512, 128),   # 187-, 221-byte rows: odd pitches
+    wl.NVFP4: (320, 448, 128, 384),   # 180-, 252-, 72-byte rows: 4-byte aligned pitches
     wl.Q4_K: (768, 512, 256, 768),
     wl.Q5_K: (512, 768, 256, 512),
     wl.Q6_K: (768, 256, 512, 768),
@@ -202,7 +203,7 @@ def test_q8_0_tiny_workload(q):
     check_close(y, acc, ab)
 
 
-@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K,
+@pytest.mark.parametrize("wtype", [wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.NVFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K,
                                    wl.Q5_K, wl.Q6_K, wl.F16, wl.BF16])
 def test_f32_twin_on_device(q, wtype):
     """out_prod(Qx, W) and out_prod(F32, dequant(W)) run the same tile on
@@ -224,7 +225,8 @@ def test_f32_twin_on_device(q, wtype):
 
 # --- invariants -----------------------------------------------------------------
 
-@pytest.mark.parametrize("wtype", [wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.Q4_0, wl.Q5_1, wl.MXFP4, wl.BF16])
+@pytest.mark.parametrize("wtype", [wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K, wl.Q4_0, wl.Q5_1, wl.MXFP4, wl.NVFP4,
+                                   wl.BF16])
 @pytest.mark.parametrize("i", [0, 3])
 def test_invariants(q, wtype, i):
     c = small_case(wtype, i, 500)
@@ -254,7 +256,7 @@ def test_empty_reduction_fills_zeros(q, wtype):
         assert np.array_equal(y, np.zeros((T, K), np.float32))
 
 
-@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q2_K, wl.Q3_K, wl.Q4_0, wl.F32, wl.MXFP4])
+@pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q2_K, wl.Q3_K, wl.Q4_0, wl.F32, wl.MXFP4, wl.NVFP4])
 def test_empty_reduction_with_a_row_stride(q, wtype):
     """N = 0 with G an empty view whose row stride is not 0 (torch hands over
     a null pointer for it): every kernel that takes the shape writes zeros and
@@ -335,7 +337,7 @@ def test_runs_on_the_given_stream(q):
 
 STRIDED = [(wl.Q4_K, 768, 96, 130), (wl.Q4_0, 512, 77, 200), (wl.F16, 264, 100, 150), (wl.Q6_K, 512, 60, 70),
            (wl.Q8_0, 416, 33, 16), (wl.Q2_K, 256, 40, 9), (wl.Q5_0, 352, 52, 90), (wl.Q5_1, 256, 44, 12),
-           (wl.MXFP4, 352, 40, 70)]
+           (wl.MXFP4, 352, 40, 70), (wl.NVFP4, 320, 40, 70)]
 
 
 @pytest.mark.parametrize("wtype,K,N,T", STRIDED)
@@ -391,7 +393,7 @@ def g_columns(g, ldg):
 
 GCOLS = [(wl.Q4_K, 768, 96, 130), (wl.Q4_0, 512, 77, 200), (wl.F16, 264, 100, 150), (wl.F32, 301, 64, 70),
          (wl.Q6_K, 512, 60, 70), (wl.Q8_0, 416, 33, 16), (wl.Q2_K, 256, 40, 9), (wl.Q5_1, 256, 44, 12),
-         (wl.MXFP4, 352, 40, 70), (wl.Q3_K, 512, 35, 100), (wl.BF16, 520, 50, 5), (wl.Q5_K, 256, 37, 67),
+         (wl.MXFP4, 352, 40, 70), (wl.NVFP4, 448, 36, 66), (wl.Q3_K, 512, 35, 100), (wl.BF16, 520, 50, 5), (wl.Q5_K, 256, 37, 67),
          (wl.Q4_1, 192, 64, 33), (wl.Q5_0, 352, 29, 16)]
 
 
@@ -608,6 +610,8 @@ FULL = [
     ("q5_0_n17408_k5120_t2048", None),
     ("q5_1_n17408_k5120_t2048", None),
     ("mxfp4_n17408_k5120_t2048", None),
+    ("nvfp4_n17408_k5120_t2048", None),
+    ("nvfp4_n4096_k14336_t16", None),
 ]
 
 

@@ -17,7 +17,7 @@ def test_deterministic_and_seed_sensitive():
 
 
 @pytest.mark.parametrize("wtype", [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4,
-                                   wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
+                                   wl.NVFP4, wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K])
 def test_shapes(wtype):
     blk, nbytes = wl.block_geometry(wtype)
     K = 2 * max(blk, 32)
@@ -31,6 +31,14 @@ def test_mxfp4_scales_and_codes():
     blk = c["W"].reshape(64, 32, 17)
     assert blk[:, :, 0].min() == 117 and blk[:, :, 0].max() == 120
     nib = np.concatenate([blk[:, :, 1:] & 15, blk[:, :, 1:] >> 4])
+    assert set(np.unique(nib)) == set(range(16))
+
+
+def test_nvfp4_scales_and_codes():
+    c = wl.make_case(wl.NVFP4, 64, 1024, 1, seed=2)
+    blk = c["W"].reshape(64, 16, 36)
+    assert blk[:, :, 0:4].min() == 0x08 and blk[:, :, 0:4].max() == 0x37
+    nib = np.concatenate([blk[:, :, 4:] & 15, blk[:, :, 4:] >> 4])
     assert set(np.unique(nib)) == set(range(16))
 
 
