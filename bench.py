@@ -519,12 +519,13 @@ def main() -> int:
 
     def back_to_back(call, reps):
         """Mean launch time (s) of `reps` launches enqueued back to back
-        between two HIP events on the launch stream. A spin of about a
-        millisecond goes first, so that the host has queued every launch
-        before the first event completes and host launch overhead cannot
-        leave the GPU idle between them."""
+        between two HIP events on the launch stream. One launch of the
+        large-T kernel (about 3.6 ms of matrix work) goes first, so that the
+        host has queued every timed launch before the first event completes:
+        host launch overhead cannot leave the GPU idle between them, and the
+        GPU clock is at its loaded level (an idle spin lets it drop)."""
         b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(2_000_000)
+        q.out_prod(q.Q4_K, Wl, Gl, large["K"], out=Dl)
         b0.record(stream)
         for i in range(reps):
             call(i)

@@ -171,6 +171,7 @@ struct TileShape {
 };
 
 template <int TYPE, int WA, int WB, int WGT, int WGK>
+// two 4-wave workgroups per CU: 2 waves per SIMD (amdgpu_waves_per_eu)
 __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
     using S = TileShape<TYPE, WA, WB, WGT, WGK>;
     using F = Format<TYPE>;

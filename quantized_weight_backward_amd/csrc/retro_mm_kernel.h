@@ -285,7 +285,10 @@ struct MmShape {
     static constexpr int CK = 4 / CT;
     static constexpr int BT = 32 * WA * CT;  // rows of x per tile
     static constexpr int BK = 32 * WB * CK;  // rows of W (outputs) per tile
+    // workgroups per CU the register budget is set for, and the same as waves
+    // per SIMD for the launch bound (see WsShape)
     static constexpr int kWgPerCu = BT == 32 ? 2 : 1;
+    static constexpr int kWavesPerSimd = kThreads / 64 / 4 * kWgPerCu;
     static constexpr int BN = 32;  // k values per chunk
     static constexpr int GP = BN + 4;
     static constexpr int WP = BN + 4;
@@ -304,7 +307,7 @@ struct MmShape {
 };
 
 template <int TYPE, int WA, int WB, int CT>
-__global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWgPerCu)) void mul_mat_ws_kernel(MmArgs args) {
+__global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWavesPerSimd)) void mul_mat_ws_kernel(MmArgs args) {
     using S = MmShape<TYPE, WA, WB, CT>;
     using C = MmCodec<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, WP = S::WP;

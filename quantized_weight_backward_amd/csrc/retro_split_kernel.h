@@ -110,7 +110,8 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& 
 }
 
 template <int TYPE>
-__global__ __launch_bounds__(512, 1) void out_prod_split_kernel(TileArgs args) {
+// one 8-wave workgroup per CU: 2 waves per SIMD (amdgpu_waves_per_eu)
+__global__ __launch_bounds__(512, 2) void out_prod_split_kernel(TileArgs args) {
     static_assert(kSuperBlock<TYPE> || kSplitNarrow<TYPE>, "no exact split for this type");
     constexpr bool kKQ = kSuperBlock<TYPE>;
     // sub-blocks of the min term per super-block (Q3_K and Q6_K values have none)

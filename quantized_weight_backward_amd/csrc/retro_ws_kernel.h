@@ -48,8 +48,12 @@ struct WsShape {
     static constexpr int BK = 32 * WB * CK;
     // Workgroups per CU the register budget is set for: two for the 32-row
     // tiles (46 KB of LDS), whose second workgroup fills the first one's
-    // barrier waits; one otherwise.
+    // barrier waits; one otherwise. The kernel's launch bound states it as
+    // waves per SIMD (amdgpu_waves_per_eu): a workgroup's waves spread over
+    // the CU's four SIMDs, so two 8-wave workgroups are 4 waves per SIMD, a
+    // budget of 128 VGPRs each.
     static constexpr int kWgPerCu = (BT == 32 && NG == 1) ? 2 : 1;
+    static constexpr int kWavesPerSimd = kThreads / 64 / 4 * kWgPerCu;
     static constexpr int BN = 32;
     static_assert(BK == 128 || BK == 256, "K tile of 128 or 256 columns");
     static_assert(!kSuperBlock<TYPE> || BK == 256, "K-quant tiles hold whole super-blocks");
@@ -231,7 +235,7 @@ __device__ __forceinline__ void ws_consume(float* lds_all, int tid, int wave, in
 // GCOLS: G stored t-fastest (args.ldg floats between its columns); the
 // consumers see the same LDS contents either way.
 template <int TYPE, int WA, int WB, int CT, int NG, bool GCOLS>
-__global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWgPerCu)) void out_prod_ws_kernel(
+__global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWavesPerSimd)) void out_prod_ws_kernel(
     TileArgs args) {
     using S = WsShape<TYPE, WA, WB, CT, NG>;
     using F = Format<TYPE>;
