@@ -112,9 +112,10 @@ def read_traffic(tag: str):
     return read_profile_value(tag, "hbm_bytes_per_launch")
 
 
-BENCH_PROFILE_ARGS = "--steps 20 --warmup 3 --reps 20 --no-cpu-baseline"
+BENCH_PROFILE_ARGS = "--steps 20 --warmup 5 --reps 20 --no-cpu-baseline"  # the step loop as the driver runs it
 COUNTER_ARGS = "--steps 3 --warmup 1 --reps 3 --no-cpu-baseline"
-PROFILE_WARMUP = 3  # launches of each kernel dropped from a trace summary (the bench's warm-up)
+PROFILE_WARMUP = 5  # launches of each kernel dropped from a trace summary (the bench's warm-up steps)
+PROFILE_STEPS = 20  # the timed steps that follow them
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d {out}/prof_trace -o run -- "
              f"python3 bench.py {BENCH_PROFILE_ARGS}",
@@ -212,13 +213,18 @@ def _copy_scale(run_dir: str, sub: str, counter: str) -> tuple[float, float]:
     return kib, (1024 << 20) / (kib * 1024)
 
 
-def _stats_row(name: str, durs: list[float]) -> list[str]:
-    us = [d / 1e3 for d in durs]
-    mean = sum(us) / len(us)
-    med = sorted(us)[len(us) // 2]
+def _stats_row(name: str, durs: list[float], steps: int = 0) -> list[str]:
+    """Table of launch durations (ns in, us out). With steps > 0 the first
+    `steps` durations are the benchmark's timed step loop, given a row of
+    their own."""
+    def row(label, part):
+        us = [d / 1e3 for d in part]
+        return (f"| {label} | {len(us)} | {sum(us) / len(us):.2f} | {sorted(us)[len(us) // 2]:.2f} | {min(us):.2f} | "
+                f"{max(us):.2f} |")
+    rows = [row("timed steps", durs[:steps])] if steps else []
     return [f"Kernel: `{name}`", "",
-            "| steady-state launches | mean (us) | median (us) | min (us) | max (us) |", "|---|---|---|---|---|",
-            f"| {len(us)} | {mean:.2f} | {med:.2f} | {min(us):.2f} | {max(us):.2f} |", ""]
+            "| launches | count | mean (us) | median (us) | min (us) | max (us) |", "|---|---|---|---|---|---|",
+            *rows, row("all after warm-up", durs), ""]
 
 
 def summarize(run_dir: str) -> None:
@@ -245,12 +251,18 @@ def summarize(run_dir: str) -> None:
         tag = f"{variant}_{workload_tag(workload, dense)}"
         name, durs = steady_dispatches(trace_csv, prefix, PROFILE_WARMUP)
         flops = 2.0 * c["T"] * c["N"] * c["K"]
-        mean_s = sum(durs) / len(durs) / 1e9
+        # the two step kernels: their first PROFILE_STEPS launches after the
+        # warm-up are the timed step loop, the bench's own figure
+        steps = PROFILE_STEPS if workload in (LARGE, SKINNY) else 0
+        head = durs[:steps] if steps else durs
+        mean_s = sum(head) / len(head) / 1e9
         lines = [f"# {tag}: rocprofv3 kernel trace", "",
                  f"Command (repository root): `{profile_command('trace', run_dir)}`", "",
                  f"Workload {workload_tag(workload, dense)}, the kernel retro_out_prod chooses ({variant}). "
-                 f"The first {PROFILE_WARMUP} launches of the kernel (the benchmark's warm-up) are left out.", "",
-                 *_stats_row(name, durs),
+                 f"The first {PROFILE_WARMUP} launches of the kernel (the benchmark's warm-up steps) are left out"
+                 + (f"; the next {steps} are the timed step loop." if steps else "."), "",
+                 *_stats_row(name, durs, steps),
+                 "Figures below at the mean of the " + ("timed steps." if steps else "launches after warm-up."), "",
                  f"F32 TFLOP/s at the mean: {flops / mean_s / 1e12:.2f} "
                  f"(2*T*N*K = {flops:.6g}); fraction of the 157.3 TFLOP/s F32 peak: "
                  f"{flops / mean_s / 1e12 / PEAK_F32_TFLOPS:.4f}", ""]
@@ -280,6 +292,34 @@ def summarize(run_dir: str) -> None:
         open(os.path.join(PROFILES, f"{tag}_traffic.md"), "w").write("\n".join(lines))
         write_counter_summary(tag, prefix, c, run_dir, src)
         print(f"{tag}: mean {sum(durs) / len(durs) / 1e3:.2f} us over {len(durs)}, traffic {hbm / 1e6:.1f} MB")
+    # the opt-in exact split, timed after the step loop on the large workload
+    c = wl.WORKLOADS[LARGE]
+    prefix, tag = "void retro::out_prod_split_kernel<12>", f"split_128x256_{LARGE}"
+    name, durs = steady_dispatches(trace_csv, prefix, 2)
+    flops = 2.0 * c["T"] * c["N"] * c["K"]
+    mean_s = sum(durs) / len(durs) / 1e9
+    lines = [f"# {tag}: rocprofv3 kernel trace", "",
+             f"Command (repository root): `{profile_command('trace', run_dir)}`", "",
+             f"Workload {LARGE}, the opt-in exact split (split_128x256); its first 2 launches (warm-up) are left "
+             "out.", "", *_stats_row(name, durs),
+             f"Algorithmic F32-equivalent TFLOP/s at the mean: {flops / mean_s / 1e12:.2f} "
+             f"({flops / mean_s / 1e12 / PEAK_F32_TFLOPS:.4f} of the F32 peak)", "",
+             f"kernel source_sha256: {src}", ""]
+    open(os.path.join(PROFILES, f"{tag}_trace.md"), "w").write("\n".join(lines))
+    fetch = _counter_means(fetch_csv, prefix)["FETCH_SIZE"]
+    write = _counter_means(write_csv, prefix)["WRITE_SIZE"]
+    hbm = fetch[0] * 1024 * f_scale + write[0] * 1024 * w_scale
+    lines = [f"# {tag}: HBM traffic per launch (rocprofv3 counters)", "", "Commands (repository root):", "",
+             *[f"- `{profile_command(k, run_dir)}`" for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE",
+                                                       "copy_WRITE_SIZE")], "",
+             f"FETCH_SIZE scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f} (1 GiB copy calibration).", "",
+             "| counter | KiB per launch (mean) | launches | scaled bytes |", "|---|---|---|---|",
+             f"| FETCH_SIZE | {fetch[0]:.1f} | {fetch[1]} | {fetch[0] * 1024 * f_scale:.4g} |",
+             f"| WRITE_SIZE | {write[0]:.1f} | {write[1]} | {write[0] * 1024 * w_scale:.4g} |", "",
+             f"hbm_bytes_per_launch: {hbm:.6g}", f"source_sha256: {src}", ""]
+    open(os.path.join(PROFILES, f"{tag}_traffic.md"), "w").write("\n".join(lines))
+    write_counter_summary(tag, prefix, c, run_dir, src)
+    print(f"{tag}: mean {sum(durs) / len(durs) / 1e3:.2f} us, traffic {hbm / 1e6:.1f} MB")
     for tag, (workload, dense, op, variant, prefix) in CASE_TRACES.items():
         path = _find_csv(run_dir, f"trace_{tag}", "kernel_trace.csv")
         if not path:
