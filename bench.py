@@ -664,6 +664,14 @@ def main() -> int:
     mfma_f32 = f32_fl / timed(lambda: q.probe_mfma(q.PROBE_MFMA_F32, sink, 4096)) / 1e12
     bf16_fl = q.probe_mfma(q.PROBE_MFMA_BF16, sink, 4096)
     mfma_bf16 = bf16_fl / timed(lambda: q.probe_mfma(q.PROBE_MFMA_BF16, sink, 4096)) / 1e12
+    # F32 MFMA waves beside FMA waves on the same SIMDs: each alone, then
+    # together. serial_frac = (both - larger) / smaller: 0 when the two run
+    # side by side, 1 when they take turns.
+    mix = {name: timed(lambda m=m, v=v: q.probe_mfma_valu(sink, m, v)) * 1e3
+           for name, m, v in (("mfma_only_ms", 4096, 0), ("valu_only_ms", 0, 8192), ("both_ms", 4096, 8192))}
+    lo, hi = sorted((mix["mfma_only_ms"], mix["valu_only_ms"]))
+    mix = {k: round(x, 4) for k, x in mix.items()}
+    mix["serial_frac"] = round((mix["both_ms"] - hi) / lo, 3)
     csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     cdst = torch.empty_like(csrc)
     copy_gbs = 2.0 * csrc.numel() * 4 / timed(lambda: q.probe_copy(csrc, cdst)) / 1e9
@@ -671,6 +679,7 @@ def main() -> int:
     ceilings = {"kind": "measured on this GPU: MFMA-only loops (no memory), 16-byte copy of 1 GiB",
                 "mfma_f32_tflops": round(mfma_f32, 2), "mfma_bf16_tflops": round(mfma_bf16, 1),
                 "copy_gbs": round(copy_gbs, 1),
+                "mfma_f32_beside_valu": mix,
                 "mfma_f32_clock_ghz": round(mfma_f32 / PEAK_F32_TFLOPS * 2.4, 3)}
     if split is not None:
         split["bf16_mfma_frac_of_measured"] = round(split["bf16_flops_issued_per_launch"] / avg_split / 1e12 / mfma_bf16, 4)

@@ -8,8 +8,10 @@
  * placed against a measured ceiling:
  *   - a matrix-core loop with no memory traffic, for F32-input and bf16
  *     MFMA;
+ *   - the F32-input matrix-core loop beside vector FMA work on the same
+ *     SIMDs, to show whether the two share issue time;
  *   - a device-to-device copy with 16-byte accesses (a STREAM-style copy).
- * They compute nothing of OUT_PROD and are not on its path. Both are
+ * They compute nothing of OUT_PROD and are not on its path. All are
  * asynchronous on `stream` (a hipStream_t, NULL = the null stream), allocate
  * nothing and return the error codes of retro_out_prod.h.
  */
@@ -40,6 +42,22 @@ int64_t retro_probe_sink_floats(void);
  * 1 <= iterations <= 2^20, RETRO_E_NULL for a null sink, RETRO_E_ALIGN for
  * a misaligned one, RETRO_E_HIP for a launch error. */
 int retro_probe_mfma(int kind, float *sink, int64_t iterations, double *flops, void *stream);
+
+/* Matrix core beside vector ALU: 512 workgroups of 8 waves (two per CU,
+ * two waves per SIMD). Waves 0-3 of each run `mfma_iterations` rounds of 4
+ * independent v_mfma_f32_16x16x4_f32 (2048 FLOP each, the small-T kernel's
+ * instruction); waves 4-7 run `valu_iterations` rounds of 16 v_fma_f32 over
+ * 8 independent chains. Either count may be 0. Timed with one count at 0,
+ * then the other, then both: if the two kinds of work ran side by side the
+ * last time would be the larger of the first two, if they share the
+ * SIMDs' issue time it is their sum. Every thread writes one float to
+ * `sink` (device memory of at least retro_probe_sink_floats() floats,
+ * 4-byte aligned). *flops and *valu_instructions (host memory, may be NULL)
+ * receive the MFMA FLOPs and the wave-level FMA instructions of one launch.
+ * Errors: RETRO_E_SHAPE unless both counts are in 0 .. 2^20, RETRO_E_NULL,
+ * RETRO_E_ALIGN, RETRO_E_HIP. */
+int retro_probe_mfma_valu(int64_t mfma_iterations, int64_t valu_iterations, float *sink, double *flops,
+                          int64_t *valu_instructions, void *stream);
 
 /* Copy probe: dst[0 .. bytes) = src[0 .. bytes), both device memory,
  * 16-byte aligned, not overlapping; bytes a multiple of 16 (0 is a no-op).

@@ -70,7 +70,7 @@ EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided",
            "retro_out_prod_views_choice",
            "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
            "retro_row_bytes", "retro_strerror",
-           "retro_probe_sink_floats", "retro_probe_mfma", "retro_probe_copy")
+           "retro_probe_sink_floats", "retro_probe_mfma", "retro_probe_mfma_valu", "retro_probe_copy")
 
 PROBE_MFMA_F32 = 0
 PROBE_MFMA_BF16 = 1
@@ -131,6 +131,8 @@ def _load() -> ctypes.CDLL:
     lib.retro_probe_sink_floats.argtypes = []
     lib.retro_probe_mfma.restype = i32
     lib.retro_probe_mfma.argtypes = [i32, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
+    lib.retro_probe_mfma_valu.restype = i32
+    lib.retro_probe_mfma_valu.argtypes = [i64, i64, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), vp]
     lib.retro_probe_copy.restype = i32
     lib.retro_probe_copy.argtypes = [vp, vp, i64, vp]
     lib.retro_strerror.restype = ctypes.c_char_p
@@ -379,6 +381,19 @@ def probe_mfma(kind: int, sink, iterations: int, stream=None) -> float:
     flops = ctypes.c_double(0.0)
     _check(lib.retro_probe_mfma(int(kind), _ptr(sink), int(iterations), ctypes.byref(flops), _stream_handle(stream)))
     return flops.value
+
+
+def probe_mfma_valu(sink, mfma_iterations: int, valu_iterations: int, stream=None):
+    """Enqueue the matrix-core-beside-vector-ALU probe; returns (MFMA FLOPs,
+    wave-level FMA instructions) of the launch."""
+    _device_tensor(sink, "sink")
+    if sink.dtype != torch.float32 or sink.numel() < int(lib.retro_probe_sink_floats()):
+        raise ValueError("sink must be a float32 buffer of retro_probe_sink_floats() elements")
+    flops = ctypes.c_double(0.0)
+    instrs = ctypes.c_int64(0)
+    _check(lib.retro_probe_mfma_valu(int(mfma_iterations), int(valu_iterations), _ptr(sink), ctypes.byref(flops),
+                                     ctypes.byref(instrs), _stream_handle(stream)))
+    return flops.value, instrs.value
 
 
 def probe_copy(src, dst, stream=None) -> None:

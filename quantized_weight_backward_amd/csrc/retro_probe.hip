@@ -1,6 +1,7 @@
 // retro_probe.hip - the measured ceilings declared in retro_probe.h: a
-// matrix-core loop with no memory traffic and a 16-byte vector copy. They
-// share nothing with the OUT_PROD kernels.
+// matrix-core loop with no memory traffic, the same loop beside vector FMA
+// work on the same SIMDs, and a 16-byte vector copy. They share nothing with
+// the OUT_PROD kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -9,6 +10,7 @@
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -53,6 +55,49 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(float* sink, 
     sink[blockIdx.x * kProbeThreads + threadIdx.x] = s;
 }
 
+// Matrix core beside vector ALU: a workgroup of 8 waves, two per SIMD
+// (waves are placed on the SIMDs in turn). Waves 0-3 run `mfma_iterations`
+// rounds of 4 independent v_mfma_f32_16x16x4_f32 chains, waves 4-7 run
+// `valu_iterations` rounds of 16 v_fma_f32 over 8 independent chains.
+// Timing the kernel with either count at 0 and then with both shows whether
+// the two kinds of work share the SIMD's issue time or run side by side.
+constexpr int kMixBlocks = 512;    // 2 workgroups per CU
+constexpr int kMixThreads = 512;   // 8 waves
+constexpr int kMixFmaChains = 8;
+__global__ __launch_bounds__(kMixThreads) void mfma_valu_probe_kernel(float* sink, int mfma_iterations,
+                                                                      int valu_iterations) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    float s = 0.f;
+    if (wave < 4) {
+        const float a = 0.0078125f * (1.f + float(lane) * 0.0009765625f);
+        const float b = 0.0078125f * (1.f - float(lane) * 0.0009765625f);
+        f32x4 acc[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < mfma_iterations; ++i)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    } else {
+        // x -> x m + c then x m - c: values stay near their start for any count
+        float v[kMixFmaChains];
+#pragma unroll
+        for (int j = 0; j < kMixFmaChains; ++j) v[j] = 1.f + float(lane) * 0.0009765625f + float(j);
+        const float m = 1.0000001f, c = 1e-7f;
+        for (int i = 0; i < valu_iterations; ++i) {
+#pragma unroll
+            for (int j = 0; j < kMixFmaChains; ++j) v[j] = __builtin_fmaf(v[j], m, c);
+#pragma unroll
+            for (int j = 0; j < kMixFmaChains; ++j) v[j] = __builtin_fmaf(v[j], m, -c);
+        }
+#pragma unroll
+        for (int j = 0; j < kMixFmaChains; ++j) s += v[j];
+    }
+    sink[blockIdx.x * kMixThreads + threadIdx.x] = s;
+}
+
 // Copy of n 16-byte units: workgroup b copies units 1024 b .. 1024 b + 1023,
 // thread i units 1024 b + 256 j + i (j = 0..3), all four loads issued before
 // the stores.
@@ -94,6 +139,22 @@ extern "C" int retro_probe_mfma(int kind, float* sink, int64_t iterations, doubl
     else
         hipLaunchKernelGGL(mfma_probe_kernel<RETRO_PROBE_MFMA_BF16>, dim3(kProbeBlocks), dim3(kProbeThreads), 0, st,
                            sink, int(iterations));
+    return launch_status();
+}
+
+extern "C" int retro_probe_mfma_valu(int64_t mfma_iterations, int64_t valu_iterations, float* sink, double* flops,
+                                     int64_t* valu_instructions, void* stream) {
+    if (mfma_iterations < 0 || mfma_iterations > kMaxIterations || valu_iterations < 0 ||
+        valu_iterations > kMaxIterations)
+        return RETRO_E_SHAPE;
+    if (!sink) return RETRO_E_NULL;
+    if (reinterpret_cast<uintptr_t>(sink) % 4) return RETRO_E_ALIGN;
+    static_assert(int64_t(kMixBlocks) * kMixThreads <= int64_t(kProbeBlocks) * kProbeThreads, "sink size");
+    if (flops) *flops = double(kMixBlocks) * 4 * double(mfma_iterations) * kChains * (16.0 * 16 * 4 * 2);
+    if (valu_instructions) *valu_instructions = int64_t(kMixBlocks) * 4 * valu_iterations * 2 * kMixFmaChains;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(mfma_valu_probe_kernel, dim3(kMixBlocks), dim3(kMixThreads), 0, static_cast<hipStream_t>(stream),
+                       sink, int(mfma_iterations), int(valu_iterations));
     return launch_status();
 }
 

@@ -351,6 +351,12 @@ def test_probe_validation():
     assert mfma(q.PROBE_MFMA_BF16, 0x100000, (1 << 20) + 1, None, None) == q.E_SHAPE
     assert mfma(q.PROBE_MFMA_F32, None, 10, None, None) == q.E_NULL
     assert mfma(q.PROBE_MFMA_F32, 0x100002, 10, None, None) == q.E_ALIGN
+    mix = q.lib.retro_probe_mfma_valu
+    # (mfma_iterations, valu_iterations, sink, flops, valu_instructions, stream)
+    assert mix(-1, 0, 0x100000, None, None, None) == q.E_SHAPE
+    assert mix(0, (1 << 20) + 1, 0x100000, None, None, None) == q.E_SHAPE
+    assert mix(1, 1, None, None, None, None) == q.E_NULL
+    assert mix(1, 1, 0x100001, None, None, None) == q.E_ALIGN
     # (src, dst, bytes, stream)
     assert copy(0x100000, 0x200000, -16, None) == q.E_SHAPE
     assert copy(0x100000, 0x200000, 24, None) == q.E_SHAPE

@@ -1,5 +1,5 @@
 """The measured-ceiling probes on the GPU: the copy is exact, the matrix-core
-loop reports the FLOPs it performs and leaves finite sums. (They compute
+loops report the work they perform and leave finite sums. (They compute
 nothing of OUT_PROD; bench.py times them.)"""
 
 import numpy as np
@@ -30,3 +30,20 @@ def test_mfma_probe(kind, per_mfma):
     assert flops == 2048 * 4 * 16 * 4 * per_mfma
     s = sink.cpu().numpy()
     assert np.isfinite(s).all() and (s > 0).all()
+
+
+@pytest.mark.parametrize("mfma_it,valu_it", [(16, 0), (0, 16), (16, 32)])
+def test_mfma_valu_probe(mfma_it, valu_it):
+    sink = q.probe_sink()
+    sink.fill_(float("nan"))
+    flops, instrs = q.probe_mfma_valu(sink, mfma_it, valu_it)
+    torch.cuda.synchronize()
+    assert flops == 512 * 4 * mfma_it * 4 * 2048
+    assert instrs == 512 * 4 * valu_it * 16
+    s = sink[:512 * 512].cpu().numpy().reshape(512, 8, 64)
+    assert np.isfinite(s).all()
+    # MFMA waves: 0 with no iterations, positive sums otherwise; FMA waves
+    # end near their start values 1 + lane/1024 + chain, summed over 8 chains
+    assert (s[:, :4] > 0).all() if mfma_it else (s[:, :4] == 0).all()
+    lanes = 8 * (1 + np.arange(64) / 1024) + 28
+    assert np.allclose(s[:, 4:], lanes, rtol=1e-4)
