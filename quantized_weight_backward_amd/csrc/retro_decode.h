@@ -290,6 +290,17 @@ __device__ __forceinline__ void q4_k_x4(uint32_t w, bool high, float a, float b,
     for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) - b;
 }
 
+// Q4_K with the nibbles selected by `mask`: 0x0F0F0F0F gives q (a = d*sc),
+// 0xF0F0F0F0 leaves the high nibbles in place as 16 q, to be scaled by
+// a = d*sc/16. Either way a times the byte is (d*sc)*q exactly, so the value
+// is the same a*q - b rounded once as q4_k_x4's, with one AND per four
+// elements instead of a shift and an AND.
+__device__ __forceinline__ void q4_k_x4_masked(uint32_t w, uint32_t mask, float a, float b, float out[4]) {
+    const uint32_t m = w & mask;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = a * static_cast<float>((m >> (8 * i)) & 0xFFu) - b;
+}
+
 // Q5_K: low (high = false) or high nibbles of four qs bytes, plus bit
 // `bit` of the four qh bytes of the same elements as the fifth bit;
 // value a*q - b with a = d*sc_j, b = dmin*m_j (q4_k_coeffs; same field).

@@ -1103,11 +1103,15 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
         const int c = (k0 & 255) >> 6;
         float am, bm;
         q4_k_coeffs(r.hdr[0], r.hdr[1], r.hdr[2], r.hdr[3], 2 * c + (lane & 1), am, bm);
+        // Q4_K: the odd sub-block's elements are the high nibbles, kept in
+        // place as 16 q by the mask below, so their scale is d*sc/16 (exact)
+        if constexpr (TYPE == kQ4_K) am *= (lane & 1) ? 0.0625f : 1.0f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int src = 2 * (4 * rq + s) + hi;
             if constexpr (TYPE == kQ4_K)
-                q4_k_x4(r.code[s][0], hi != 0, lane_value(am, src), lane_value(bm, src), wv[s]);
+                q4_k_x4_masked(r.code[s][0], hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu, lane_value(am, src), lane_value(bm, src),
+                               wv[s]);
             else
                 q5_k_x4(r.code[s][0], r.code[s][1], 2 * c + hi, hi != 0, lane_value(am, src), lane_value(bm, src),
                         wv[s]);

@@ -46,14 +46,6 @@ struct WsShape {
     static constexpr int CK = 4 / CT;
     static constexpr int BT = 32 * WA * CT;
     static constexpr int BK = 32 * WB * CK;
-    // Workgroups per CU the register budget is set for: two for the 32-row
-    // tiles (46 KB of LDS), whose second workgroup fills the first one's
-    // barrier waits; one otherwise. The kernel's launch bound states it as
-    // waves per SIMD (amdgpu_waves_per_eu): a workgroup's waves spread over
-    // the CU's four SIMDs, so two 8-wave workgroups are 4 waves per SIMD, a
-    // budget of 128 VGPRs each.
-    static constexpr int kWgPerCu = (BT == 32 && NG == 1) ? 2 : 1;
-    static constexpr int kWavesPerSimd = kThreads / 64 / 4 * kWgPerCu;
     static constexpr int BN = 32;
     static_assert(BK == 128 || BK == 256, "K tile of 128 or 256 columns");
     static_assert(!kSuperBlock<TYPE> || BK == 256, "K-quant tiles hold whole super-blocks");
@@ -64,6 +56,14 @@ struct WsShape {
     static constexpr int BUF_FLOATS = G_FLOATS + W_FLOATS;
     // workgroups that fit on a CU by LDS (160 KB), at most two (16 waves)
     static constexpr int kResident = (NG == 2 || (160 * 1024) / (2 * BUF_FLOATS * 4) < 2) ? 1 : 2;
+    // Workgroups per CU the register budget is set for: two for the 32-row
+    // tiles whose LDS allows it (32x128, 45 KB), whose second workgroup fills
+    // the first one's barrier waits; one otherwise. The kernel's launch bound
+    // states it as waves per SIMD (amdgpu_waves_per_eu): a workgroup's waves
+    // spread over the CU's four SIMDs, so two 8-wave workgroups are 4 waves
+    // per SIMD, a budget of 128 VGPRs each.
+    static constexpr int kWgPerCu = (BT == 32 && kResident == 2) ? 2 : 1;
+    static constexpr int kWavesPerSimd = kThreads / 64 / 4 * kWgPerCu;
     static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // float4 of G per producer thread
     static_assert(GSLOTS * kPThreads * 4 == BT * BN, "G chunk splits evenly");
     // Dense W: units of 4 rows x 4 consecutive k (16 bytes of F32 or 8 of
