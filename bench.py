@@ -113,7 +113,7 @@ def read_traffic(tag: str):
 
 
 BENCH_PROFILE_ARGS = "--steps 20 --warmup 5 --reps 20 --no-cpu-baseline"  # the step loop as the driver runs it
-COUNTER_ARGS = "--steps 3 --warmup 1 --reps 3 --no-cpu-baseline"
+COUNTER_ARGS = "--steps 3 --warmup 1 --reps 3 --min-ms 0 --no-cpu-baseline"
 PROFILE_WARMUP = 5  # launches of each kernel dropped from a trace summary (the bench's warm-up steps)
 PROFILE_STEPS = 20  # the timed steps that follow them
 PROFILE_COMMANDS = {
@@ -428,12 +428,69 @@ def cpu_baseline_skinny(case: dict) -> dict:
             "sample": f"all {case['T']} t rows of {SKINNY} (full decode of W included), {secs:.2f} s"}
 
 
+def oracle_timing(case: dict) -> dict:
+    """The CPU oracle beside a workload's GPU figure: single-threaded, median of
+    3 calls (100 for shapes under 10 MFLOP), on all t rows or, for the larger
+    shapes, a bounded sample of them (threaded over t rows on up to 16 host
+    threads when even the sample is large)."""
+    import numpy as np
+
+    import oracle
+
+    T, N, K = case["T"], case["N"], case["K"]
+    full = 2.0 * T * N * K
+    threads, rows = 1, T
+    if full > 1e11:  # hundreds of GFLOP: threaded over a sample of t rows
+        threads = max(1, min(16, os.cpu_count() or 1))
+        rows = min(T, 16 * threads)
+    elif full > 1e10:  # tens of GFLOP: one thread on a sample of t rows
+        rows = min(T, 16)
+    sel = np.arange(rows)
+    repeats = 100 if full < 1e7 else 3
+    secs = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.out_prod(case["type"], case["W"], case["G"], K, rows=sel, nthreads=threads)
+        secs.append(time.perf_counter() - t0)
+    med = float(np.median(secs))
+    return {"value": 2.0 * N * K * rows / med / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {T} t rows (full decode of W included), median of {repeats}: {med:.4f} s"}
+
+
+def smi_clock_under_load(sink) -> dict:
+    """Graphics clocks that amd-smi reports while about 4 s of the F32 matrix-
+    core probe run (queued before the query, so the query lands inside them)."""
+    import subprocess
+
+    import torch
+
+    import quantized_weight_backward_amd as q
+
+    for _ in range(1100):
+        q.probe_mfma(q.PROBE_MFMA_F32, sink, 4096)
+    res = {"source": "amd-smi metric -c --json"}
+    try:
+        time.sleep(0.5)
+        txt = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        gpu = json.loads(txt)["gpu_data"][0]["clock"]
+        gfx = sorted(k for k in gpu if k.startswith("gfx_"))
+        res["gfx_mhz"] = [gpu[k]["clk"]["value"] for k in gfx]
+        res["max_mhz"] = gpu[gfx[0]]["max_clk"]["value"]
+    except Exception as exc:  # the tool may be absent or print something else
+        res["error"] = f"{type(exc).__name__}: {exc}"[:200]
+    torch.cuda.synchronize()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--reps", type=int, default=20, help="back-to-back launches per workload timed after the steps")
+    ap.add_argument("--reps", type=int, default=20, help="launches per workload timed after the steps (at least)")
+    ap.add_argument("--min-ms", type=float, default=100.0,
+                    help="each back-to-back batch covers at least this many ms of launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this size (counter calibration)")
@@ -576,12 +633,19 @@ def main() -> int:
     # The small-T kernel on its own: launch pairs inside the step include the
     # events' own overhead (a few us against a ~25 us kernel), so its figures
     # come from launches back to back on rotated W copies.
-    avg_skinny = back_to_back(lambda i: q.out_prod(q.Q4_K, Ws[i % n_rot], Gs, skinny["K"], out=Ds),
-                              max(args.reps, 2 * n_rot))
+    def batch_reps(est_s):
+        """Launches in a back-to-back batch: at least --reps and two rounds of
+        the rotated copies, and enough to cover --min-ms (at most 5000)."""
+        return max(args.reps, 2 * n_rot, min(5000, int(np.ceil(args.min_ms * 1e-3 / max(est_s, 1e-7)))))
+
+    call_skinny = lambda i: q.out_prod(q.Q4_K, Ws[i % n_rot], Gs, skinny["K"], out=Ds)  # noqa: E731
+    skinny_reps = batch_reps(float(np.median(t_skinny)))
+    avg_skinny = back_to_back(call_skinny, skinny_reps)
 
     # Every benchmarked workload at the kernel retro_out_prod chooses.
     print("bench: timing every workload", file=sys.stderr, flush=True)
     per_workload = []
+    oracle_cases = []  # (entry, case) timed on the CPU after all GPU work
     for workload, dense in WORKLOADS:
         if workload == LARGE:
             c, W_list, G, D = large, [Wl], Gl, Dl
@@ -595,24 +659,40 @@ def main() -> int:
         wtype, K, N, T = c["type"], c["K"], c["N"], c["T"]
         variant = q.VARIANT_NAMES[q.choice(wtype, K, N, T)]
         call = lambda i: q.out_prod(wtype, W_list[i % len(W_list)], G, K, out=D)  # noqa: E731
-        for i in range(3):
+        for i in range(5):
             call(i)
         torch.cuda.synchronize()
-        reps = max(args.reps, 2 * len(W_list))
+        # The mean launch time from one back-to-back batch of at least
+        # --min-ms (sized from 5 launches timed together); then per-launch
+        # event pairs (median, min), with the clock at its loaded level.
+        npairs = max(args.reps, 2 * len(W_list))
+        est = back_to_back(call, 5)
+        reps = max(npairs, min(5000, int(np.ceil(args.min_ms * 1e-3 / est))))
         sec = back_to_back(call, reps)
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(npairs)]
+        for i, e in enumerate(pev):
+            e[0].record(stream)
+            call(i)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        pairs = np.array([e[0].elapsed_time(e[1]) for e in pev]) * 1e-3
         flops = 2.0 * T * N * K
         wb = float(c["W"].nbytes)
         t_roof = max(wb / (PEAK_HBM_GBS * 1e9), flops / (PEAK_F32_TFLOPS * 1e12))
         tag = f"{variant}_{workload_tag(workload, dense)}"
         per_workload.append({
             "workload": workload_tag(workload, dense), "weight_type": wl.TYPE_NAMES[wtype], "kernel": variant,
-            "launches": reps, "avg_launch_us": round(sec * 1e6, 3), "tflops": round(flops / sec / 1e12, 3),
+            "launches": reps, "avg_launch_us": round(sec * 1e6, 3),
+            "event_pairs": {"launches": npairs, "median_us": round(float(np.median(pairs)) * 1e6, 3),
+                            "min_us": round(float(pairs.min()) * 1e6, 3)},
+            "tflops": round(flops / sec / 1e12, 3),
             "f32_mfma_frac": round(flops / sec / 1e12 / PEAK_F32_TFLOPS, 4),
             "weight_gbs": round(wb / sec / 1e9, 1), "hbm_frac_weights": round(wb / sec / 1e9 / PEAK_HBM_GBS, 4),
             "binding_roof": "f32_mfma" if flops / (PEAK_F32_TFLOPS * 1e12) >= wb / (PEAK_HBM_GBS * 1e9) else "hbm",
             "binding_roof_frac": round(t_roof / sec, 4), "traffic": read_traffic(tag),
             "w_copies_rotated": len(W_list)})
         if workload not in (LARGE, SKINNY):
+            oracle_cases.append((per_workload[-1], c))
             del W_list, G, D
             torch.cuda.empty_cache()
 
@@ -675,11 +755,15 @@ def main() -> int:
     csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     cdst = torch.empty_like(csrc)
     copy_gbs = 2.0 * csrc.numel() * 4 / timed(lambda: q.probe_copy(csrc, cdst)) / 1e9
-    del csrc, cdst, sink
+    del csrc, cdst
+    clock = None
+    if not args.no_cpu_baseline:
+        clock = smi_clock_under_load(sink)
     ceilings = {"kind": "measured on this GPU: MFMA-only loops (no memory), 16-byte copy of 1 GiB",
                 "mfma_f32_tflops": round(mfma_f32, 2), "mfma_bf16_tflops": round(mfma_bf16, 1),
                 "copy_gbs": round(copy_gbs, 1),
                 "mfma_f32_beside_valu": mix,
+                "smi_clock_under_mfma_load": clock,
                 "mfma_f32_clock_ghz": round(mfma_f32 / PEAK_F32_TFLOPS * 2.4, 3)}
     if split is not None:
         split["bf16_mfma_frac_of_measured"] = round(split["bf16_flops_issued_per_launch"] / avg_split / 1e12 / mfma_bf16, 4)
@@ -735,6 +819,13 @@ def main() -> int:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(large)
         out["cpu_baseline_skinny"] = cpu_baseline_skinny(skinny)
+        for entry, c in oracle_cases:
+            entry["oracle"] = oracle_timing(c)
+        for entry in per_workload:
+            if entry["workload"] == LARGE:
+                entry["oracle"] = {k: out["cpu_baseline"][k] for k in ("value", "unit", "cores", "sample")}
+            elif entry["workload"] == SKINNY:
+                entry["oracle"] = {k: out["cpu_baseline_skinny"][k] for k in ("value", "unit", "cores", "sample")}
     print(json.dumps(out), flush=True)
     return 0
 
