@@ -5,9 +5,9 @@
  *
  *     dst[t][k] = sum_{n=0}^{N-1} W[n][k] * G[t][n]
  *
- * This is the backward of mul_mat(W, x) with respect to x (llama.cpp PR #3
- * "cuda: out_prod accepts a quantized src0", commit message: the backward of
- * mul_mat(W, x) w.r.t. x is out_prod(W, grad^T)). The PR admits a contiguous
+ * It gives the gradient of mul_mat(W, x) with respect to its input x: an
+ * OUT_PROD of W with the transposed output gradient (llama.cpp PR #3 "cuda:
+ * out_prod accepts a quantized src0", commit message). The PR admits a contiguous
  * quantized, F16 or BF16 src0 with F32 src1 and dst (section "What"); the
  * Retrograd CUDA status page lists OUT_PROD for F32, F16, BF16 and quantized
  * types (section "What works on the GPU"). W[n][k] is the value the stored
@@ -392,8 +392,8 @@ int retro_out_prod_strided_variant_applies(int variant, int type, int64_t K, int
 /*
  * mul_mat, the forward of the layer whose input gradient retro_out_prod
  * computes (the llama.cpp PR #3 "cuda: out_prod accepts a quantized src0",
- * commit message: the backward of mul_mat(W, x) with respect to x is
- * out_prod(W, grad^T)), through the same packed W:
+ * commit message, takes that input gradient as an OUT_PROD of W with the
+ * transposed output gradient), through the same packed W:
  *
  *     Y[t][n] = sum_{k=0}^{K-1} W[n][k] * X[t][k]        t < T, n < N
  *
