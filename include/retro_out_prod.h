@@ -208,6 +208,11 @@ const char *retro_strerror(int code);
  *                           the TILE_* kernel takes the others
  *   RETRO_VARIANT_SIMPLE    retro_mul_mat only: one thread per output, for
  *                           the shapes the tiled kernel refuses
+ *   RETRO_VARIANT_WS_256x256  the 256 x 256 tile: eight MFMA waves (each
+ *                           the 64 x 128 block of WS_128x256's) share one set
+ *                           of four producer waves, so every decoded weight
+ *                           feeds twice as many products; 144 KB of LDS, one
+ *                           workgroup of 12 waves per CU
  *   RETRO_VARIANT_WS2_64x128  WS_64x128 with two pipelines in one
  *                           workgroup (even and odd 32-row chunks of W,
  *                           partial sums added in LDS in that order): two
@@ -258,7 +263,8 @@ enum {
     RETRO_VARIANT_WS2_64x128 = 13,
     RETRO_VARIANT_SIMPLE = 15,
     RETRO_VARIANT_SPLIT_128x256 = 16,
-    RETRO_VARIANT_SPLIT_128x128 = 17
+    RETRO_VARIANT_SPLIT_128x128 = 17,
+    RETRO_VARIANT_WS_256x256 = 18
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the

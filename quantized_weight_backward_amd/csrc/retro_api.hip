@@ -82,6 +82,9 @@ constexpr TileVariant kTiles[] = {
     {RETRO_VARIANT_TILE_64x128, 64, 128, 1.08, false},
     {RETRO_VARIANT_TILE_64x64, 64, 64, 1.20, false},
     {RETRO_VARIANT_WS_128x256, 128, 256, 1.00, true},
+    // eight MFMA waves share the producers' decode: 0.88 against 0.84 of the
+    // F32 peak for 128 x 256 at Q4_K 14336 x 4096, T = 4096 (equal rounds)
+    {RETRO_VARIANT_WS_256x256, 256, 256, 0.95, true},
     {RETRO_VARIANT_WS_64x256, 64, 256, 1.04, true},
     {RETRO_VARIANT_WS_128x128, 128, 128, 1.00, true},
     {RETRO_VARIANT_WS_64x128, 64, 128, 1.02, true},

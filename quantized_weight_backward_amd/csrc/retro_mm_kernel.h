@@ -281,6 +281,7 @@ struct MmShape {
     static constexpr bool kDense = F::kBlock == 1;
     static constexpr int kPThreads = 256;
     static constexpr int kThreads = 2 * kPThreads;
+    static constexpr int NC = 4;  // consumer waves
     static_assert(CT == 1 || CT == 2, "consumer grid 1 x 4 or 2 x 2");
     static constexpr int CK = 4 / CT;
     static constexpr int BT = 32 * WA * CT;  // rows of x per tile

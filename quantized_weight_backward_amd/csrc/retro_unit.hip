@@ -82,10 +82,10 @@ int launch_tile(const void* W, const float* G, float* dst, int64_t K, int64_t N,
     return launch_status();
 }
 
-template <int TYPE, int WA, int WB, int CT, int NG = 1>
+template <int TYPE, int WA, int WB, int CT, int NG = 1, int NC = 4>
 int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
               hipStream_t st) {
-    using S = WsShape<TYPE, WA, WB, CT, NG>;
+    using S = WsShape<TYPE, WA, WB, CT, NG, NC>;
     TileArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.G = G;
@@ -107,9 +107,9 @@ int launch_ws(const void* W, const float* G, float* dst, int64_t K, int64_t N, i
     clear_last_error();
     const dim3 grid(nt, unsigned(s.batches()));
     if (s.gcols)
-        hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG, true>), grid, dim3(S::kThreads), 0, st, a);
+        hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG, NC, true>), grid, dim3(S::kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG, false>), grid, dim3(S::kThreads), 0, st, a);
+        hipLaunchKernelGGL((out_prod_ws_kernel<TYPE, WA, WB, CT, NG, NC, false>), grid, dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
 
@@ -213,6 +213,7 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
         case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, st);
         case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, s, st);
         case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_WS_256x256: return launch_ws<TYPE, 4, 2, 2, 1, 8>(W, G, dst, K, N, T, s, st);
         case RETRO_VARIANT_WS_128x256: return launch_ws<TYPE, 2, 4, 2>(W, G, dst, K, N, T, s, st);
         case RETRO_VARIANT_WS_64x256: return launch_ws<TYPE, 1, 4, 2>(W, G, dst, K, N, T, s, st);
         case RETRO_VARIANT_WS_32x256: return launch_ws<TYPE, 1, 2, 1>(W, G, dst, K, N, T, s, st);

@@ -34,16 +34,21 @@
 
 namespace retro {
 
-template <int TYPE, int WA, int WB, int CT, int NG = 1>
+template <int TYPE, int WA, int WB, int CT, int NG = 1, int NC_ = 4>
 struct WsShape {
     using F = Format<TYPE>;
     static constexpr bool kDense = F::kBlock == 1;
     static_assert(NG == 1 || NG == 2, "one or two pipelines");
-    static constexpr int kPThreads = 256;               // producer threads of one pipeline (4 waves)
-    static constexpr int kThreads = 2 * kPThreads * NG;  // + 4 consumer waves per pipeline
+    // consumer waves per pipeline: 4, or 8 (one pipeline) for the 256 x 256
+    // tile, whose producers' decode then feeds twice the matrix work
+    static constexpr int NC = NC_;
+    static_assert(NC == 4 || (NC == 8 && NG == 1), "4 consumer waves, or 8 with one pipeline");
+    static constexpr int kPThreads = 256;                        // producer threads of one pipeline (4 waves)
+    static constexpr int kCThreads = 64 * NC;                    // consumer threads of one pipeline
+    static constexpr int kThreads = (kCThreads + kPThreads) * NG;
     // consumer waves CT x CK, each (32*WA) x (32*WB) outputs
-    static_assert(CT == 1 || CT == 2, "consumer grid 1 x 4 or 2 x 2");
-    static constexpr int CK = 4 / CT;
+    static_assert((NC == 4 && (CT == 1 || CT == 2)) || (NC == 8 && CT == 2), "consumer grid 1x4, 2x2 or 2x4");
+    static constexpr int CK = NC / CT;
     static constexpr int BT = 32 * WA * CT;
     static constexpr int BK = 32 * WB * CK;
     static constexpr int BN = 32;
@@ -64,6 +69,7 @@ struct WsShape {
     // per SIMD, a budget of 128 VGPRs each.
     static constexpr int kWgPerCu = (BT == 32 && kResident == 2) ? 2 : 1;
     static constexpr int kWavesPerSimd = kThreads / 64 / 4 * kWgPerCu;
+    static_assert(kThreads % 256 == 0, "whole waves on each of the four SIMDs");
     static constexpr int GSLOTS = BT * BN / 4 / kPThreads;  // float4 of G per producer thread
     static_assert(GSLOTS * kPThreads * 4 == BT * BN, "G chunk splits evenly");
     // Dense W: units of 4 rows x 4 consecutive k (16 bytes of F32 or 8 of
@@ -127,7 +133,8 @@ template <typename S, int WA, int WB, int NG>
 __device__ __forceinline__ void ws_consume(float* lds_all, int tid, int wave, int nloc, int t0, int c0, int T,
                                            int ncols, float* dst, long long ldd) {
     const int lane = tid & 63;
-    const int cg = wave >> 2, cw = wave & 3;  // pipeline, wave within it
+    static_assert(NG == 1 || S::NC == 4, "two pipelines have four consumer waves each");
+    const int cg = wave / S::NC, cw = wave % S::NC;  // pipeline, wave within it
     const int wt = cw / S::CK, wk = cw % S::CK;
     const float* const lds = lds_all + cg * 2 * S::BUF_FLOATS;
     constexpr int GP = S::GP, WP = S::WP;
@@ -171,23 +178,37 @@ __device__ __forceinline__ void ws_consume(float* lds_all, int tid, int wave, in
     // run; phase 0 of the next chunk (buffer 1 - BUF) is read right after the
     // barrier that publishes it, ahead of this chunk's last MFMAs. After the
     // last chunk that read sees a stale buffer and its values are unused.
-    f32x4 a0[WA], a1[WA], b0[WB], b1[WB];
+    // With eight consumer waves (two per SIMD) the register budget holds one
+    // operand set: each phase is read, then contracted, and the SIMD's other
+    // consumer wave covers the read latency.
+    constexpr bool kPrefetch = S::NC == 4;
+    f32x4 a0[WA], b0[WB];
+    f32x4 a1[kPrefetch ? WA : 1], b1[kPrefetch ? WB : 1];
     auto chunk = [&](auto buf_tag) {
         using Next = std::integral_constant<int, 1 - decltype(buf_tag)::value>;
-        read_phase(buf_tag, 1, a1, b1);
-        mfma_phase(a0, b0);
-        read_phase(buf_tag, 2, a0, b0);
-        mfma_phase(a1, b1);
-        read_phase(buf_tag, 3, a1, b1);
-        mfma_phase(a0, b0);
-        __syncthreads();
-        read_phase(Next{}, 0, a0, b0);
-        mfma_phase(a1, b1);
+        if constexpr (kPrefetch) {
+            read_phase(buf_tag, 1, a1, b1);
+            mfma_phase(a0, b0);
+            read_phase(buf_tag, 2, a0, b0);
+            mfma_phase(a1, b1);
+            read_phase(buf_tag, 3, a1, b1);
+            mfma_phase(a0, b0);
+            __syncthreads();
+            read_phase(Next{}, 0, a0, b0);
+            mfma_phase(a1, b1);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                read_phase(buf_tag, q, a0, b0);
+                mfma_phase(a0, b0);
+            }
+            __syncthreads();
+        }
     };
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
     __syncthreads();
-    read_phase(Buf0{}, 0, a0, b0);
+    if constexpr (kPrefetch) read_phase(Buf0{}, 0, a0, b0);
     for (int c = 0; c < nloc; c += 2) {
         chunk(Buf0{});
         if (c + 1 < nloc) chunk(Buf1{});
@@ -234,10 +255,10 @@ __device__ __forceinline__ void ws_consume(float* lds_all, int tid, int wave, in
 
 // GCOLS: G stored t-fastest (args.ldg floats between its columns); the
 // consumers see the same LDS contents either way.
-template <int TYPE, int WA, int WB, int CT, int NG, bool GCOLS>
-__global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWavesPerSimd)) void out_prod_ws_kernel(
-    TileArgs args) {
-    using S = WsShape<TYPE, WA, WB, CT, NG>;
+template <int TYPE, int WA, int WB, int CT, int NG, int NC, bool GCOLS>
+__global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
+                             (WsShape<TYPE, WA, WB, CT, NG, NC>::kWavesPerSimd)) void out_prod_ws_kernel(TileArgs args) {
+    using S = WsShape<TYPE, WA, WB, CT, NG, NC>;
     using F = Format<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, WP = S::WP;
 
@@ -258,10 +279,10 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWavesPer
     // after the prologue, one per chunk): the role test is uniform per wave,
     // and keeping the loops apart keeps the consumers' accumulators and the
     // producers' staging registers from being allocated side by side.
-    if (wave >= 4 * NG) {
+    if (wave >= NC * NG) {
         // ---------------- producer ----------------
-        const int pg = (tid - NG * S::kPThreads) >> 8;  // pipeline
-        const int p = (tid - NG * S::kPThreads) & (S::kPThreads - 1);
+        const int pg = (tid - NG * S::kCThreads) >> 8;  // pipeline
+        const int p = (tid - NG * S::kCThreads) & (S::kPThreads - 1);
         float* const lds = lds_all + pg * 2 * S::BUF_FLOATS;
         auto chunk_n0 = [&](int c) { return (pg + NG * c) * BN; };
         const long long kb0 = (long long)(k0 / F::kBlock) * F::kBytes;
@@ -495,12 +516,15 @@ __global__ __launch_bounds__(512 * NG, (WsShape<TYPE, WA, WB, CT, NG>::kWavesPer
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float* row = gs + (4 * (p / CG) + j) * GP + c0;
-                    if constexpr (GS == 4) {
-                        *reinterpret_cast<float4*>(row) =
-                            make_float4(elem(greg[0], j), elem(greg[1], j), elem(greg[2], j), elem(greg[3], j));
+                    if constexpr (GS % 4 == 0) {  // GS / 4 vectors of 4 columns
+#pragma unroll
+                        for (int v = 0; v < GS; v += 4)
+                            *reinterpret_cast<float4*>(row + v) = make_float4(elem(greg[v], j), elem(greg[v + 1], j),
+                                                                              elem(greg[v + 2], j), elem(greg[v + 3], j));
                     } else if constexpr (GS == 2) {
                         *reinterpret_cast<float2*>(row) = make_float2(elem(greg[0], j), elem(greg[1], j));
                     } else {
+                        static_assert(GS == 1, "G slots per producer thread: 1, 2 or a multiple of 4");
                         row[0] = elem(greg[0], j);
                     }
                 }

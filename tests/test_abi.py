@@ -97,7 +97,13 @@ def test_supported():
 
 def test_choice():
     assert q.choice(q.Q4_K, 14336, 4096, 16) == q.VARIANT_SKINNY
-    assert q.choice(q.Q4_K, 4096, 14336, 4096) == q.VARIANT_WS_128x256
+    # one round of 256 x 256 tiles (eight MFMA waves per workgroup) ties with
+    # two of 128 x 256 by tile area and measures faster; fewer tiles than
+    # CUs keep the smaller tiles
+    assert q.choice(q.Q4_K, 4096, 14336, 4096) == q.VARIANT_WS_256x256
+    assert q.choice(q.Q4_K, 4096, 14336, 8192) == q.VARIANT_WS_256x256
+    assert q.choice(q.Q4_K, 4096, 14336, 2048) == q.VARIANT_WS_128x256
+    assert q.choice(q.Q4_K, 14336, 4096, 4096) == q.VARIANT_WS_128x256  # 3.5 rounds of 256 x 256
     assert q.choice(q.Q4_0, 5120, 17408, 2048) == q.VARIANT_WS_64x128
     assert q.choice(q.Q4_0, 5120, 17407, 2048) == q.VARIANT_TILE_64x128  # N % 4 != 0: the fallback family
     for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0, q.Q4_1, q.Q5_0, q.Q5_1):
@@ -115,7 +121,7 @@ def test_choice():
     assert q.choice(q.F16, 301, 77, 200) == q.VARIANT_TILE_64x64  # 602-byte rows: no 16-byte units
     assert q.choice(q.Q4_K, 100, 1, 1) == q.E_SHAPE
     for wtype in (q.Q2_K, q.Q3_K, q.Q5_K, q.Q6_K):  # K-quants: 256-column tiles, as Q4_K
-        assert q.choice(wtype, 4096, 14336, 4096) == q.VARIANT_WS_128x256
+        assert q.choice(wtype, 4096, 14336, 4096) == q.VARIANT_WS_256x256
         assert q.choice(wtype, 14336, 4096, 16) == q.VARIANT_SKINNY
         assert not q.variant_applies(q.VARIANT_WS_64x128, wtype, 4096, 14336, 4096)
         assert q.choice(wtype, 128, 1, 1) == q.E_SHAPE
@@ -128,6 +134,9 @@ def test_variant_applies():
     assert q.variant_applies(q.VARIANT_TILE_128x256, q.Q4_K, 4096, 14336, 4096)
     assert not q.variant_applies(q.VARIANT_TILE_128x128, q.Q4_K, 4096, 14336, 4096)
     assert q.variant_applies(q.VARIANT_WS_128x256, q.Q4_K, 4096, 14336, 4096)
+    assert q.variant_applies(q.VARIANT_WS_256x256, q.Q4_K, 4096, 14336, 4096)
+    assert q.variant_applies(q.VARIANT_WS_256x256, q.F32, 300, 76, 200)
+    assert not q.variant_applies(q.VARIANT_WS_256x256, q.F32, 300, 77, 200)  # G rows not 16-byte units
     assert q.variant_applies(q.VARIANT_WS_128x128, q.F32, 300, 76, 200)      # K % 4 == 0
     assert q.variant_applies(q.VARIANT_WS_128x128, q.F16, 300, 76, 200)
     assert not q.variant_applies(q.VARIANT_WS_128x128, q.F16, 301, 76, 200)  # K % 4 != 0

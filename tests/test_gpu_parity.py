@@ -33,7 +33,8 @@ TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, w
          wl.Q4_K, wl.Q5_K, wl.Q6_K]
 KQUANTS = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
 ALL_TILES = ["tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
-             "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128", "ws_32x256", "ws_32x128", "ws2_64x128"]
+             "ws_256x256", "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128", "ws_32x256", "ws_32x128",
+             "ws2_64x128"]
 
 
 @pytest.fixture(scope="module")
@@ -54,7 +55,7 @@ def variant_id(q, name):
 
 def tile_variants(wtype):
     if wtype in KQUANTS:
-        return ["tile_128x256", "tile_64x256", "ws_128x256", "ws_64x256", "ws_32x256"]
+        return ["tile_128x256", "tile_64x256", "ws_256x256", "ws_128x256", "ws_64x256", "ws_32x256"]
     return ALL_TILES
 
 
