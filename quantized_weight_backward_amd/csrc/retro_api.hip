@@ -145,6 +145,10 @@ int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     double best_cost = 0;
     for (const auto& v : kTiles) {
         if (!tile_applies(v, type, K, N, T, s)) continue;
+        // F32 rows spill registers in the 256 x 256 tile (their producers
+        // stage 16 bytes per element group): measured 0.99-1.04x the time of
+        // 128 x 256, where every other type gains 3-5%
+        if (v.id == RETRO_VARIANT_WS_256x256 && type == RETRO_F32) continue;
         const double weight = v.penalty * (v.ws == prefers_ws(type) ? 1.0 : kOtherFamily);
         const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk) * s.batches();
         const double cost = double(cdiv(nt, kNumCUs)) * v.bt * v.bk * weight;

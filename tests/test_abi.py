@@ -104,6 +104,9 @@ def test_choice():
     assert q.choice(q.Q4_K, 4096, 14336, 8192) == q.VARIANT_WS_256x256
     assert q.choice(q.Q4_K, 4096, 14336, 2048) == q.VARIANT_WS_128x256
     assert q.choice(q.Q4_K, 14336, 4096, 4096) == q.VARIANT_WS_128x256  # 3.5 rounds of 256 x 256
+    for wtype in (q.F16, q.BF16, q.Q8_0, q.Q4_0, q.MXFP4):
+        assert q.choice(wtype, 4096, 11008, 4096) == q.VARIANT_WS_256x256
+    assert q.choice(q.F32, 4096, 11008, 4096) == q.VARIANT_WS_128x256   # F32 rows spill there
     assert q.choice(q.Q4_0, 5120, 17408, 2048) == q.VARIANT_WS_64x128
     assert q.choice(q.Q4_0, 5120, 17407, 2048) == q.VARIANT_TILE_64x128  # N % 4 != 0: the fallback family
     for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0, q.Q4_1, q.Q5_0, q.Q5_1):
