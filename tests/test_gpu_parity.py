@@ -526,7 +526,7 @@ def test_split_full_size_sampled_rows(q, name, wtype):
 
 # --- batches over two outer dimensions, with W broadcast ------------------------------
 
-BATCHED = [(wl.Q4_K, 512, 64, 40, ["auto", "ws_64x256", "tile_64x256"]),
+BATCHED = [(wl.Q4_K, 512, 64, 40, ["auto", "ws_64x256", "ws_256x256", "tile_64x256"]),
            (wl.Q5_0, 352, 48, 12, ["auto", "skinny", "tile_64x64"]),
            (wl.BF16, 264, 40, 70, ["auto", "ws_32x128", "ws2_64x128", "tile_128x128"])]
 
