@@ -2,14 +2,18 @@
 //
 // Same contraction and tile mapping as out_prod_tile_kernel, organised so
 // that the matrix pipe never waits on staging:
-//   * 8 waves per workgroup. Waves 0-3 (consumers, CT x 4/CT over the tile) only
-//     read operands from LDS and issue v_mfma_f32_32x32x2_f32. Waves 4-7
+//   * NC + 4 waves per workgroup (NC = 4, or 8 for the 256 x 256 tile). Waves
+//     0 .. NC - 1 (consumers, a CT x NC/CT grid over the tile) only read
+//     operands from LDS and issue v_mfma_f32_32x32x2_f32. The last 4 waves
 //     (producers) load G and packed W with buffer loads, decode W in
 //     registers and write both into LDS.
 //   * G and decoded W are double-buffered in LDS: while the consumers contract
 //     chunk c from buffer c % 2, the producers fill buffer (c + 1) % 2 with
 //     chunk c + 1, whose loads they issued one chunk earlier. One workgroup
 //     barrier per 32-row chunk.
+//   * With eight consumers (12 waves, three per SIMD) every decoded weight
+//     feeds twice the matrix work of four, at the cost of one operand set per
+//     consumer in the 168-register budget (see ws_consume).
 //   * With NG = 2 the workgroup holds two such pipelines (16 waves) over the
 //     same output tile, one for the even and one for the odd chunks, sharing
 //     the barriers; their partial sums are added in LDS at the end. Each SIMD
@@ -124,7 +128,7 @@ __device__ __forceinline__ int ws_w_index(int k, int n) {
     return k * WP + (n ^ (((k >> 4) & 7) << 2));
 }
 
-// Consumer waves 0 .. 4 NG - 1 of a producer/consumer tile kernel: contract
+// Consumer waves 0 .. NC NG - 1 of a producer/consumer tile kernel: contract
 // the nloc chunks its pipeline's producers publish in LDS (shape S: BT x BK
 // outputs, chunks of 32 reduction values; G-side operand t-major with pitch
 // GP, W-side operand k-major through ws_w_index) and store the BT x BK tile
