@@ -775,7 +775,7 @@ def main() -> int:
     t_roof = max(wbytes / (PEAK_HBM_GBS * 1e9), fl_skinny / (PEAK_F32_TFLOPS * 1e12))
 
     out = {
-        "metric": "OUT_PROD TFLOP/s and weight GB/s vs roofline, Q4_K 4096x14336 T=4096 and T=16",
+        "metric": "OUT_PROD TFLOP/s and weight GB/s vs roofline, Q4_K 4096\u00d714336 T=4096 and T=16",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
