@@ -213,6 +213,9 @@ const char *retro_strerror(int code);
  *                           of four producer waves, so every decoded weight
  *                           feeds twice as many products; 144 KB of LDS, one
  *                           workgroup of 12 waves per CU
+ *   RETRO_VARIANT_WS_256x128  retro_mul_mat only: 256 rows of x by 128 rows
+ *                           of W per workgroup, eight MFMA waves (64 x 64
+ *                           each) over one set of four producer waves
  *   RETRO_VARIANT_WS2_64x128  WS_64x128 with two pipelines in one
  *                           workgroup (even and odd 32-row chunks of W,
  *                           partial sums added in LDS in that order): two
@@ -264,7 +267,8 @@ enum {
     RETRO_VARIANT_SIMPLE = 15,
     RETRO_VARIANT_SPLIT_128x256 = 16,
     RETRO_VARIANT_SPLIT_128x128 = 17,
-    RETRO_VARIANT_WS_256x256 = 18
+    RETRO_VARIANT_WS_256x256 = 18,
+    RETRO_VARIANT_WS_256x128 = 19
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the
@@ -407,8 +411,8 @@ int retro_out_prod_strided_variant_applies(int variant, int type, int64_t K, int
  *   X  T x K float32, row-major contiguous
  *   Y  T x N float32, row-major contiguous, overwritten (K = 0 writes zeros)
  * Pointers, alignment, aliasing, errors and execution as retro_out_prod.
- * Variants: RETRO_VARIANT_WS_128x128 / _64x128 / _32x128 (tiles of T x N;
- * need K % 4 == 0 for F32/F16/BF16), RETRO_VARIANT_SKINNY (T <= 16: one
+ * Variants: RETRO_VARIANT_WS_256x128 / _128x128 / _64x128 / _32x128 (tiles of
+ * T x N; need K % 4 == 0 for F32/F16/BF16), RETRO_VARIANT_SKINNY (T <= 16: one
  * workgroup per 16 rows of W over all of k; the same condition on K) and
  * RETRO_VARIANT_SIMPLE (any shape).
  */

@@ -275,15 +275,21 @@ struct MmCodec<kQ3_K> {
     }
 };
 
-template <int TYPE, int WA, int WB, int CT>
+template <int TYPE, int WA, int WB, int CT, int NC_ = 4>
 struct MmShape {
     using F = Format<TYPE>;
     static constexpr bool kDense = F::kBlock == 1;
     static constexpr int kPThreads = 256;
-    static constexpr int kThreads = 2 * kPThreads;
-    static constexpr int NC = 4;  // consumer waves
-    static_assert(CT == 1 || CT == 2, "consumer grid 1 x 4 or 2 x 2");
-    static constexpr int CK = 4 / CT;
+    // consumer waves: 4, or 8 for the 256 x 128 tile, whose producers' decode
+    // then feeds twice the matrix work
+    static constexpr int NC = NC_;
+    static constexpr int kCThreads = 64 * NC;
+    static constexpr int kThreads = kCThreads + kPThreads;
+    static_assert((NC == 4 && (CT == 1 || CT == 2)) || (NC == 8 && CT == 4), "consumer grid 1x4, 2x2 or 4x2");
+    static constexpr int CK = NC / CT;
+    // consumers keep two operand sets (the next phase read during this one's
+    // MFMAs) when the register budget allows
+    static constexpr bool kPrefetch = NC == 4 || WA * WB <= 4;
     static constexpr int BT = 32 * WA * CT;  // rows of x per tile
     static constexpr int BK = 32 * WB * CK;  // rows of W (outputs) per tile
     // workgroups per CU the register budget is set for, and the same as waves
@@ -307,9 +313,10 @@ struct MmShape {
     static constexpr int RING = SLOT_REGS <= 32 ? 4 : 2;
 };
 
-template <int TYPE, int WA, int WB, int CT>
-__global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWavesPerSimd)) void mul_mat_ws_kernel(MmArgs args) {
-    using S = MmShape<TYPE, WA, WB, CT>;
+template <int TYPE, int WA, int WB, int CT, int NC>
+__global__ __launch_bounds__((MmShape<TYPE, WA, WB, CT, NC>::kThreads),
+                             (MmShape<TYPE, WA, WB, CT, NC>::kWavesPerSimd)) void mul_mat_ws_kernel(MmArgs args) {
+    using S = MmShape<TYPE, WA, WB, CT, NC>;
     using C = MmCodec<TYPE>;
     constexpr int BT = S::BT, BK = S::BK, BN = S::BN, GP = S::GP, WP = S::WP;
 
@@ -323,9 +330,9 @@ __global__ __launch_bounds__(512, (MmShape<TYPE, WA, WB, CT>::kWavesPerSimd)) vo
     const int K = args.K, N = args.N, T = args.T;
     const int nloc = (K + BN - 1) / BN;
 
-    if (wave >= 4) {
+    if (wave >= NC) {
         // ---------------- producer ----------------
-        const int p = tid - S::kPThreads;
+        const int p = tid - S::kCThreads;
         float* const lds = lds_all;
         constexpr int R = S::RING;
         float4 gring[R][S::GSLOTS];

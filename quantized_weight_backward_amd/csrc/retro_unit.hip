@@ -167,9 +167,9 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     return launch_status();
 }
 
-template <int TYPE, int WA, int WB, int CT>
+template <int TYPE, int WA, int WB, int CT, int NC = 4>
 int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
-    using S = MmShape<TYPE, WA, WB, CT>;
+    using S = MmShape<TYPE, WA, WB, CT, NC>;
     MmArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.X = X;
@@ -185,7 +185,7 @@ int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int
     a.group = group_height(a.tiles_t, a.tiles_n, S::kResident, 4.0 * T * K, double(N) * a.pitch);
     const unsigned nt = unsigned(a.tiles_t) * unsigned(a.tiles_n);
     clear_last_error();
-    hipLaunchKernelGGL((mul_mat_ws_kernel<TYPE, WA, WB, CT>), dim3(nt), dim3(S::kThreads), 0, st, a);
+    hipLaunchKernelGGL((mul_mat_ws_kernel<TYPE, WA, WB, CT, NC>), dim3(nt), dim3(S::kThreads), 0, st, a);
     return launch_status();
 }
 
@@ -242,6 +242,7 @@ template <int TYPE>
 int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
                    hipStream_t st) {
     switch (variant) {
+        case RETRO_VARIANT_WS_256x128: return launch_mm<TYPE, 2, 2, 4, 8>(W, X, Y, K, N, T, st);
         case RETRO_VARIANT_WS_128x128: return launch_mm<TYPE, 2, 2, 2>(W, X, Y, K, N, T, st);
         case RETRO_VARIANT_WS_64x128: return launch_mm<TYPE, 1, 2, 2>(W, X, Y, K, N, T, st);
         case RETRO_VARIANT_WS_32x128: return launch_mm<TYPE, 1, 1, 1>(W, X, Y, K, N, T, st);

@@ -53,6 +53,9 @@ struct WsShape {
     // consumer waves CT x CK, each (32*WA) x (32*WB) outputs
     static_assert((NC == 4 && (CT == 1 || CT == 2)) || (NC == 8 && CT == 2), "consumer grid 1x4, 2x2 or 2x4");
     static constexpr int CK = NC / CT;
+    // consumers keep two operand sets (the next phase read during this one's
+    // MFMAs) when the register budget allows
+    static constexpr bool kPrefetch = NC == 4 || WA * WB <= 4;
     static constexpr int BT = 32 * WA * CT;
     static constexpr int BK = 32 * WB * CK;
     static constexpr int BN = 32;
@@ -182,10 +185,10 @@ __device__ __forceinline__ void ws_consume(float* lds_all, int tid, int wave, in
     // run; phase 0 of the next chunk (buffer 1 - BUF) is read right after the
     // barrier that publishes it, ahead of this chunk's last MFMAs. After the
     // last chunk that read sees a stale buffer and its values are unused.
-    // With eight consumer waves (two per SIMD) the register budget holds one
-    // operand set: each phase is read, then contracted, and the SIMD's other
-    // consumer wave covers the read latency.
-    constexpr bool kPrefetch = S::NC == 4;
+    // With eight consumer waves of 128 accumulators each (two per SIMD) the
+    // register budget holds one operand set: each phase is read, then
+    // contracted, and the SIMD's other consumer wave covers the read latency.
+    constexpr bool kPrefetch = S::kPrefetch;
     f32x4 a0[WA], b0[WB];
     f32x4 a1[kPrefetch ? WA : 1], b1[kPrefetch ? WB : 1];
     auto chunk = [&](auto buf_tag) {

@@ -42,7 +42,7 @@ OUT_PROD_VARIANTS = ["skinny", "tile_128x128", "tile_128x256", "tile_64x128", "t
                      "ws_256x256", "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128", "ws_32x256", "ws_32x128",
                      "ws2_64x128",
                      "split_128x256", "split_128x128"]
-MUL_MAT_VARIANTS = ["skinny", "ws_128x128", "ws_64x128", "ws_32x128", "simple"]
+MUL_MAT_VARIANTS = ["skinny", "ws_256x128", "ws_128x128", "ws_64x128", "ws_32x128", "simple"]
 
 # Byte offsets of the fp16 scale fields in one block (d first; then the
 # second field: dmin for the K-quants with sub-mins, the offset m for Q4_1

@@ -21,7 +21,7 @@ ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.NVFP4, wl.Q2_K, wl.Q3_K,
          wl.Q4_K, wl.Q5_K, wl.Q6_K]
-VARIANTS = ["auto", "ws_128x128", "ws_64x128", "ws_32x128", "skinny", "simple"]
+VARIANTS = ["auto", "ws_256x128", "ws_128x128", "ws_64x128", "ws_32x128", "skinny", "simple"]
 # K per type: several 32-column chunks and, for the K-quants, several
 # super-blocks; dense K not a multiple of 32 (a partial last chunk)
 K_OF = {wl.F32: 300, wl.F16: 264, wl.BF16: 520, wl.Q8_0: 416, wl.Q4_0: 352, wl.Q4_1: 192, wl.Q5_0: 416,
@@ -76,7 +76,7 @@ def test_mul_mat_matches_oracle(q, wtype, shape):
         check_close(run(q, wtype, c["W"], x, N, v), acc, ab, v)
         ran.append(v)
     dense = wtype in (wl.F32, wl.F16, wl.BF16)
-    tiled = {"ws_128x128", "ws_64x128", "ws_32x128"}
+    tiled = {"ws_256x128", "ws_128x128", "ws_64x128", "ws_32x128"}
     assert ("simple" in ran) and (tiled <= set(ran)) == (not dense or K % 4 == 0), ran
     assert ("skinny" in ran) == (T <= 16), ran
 
