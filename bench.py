@@ -487,7 +487,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=20, help="launches per workload timed after the steps (at least)")
     ap.add_argument("--min-ms", type=float, default=100.0,
                     help="each back-to-back batch covers at least this many ms of launches")
