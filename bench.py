@@ -87,11 +87,53 @@ def kernel_family(variant: str) -> str:
             "split": "out_prod_split_kernel"}.get(head, "out_prod_skinny_kernel")
 
 
+# Template arguments (WA, WB, CT, NG, NC) of the producer/consumer kernel of
+# each variant, as the launches instantiate it (G stored by rows).
+WS_ARGS = {"ws_256x256": "4, 2, 2, 1, 8", "ws_128x256": "2, 4, 2, 1, 4", "ws_64x256": "1, 4, 2, 1, 4",
+           "ws_32x256": "1, 2, 1, 1, 4", "ws_128x128": "2, 2, 2, 1, 4", "ws_64x128": "1, 2, 2, 1, 4",
+           "ws2_64x128": "1, 2, 2, 2, 4", "ws_32x128": "1, 1, 1, 1, 4"}
+
+
 def kernel_prefix(variant: str, wtype: int) -> str:
     """Start of the demangled kernel name rocprofv3 reports for a variant
-    and weight type (unique within one benchmark run: each type runs one
-    variant of each kernel family)."""
+    and weight type: the producer/consumer kernel's full template argument
+    list, so that the two launches of a plan are told apart."""
+    if variant in WS_ARGS:
+        return f"void retro::out_prod_ws_kernel<{wtype}, {WS_ARGS[variant]}, false>"
     return f"void retro::{kernel_family(variant)}<{wtype},"
+
+
+def launch_plan(q, wtype: int, K: int, N: int, T: int) -> list[tuple[str, int, int]]:
+    """The launches out_prod makes: [(variant name, first column, end column)]."""
+    v0, ks, v1 = q.plan(wtype, K, N, T)
+    parts = [(q.VARIANT_NAMES[v0], 0, ks)]
+    if ks < K:
+        parts.append((q.VARIANT_NAMES[v1], ks, K))
+    return parts
+
+
+def plan_label(parts) -> str:
+    """ws_64x128, or ws_128x256[0:4096]+ws2_64x128[4096:5120]."""
+    if len(parts) == 1:
+        return parts[0][0]
+    return "+".join(f"{v}[{a}:{b}]" for v, a, b in parts)
+
+
+def plan_tag(parts) -> str:
+    """File-name part of a plan: ws_64x128, or ws_128x256+ws2_64x128."""
+    return "+".join(v for v, _, _ in parts)
+
+
+def call_durations(trace_csv: str, prefixes: list[str], drop: int) -> tuple[list[str], list[list[float]], list[float]]:
+    """Per-launch durations of each launch of a call (one kernel per prefix,
+    distinct), and their per-call sums."""
+    names, per = [], []
+    for prefix in prefixes:
+        name, durs = steady_dispatches(trace_csv, prefix, drop)
+        names.append(name)
+        per.append(durs)
+    n = min(len(d) for d in per)
+    return names, per, [sum(d[i] for d in per) for i in range(n)]
 
 
 def read_profile_value(tag: str, key: str):
@@ -246,22 +288,30 @@ def summarize(run_dir: str) -> None:
     for workload, dense in WORKLOADS:
         c = wl.WORKLOADS[workload]
         wtype = TYPE_IDS[dense] if dense else c["type"]
-        variant = q.VARIANT_NAMES[q.choice(wtype, c["K"], c["N"], c["T"])]
-        prefix = kernel_prefix(variant, wtype)
-        tag = f"{variant}_{workload_tag(workload, dense)}"
-        name, durs = steady_dispatches(trace_csv, prefix, PROFILE_WARMUP)
+        parts = launch_plan(q, wtype, c["K"], c["N"], c["T"])
+        prefixes = [kernel_prefix(v, wtype) for v, _, _ in parts]
+        variant = plan_label(parts)
+        tag = f"{plan_tag(parts)}_{workload_tag(workload, dense)}"
+        names, per, durs = call_durations(trace_csv, prefixes, PROFILE_WARMUP)
         flops = 2.0 * c["T"] * c["N"] * c["K"]
         # the two step kernels: their first PROFILE_STEPS launches after the
         # warm-up are the timed step loop, the bench's own figure
         steps = PROFILE_STEPS if workload in (LARGE, SKINNY) else 0
         head = durs[:steps] if steps else durs
         mean_s = sum(head) / len(head) / 1e9
+        part_rows = []
+        if len(parts) > 1:
+            for (v, a, b), n, d in zip(parts, names, per):
+                part_rows += [f"Launch over dst columns [{a}, {b}) ({v}):", "", *_stats_row(n, d)]
+            part_rows += ["Per call (the two launches summed):", ""]
         lines = [f"# {tag}: rocprofv3 kernel trace", "",
                  f"Command (repository root): `{profile_command('trace', run_dir)}`", "",
-                 f"Workload {workload_tag(workload, dense)}, the kernel retro_out_prod chooses ({variant}). "
-                 f"The first {PROFILE_WARMUP} launches of the kernel (the benchmark's warm-up steps) are left out"
+                 f"Workload {workload_tag(workload, dense)}, the launches retro_out_prod makes ({variant}). "
+                 f"The first {PROFILE_WARMUP} launches of each kernel (the benchmark's warm-up) are left out"
                  + (f"; the next {steps} are the timed step loop." if steps else "."), "",
-                 *_stats_row(name, durs, steps),
+                 *part_rows,
+                 *(_stats_row(names[0], durs, steps) if len(parts) == 1 else
+                   _stats_row(" + ".join(names), durs, steps)),
                  "Figures below at the mean of the " + ("timed steps." if steps else "launches after warm-up."), "",
                  f"F32 TFLOP/s at the mean: {flops / mean_s / 1e12:.2f} "
                  f"(2*T*N*K = {flops:.6g}); fraction of the 157.3 TFLOP/s F32 peak: "
@@ -274,23 +324,28 @@ def summarize(run_dir: str) -> None:
                       f"{t_roof / mean_s:.4f}", ""]
         lines += [f"kernel source_sha256: {src}", ""]
         open(os.path.join(PROFILES, f"{tag}_trace.md"), "w").write("\n".join(lines))
-        fetch = _counter_means(fetch_csv, prefix)["FETCH_SIZE"]
-        write = _counter_means(write_csv, prefix)["WRITE_SIZE"]
+        # per call: the launches' per-dispatch means added
+        fetch = [sum(_counter_means(fetch_csv, p)["FETCH_SIZE"][0] for p in prefixes),
+                 min(_counter_means(fetch_csv, p)["FETCH_SIZE"][1] for p in prefixes)]
+        write = [sum(_counter_means(write_csv, p)["WRITE_SIZE"][0] for p in prefixes),
+                 min(_counter_means(write_csv, p)["WRITE_SIZE"][1] for p in prefixes)]
         hbm = fetch[0] * 1024 * f_scale + write[0] * 1024 * w_scale
-        lines = [f"# {tag}: HBM traffic per launch (rocprofv3 counters)", "",
+        lines = [f"# {tag}: HBM traffic per call (rocprofv3 counters)", "",
                  "Commands (repository root):", "",
                  *[f"- `{profile_command(k, run_dir)}`" for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE",
                                                            "copy_WRITE_SIZE")], "",
                  "Calibration: a 1 GiB device-to-device copy reads and writes 1073741824 bytes; the counters "
                  f"read FETCH_SIZE = {f_copy:.1f} KiB and WRITE_SIZE = {w_copy:.1f} KiB per copy launch, so "
                  f"FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}.", "",
-                 "| counter | KiB per launch (mean) | launches | scaled bytes |", "|---|---|---|---|",
+                 *([f"The call makes {len(parts)} launches ({variant}); each counter is the sum of their "
+                     "per-dispatch means.", ""] if len(parts) > 1 else []),
+                 "| counter | KiB per call (mean) | calls | scaled bytes |", "|---|---|---|---|",
                  f"| FETCH_SIZE | {fetch[0]:.1f} | {fetch[1]} | {fetch[0] * 1024 * f_scale:.4g} |",
                  f"| WRITE_SIZE | {write[0]:.1f} | {write[1]} | {write[0] * 1024 * w_scale:.4g} |", "",
                  f"hbm_bytes_per_launch: {hbm:.6g}",
                  f"source_sha256: {src}", ""]
         open(os.path.join(PROFILES, f"{tag}_traffic.md"), "w").write("\n".join(lines))
-        write_counter_summary(tag, prefix, c, run_dir, src)
+        write_counter_summary(tag, prefixes, c, run_dir, src)
         print(f"{tag}: mean {sum(durs) / len(durs) / 1e3:.2f} us over {len(durs)}, traffic {hbm / 1e6:.1f} MB")
     # the opt-in exact split, timed after the step loop on the large workload
     c = wl.WORKLOADS[LARGE]
@@ -318,7 +373,7 @@ def summarize(run_dir: str) -> None:
              f"| WRITE_SIZE | {write[0]:.1f} | {write[1]} | {write[0] * 1024 * w_scale:.4g} |", "",
              f"hbm_bytes_per_launch: {hbm:.6g}", f"source_sha256: {src}", ""]
     open(os.path.join(PROFILES, f"{tag}_traffic.md"), "w").write("\n".join(lines))
-    write_counter_summary(tag, prefix, c, run_dir, src)
+    write_counter_summary(tag, [prefix], c, run_dir, src)
     print(f"{tag}: mean {sum(durs) / len(durs) / 1e3:.2f} us, traffic {hbm / 1e6:.1f} MB")
     for tag, (workload, dense, op, variant, prefix) in CASE_TRACES.items():
         path = _find_csv(run_dir, f"trace_{tag}", "kernel_trace.csv")
@@ -334,21 +389,26 @@ def summarize(run_dir: str) -> None:
         print(f"{tag}: mean {sum(durs) / len(durs) / 1e3:.2f} us")
 
 
-def write_counter_summary(tag: str, prefix: str, case: dict, run_dir: str, src: str) -> None:
-    """profiles/<tag>_counters.md: per-launch means of the counter passes,
-    with the F32 MFMA work checked against 2*T*N*K (one MOP = 512 FLOPs)."""
+def write_counter_summary(tag: str, prefixes: list[str], case: dict, run_dir: str, src: str) -> None:
+    """profiles/<tag>_counters.md: per-call means of the counter passes (the
+    per-dispatch means of a call's launches added), with the F32 MFMA work
+    checked against 2*T*N*K (one MOP = 512 FLOPs)."""
     mean, commands = {}, []
     for p in COUNTER_PASSES:
         path = _find_csv(run_dir, f"pmc_{p}", "counter_collection.csv")
         if path:
-            mean.update({k: v[0] for k, v in _counter_means(path, prefix).items()})
+            for prefix in prefixes:
+                for k, v in _counter_means(path, prefix).items():
+                    mean[k] = mean.get(k, 0.0) + v[0]
             commands.append(profile_command(p, run_dir))
     if not mean:
         return
     flops = 2.0 * case["T"] * case["N"] * case["K"]
-    lines = [f"# {tag}: counters per launch (rocprofv3)", "", "Commands (repository root), one pass each:", "",
+    lines = [f"# {tag}: counters per call (rocprofv3)", "", "Commands (repository root), one pass each:", "",
              *[f"- `{c}`" for c in commands], "",
-             "| counter | mean per launch |", "|---|---|",
+             *([f"The call makes {len(prefixes)} launches; each counter is the sum of their per-dispatch means.", ""]
+               if len(prefixes) > 1 else []),
+             "| counter | mean per call |", "|---|---|",
              *[f"| {k} | {v:.6g} |" for k, v in sorted(mean.items())], ""]
     mops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_F32")
     if mops:
@@ -657,7 +717,8 @@ def main() -> int:
             G = torch.from_numpy(c["G"]).to(dev)
             D = torch.empty((c["T"], c["K"]), dtype=torch.float32, device=dev)
         wtype, K, N, T = c["type"], c["K"], c["N"], c["T"]
-        variant = q.VARIANT_NAMES[q.choice(wtype, K, N, T)]
+        parts = launch_plan(q, wtype, K, N, T)
+        variant = plan_label(parts)
         call = lambda i: q.out_prod(wtype, W_list[i % len(W_list)], G, K, out=D)  # noqa: E731
         for i in range(5):
             call(i)
@@ -679,10 +740,10 @@ def main() -> int:
         flops = 2.0 * T * N * K
         wb = float(c["W"].nbytes)
         t_roof = max(wb / (PEAK_HBM_GBS * 1e9), flops / (PEAK_F32_TFLOPS * 1e12))
-        tag = f"{variant}_{workload_tag(workload, dense)}"
+        tag = f"{plan_tag(parts)}_{workload_tag(workload, dense)}"
         per_workload.append({
             "workload": workload_tag(workload, dense), "weight_type": wl.TYPE_NAMES[wtype], "kernel": variant,
-            "launches": reps, "avg_launch_us": round(sec * 1e6, 3),
+            "launches": reps, "launches_per_call": len(parts), "avg_launch_us": round(sec * 1e6, 3),
             "event_pairs": {"launches": npairs, "median_us": round(float(np.median(pairs)) * 1e6, 3),
                             "min_us": round(float(pairs.min()) * 1e6, 3)},
             "tflops": round(flops / sec / 1e12, 3),

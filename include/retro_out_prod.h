@@ -192,7 +192,8 @@ const char *retro_strerror(int code);
 
 /*
  * Kernel variants (for tests and benchmarks; retro_out_prod chooses one):
- *   RETRO_VARIANT_AUTO      what retro_out_prod runs
+ *   RETRO_VARIANT_AUTO      what retro_out_prod runs (one variant, or two over
+ *                           column ranges of dst: retro_out_prod_plan)
  *   RETRO_VARIANT_SKINNY    one pass over W, all of n per workgroup; T <= 16
  *   RETRO_VARIANT_TILE_*    tiled F32-MFMA kernel, tile = rows of T x columns
  *                           of K per workgroup (256-column tiles need K tiles
@@ -387,9 +388,46 @@ int retro_out_prod_views_choice(int type, int64_t K, int64_t N, int64_t T, int64
                                 int64_t ldd, int64_t ne2, int64_t ne3);
 
 /* The variant retro_out_prod would run for this type and shape, or a
- * negative error code (as retro_out_prod_supported would refuse). Touches no
- * device. */
+ * negative error code (as retro_out_prod_supported would refuse). When its
+ * plan has two launches (retro_out_prod_plan) this is the first one's. Touches
+ * no device. The views form above does the same for retro_out_prod_views. */
 int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T);
+
+/* The launches retro_out_prod makes for this type and shape (contiguous
+ * operands): returns 1 (one launch of *variant0 over all of dst; *k_split = K,
+ * *variant1 = 0) or 2 (*variant0 over dst columns [0, *k_split), then
+ * *variant1 over [*k_split, K)), or a negative error code (the three
+ * pointers NULL: RETRO_E_NULL). Touches no device.
+ * Two launches are planned when the tiles of one variant would leave the
+ * last round over the 256 CUs partly empty and a larger tile fills whole
+ * rounds on a leading column range (e.g. Q4_0, K = 5120, T = 2048: 128 x 256
+ * tiles over 4096 columns, two-pipeline 64 x 128 over the other 1024). The
+ * same rule applies to the strided, batched and views entry points. Each
+ * launch computes its columns of the OUT_PROD of llama.cpp PR #3 ("cuda:
+ * out_prod accepts a quantized src0", section "What") completely, so the
+ * result is that of its variants on their columns. */
+int retro_out_prod_plan(int type, int64_t K, int64_t N, int64_t T, int32_t *variant0, int64_t *k_split,
+                        int32_t *variant1);
+
+/* The launches retro_out_prod_views makes for ne2 x ne3 matrices of this
+ * type, shape and strides (the W batch counts do not enter), as
+ * retro_out_prod_plan. Touches no device. */
+int retro_out_prod_views_plan(int type, int64_t K, int64_t N, int64_t T, int64_t ldw, int64_t sgt, int64_t sgn,
+                              int64_t ldd, int64_t ne2, int64_t ne3, int32_t *variant0, int64_t *k_split,
+                              int32_t *variant1);
+
+/* retro_out_prod as two launches on `stream`: variant0 over dst columns
+ * [0, k_split) (W's bytes before column k_split), then variant1 over
+ * [k_split, K), for contiguous operands. Either variant may be
+ * RETRO_VARIANT_AUTO (the choice for its part alone). 0 < k_split < K and a
+ * whole number of blocks (RETRO_E_SHAPE otherwise); the W bytes before it a
+ * multiple of 16 and k_split % 4 == 0 (RETRO_E_ALIGN otherwise), so that the
+ * second part keeps the alignment of the whole; RETRO_E_VARIANT when a
+ * variant does not apply to its part. Every check is made before either
+ * launch. Pointers, aliasing, errors and execution as retro_out_prod. For
+ * tests and benchmarks of the plans above. */
+int retro_out_prod_column_split(int variant0, int64_t k_split, int variant1, int type, const void *W,
+                                const float *G, float *dst, int64_t K, int64_t N, int64_t T, void *stream);
 
 /* 1 if retro_out_prod_variant(variant, type, ..., K, N, T) with valid buffers
  * would run, 0 otherwise. Touches no device. */

@@ -70,7 +70,8 @@ EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided",
            "retro_dequantize", "retro_out_prod_supported", "retro_out_prod_choice", "retro_out_prod_variant_applies",
            "retro_out_prod_strided_variant_applies", "retro_out_prod_batched", "retro_out_prod_batched_variant",
            "retro_out_prod_views", "retro_out_prod_views_variant", "retro_out_prod_views_variant_applies",
-           "retro_out_prod_views_choice",
+           "retro_out_prod_views_choice", "retro_out_prod_plan", "retro_out_prod_views_plan",
+           "retro_out_prod_column_split",
            "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
            "retro_row_bytes", "retro_strerror",
            "retro_probe_sink_floats", "retro_probe_mfma", "retro_probe_mfma_valu", "retro_probe_copy")
@@ -126,6 +127,15 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod_supported.argtypes = [i32, i64, i64, i64]
     lib.retro_out_prod_choice.restype = i32
     lib.retro_out_prod_choice.argtypes = [i32, i64, i64, i64]
+    lib.retro_out_prod_plan.restype = i32
+    lib.retro_out_prod_plan.argtypes = [i32, i64, i64, i64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(i64),
+                                        ctypes.POINTER(ctypes.c_int32)]
+    lib.retro_out_prod_views_plan.restype = i32
+    lib.retro_out_prod_views_plan.argtypes = [i32, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                              ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(i64),
+                                              ctypes.POINTER(ctypes.c_int32)]
+    lib.retro_out_prod_column_split.restype = i32
+    lib.retro_out_prod_column_split.argtypes = [i32, i64, i32, i32, vp, vp, vp, i64, i64, i64, vp]
     lib.retro_out_prod_variant_applies.restype = i32
     lib.retro_out_prod_variant_applies.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_row_bytes.restype = i64
@@ -166,6 +176,36 @@ def supported(wtype: int, K: int, N: int, T: int) -> bool:
 
 def choice(wtype: int, K: int, N: int, T: int) -> int:
     return int(lib.retro_out_prod_choice(int(wtype), int(K), int(N), int(T)))
+
+
+def plan(wtype: int, K: int, N: int, T: int) -> tuple[int, int, int]:
+    """The launches out_prod makes: (variant0, k_split, variant1), variant0
+    over dst columns [0, k_split) and variant1 (0 when k_split == K: one
+    launch) over the rest."""
+    v0, v1, ks = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
+    n = lib.retro_out_prod_plan(int(wtype), int(K), int(N), int(T), ctypes.byref(v0), ctypes.byref(ks),
+                                ctypes.byref(v1))
+    _check(OK if n > 0 else n)
+    return int(v0.value), int(ks.value), int(v1.value)
+
+
+def views_plan(wtype: int, K: int, N: int, T: int, ldw: int, sgt: int, sgn: int, ldd: int, ne2: int = 1,
+               ne3: int = 1) -> tuple[int, int, int]:
+    """The launches out_prod_batched makes for ne2 x ne3 matrices with these
+    strides, as plan()."""
+    v0, v1, ks = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
+    n = lib.retro_out_prod_views_plan(int(wtype), int(K), int(N), int(T), int(ldw), int(sgt), int(sgn), int(ldd),
+                                      int(ne2), int(ne3), ctypes.byref(v0), ctypes.byref(ks), ctypes.byref(v1))
+    _check(OK if n > 0 else n)
+    return int(v0.value), int(ks.value), int(v1.value)
+
+
+def plan_names(wtype: int, K: int, N: int, T: int) -> str:
+    """The plan as text: 'ws_64x128', or 'ws_128x256[0:4096]+ws2_64x128[4096:5120]'."""
+    v0, ks, v1 = plan(wtype, K, N, T)
+    if ks >= K:
+        return VARIANT_NAMES[v0]
+    return f"{VARIANT_NAMES[v0]}[0:{ks}]+{VARIANT_NAMES[v1]}[{ks}:{K}]"
 
 
 def variant_applies(variant: int, wtype: int, K: int, N: int, T: int) -> bool:
@@ -248,6 +288,31 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
                                                 _stream_handle(stream)))
     return out
 
+
+
+def out_prod_column_split(wtype: int, W, G, K: int, variant0: int, k_split: int, variant1: int, out=None,
+                          stream=None):
+    """out_prod as two launches: variant0 over dst columns [0, k_split),
+    variant1 over [k_split, K) (contiguous W, G and out)."""
+    _device_tensor(W, "W")
+    _device_tensor(G, "G")
+    if G.dtype != torch.float32 or G.dim() != 2:
+        raise ValueError("G must be a contiguous 2-D float32 tensor (T x N)")
+    T, N = G.shape
+    rb = row_bytes(wtype, K)
+    if rb < 0:
+        _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
+    if W.numel() * W.element_size() != N * rb:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.float32, device=G.device)
+    else:
+        _device_tensor(out, "out")
+        if out.dtype != torch.float32 or tuple(out.shape) != (T, K):
+            raise ValueError("out must be a contiguous float32 T x K tensor")
+    _check(lib.retro_out_prod_column_split(int(variant0), int(k_split), int(variant1), int(wtype), _ptr(W), _ptr(G),
+                                           _ptr(out), int(K), int(N), int(T), _stream_handle(stream)))
+    return out
 
 def _as4(t):
     while t.dim() < 4:

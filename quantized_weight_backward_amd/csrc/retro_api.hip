@@ -137,35 +137,116 @@ bool skinny_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s)
            16 * s.ldg * 4 < (int64_t(1) << 31);
 }
 
-// Pick the tile that minimises (tiles per CU, rounded up) x tile area x
-// relative cost: the rounding is the wave quantisation over 256 CUs.
-int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    if (skinny_applies(type, K, N, T, s)) return RETRO_VARIANT_SKINNY;
-    int best = -1;
-    double best_cost = 0;
+// Whether the automatic choice may take tile v for this type. F32 rows spill
+// registers in the 256 x 256 tile (their producers stage 16 bytes per
+// element group): measured 0.99-1.04x the time of 128 x 256, where every
+// other type gains 3-5%.
+bool auto_takes(const TileVariant& v, int type) {
+    return !(v.id == RETRO_VARIANT_WS_256x256 && type == RETRO_F32);
+}
+
+// Estimated cost of covering dst with tile v: (tiles per CU, rounded up) x
+// tile area x relative cost. The rounding is the wave quantisation over 256
+// CUs.
+double tile_cost(const TileVariant& v, int type, int64_t K, int64_t T, const Strides& s) {
+    const double weight = v.penalty * (v.ws == prefers_ws(type) ? 1.0 : kOtherFamily);
+    const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk) * s.batches();
+    return double(cdiv(nt, kNumCUs)) * v.bt * v.bk * weight;
+}
+
+struct Choice {
+    int id;       // variant, or RETRO_E_SHAPE when no tile applies
+    double cost;  // tile_cost of the tile it was chosen by
+};
+
+// The tiled kernel of least cost (T > 16).
+Choice choose_tile(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    Choice best{-1, 0.0};
     for (const auto& v : kTiles) {
-        if (!tile_applies(v, type, K, N, T, s)) continue;
-        // F32 rows spill registers in the 256 x 256 tile (their producers
-        // stage 16 bytes per element group): measured 0.99-1.04x the time of
-        // 128 x 256, where every other type gains 3-5%
-        if (v.id == RETRO_VARIANT_WS_256x256 && type == RETRO_F32) continue;
-        const double weight = v.penalty * (v.ws == prefers_ws(type) ? 1.0 : kOtherFamily);
-        const int64_t nt = cdiv(T, v.bt) * cdiv(K, v.bk) * s.batches();
-        const double cost = double(cdiv(nt, kNumCUs)) * v.bt * v.bk * weight;
-        if (best < 0 || cost < best_cost) {
-            best = v.id;
-            best_cost = cost;
-        }
+        if (!tile_applies(v, type, K, N, T, s) || !auto_takes(v, type)) continue;
+        const double cost = tile_cost(v, type, K, T, s);
+        if (best.id < 0 || cost < best.cost) best = {v.id, cost};
     }
     // 64 x 128 tiles in two pipelines per workgroup beat one pipeline per
     // workgroup when a CU gets at most one tile (one pipeline then leaves a
     // single MFMA wave per SIMD), and for F32 rows at any tile count
     // (measured: 0.64-0.70 vs 0.58-0.65 of the F32 peak at one tile per CU;
     // 0.75 vs 0.71 for F32 with several).
-    if (best == RETRO_VARIANT_WS_64x128 &&
+    if (best.id == RETRO_VARIANT_WS_64x128 &&
         (type == RETRO_F32 || cdiv(T, 64) * cdiv(K, 128) * s.batches() <= kNumCUs))
-        best = RETRO_VARIANT_WS2_64x128;
-    return best < 0 ? RETRO_E_SHAPE : best;
+        best.id = RETRO_VARIANT_WS2_64x128;
+    if (best.id < 0) best.id = RETRO_E_SHAPE;
+    return best;
+}
+
+// The kernel one launch over all of dst would use.
+int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    if (skinny_applies(type, K, N, T, s)) return RETRO_VARIANT_SKINNY;
+    return choose_tile(type, K, N, T, s).id;
+}
+
+// A launch plan: variant v0 over dst columns [0, k_split), then, when
+// k_split < K, variant v1 over columns [k_split, K).
+struct Plan {
+    int v0;
+    int64_t k_split;
+    int v1;
+};
+
+// Byte offset of column k within a W row (k a whole number of blocks).
+int64_t column_offset(int type, int64_t k) {
+    Geometry g;
+    return geometry(type, g) ? k / g.block * g.bytes : 0;
+}
+
+// A column split must start the second part on a whole block whose bytes,
+// and whose dst column, keep the 16-byte alignment of the whole call.
+bool split_point_ok(int type, int64_t k) {
+    Geometry g;
+    return geometry(type, g) && k % g.block == 0 && column_offset(type, k) % 16 == 0 && k % 4 == 0;
+}
+
+// Wave quantisation can leave the last round of tiles partly empty: Q4_0
+// 17408 x 5120 at T = 2048 takes 1280 tiles of 64 x 128 (5 rounds of a
+// small tile) or 320 of 128 x 256 (1.25 rounds). Two launches over disjoint
+// column ranges of dst can do better: a larger tile over the columns whose
+// tiles fill whole rounds, and the best tile over the rest (measured there:
+// 128 x 256 over 4096 columns in 2.17 ms plus two-pipeline 64 x 128 over
+// 1024 in 0.62 ms, against 2.99 ms for one launch). The plan is taken when
+// its estimated cost is at least 1% lower and saves at least ~5 us of
+// matrix time, which pays for the second launch.
+constexpr double kPlanMargin = 0.99;
+constexpr double kCuFlops = 157.3e12 / kNumCUs * 0.8;  // F32 FLOP/s of one CU at a typical tile efficiency
+constexpr double kPlanMinSaving = 5e-6;                // seconds
+
+Plan plan_for(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    const int single = choose(type, K, N, T, s);
+    Plan best{single, K, 0};
+    if (single <= 0 || single == RETRO_VARIANT_SKINNY || N == 0) return best;
+    const double one = choose_tile(type, K, N, T, s).cost;
+    double best_cost = one;
+    for (const auto& v : kTiles) {
+        // the two-pipeline tile is taken only through choose_tile's rule
+        if (!v.ws || v.id == RETRO_VARIANT_WS2_64x128 || !auto_takes(v, type)) continue;
+        if (!tile_applies(v, type, K, N, T, s)) continue;
+        const int64_t tiles_t = cdiv(T, v.bt) * s.batches();
+        for (int64_t c = 1; c * v.bk < K; ++c) {
+            if ((tiles_t * c) % kNumCUs != 0) continue;  // whole rounds only
+            const int64_t k1 = c * v.bk;
+            if (!split_point_ok(type, k1)) continue;
+            const Choice tail = choose_tile(type, K - k1, N, T, s);
+            if (tail.id < 0) continue;
+            const double cost = tile_cost(v, type, k1, T, s) + tail.cost;
+            if (cost < best_cost) {
+                best = {v.id, k1, tail.id};
+                best_cost = cost;
+            }
+        }
+    }
+    if (best.k_split < K &&
+        (best_cost > kPlanMargin * one || (one - best_cost) * 2.0 * double(N) / kCuFlops < kPlanMinSaving))
+        return {single, K, 0};
+    return best;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -216,13 +297,17 @@ bool g_layout(int64_t sgt, int64_t sgn, Strides& s) {
     return false;
 }
 
-int out_prod_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
-                  int64_t T, const Strides& s, void* stream) {
+// Validation shared by the out_prod entry points: shape, strides, then (for
+// a non-empty call) pointers, alignment and aliasing. `empty` is set when
+// there is nothing to compute.
+int check_call(int type, const void* W, const float* G, const float* dst, int64_t K, int64_t N, int64_t T,
+               const Strides& s, bool& empty) {
     int rc = check_shape(type, K, N, T);
     if (rc != RETRO_OK) return rc;
     rc = check_strides(type, K, N, T, s);
     if (rc != RETRO_OK) return rc;
-    if (T == 0 || K == 0 || s.batches() == 0) return RETRO_OK;
+    empty = T == 0 || K == 0 || s.batches() == 0;
+    if (empty) return RETRO_OK;
     // bytes each operand spans: one matrix, then all batches
     const int64_t w_bytes = N > 0 ? (N - 1) * s.ldw + row_bytes_of(type, K) : 0;
     const int64_t g_bytes = N > 0 ? (s.gcols ? (N - 1) * s.ldg + T : (T - 1) * s.ldg + N) * 4 : 0;
@@ -237,13 +322,12 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
     // batch i3 after the whole of i3 - 1
     if ((s.ne2 > 1 && s.sd2 * 4 < d_bytes) || (s.ne3 > 1 && s.sd3 * 4 < (s.ne2 - 1) * s.sd2 * 4 + d_bytes))
         return RETRO_E_ALIAS;
-    if (variant == RETRO_VARIANT_AUTO) {
-        variant = choose(type, K, N, T, s);
-        if (variant < 0) return variant;
-    } else if (!variant_applies(variant, type, K, N, T, s)) {
-        return RETRO_E_VARIANT;
-    }
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    return RETRO_OK;
+}
+
+// One launch of `variant` (already checked to apply) over the call as given.
+int launch_typed(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                 const Strides& s, hipStream_t st) {
     switch (type) {
         case RETRO_F32: return launch_out_prod<RETRO_F32>(variant, W, G, dst, K, N, T, s, st);
         case RETRO_F16: return launch_out_prod<RETRO_F16>(variant, W, G, dst, K, N, T, s, st);
@@ -262,6 +346,33 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
         case RETRO_Q6_K: return launch_out_prod<RETRO_Q6_K>(variant, W, G, dst, K, N, T, s, st);
         default: return RETRO_E_TYPE;
     }
+}
+
+// The launches of a plan: the columns [0, k_split) of W and dst, then the
+// rest. Each part reads all of G and writes only its own columns of dst.
+int run_plan(const Plan& p, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+             const Strides& s, hipStream_t st) {
+    int rc = launch_typed(p.v0, type, W, G, dst, p.k_split, N, T, s, st);
+    if (rc != RETRO_OK || p.k_split >= K) return rc;
+    // with N = 0 there is no W to offset (it may be null, and is never read)
+    const void* W1 = N > 0 ? static_cast<const void*>(static_cast<const char*>(W) + column_offset(type, p.k_split))
+                           : W;
+    return launch_typed(p.v1, type, W1, G, dst + p.k_split, K - p.k_split, N, T, s, st);
+}
+
+int out_prod_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
+                  int64_t T, const Strides& s, void* stream) {
+    bool empty = false;
+    const int rc = check_call(type, W, G, dst, K, N, T, s, empty);
+    if (rc != RETRO_OK || empty) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (variant == RETRO_VARIANT_AUTO) {
+        const Plan p = plan_for(type, K, N, T, s);
+        if (p.v0 < 0) return p.v0;
+        return run_plan(p, type, W, G, dst, K, N, T, s, st);
+    }
+    if (!variant_applies(variant, type, K, N, T, s)) return RETRO_E_VARIANT;
+    return launch_typed(variant, type, W, G, dst, K, N, T, s, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -513,13 +624,66 @@ int retro_out_prod_views_choice(int type, int64_t K, int64_t N, int64_t T, int64
     s.ne2 = ne2;
     s.ne3 = ne3;
     rc = check_strides(type, K, N, T, s);
-    return rc != RETRO_OK ? rc : choose(type, K, N, T, s);
+    return rc != RETRO_OK ? rc : plan_for(type, K, N, T, s).v0;
 }
 
 int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T) {
     const int rc = check_shape(type, K, N, T);
     if (rc != RETRO_OK) return rc;
-    return choose(type, K, N, T, contiguous(type, K, N));
+    return plan_for(type, K, N, T, contiguous(type, K, N)).v0;
+}
+
+int retro_out_prod_plan(int type, int64_t K, int64_t N, int64_t T, int32_t* variant0, int64_t* k_split,
+                        int32_t* variant1) {
+    const int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    if (!variant0 || !k_split || !variant1) return RETRO_E_NULL;
+    const Plan p = plan_for(type, K, N, T, contiguous(type, K, N));
+    if (p.v0 < 0) return p.v0;
+    *variant0 = p.v0;
+    *k_split = p.k_split;
+    *variant1 = p.k_split < K ? p.v1 : 0;
+    return p.k_split < K ? 2 : 1;
+}
+
+int retro_out_prod_views_plan(int type, int64_t K, int64_t N, int64_t T, int64_t ldw, int64_t sgt, int64_t sgn,
+                              int64_t ldd, int64_t ne2, int64_t ne3, int32_t* variant0, int64_t* k_split,
+                              int32_t* variant1) {
+    int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    if (!variant0 || !k_split || !variant1) return RETRO_E_NULL;
+    Strides s{ldw, 0, ldd};
+    if (!g_layout(sgt, sgn, s)) return RETRO_E_SHAPE;
+    s.ne2 = ne2;
+    s.ne3 = ne3;
+    rc = check_strides(type, K, N, T, s);
+    if (rc != RETRO_OK) return rc;
+    const Plan p = plan_for(type, K, N, T, s);
+    if (p.v0 < 0) return p.v0;
+    *variant0 = p.v0;
+    *k_split = p.k_split;
+    *variant1 = p.k_split < K ? p.v1 : 0;
+    return p.k_split < K ? 2 : 1;
+}
+
+int retro_out_prod_column_split(int variant0, int64_t k_split, int variant1, int type, const void* W,
+                                const float* G, float* dst, int64_t K, int64_t N, int64_t T, void* stream) {
+    const Strides s = contiguous(type, K, N);
+    bool empty = false;
+    const int rc = check_call(type, W, G, dst, K, N, T, s, empty);
+    if (rc != RETRO_OK) return rc;
+    Geometry g;
+    geometry(type, g);  // known: check_call accepted the type
+    if (k_split <= 0 || k_split >= K || k_split % g.block) return RETRO_E_SHAPE;
+    if (!split_point_ok(type, k_split)) return RETRO_E_ALIGN;
+    Plan p{variant0, k_split, variant1};
+    if (p.v0 == RETRO_VARIANT_AUTO) p.v0 = choose(type, k_split, N, T, s);
+    if (p.v1 == RETRO_VARIANT_AUTO) p.v1 = choose(type, K - k_split, N, T, s);
+    if (p.v0 <= 0 || p.v1 <= 0 || !variant_applies(p.v0, type, k_split, N, T, s) ||
+        !variant_applies(p.v1, type, K - k_split, N, T, s))
+        return RETRO_E_VARIANT;
+    if (empty) return RETRO_OK;
+    return run_plan(p, type, W, G, dst, K, N, T, s, static_cast<hipStream_t>(stream));
 }
 
 int64_t retro_row_bytes(int type, int64_t K) { return row_bytes_of(type, K); }

@@ -2,7 +2,9 @@
 declares, and every validation path returns its error before touching a
 device."""
 
+import ctypes
 import glob
+import itertools
 import os
 import re
 
@@ -14,6 +16,7 @@ from conftest import REPO
 q = pytest.importorskip("quantized_weight_backward_amd")  # raises if the library is missing
 
 HEADER = os.path.join(REPO, "include", "retro_out_prod.h")
+KQUANT_TYPES = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
 HEADERS = sorted(glob.glob(os.path.join(REPO, "include", "*.h")))
 
 
@@ -107,12 +110,13 @@ def test_choice():
     for wtype in (q.F16, q.BF16, q.Q8_0, q.Q4_0, q.MXFP4):
         assert q.choice(wtype, 4096, 11008, 4096) == q.VARIANT_WS_256x256
     assert q.choice(q.F32, 4096, 11008, 4096) == q.VARIANT_WS_128x256   # F32 rows spill there
-    assert q.choice(q.Q4_0, 5120, 17408, 2048) == q.VARIANT_WS_64x128
+    # Q4_0 17408 x 5120 at T = 2048: two launches (test_plan), the first 128 x 256
+    assert q.choice(q.Q4_0, 5120, 17408, 2048) == q.VARIANT_WS_128x256
     assert q.choice(q.Q4_0, 5120, 17407, 2048) == q.VARIANT_TILE_64x128  # N % 4 != 0: the fallback family
     for wtype in (q.F32, q.F16, q.BF16, q.Q8_0, q.Q4_0, q.Q4_1, q.Q5_0, q.Q5_1):
         assert q.choice(wtype, 4096, 4096, 512) in q.VARIANT_NAMES
     for wtype in (q.Q4_1, q.Q5_0, q.Q5_1, q.MXFP4):  # the 32-element blocks, as Q4_0
-        assert q.choice(wtype, 5120, 17408, 2048) == q.VARIANT_WS_64x128
+        assert q.choice(wtype, 5120, 17408, 2048) == q.VARIANT_WS_128x256
         assert q.choice(wtype, 5120, 4096, 16) == q.VARIANT_SKINNY
         assert q.choice(wtype, 48, 1, 1) == q.E_SHAPE
     for wtype in (q.F32, q.F16, q.BF16):  # dense rows go to the producer/consumer kernel
@@ -120,7 +124,7 @@ def test_choice():
     # one 64 x 128 tile per CU (or F32 rows): two pipelines per workgroup
     for wtype in (q.F32, q.F16, q.BF16, q.Q4_0, q.Q8_0):
         assert q.choice(wtype, 4096, 4096, 512) == q.VARIANT_WS2_64x128
-    assert q.choice(q.F32, 5120, 17408, 2048) == q.VARIANT_WS2_64x128
+    assert q.choice(q.F32, 5120, 64, 2048) == q.VARIANT_WS2_64x128  # short reduction: one launch
     assert q.choice(q.F16, 301, 77, 200) == q.VARIANT_TILE_64x64  # 602-byte rows: no 16-byte units
     assert q.choice(q.Q4_K, 100, 1, 1) == q.E_SHAPE
     for wtype in (q.Q2_K, q.Q3_K, q.Q5_K, q.Q6_K):  # K-quants: 256-column tiles, as Q4_K
@@ -129,6 +133,107 @@ def test_choice():
         assert not q.variant_applies(q.VARIANT_WS_64x128, wtype, 4096, 14336, 4096)
         assert q.choice(wtype, 128, 1, 1) == q.E_SHAPE
     assert q.choice(5, 32, 1, 1) == q.E_TYPE
+
+
+def tile_dims(name):
+    """(rows of T, columns of K) of a tiled variant's name, e.g. ws_128x256."""
+    bt, bk = name.split("_")[-1].split("x")
+    return int(bt), int(bk)
+
+
+def test_plan():
+    """Two launches over column ranges of dst where one tile would leave the
+    last round over the 256 CUs partly empty and a larger tile fills whole
+    rounds (measured faster in every case listed: DESIGN's kernel-choice
+    section); one launch elsewhere."""
+    two = {
+        (q.Q4_0, 5120, 17408, 2048): (q.VARIANT_WS_128x256, 4096, q.VARIANT_WS2_64x128),
+        (q.Q4_K, 14336, 4096, 4096): (q.VARIANT_WS_128x256, 2048, q.VARIANT_WS_256x256),
+        (q.Q4_K, 4352, 4096, 4096): (q.VARIANT_WS_256x256, 4096, q.VARIANT_WS_32x256),
+        (q.Q4_K, 11008, 4096, 4096): (q.VARIANT_WS_256x256, 8192, q.VARIANT_WS_64x256),
+    }
+    for wtype in (q.Q8_0, q.Q4_1, q.Q5_0, q.Q5_1, q.MXFP4, q.NVFP4, q.F16, q.BF16, q.F32):
+        two[(wtype, 5120, 17408, 2048)] = (q.VARIANT_WS_128x256, 4096, q.VARIANT_WS2_64x128)
+    for (wtype, K, N, T), p in two.items():
+        assert q.plan(wtype, K, N, T) == p, (wtype, K, N, T, q.plan_names(wtype, K, N, T))
+        assert q.choice(wtype, K, N, T) == p[0]
+    one = {
+        (q.Q4_K, 4096, 14336, 4096): q.VARIANT_WS_256x256,   # 256 tiles: one whole round
+        (q.Q4_K, 14336, 4096, 16): q.VARIANT_SKINNY,
+        (q.F32, 4096, 4096, 512): q.VARIANT_WS2_64x128,
+        (q.BF16, 4096, 4096, 512): q.VARIANT_WS2_64x128,
+        (q.Q8_0, 256, 128, 64): q.VARIANT_WS_32x128,
+        (q.Q4_0, 5120, 64, 2048): q.VARIANT_WS_64x128,        # saves less than a launch costs
+        (q.Q4_K, 4096, 14336, 2048): q.VARIANT_WS_128x256,
+    }
+    for (wtype, K, N, T), v in one.items():
+        assert q.plan(wtype, K, N, T) == (v, K, 0), (wtype, K, N, T, q.plan_names(wtype, K, N, T))
+    assert q.plan_names(q.Q4_0, 5120, 17408, 2048) == "ws_128x256[0:4096]+ws2_64x128[4096:5120]"
+    v0, v1, ks = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    assert q.lib.retro_out_prod_plan(q.Q4_0, 5120, 17408, 2048, None, ctypes.byref(ks), ctypes.byref(v1)) == q.E_NULL
+    assert q.lib.retro_out_prod_plan(q.Q4_K, 100, 1, 1, ctypes.byref(v0), ctypes.byref(ks),
+                                     ctypes.byref(v1)) == q.E_SHAPE
+
+
+def test_plan_invariants_over_shapes():
+    """Every two-launch plan over a grid of shapes splits at a whole block
+    whose W bytes and dst column keep 16-byte alignment, runs variants that
+    apply to their parts, and gives its first part whole rounds of tiles."""
+    Ks = (1024, 2304, 4352, 5120, 11008, 14336)
+    Ns = (64, 4096, 17408)
+    Ts = (17, 100, 512, 2048, 4096)
+    split = 0
+    for wtype in q.TYPES.values():
+        blk = {q.F32: 1, q.F16: 1, q.BF16: 1, q.NVFP4: 64}.get(wtype, 256 if wtype in KQUANT_TYPES else 32)
+        for K, N, T in itertools.product(Ks, Ns, Ts):
+            if K % blk or q.row_bytes(wtype, K) < 0:
+                continue
+            v0, ks, v1 = q.plan(wtype, K, N, T)
+            assert q.choice(wtype, K, N, T) == v0
+            if ks == K:
+                assert v1 == 0
+                continue
+            split += 1
+            assert 0 < ks < K and ks % blk == 0 and ks % 4 == 0, (wtype, K, N, T, ks)
+            assert q.row_bytes(wtype, ks) % 16 == 0, (wtype, K, ks)
+            assert q.variant_applies(v0, wtype, ks, N, T) and q.variant_applies(v1, wtype, K - ks, N, T)
+            bt, bk = tile_dims(q.VARIANT_NAMES[v0])
+            assert ks % bk == 0 and (-(-T // bt) * (ks // bk)) % 256 == 0, (wtype, K, N, T, q.VARIANT_NAMES[v0], ks)
+    assert split > 20
+
+
+def test_views_plan():
+    """Batches count toward the rounds: 16 matrices of Q4_0 200 x 1280 with
+    N = 2048 fill whole rounds of 128 x 128 tiles on 1024 columns."""
+    rb = q.row_bytes(q.Q4_0, 1280)
+    for sgt, sgn in ((2048, 1), (1, 200)):
+        assert q.views_plan(q.Q4_0, 1280, 2048, 200, rb, sgt, sgn, 1280, 4, 4) == (
+            q.VARIANT_WS_128x128, 1024, q.VARIANT_WS_32x128)
+    assert q.views_plan(q.Q4_0, 1280, 2048, 200, rb, 2048, 1, 1280, 1, 1)[1] == 1280
+    assert q.views_plan(q.Q4_0, 5120, 17408, 2048, q.row_bytes(q.Q4_0, 5120), 17408, 1, 5120) == \
+        q.plan(q.Q4_0, 5120, 17408, 2048)
+
+
+def test_column_split_validation():
+    """Errors of the two-launch entry point, all found before any launch
+    (fake addresses, never dereferenced)."""
+    cs = q.lib.retro_out_prod_column_split
+    W, G, D = 0x100000, 0x200000, 0x300000
+    a, b = q.VARIANT_WS_128x256, q.VARIANT_WS_64x128
+    assert cs(a, 256, b, q.Q4_0, W, G, None, 512, 4, 40, None) == q.E_NULL
+    assert cs(a, 0, b, q.Q4_0, W, G, D, 512, 4, 40, None) == q.E_SHAPE      # empty first part
+    assert cs(a, 512, b, q.Q4_0, W, G, D, 512, 4, 40, None) == q.E_SHAPE    # empty second part
+    assert cs(a, 48, b, q.Q4_0, W, G, D, 512, 4, 40, None) == q.E_SHAPE     # not a whole block
+    assert cs(a, 160, b, q.Q4_0, W, G, D, 512, 4, 40, None) == q.E_ALIGN    # 90 bytes of W before it
+    assert cs(a, 128, b, q.Q8_0, W, G, D, 512, 4, 40, None) == q.E_ALIGN    # 136 bytes
+    assert cs(a, 256, b, q.Q4_K, W, G, D, 512, 4, 40, None) == q.E_VARIANT  # 128-column tile on Q4_K
+    assert cs(q.VARIANT_SKINNY, 256, b, q.Q4_0, W, G, D, 512, 4, 17, None) == q.E_VARIANT
+    assert cs(42, 256, b, q.Q4_0, W, G, D, 512, 4, 40, None) == q.E_VARIANT
+    assert cs(a, 256, b, q.Q4_0, W, G, D, 0, 4, 40, None) == q.E_SHAPE      # K = 0: no split point
+    assert cs(a, 256, b, 5, W, G, D, 512, 4, 40, None) == q.E_TYPE
+    # nothing to compute: checked, then no launch
+    assert cs(a, 256, b, q.Q4_0, W, G, D, 512, 4, 0, None) == q.OK
+    assert cs(q.VARIANT_AUTO, 256, q.VARIANT_AUTO, q.Q4_0, W, G, D, 512, 4, 0, None) == q.OK
 
 
 def test_variant_applies():

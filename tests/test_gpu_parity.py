@@ -531,6 +531,47 @@ BATCHED = [(wl.Q4_K, 512, 64, 40, ["auto", "ws_64x256", "ws_256x256", "tile_64x2
            (wl.BF16, 264, 40, 70, ["auto", "ws_32x128", "ws2_64x128", "tile_128x128"])]
 
 
+def batched_operands(wtype, K, N, T, layout, ne03, ne02, ne3, ne2, seed):
+    """W: ne03 x ne02 matrices with rows padded to 16-byte multiples; G: a
+    permuted view of ne3 x ne2 matrices (its i3 batches closer than its i2
+    ones), each stored by rows or t-fastest. Returns the cases, W, G, the
+    host G values [i2][i3] and G's (t, n) strides."""
+    rb = wl.row_bytes(wtype, K)
+    ldw = (rb + 15) // 16 * 16
+    cases = [wl.make_case(wtype, N, K, T, seed=seed + i) for i in range(ne03 * ne02)]
+    wbig = torch.zeros((ne03, ne02, N, ldw), dtype=torch.uint8, device="cuda")
+    for i, c in enumerate(cases):
+        wbig[i // ne02, i % ne02, :, :rb] = dev(c["W"])
+    rng = np.random.default_rng(seed + 77)
+    g_host = rng.standard_normal((ne2, ne3, T, N)).astype(np.float32)
+    if layout == "rows":
+        G = dev(g_host).permute(1, 0, 2, 3)              # [ne3, ne2, T, N], not contiguous
+    else:
+        G = dev(np.ascontiguousarray(g_host.transpose(0, 1, 3, 2))).permute(1, 0, 3, 2)
+        assert G.stride(2) == 1
+    sgt, sgn = (N, 1) if layout == "rows" else (1, T)
+    return cases, wbig, G, g_host, ldw, sgt, sgn
+
+
+def check_batches(q, wtype, K, T, cases, wbig, G, g_host, ne03, ne02, ne3, ne2, variant, label):
+    """Run out_prod_batched into dst matrices with gaps; every batch must
+    match the oracle on its own pair of matrices, and the gaps keep their
+    sentinel."""
+    dbig = torch.full((ne3, ne2, T + 1, K + 4), 7.0, device="cuda")
+    out = dbig[:, :, :T, :K]
+    q.out_prod_batched(wtype, wbig, G, K, out=out, variant=variant)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i3 in range(ne3):
+        for i2 in range(ne2):
+            c = cases[(i3 // (ne3 // ne03)) * ne02 + i2 // (ne2 // ne02)]
+            _, acc, ab = oracle.out_prod(wtype, c["W"], g_host[i2, i3], K, nthreads=ORACLE_THREADS)
+            check_close(got[i3, i2], acc, ab, f"batch {i3},{i2} {label}")
+    rest = dbig.clone()
+    rest[:, :, :T, :K] = 7.0
+    assert bool((rest == 7.0).all()), label
+
+
 @pytest.mark.parametrize("wtype,K,N,T,variants", BATCHED)
 @pytest.mark.parametrize("layout", ["rows", "columns"])
 def test_batched_broadcast_matches_oracle(q, wtype, K, N, T, variants, layout):
@@ -540,36 +581,28 @@ def test_batched_broadcast_matches_oracle(q, wtype, K, N, T, variants, layout):
     or t-fastest), dst matrices with gaps. Every batch matches the oracle on
     its own pair of matrices, and the gaps of dst keep their sentinel."""
     ne03, ne02, ne3, ne2 = 1, 2, 2, 4
-    rb = wl.row_bytes(wtype, K)
-    ldw = (rb + 15) // 16 * 16
-    cases = [wl.make_case(wtype, N, K, T, seed=1200 + i) for i in range(ne03 * ne02)]
-    wbig = torch.zeros((ne03, ne02, N, ldw), dtype=torch.uint8, device="cuda")
-    for i, c in enumerate(cases):
-        wbig[i // ne02, i % ne02, :, :rb] = dev(c["W"])
-    rng = np.random.default_rng(77)
-    g_host = rng.standard_normal((ne2, ne3, T, N)).astype(np.float32)
-    if layout == "rows":
-        G = dev(g_host).permute(1, 0, 2, 3)              # [ne3, ne2, T, N], not contiguous
-    else:
-        G = dev(np.ascontiguousarray(g_host.transpose(0, 1, 3, 2))).permute(1, 0, 3, 2)
-        assert G.stride(2) == 1
-    sgt, sgn = (N, 1) if layout == "rows" else (1, T)
+    cases, wbig, G, g_host, ldw, sgt, sgn = batched_operands(wtype, K, N, T, layout, ne03, ne02, ne3, ne2, 1200)
     for v in variants:
         if v != "auto" and not q.variant_applies_views(variant_id(q, v), wtype, K, N, T, ldw, sgt, sgn, K):
             continue
-        dbig = torch.full((ne3, ne2, T + 1, K + 4), 7.0, device="cuda")
-        out = dbig[:, :, :T, :K]
-        q.out_prod_batched(wtype, wbig, G, K, out=out, variant=variant_id(q, v) if v != "auto" else 0)
-        torch.cuda.synchronize()
-        got = out.cpu().numpy()
-        for i3 in range(ne3):
-            for i2 in range(ne2):
-                c = cases[(i3 // (ne3 // ne03)) * ne02 + i2 // (ne2 // ne02)]
-                _, acc, ab = oracle.out_prod(wtype, c["W"], g_host[i2, i3], K)
-                check_close(got[i3, i2], acc, ab, f"batch {i3},{i2} {v}")
-        rest = dbig.clone()
-        rest[:, :, :T, :K] = 7.0
-        assert bool((rest == 7.0).all()), v
+        check_batches(q, wtype, K, T, cases, wbig, G, g_host, ne03, ne02, ne3, ne2,
+                      variant_id(q, v) if v != "auto" else 0, v)
+
+
+@pytest.mark.parametrize("wtype", [wl.Q4_0, wl.BF16, wl.MXFP4])
+@pytest.mark.parametrize("layout", ["rows", "columns"])
+def test_batched_two_launch_plan_matches_oracle(q, wtype, layout):
+    """16 matrices of 200 x 1280 with N = 2048: their tiles fill whole rounds
+    of 128 x 128 on 1024 columns, so the automatic choice runs two launches
+    over column ranges of every dst matrix; W broadcast 2 x 4 times, G
+    permuted, dst with gaps."""
+    K, N, T = 1280, 2048, 200
+    ne03, ne02, ne3, ne2 = 1, 2, 4, 4
+    cases, wbig, G, g_host, ldw, sgt, sgn = batched_operands(wtype, K, N, T, layout, ne03, ne02, ne3, ne2, 1400)
+    v0, ks, v1 = q.views_plan(wtype, K, N, T, ldw, sgt, sgn, K + 4, ne2, ne3)
+    assert ks < K, (v0, ks, v1)
+    print(f"plan {q.VARIANT_NAMES[v0]}[0:{ks}] + {q.VARIANT_NAMES[v1]}[{ks}:{K}]", flush=True)
+    check_batches(q, wtype, K, T, cases, wbig, G, g_host, ne03, ne02, ne3, ne2, 0, "auto")
 
 
 def test_batched_empty_and_single(q):
@@ -582,6 +615,47 @@ def test_batched_empty_and_single(q):
     assert np.array_equal(one.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     empty = torch.zeros((0, 20, 256), device="cuda")
     q.out_prod_batched(wl.Q4_0, W, G.unsqueeze(0)[:0], 256, out=empty)
+
+
+# --- two launches over column ranges of dst ---------------------------------------
+
+# (type, K, N, T, k_split, variant0, variant1): ragged T, N and parts, both
+# kernel families, the skinny kernel and the exact splits
+COLUMN_SPLITS = [
+    (wl.Q4_0, 640, 100, 200, 512, "ws_128x256", "ws2_64x128"),
+    (wl.Q4_K, 768, 96, 130, 256, "ws_256x256", "ws_32x256"),
+    (wl.Q4_K, 1024, 64, 67, 768, "ws_128x256", "tile_64x256"),
+    (wl.F16, 520, 76, 150, 256, "ws_128x128", "tile_64x64"),
+    (wl.MXFP4, 640, 36, 90, 512, "ws_64x256", "ws_32x128"),
+    (wl.Q8_0, 512, 40, 16, 256, "skinny", "skinny"),
+    (wl.F32, 300, 64, 70, 128, "auto", "auto"),
+    (wl.NVFP4, 448, 48, 100, 256, "ws_128x256", "ws_64x128"),
+    (wl.Q5_K, 768, 60, 70, 512, "split_128x256", "ws_32x256"),
+    (wl.BF16, 520, 40, 33, 256, "split_128x128", "ws_32x128"),
+]
+
+
+@pytest.mark.parametrize("wtype,K,N,T,ks,v0,v1", COLUMN_SPLITS)
+def test_column_split_matches_parts_and_oracle(q, wtype, K, N, T, ks, v0, v1):
+    """retro_out_prod_column_split: the whole dst (NaN-prefilled) within the
+    bars of the oracle, and each column range bit-identical to its variant
+    run alone on those columns of W."""
+    c = wl.make_case(wtype, N, K, T, seed=1300 + K + N)
+    ids = [q.VARIANT_AUTO if v == "auto" else variant_id(q, v) for v in (v0, v1)]
+    W, G = dev(c["W"]), dev(c["G"])
+    out = torch.full((T, K), float("nan"), device="cuda")
+    q.out_prod_column_split(wtype, W, G, K, ids[0], ks, ids[1], out=out)
+    torch.cuda.synchronize()
+    y = out.cpu().numpy()
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
+    check_close(y, acc, ab, f"{v0}+{v1}")
+    rb, off = wl.row_bytes(wtype, K), wl.row_bytes(wtype, ks)
+    rows = np.asarray(c["W"]).reshape(N, rb)
+    parts = [dict(c, W=np.ascontiguousarray(rows[:, :off]), K=ks), dict(c, W=np.ascontiguousarray(rows[:, off:]),
+                                                                      K=K - ks)]
+    for part, v, cols in zip(parts, (v0, v1), (slice(0, ks), slice(ks, K))):
+        assert applies(q, part, v), v
+        assert same_bits(y[:, cols], run(q, part, v)), v
 
 
 # --- full-size workloads ----------------------------------------------------------
@@ -622,8 +696,7 @@ def test_full_size_whole_output(q, name, wtype):
     with the oracle element by element (NMSE over the whole output, the
     relative error of each output), then determinism of a second call."""
     c = wl.workload(name, wtype)
-    print(f"{name} {wl.TYPE_NAMES[c['type']]}: kernel {q.VARIANT_NAMES[q.choice(c['type'], c['K'], c['N'], c['T'])]}",
-          flush=True)
+    print(f"{name} {wl.TYPE_NAMES[c['type']]}: kernel {q.plan_names(c['type'], c['K'], c['N'], c['T'])}", flush=True)
     W, G = dev(c["W"]), dev(c["G"])
     out = torch.full((c["T"], c["K"]), float("nan"), device="cuda")
     q.out_prod(c["type"], W, G, c["K"], out=out)
@@ -690,8 +763,12 @@ def test_full_size_decode_through_identity(q, name):
     N, K = c["N"], c["K"]
     ref = oracle.dequantize(c["type"], c["W"], K)
     W = dev(c["W"])
-    variant = q.choice(c["type"], K, N, c["T"])
-    if variant == q.VARIANT_SKINNY:
+    variant, ks, v1 = q.plan(c["type"], K, N, c["T"])
+    if ks < K:
+        # the two launches of the benchmarked call, each over its columns
+        out = q.out_prod_column_split(c["type"], W, torch.eye(N, device="cuda"), K, variant, ks, v1)
+        assert np.array_equal(out.cpu().numpy(), ref)
+    elif variant == q.VARIANT_SKINNY:
         # T = N would leave the skinny range; check 16-row slices of W instead
         for n0 in range(0, N, N // 8):
             sl = slice(n0, n0 + 16)
