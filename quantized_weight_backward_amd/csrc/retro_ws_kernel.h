@@ -122,13 +122,23 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 }
 
 // Float index of W element (row n, column k) of a chunk inside the W part of
-// an LDS buffer: column k holds its 32 rows with the 4-row groups permuted
-// by bits 4-6 of k, which spreads the producers' 4-byte writes over banks.
-// The permutation keeps every aligned 4-row group together and in order, so
-// a consumer still reads 4 rows as one float4.
+// an LDS buffer: column k holds its 32 rows with the aligned 4-row groups
+// XOR-permuted by a 3-bit function of bits 3-7 of k (bit 0: k4 ^ k5, bit 1:
+// k3 ^ k6, bit 2: k3 ^ k4 ^ k7). The permutation keeps every 4-row group
+// together and in order, so a consumer still reads 4 rows as one float4; it
+// is constant over each aligned group of 8 columns, so the 8 lanes of a
+// float4 read (8 consecutive columns) still cover the 32 banks once; and it
+// gives the lanes of every producer store pattern distinct banks: 4-byte
+// stores of one row into 8 or 16 consecutive columns per lane (the lanes
+// differing in row and in column bits 3-7 by the type's thread mapping) and
+// float4 stores of 4 rows. A model of the 32-bank LDS counts no conflicts
+// for any type or tile with it, against 128-768 extra cycles per chunk with
+// bits 4-6 of k alone (which the conflict counters matched).
 template <int WP>
 __device__ __forceinline__ int ws_w_index(int k, int n) {
-    return k * WP + (n ^ (((k >> 4) & 7) << 2));
+    const int v = (((k >> 4) ^ (k >> 5)) & 1) | ((((k >> 3) ^ (k >> 6)) & 1) << 1) |
+                  ((((k >> 3) ^ (k >> 4) ^ (k >> 7)) & 1) << 2);
+    return k * WP + (n ^ (v << 2));
 }
 
 // Consumer waves 0 .. NC NG - 1 of a producer/consumer tile kernel: contract
@@ -312,9 +322,11 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
                             : uint32_t(((id >> 3) * args.ldg + 4 * (id & 7)) * 4);
         }
         // W: byte offset of this thread's block in the chunk, and the LDS
-        // float index of the first element it writes in each 16-column group.
+        // float index of the first element it writes in each aligned group of
+        // 8 columns (ws_w_index permutes rows per such group; the columns of
+        // a group are then WP floats apart).
         uint32_t woff = 0;
-        int wlds[S::kDense ? S::DUNITS : (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) ? 4 : 2];
+        int wlds[S::kDense ? S::DUNITS : 4];
         if constexpr (S::kDense) {
             // unit id: rows 4 (id / (BK / 4)) .. + 3, columns 4 (id % (BK / 4)) .. + 3
 #pragma unroll
@@ -328,7 +340,9 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
             const int r = p >> 3, u = p & 7, c = u >> 1, h = u & 1;
             woff = uint32_t(r * args.pitch);
             wlds[0] = ws_w_index<WP>(64 * c + 16 * h, r);
-            wlds[1] = ws_w_index<WP>(64 * c + 32 + 16 * h, r);
+            wlds[1] = ws_w_index<WP>(64 * c + 16 * h + 8, r);
+            wlds[2] = ws_w_index<WP>(64 * c + 32 + 16 * h, r);
+            wlds[3] = ws_w_index<WP>(64 * c + 32 + 16 * h + 8, r);
         } else if constexpr (TYPE == kQ6_K || TYPE == kQ2_K || TYPE == kQ3_K) {
             // half hh, l range 8j .. 8j + 7 of row p / 8: columns
             // 128 hh + 32 qq + 8j + 0..7 of the four quarters qq
@@ -342,20 +356,24 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
             const int r = p >> 3, col = 16 * S::NV_SB * (p & 7);
             woff = uint32_t(r * args.pitch + (col >> 6) * 36);
 #pragma unroll
-            for (int i = 0; i < S::NV_SB; ++i) wlds[i] = ws_w_index<WP>(col + 16 * i, r);
+            for (int i = 0; i < 2 * S::NV_SB; ++i) wlds[i] = ws_w_index<WP>(col + 8 * i, r);
         } else {
             // part s of block b of row r: code bytes CB s .. CB s + CB - 1
             const int id = p / S::QSPLIT, s = p - id * S::QSPLIT;
             const int r = id / (BK / 32), b = id - r * (BK / 32);
             woff = uint32_t(r * args.pitch + b * F::kBytes);
             if constexpr (TYPE == kQ8_0) {
-                // columns 32b + CB s + 0 .. CB - 1 (one or two 16-column groups)
-                wlds[0] = ws_w_index<WP>(32 * b + S::CB * s, r);
-                wlds[1] = ws_w_index<WP>(32 * b + S::CB * s + 16, r);
+                // columns 32b + CB s + 0 .. CB - 1: CB / 8 groups of 8
+#pragma unroll
+                for (int g = 0; g < S::CB / 8; ++g) wlds[g] = ws_w_index<WP>(32 * b + S::CB * s + 8 * g, r);
             } else {
-                // byte j: low nibble is column 32b + j, high nibble 32b + 16 + j
-                wlds[0] = ws_w_index<WP>(32 * b, r) + S::CB * s * WP;
-                wlds[1] = ws_w_index<WP>(32 * b + 16, r) + S::CB * s * WP;
+                // byte j: low nibble is column 32b + j, high nibble 32b + 16 + j;
+                // the thread's bytes CB s .. give CB / 8 groups of 8 in each half
+#pragma unroll
+                for (int g = 0; g < S::CB / 8; ++g) {
+                    wlds[g] = ws_w_index<WP>(32 * b + S::CB * s + 8 * g, r);
+                    wlds[2 + g] = ws_w_index<WP>(32 * b + 16 + S::CB * s + 8 * g, r);
+                }
             }
         }
         // elements spanned by G (none when N = 0: G is empty and its pointer
@@ -580,34 +598,35 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
                 float a0, b0, a1, b1;
                 q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c, a0, b0);
                 q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c + 1, a1, b1);
-                float* lo = ws + wlds[0];
-                float* hi = ws + wlds[1];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    // columns 4i .. 4i + 3 of the 16: group i / 2 of the low and high halves
+                    float* lo = ws + wlds[i >> 1] + 4 * (i & 1) * WP;
+                    float* hi = ws + wlds[2 + (i >> 1)] + 4 * (i & 1) * WP;
                     float e[4];
                     q4_k_x4(wreg[i], false, a0, b0, e);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) lo[(4 * i + j) * WP] = e[j];
+                    for (int j = 0; j < 4; ++j) lo[j * WP] = e[j];
                     q4_k_x4(wreg[i], true, a1, b1, e);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) hi[(4 * i + j) * WP] = e[j];
+                    for (int j = 0; j < 4; ++j) hi[j * WP] = e[j];
                 }
             } else if constexpr (TYPE == kQ5_K) {
                 const int c = (p & 7) >> 1;
                 float a0, b0, a1, b1;
                 q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c, a0, b0);
                 q4_k_coeffs(wreg[4], wreg[5], wreg[6], wreg[7], 2 * c + 1, a1, b1);
-                float* lo = ws + wlds[0];
-                float* hi = ws + wlds[1];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    float* lo = ws + wlds[i >> 1] + 4 * (i & 1) * WP;
+                    float* hi = ws + wlds[2 + (i >> 1)] + 4 * (i & 1) * WP;
                     float e[4];
                     q5_k_x4(wreg[i], wreg[8 + i], 2 * c, false, a0, b0, e);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) lo[(4 * i + j) * WP] = e[j];
+                    for (int j = 0; j < 4; ++j) lo[j * WP] = e[j];
                     q5_k_x4(wreg[i], wreg[8 + i], 2 * c + 1, true, a1, b1, e);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) hi[(4 * i + j) * WP] = e[j];
+                    for (int j = 0; j < 4; ++j) hi[j * WP] = e[j];
                 }
             } else if constexpr (TYPE == kQ6_K) {
                 const int j = p & 3;
@@ -660,8 +679,8 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
                 for (int w = 0; w < CW; ++w) {
                     float e[4];
                     q8_0_x4(wreg[w], d, e);
-                    // columns CB s + 4w + j: the first group for 4w < 16
-                    float* col = (4 * w < 16) ? ws + wlds[0] + (4 * w) * WP : ws + wlds[1] + (4 * w - 16) * WP;
+                    // columns CB s + 4w + j: group w / 2 of 8
+                    float* col = ws + wlds[w >> 1] + 4 * (w & 1) * WP;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) col[j * WP] = e[j];
                 }
@@ -675,11 +694,12 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
                     for (int w = 0; w < 2; ++w) {
                         float el[4], eh[4];
                         nvfp4_x8(wreg[2 * i + w], sc, el, eh);
+                        // each base's stores together, so that the compiler pairs
+                        // them into two-address stores
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            ws[wlds[i] + (4 * w + j) * WP] = el[j];
-                            ws[wlds[i] + (8 + 4 * w + j) * WP] = eh[j];
-                        }
+                        for (int j = 0; j < 4; ++j) ws[wlds[2 * i] + (4 * w + j) * WP] = el[j];      // columns 0 .. 7
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ws[wlds[2 * i + 1] + (4 * w + j) * WP] = eh[j];  // columns 8 .. 15
                     }
                 }
             } else if constexpr (TYPE == kMXFP4) {  // code bytes CB s .. of the block
@@ -689,11 +709,11 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
                 for (int w = 0; w < CW; ++w) {
                     float el[4], eh[4];
                     mxfp4_x8(wreg[w], sc, el, eh);
+                    // bytes 4w .. 4w + 3 of the thread's CB: group w / 2 of 8 in each half
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        ws[wlds[0] + (4 * w + j) * WP] = el[j];
-                        ws[wlds[1] + (4 * w + j) * WP] = eh[j];
-                    }
+                    for (int j = 0; j < 4; ++j) ws[wlds[w >> 1] + (4 * (w & 1) + j) * WP] = el[j];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ws[wlds[2 + (w >> 1)] + (4 * (w & 1) + j) * WP] = eh[j];
                 }
             } else {  // 32-element nibble blocks: code bytes CB s .. of the block
                 constexpr int CW = S::CB / 4;
@@ -709,10 +729,10 @@ __global__ __launch_bounds__((WsShape<TYPE, WA, WB, CT, NG, NC>::kThreads),
                     float e[4];
                     nibble32_x4<TYPE>(wreg[w], qh, first + 4 * w, d, m, e);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ws[wlds[0] + (4 * w + j) * WP] = e[j];
+                    for (int j = 0; j < 4; ++j) ws[wlds[w >> 1] + (4 * (w & 1) + j) * WP] = e[j];
                     nibble32_x4<TYPE>(wreg[w], qh, 16 + first + 4 * w, d, m, e);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ws[wlds[1] + (4 * w + j) * WP] = e[j];
+                    for (int j = 0; j < 4; ++j) ws[wlds[2 + (w >> 1)] + (4 * (w & 1) + j) * WP] = e[j];
                 }
             }
         };
