@@ -517,26 +517,26 @@ def oracle_timing(case: dict) -> dict:
             "sample": f"{rows} of {T} t rows (full decode of W included), median of {repeats}: {med:.4f} s"}
 
 
-def smi_clock_under_load(sink) -> dict:
-    """Graphics clocks that amd-smi reports while about 4 s of the F32 matrix-
-    core probe run (queued before the query, so the query lands inside them)."""
+def smi_under_load(enqueue) -> dict:
+    """Graphics clocks and socket power that amd-smi reports while about 4 s
+    of queued GPU work run (enqueue() queues them before the query, so the
+    query lands inside them)."""
     import subprocess
 
     import torch
 
-    import quantized_weight_backward_amd as q
-
-    for _ in range(1100):
-        q.probe_mfma(q.PROBE_MFMA_F32, sink, 4096)
-    res = {"source": "amd-smi metric -c --json"}
+    enqueue()
+    res = {"source": "amd-smi metric -c -p --json"}
     try:
         time.sleep(0.5)
-        txt = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+        txt = subprocess.run(["amd-smi", "metric", "-c", "-p", "--json"], capture_output=True, text=True,
                              timeout=20).stdout
-        gpu = json.loads(txt)["gpu_data"][0]["clock"]
-        gfx = sorted(k for k in gpu if k.startswith("gfx_"))
-        res["gfx_mhz"] = [gpu[k]["clk"]["value"] for k in gfx]
-        res["max_mhz"] = gpu[gfx[0]]["max_clk"]["value"]
+        gpu = json.loads(txt)["gpu_data"][0]
+        clk = gpu["clock"]
+        gfx = sorted(k for k in clk if k.startswith("gfx_"))
+        res["gfx_mhz"] = [clk[k]["clk"]["value"] for k in gfx]
+        res["max_mhz"] = clk[gfx[0]]["max_clk"]["value"]
+        res["socket_power_w"] = gpu.get("power", {}).get("socket_power", {}).get("value")
     except Exception as exc:  # the tool may be absent or print something else
         res["error"] = f"{type(exc).__name__}: {exc}"[:200]
     torch.cuda.synchronize()
@@ -817,14 +817,19 @@ def main() -> int:
     cdst = torch.empty_like(csrc)
     copy_gbs = 2.0 * csrc.numel() * 4 / timed(lambda: q.probe_copy(csrc, cdst)) / 1e9
     del csrc, cdst
-    clock = None
+    clock = clock_large = None
     if not args.no_cpu_baseline:
-        clock = smi_clock_under_load(sink)
+        # about 4 s each: the F32 matrix-core probe, then the large-T kernel
+        clock = smi_under_load(lambda: [q.probe_mfma(q.PROBE_MFMA_F32, sink, 4096) for _ in range(1100)])
+        n_large = max(1, int(4.0 / avg_large))
+        clock_large = smi_under_load(
+            lambda: [q.out_prod(q.Q4_K, Wl, Gl, large["K"], out=Dl) for _ in range(n_large)])
     ceilings = {"kind": "measured on this GPU: MFMA-only loops (no memory), 16-byte copy of 1 GiB",
                 "mfma_f32_tflops": round(mfma_f32, 2), "mfma_bf16_tflops": round(mfma_bf16, 1),
                 "copy_gbs": round(copy_gbs, 1),
                 "mfma_f32_beside_valu": mix,
                 "smi_clock_under_mfma_load": clock,
+                "smi_under_large_kernel": clock_large,
                 "mfma_f32_clock_ghz": round(mfma_f32 / PEAK_F32_TFLOPS * 2.4, 3)}
     if split is not None:
         split["bf16_mfma_frac_of_measured"] = round(split["bf16_flops_issued_per_launch"] / avg_split / 1e12 / mfma_bf16, 4)
