@@ -220,18 +220,27 @@ constexpr double kCuFlops = 157.3e12 / kNumCUs * 0.8;  // F32 FLOP/s of one CU a
 constexpr double kPlanMinSaving = 5e-6;                // seconds
 
 Plan plan_for(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    const int single = choose(type, K, N, T, s);
-    Plan best{single, K, 0};
-    if (single <= 0 || single == RETRO_VARIANT_SKINNY || N == 0) return best;
-    const double one = choose_tile(type, K, N, T, s).cost;
+    if (skinny_applies(type, K, N, T, s)) return {RETRO_VARIANT_SKINNY, K, 0};
+    const Choice single = choose_tile(type, K, N, T, s);
+    Plan best{single.id, K, 0};
+    if (single.id <= 0 || N == 0) return best;
+    const double one = single.cost;
     double best_cost = one;
     for (const auto& v : kTiles) {
         // the two-pipeline tile is taken only through choose_tile's rule
         if (!v.ws || v.id == RETRO_VARIANT_WS2_64x128 || !auto_takes(v, type)) continue;
         if (!tile_applies(v, type, K, N, T, s)) continue;
         const int64_t tiles_t = cdiv(T, v.bt) * s.batches();
-        for (int64_t c = 1; c * v.bk < K; ++c) {
-            if ((tiles_t * c) % kNumCUs != 0) continue;  // whole rounds only
+        // whole rounds: tiles_t * c a multiple of kNumCUs, i.e. c a multiple
+        // of kNumCUs / gcd(tiles_t, kNumCUs)
+        int64_t g = kNumCUs, r = tiles_t % kNumCUs;
+        while (r) {
+            const int64_t t = g % r;
+            g = r;
+            r = t;
+        }
+        const int64_t step = kNumCUs / g;
+        for (int64_t c = step; c * v.bk < K; c += step) {
             const int64_t k1 = c * v.bk;
             if (!split_point_ok(type, k1)) continue;
             const Choice tail = choose_tile(type, K - k1, N, T, s);
@@ -245,8 +254,39 @@ Plan plan_for(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     }
     if (best.k_split < K &&
         (best_cost > kPlanMargin * one || (one - best_cost) * 2.0 * double(N) / kCuFlops < kPlanMinSaving))
-        return {single, K, 0};
+        return {single.id, K, 0};
     return best;
+}
+
+// The plan of the last few shapes seen on this thread. Automatic calls tend
+// to repeat a shape, and a plan search costs a few microseconds of host time
+// (about 20 tail choices over 13 tiles each), which a launch-bound call
+// would feel. The plan depends on the type, the shape, W's and G's row
+// strides, G's orientation and the number of matrices, nothing else.
+struct PlanKey {
+    int type;
+    int64_t K, N, T, ldw, ldg, batches;
+    bool gcols;
+    bool operator==(const PlanKey& o) const {
+        return type == o.type && K == o.K && N == o.N && T == o.T && ldw == o.ldw && ldg == o.ldg &&
+               batches == o.batches && gcols == o.gcols;
+    }
+};
+
+Plan cached_plan(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    constexpr int kSlots = 4;
+    thread_local PlanKey keys[kSlots];
+    thread_local Plan plans[kSlots];
+    thread_local int used = 0, next = 0;
+    const PlanKey key{type, K, N, T, s.ldw, s.ldg, s.batches(), s.gcols};
+    for (int i = 0; i < used; ++i)
+        if (keys[i] == key) return plans[i];
+    const Plan p = plan_for(type, K, N, T, s);
+    keys[next] = key;
+    plans[next] = p;
+    next = (next + 1) % kSlots;
+    if (used < kSlots) ++used;
+    return p;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -367,7 +407,7 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
     if (rc != RETRO_OK || empty) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (variant == RETRO_VARIANT_AUTO) {
-        const Plan p = plan_for(type, K, N, T, s);
+        const Plan p = cached_plan(type, K, N, T, s);
         if (p.v0 < 0) return p.v0;
         return run_plan(p, type, W, G, dst, K, N, T, s, st);
     }
@@ -624,13 +664,13 @@ int retro_out_prod_views_choice(int type, int64_t K, int64_t N, int64_t T, int64
     s.ne2 = ne2;
     s.ne3 = ne3;
     rc = check_strides(type, K, N, T, s);
-    return rc != RETRO_OK ? rc : plan_for(type, K, N, T, s).v0;
+    return rc != RETRO_OK ? rc : cached_plan(type, K, N, T, s).v0;
 }
 
 int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T) {
     const int rc = check_shape(type, K, N, T);
     if (rc != RETRO_OK) return rc;
-    return plan_for(type, K, N, T, contiguous(type, K, N)).v0;
+    return cached_plan(type, K, N, T, contiguous(type, K, N)).v0;
 }
 
 int retro_out_prod_plan(int type, int64_t K, int64_t N, int64_t T, int32_t* variant0, int64_t* k_split,
@@ -638,7 +678,7 @@ int retro_out_prod_plan(int type, int64_t K, int64_t N, int64_t T, int32_t* vari
     const int rc = check_shape(type, K, N, T);
     if (rc != RETRO_OK) return rc;
     if (!variant0 || !k_split || !variant1) return RETRO_E_NULL;
-    const Plan p = plan_for(type, K, N, T, contiguous(type, K, N));
+    const Plan p = cached_plan(type, K, N, T, contiguous(type, K, N));
     if (p.v0 < 0) return p.v0;
     *variant0 = p.v0;
     *k_split = p.k_split;
@@ -658,7 +698,7 @@ int retro_out_prod_views_plan(int type, int64_t K, int64_t N, int64_t T, int64_t
     s.ne3 = ne3;
     rc = check_strides(type, K, N, T, s);
     if (rc != RETRO_OK) return rc;
-    const Plan p = plan_for(type, K, N, T, s);
+    const Plan p = cached_plan(type, K, N, T, s);
     if (p.v0 < 0) return p.v0;
     *variant0 = p.v0;
     *k_split = p.k_split;

@@ -202,6 +202,18 @@ def test_plan_invariants_over_shapes():
     assert split > 20
 
 
+def test_plan_is_the_same_from_the_cache():
+    """Plans are kept per thread for the last few shapes: asking for more
+    shapes than it holds, in two orders, gives the same answers."""
+    shapes = [(q.Q4_0, 5120, 17408, 2048), (q.Q4_K, 14336, 4096, 4096), (q.Q8_0, 256, 128, 64),
+              (q.F32, 4096, 4096, 512), (q.Q4_K, 4352, 4096, 4096), (q.MXFP4, 5120, 17408, 2048),
+              (q.Q4_K, 14336, 4096, 16), (q.F16, 11008, 4096, 4096)]
+    first = [q.plan(*sh) for sh in shapes]
+    for _ in range(3):
+        assert [q.plan(*sh) for sh in reversed(shapes)] == first[::-1]
+        assert [q.choice(*sh) for sh in shapes] == [p[0] for p in first]
+
+
 def test_views_plan():
     """Batches count toward the rounds: 16 matrices of Q4_0 200 x 1280 with
     N = 2048 fill whole rounds of 128 x 128 tiles on 1024 columns."""
