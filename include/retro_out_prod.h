@@ -462,9 +462,31 @@ int retro_mul_mat(int type, const void *W, const float *X, float *Y, int64_t K, 
 int retro_mul_mat_variant(int variant, int type, const void *W, const float *X, float *Y, int64_t K, int64_t N,
                           int64_t T, void *stream);
 
-/* The variant retro_mul_mat would run, or a negative error code. Touches no
- * device. */
+/* The variant retro_mul_mat would run (the first launch's when its plan has
+ * two), or a negative error code. Touches no device. */
 int retro_mul_mat_choice(int type, int64_t K, int64_t N, int64_t T);
+
+/* The launches retro_mul_mat makes: returns 1 (*variant0 over all rows of W;
+ * *n_split = N, *variant1 = 0) or 2 (*variant0 over W rows, i.e. Y columns,
+ * [0, *n_split), then *variant1 over [*n_split, N)), or a negative error code
+ * (the three pointers NULL: RETRO_E_NULL). Every Y[t][n] is complete in one
+ * tile, so the rows of W can be split between two launches with no
+ * reduction: taken where one tile size would leave the last round over the
+ * 256 CUs partly empty and a larger tile fills whole rounds on the leading
+ * rows. Touches no device. */
+int retro_mul_mat_plan(int type, int64_t K, int64_t N, int64_t T, int32_t *variant0, int64_t *n_split,
+                       int32_t *variant1);
+
+/* retro_mul_mat as two launches on `stream`: variant0 over W rows (Y
+ * columns) [0, n_split), then variant1 over [n_split, N); either may be
+ * RETRO_VARIANT_AUTO (the choice for its part alone). 0 < n_split < N
+ * (RETRO_E_SHAPE otherwise); n_split % 4 == 0 and the W bytes before row
+ * n_split a multiple of 16 (RETRO_E_ALIGN otherwise); RETRO_E_VARIANT when a
+ * variant does not apply to its part. Every check is made before either
+ * launch. Pointers, aliasing, errors and execution as retro_mul_mat. For
+ * tests and benchmarks of the plans above. */
+int retro_mul_mat_row_split(int variant0, int64_t n_split, int variant1, int type, const void *W, const float *X,
+                            float *Y, int64_t K, int64_t N, int64_t T, void *stream);
 
 /* 1 if retro_mul_mat_variant(variant, type, ..., K, N, T) with valid buffers
  * would run, 0 otherwise. Touches no device. */

@@ -73,6 +73,7 @@ EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided",
            "retro_out_prod_views_choice", "retro_out_prod_plan", "retro_out_prod_views_plan",
            "retro_out_prod_column_split",
            "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
+           "retro_mul_mat_plan", "retro_mul_mat_row_split",
            "retro_row_bytes", "retro_strerror",
            "retro_probe_sink_floats", "retro_probe_mfma", "retro_probe_mfma_valu", "retro_probe_copy")
 
@@ -117,6 +118,11 @@ def _load() -> ctypes.CDLL:
     lib.retro_mul_mat_variant.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, vp]
     lib.retro_mul_mat_choice.restype = i32
     lib.retro_mul_mat_choice.argtypes = [i32, i64, i64, i64]
+    lib.retro_mul_mat_plan.restype = i32
+    lib.retro_mul_mat_plan.argtypes = [i32, i64, i64, i64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(i64),
+                                       ctypes.POINTER(ctypes.c_int32)]
+    lib.retro_mul_mat_row_split.restype = i32
+    lib.retro_mul_mat_row_split.argtypes = [i32, i64, i32, i32, vp, vp, vp, i64, i64, i64, vp]
     lib.retro_mul_mat_variant_applies.restype = i32
     lib.retro_mul_mat_variant_applies.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_out_prod_strided_variant_applies.restype = i32
@@ -429,6 +435,48 @@ def mul_mat(wtype: int, W, X, N: int | None = None, out=None, variant: int = VAR
 
 def mul_mat_choice(wtype: int, K: int, N: int, T: int) -> int:
     return int(lib.retro_mul_mat_choice(int(wtype), int(K), int(N), int(T)))
+
+
+def mul_mat_plan(wtype: int, K: int, N: int, T: int) -> tuple[int, int, int]:
+    """The launches mul_mat makes: (variant0, n_split, variant1), variant0
+    over W rows [0, n_split) and variant1 (0 when n_split == N: one launch)
+    over the rest."""
+    v0, v1, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
+    n = lib.retro_mul_mat_plan(int(wtype), int(K), int(N), int(T), ctypes.byref(v0), ctypes.byref(ns),
+                               ctypes.byref(v1))
+    _check(OK if n > 0 else n)
+    return int(v0.value), int(ns.value), int(v1.value)
+
+
+def mul_mat_plan_names(wtype: int, K: int, N: int, T: int) -> str:
+    v0, ns, v1 = mul_mat_plan(wtype, K, N, T)
+    if ns >= N:
+        return VARIANT_NAMES[v0]
+    return f"{VARIANT_NAMES[v0]}[0:{ns}]+{VARIANT_NAMES[v1]}[{ns}:{N}]"
+
+
+def mul_mat_row_split(wtype: int, W, X, N: int, variant0: int, n_split: int, variant1: int, out=None, stream=None):
+    """mul_mat as two launches: variant0 over W rows [0, n_split), variant1
+    over the rest (contiguous W, X and out)."""
+    _device_tensor(W, "W")
+    _device_tensor(X, "X")
+    if X.dtype != torch.float32 or X.dim() != 2:
+        raise ValueError("X must be a contiguous 2-D float32 tensor (T x K)")
+    T, K = X.shape
+    rb = row_bytes(wtype, K)
+    if rb < 0:
+        _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
+    if W.numel() * W.element_size() != N * rb:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=X.device)
+    else:
+        _device_tensor(out, "out")
+        if out.dtype != torch.float32 or tuple(out.shape) != (T, N):
+            raise ValueError("out must be contiguous float32 T x N")
+    _check(lib.retro_mul_mat_row_split(int(variant0), int(n_split), int(variant1), int(wtype), _ptr(W), _ptr(X),
+                                       _ptr(out), int(K), int(N), int(T), _stream_handle(stream)))
+    return out
 
 
 def mul_mat_variant_applies(variant: int, wtype: int, K: int, N: int, T: int) -> bool:

@@ -264,29 +264,35 @@ Plan plan_for(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
 // would feel. The plan depends on the type, the shape, W's and G's row
 // strides, G's orientation and the number of matrices, nothing else.
 struct PlanKey {
+    int op;  // 0: out_prod, 1: mul_mat
     int type;
     int64_t K, N, T, ldw, ldg, batches;
     bool gcols;
     bool operator==(const PlanKey& o) const {
-        return type == o.type && K == o.K && N == o.N && T == o.T && ldw == o.ldw && ldg == o.ldg &&
-               batches == o.batches && gcols == o.gcols;
+        return op == o.op && type == o.type && K == o.K && N == o.N && T == o.T && ldw == o.ldw &&
+               ldg == o.ldg && batches == o.batches && gcols == o.gcols;
     }
 };
 
-Plan cached_plan(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+template <typename Search>
+Plan cached(const PlanKey& key, Search search) {
     constexpr int kSlots = 4;
     thread_local PlanKey keys[kSlots];
     thread_local Plan plans[kSlots];
     thread_local int used = 0, next = 0;
-    const PlanKey key{type, K, N, T, s.ldw, s.ldg, s.batches(), s.gcols};
     for (int i = 0; i < used; ++i)
         if (keys[i] == key) return plans[i];
-    const Plan p = plan_for(type, K, N, T, s);
+    const Plan p = search();
     keys[next] = key;
     plans[next] = p;
     next = (next + 1) % kSlots;
     if (used < kSlots) ++used;
     return p;
+}
+
+Plan cached_plan(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    return cached(PlanKey{0, type, K, N, T, s.ldw, s.ldg, s.batches(), s.gcols},
+                  [&] { return plan_for(type, K, N, T, s); });
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -453,58 +459,133 @@ bool mm_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) 
     return false;
 }
 
-int mm_choose(int type, int64_t K, int64_t N, int64_t T) {
-    if (mm_variant_applies(RETRO_VARIANT_SKINNY, type, K, N, T)) return RETRO_VARIANT_SKINNY;
-    int best = -1;
-    double best_cost = 0;
+double mm_tile_cost(const MmTile& v, int64_t N, int64_t T) {
+    return double(cdiv(cdiv(T, v.bt) * cdiv(N, v.bn), kNumCUs)) * v.bt * v.bn * v.penalty;
+}
+
+// The tiled forward kernel of least cost (wave quantisation over 256 CUs).
+Choice mm_choose_tile(int type, int64_t K, int64_t N, int64_t T) {
+    Choice best{-1, 0.0};
     for (const auto& v : kMmTiles) {
         if (!mm_tile_applies(v, type, K, N, T)) continue;
-        const double cost = double(cdiv(cdiv(T, v.bt) * cdiv(N, v.bn), kNumCUs)) * v.bt * v.bn * v.penalty;
-        if (best < 0 || cost < best_cost) {
-            best = v.id;
-            best_cost = cost;
-        }
+        const double cost = mm_tile_cost(v, N, T);
+        if (best.id < 0 || cost < best.cost) best = {v.id, cost};
     }
+    return best;
+}
+
+int mm_choose(int type, int64_t K, int64_t N, int64_t T) {
+    if (mm_variant_applies(RETRO_VARIANT_SKINNY, type, K, N, T)) return RETRO_VARIANT_SKINNY;
+    int best = mm_choose_tile(type, K, N, T).id;
     if (best < 0 && mm_variant_applies(RETRO_VARIANT_SIMPLE, type, K, N, T)) best = RETRO_VARIANT_SIMPLE;
     return best < 0 ? RETRO_E_SHAPE : best;
 }
 
-int mul_mat_impl(int variant, int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
-                 void* stream) {
-    int rc = check_shape(type, K, N, T);
+// The forward's plan: as for out_prod, but over W's rows (Y's columns),
+// since Y[t][n] is complete in one tile. W rows [0, n_split) and the rest;
+// every tile is 128 rows of W wide, so a split point is a multiple of 128
+// and keeps the 16-byte alignment of W and Y. Measured on Q4_0 17408 x 5120,
+// T = 2048: 128 x 128 tiles on 16384 rows plus one round of 64 x 128 on
+// the last 1024, against 17 rounds of 64 x 128 (DESIGN's forward section).
+Plan mm_plan_for(int type, int64_t K, int64_t N, int64_t T) {
+    const int single = mm_choose(type, K, N, T);
+    Plan best{single, N, 0};
+    if (single <= 0 || single == RETRO_VARIANT_SKINNY || single == RETRO_VARIANT_SIMPLE || K == 0) return best;
+    const double one = mm_choose_tile(type, K, N, T).cost;
+    double best_cost = one;
+    for (const auto& v : kMmTiles) {
+        if (!mm_tile_applies(v, type, K, N, T)) continue;
+        const int64_t tiles_t = cdiv(T, v.bt);
+        int64_t g = kNumCUs, r = tiles_t % kNumCUs;
+        while (r) {
+            const int64_t t = g % r;
+            g = r;
+            r = t;
+        }
+        const int64_t step = kNumCUs / g;
+        for (int64_t c = step; c * v.bn < N; c += step) {
+            const int64_t n1 = c * v.bn;
+            const Choice tail = mm_choose_tile(type, K, N - n1, T);
+            if (tail.id < 0) continue;
+            const double cost = mm_tile_cost(v, n1, T) + tail.cost;
+            if (cost < best_cost) {
+                best = {v.id, n1, tail.id};
+                best_cost = cost;
+            }
+        }
+    }
+    if (best.k_split < N &&
+        (best_cost > kPlanMargin * one || (one - best_cost) * 2.0 * double(K) / kCuFlops < kPlanMinSaving))
+        return {single, N, 0};
+    return best;
+}
+
+Plan mm_cached_plan(int type, int64_t K, int64_t N, int64_t T) {
+    return cached(PlanKey{1, type, K, N, T, 0, 0, 1, false}, [&] { return mm_plan_for(type, K, N, T); });
+}
+
+int launch_typed_mm(int variant, int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                    int64_t ldy, hipStream_t st) {
+    switch (type) {
+        case RETRO_F32: return launch_mul_mat<RETRO_F32>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_F16: return launch_mul_mat<RETRO_F16>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_BF16: return launch_mul_mat<RETRO_BF16>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q8_0: return launch_mul_mat<RETRO_Q8_0>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q4_0: return launch_mul_mat<RETRO_Q4_0>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q4_1: return launch_mul_mat<RETRO_Q4_1>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q5_0: return launch_mul_mat<RETRO_Q5_0>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q5_1: return launch_mul_mat<RETRO_Q5_1>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_MXFP4: return launch_mul_mat<RETRO_MXFP4>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_NVFP4: return launch_mul_mat<RETRO_NVFP4>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q4_K: return launch_mul_mat<RETRO_Q4_K>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q5_K: return launch_mul_mat<RETRO_Q5_K>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q2_K: return launch_mul_mat<RETRO_Q2_K>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q3_K: return launch_mul_mat<RETRO_Q3_K>(variant, W, X, Y, K, N, T, ldy, st);
+        case RETRO_Q6_K: return launch_mul_mat<RETRO_Q6_K>(variant, W, X, Y, K, N, T, ldy, st);
+        default: return RETRO_E_TYPE;
+    }
+}
+
+// The launches of a forward plan: W rows and Y columns [0, n_split), then
+// the rest (each reads all of X).
+int run_mm_plan(const Plan& p, int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                hipStream_t st) {
+    const int64_t n1 = p.k_split;
+    int rc = launch_typed_mm(p.v0, type, W, X, Y, K, n1, T, N, st);
+    if (rc != RETRO_OK || n1 >= N) return rc;
+    const void* W1 = static_cast<const char*>(W) + n1 * row_bytes_of(type, K);
+    return launch_typed_mm(p.v1, type, W1, X, Y + n1, K, N - n1, T, N, st);
+}
+
+// Validation shared by the mul_mat entry points.
+int check_mm_call(int type, const void* W, const float* X, const float* Y, int64_t K, int64_t N, int64_t T,
+                  bool& empty) {
+    const int rc = check_shape(type, K, N, T);
     if (rc != RETRO_OK) return rc;
-    if (T == 0 || N == 0) return RETRO_OK;
+    empty = T == 0 || N == 0;
+    if (empty) return RETRO_OK;
     const int64_t w_bytes = N * row_bytes_of(type, K);
     const int64_t x_bytes = T * K * 4;
     const int64_t y_bytes = T * N * 4;
     if (!Y || (K > 0 && (!W || !X))) return RETRO_E_NULL;
     if (!aligned16(Y) || (K > 0 && (!aligned16(W) || !aligned16(X)))) return RETRO_E_ALIGN;
     if (overlap(Y, y_bytes, W, w_bytes) || overlap(Y, y_bytes, X, x_bytes)) return RETRO_E_ALIAS;
-    if (variant == RETRO_VARIANT_AUTO) {
-        variant = mm_choose(type, K, N, T);
-        if (variant < 0) return variant;
-    } else if (!mm_variant_applies(variant, type, K, N, T)) {
-        return RETRO_E_VARIANT;
-    }
+    return RETRO_OK;
+}
+
+int mul_mat_impl(int variant, int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                 void* stream) {
+    bool empty = false;
+    const int rc = check_mm_call(type, W, X, Y, K, N, T, empty);
+    if (rc != RETRO_OK || empty) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    switch (type) {
-        case RETRO_F32: return launch_mul_mat<RETRO_F32>(variant, W, X, Y, K, N, T, st);
-        case RETRO_F16: return launch_mul_mat<RETRO_F16>(variant, W, X, Y, K, N, T, st);
-        case RETRO_BF16: return launch_mul_mat<RETRO_BF16>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q8_0: return launch_mul_mat<RETRO_Q8_0>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q4_0: return launch_mul_mat<RETRO_Q4_0>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q4_1: return launch_mul_mat<RETRO_Q4_1>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q5_0: return launch_mul_mat<RETRO_Q5_0>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q5_1: return launch_mul_mat<RETRO_Q5_1>(variant, W, X, Y, K, N, T, st);
-        case RETRO_MXFP4: return launch_mul_mat<RETRO_MXFP4>(variant, W, X, Y, K, N, T, st);
-        case RETRO_NVFP4: return launch_mul_mat<RETRO_NVFP4>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q4_K: return launch_mul_mat<RETRO_Q4_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q5_K: return launch_mul_mat<RETRO_Q5_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q2_K: return launch_mul_mat<RETRO_Q2_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q3_K: return launch_mul_mat<RETRO_Q3_K>(variant, W, X, Y, K, N, T, st);
-        case RETRO_Q6_K: return launch_mul_mat<RETRO_Q6_K>(variant, W, X, Y, K, N, T, st);
-        default: return RETRO_E_TYPE;
+    if (variant == RETRO_VARIANT_AUTO) {
+        const Plan p = mm_cached_plan(type, K, N, T);
+        if (p.v0 < 0) return p.v0;
+        return run_mm_plan(p, type, W, X, Y, K, N, T, st);
     }
+    if (!mm_variant_applies(variant, type, K, N, T)) return RETRO_E_VARIANT;
+    return launch_typed_mm(variant, type, W, X, Y, K, N, T, N, st);
 }
 
 }  // namespace
@@ -523,7 +604,37 @@ int retro_mul_mat_variant(int variant, int type, const void* W, const float* X, 
 
 int retro_mul_mat_choice(int type, int64_t K, int64_t N, int64_t T) {
     const int rc = check_shape(type, K, N, T);
-    return rc != RETRO_OK ? rc : mm_choose(type, K, N, T);
+    return rc != RETRO_OK ? rc : mm_cached_plan(type, K, N, T).v0;
+}
+
+int retro_mul_mat_plan(int type, int64_t K, int64_t N, int64_t T, int32_t* variant0, int64_t* n_split,
+                       int32_t* variant1) {
+    const int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    if (!variant0 || !n_split || !variant1) return RETRO_E_NULL;
+    const Plan p = mm_cached_plan(type, K, N, T);
+    if (p.v0 < 0) return p.v0;
+    *variant0 = p.v0;
+    *n_split = p.k_split;
+    *variant1 = p.k_split < N ? p.v1 : 0;
+    return p.k_split < N ? 2 : 1;
+}
+
+int retro_mul_mat_row_split(int variant0, int64_t n_split, int variant1, int type, const void* W, const float* X,
+                            float* Y, int64_t K, int64_t N, int64_t T, void* stream) {
+    bool empty = false;
+    const int rc = check_mm_call(type, W, X, Y, K, N, T, empty);
+    if (rc != RETRO_OK) return rc;
+    if (n_split <= 0 || n_split >= N) return RETRO_E_SHAPE;
+    if (n_split % 4 || (n_split * row_bytes_of(type, K)) % 16) return RETRO_E_ALIGN;
+    Plan p{variant0, n_split, variant1};
+    if (p.v0 == RETRO_VARIANT_AUTO) p.v0 = mm_choose(type, K, n_split, T);
+    if (p.v1 == RETRO_VARIANT_AUTO) p.v1 = mm_choose(type, K, N - n_split, T);
+    if (p.v0 <= 0 || p.v1 <= 0 || !mm_variant_applies(p.v0, type, K, n_split, T) ||
+        !mm_variant_applies(p.v1, type, K, N - n_split, T))
+        return RETRO_E_VARIANT;
+    if (empty) return RETRO_OK;
+    return run_mm_plan(p, type, W, X, Y, K, N, T, static_cast<hipStream_t>(stream));
 }
 
 int retro_mul_mat_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {

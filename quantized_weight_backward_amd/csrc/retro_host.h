@@ -98,9 +98,10 @@ inline int launch_status() { return hipGetLastError() == hipSuccess ? RETRO_OK :
 template <int TYPE>
 int launch_out_prod(int variant, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
                     const Strides& s, hipStream_t st);
+// Y's rows are ldy floats apart (ldy >= N: a column range of a wider Y).
 template <int TYPE>
 int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
-                   hipStream_t st);
+                   int64_t ldy, hipStream_t st);
 template <int TYPE>
 int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t st);
 

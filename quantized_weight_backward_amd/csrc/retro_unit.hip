@@ -168,7 +168,8 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
 }
 
 template <int TYPE, int WA, int WB, int CT, int NC = 4>
-int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, hipStream_t st) {
+int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T, int64_t ldy,
+              hipStream_t st) {
     using S = MmShape<TYPE, WA, WB, CT, NC>;
     MmArgs a;
     a.W = static_cast<const uint8_t*>(W);
@@ -179,7 +180,7 @@ int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int
     a.T = int(T);
     a.pitch = row_bytes_of(TYPE, K);
     a.ldx = K;
-    a.ldy = N;
+    a.ldy = ldy;
     a.tiles_t = int(cdiv(T, S::BT));
     a.tiles_n = int(cdiv(N, S::BK));
     a.group = group_height(a.tiles_t, a.tiles_n, S::kResident, 4.0 * T * K, double(N) * a.pitch);
@@ -189,7 +190,8 @@ int launch_mm(const void* W, const float* X, float* Y, int64_t K, int64_t N, int
     return launch_status();
 }
 
-MmSimpleArgs mm_simple_args(int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T) {
+MmSimpleArgs mm_simple_args(int type, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
+                            int64_t ldy) {
     MmSimpleArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.X = X;
@@ -199,7 +201,7 @@ MmSimpleArgs mm_simple_args(int type, const void* W, const float* X, float* Y, i
     a.T = int(T);
     a.pitch = row_bytes_of(type, K);
     a.ldx = K;
-    a.ldy = N;
+    a.ldy = ldy;
     a.wide = (K % 4 == 0) ? 1 : 0;
     return a;
 }
@@ -240,21 +242,21 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
 
 template <int TYPE>
 int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
-                   hipStream_t st) {
+                   int64_t ldy, hipStream_t st) {
     switch (variant) {
-        case RETRO_VARIANT_WS_256x128: return launch_mm<TYPE, 2, 2, 4, 8>(W, X, Y, K, N, T, st);
-        case RETRO_VARIANT_WS_128x128: return launch_mm<TYPE, 2, 2, 2>(W, X, Y, K, N, T, st);
-        case RETRO_VARIANT_WS_64x128: return launch_mm<TYPE, 1, 2, 2>(W, X, Y, K, N, T, st);
-        case RETRO_VARIANT_WS_32x128: return launch_mm<TYPE, 1, 1, 1>(W, X, Y, K, N, T, st);
+        case RETRO_VARIANT_WS_256x128: return launch_mm<TYPE, 2, 2, 4, 8>(W, X, Y, K, N, T, ldy, st);
+        case RETRO_VARIANT_WS_128x128: return launch_mm<TYPE, 2, 2, 2>(W, X, Y, K, N, T, ldy, st);
+        case RETRO_VARIANT_WS_64x128: return launch_mm<TYPE, 1, 2, 2>(W, X, Y, K, N, T, ldy, st);
+        case RETRO_VARIANT_WS_32x128: return launch_mm<TYPE, 1, 1, 1>(W, X, Y, K, N, T, ldy, st);
         case RETRO_VARIANT_SIMPLE: {
-            const MmSimpleArgs a = mm_simple_args(TYPE, W, X, Y, K, N, T);
+            const MmSimpleArgs a = mm_simple_args(TYPE, W, X, Y, K, N, T, ldy);
             clear_last_error();
             hipLaunchKernelGGL((mul_mat_simple_kernel<TYPE>), dim3(unsigned(cdiv(T * N, 256))), dim3(256), 0, st,
                                a);
             return launch_status();
         }
         case RETRO_VARIANT_SKINNY: {
-            const MmSimpleArgs a = mm_simple_args(TYPE, W, X, Y, K, N, T);
+            const MmSimpleArgs a = mm_simple_args(TYPE, W, X, Y, K, N, T, ldy);
             clear_last_error();
             hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE>), dim3(unsigned(cdiv(N, 16))), dim3(1024), 0, st, a);
             return launch_status();
@@ -281,7 +283,7 @@ int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t 
 
 template int launch_out_prod<RETRO_UNIT_TYPE>(int, const void*, const float*, float*, int64_t, int64_t, int64_t,
                                               const Strides&, hipStream_t);
-template int launch_mul_mat<RETRO_UNIT_TYPE>(int, const void*, const float*, float*, int64_t, int64_t, int64_t,
+template int launch_mul_mat<RETRO_UNIT_TYPE>(int, const void*, const float*, float*, int64_t, int64_t, int64_t, int64_t,
                                              hipStream_t);
 template int launch_dequant<RETRO_UNIT_TYPE>(const void*, float*, int64_t, int64_t, hipStream_t);
 

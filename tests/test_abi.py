@@ -214,6 +214,59 @@ def test_plan_is_the_same_from_the_cache():
         assert [q.choice(*sh) for sh in shapes] == [p[0] for p in first]
 
 
+def test_mul_mat_plan():
+    """The forward splits W's rows the same way: 128 x 128 tiles over 16384
+    rows (8 whole rounds at T = 2048) and one round of 64 x 128 over the
+    rest, where one launch would run 17 rounds of 64 x 128."""
+    for wtype in (q.Q4_0, q.MXFP4, q.Q8_0):
+        assert q.mul_mat_plan(wtype, 5120, 17408, 2048) == (q.VARIANT_WS_128x128, 16384, q.VARIANT_WS_64x128)
+        assert q.mul_mat_choice(wtype, 5120, 17408, 2048) == q.VARIANT_WS_128x128
+    for args, v in (((q.Q4_K, 4096, 14336, 4096), q.VARIANT_WS_128x128), ((q.F32, 4096, 4096, 512), q.VARIANT_WS_64x128),
+                    ((q.Q4_K, 14336, 4096, 16), q.VARIANT_SKINNY), ((q.F16, 301, 64, 100), q.VARIANT_SIMPLE)):
+        assert q.mul_mat_plan(*args) == (v, args[2], 0), args
+    v0, v1, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    assert q.lib.retro_mul_mat_plan(q.Q4_0, 5120, 17408, 2048, ctypes.byref(v0), None, ctypes.byref(v1)) == q.E_NULL
+    # the two ops' plans are kept apart in the per-thread cache
+    for _ in range(2):
+        assert q.plan(q.Q4_0, 5120, 17408, 2048) == (q.VARIANT_WS_128x256, 4096, q.VARIANT_WS2_64x128)
+        assert q.mul_mat_plan(q.Q4_0, 5120, 17408, 2048) == (q.VARIANT_WS_128x128, 16384, q.VARIANT_WS_64x128)
+
+
+def test_mul_mat_plan_invariants_over_shapes():
+    split = 0
+    for wtype in q.TYPES.values():
+        blk = {q.F32: 1, q.F16: 1, q.BF16: 1, q.NVFP4: 64}.get(wtype, 256 if wtype in KQUANT_TYPES else 32)
+        for K, N, T in itertools.product((1024, 4096, 5120), (4096, 11008, 14336, 17408), (17, 512, 2048, 4096)):
+            if K % blk:
+                continue
+            v0, ns, v1 = q.mul_mat_plan(wtype, K, N, T)
+            assert q.mul_mat_choice(wtype, K, N, T) == v0
+            if ns == N:
+                assert v1 == 0
+                continue
+            split += 1
+            bt, bn = tile_dims(q.VARIANT_NAMES[v0])
+            assert 0 < ns < N and ns % bn == 0 and (ns * q.row_bytes(wtype, K)) % 16 == 0
+            assert (-(-T // bt) * (ns // bn)) % 256 == 0, (wtype, K, N, T, ns)
+            assert q.mul_mat_variant_applies(v0, wtype, K, ns, T) and q.mul_mat_variant_applies(v1, wtype, K, N - ns, T)
+    assert split > 10
+
+
+def test_mul_mat_row_split_validation():
+    rs = q.lib.retro_mul_mat_row_split
+    W, X, Y = 0x100000, 0x2000000, 0x3000000
+    a, b = q.VARIANT_WS_128x128, q.VARIANT_WS_64x128
+    assert rs(a, 128, b, q.Q4_0, W, X, None, 512, 256, 40, None) == q.E_NULL
+    assert rs(a, 0, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_SHAPE
+    assert rs(a, 256, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_SHAPE
+    assert rs(a, 126, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_ALIGN    # not a multiple of 4 rows
+    assert rs(a, 100, b, q.Q8_0, W, X, Y, 416, 256, 40, None) == q.E_ALIGN    # 100 rows of 442 bytes
+    assert rs(q.VARIANT_SKINNY, 128, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_VARIANT  # T > 16
+    assert rs(42, 128, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_VARIANT
+    assert rs(a, 128, b, 5, W, X, Y, 512, 256, 40, None) == q.E_TYPE
+    assert rs(a, 128, b, q.Q4_0, W, X, Y, 512, 256, 0, None) == q.OK         # nothing to compute
+
+
 def test_views_plan():
     """Batches count toward the rounds: 16 matrices of Q4_0 200 x 1280 with
     N = 2048 fill whole rounds of 128 x 128 tiles on 1024 columns."""

@@ -127,12 +127,48 @@ def test_mul_mat_edges(q):
     assert np.isfinite(a).all() and np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["q4_k_n14336_k4096_t4096", "q4_0_n17408_k5120_t2048"])
+# (type, K, N, T, n_split, variant0, variant1): ragged parts, every kernel
+# family, split points that keep W's and Y's 16-byte alignment
+ROW_SPLITS = [
+    (wl.Q4_0, 352, 300, 200, 256, "ws_128x128", "ws_64x128"),
+    (wl.Q4_K, 768, 260, 67, 128, "ws_32x128", "ws_128x128"),
+    (wl.F32, 300, 200, 130, 128, "ws_256x128", "simple"),
+    (wl.MXFP4, 352, 260, 16, 128, "skinny", "skinny"),
+    (wl.BF16, 520, 136, 90, 4, "simple", "ws_64x128"),
+    (wl.Q8_0, 416, 200, 40, 104, "auto", "auto"),
+    (wl.NVFP4, 320, 160, 33, 128, "ws_128x128", "ws_32x128"),
+]
+
+
+@pytest.mark.parametrize("wtype,K,N,T,ns,v0,v1", ROW_SPLITS)
+def test_mul_mat_row_split_matches_parts_and_oracle(q, wtype, K, N, T, ns, v0, v1):
+    """retro_mul_mat_row_split: the whole Y (NaN-prefilled) within the bars of
+    the oracle, and each column range of Y bit-identical to its variant run
+    alone on those rows of W."""
+    c = wl.make_case(wtype, N, K, 1, seed=900 + N)
+    x = wl.make_input(T, K, seed=901 + T)
+    out = torch.full((T, N), float("nan"), device="cuda")
+    q.mul_mat_row_split(wtype, dev(c["W"]), dev(x), N, vid(q, v0), ns, vid(q, v1), out=out)
+    torch.cuda.synchronize()
+    y = out.cpu().numpy()
+    _, acc, ab = oracle.mul_mat(wtype, c["W"], x, K, nthreads=ORACLE_THREADS)
+    check_close(y, acc, ab, f"{v0}+{v1}")
+    rows = np.asarray(c["W"]).reshape(N, wl.row_bytes(wtype, K))
+    for part, v, cols in ((rows[:ns], v0, slice(0, ns)), (rows[ns:], v1, slice(ns, N))):
+        n = part.shape[0]
+        assert v == "auto" or q.mul_mat_variant_applies(vid(q, v), wtype, K, n, T), v
+        alone = run(q, wtype, np.ascontiguousarray(part), x, n, v)
+        assert np.array_equal(y[:, cols].view(np.uint32), alone.view(np.uint32)), v
+
+
+@pytest.mark.parametrize("name", ["q4_k_n14336_k4096_t4096", "q4_0_n17408_k5120_t2048", "mxfp4_n17408_k5120_t2048"])
 def test_mul_mat_full_size_sampled_rows(q, name):
     """The forward at the OUT_PROD workloads' weights (y = x W^T with x of
-    T x K), checked on sampled t rows the oracle computes one by one."""
+    T x K), checked on sampled t rows the oracle computes one by one; the
+    17408-row weights run their two-launch plan."""
     c = wl.workload(name)
     K, N, T = c["K"], c["N"], c["T"]
+    print(f"mul_mat {name}: {q.mul_mat_plan_names(c['type'], K, N, T)}", flush=True)
     x = wl.make_input(T, K, seed=1100)
     y = q.mul_mat(c["type"], dev(c["W"]), dev(x), N=N)
     again = q.mul_mat(c["type"], dev(c["W"]), dev(x), N=N)
