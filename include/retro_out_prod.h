@@ -195,6 +195,10 @@ const char *retro_strerror(int code);
  *   RETRO_VARIANT_AUTO      what retro_out_prod runs (one variant, or two over
  *                           column ranges of dst: retro_out_prod_plan)
  *   RETRO_VARIANT_SKINNY    one pass over W, all of n per workgroup; T <= 16
+ *                           (8 or 16 waves per workgroup, chosen by type
+ *                           and T; the two are summed in different orders)
+ *   RETRO_VARIANT_SKINNY_8, RETRO_VARIANT_SKINNY_16  the skinny kernel with
+ *                           that many waves per workgroup
  *   RETRO_VARIANT_TILE_*    tiled F32-MFMA kernel, tile = rows of T x columns
  *                           of K per workgroup (256-column tiles need K tiles
  *                           that are whole K-quant super-blocks; the K-quants
@@ -269,7 +273,9 @@ enum {
     RETRO_VARIANT_SPLIT_128x256 = 16,
     RETRO_VARIANT_SPLIT_128x128 = 17,
     RETRO_VARIANT_WS_256x256 = 18,
-    RETRO_VARIANT_WS_256x128 = 19
+    RETRO_VARIANT_WS_256x128 = 19,
+    RETRO_VARIANT_SKINNY_8 = 20,
+    RETRO_VARIANT_SKINNY_16 = 21
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the

@@ -52,6 +52,8 @@ VARIANT_SPLIT_128x256 = 16
 VARIANT_SPLIT_128x128 = 17
 VARIANT_WS_256x256 = 18
 VARIANT_WS_256x128 = 19
+VARIANT_SKINNY_8 = 20
+VARIANT_SKINNY_16 = 21
 VARIANT_NAMES = {
     VARIANT_SKINNY: "skinny", VARIANT_TILE_128x128: "tile_128x128", VARIANT_TILE_128x256: "tile_128x256",
     VARIANT_TILE_64x128: "tile_64x128", VARIANT_TILE_64x64: "tile_64x64", VARIANT_TILE_64x256: "tile_64x256",
@@ -59,7 +61,7 @@ VARIANT_NAMES = {
     VARIANT_WS_64x128: "ws_64x128", VARIANT_WS_32x256: "ws_32x256", VARIANT_WS_32x128: "ws_32x128",
     VARIANT_WS2_64x128: "ws2_64x128", VARIANT_SIMPLE: "simple", VARIANT_SPLIT_128x256: "split_128x256",
     VARIANT_SPLIT_128x128: "split_128x128", VARIANT_WS_256x256: "ws_256x256",
-    VARIANT_WS_256x128: "ws_256x128",
+    VARIANT_WS_256x128: "ws_256x128", VARIANT_SKINNY_8: "skinny_8", VARIANT_SKINNY_16: "skinny_16",
 }
 
 LIB_PATH = _build.LIB_PATH

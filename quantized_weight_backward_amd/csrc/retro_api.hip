@@ -307,7 +307,8 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 // checked).
 bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     if (variant == RETRO_VARIANT_AUTO) return choose(type, K, N, T, s) > 0;
-    if (variant == RETRO_VARIANT_SKINNY) return skinny_applies(type, K, N, T, s);
+    if (variant == RETRO_VARIANT_SKINNY || variant == RETRO_VARIANT_SKINNY_8 || variant == RETRO_VARIANT_SKINNY_16)
+        return skinny_applies(type, K, N, T, s);
     if (variant == RETRO_VARIANT_SPLIT_128x256) {
         // the 128 x 256 producer/consumer tile's limits, for G by rows
         constexpr TileVariant tile{RETRO_VARIANT_SPLIT_128x256, 128, 256, 1.0, true};

@@ -15,12 +15,6 @@
 #error "RETRO_UNIT_TYPE (a GGUF weight type id) must be defined"
 #endif
 
-// Waves per skinny workgroup (each CU runs one skinny workgroup at the
-// benchmarked shapes, so this sets the waves per SIMD available to hide
-// memory latency).
-#ifndef RETRO_SKINNY_WAVES
-#define RETRO_SKINNY_WAVES 16
-#endif
 
 namespace retro {
 namespace host {
@@ -140,10 +134,33 @@ int launch_split(const void* W, const float* G, float* dst, int64_t K, int64_t N
     return launch_status();
 }
 
+// Waves per skinny workgroup. Each CU runs one skinny workgroup (64 columns
+// of dst over all of n), so this is the waves per SIMD, and 16 n rows per
+// group go to the waves in turn. Measured on MI355X at N = 4096, K = 14336
+// (interleaved in one process, 8 rounds of 40 launches): eight waves, each
+// walking twice the groups, take 0.94-0.95x the time of sixteen at T = 16
+// for Q4_0, Q4_1, Q5_0, MXFP4 and Q5_K, 0.96-0.98x for Q4_K, Q6_K, Q8_0,
+// Q5_1, F16 and BF16, and the same for Q3_K and F32; at T = 8 and 4, 0.94-0.95x
+// for Q4_0 and Q6_K and 0.98 for BF16. Sixteen stay faster for Q2_K and NVFP4
+// (by 2-3%) and for Q4_K below T = 12 (1-4%).
+int skinny_waves(int type, int64_t T) {
+    if (type == RETRO_Q2_K || type == RETRO_NVFP4) return 16;
+    if (type == RETRO_Q4_K && T < 12) return 16;
+    return 8;
+}
+
+template <int TYPE, int kWaves>
+void launch_skinny_waves(const SkinnyArgs& a, dim3 grid, hipStream_t st) {
+    const dim3 block(kWaves * 64);
+    if (a.wide && a.gvec)
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false>), grid, block, 0, st, a);
+}
+
 template <int TYPE>
 int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
-                  hipStream_t st) {
-    constexpr int kWaves = RETRO_SKINNY_WAVES;
+                  int waves, hipStream_t st) {
     SkinnyArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.G = G;
@@ -158,12 +175,12 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     a.gvec = (s.gcols || s.ldg % 4 == 0) ? 1 : 0;
     a.gcols = s.gcols ? 1 : 0;
     a.batch = batch_args(s);
-    const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches())), block(kWaves * 64);
+    const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches()));
     clear_last_error();
-    if (a.wide && a.gvec)
-        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true>), grid, block, 0, st, a);
+    if (waves == 8)
+        launch_skinny_waves<TYPE, 8>(a, grid, st);
     else
-        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false>), grid, block, 0, st, a);
+        launch_skinny_waves<TYPE, 16>(a, grid, st);
     return launch_status();
 }
 
@@ -212,7 +229,9 @@ template <int TYPE>
 int launch_out_prod(int variant, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
                     const Strides& s, hipStream_t st) {
     switch (variant) {
-        case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, st);
+        case RETRO_VARIANT_SKINNY: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, skinny_waves(TYPE, T), st);
+        case RETRO_VARIANT_SKINNY_8: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, 8, st);
+        case RETRO_VARIANT_SKINNY_16: return launch_skinny<TYPE>(W, G, dst, K, N, T, s, 16, st);
         case RETRO_VARIANT_TILE_128x256: return launch_tile<TYPE, 2, 4, 2, 2>(W, G, dst, K, N, T, s, st);
         case RETRO_VARIANT_TILE_64x256: return launch_tile<TYPE, 1, 4, 2, 2>(W, G, dst, K, N, T, s, st);
         case RETRO_VARIANT_WS_256x256: return launch_ws<TYPE, 4, 2, 2, 1, 8>(W, G, dst, K, N, T, s, st);

@@ -38,7 +38,7 @@ pytestmark = pytest.mark.gpu
 TYPES = [wl.F32, wl.F16, wl.BF16, wl.Q8_0, wl.Q4_0, wl.Q4_1, wl.Q5_0, wl.Q5_1, wl.MXFP4, wl.NVFP4, wl.Q2_K, wl.Q3_K,
          wl.Q4_K, wl.Q5_K, wl.Q6_K]
 KQUANTS = (wl.Q2_K, wl.Q3_K, wl.Q4_K, wl.Q5_K, wl.Q6_K)
-OUT_PROD_VARIANTS = ["skinny", "tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
+OUT_PROD_VARIANTS = ["skinny", "skinny_8", "skinny_16", "tile_128x128", "tile_128x256", "tile_64x128", "tile_64x64", "tile_64x256",
                      "ws_256x256", "ws_128x256", "ws_64x256", "ws_128x128", "ws_64x128", "ws_32x256", "ws_32x128",
                      "ws2_64x128",
                      "split_128x256", "split_128x128"]
