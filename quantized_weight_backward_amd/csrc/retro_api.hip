@@ -215,6 +215,18 @@ bool split_point_ok(int type, int64_t k) {
 // 1024 in 0.62 ms, against 2.99 ms for one launch). The plan is taken when
 // its estimated cost is at least 1% lower and saves at least ~5 us of
 // matrix time, which pays for the second launch.
+// The smallest count c of column tiles for which tiles_t * c tiles fill
+// whole rounds over the CUs: kNumCUs / gcd(tiles_t, kNumCUs).
+int64_t whole_round_step(int64_t tiles_t) {
+    int64_t g = kNumCUs, r = tiles_t % kNumCUs;
+    while (r) {
+        const int64_t t = g % r;
+        g = r;
+        r = t;
+    }
+    return kNumCUs / g;
+}
+
 constexpr double kPlanMargin = 0.99;
 constexpr double kCuFlops = 157.3e12 / kNumCUs * 0.8;  // F32 FLOP/s of one CU at a typical tile efficiency
 constexpr double kPlanMinSaving = 5e-6;                // seconds
@@ -231,15 +243,7 @@ Plan plan_for(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
         if (!v.ws || v.id == RETRO_VARIANT_WS2_64x128 || !auto_takes(v, type)) continue;
         if (!tile_applies(v, type, K, N, T, s)) continue;
         const int64_t tiles_t = cdiv(T, v.bt) * s.batches();
-        // whole rounds: tiles_t * c a multiple of kNumCUs, i.e. c a multiple
-        // of kNumCUs / gcd(tiles_t, kNumCUs)
-        int64_t g = kNumCUs, r = tiles_t % kNumCUs;
-        while (r) {
-            const int64_t t = g % r;
-            g = r;
-            r = t;
-        }
-        const int64_t step = kNumCUs / g;
+        const int64_t step = whole_round_step(tiles_t);
         for (int64_t c = step; c * v.bk < K; c += step) {
             const int64_t k1 = c * v.bk;
             if (!split_point_ok(type, k1)) continue;
@@ -497,13 +501,7 @@ Plan mm_plan_for(int type, int64_t K, int64_t N, int64_t T) {
     for (const auto& v : kMmTiles) {
         if (!mm_tile_applies(v, type, K, N, T)) continue;
         const int64_t tiles_t = cdiv(T, v.bt);
-        int64_t g = kNumCUs, r = tiles_t % kNumCUs;
-        while (r) {
-            const int64_t t = g % r;
-            g = r;
-            r = t;
-        }
-        const int64_t step = kNumCUs / g;
+        const int64_t step = whole_round_step(tiles_t);
         for (int64_t c = step; c * v.bn < N; c += step) {
             const int64_t n1 = c * v.bn;
             const Choice tail = mm_choose_tile(type, K, N - n1, T);
