@@ -144,8 +144,9 @@ def tile_dims(name):
 def test_plan():
     """Two launches over column ranges of dst where one tile would leave the
     last round over the 256 CUs partly empty and a larger tile fills whole
-    rounds (measured faster in every case listed: DESIGN's kernel-choice
-    section); one launch elsewhere."""
+    rounds (each listed plan measured faster on MI355X than the one launch it
+    replaces, e.g. Q4_0 17408 x 5120 at T = 2048: 2.77 against 2.98 ms); one
+    launch elsewhere."""
     two = {
         (q.Q4_0, 5120, 17408, 2048): (q.VARIANT_WS_128x256, 4096, q.VARIANT_WS2_64x128),
         (q.Q4_K, 14336, 4096, 4096): (q.VARIANT_WS_128x256, 2048, q.VARIANT_WS_256x256),
