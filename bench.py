@@ -154,7 +154,7 @@ def read_traffic(tag: str):
     return read_profile_value(tag, "hbm_bytes_per_launch")
 
 
-BENCH_PROFILE_ARGS = "--steps 20 --warmup 5 --reps 20 --no-cpu-baseline"  # the step loop as the driver runs it
+BENCH_PROFILE_ARGS = "--steps 20 --warmup 5 --reps 20 --no-cpu-baseline"  # the default step loop
 COUNTER_ARGS = "--steps 3 --warmup 1 --reps 3 --min-ms 0 --no-cpu-baseline"
 PROFILE_WARMUP = 5  # launches of each kernel dropped from a trace summary (the bench's warm-up steps)
 PROFILE_STEPS = 20  # the timed steps that follow them
