@@ -83,8 +83,9 @@
  * memory (no dequantized copy of W exists at any size, so the scratch
  * budget of the prior sliced design - Retrograd CUDA status, sections
  * "Building" and "Limitations" - is zero) and never falls back to the CPU:
- * an unsupported call returns an error. The library holds no mutable global
- * state; calls are thread-safe.
+ * an unsupported call returns an error. The library's only mutable state is
+ * a small per-thread (thread-local) cache of recent launch plans; calls are
+ * thread-safe.
  *
  * Errors: functions returning int return RETRO_OK (0) or a negative code;
  * nothing throws across the ABI; retro_strerror names a code.
