@@ -14,6 +14,7 @@ package raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 # torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
@@ -174,6 +175,7 @@ def strerror(code: int) -> str:
     return lib.retro_strerror(int(code)).decode()
 
 
+@functools.lru_cache(maxsize=256)
 def row_bytes(wtype: int, K: int) -> int:
     return int(lib.retro_row_bytes(int(wtype), int(K)))
 
@@ -225,9 +227,18 @@ def _check(code: int) -> None:
         raise RetroError(code)
 
 
+# The current stream's handle without building a torch Stream object per call
+# (torch's raw accessor, when this torch has it).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_current_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream_handle(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return int(s.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    if _raw_stream is not None and _current_device is not None:
+        return int(_raw_stream(_current_device()))
+    return int(torch.cuda.current_stream().cuda_stream)
 
 
 def _ptr(t) -> int | None:
@@ -276,7 +287,7 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
         if W.dtype != torch.uint8 or W.shape[0] != N or W.shape[1] < rb:
             raise ValueError(f"a strided W must be a uint8 view of N rows of at least {rb} bytes")
         ldw = _row_stride(W, "W")
-    sgt, sgn = _g_strides(G.unsqueeze(0).unsqueeze(0))
+    sgt, sgn = _g_strides2(G)
     if out is None:
         out = torch.empty((T, K), dtype=torch.float32, device=G.device)
     else:
@@ -336,6 +347,17 @@ def _matrix_strides(t, rows, name):
         raise ValueError(f"{name} must have contiguous rows")
     ld = int(t.stride(2)) if t.shape[2] > 1 else rows
     return ld, (int(t.stride(1)) if t.shape[1] > 1 else 0), (int(t.stride(0)) if t.shape[0] > 1 else 0)
+
+
+def _g_strides2(G):
+    """_g_strides of one T x N matrix, read from the 2-D view itself."""
+    T, N = G.shape
+    st, sn = G.stride()
+    if N <= 1 or sn == 1:
+        return (st if T > 1 else max(N, 1)), 1
+    if T <= 1 or st == 1:
+        return 1, sn
+    raise ValueError("G must have contiguous rows or contiguous columns")
 
 
 def _g_strides(G4):
