@@ -193,7 +193,7 @@ CASE_TRACES = {
     "split128_bf16_n4096_k4096_t512": ("dense_n4096_k4096_t512", "bf16", "out_prod", "split_128x128",
                                        "void retro::out_prod_split_kernel<30>"),
     "mulmat_skinny_q4_k_n4096_k14336_t16": ("q4_k_n4096_k14336_t16", "", "mul_mat", "skinny",
-                                            "void retro::mul_mat_skinny_kernel<12>"),
+                                            "void retro::mul_mat_skinny_kernel<12,"),
 }
 CASE_WARMUP = 2  # launches --profile-case makes before its timed ones
 

@@ -453,7 +453,7 @@ __global__ __launch_bounds__((MmShape<TYPE, WA, WB, CT, NC>::kThreads),
     ws_consume<S, WA, WB, 1>(lds_all, tid, wave, nloc, t0, n0, T, N, args.Y, args.ldy);
 }
 
-// mul_mat for T <= 16: one workgroup (16 waves) per 16 rows of W over all
+// mul_mat for T <= 16: one workgroup (NW = 8 or 16 waves) per 16 rows of W over all
 // of k, v_mfma_f32_16x16x4_f32 with M = t, N = W row, K = 4 steps of k.
 // Iteration g of a wave covers k = 64 g .. 64 g + 63: lane l decodes the 16
 // elements 64 g + 16 (l / 16) .. + 15 of row n0 + l % 16 (one MmCodec unit,
@@ -465,11 +465,11 @@ __global__ __launch_bounds__((MmShape<TYPE, WA, WB, CT, NC>::kThreads),
 // MFMA layout. The next iteration's loads are issued before the current one
 // is decoded. Partial sums are added over waves in increasing wave order in
 // LDS.
-template <int TYPE>
-__global__ __launch_bounds__(1024) void mul_mat_skinny_kernel(MmSimpleArgs a) {
+template <int TYPE, int NW>
+__global__ __launch_bounds__(NW * 64) void mul_mat_skinny_kernel(MmSimpleArgs a) {
+    static_assert(NW >= 4, "the final sum uses 256 threads");
     using C = MmCodec<TYPE>;
     using F = Format<TYPE>;
-    constexpr int NW = 16;
     constexpr int XP = 68;  // floats per t row of a wave's x tile (64 + 4: conflict-free reads)
     __shared__ __attribute__((aligned(16))) float part[NW * 256];
     __shared__ __attribute__((aligned(16))) float xtile[NW * 16 * XP];

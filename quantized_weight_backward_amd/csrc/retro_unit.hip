@@ -277,7 +277,15 @@ int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t
         case RETRO_VARIANT_SKINNY: {
             const MmSimpleArgs a = mm_simple_args(TYPE, W, X, Y, K, N, T, ldy);
             clear_last_error();
-            hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE>), dim3(unsigned(cdiv(N, 16))), dim3(1024), 0, st, a);
+            // the out_prod skinny kernel's wave rule; measured on the forward at
+            // T = 16: eight waves 0.96-0.98x the time of sixteen for Q4_K, Q6_K,
+            // Q4_0 and Q8_0 at N = 4096, K = 14336 (0.83x at N = 14336, K =
+            // 4096), 1.007x for Q2_K, 1.025x for Q4_K at T = 4
+            if (skinny_waves(TYPE, T) == 8)
+                hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 8>), dim3(unsigned(cdiv(N, 16))), dim3(512), 0, st, a);
+            else
+                hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 16>), dim3(unsigned(cdiv(N, 16))), dim3(1024), 0, st,
+                                   a);
             return launch_status();
         }
         default: return RETRO_E_VARIANT;
