@@ -6,7 +6,9 @@ import ctypes
 import glob
 import itertools
 import os
+import random
 import re
+import threading
 
 import pytest
 
@@ -213,6 +215,34 @@ def test_plan_is_the_same_from_the_cache():
     for _ in range(3):
         assert [q.plan(*sh) for sh in reversed(shapes)] == first[::-1]
         assert [q.choice(*sh) for sh in shapes] == [p[0] for p in first]
+
+
+def test_plans_from_many_threads():
+    """The plan cache is per thread: eight threads asking for interleaved
+    shapes at once (ctypes releases the GIL around each call) all get the
+    plans one thread gets alone."""
+    shapes = [(q.Q4_0, 5120, 17408, 2048), (q.Q4_K, 14336, 4096, 4096), (q.Q8_0, 256, 128, 64),
+              (q.F32, 4096, 4096, 512), (q.Q4_K, 4352, 4096, 4096), (q.MXFP4, 5120, 17408, 2048),
+              (q.Q4_K, 14336, 4096, 16), (q.F16, 11008, 4096, 4096), (q.Q6_K, 11008, 4096, 100)]
+    want = [(q.plan(*sh), q.mul_mat_plan(*sh)) for sh in shapes]
+    errors = []
+
+    def worker(seed):
+        order = list(range(len(shapes)))
+        random.Random(seed).shuffle(order)
+        for _ in range(200):
+            for i in order:
+                got = (q.plan(*shapes[i]), q.mul_mat_plan(*shapes[i]))
+                if got != want[i]:
+                    errors.append((seed, shapes[i], got, want[i]))
+                    return
+
+    threads = [threading.Thread(target=worker, args=(s,)) for s in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:3]
 
 
 def test_mul_mat_plan():
