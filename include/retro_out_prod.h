@@ -128,8 +128,11 @@ enum {
     RETRO_E_ALIGN = -4, /* W, G or dst not 16-byte aligned */
     RETRO_E_ALIAS = -5, /* dst overlaps W or G */
     RETRO_E_HIP = -6,   /* the HIP runtime reported an error at launch */
-    RETRO_E_VARIANT = -7 /* retro_out_prod_variant: variant unknown or not
-                            applicable to this type/shape */
+    RETRO_E_VARIANT = -7, /* retro_out_prod_variant: variant unknown or not
+                             applicable to this type/shape */
+    RETRO_E_WORKSPACE = -8 /* retro_out_prod_ws: a forced variant needs a
+                              workspace that is missing, too small, not
+                              16-byte aligned or overlapping W, G or dst */
 };
 
 /* Size limits: K, N and T are each below 2^31, T*K and T*N below 2^60, and
@@ -200,6 +203,12 @@ const char *retro_strerror(int code);
  *                           and T; the two are summed in different orders)
  *   RETRO_VARIANT_SKINNY_8, RETRO_VARIANT_SKINNY_16  the skinny kernel with
  *                           that many waves per workgroup
+ *   RETRO_VARIANT_SKINNY_SPLIT  retro_out_prod_ws only: the skinny kernel's
+ *                           groups of 16 W rows, all slabs of 64 dst columns
+ *                           in turn, cut into one equal share per CU, the
+ *                           parts of a slab added through a workspace (see
+ *                           retro_out_prod_ws). T <= 16, N % 16 == 0,
+ *                           K % 4 == 0, G rows in 16-byte units
  *   RETRO_VARIANT_TILE_*    tiled F32-MFMA kernel, tile = rows of T x columns
  *                           of K per workgroup (256-column tiles need K tiles
  *                           that are whole K-quant super-blocks; the K-quants
@@ -276,7 +285,8 @@ enum {
     RETRO_VARIANT_WS_256x256 = 18,
     RETRO_VARIANT_WS_256x128 = 19,
     RETRO_VARIANT_SKINNY_8 = 20,
-    RETRO_VARIANT_SKINNY_16 = 21
+    RETRO_VARIANT_SKINNY_16 = 21,
+    RETRO_VARIANT_SKINNY_SPLIT = 22
 };
 
 /* retro_out_prod with a forced kernel variant; RETRO_E_VARIANT when the
@@ -435,6 +445,44 @@ int retro_out_prod_views_plan(int type, int64_t K, int64_t N, int64_t T, int64_t
  * tests and benchmarks of the plans above. */
 int retro_out_prod_column_split(int variant0, int64_t k_split, int variant1, int type, const void *W,
                                 const float *G, float *dst, int64_t K, int64_t N, int64_t T, void *stream);
+
+/*
+ * retro_out_prod with a caller-owned workspace: the same contraction (the
+ * OUT_PROD of llama.cpp PR #3 "cuda: out_prod accepts a quantized src0",
+ * section "What") and contract, for contiguous operands. The skinny kernel (T <= 16) gives each
+ * 64-column slab of dst to one workgroup, so with fewer slabs than CUs (K
+ * below 16384) part of the GPU idles; RETRO_VARIANT_SKINNY_SPLIT spreads the
+ * rows of W evenly over all CUs and adds the parts of each slab through the
+ * workspace (measured on MI355X, Q4_K, T = 16: K = 4096, N = 14336 in 27 us
+ * against 79 us; K = 4096, N = 4096 in 11.5 against 25 us).
+ *   variant     RETRO_VARIANT_AUTO: the split when the estimated time gain is
+ *               at least 10% (fewer than 193 slabs and enough rows), else
+ *               what retro_out_prod runs; any other variant as
+ *               retro_out_prod_variant, RETRO_VARIANT_SKINNY_SPLIT included
+ *   workspace   device memory of workspace_bytes bytes, 16-byte aligned,
+ *               overlapping none of W, G and dst; the split uses a fixed
+ *               2 MiB + 1 KiB (retro_out_prod_workspace_size). Its first
+ *               1 KiB holds counters that must be zero before the first call
+ *               that uses it (zero the whole workspace once); every call
+ *               leaves them at zero, so later calls need no clearing. Calls
+ *               that share a workspace must not overlap in time (one stream,
+ *               or synchronised): they would race on it.
+ * With RETRO_VARIANT_AUTO, a NULL workspace or one smaller than
+ * retro_out_prod_workspace_size reports runs what retro_out_prod runs; a
+ * forced RETRO_VARIANT_SKINNY_SPLIT returns RETRO_E_WORKSPACE instead. The
+ * split adds each slab's parts in a fixed order, so its result does not
+ * depend on which workgroup finishes first, but it sums in another order than
+ * the skinny kernel (both within the same error bars). No waiting between
+ * workgroups: every workgroup runs to its end whatever the others do.
+ */
+int retro_out_prod_ws(int variant, int type, const void *W, const float *G, float *dst, int64_t K, int64_t N,
+                      int64_t T, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace retro_out_prod_ws(variant, type, ..., K, N, T, ...) uses:
+ * 0 when the call runs a kernel that needs none, else the split's fixed
+ * size. A negative code for an invalid type or shape, or a variant that does
+ * not apply. Touches no device. */
+int64_t retro_out_prod_workspace_size(int variant, int type, int64_t K, int64_t N, int64_t T);
 
 /* 1 if retro_out_prod_variant(variant, type, ..., K, N, T) with valid buffers
  * would run, 0 otherwise. Touches no device. */

@@ -32,7 +32,7 @@ TYPES = {"f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0, "q4_1
          "q5_1": Q5_1, "mxfp4": MXFP4, "nvfp4": NVFP4, "q2_k": Q2_K, "q3_k": Q3_K, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 
 OK = 0
-E_TYPE, E_SHAPE, E_NULL, E_ALIGN, E_ALIAS, E_HIP, E_VARIANT = -1, -2, -3, -4, -5, -6, -7
+E_TYPE, E_SHAPE, E_NULL, E_ALIGN, E_ALIAS, E_HIP, E_VARIANT, E_WORKSPACE = -1, -2, -3, -4, -5, -6, -7, -8
 
 VARIANT_AUTO = 0
 VARIANT_SKINNY = 1
@@ -55,6 +55,7 @@ VARIANT_WS_256x256 = 18
 VARIANT_WS_256x128 = 19
 VARIANT_SKINNY_8 = 20
 VARIANT_SKINNY_16 = 21
+VARIANT_SKINNY_SPLIT = 22
 VARIANT_NAMES = {
     VARIANT_SKINNY: "skinny", VARIANT_TILE_128x128: "tile_128x128", VARIANT_TILE_128x256: "tile_128x256",
     VARIANT_TILE_64x128: "tile_64x128", VARIANT_TILE_64x64: "tile_64x64", VARIANT_TILE_64x256: "tile_64x256",
@@ -63,6 +64,7 @@ VARIANT_NAMES = {
     VARIANT_WS2_64x128: "ws2_64x128", VARIANT_SIMPLE: "simple", VARIANT_SPLIT_128x256: "split_128x256",
     VARIANT_SPLIT_128x128: "split_128x128", VARIANT_WS_256x256: "ws_256x256",
     VARIANT_WS_256x128: "ws_256x128", VARIANT_SKINNY_8: "skinny_8", VARIANT_SKINNY_16: "skinny_16",
+    VARIANT_SKINNY_SPLIT: "skinny_split",
 }
 
 LIB_PATH = _build.LIB_PATH
@@ -74,7 +76,7 @@ EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided",
            "retro_out_prod_strided_variant_applies", "retro_out_prod_batched", "retro_out_prod_batched_variant",
            "retro_out_prod_views", "retro_out_prod_views_variant", "retro_out_prod_views_variant_applies",
            "retro_out_prod_views_choice", "retro_out_prod_plan", "retro_out_prod_views_plan",
-           "retro_out_prod_column_split",
+           "retro_out_prod_column_split", "retro_out_prod_ws", "retro_out_prod_workspace_size",
            "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
            "retro_mul_mat_plan", "retro_mul_mat_row_split",
            "retro_row_bytes", "retro_strerror",
@@ -145,6 +147,10 @@ def _load() -> ctypes.CDLL:
                                               ctypes.POINTER(ctypes.c_int32)]
     lib.retro_out_prod_column_split.restype = i32
     lib.retro_out_prod_column_split.argtypes = [i32, i64, i32, i32, vp, vp, vp, i64, i64, i64, vp]
+    lib.retro_out_prod_ws.restype = i32
+    lib.retro_out_prod_ws.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.retro_out_prod_workspace_size.restype = i64
+    lib.retro_out_prod_workspace_size.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_out_prod_variant_applies.restype = i32
     lib.retro_out_prod_variant_applies.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_row_bytes.restype = i64
@@ -307,6 +313,46 @@ def out_prod(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, st
                                                 _stream_handle(stream)))
     return out
 
+
+
+def workspace_size(wtype: int, K: int, N: int, T: int, variant: int = VARIANT_AUTO) -> int:
+    """Bytes of workspace out_prod_ws uses for this shape (0: none; negative: an error code)."""
+    return int(lib.retro_out_prod_workspace_size(int(variant), int(wtype), int(K), int(N), int(T)))
+
+
+def new_workspace(device=None):
+    """A zeroed workspace for out_prod_ws, large enough for any shape."""
+    nbytes = workspace_size(Q4_K, 4096, 4096, 16, VARIANT_SKINNY_SPLIT)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device if device is not None else "cuda")
+
+
+def out_prod_ws(wtype: int, W, G, K: int, workspace, out=None, variant: int = VARIANT_AUTO, stream=None):
+    """out_prod with a workspace (contiguous W, G and out): for T <= 16 and
+    few 64-column slabs of dst, the split over all CUs. The workspace is a
+    device tensor from new_workspace (or None); calls sharing one must be
+    ordered on a stream."""
+    _device_tensor(W, "W")
+    _device_tensor(G, "G")
+    if G.dtype != torch.float32 or G.dim() != 2:
+        raise ValueError("G must be a contiguous 2-D float32 tensor (T x N)")
+    T, N = G.shape
+    rb = row_bytes(wtype, K)
+    if rb < 0:
+        _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
+    if W.numel() * W.element_size() != N * rb:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.float32, device=G.device)
+    else:
+        _device_tensor(out, "out")
+        if out.dtype != torch.float32 or tuple(out.shape) != (T, K):
+            raise ValueError("out must be a contiguous float32 T x K tensor")
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.retro_out_prod_ws(int(variant), int(wtype), _ptr(W), _ptr(G), _ptr(out), int(K), int(N), int(T),
+                                 _ptr(workspace), int(nbytes), _stream_handle(stream)))
+    return out
 
 
 def out_prod_column_split(wtype: int, W, G, K: int, variant0: int, k_split: int, variant1: int, out=None,

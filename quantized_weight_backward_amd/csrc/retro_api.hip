@@ -137,6 +137,29 @@ bool skinny_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s)
            16 * s.ldg * 4 < (int64_t(1) << 31);
 }
 
+// The n-split skinny kernel: the skinny kernel's fast path (whole 16-row
+// groups, K in 4-element units, G rows in 16-byte units) over one matrix.
+bool skinny_split_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    return skinny_applies(type, K, N, T, s) && T >= 1 && N >= 16 && N % 16 == 0 && K % 4 == 0 &&
+           (s.gcols || s.ldg % 4 == 0) && s.batches() == 1;
+}
+
+// Whether the split is worth its workspace: estimated times, fitted to Q4_K
+// on MI355X at T = 16 (K = 2048 .. 16384, N = 1024 .. 14336): the skinny
+// kernel about 3 us plus 0.09 us per 16-row group on its busiest CU, the
+// split 5.6 us (a second piece and the finishing sums) plus the same per
+// group of its share. Taken at an estimated gain of 10% or more, and only
+// below 193 slabs: from 224 slabs on (Q4_K, K = 14336) the split measured
+// 1.04-1.27x the time, reading W without the L2 sharing of neighbouring
+// slabs that the skinny kernel's side-by-side workgroups get.
+bool skinny_split_pays(int64_t K, int64_t N) {
+    const int64_t slabs = cdiv(K, 64), ng = N / 16;
+    if (slabs > 192) return false;
+    const double one = 3.0 + double(ng) * 0.09;
+    const double split = 5.6 + double(cdiv(slabs * ng, kSplitGrid)) * 0.09;
+    return split <= 0.9 * one;
+}
+
 // Whether the automatic choice may take tile v for this type. F32 rows spill
 // registers in the 256 x 256 tile (their producers stage 16 bytes per
 // element group): measured 0.99-1.04x the time of 128 x 256, where every
@@ -427,6 +450,62 @@ int out_prod_impl(int variant, int type, const void* W, const float* G, float* d
 }
 
 // ---------------------------------------------------------------------------
+// out_prod with a workspace: the n-split skinny kernel
+// ---------------------------------------------------------------------------
+
+int launch_split_typed(int type, const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                       const Strides& s, void* ws, hipStream_t st) {
+    switch (type) {
+        case RETRO_F32: return launch_out_prod_split<RETRO_F32>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_F16: return launch_out_prod_split<RETRO_F16>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_BF16: return launch_out_prod_split<RETRO_BF16>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q8_0: return launch_out_prod_split<RETRO_Q8_0>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q4_0: return launch_out_prod_split<RETRO_Q4_0>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q4_1: return launch_out_prod_split<RETRO_Q4_1>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q5_0: return launch_out_prod_split<RETRO_Q5_0>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q5_1: return launch_out_prod_split<RETRO_Q5_1>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_MXFP4: return launch_out_prod_split<RETRO_MXFP4>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_NVFP4: return launch_out_prod_split<RETRO_NVFP4>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q4_K: return launch_out_prod_split<RETRO_Q4_K>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q5_K: return launch_out_prod_split<RETRO_Q5_K>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q2_K: return launch_out_prod_split<RETRO_Q2_K>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q3_K: return launch_out_prod_split<RETRO_Q3_K>(W, G, dst, K, N, T, s, ws, st);
+        case RETRO_Q6_K: return launch_out_prod_split<RETRO_Q6_K>(W, G, dst, K, N, T, s, ws, st);
+        default: return RETRO_E_TYPE;
+    }
+}
+
+// Workspace bytes a call of `variant` uses for this (checked) shape: the
+// split's fixed size, 0 for any other kernel, or RETRO_E_VARIANT.
+int64_t workspace_need(int variant, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    if (variant == RETRO_VARIANT_SKINNY_SPLIT)
+        return skinny_split_applies(type, K, N, T, s) ? kSplitWorkspaceBytes : RETRO_E_VARIANT;
+    if (variant == RETRO_VARIANT_AUTO)
+        return skinny_split_applies(type, K, N, T, s) && skinny_split_pays(K, N) ? kSplitWorkspaceBytes : 0;
+    return variant_applies(variant, type, K, N, T, s) ? 0 : RETRO_E_VARIANT;
+}
+
+int out_prod_ws_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
+                     int64_t T, void* workspace, int64_t workspace_bytes, void* stream) {
+    const Strides s = contiguous(type, K, N);
+    bool empty = false;
+    const int rc = check_call(type, W, G, dst, K, N, T, s, empty);
+    if (rc != RETRO_OK) return rc;
+    if (empty) return RETRO_OK;
+    const int64_t need = workspace_need(variant, type, K, N, T, s);
+    if (need < 0) return int(need);
+    if (need == 0) return out_prod_impl(variant, type, W, G, dst, K, N, T, s, stream);
+    if (!workspace || workspace_bytes < need) {
+        if (variant == RETRO_VARIANT_SKINNY_SPLIT) return RETRO_E_WORKSPACE;
+        return out_prod_impl(RETRO_VARIANT_AUTO, type, W, G, dst, K, N, T, s, stream);
+    }
+    if (!aligned16(workspace) || overlap(workspace, need, W, N * s.ldw) || overlap(workspace, need, G, T * N * 4) ||
+        overlap(workspace, need, dst, T * K * 4))
+        return RETRO_E_WORKSPACE;
+    return launch_split_typed(type, W, G, dst, K, N, T, s, workspace, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
 // mul_mat
 // ---------------------------------------------------------------------------
 
@@ -648,6 +727,17 @@ int retro_out_prod(int type, const void* W, const float* G, float* dst, int64_t 
     return out_prod_impl(RETRO_VARIANT_AUTO, type, W, G, dst, K, N, T, contiguous(type, K, N), stream);
 }
 
+int retro_out_prod_ws(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
+                      int64_t T, void* workspace, int64_t workspace_bytes, void* stream) {
+    return out_prod_ws_impl(variant, type, W, G, dst, K, N, T, workspace, workspace_bytes, stream);
+}
+
+int64_t retro_out_prod_workspace_size(int variant, int type, int64_t K, int64_t N, int64_t T) {
+    const int rc = check_shape(type, K, N, T);
+    if (rc != RETRO_OK) return rc;
+    return workspace_need(variant, type, K, N, T, contiguous(type, K, N));
+}
+
 int retro_out_prod_variant(int variant, int type, const void* W, const float* G, float* dst, int64_t K,
                            int64_t N, int64_t T, void* stream) {
     return out_prod_impl(variant, type, W, G, dst, K, N, T, contiguous(type, K, N), stream);
@@ -848,8 +938,10 @@ const char* retro_strerror(int code) {
         case RETRO_E_ALIAS: return "dst overlaps W or G";
         case RETRO_E_HIP: return "HIP launch error";
         case RETRO_E_VARIANT: return "kernel variant unknown or not applicable to this type and shape";
+        case RETRO_E_WORKSPACE: return "workspace missing, too small, misaligned or overlapping an operand";
         default: return "unknown error code";
     }
 }
 
 }  // extern "C"
+

@@ -102,6 +102,21 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
 template <int TYPE>
 int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
                    int64_t ldy, hipStream_t st);
+// The n-split skinny kernel's workspace: a counter word per workgroup
+// (kSplitCountBytes in all), then two 16 x 64 float slots per workgroup. The
+// counters must be zero before a call and are zero after it; the slots need
+// no initial value. Its grid is one workgroup per CU.
+constexpr int kSplitGrid = kNumCUs;
+constexpr int64_t kSplitCountBytes = 4 * kSplitGrid;
+constexpr int64_t kSplitSlotBytes = 16 * 64 * 4;
+constexpr int64_t kSplitWorkspaceBytes = kSplitCountBytes + 2 * kSplitGrid * kSplitSlotBytes;
+static_assert(kSplitCountBytes % 256 == 0, "slots start 256-byte aligned");
+
+// One launch of the n-split skinny kernel (one matrix; applicability checked
+// by the caller), with a workspace of kSplitWorkspaceBytes.
+template <int TYPE>
+int launch_out_prod_split(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                          const Strides& s, void* workspace, hipStream_t st);
 template <int TYPE>
 int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t st);
 

@@ -1239,6 +1239,221 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
 }
 
 // ---------------------------------------------------------------------------
+// Skinny kernel with n split across workgroups (T <= 16, needs a workspace)
+// ---------------------------------------------------------------------------
+//
+// The skinny kernel gives each 64-column slab of dst to one workgroup, so
+// with fewer slabs than CUs part of the chip idles. Here the 16-row groups of
+// all slabs, slab after slab, are cut into equal shares, one per workgroup
+// (one per CU). A share covers the tail of one slab and the head of the next
+// (or several whole slabs in between when shares are long). Each piece of a
+// slab is summed as in the skinny kernel. A piece that is a whole slab is
+// stored to dst; any other goes to its slot of the workspace, and the
+// workgroup that finishes a slab's pieces last (a per-slab counter) adds the
+// slab's slots in slot order and stores dst, so the result has the same bits
+// whichever workgroup finishes last. Only a share's first and last piece can
+// be part of a slab, so each workgroup owns two slots, and the counter of a
+// split slab belongs to the workgroup holding its first group (no workgroup
+// holds the first group of two split slabs): the workspace is a fixed
+// 2 x 4 KB + 4 bytes per workgroup whatever the shape. Slots and counters are
+// read and written at device scope (the pieces of a slab may run on
+// different XCDs); every counter is back at zero when the call ends. There is
+// no waiting on other workgroups: each one runs to its end whatever the
+// others do.
+struct SkinnySplitArgs {
+    unsigned* count;  // one word per workgroup: pieces of its counted slab finished so far
+    float* slots;     // 16 x 64 floats per (workgroup, first or last piece)
+    int ng;           // 16-row groups per slab (N / 16)
+    long long share;  // groups per workgroup
+};
+
+template <int TYPE, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(SkinnyArgs args, SkinnySplitArgs sp) {
+    constexpr int KS = 64;
+    constexpr int PER = 16 * KS / (NWAVES * 64);  // slab outputs per thread
+    static_assert(PER * NWAVES * 64 == 16 * KS, "whole outputs per thread");
+    __shared__ __attribute__((aligned(16))) float part[NWAVES * 16 * KS];
+    __shared__ unsigned finisher[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = args.K, T = args.T, ng = sp.ng;
+    const long long groups = (long long)((K + KS - 1) / KS) * ng;
+    // consecutive shares (the two ends of a slab) on one XCD
+    const int p = xcd_remap(blockIdx.x, gridDim.x);
+    const long long begin = (long long)p * sp.share;
+    const long long end = min(begin + sp.share, groups);
+    if (begin >= end) return;
+    const int j = lane & 15, rq = lane >> 4;
+
+    // Piece [a, b) of slab s: the groups of this share inside that slab.
+    struct Piece {
+        int s, a, b;
+    };
+    auto piece_at = [&](long long at) {
+        Piece pc;
+        pc.s = int(at / ng);
+        pc.a = int(at - (long long)pc.s * ng);
+        pc.b = int(min(end - (long long)pc.s * ng, (long long)ng));
+        return pc;
+    };
+    // Slabs this workgroup adds to without holding them whole: at most its
+    // first piece and its last one.
+    const int first_slab = int(begin / ng);
+    int open0 = -1, open1 = -1;
+    // the shares holding the first and the last group of slab s
+    auto first_share = [&](int s) { return int((long long)s * ng / sp.share); };
+    auto last_share = [&](int s) { return int(((long long)s * ng + ng - 1) / sp.share); };
+
+    Piece cur = piece_at(begin);
+    SkinnyOffsets off = skinny_offsets<TYPE>(args, cur.s * KS, lane);
+    SkinnyRaw<TYPE> r0, r1, r2;
+    // The first two groups of a piece for this wave, as the group loop
+    // expects them (a repeat of a valid group past the wave's last one).
+    auto prefetch = [&](const Piece& pc, const SkinnyOffsets& o) {
+        const int g0 = min(pc.a + wave, pc.b - 1);
+        skinny_fetch_fast<TYPE>(args, 16 * g0, o, r0);
+        skinny_fetch_fast<TYPE>(args, 16 * min(g0 + NWAVES, pc.b - 1), o, r1);
+    };
+    prefetch(cur, off);
+
+    for (;;) {
+        const int k0 = cur.s * KS;
+        f32x4 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto contract = [&](const SkinnyRaw<TYPE>& r) {
+            float wv[4][4];
+            skinny_decode<TYPE>(r, k0, lane, wv);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.g[q], wv[q][c], acc[c], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // groups a + wave, a + wave + NWAVES, ... below b: the skinny
+        // kernel's loop, two groups ahead
+        const int g0 = cur.a + wave;
+        if (g0 < cur.b) {
+            const int last = cur.b - 1;
+            const int cnt = (cur.b - g0 + NWAVES - 1) / NWAVES;
+            auto row0 = [&](int i) { return 16 * min(g0 + i * NWAVES, last); };
+            const int triples = cnt / 3;
+            for (int t3 = 0, i = 0; t3 < triples; ++t3, i += 3) {
+                skinny_fetch_fast<TYPE>(args, row0(i + 2), off, r2);
+                contract(r0);
+                skinny_fetch_fast<TYPE>(args, row0(i + 3), off, r0);
+                contract(r1);
+                skinny_fetch_fast<TYPE>(args, row0(i + 4), off, r1);
+                contract(r2);
+            }
+            const int left = cnt - 3 * triples;
+            if (left >= 1) contract(r0);
+            if (left >= 2) contract(r1);
+        }
+        const long long next_at = (long long)cur.s * ng + cur.b;
+        const Piece done = cur;
+        // the next piece's first loads are in flight while this one is reduced
+        if (next_at < end) {
+            cur = piece_at(next_at);
+            off = skinny_offsets<TYPE>(args, cur.s * KS, lane);
+            prefetch(cur, off);
+        }
+
+        // The skinny kernel's reduction over waves, in wave order.
+        float* mine = part + wave * 16 * KS;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mine[(4 * rq + v) * KS + 4 * j + c] = acc[c][v];
+        __syncthreads();
+        const bool whole = (done.a == 0 && done.b == ng);
+        // slot 2p for the share's first piece, 2p + 1 for its last
+        float* slot = sp.slots + (2ll * p + (done.s != first_slab)) * (16 * KS);
+        for (int o = tid; o < 16 * KS; o += NWAVES * 64) {
+            const int tr = o / KS, kk = o - tr * KS;
+            float sum = part[o];
+#pragma unroll
+            for (int w = 1; w < NWAVES; ++w) sum += part[w * 16 * KS + o];
+            if (whole) {
+                if (tr < T && done.s * KS + kk < K) args.dst[(long long)tr * args.ldd + done.s * KS + kk] = sum;
+            } else {
+                __hip_atomic_store(reinterpret_cast<unsigned*>(slot) + o, __float_as_uint(sum), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (!whole) {
+            if (open0 < 0)
+                open0 = done.s;
+            else
+                open1 = done.s;
+        }
+        __syncthreads();  // part is rewritten by the next piece
+        if (next_at >= end) break;
+    }
+
+    if (open0 < 0) return;
+    // This workgroup's slots are complete at device scope before its counters
+    // move; the last of a slab's pieces to arrive adds the slab's slots.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0) {
+        finisher[0] = __hip_atomic_fetch_add(sp.count + first_share(open0), 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) ==
+                      unsigned(last_share(open0) - first_share(open0));
+        finisher[1] = open1 >= 0 && __hip_atomic_fetch_add(sp.count + first_share(open1), 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT) ==
+                                        unsigned(last_share(open1) - first_share(open1));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        if (!finisher[f]) continue;
+        const int s = f ? open1 : open0, q0 = first_share(s), npieces = last_share(s) - q0 + 1;
+        // Slot of share q0 + c: its first piece's (2q) unless slab s is not
+        // where that share starts (2q + 1). Device-scope loads (sc1), a round
+        // of four slots in flight at once.
+        const __amdgpu_buffer_rsrc_t slots =
+            buffer_rsrc(sp.slots + 2ll * q0 * (16 * KS), uint32_t(2 * npieces * 16 * KS * 4));
+        auto slot_of = [&](int c) {
+            const int q = q0 + c;
+            return 2 * c + (int((long long)q * sp.share / ng) != s ? 1 : 0);
+        };
+        float sum[PER];
+        for (int c0 = 0; c0 < npieces; c0 += 4) {
+            float v[4][PER];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t base = uint32_t(slot_of(c0 + c) * 16 * KS * 4);
+#pragma unroll
+                for (int m = 0; m < PER; ++m)
+                    v[c][m] = c0 + c < npieces
+                                  ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                        slots, base + uint32_t((tid + m * NWAVES * 64) * 4), 0, 16))
+                                  : 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int m = 0; m < PER; ++m) {
+                    if (c0 + c == 0)
+                        sum[m] = v[c][m];
+                    else if (c0 + c < npieces)
+                        sum[m] += v[c][m];
+                }
+        }
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int o = tid + m * NWAVES * 64, tr = o / KS, kk = o - tr * KS;
+            if (tr < T && s * KS + kk < K) args.dst[(long long)tr * args.ldd + s * KS + kk] = sum[m];
+        }
+        if (tid == 0) __hip_atomic_store(sp.count + q0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dequantize kernel: out[n][k] = W[n][k]
 // ---------------------------------------------------------------------------
 

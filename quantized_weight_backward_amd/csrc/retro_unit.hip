@@ -158,9 +158,8 @@ void launch_skinny_waves(const SkinnyArgs& a, dim3 grid, hipStream_t st) {
         hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false>), grid, block, 0, st, a);
 }
 
-template <int TYPE>
-int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
-                  int waves, hipStream_t st) {
+SkinnyArgs skinny_args(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                       const Strides& s) {
     SkinnyArgs a;
     a.W = static_cast<const uint8_t*>(W);
     a.G = G;
@@ -175,6 +174,13 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     a.gvec = (s.gcols || s.ldg % 4 == 0) ? 1 : 0;
     a.gcols = s.gcols ? 1 : 0;
     a.batch = batch_args(s);
+    return a;
+}
+
+template <int TYPE>
+int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
+                  int waves, hipStream_t st) {
+    const SkinnyArgs a = skinny_args(W, G, dst, K, N, T, s);
     const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches()));
     clear_last_error();
     if (waves == 8)
@@ -308,11 +314,31 @@ int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t 
     return launch_status();
 }
 
+template <int TYPE>
+int launch_out_prod_split(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
+                          const Strides& s, void* workspace, hipStream_t st) {
+    const SkinnyArgs a = skinny_args(W, G, dst, K, N, T, s);
+    SkinnySplitArgs sp;
+    sp.count = static_cast<unsigned*>(workspace);
+    sp.slots = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSplitCountBytes);
+    sp.ng = int(N / 16);
+    sp.share = cdiv(cdiv(K, 64) * (N / 16), kSplitGrid);
+    clear_last_error();
+    if (skinny_waves(TYPE, T) == 8)
+        hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 8>), dim3(kSplitGrid), dim3(512), 0, st, a, sp);
+    else
+        hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 16>), dim3(kSplitGrid), dim3(1024), 0, st, a, sp);
+    return launch_status();
+}
+
 template int launch_out_prod<RETRO_UNIT_TYPE>(int, const void*, const float*, float*, int64_t, int64_t, int64_t,
                                               const Strides&, hipStream_t);
+template int launch_out_prod_split<RETRO_UNIT_TYPE>(const void*, const float*, float*, int64_t, int64_t, int64_t,
+                                                    const Strides&, void*, hipStream_t);
 template int launch_mul_mat<RETRO_UNIT_TYPE>(int, const void*, const float*, float*, int64_t, int64_t, int64_t, int64_t,
                                              hipStream_t);
 template int launch_dequant<RETRO_UNIT_TYPE>(const void*, float*, int64_t, int64_t, hipStream_t);
 
 }  // namespace host
 }  // namespace retro
+

@@ -51,7 +51,8 @@ def test_enum_values_match_header():
                         ("RETRO_BF16", q.BF16), ("RETRO_E_TYPE", q.E_TYPE),
                         ("RETRO_E_SHAPE", q.E_SHAPE), ("RETRO_E_NULL", q.E_NULL), ("RETRO_E_ALIGN", q.E_ALIGN),
                         ("RETRO_E_ALIAS", q.E_ALIAS), ("RETRO_E_HIP", q.E_HIP), ("RETRO_E_VARIANT", q.E_VARIANT),
-                        ("RETRO_VARIANT_SKINNY", q.VARIANT_SKINNY),
+                        ("RETRO_VARIANT_SKINNY", q.VARIANT_SKINNY), ("RETRO_E_WORKSPACE", q.E_WORKSPACE),
+                        ("RETRO_VARIANT_SKINNY_SPLIT", q.VARIANT_SKINNY_SPLIT),
                         ("RETRO_VARIANT_TILE_128x256", q.VARIANT_TILE_128x256),
                         ("RETRO_VARIANT_TILE_64x64", q.VARIANT_TILE_64x64)]:
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
@@ -215,6 +216,56 @@ def test_plan_is_the_same_from_the_cache():
     for _ in range(3):
         assert [q.plan(*sh) for sh in reversed(shapes)] == first[::-1]
         assert [q.choice(*sh) for sh in shapes] == [p[0] for p in first]
+
+
+def test_workspace_size():
+    """The n-split skinny kernel's workspace: a fixed 1 KiB of counters and
+    two 4 KiB slots per CU, taken automatically only for T <= 16 with few
+    slabs and enough rows."""
+    full = 4 * 256 + 2 * 256 * 16 * 64 * 4
+    split = q.VARIANT_SKINNY_SPLIT
+    assert q.workspace_size(q.Q4_K, 4096, 14336, 16) == full      # 64 slabs
+    assert q.workspace_size(q.Q4_0, 5120, 4096, 16) == full       # 80 slabs
+    assert q.workspace_size(q.Q4_K, 11008, 4096, 16) == full      # 172 slabs
+    assert q.workspace_size(q.Q4_K, 14336, 4096, 16) == 0         # 224 slabs: the skinny kernel
+    assert q.workspace_size(q.Q8_0, 256, 128, 16) == 0            # too few rows to share
+    assert q.workspace_size(q.Q4_K, 4096, 14336, 17) == 0         # T > 16: tiles
+    for wtype in q.TYPES.values():
+        K = 256 * 8
+        assert q.workspace_size(wtype, K, 4096, 16, split) == full
+        assert q.workspace_size(wtype, K, 4096, 17, split) == q.E_VARIANT
+        assert q.workspace_size(wtype, K, 4088, 16, split) == q.E_VARIANT   # N % 16 != 0
+        assert q.workspace_size(wtype, K, 0, 16, split) == q.E_VARIANT
+    assert q.workspace_size(q.F32, 4094, 4096, 16, split) == q.E_VARIANT     # K % 4 != 0
+    assert q.workspace_size(q.Q4_K, 4096, 4096, 512, q.VARIANT_WS_128x256) == 0
+    assert q.workspace_size(q.Q4_K, 4096, 4096, 512, q.VARIANT_SKINNY) == q.E_VARIANT
+    assert q.workspace_size(q.Q4_K, 100, 16, 16) == q.E_SHAPE
+    assert q.workspace_size(5, 32, 16, 16) == q.E_TYPE
+    # the split needs the workspace call: the others refuse it
+    assert not q.variant_applies(split, q.Q4_K, 4096, 4096, 16)
+    assert q.lib.retro_out_prod_variant(split, q.Q4_K, 0x100000, 0x2000000, 0x3000000, 4096, 4096, 16,
+                                        None) == q.E_VARIANT
+
+
+def test_workspace_call_validation():
+    """Errors of retro_out_prod_ws, all returned before any launch."""
+    f = q.lib.retro_out_prod_ws
+    W, G, D, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    full = q.workspace_size(q.Q4_K, 4096, 4096, 16, q.VARIANT_SKINNY_SPLIT)
+    split = q.VARIANT_SKINNY_SPLIT
+    args = (q.Q4_K, W, G, D, 4096, 4096, 16)
+    assert f(split, *args, None, 0, None) == q.E_WORKSPACE
+    assert f(split, *args, WS, full - 1, None) == q.E_WORKSPACE
+    assert f(split, *args, WS + 4, full, None) == q.E_WORKSPACE          # not 16-byte aligned
+    assert f(split, *args, D - 16, full, None) == q.E_WORKSPACE          # overlaps dst
+    assert f(split, *args, W, full, None) == q.E_WORKSPACE               # overlaps W
+    assert f(q.VARIANT_AUTO, *args, G + 64, full, None) == q.E_WORKSPACE  # overlaps G
+    assert f(split, q.Q4_K, W, G, D, 4096, 4096, 17, WS, full, None) == q.E_VARIANT
+    assert f(split, q.Q4_K, W, G, W, 4096, 4096, 16, WS, full, None) == q.E_ALIAS
+    assert f(split, q.Q4_K, W, None, D, 4096, 4096, 16, WS, full, None) == q.E_NULL
+    assert f(split, q.Q4_K, W, G, D, 100, 4096, 16, WS, full, None) == q.E_SHAPE
+    assert f(99, *args, WS, full, None) == q.E_VARIANT
+    assert f(split, q.Q4_K, W, G, D, 4096, 4096, 0, WS, full, None) == q.OK   # nothing to compute
 
 
 def test_plans_from_many_threads():
