@@ -478,6 +478,22 @@ int retro_out_prod_column_split(int variant0, int64_t k_split, int variant1, int
 int retro_out_prod_ws(int variant, int type, const void *W, const float *G, float *dst, int64_t K, int64_t N,
                       int64_t T, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * retro_out_prod_ws with the library's own workspace, a static device array
+ * of 2 MiB + 1 KiB on each GPU it runs on, held until the process ends. The
+ * call allocates nothing and calls no allocating routine; the caller passes
+ * inputs and outputs only. Same variants, results and errors as
+ * retro_out_prod_ws with a workspace of that size (RETRO_E_WORKSPACE if a
+ * call ever needed more; RETRO_E_HIP if the runtime cannot give the array's
+ * address on the current device, which must be the stream's). Every call on
+ * a GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race on it and may return wrong sums, so they must
+ * be ordered (one stream, or synchronised). The array's counters are zero
+ * at load and every call leaves them at zero. */
+int retro_out_prod_noalloc(int variant, int type, const void *W, const float *G, float *dst, int64_t K, int64_t N,
+                           int64_t T, void *stream);
+
 /* Bytes of workspace retro_out_prod_ws(variant, type, ..., K, N, T, ...) uses:
  * 0 when the call runs a kernel that needs none, else the split's fixed
  * size. A negative code for an invalid type or shape, or a variant that does

@@ -77,6 +77,7 @@ EXPORTS = ("retro_out_prod", "retro_out_prod_variant", "retro_out_prod_strided",
            "retro_out_prod_views", "retro_out_prod_views_variant", "retro_out_prod_views_variant_applies",
            "retro_out_prod_views_choice", "retro_out_prod_plan", "retro_out_prod_views_plan",
            "retro_out_prod_column_split", "retro_out_prod_ws", "retro_out_prod_workspace_size",
+           "retro_out_prod_noalloc",
            "retro_mul_mat", "retro_mul_mat_variant", "retro_mul_mat_choice", "retro_mul_mat_variant_applies",
            "retro_mul_mat_plan", "retro_mul_mat_row_split",
            "retro_row_bytes", "retro_strerror",
@@ -149,6 +150,8 @@ def _load() -> ctypes.CDLL:
     lib.retro_out_prod_column_split.argtypes = [i32, i64, i32, i32, vp, vp, vp, i64, i64, i64, vp]
     lib.retro_out_prod_ws.restype = i32
     lib.retro_out_prod_ws.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.retro_out_prod_noalloc.restype = i32
+    lib.retro_out_prod_noalloc.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, vp]
     lib.retro_out_prod_workspace_size.restype = i64
     lib.retro_out_prod_workspace_size.argtypes = [i32, i32, i64, i64, i64]
     lib.retro_out_prod_variant_applies.restype = i32
@@ -352,6 +355,31 @@ def out_prod_ws(wtype: int, W, G, K: int, workspace, out=None, variant: int = VA
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.retro_out_prod_ws(int(variant), int(wtype), _ptr(W), _ptr(G), _ptr(out), int(K), int(N), int(T),
                                  _ptr(workspace), int(nbytes), _stream_handle(stream)))
+    return out
+
+
+def out_prod_noalloc(wtype: int, W, G, K: int, out=None, variant: int = VARIANT_AUTO, stream=None):
+    """out_prod_ws with the library's static per-GPU workspace: the library
+    call allocates nothing (pass out, or this wrapper allocates dst). Calls
+    on one GPU must be ordered."""
+    _device_tensor(W, "W")
+    _device_tensor(G, "G")
+    if G.dtype != torch.float32 or G.dim() != 2:
+        raise ValueError("G must be a contiguous 2-D float32 tensor (T x N)")
+    T, N = G.shape
+    rb = row_bytes(wtype, K)
+    if rb < 0:
+        _check(E_SHAPE if wtype in TYPES.values() else E_TYPE)
+    if W.numel() * W.element_size() != N * rb:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, expected N*row_bytes = {N * rb}")
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.float32, device=G.device)
+    else:
+        _device_tensor(out, "out")
+        if out.dtype != torch.float32 or tuple(out.shape) != (T, K):
+            raise ValueError("out must be a contiguous float32 T x K tensor")
+    _check(lib.retro_out_prod_noalloc(int(variant), int(wtype), _ptr(W), _ptr(G), _ptr(out), int(K), int(N), int(T),
+                                      _stream_handle(stream)))
     return out
 
 

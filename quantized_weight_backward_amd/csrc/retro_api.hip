@@ -11,8 +11,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "retro_host.h"
 #include "retro_out_prod.h"
+
+// The workspace of retro_out_prod_noalloc, for callers that cannot allocate:
+// one copy on every GPU the library runs on, held until the process ends,
+// zero at load (the split kernel's counters must start at zero, and every
+// call leaves them so). In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the address hipGetSymbolAddress returns for
+// the current device, never the name itself.
+static __device__ __align__(256) unsigned char scratch[retro::host::kSplitWorkspaceBytes];
 
 namespace {
 
@@ -505,6 +516,44 @@ int out_prod_ws_impl(int variant, int type, const void* W, const float* G, float
     return launch_split_typed(type, W, G, dst, K, N, T, s, workspace, static_cast<hipStream_t>(stream));
 }
 
+// The device address of the current device's `scratch`, found once per
+// device (with that device current) and kept; NULL if the runtime cannot
+// give it.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mutex;
+
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    p = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+// retro_out_prod_ws with the static scratch as its workspace: validation
+// first, and the scratch looked up only for a call that uses it.
+int out_prod_noalloc_impl(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
+                          int64_t T, void* stream) {
+    const Strides s = contiguous(type, K, N);
+    bool empty = false;
+    const int rc = check_call(type, W, G, dst, K, N, T, s, empty);
+    if (rc != RETRO_OK || empty) return rc;
+    const int64_t need = workspace_need(variant, type, K, N, T, s);
+    if (need < 0) return int(need);
+    if (need == 0) return out_prod_impl(variant, type, W, G, dst, K, N, T, s, stream);
+    if (need > int64_t(sizeof(scratch))) return RETRO_E_WORKSPACE;
+    void* ws = scratch_for_current_device();
+    if (!ws) return RETRO_E_HIP;
+    return out_prod_ws_impl(variant, type, W, G, dst, K, N, T, ws, int64_t(sizeof(scratch)), stream);
+}
+
 // ---------------------------------------------------------------------------
 // mul_mat
 // ---------------------------------------------------------------------------
@@ -730,6 +779,11 @@ int retro_out_prod(int type, const void* W, const float* G, float* dst, int64_t 
 int retro_out_prod_ws(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
                       int64_t T, void* workspace, int64_t workspace_bytes, void* stream) {
     return out_prod_ws_impl(variant, type, W, G, dst, K, N, T, workspace, workspace_bytes, stream);
+}
+
+int retro_out_prod_noalloc(int variant, int type, const void* W, const float* G, float* dst, int64_t K, int64_t N,
+                           int64_t T, void* stream) {
+    return out_prod_noalloc_impl(variant, type, W, G, dst, K, N, T, stream);
 }
 
 int64_t retro_out_prod_workspace_size(int variant, int type, int64_t K, int64_t N, int64_t T) {

@@ -628,3 +628,19 @@ def test_probe_validation():
     assert copy(None, 0x200000, 16, None) == q.E_NULL
     assert copy(0x100008, 0x200000, 16, None) == q.E_ALIGN
     assert copy(0x100000, 0x100010, 64, None) == q.E_ALIAS
+
+
+def test_noalloc_validation():
+    """retro_out_prod_noalloc checks its arguments before it looks up its
+    static array or touches a device."""
+    f = q.lib.retro_out_prod_noalloc
+    W, G, D = 0x10000000, 0x20000000, 0x30000000
+    split = q.VARIANT_SKINNY_SPLIT
+    assert f(split, q.Q4_K, W, G, D, 4096, 4096, 17, None) == q.E_VARIANT
+    assert f(split, q.Q4_K, W, G, D, 4096, 4088, 16, None) == q.E_VARIANT
+    assert f(q.VARIANT_AUTO, q.Q4_K, W, None, D, 4096, 4096, 16, None) == q.E_NULL
+    assert f(q.VARIANT_AUTO, q.Q4_K, W, G, W, 4096, 4096, 16, None) == q.E_ALIAS
+    assert f(q.VARIANT_AUTO, q.Q4_K, W + 4, G, D, 4096, 4096, 16, None) == q.E_ALIGN
+    assert f(q.VARIANT_AUTO, 5, W, G, D, 4096, 4096, 16, None) == q.E_TYPE
+    assert f(99, q.Q4_K, W, G, D, 4096, 4096, 16, None) == q.E_VARIANT
+    assert f(split, q.Q4_K, W, G, D, 4096, 4096, 0, None) == q.OK
