@@ -38,6 +38,9 @@ PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 LARGE = "q4_k_n14336_k4096_t4096"
 SKINNY = "q4_k_n4096_k14336_t16"
+# T = 16 through the other matrix of the MLP: 64 slabs of dst (the workspace
+# call's n-split kernel against the skinny kernel, reported beside the step)
+SKINNY_FEW = "q4_k_n14336_k4096_t16"
 # Every benchmarked workload: (workload, dense storage type or "").
 WORKLOADS = [
     ("q8_0_n128_k256_t64", ""),
@@ -154,8 +157,11 @@ def read_traffic(tag: str):
     return read_profile_value(tag, "hbm_bytes_per_launch")
 
 
-BENCH_PROFILE_ARGS = "--steps 20 --warmup 5 --reps 20 --no-cpu-baseline"  # the default step loop
-COUNTER_ARGS = "--steps 3 --warmup 1 --reps 3 --min-ms 0 --no-cpu-baseline"
+# The default step loop. The profiled runs leave out the few-slab comparison,
+# whose skinny launches (another shape of the same kernel) would mix into the
+# step kernel's figures; its two kernels have traces of their own (CASE_TRACES).
+BENCH_PROFILE_ARGS = "--steps 20 --warmup 5 --reps 20 --no-cpu-baseline --no-few-slab"
+COUNTER_ARGS = "--steps 3 --warmup 1 --reps 3 --min-ms 0 --no-cpu-baseline --no-few-slab"
 PROFILE_WARMUP = 5  # launches of each kernel dropped from a trace summary (the bench's warm-up steps)
 PROFILE_STEPS = 20  # the timed steps that follow them
 PROFILE_COMMANDS = {
@@ -194,6 +200,12 @@ CASE_TRACES = {
                                        "void retro::out_prod_split_kernel<30>"),
     "mulmat_skinny_q4_k_n4096_k14336_t16": ("q4_k_n4096_k14336_t16", "", "mul_mat", "skinny",
                                             "void retro::mul_mat_skinny_kernel<12,"),
+    # T = 16 with 64 slabs of dst: the skinny kernel, then the workspace
+    # call's n-split form
+    "skinny_q4_k_n14336_k4096_t16": (SKINNY_FEW, "", "out_prod", "skinny",
+                                     "void retro::out_prod_skinny_kernel<12, 8, true>"),
+    "skinny_split_q4_k_n14336_k4096_t16": (SKINNY_FEW, "", "out_prod_ws", "skinny_split",
+                                           "void retro::out_prod_skinny_split_kernel<12, 8>"),
 }
 CASE_WARMUP = 2  # launches --profile-case makes before its timed ones
 
@@ -552,12 +564,14 @@ def main() -> int:
     ap.add_argument("--min-ms", type=float, default=100.0,
                     help="each back-to-back batch covers at least this many ms of launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-few-slab", action="store_true",
+                    help="leave out the T = 16, 64-slab comparison of retro_out_prod and retro_out_prod_ws")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this size (counter calibration)")
     ap.add_argument("--profile-case", metavar="WORKLOAD", default=None,
                     help="only run one workload LAUNCHES times (for a kernel trace) and exit")
     ap.add_argument("--wtype", default="", help="with --profile-case: f32, f16 or bf16 for the dense workload")
-    ap.add_argument("--op", choices=("out_prod", "mul_mat"), default="out_prod")
+    ap.add_argument("--op", choices=("out_prod", "out_prod_ws", "mul_mat"), default="out_prod")
     ap.add_argument("--variant", default="auto", help="with --profile-case: a variant name, or auto")
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--summarize", metavar="RUN_DIR", default=None,
@@ -602,6 +616,11 @@ def main() -> int:
             G = torch.from_numpy(c["G"]).to(dev)
             out = torch.empty((c["T"], c["K"]), dtype=torch.float32, device=dev)
             call = lambda: q.out_prod(c["type"], W, G, c["K"], out=out, variant=vid)
+        elif args.op == "out_prod_ws":
+            G = torch.from_numpy(c["G"]).to(dev)
+            out = torch.empty((c["T"], c["K"]), dtype=torch.float32, device=dev)
+            wsp = q.new_workspace(dev)
+            call = lambda: q.out_prod_ws(c["type"], W, G, c["K"], wsp, out=out, variant=vid)
         else:
             X = torch.randn((c["T"], c["K"]), device=dev)
             out = torch.empty((c["T"], c["N"]), dtype=torch.float32, device=dev)
@@ -787,6 +806,42 @@ def main() -> int:
                  "bf16_mfma_frac": round(issued / avg_split / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "speedup_vs_f32_kernel": round(avg_large / avg_split, 3)}
 
+    # T = 16 with few slabs of dst (64 for K = 4096): retro_out_prod's skinny
+    # kernel against retro_out_prod_ws, whose n-split kernel spreads the rows
+    # of W over every CU; rotated W copies, back-to-back batches.
+    skinny_split = None
+    few = None if args.no_few_slab else wl.workload(SKINNY_FEW)
+    if few is not None:
+        few_W = [torch.from_numpy(few["W"]).to(dev) for _ in range(ROTATE[SKINNY])]
+        few_G = torch.from_numpy(few["G"]).to(dev)
+        few_D = torch.empty((few["T"], few["K"]), dtype=torch.float32, device=dev)
+        few_ws = q.new_workspace(dev)
+        few_calls = {
+            "skinny": lambda i: q.out_prod(q.Q4_K, few_W[i % len(few_W)], few_G, few["K"], out=few_D),
+            "workspace": lambda i: q.out_prod_ws(q.Q4_K, few_W[i % len(few_W)], few_G, few["K"], few_ws, out=few_D),
+        }
+        few_fl = 2.0 * few["T"] * few["N"] * few["K"]
+        few_t = {}
+        for name, call in few_calls.items():
+            for i in range(5):
+                call(i)
+            torch.cuda.synchronize()
+            few_t[name] = back_to_back(call, batch_reps(back_to_back(call, 5)))
+        few_roof = max(float(few["W"].nbytes) / (PEAK_HBM_GBS * 1e9), few_fl / (PEAK_F32_TFLOPS * 1e12))
+        skinny_split = {
+            "workload": SKINNY_FEW, "slabs_of_dst": -(-few["K"] // 64),
+            "workspace_bytes": q.workspace_size(q.Q4_K, few["K"], few["N"], few["T"]),
+            "skinny": {"kernel": "out_prod_skinny_kernel (retro_out_prod)", "avg_launch_us": round(few_t["skinny"] * 1e6, 3),
+                       "f32_mfma_frac": round(few_fl / few_t["skinny"] / 1e12 / PEAK_F32_TFLOPS, 4),
+                       "binding_roof_frac": round(few_roof / few_t["skinny"], 4)},
+            "workspace": {"kernel": "out_prod_skinny_split_kernel (retro_out_prod_ws)",
+                          "avg_launch_us": round(few_t["workspace"] * 1e6, 3),
+                          "f32_mfma_frac": round(few_fl / few_t["workspace"] / 1e12 / PEAK_F32_TFLOPS, 4),
+                          "binding_roof_frac": round(few_roof / few_t["workspace"], 4)},
+            "speedup": round(few_t["skinny"] / few_t["workspace"], 3),
+        }
+        del few_W, few_G, few_D, few_ws
+
     # Measured ceilings on this GPU, timed after the rest: MFMA-only loops
     # (no memory traffic) for the F32-input and bf16 instructions, and a
     # 16-byte device copy of 1 GiB (2 GiB over HBM).
@@ -878,6 +933,7 @@ def main() -> int:
                    "weight_bytes": wbytes},
         "workloads": per_workload,
         "exact_split": split,
+        "skinny_split": skinny_split,
         "ceilings": ceilings,
         "kernel_source": kernel_source_hash(),
     }

@@ -93,7 +93,7 @@ def test_auto_takes_the_split_where_it_pays(q, ws):
     K, N, T = 4096, 14336, 16
     assert q.workspace_size(q.Q4_K, K, N, T) == q.workspace_size(q.Q4_K, K, N, T, q.VARIANT_SKINNY_SPLIT) > 0
     assert q.workspace_size(q.Q4_K, 14336, 4096, 16) == 0
-    c = wl.make_case(q.Q4_K, N, K, T, seed=960)
+    c = wl.workload("q4_k_n14336_k4096_t16")
     W, G = dev(c["W"]), dev(c["G"])
     forced = q.out_prod_ws(q.Q4_K, W, G, K, ws, variant=q.VARIANT_SKINNY_SPLIT)
     auto = q.out_prod_ws(q.Q4_K, W, G, K, ws)

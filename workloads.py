@@ -257,6 +257,9 @@ WORKLOADS = {
     "mxfp4_n17408_k5120_t2048": dict(type=MXFP4, N=17408, K=5120, T=2048, seed=1017, g_sigma=1e-2),
     "nvfp4_n17408_k5120_t2048": dict(type=NVFP4, N=17408, K=5120, T=2048, seed=1018, g_sigma=1e-2),
     "nvfp4_n4096_k14336_t16": dict(type=NVFP4, N=4096, K=14336, T=16, seed=1019, g_sigma=1.0),
+    # The small-T backward through the other matrix of the same MLP (W of
+    # 14336 rows of 4096): 64 slabs of dst against the 256 CUs.
+    "q4_k_n14336_k4096_t16": dict(type=Q4_K, N=14336, K=4096, T=16, seed=1020, g_sigma=1.0),
 }
 
 
