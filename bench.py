@@ -203,9 +203,9 @@ CASE_TRACES = {
     # T = 16 with 64 slabs of dst: the skinny kernel, then the workspace
     # call's n-split form
     "skinny_q4_k_n14336_k4096_t16": (SKINNY_FEW, "", "out_prod", "skinny",
-                                     "void retro::out_prod_skinny_kernel<12, 8, true>"),
+                                     "void retro::out_prod_skinny_kernel<12, 8, true, 1>"),
     "skinny_split_q4_k_n14336_k4096_t16": (SKINNY_FEW, "", "out_prod_ws", "skinny_split",
-                                           "void retro::out_prod_skinny_split_kernel<12, 8>"),
+                                           "void retro::out_prod_skinny_split_kernel<12, 8, 1>"),
 }
 CASE_WARMUP = 2  # launches --profile-case makes before its timed ones
 
@@ -842,6 +842,28 @@ def main() -> int:
         }
         del few_W, few_G, few_D, few_ws
 
+    # Between the skinny step (T = 16) and the large-T step: the skinny
+    # workload's W at T = 32 and 64 through retro_out_prod (the skinny kernel
+    # with two and four blocks of 16 rows of G), back-to-back batches on the
+    # rotated W copies.
+    mid_t = []
+    if not args.no_few_slab:
+        g_mid = torch.randn((64, skinny["N"]), device=dev)
+        for T_mid in (32, 64):
+            G_mid = g_mid[:T_mid].contiguous()
+            D_mid = torch.empty((T_mid, skinny["K"]), dtype=torch.float32, device=dev)
+            call = lambda i, G_mid=G_mid, D_mid=D_mid: q.out_prod(q.Q4_K, Ws[i % n_rot], G_mid, skinny["K"], out=D_mid)  # noqa: E731
+            for i in range(5):
+                call(i)
+            torch.cuda.synchronize()
+            sec = back_to_back(call, batch_reps(back_to_back(call, 5)))
+            fl = 2.0 * T_mid * skinny["N"] * skinny["K"]
+            mid_t.append({"workload": f"q4_k_n{skinny['N']}_k{skinny['K']}_t{T_mid}",
+                          "kernel": q.plan_names(q.Q4_K, skinny["K"], skinny["N"], T_mid),
+                          "avg_launch_us": round(sec * 1e6, 3), "tflops": round(fl / sec / 1e12, 3),
+                          "f32_mfma_frac": round(fl / sec / 1e12 / PEAK_F32_TFLOPS, 4)})
+        del g_mid
+
     # Measured ceilings on this GPU, timed after the rest: MFMA-only loops
     # (no memory traffic) for the F32-input and bf16 instructions, and a
     # 16-byte device copy of 1 GiB (2 GiB over HBM).
@@ -934,6 +956,7 @@ def main() -> int:
         "workloads": per_workload,
         "exact_split": split,
         "skinny_split": skinny_split,
+        "mid_t": mid_t,
         "ceilings": ceilings,
         "kernel_source": kernel_source_hash(),
     }

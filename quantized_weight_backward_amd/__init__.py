@@ -325,7 +325,7 @@ def workspace_size(wtype: int, K: int, N: int, T: int, variant: int = VARIANT_AU
 
 def new_workspace(device=None):
     """A zeroed workspace for out_prod_ws, large enough for any shape."""
-    nbytes = workspace_size(Q4_K, 4096, 4096, 16, VARIANT_SKINNY_SPLIT)
+    nbytes = workspace_size(Q4_K, 4096, 4096, 48, VARIANT_SKINNY_SPLIT)
     return torch.zeros(nbytes, dtype=torch.uint8, device=device if device is not None else "cuda")
 
 

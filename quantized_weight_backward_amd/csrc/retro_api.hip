@@ -23,7 +23,7 @@
 // call leaves them so). In host code `scratch` names a host-side stand-in,
 // not device memory: kernels get the address hipGetSymbolAddress returns for
 // the current device, never the name itself.
-static __device__ __align__(256) unsigned char scratch[retro::host::kSplitWorkspaceBytes];
+static __device__ __align__(256) unsigned char scratch[retro::host::kSplitWorkspaceMax];
 
 namespace {
 
@@ -138,37 +138,45 @@ bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t 
            33 * s.ldw < (int64_t(1) << 31);
 }
 
-// The skinny kernel addresses one 16-row group of W, and the 16 rows of G
-// it reads (16 columns, when G is stored t-fastest: at most 16 ldg floats),
-// through buffer descriptors whose sizes are signed 32-bit.
+// The skinny kernel (T <= 64) addresses one 16-row group of W, and the T
+// rows of G it reads (16 columns, when G is stored t-fastest: at most 16 ldg
+// floats), through buffer descriptors whose sizes are signed 32-bit.
 bool skinny_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     (void)type;
     (void)N;
-    return T <= 16 && cdiv(K, 64) < kGridLimit && 16 * s.ldw < (int64_t(1) << 31) &&
-           16 * s.ldg * 4 < (int64_t(1) << 31);
+    const int64_t g_span = s.gcols ? 16 * s.ldg + T : (T > 16 ? T : 16) * s.ldg + 16;
+    return T <= kSkinnyMaxT && cdiv(K, 64) < kGridLimit && 16 * s.ldw < (int64_t(1) << 31) &&
+           g_span * 4 < (int64_t(1) << 31);
+}
+
+// Estimated time (us) of the skinny kernel: per 16-row group and wave, 512
+// cycles of MFMA per block of 16 rows of G plus about 300 of decode and
+// waits, two waves per SIMD taking turns, one workgroup per CU per round,
+// and about 4 us of launch and reduction plus 1.5 us per further block
+// (fitted to Q4_K at N = 4096, K = 14336: 26.6, 44, 59 and 73 us for one to
+// four blocks).
+double skinny_estimate_us(int64_t K, int64_t N, int64_t T) {
+    const double rounds = double(cdiv(cdiv(K, 64), kNumCUs)), per_wave = double(cdiv(cdiv(N, 16), 8));
+    const double blocks = double(skinny_blocks(T));
+    return 4.0 + 1.5 * (blocks - 1.0) + rounds * per_wave * 2.0 * (512.0 * blocks + 300.0) / 2400.0;
 }
 
 // The n-split skinny kernel: the skinny kernel's fast path (whole 16-row
-// groups, K in 4-element units, G rows in 16-byte units) over one matrix.
+// groups, K in 4-element units, G rows in 16-byte units) over one matrix,
+// T <= 48.
 bool skinny_split_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    return skinny_applies(type, K, N, T, s) && T >= 1 && N >= 16 && N % 16 == 0 && K % 4 == 0 &&
+    return skinny_applies(type, K, N, T, s) && T >= 1 && T <= kSplitMaxT && N >= 16 && N % 16 == 0 && K % 4 == 0 &&
            (s.gcols || s.ldg % 4 == 0) && s.batches() == 1;
 }
 
-// Whether the split is worth its workspace: estimated times, fitted to Q4_K
-// on MI355X at T = 16 (K = 2048 .. 16384, N = 1024 .. 14336): the skinny
-// kernel about 3 us plus 0.09 us per 16-row group on its busiest CU, the
-// split 5.6 us (a second piece and the finishing sums) plus the same per
-// group of its share. Taken at an estimated gain of 10% or more, and only
-// below 193 slabs: from 224 slabs on (Q4_K, K = 14336) the split measured
-// 1.04-1.27x the time, reading W without the L2 sharing of neighbouring
-// slabs that the skinny kernel's side-by-side workgroups get.
-bool skinny_split_pays(int64_t K, int64_t N) {
-    const int64_t slabs = cdiv(K, 64), ng = N / 16;
-    if (slabs > 192) return false;
-    const double one = 3.0 + double(ng) * 0.09;
-    const double split = 5.6 + double(cdiv(slabs * ng, kSplitGrid)) * 0.09;
-    return split <= 0.9 * one;
+// Estimated time (us) of the n-split skinny kernel: the skinny kernel's rate
+// over one share per CU, plus about 5.6 us of launch, a second piece and the
+// finishing sums (fitted to Q4_K at T = 16, K = 2048 .. 16384), and 1.5 us
+// per further block of 16 rows of G.
+double skinny_split_estimate_us(int64_t K, int64_t N, int64_t T) {
+    const int64_t share = cdiv(cdiv(K, 64) * (N / 16), kSplitGrid);
+    const double blocks = double(skinny_blocks(T));
+    return 5.6 + 1.5 * (blocks - 1.0) + double(cdiv(share, 8)) * 2.0 * (512.0 * blocks + 300.0) / 2400.0;
 }
 
 // Whether the automatic choice may take tile v for this type. F32 rows spill
@@ -213,10 +221,41 @@ Choice choose_tile(int type, int64_t K, int64_t N, int64_t T, const Strides& s) 
     return best;
 }
 
-// The kernel one launch over all of dst would use.
+// Estimated time (us) of tile v over dst: rounds of one tile per CU, each
+// tile a loop over 32-row chunks of W at 128 F32 MACs per cycle per CU, at
+// the efficiency measured for the tile's rows of G (Q4_K N = 4096,
+// K = 14336: 32-row tiles about 0.6, larger ones about 0.85).
+double tile_estimate_us(int variant, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    const TileVariant* v = find_tile(variant);
+    if (!v) return 1e30;
+    const double rounds = double(cdiv(cdiv(T, v->bt) * cdiv(K, v->bk) * s.batches(), kNumCUs));
+    const double eff = v->bt <= 32 ? 0.6 : 0.85;
+    return 4.0 + rounds * double(cdiv(N, 32)) * double(v->bt) * v->bk * 32.0 / 128.0 / eff / 2400.0;
+}
+
+// The kernel one launch over all of dst would use: the skinny kernel for
+// T <= 16, and up to T = 64 where its estimate beats the best tile's (with
+// few tiles per CU the tiled kernels leave most CUs idle: Q4_K N = 4096,
+// K = 14336 at T = 17 .. 64 ran 183 us in 32 x 256 tiles).
 int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    if (skinny_applies(type, K, N, T, s)) return RETRO_VARIANT_SKINNY;
-    return choose_tile(type, K, N, T, s).id;
+    const bool skinny = skinny_applies(type, K, N, T, s);
+    if (skinny && T <= 16) return RETRO_VARIANT_SKINNY;
+    const Choice tile = choose_tile(type, K, N, T, s);
+    if (skinny && (tile.id < 0 || skinny_estimate_us(K, N, T) < tile_estimate_us(tile.id, K, N, T, s)))
+        return RETRO_VARIANT_SKINNY;
+    return tile.id;
+}
+
+// Whether the workspace calls take the split: an estimated gain of 10% or
+// more over what retro_out_prod runs, and at most 192 slabs. From 224 slabs
+// on (Q4_K, K = 14336) the split measured 1.04-1.24x the skinny kernel's
+// time: it reads W without the L2 sharing that the skinny kernel's
+// side-by-side slabs get.
+bool skinny_split_pays(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
+    if (cdiv(K, 64) > 192) return false;
+    const int v = choose(type, K, N, T, s);
+    const double one = v == RETRO_VARIANT_SKINNY ? skinny_estimate_us(K, N, T) : tile_estimate_us(v, K, N, T, s);
+    return skinny_split_estimate_us(K, N, T) <= 0.9 * one;
 }
 
 // A launch plan: variant v0 over dst columns [0, k_split), then, when
@@ -266,7 +305,7 @@ constexpr double kCuFlops = 157.3e12 / kNumCUs * 0.8;  // F32 FLOP/s of one CU a
 constexpr double kPlanMinSaving = 5e-6;                // seconds
 
 Plan plan_for(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    if (skinny_applies(type, K, N, T, s)) return {RETRO_VARIANT_SKINNY, K, 0};
+    if (choose(type, K, N, T, s) == RETRO_VARIANT_SKINNY) return {RETRO_VARIANT_SKINNY, K, 0};
     const Choice single = choose_tile(type, K, N, T, s);
     Plan best{single.id, K, 0};
     if (single.id <= 0 || N == 0) return best;
@@ -345,8 +384,8 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 // checked).
 bool variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     if (variant == RETRO_VARIANT_AUTO) return choose(type, K, N, T, s) > 0;
-    if (variant == RETRO_VARIANT_SKINNY || variant == RETRO_VARIANT_SKINNY_8 || variant == RETRO_VARIANT_SKINNY_16)
-        return skinny_applies(type, K, N, T, s);
+    if (variant == RETRO_VARIANT_SKINNY || variant == RETRO_VARIANT_SKINNY_8) return skinny_applies(type, K, N, T, s);
+    if (variant == RETRO_VARIANT_SKINNY_16) return T <= 16 && skinny_applies(type, K, N, T, s);
     if (variant == RETRO_VARIANT_SPLIT_128x256) {
         // the 128 x 256 producer/consumer tile's limits, for G by rows
         constexpr TileVariant tile{RETRO_VARIANT_SPLIT_128x256, 128, 256, 1.0, true};
@@ -489,10 +528,10 @@ int launch_split_typed(int type, const void* W, const float* G, float* dst, int6
 // Workspace bytes a call of `variant` uses for this (checked) shape: the
 // split's fixed size, 0 for any other kernel, or RETRO_E_VARIANT.
 int64_t workspace_need(int variant, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    if (variant == RETRO_VARIANT_SKINNY_SPLIT)
-        return skinny_split_applies(type, K, N, T, s) ? kSplitWorkspaceBytes : RETRO_E_VARIANT;
+    const int64_t bytes = split_workspace_bytes(skinny_blocks(T));
+    if (variant == RETRO_VARIANT_SKINNY_SPLIT) return skinny_split_applies(type, K, N, T, s) ? bytes : RETRO_E_VARIANT;
     if (variant == RETRO_VARIANT_AUTO)
-        return skinny_split_applies(type, K, N, T, s) && skinny_split_pays(K, N) ? kSplitWorkspaceBytes : 0;
+        return skinny_split_applies(type, K, N, T, s) && skinny_split_pays(type, K, N, T, s) ? bytes : 0;
     return variant_applies(variant, type, K, N, T, s) ? 0 : RETRO_E_VARIANT;
 }
 

@@ -102,18 +102,29 @@ int launch_out_prod(int variant, const void* W, const float* G, float* dst, int6
 template <int TYPE>
 int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t K, int64_t N, int64_t T,
                    int64_t ldy, hipStream_t st);
+// The skinny kernels take T up to 64, in blocks of 16 rows of G.
+constexpr int64_t kSkinnyMaxT = 64;
+inline int skinny_blocks(int64_t T) { return int(cdiv(T, 16)); }
+
 // The n-split skinny kernel's workspace: a counter word per workgroup
-// (kSplitCountBytes in all), then two 16 x 64 float slots per workgroup. The
-// counters must be zero before a call and are zero after it; the slots need
-// no initial value. Its grid is one workgroup per CU.
+// (kSplitCountBytes in all), then two slots of 16 x 64 floats per block of
+// 16 rows of G per workgroup. The counters must be zero before a call and
+// are zero after it; the slots need no initial value. Its grid is one
+// workgroup per CU.
 constexpr int kSplitGrid = kNumCUs;
 constexpr int64_t kSplitCountBytes = 4 * kSplitGrid;
-constexpr int64_t kSplitSlotBytes = 16 * 64 * 4;
-constexpr int64_t kSplitWorkspaceBytes = kSplitCountBytes + 2 * kSplitGrid * kSplitSlotBytes;
+constexpr int64_t kSplitSlotBytes = 16 * 64 * 4;  // per block of 16 rows of G
+constexpr int64_t split_workspace_bytes(int blocks) {
+    return kSplitCountBytes + 2 * kSplitGrid * kSplitSlotBytes * blocks;
+}
+// The n-split form takes T up to 48: at 64 its state would not fit the 256
+// registers of a wave without spilling.
+constexpr int64_t kSplitMaxT = 48;
+constexpr int64_t kSplitWorkspaceMax = split_workspace_bytes(int(kSplitMaxT / 16));
 static_assert(kSplitCountBytes % 256 == 0, "slots start 256-byte aligned");
 
 // One launch of the n-split skinny kernel (one matrix; applicability checked
-// by the caller), with a workspace of kSplitWorkspaceBytes.
+// by the caller), with a workspace of split_workspace_bytes(skinny_blocks(T)).
 template <int TYPE>
 int launch_out_prod_split(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
                           const Strides& s, void* workspace, hipStream_t st);

@@ -728,8 +728,9 @@ __device__ __forceinline__ void skinny_load4(const uint8_t* row, int k, int K, i
 
 // Per-lane raw data of one 16-row group (see out_prod_skinny_kernel for the
 // lane layout): the code words of the lane's 4 rows, the header words of the
-// (row, block) scale this lane decodes for the whole wave, and 4 G values.
-template <int TYPE>
+// (row, block) scale this lane decodes for the whole wave, and 4 G values
+// for each of the TB blocks of 16 rows of G.
+template <int TYPE, int TB = 1>
 struct SkinnyRaw {
     static constexpr int CW = (TYPE == kF32) ? 4
                               : (TYPE == kF16 || TYPE == kBF16 || TYPE == kQ5_K || TYPE == kQ6_K || TYPE == kQ3_K) ? 2
@@ -739,7 +740,7 @@ struct SkinnyRaw {
                                                                                    : 1;
     uint32_t code[4][CW];
     uint32_t hdr[HW];
-    float g[4];
+    float g[TB][4];
 };
 
 // Byte offsets, relative to the first W row / G column of a 16-row group,
@@ -750,14 +751,14 @@ struct SkinnyOffsets {
     uint32_t code2[4];  // Q5_K fifth bits / Q6_K high parts of the same elements
     uint32_t hdr;       // header of the scale pair this lane decodes (Q6_K, Q2_K, Q3_K: see skinny_offsets)
     uint32_t hdr2;      // Q6_K, Q2_K: the scales of that row
-    uint32_t g;         // G[min(l%16, T-1)][n0 + 4*(l/16)] (bytes from G[0][n0])
+    uint32_t g[4];      // G[min(16 tb + l%16, T-1)][n0 + 4*(l/16)] for t-block tb (bytes from G[0][n0])
 };
 
 // Fast path (K % 4 == 0, G rows 16-byte aligned or G stored t-fastest,
 // whole group inside W). Columns at or beyond K and rows of G at or beyond T
 // are clamped to valid addresses: they only feed dst columns and rows that
 // are never stored.
-template <int TYPE>
+template <int TYPE, int TB = 1>
 __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int k0, int lane) {
     const int j = lane & 15, rq = lane >> 4;
     const int K = a.K;
@@ -827,14 +828,17 @@ __device__ __forceinline__ SkinnyOffsets skinny_offsets(const SkinnyArgs& a, int
             o.hdr = rowb + 96;
         }
     }
-    const long long gt = min(j, a.T - 1);
-    o.g = uint32_t((a.gcols ? 4 * rq * a.ldg + gt : gt * a.ldg + 4 * rq) * 4);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const long long gt = min(16 * tb + j, a.T - 1);
+        o.g[tb] = uint32_t((a.gcols ? 4 * rq * a.ldg + gt : gt * a.ldg + 4 * rq) * 4);
+    }
     return o;
 }
 
-template <int TYPE>
+template <int TYPE, int TB>
 __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, const SkinnyOffsets& o,
-                                                  SkinnyRaw<TYPE>& r) {
+                                                  SkinnyRaw<TYPE, TB>& r) {
     // n0 is the same in every lane; readfirstlane makes that visible to the
     // compiler, so the two descriptors (this group's 16 W rows; the G columns
     // from n0 on) are built in scalar registers and every load is a fixed
@@ -848,13 +852,18 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
             buffer_rsrc(a.G + (long long)n0 * a.ldg, uint32_t(4 * (15 * a.ldg + a.T)));
         const uint32_t step = uint32_t(4 * a.ldg);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            r.g[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, o.g + q * step, 0, 0));
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r.g[tb][q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, o.g[tb] + q * step, 0, 0));
     } else {
         const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(a.G + n0, uint32_t(4 * ((long long)(a.T - 1) * a.ldg + 16)));
-        const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(gr, o.g, 0, 0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r.g[q] = __uint_as_float(gv[q]);
+        for (int tb = 0; tb < TB; ++tb) {
+            const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(gr, o.g[tb], 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r.g[tb][q] = __uint_as_float(gv[q]);
+        }
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -910,27 +919,31 @@ __device__ __forceinline__ void skinny_fetch_fast(const SkinnyArgs& a, int n0, c
 }
 
 // Any group and shape: out-of-range elements read as zero.
-template <int TYPE>
+template <int TYPE, int TB>
 __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0, int k0, int lane,
-                                                    SkinnyRaw<TYPE>& r) {
+                                                    SkinnyRaw<TYPE, TB>& r) {
     const int j = lane & 15, rq = lane >> 4;
     const int K = a.K, N = a.N;
     const int nq = n0 + 4 * rq;
     const int kl = k0 + 4 * j;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r.g[s] = 0.f;
-    if (j < a.T) {
-        // G[j][nq + s]
-        const long long gs = a.gcols ? a.ldg : 1;
-        const float* gp = a.G + (a.gcols ? (long long)nq * a.ldg + j : (long long)j * a.ldg + nq);
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = 16 * tb + j;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            if (nq + s < N) r.g[s] = gp[s * gs];
+        for (int s = 0; s < 4; ++s) r.g[tb][s] = 0.f;
+        if (t < a.T) {
+            // G[t][nq + s]
+            const long long gs = a.gcols ? a.ldg : 1;
+            const float* gp = a.G + (a.gcols ? (long long)nq * a.ldg + t : (long long)t * a.ldg + nq);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (nq + s < N) r.g[tb][s] = gp[s * gs];
+        }
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int w = 0; w < SkinnyRaw<TYPE>::CW; ++w) r.code[s][w] = 0u;
+        for (int w = 0; w < SkinnyRaw<TYPE, TB>::CW; ++w) r.code[s][w] = 0u;
         if (nq + s >= N) continue;
         const uint8_t* row = a.W + (long long)(nq + s) * a.pitch;
         if constexpr (TYPE == kF32) {
@@ -997,7 +1010,7 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
         const int e0 = k0 & 255, h = e0 >> 7, p0 = (e0 >> 5) & 3, w = lane & 3;
         const int si = 8 * h + 2 * (p0 + (w >> 1)) + (w & 1);
 #pragma unroll
-        for (int i = 0; i < SkinnyRaw<TYPE>::HW; ++i) r.hdr[i] = 0u;
+        for (int i = 0; i < SkinnyRaw<TYPE, TB>::HW; ++i) r.hdr[i] = 0u;
         if (n0 + (lane >> 2) < N) {
             const uint8_t* sb = a.W + (long long)(n0 + (lane >> 2)) * a.pitch + (k0 >> 8) * Format<TYPE>::kBytes;
             if constexpr (TYPE == kQ6_K) {
@@ -1025,7 +1038,7 @@ __device__ __forceinline__ void skinny_fetch_masked(const SkinnyArgs& a, int n0,
         constexpr int HH = TYPE == kQ8_0 ? 1 : (kHeader<TYPE> / 2 < 4 ? kHeader<TYPE> / 2 : 4);
         const int kb = k0 + 32 * sel;
 #pragma unroll
-        for (int i = 0; i < SkinnyRaw<TYPE>::HW; ++i) r.hdr[i] = 0u;
+        for (int i = 0; i < SkinnyRaw<TYPE, TB>::HW; ++i) r.hdr[i] = 0u;
         if (hvalid && kb < K) {
             const uint16_t* h = reinterpret_cast<const uint16_t*>(hrow + (kb >> 5) * Format<TYPE>::kBytes);
 #pragma unroll
@@ -1041,8 +1054,8 @@ __device__ __forceinline__ float lane_value(float v, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
-template <int TYPE>
-__device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, int lane, float wv[4][4]) {
+template <int TYPE, int TB>
+__device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE, TB>& r, int k0, int lane, float wv[4][4]) {
     const int j = lane & 15, rq = lane >> 4;
     const int hi = (j >= 8) ? 1 : 0;  // second block / sub-block of the 64-column slab
     if constexpr (TYPE == kF32) {
@@ -1140,16 +1153,18 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE>& r, int k0, 
     }
 }
 
-// dst[t][k0 .. k0+63] for all t < T (T <= 16). MFMA 16x16x4 operands: lane l
-// supplies A[i = l%16][kk = l/16] and B[kk = l/16][j = l%16]. Step s of a
-// 16-row group starting at n0 uses W row n0 + 4*(l/16) + s for lane l, so a
-// lane reads G[t][n0 + 4*(l/16) .. +3] with one float4. Column j of
-// accumulator block b is dst column k0 + 4*j + b, so a lane decodes 4
-// consecutive elements per row. Each wave walks its own 16-row groups with
-// the next group's loads in flight while the current one is decoded and
-// contracted; the scale of each (row, block) is decoded by one lane and
-// handed to the lanes that need it.
-template <int TYPE, int NWAVES, bool FAST>
+// dst[t][k0 .. k0+63] for all t < T (T <= 16 TB). MFMA 16x16x4 operands:
+// lane l supplies A[i = l%16][kk = l/16] and B[kk = l/16][j = l%16]. Step s
+// of a 16-row group starting at n0 uses W row n0 + 4*(l/16) + s for lane l,
+// so a lane reads G[t][n0 + 4*(l/16) .. +3] with one float4 per block of 16
+// rows of G. Column j of accumulator block b is dst column k0 + 4*j + b, so a
+// lane decodes 4 consecutive elements per row; each decoded element feeds
+// one MFMA per block of 16 rows of G (TB of them), so the decode is shared
+// by all of T. Each wave walks its own 16-row groups with the next group's
+// loads in flight while the current one is decoded and contracted; the scale
+// of each (row, block) is decoded by one lane and handed to the lanes that
+// need it.
+template <int TYPE, int NWAVES, bool FAST, int TB>
 __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs args) {
     constexpr int KS = 64;  // dst columns per workgroup
     __shared__ __attribute__((aligned(16))) float part[NWAVES * 16 * KS];
@@ -1163,22 +1178,26 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
     const int k0 = xcd_remap(blockIdx.x, gridDim.x) * KS;
     const int j = lane & 15, rq = lane >> 4;
 
-    f32x4 acc[4];
+    f32x4 acc[TB][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[tb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Decode a whole group, then issue its 16 MFMAs back to back (the fences
-    // keep the compiler from interleaving each MFMA with the decode of its
-    // own operand, which would stall on that dependency).
-    auto contract = [&](const SkinnyRaw<TYPE>& r) {
+    // Decode a whole group, then issue its 16 TB MFMAs back to back (the
+    // fences keep the compiler from interleaving each MFMA with the decode
+    // of its own operand, which would stall on that dependency).
+    auto contract = [&](const SkinnyRaw<TYPE, TB>& r) {
         float wv[4][4];
         skinny_decode<TYPE>(r, k0, lane, wv);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.g[s], wv[s][b], acc[b], 0, 0, 0);
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.g[tb][s], wv[s][b], acc[tb][b], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -1191,20 +1210,20 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
     if (g < nfull) {
         const int last = nfull - 1;
         const int cnt = (nfull - wave + NWAVES - 1) / NWAVES;  // groups of this wave
-        const SkinnyOffsets off = skinny_offsets<TYPE>(args, k0, lane);
+        const SkinnyOffsets off = skinny_offsets<TYPE, TB>(args, k0, lane);
         auto row0 = [&](int i) { return 16 * min(wave + i * NWAVES, last); };
-        SkinnyRaw<TYPE> r0, r1, r2;
-        skinny_fetch_fast<TYPE>(args, row0(0), off, r0);
-        skinny_fetch_fast<TYPE>(args, row0(1), off, r1);
+        SkinnyRaw<TYPE, TB> r0, r1, r2;
+        skinny_fetch_fast(args, row0(0), off, r0);
+        skinny_fetch_fast(args, row0(1), off, r1);
         // whole triples: no branch inside, so the loads of the next two groups
         // stay in flight while a group is contracted
         const int triples = cnt / 3;
         for (int t3 = 0, i = 0; t3 < triples; ++t3, i += 3) {
-            skinny_fetch_fast<TYPE>(args, row0(i + 2), off, r2);
+            skinny_fetch_fast(args, row0(i + 2), off, r2);
             contract(r0);
-            skinny_fetch_fast<TYPE>(args, row0(i + 3), off, r0);
+            skinny_fetch_fast(args, row0(i + 3), off, r0);
             contract(r1);
-            skinny_fetch_fast<TYPE>(args, row0(i + 4), off, r1);
+            skinny_fetch_fast(args, row0(i + 4), off, r1);
             contract(r2);
         }
         // 0, 1 or 2 groups left, already in r0 and r1
@@ -1215,26 +1234,31 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
     }
     // Remaining (partial, or all groups of a shape off the fast path), masked.
     for (; 16 * g < N; g += NWAVES) {
-        SkinnyRaw<TYPE> r;
-        skinny_fetch_masked<TYPE>(args, 16 * g, k0, lane, r);
+        SkinnyRaw<TYPE, TB> r;
+        skinny_fetch_masked(args, 16 * g, k0, lane, r);
         contract(r);
     }
 
     // D layout of v_mfma_f32_16x16x4f32: lane l, register v holds row
     // 4*(l/16) + v, column l%16. Partials of each wave go to LDS, then are
-    // summed over waves in increasing wave order (deterministic).
+    // summed over waves in increasing wave order (deterministic), one block
+    // of 16 rows of G at a time.
     float* mine = part + wave * 16 * KS;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int tb = 0; tb < TB; ++tb) {
+        if (tb > 0) __syncthreads();  // the previous block's sums are read
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mine[(4 * rq + v) * KS + 4 * j + b] = acc[b][v];
-    __syncthreads();
-    for (int o = tid; o < 16 * KS; o += NWAVES * 64) {
-        const int tr = o / KS, kk = o - tr * KS;
-        float sum = part[o];
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int w = 1; w < NWAVES; ++w) sum += part[w * 16 * KS + o];
-        if (tr < T && k0 + kk < K) args.dst[(long long)tr * args.ldd + k0 + kk] = sum;
+            for (int v = 0; v < 4; ++v) mine[(4 * rq + v) * KS + 4 * j + b] = acc[tb][b][v];
+        __syncthreads();
+        for (int o = tid; o < 16 * KS; o += NWAVES * 64) {
+            const int tr = 16 * tb + o / KS, kk = o % KS;
+            float sum = part[o];
+#pragma unroll
+            for (int w = 1; w < NWAVES; ++w) sum += part[w * 16 * KS + o];
+            if (tr < T && k0 + kk < K) args.dst[(long long)tr * args.ldd + k0 + kk] = sum;
+        }
     }
 }
 
@@ -1255,23 +1279,24 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
 // be part of a slab, so each workgroup owns two slots, and the counter of a
 // split slab belongs to the workgroup holding its first group (no workgroup
 // holds the first group of two split slabs): the workspace is a fixed
-// 2 x 4 KB + 4 bytes per workgroup whatever the shape. Slots and counters are
+// 2 x 4 TB KiB + 4 bytes per workgroup whatever the shape. Slots and counters are
 // read and written at device scope (the pieces of a slab may run on
 // different XCDs); every counter is back at zero when the call ends. There is
 // no waiting on other workgroups: each one runs to its end whatever the
 // others do.
 struct SkinnySplitArgs {
     unsigned* count;  // one word per workgroup: pieces of its counted slab finished so far
-    float* slots;     // 16 x 64 floats per (workgroup, first or last piece)
+    float* slots;     // 16 TB x 64 floats per (workgroup, first or last piece)
     int ng;           // 16-row groups per slab (N / 16)
     long long share;  // groups per workgroup
 };
 
-template <int TYPE, int NWAVES>
+template <int TYPE, int NWAVES, int TB>
 __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(SkinnyArgs args, SkinnySplitArgs sp) {
     constexpr int KS = 64;
-    constexpr int PER = 16 * KS / (NWAVES * 64);  // slab outputs per thread
-    static_assert(PER * NWAVES * 64 == 16 * KS, "whole outputs per thread");
+    constexpr int SLOT = 16 * TB * KS;            // floats of a slot: all of T by the slab's columns
+    constexpr int PER = SLOT / (NWAVES * 64);     // slab outputs per thread
+    static_assert(PER * NWAVES * 64 == SLOT, "whole outputs per thread");
     __shared__ __attribute__((aligned(16))) float part[NWAVES * 16 * KS];
     __shared__ unsigned finisher[2];
 
@@ -1306,31 +1331,35 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(Skin
     auto last_share = [&](int s) { return int(((long long)s * ng + ng - 1) / sp.share); };
 
     Piece cur = piece_at(begin);
-    SkinnyOffsets off = skinny_offsets<TYPE>(args, cur.s * KS, lane);
-    SkinnyRaw<TYPE> r0, r1, r2;
+    SkinnyOffsets off = skinny_offsets<TYPE, TB>(args, cur.s * KS, lane);
+    SkinnyRaw<TYPE, TB> r0, r1, r2;
     // The first two groups of a piece for this wave, as the group loop
     // expects them (a repeat of a valid group past the wave's last one).
     auto prefetch = [&](const Piece& pc, const SkinnyOffsets& o) {
         const int g0 = min(pc.a + wave, pc.b - 1);
-        skinny_fetch_fast<TYPE>(args, 16 * g0, o, r0);
-        skinny_fetch_fast<TYPE>(args, 16 * min(g0 + NWAVES, pc.b - 1), o, r1);
+        skinny_fetch_fast(args, 16 * g0, o, r0);
+        skinny_fetch_fast(args, 16 * min(g0 + NWAVES, pc.b - 1), o, r1);
     };
     prefetch(cur, off);
 
     for (;;) {
         const int k0 = cur.s * KS;
-        f32x4 acc[4];
+        f32x4 acc[TB][4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto contract = [&](const SkinnyRaw<TYPE>& r) {
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[tb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto contract = [&](const SkinnyRaw<TYPE, TB>& r) {
             float wv[4][4];
             skinny_decode<TYPE>(r, k0, lane, wv);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.g[q], wv[q][c], acc[c], 0, 0, 0);
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[tb][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.g[tb][q], wv[q][c], acc[tb][c], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         };
         // groups a + wave, a + wave + NWAVES, ... below b: the skinny
@@ -1342,11 +1371,11 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(Skin
             auto row0 = [&](int i) { return 16 * min(g0 + i * NWAVES, last); };
             const int triples = cnt / 3;
             for (int t3 = 0, i = 0; t3 < triples; ++t3, i += 3) {
-                skinny_fetch_fast<TYPE>(args, row0(i + 2), off, r2);
+                skinny_fetch_fast(args, row0(i + 2), off, r2);
                 contract(r0);
-                skinny_fetch_fast<TYPE>(args, row0(i + 3), off, r0);
+                skinny_fetch_fast(args, row0(i + 3), off, r0);
                 contract(r1);
-                skinny_fetch_fast<TYPE>(args, row0(i + 4), off, r1);
+                skinny_fetch_fast(args, row0(i + 4), off, r1);
                 contract(r2);
             }
             const int left = cnt - 3 * triples;
@@ -1358,30 +1387,35 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(Skin
         // the next piece's first loads are in flight while this one is reduced
         if (next_at < end) {
             cur = piece_at(next_at);
-            off = skinny_offsets<TYPE>(args, cur.s * KS, lane);
+            off = skinny_offsets<TYPE, TB>(args, cur.s * KS, lane);
             prefetch(cur, off);
         }
 
-        // The skinny kernel's reduction over waves, in wave order.
-        float* mine = part + wave * 16 * KS;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) mine[(4 * rq + v) * KS + 4 * j + c] = acc[c][v];
-        __syncthreads();
+        // The skinny kernel's reduction over waves, in wave order, one block
+        // of 16 rows of G at a time.
         const bool whole = (done.a == 0 && done.b == ng);
         // slot 2p for the share's first piece, 2p + 1 for its last
-        float* slot = sp.slots + (2ll * p + (done.s != first_slab)) * (16 * KS);
-        for (int o = tid; o < 16 * KS; o += NWAVES * 64) {
-            const int tr = o / KS, kk = o - tr * KS;
-            float sum = part[o];
+        float* slot = sp.slots + (2ll * p + (done.s != first_slab)) * SLOT;
+        float* mine = part + wave * 16 * KS;
 #pragma unroll
-            for (int w = 1; w < NWAVES; ++w) sum += part[w * 16 * KS + o];
-            if (whole) {
-                if (tr < T && done.s * KS + kk < K) args.dst[(long long)tr * args.ldd + done.s * KS + kk] = sum;
-            } else {
-                __hip_atomic_store(reinterpret_cast<unsigned*>(slot) + o, __float_as_uint(sum), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int tb = 0; tb < TB; ++tb) {
+            if (tb > 0) __syncthreads();  // the previous block's sums are read
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) mine[(4 * rq + v) * KS + 4 * j + c] = acc[tb][c][v];
+            __syncthreads();
+            for (int o = tid; o < 16 * KS; o += NWAVES * 64) {
+                const int tr = 16 * tb + o / KS, kk = o % KS;
+                float sum = part[o];
+#pragma unroll
+                for (int w = 1; w < NWAVES; ++w) sum += part[w * 16 * KS + o];
+                if (whole) {
+                    if (tr < T && done.s * KS + kk < K) args.dst[(long long)tr * args.ldd + done.s * KS + kk] = sum;
+                } else {
+                    __hip_atomic_store(reinterpret_cast<unsigned*>(slot) + tb * 16 * KS + o, __float_as_uint(sum),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
         if (!whole) {
@@ -1415,8 +1449,7 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(Skin
         // Slot of share q0 + c: its first piece's (2q) unless slab s is not
         // where that share starts (2q + 1). Device-scope loads (sc1), a round
         // of four slots in flight at once.
-        const __amdgpu_buffer_rsrc_t slots =
-            buffer_rsrc(sp.slots + 2ll * q0 * (16 * KS), uint32_t(2 * npieces * 16 * KS * 4));
+        const __amdgpu_buffer_rsrc_t slots = buffer_rsrc(sp.slots + 2ll * q0 * SLOT, uint32_t(2 * npieces * SLOT * 4));
         auto slot_of = [&](int c) {
             const int q = q0 + c;
             return 2 * c + (int((long long)q * sp.share / ng) != s ? 1 : 0);
@@ -1426,7 +1459,7 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(Skin
             float v[4][PER];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint32_t base = uint32_t(slot_of(c0 + c) * 16 * KS * 4);
+                const uint32_t base = uint32_t(slot_of(c0 + c) * SLOT * 4);
 #pragma unroll
                 for (int m = 0; m < PER; ++m)
                     v[c][m] = c0 + c < npieces
@@ -1446,7 +1479,7 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_split_kernel(Skin
         }
 #pragma unroll
         for (int m = 0; m < PER; ++m) {
-            const int o = tid + m * NWAVES * 64, tr = o / KS, kk = o - tr * KS;
+            const int o = tid + m * NWAVES * 64, tr = o / KS, kk = o % KS;  // slot row tr = 16 tb + row of the block
             if (tr < T && s * KS + kk < K) args.dst[(long long)tr * args.ldd + s * KS + kk] = sum[m];
         }
         if (tid == 0) __hip_atomic_store(sp.count + q0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -142,20 +142,22 @@ int launch_split(const void* W, const float* G, float* dst, int64_t K, int64_t N
 // for Q4_0, Q4_1, Q5_0, MXFP4 and Q5_K, 0.96-0.98x for Q4_K, Q6_K, Q8_0,
 // Q5_1, F16 and BF16, and the same for Q3_K and F32; at T = 8 and 4, 0.94-0.95x
 // for Q4_0 and Q6_K and 0.98 for BF16. Sixteen stay faster for Q2_K and NVFP4
-// (by 2-3%) and for Q4_K below T = 12 (1-4%).
+// (by 2-3%) and for Q4_K below T = 12 (1-4%). Above T = 16 the accumulators
+// of the extra blocks of G take the registers of a 16-wave workgroup: eight.
 int skinny_waves(int type, int64_t T) {
+    if (T > 16) return 8;
     if (type == RETRO_Q2_K || type == RETRO_NVFP4) return 16;
     if (type == RETRO_Q4_K && T < 12) return 16;
     return 8;
 }
 
-template <int TYPE, int kWaves>
+template <int TYPE, int kWaves, int TB>
 void launch_skinny_waves(const SkinnyArgs& a, dim3 grid, hipStream_t st) {
     const dim3 block(kWaves * 64);
     if (a.wide && a.gvec)
-        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, true, TB>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((out_prod_skinny_kernel<TYPE, kWaves, false, TB>), grid, block, 0, st, a);
 }
 
 SkinnyArgs skinny_args(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
@@ -183,10 +185,17 @@ int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t 
     const SkinnyArgs a = skinny_args(W, G, dst, K, N, T, s);
     const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches()));
     clear_last_error();
-    if (waves == 8)
-        launch_skinny_waves<TYPE, 8>(a, grid, st);
-    else
-        launch_skinny_waves<TYPE, 16>(a, grid, st);
+    switch (skinny_blocks(T)) {
+        case 1:
+            if (waves == 8)
+                launch_skinny_waves<TYPE, 8, 1>(a, grid, st);
+            else
+                launch_skinny_waves<TYPE, 16, 1>(a, grid, st);
+            break;
+        case 2: launch_skinny_waves<TYPE, 8, 2>(a, grid, st); break;
+        case 3: launch_skinny_waves<TYPE, 8, 3>(a, grid, st); break;
+        default: launch_skinny_waves<TYPE, 8, 4>(a, grid, st); break;
+    }
     return launch_status();
 }
 
@@ -324,10 +333,18 @@ int launch_out_prod_split(const void* W, const float* G, float* dst, int64_t K, 
     sp.ng = int(N / 16);
     sp.share = cdiv(cdiv(K, 64) * (N / 16), kSplitGrid);
     clear_last_error();
-    if (skinny_waves(TYPE, T) == 8)
-        hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 8>), dim3(kSplitGrid), dim3(512), 0, st, a, sp);
-    else
-        hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 16>), dim3(kSplitGrid), dim3(1024), 0, st, a, sp);
+    const dim3 grid(kSplitGrid), b8(512), b16(1024);
+    switch (skinny_blocks(T)) {
+        case 1:
+            if (skinny_waves(TYPE, T) == 8)
+                hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 8, 1>), grid, b8, 0, st, a, sp);
+            else
+                hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 16, 1>), grid, b16, 0, st, a, sp);
+            break;
+        case 2: hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 8, 2>), grid, b8, 0, st, a, sp); break;
+        case 3: hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 8, 3>), grid, b8, 0, st, a, sp); break;
+        default: return RETRO_E_VARIANT;  // T > kSplitMaxT: the caller does not ask for it
+    }
     return launch_status();
 }
 

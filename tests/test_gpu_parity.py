@@ -197,6 +197,26 @@ def test_skinny_matches_oracle(q, wtype, T, N):
             check_close(run(q, c, v), acc, ab, v + " at small T")
 
 
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("T,N", [(17, 77), (33, 300), (48, 96), (64, 33), (40, 1)])
+def test_skinny_blocks_of_t_match_oracle(q, wtype, T, N):
+    """Up to T = 64 the skinny kernel feeds each decoded weight to every block
+    of 16 rows of G (ragged last block, N ragged and below a group)."""
+    c = wl.make_case(wtype, N, SMALL_K[wtype][1], T, seed=320 + T + N)
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], c["K"], nthreads=ORACLE_THREADS)
+    assert applies(q, c, "skinny") and applies(q, c, "skinny_8") and not applies(q, c, "skinny_16")
+    for v in ("skinny", "skinny_8", "auto"):
+        check_close(run(q, c, v), acc, ab, v)
+    # G stored t-fastest and a padded dst through the strided views
+    W, G = dev(c["W"]), dev(c["G"])
+    gt = torch.zeros((N, T + 5), device="cuda")
+    gt[:, :T] = G.t()
+    out = torch.full((T, c["K"] + 4), float("nan"), device="cuda")[:, 4:]
+    q.out_prod(wtype, W, gt[:, :T].t(), c["K"], out=out, variant=q.VARIANT_SKINNY)
+    torch.cuda.synchronize()
+    check_close(out.cpu().numpy(), acc, ab, "skinny, G t-fastest")
+
+
 def test_q8_0_tiny_workload(q):
     c = wl.workload("q8_0_n128_k256_t64")
     dst, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"])
@@ -214,10 +234,13 @@ def test_f32_twin_on_device(q, wtype):
     twin = dict(c, type=wl.F32, W=w32.view(np.uint8))
     # the skinny kernel with its wave count pinned: the automatic count
     # depends on the type (and sets the order of the cross-wave sum)
-    for v in tile_variants(wtype) + ["skinny_8", "skinny_16"]:
-        if not applies(q, twin, v) or not applies(q, c, v):
+    for v in tile_variants(wtype) + ["skinny_8", "skinny_16", "skinny_8_t40"]:
+        if v == "skinny_8_t40":  # three blocks of 16 rows of G
+            c2, t2 = dict(c, T=40, G=c["G"][:40]), dict(twin, T=40, G=c["G"][:40])
+            v = "skinny_8"
+        elif not applies(q, twin, v) or not applies(q, c, v):
             continue
-        if v.startswith("skinny"):
+        elif v.startswith("skinny"):
             c2, t2 = dict(c, T=16, G=c["G"][:16]), dict(twin, T=16, G=c["G"][:16])
         else:
             c2, t2 = c, twin
@@ -321,7 +344,7 @@ def test_device_side_argument_errors(q):
     assert lib.retro_out_prod_variant(q.VARIANT_TILE_128x128, *args(W.data_ptr(), G.data_ptr(),
                                                                    out.data_ptr())) == q.E_VARIANT
     with pytest.raises(q.RetroError):
-        q.out_prod(wl.Q4_K, W, G, K, variant=q.VARIANT_SKINNY)  # T > 16
+        q.out_prod(wl.Q4_K, W, G, K, variant=q.VARIANT_SKINNY)  # T > 64
 
 
 def test_runs_on_the_given_stream(q):
@@ -378,7 +401,7 @@ def test_strided_operands_match_oracle(q, wtype, K, N, T, gpad, wpad):
         assert bool((rest == 7.0).all()), v
         ran.append(v)
     families = {v.split("_")[0].rstrip("2") for v in ran if v != "auto"}
-    assert ("skinny" in families) == (T <= 16), ran
+    assert ("skinny" in families) == (T <= 64), ran
     if T > 16:
         assert "tile" in families and (("ws" in families) == (ldg % 4 == 0)), ran
 
@@ -435,7 +458,7 @@ def test_g_columns_match_rows_and_oracle(q, wtype, K, N, T, pad):
             assert np.array_equal(got.view(np.uint32), ref.cpu().numpy().view(np.uint32)), v
         ran.append(v)
     families = {v.split("_")[0].rstrip("2") for v in ran if v != "auto"}
-    assert ("skinny" in families) == (T <= 16), ran
+    assert ("skinny" in families) == (T <= 64), ran
     dense_odd = wtype in (wl.F32, wl.F16, wl.BF16) and K % 4 != 0
     if T > 16:
         assert "tile" in families and (("ws" in families) == (ldg % 4 == 0 and not dense_odd)), ran

@@ -56,7 +56,8 @@ def block_k(wtype, slabs_wanted):
 # (slabs, N, T): shares of a few groups (idle waves, many pieces per slab),
 # of about a slab, and longer than a slab (whole slabs inside a share: 260
 # slabs); N = 16 puts every slab whole in one share.
-SHAPES = [(12, 1024, 16), (12, 16, 5), (40, 4096, 1), (100, 2048, 16), (260, 32, 3)]
+SHAPES = [(12, 1024, 16), (12, 16, 5), (40, 4096, 1), (100, 2048, 16), (260, 32, 3), (20, 512, 40), (30, 256, 48),
+          (12, 1024, 17)]
 
 
 @pytest.mark.parametrize("wtype", TYPES)
@@ -75,11 +76,12 @@ def test_split_matches_oracle(q, ws, wtype, slabs, N, T):
 
 
 @pytest.mark.parametrize("wtype", [t for t in TYPES if t not in (wl.F32, wl.Q2_K, wl.NVFP4)])
-def test_split_f32_twin(q, ws, wtype):
+@pytest.mark.parametrize("T", [16, 33])
+def test_split_f32_twin(q, ws, wtype, T):
     """The split on Qx and on F32 rows holding the decoded values sum the same
-    products in the same order (both with eight waves at T = 16)."""
+    products in the same order (both with eight waves)."""
     K = block_k(wtype, 30)
-    c = wl.make_case(wtype, 512, K, 16, seed=950)
+    c = wl.make_case(wtype, 512, K, T, seed=950)
     w32 = oracle.dequantize(wtype, c["W"], K)
     twin = dict(c, type=wl.F32, W=w32.view(np.uint8))
     a, b = split(q, ws, c), split(q, ws, twin)
