@@ -198,22 +198,23 @@ const char *retro_strerror(int code);
  * Kernel variants (for tests and benchmarks; retro_out_prod chooses one):
  *   RETRO_VARIANT_AUTO      what retro_out_prod runs (one variant, or two over
  *                           column ranges of dst: retro_out_prod_plan)
- *   RETRO_VARIANT_SKINNY    one pass over W, all of n per workgroup, each
- *                           decoded weight feeding one MFMA per block of 16
- *                           rows of G; T <= 64 (8 or 16 waves per workgroup
- *                           up to T = 16, chosen by type and T, and 8 above;
- *                           the two are summed in different orders).
- *                           retro_out_prod runs it for T <= 16, and up to
- *                           T = 64 where its estimate beats the tiles' (with
- *                           few tiles per CU)
+ *   RETRO_VARIANT_SKINNY    one pass over W per 64 rows of G, all of n per
+ *                           workgroup, each decoded weight feeding one MFMA
+ *                           per block of 16 rows of G (8 or 16 waves per
+ *                           workgroup up to T = 16, chosen by type and T,
+ *                           and 8 above; the two are summed in different
+ *                           orders). retro_out_prod runs it for T <= 16, and
+ *                           above where its estimate beats the tiles' (with
+ *                           few tiles per CU; by 10% past one pass)
  *   RETRO_VARIANT_SKINNY_8, RETRO_VARIANT_SKINNY_16  the skinny kernel with
  *                           that many waves per workgroup (16: T <= 16)
  *   RETRO_VARIANT_SKINNY_SPLIT  retro_out_prod_ws only: the skinny kernel's
  *                           groups of 16 W rows, all slabs of 64 dst columns
  *                           in turn, cut into one equal share per CU, the
  *                           parts of a slab added through a workspace (see
- *                           retro_out_prod_ws). T <= 48, N % 16 == 0,
- *                           K % 4 == 0, G rows in 16-byte units
+ *                           retro_out_prod_ws), one pass over W per 48
+ *                           rows of G. N % 16 == 0, K % 4 == 0, G rows in
+ *                           16-byte units, one matrix
  *   RETRO_VARIANT_TILE_*    tiled F32-MFMA kernel, tile = rows of T x columns
  *                           of K per workgroup (256-column tiles need K tiles
  *                           that are whole K-quant super-blocks; the K-quants
@@ -457,7 +458,7 @@ int retro_out_prod_column_split(int variant0, int64_t k_split, int variant1, int
  * section "What") and contract, for contiguous operands. The skinny kernel
  * gives each 64-column slab of dst to one workgroup, so with fewer slabs than
  * CUs (K below 16384) part of the GPU idles; RETRO_VARIANT_SKINNY_SPLIT
- * (T <= 48) spreads the rows of W evenly over all CUs and adds the parts of
+ * spreads the rows of W evenly over all CUs and adds the parts of
  * each slab through the workspace (measured on MI355X, Q4_K, T = 16:
  * K = 4096, N = 14336 in 27 us against 79 us; K = 4096, N = 4096 in 11.5
  * against 25 us; at T = 32, K = 4096, N = 14336: 44 against 131 us).
@@ -467,8 +468,8 @@ int retro_out_prod_column_split(int variant0, int64_t k_split, int variant1, int
  *               retro_out_prod_variant, RETRO_VARIANT_SKINNY_SPLIT included
  *   workspace   device memory of workspace_bytes bytes, 16-byte aligned,
  *               overlapping none of W, G and dst; the split uses 1 KiB +
- *               2 MiB per block of 16 rows of G, at most 6 MiB + 1 KiB
- *               (retro_out_prod_workspace_size). Its first
+ *               2 MiB per block of 16 rows of G in a pass, at most
+ *               6 MiB + 1 KiB (retro_out_prod_workspace_size). Its first
  *               1 KiB holds counters that must be zero before the first call
  *               that uses it (zero the whole workspace once); every call
  *               leaves them at zero, so later calls need no clearing. Calls

@@ -138,15 +138,16 @@ bool tile_applies(const TileVariant& v, int type, int64_t K, int64_t N, int64_t 
            33 * s.ldw < (int64_t(1) << 31);
 }
 
-// The skinny kernel (T <= 64) addresses one 16-row group of W, and the T
-// rows of G it reads (16 columns, when G is stored t-fastest: at most 16 ldg
-// floats), through buffer descriptors whose sizes are signed 32-bit.
+// The skinny kernel runs one pass over W per 64 rows of G. A pass addresses
+// one 16-row group of W, and the rows of G it reads (16 columns, when G is
+// stored t-fastest: at most 16 ldg floats), through buffer descriptors whose
+// sizes are signed 32-bit.
 bool skinny_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     (void)type;
     (void)N;
-    const int64_t g_span = s.gcols ? 16 * s.ldg + T : (T > 16 ? T : 16) * s.ldg + 16;
-    return T <= kSkinnyMaxT && cdiv(K, 64) < kGridLimit && 16 * s.ldw < (int64_t(1) << 31) &&
-           g_span * 4 < (int64_t(1) << 31);
+    const int64_t tp = T < kSkinnyMaxT ? T : kSkinnyMaxT;  // rows of G per pass
+    const int64_t g_span = s.gcols ? 16 * s.ldg + tp : (tp > 16 ? tp : 16) * s.ldg + 16;
+    return cdiv(K, 64) < kGridLimit && 16 * s.ldw < (int64_t(1) << 31) && g_span * 4 < (int64_t(1) << 31);
 }
 
 // Estimated time (us) of the skinny kernel: per 16-row group and wave, 512
@@ -155,17 +156,28 @@ bool skinny_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s)
 // and about 4 us of launch and reduction plus 1.5 us per further block
 // (fitted to Q4_K at N = 4096, K = 14336: 26.6, 44, 59 and 73 us for one to
 // four blocks).
-double skinny_estimate_us(int64_t K, int64_t N, int64_t T) {
-    const double rounds = double(cdiv(cdiv(K, 64), kNumCUs)), per_wave = double(cdiv(cdiv(N, 16), 8));
+double skinny_pass_us(int64_t K, int64_t N, int64_t T, int64_t batches) {
+    const double rounds = double(cdiv(cdiv(K, 64) * batches, kNumCUs)), per_wave = double(cdiv(cdiv(N, 16), 8));
     const double blocks = double(skinny_blocks(T));
     return 4.0 + 1.5 * (blocks - 1.0) + rounds * per_wave * 2.0 * (512.0 * blocks + 300.0) / 2400.0;
 }
 
+// Time of passes over rows of G, `per` rows a pass, the last one the rest.
+template <typename Pass>
+double passes_us(int64_t T, int64_t per, Pass pass) {
+    const int64_t full = T / per, rest = T % per;
+    return double(full) * pass(per) + (rest ? pass(rest) : 0.0);
+}
+
+double skinny_estimate_us(int64_t K, int64_t N, int64_t T, int64_t batches = 1) {
+    return passes_us(T, kSkinnyMaxT, [&](int64_t t) { return skinny_pass_us(K, N, t, batches); });
+}
+
 // The n-split skinny kernel: the skinny kernel's fast path (whole 16-row
-// groups, K in 4-element units, G rows in 16-byte units) over one matrix,
-// T <= 48.
+// groups, K in 4-element units, G rows in 16-byte units) over one matrix, in
+// passes of up to 48 rows of G.
 bool skinny_split_applies(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    return skinny_applies(type, K, N, T, s) && T >= 1 && T <= kSplitMaxT && N >= 16 && N % 16 == 0 && K % 4 == 0 &&
+    return skinny_applies(type, K, N, T, s) && T >= 1 && N >= 16 && N % 16 == 0 && K % 4 == 0 &&
            (s.gcols || s.ldg % 4 == 0) && s.batches() == 1;
 }
 
@@ -175,8 +187,10 @@ bool skinny_split_applies(int type, int64_t K, int64_t N, int64_t T, const Strid
 // per further block of 16 rows of G.
 double skinny_split_estimate_us(int64_t K, int64_t N, int64_t T) {
     const int64_t share = cdiv(cdiv(K, 64) * (N / 16), kSplitGrid);
-    const double blocks = double(skinny_blocks(T));
-    return 5.6 + 1.5 * (blocks - 1.0) + double(cdiv(share, 8)) * 2.0 * (512.0 * blocks + 300.0) / 2400.0;
+    return passes_us(T, kSplitMaxT, [&](int64_t t) {
+        const double blocks = double(skinny_blocks(t));
+        return 5.6 + 1.5 * (blocks - 1.0) + double(cdiv(share, 8)) * 2.0 * (512.0 * blocks + 300.0) / 2400.0;
+    });
 }
 
 // Whether the automatic choice may take tile v for this type. F32 rows spill
@@ -223,25 +237,31 @@ Choice choose_tile(int type, int64_t K, int64_t N, int64_t T, const Strides& s) 
 
 // Estimated time (us) of tile v over dst: rounds of one tile per CU, each
 // tile a loop over 32-row chunks of W at 128 F32 MACs per cycle per CU, at
-// the efficiency measured for the tile's rows of G (Q4_K N = 4096,
-// K = 14336: 32-row tiles about 0.6, larger ones about 0.85).
+// the efficiency measured for the tile's rows of G with one tile per CU
+// (Q4_K N = 4096, K = 14336 and F32 4096 x 4096: 32-row tiles 0.6, 64-row
+// 0.72, larger 0.85).
 double tile_estimate_us(int variant, int64_t K, int64_t N, int64_t T, const Strides& s) {
     const TileVariant* v = find_tile(variant);
     if (!v) return 1e30;
     const double rounds = double(cdiv(cdiv(T, v->bt) * cdiv(K, v->bk) * s.batches(), kNumCUs));
-    const double eff = v->bt <= 32 ? 0.6 : 0.85;
+    const double eff = v->bt <= 32 ? 0.6 : v->bt <= 64 ? 0.72 : 0.85;
     return 4.0 + rounds * double(cdiv(N, 32)) * double(v->bt) * v->bk * 32.0 / 128.0 / eff / 2400.0;
 }
 
 // The kernel one launch over all of dst would use: the skinny kernel for
-// T <= 16, and up to T = 64 where its estimate beats the best tile's (with
-// few tiles per CU the tiled kernels leave most CUs idle: Q4_K N = 4096,
-// K = 14336 at T = 17 .. 64 ran 183 us in 32 x 256 tiles).
+// T <= 16, and above that where its estimate (one pass over W per 64 rows of
+// G) beats the best tile's (with few tiles per CU the tiled kernels leave
+// most CUs idle: Q4_K N = 4096, K = 14336 at T = 17 .. 64 ran 183 us in
+// 32 x 256 tiles).
 int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     const bool skinny = skinny_applies(type, K, N, T, s);
     if (skinny && T <= 16) return RETRO_VARIANT_SKINNY;
     const Choice tile = choose_tile(type, K, N, T, s);
-    if (skinny && (tile.id < 0 || skinny_estimate_us(K, N, T) < tile_estimate_us(tile.id, K, N, T, s)))
+    // past one pass (T > 64) the skinny kernel must win by 10%: the
+    // estimates are rougher there
+    const double margin = T <= kSkinnyMaxT ? 1.0 : 0.9;
+    if (skinny && (tile.id < 0 || skinny_estimate_us(K, N, T, s.batches()) <
+                                      margin * tile_estimate_us(tile.id, K, N, T, s)))
         return RETRO_VARIANT_SKINNY;
     return tile.id;
 }
@@ -254,7 +274,8 @@ int choose(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
 bool skinny_split_pays(int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
     if (cdiv(K, 64) > 192) return false;
     const int v = choose(type, K, N, T, s);
-    const double one = v == RETRO_VARIANT_SKINNY ? skinny_estimate_us(K, N, T) : tile_estimate_us(v, K, N, T, s);
+    const double one = v == RETRO_VARIANT_SKINNY ? skinny_estimate_us(K, N, T, s.batches())
+                                                 : tile_estimate_us(v, K, N, T, s);
     return skinny_split_estimate_us(K, N, T) <= 0.9 * one;
 }
 
@@ -528,7 +549,7 @@ int launch_split_typed(int type, const void* W, const float* G, float* dst, int6
 // Workspace bytes a call of `variant` uses for this (checked) shape: the
 // split's fixed size, 0 for any other kernel, or RETRO_E_VARIANT.
 int64_t workspace_need(int variant, int type, int64_t K, int64_t N, int64_t T, const Strides& s) {
-    const int64_t bytes = split_workspace_bytes(skinny_blocks(T));
+    const int64_t bytes = split_workspace_bytes(skinny_blocks(T < kSplitMaxT ? T : kSplitMaxT));
     if (variant == RETRO_VARIANT_SKINNY_SPLIT) return skinny_split_applies(type, K, N, T, s) ? bytes : RETRO_E_VARIANT;
     if (variant == RETRO_VARIANT_AUTO)
         return skinny_split_applies(type, K, N, T, s) && skinny_split_pays(type, K, N, T, s) ? bytes : 0;

@@ -179,24 +179,34 @@ SkinnyArgs skinny_args(const void* W, const float* G, float* dst, int64_t K, int
     return a;
 }
 
+// Offset of row t0 of G within each matrix: rows of ldg floats, or (G
+// stored t-fastest) the t0-th float of every column.
+int64_t g_row_offset(const Strides& s, int64_t t0) { return s.gcols ? t0 : t0 * s.ldg; }
+
+// One pass over W per kSkinnyMaxT rows of G (the last pass takes the rest).
 template <int TYPE>
 int launch_skinny(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T, const Strides& s,
                   int waves, hipStream_t st) {
-    const SkinnyArgs a = skinny_args(W, G, dst, K, N, T, s);
     const dim3 grid(unsigned(cdiv(K, 64)), unsigned(s.batches()));
-    clear_last_error();
-    switch (skinny_blocks(T)) {
-        case 1:
-            if (waves == 8)
-                launch_skinny_waves<TYPE, 8, 1>(a, grid, st);
-            else
-                launch_skinny_waves<TYPE, 16, 1>(a, grid, st);
-            break;
-        case 2: launch_skinny_waves<TYPE, 8, 2>(a, grid, st); break;
-        case 3: launch_skinny_waves<TYPE, 8, 3>(a, grid, st); break;
-        default: launch_skinny_waves<TYPE, 8, 4>(a, grid, st); break;
+    for (int64_t t0 = 0; t0 < T; t0 += kSkinnyMaxT) {
+        const int64_t tc = T - t0 < kSkinnyMaxT ? T - t0 : kSkinnyMaxT;
+        const SkinnyArgs a = skinny_args(W, G + g_row_offset(s, t0), dst + t0 * s.ldd, K, N, tc, s);
+        clear_last_error();
+        switch (skinny_blocks(tc)) {
+            case 1:
+                if (waves == 8)
+                    launch_skinny_waves<TYPE, 8, 1>(a, grid, st);
+                else
+                    launch_skinny_waves<TYPE, 16, 1>(a, grid, st);
+                break;
+            case 2: launch_skinny_waves<TYPE, 8, 2>(a, grid, st); break;
+            case 3: launch_skinny_waves<TYPE, 8, 3>(a, grid, st); break;
+            default: launch_skinny_waves<TYPE, 8, 4>(a, grid, st); break;
+        }
+        const int rc = launch_status();
+        if (rc != RETRO_OK) return rc;
     }
-    return launch_status();
+    return RETRO_OK;
 }
 
 template <int TYPE, int WA, int WB, int CT, int NC = 4>
@@ -326,6 +336,17 @@ int launch_dequant(const void* W, float* out, int64_t K, int64_t N, hipStream_t 
 template <int TYPE>
 int launch_out_prod_split(const void* W, const float* G, float* dst, int64_t K, int64_t N, int64_t T,
                           const Strides& s, void* workspace, hipStream_t st) {
+    // one pass over W per kSplitMaxT rows of G, in turn on the stream (each
+    // leaves the workspace's counters at zero for the next)
+    if (T > kSplitMaxT) {
+        for (int64_t t0 = 0; t0 < T; t0 += kSplitMaxT) {
+            const int64_t tc = T - t0 < kSplitMaxT ? T - t0 : kSplitMaxT;
+            const int rc = launch_out_prod_split<TYPE>(W, G + g_row_offset(s, t0), dst + t0 * s.ldd, K, N, tc, s,
+                                                       workspace, st);
+            if (rc != RETRO_OK) return rc;
+        }
+        return RETRO_OK;
+    }
     const SkinnyArgs a = skinny_args(W, G, dst, K, N, T, s);
     SkinnySplitArgs sp;
     sp.count = static_cast<unsigned*>(workspace);
@@ -343,7 +364,7 @@ int launch_out_prod_split(const void* W, const float* G, float* dst, int64_t K, 
             break;
         case 2: hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 8, 2>), grid, b8, 0, st, a, sp); break;
         case 3: hipLaunchKernelGGL((out_prod_skinny_split_kernel<TYPE, 8, 3>), grid, b8, 0, st, a, sp); break;
-        default: return RETRO_E_VARIANT;  // T > kSplitMaxT: the caller does not ask for it
+        default: return RETRO_E_VARIANT;  // not reached: T <= kSplitMaxT here
     }
     return launch_status();
 }

@@ -232,20 +232,21 @@ def test_workspace_size():
     assert q.workspace_size(q.Q8_0, 256, 128, 16) == 0            # too few rows to share
     assert q.workspace_size(q.Q4_K, 4096, 14336, 17) == full(17)  # two blocks of G
     assert q.workspace_size(q.Q4_K, 4096, 14336, 48) == full(48)
-    assert q.workspace_size(q.Q4_K, 4096, 14336, 49) == 0         # past the split's T
+    assert q.workspace_size(q.Q4_K, 4096, 14336, 512) == full(48)  # passes of 48 rows of G
     for wtype in q.TYPES.values():
         K = 256 * 8
         assert q.workspace_size(wtype, K, 4096, 16, split) == full()
         assert q.workspace_size(wtype, K, 4096, 40, split) == full(40)
-        assert q.workspace_size(wtype, K, 4096, 49, split) == q.E_VARIANT
+        assert q.workspace_size(wtype, K, 4096, 49, split) == full(48)
         assert q.workspace_size(wtype, K, 4088, 16, split) == q.E_VARIANT   # N % 16 != 0
         assert q.workspace_size(wtype, K, 0, 16, split) == q.E_VARIANT
     assert q.workspace_size(q.F32, 4094, 4096, 16, split) == q.E_VARIANT     # K % 4 != 0
-    assert q.variant_applies(q.VARIANT_SKINNY, q.Q4_K, 4096, 4096, 64)          # the skinny kernel: T <= 64
-    assert not q.variant_applies(q.VARIANT_SKINNY, q.Q4_K, 4096, 4096, 65)
+    assert q.variant_applies(q.VARIANT_SKINNY, q.Q4_K, 4096, 4096, 64)          # passes of 64 rows of G
+    assert q.variant_applies(q.VARIANT_SKINNY, q.Q4_K, 4096, 4096, 4096)
     assert not q.variant_applies(q.VARIANT_SKINNY_16, q.Q4_K, 4096, 4096, 17)   # sixteen waves: T <= 16
     assert q.workspace_size(q.Q4_K, 4096, 4096, 512, q.VARIANT_WS_128x256) == 0
-    assert q.workspace_size(q.Q4_K, 4096, 4096, 512, q.VARIANT_SKINNY) == q.E_VARIANT
+    assert q.workspace_size(q.Q4_K, 4096, 4096, 512, q.VARIANT_SKINNY) == 0
+    assert q.workspace_size(q.Q4_K, 4096, 4096, 512, q.VARIANT_SKINNY_16) == q.E_VARIANT
     assert q.workspace_size(q.Q4_K, 100, 16, 16) == q.E_SHAPE
     assert q.workspace_size(5, 32, 16, 16) == q.E_TYPE
     # the split needs the workspace call: the others refuse it
@@ -268,7 +269,7 @@ def test_workspace_call_validation():
     assert f(split, *args, D - 16, full, None) == q.E_WORKSPACE          # overlaps dst
     assert f(split, *args, W, full, None) == q.E_WORKSPACE               # overlaps W
     assert f(q.VARIANT_AUTO, *args, G + 64, full, None) == q.E_WORKSPACE  # overlaps G
-    assert f(split, q.Q4_K, W, G, D, 4096, 4096, 49, WS, full, None) == q.E_VARIANT
+    assert f(split, q.Q4_K, W, G, D, 4096, 4096, 49, WS, full, None) == q.E_WORKSPACE  # three blocks
     assert f(split, q.Q4_K, W, G, W, 4096, 4096, 16, WS, full, None) == q.E_ALIAS
     assert f(split, q.Q4_K, W, None, D, 4096, 4096, 16, WS, full, None) == q.E_NULL
     assert f(split, q.Q4_K, W, G, D, 100, 4096, 16, WS, full, None) == q.E_SHAPE
@@ -382,7 +383,7 @@ def test_column_split_validation():
     assert cs(a, 160, b, q.Q4_0, W, G, D, 512, 4, 40, None) == q.E_ALIGN    # 90 bytes of W before it
     assert cs(a, 128, b, q.Q8_0, W, G, D, 512, 4, 40, None) == q.E_ALIGN    # 136 bytes
     assert cs(a, 256, b, q.Q4_K, W, G, D, 512, 4, 40, None) == q.E_VARIANT  # 128-column tile on Q4_K
-    assert cs(q.VARIANT_SKINNY, 256, b, q.Q4_0, W, G, D, 512, 4, 65, None) == q.E_VARIANT
+    assert cs(q.VARIANT_SKINNY_16, 256, b, q.Q4_0, W, G, D, 512, 4, 17, None) == q.E_VARIANT
     assert cs(42, 256, b, q.Q4_0, W, G, D, 512, 4, 40, None) == q.E_VARIANT
     assert cs(a, 256, b, q.Q4_0, W, G, D, 0, 4, 40, None) == q.E_SHAPE      # K = 0: no split point
     assert cs(a, 256, b, 5, W, G, D, 512, 4, 40, None) == q.E_TYPE
@@ -393,7 +394,7 @@ def test_column_split_validation():
 
 def test_variant_applies():
     assert q.variant_applies(q.VARIANT_SKINNY, q.Q4_K, 14336, 4096, 16)
-    assert not q.variant_applies(q.VARIANT_SKINNY, q.Q4_K, 14336, 4096, 65)
+    assert not q.variant_applies(q.VARIANT_SKINNY_16, q.Q4_K, 14336, 4096, 17)
     assert q.variant_applies(q.VARIANT_TILE_128x256, q.Q4_K, 4096, 14336, 4096)
     assert not q.variant_applies(q.VARIANT_TILE_128x128, q.Q4_K, 4096, 14336, 4096)
     assert q.variant_applies(q.VARIANT_WS_128x256, q.Q4_K, 4096, 14336, 4096)
@@ -579,7 +580,7 @@ def test_validation_errors_before_any_device_work():
     assert lib.retro_out_prod(q.F32, 0x100000, 0x200000, 0x1FFFD0, 4, 4, 4, None) == q.E_ALIAS
     # variants
     assert lib.retro_out_prod_variant(42, q.F32, 0x100000, 0x200000, 0x300000, 4, 4, 4, None) == q.E_VARIANT
-    assert lib.retro_out_prod_variant(q.VARIANT_SKINNY, q.F32, 0x100000, 0x200000, 0x300000, 4, 4, 65,
+    assert lib.retro_out_prod_variant(q.VARIANT_SKINNY_16, q.F32, 0x100000, 0x200000, 0x300000, 4, 4, 17,
                                       None) == q.E_VARIANT
     assert lib.retro_out_prod_variant(q.VARIANT_TILE_128x128, q.Q4_K, 0x100000, 0x200000, 0x300000, 256, 4, 64,
                                       None) == q.E_VARIANT
@@ -644,7 +645,7 @@ def test_noalloc_validation():
     f = q.lib.retro_out_prod_noalloc
     W, G, D = 0x10000000, 0x20000000, 0x30000000
     split = q.VARIANT_SKINNY_SPLIT
-    assert f(split, q.Q4_K, W, G, D, 4096, 4096, 49, None) == q.E_VARIANT
+    assert f(split, q.F32, W, G, D, 4094, 4096, 16, None) == q.E_VARIANT  # K % 4 != 0
     assert f(split, q.Q4_K, W, G, D, 4096, 4088, 16, None) == q.E_VARIANT
     assert f(q.VARIANT_AUTO, q.Q4_K, W, None, D, 4096, 4096, 16, None) == q.E_NULL
     assert f(q.VARIANT_AUTO, q.Q4_K, W, G, W, 4096, 4096, 16, None) == q.E_ALIAS

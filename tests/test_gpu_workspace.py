@@ -55,9 +55,10 @@ def block_k(wtype, slabs_wanted):
 
 # (slabs, N, T): shares of a few groups (idle waves, many pieces per slab),
 # of about a slab, and longer than a slab (whole slabs inside a share: 260
-# slabs); N = 16 puts every slab whole in one share.
+# slabs); N = 16 puts every slab whole in one share; T from 1 to 48 in one
+# pass over W, and T = 100 in three (48, 48 and 4 rows of G).
 SHAPES = [(12, 1024, 16), (12, 16, 5), (40, 4096, 1), (100, 2048, 16), (260, 32, 3), (20, 512, 40), (30, 256, 48),
-          (12, 1024, 17)]
+          (12, 1024, 17), (12, 512, 100)]
 
 
 @pytest.mark.parametrize("wtype", TYPES)
