@@ -644,8 +644,8 @@ bool mm_tile_applies(const MmTile& v, int type, int64_t K, int64_t N, int64_t T)
 
 bool mm_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
     if (variant == RETRO_VARIANT_SIMPLE) return cdiv(T * N, 256) < kGridLimit;
-    if (variant == RETRO_VARIANT_SKINNY)  // 16 rows of W and of x addressed with 32-bit offsets
-        return T <= 16 && cdiv(N, 16) < kGridLimit && !(is_dense(type) && K % 4) &&
+    if (variant == RETRO_VARIANT_SKINNY)  // 16 rows of W and of x (a pass) addressed with 32-bit offsets
+        return cdiv(N, 16) < kGridLimit && !(is_dense(type) && K % 4) &&
                16 * row_bytes_of(type, K) < (int64_t(1) << 31) && 16 * K * 4 < (int64_t(1) << 31);
     for (const auto& v : kMmTiles)
         if (v.id == variant) return mm_tile_applies(v, type, K, N, T);
@@ -667,9 +667,39 @@ Choice mm_choose_tile(int type, int64_t K, int64_t N, int64_t T) {
     return best;
 }
 
+// Estimated times (us) for the forward. The skinny kernel, one pass per 16
+// rows of x: about 4 us plus 0.88 us per 64-element k group of a wave (eight
+// waves, one workgroup of 16 W rows per CU per round; fitted to Q4_K 4096 x
+// 14336 and 14336 x 4096 and Q4_0 17408 x 5120 at T = 16: 28.8, 32.1 and
+// 48.8 us). A tile: rounds of one tile per CU, bt x bn x K MACs at 128 per
+// cycle per CU and the efficiency of its rows of x (as for out_prod).
+double mm_skinny_estimate_us(int64_t K, int64_t N, int64_t T) {
+    const double rounds = double(cdiv(cdiv(N, 16), kNumCUs)), per_wave = double(cdiv(cdiv(K, 64), 8));
+    return double(cdiv(T, 16)) * (4.0 + rounds * per_wave * 0.88);
+}
+
+double mm_tile_estimate_us(const MmTile& v, int64_t K, int64_t N, int64_t T) {
+    const double rounds = double(cdiv(cdiv(T, v.bt) * cdiv(N, v.bn), kNumCUs));
+    const double eff = v.bt <= 32 ? 0.6 : v.bt <= 64 ? 0.72 : 0.85;
+    return 4.0 + rounds * double(v.bt) * v.bn * double(K) / 128.0 / eff / 2400.0;
+}
+
+// The skinny kernel for T <= 16, and above where its passes are estimated
+// 10% faster than the best tile (with few tiles per CU the tiles leave most
+// CUs idle: Q4_K 4096 x 14336 at T = 17 .. 128 ran 352 us in 32 x 128
+// tiles, against 28.8 us per pass).
 int mm_choose(int type, int64_t K, int64_t N, int64_t T) {
-    if (mm_variant_applies(RETRO_VARIANT_SKINNY, type, K, N, T)) return RETRO_VARIANT_SKINNY;
-    int best = mm_choose_tile(type, K, N, T).id;
+    const bool skinny = mm_variant_applies(RETRO_VARIANT_SKINNY, type, K, N, T);
+    if (skinny && T <= 16) return RETRO_VARIANT_SKINNY;
+    const Choice tile = mm_choose_tile(type, K, N, T);
+    if (skinny) {
+        const MmTile* v = nullptr;
+        for (const auto& m : kMmTiles)
+            if (m.id == tile.id) v = &m;
+        if (!v || mm_skinny_estimate_us(K, N, T) < 0.9 * mm_tile_estimate_us(*v, K, N, T))
+            return RETRO_VARIANT_SKINNY;
+    }
+    int best = tile.id;
     if (best < 0 && mm_variant_applies(RETRO_VARIANT_SIMPLE, type, K, N, T)) best = RETRO_VARIANT_SIMPLE;
     return best < 0 ? RETRO_E_SHAPE : best;
 }

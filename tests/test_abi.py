@@ -352,7 +352,7 @@ def test_mul_mat_row_split_validation():
     assert rs(a, 256, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_SHAPE
     assert rs(a, 126, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_ALIGN    # not a multiple of 4 rows
     assert rs(a, 100, b, q.Q8_0, W, X, Y, 416, 256, 40, None) == q.E_ALIGN    # 100 rows of 442 bytes
-    assert rs(q.VARIANT_SKINNY, 128, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_VARIANT  # T > 16
+    assert rs(q.VARIANT_SKINNY, 128, b, q.F16, W, X, Y, 301, 256, 40, None) == q.E_VARIANT  # x rows of 301
     assert rs(42, 128, b, q.Q4_0, W, X, Y, 512, 256, 40, None) == q.E_VARIANT
     assert rs(a, 128, b, 5, W, X, Y, 512, 256, 40, None) == q.E_TYPE
     assert rs(a, 128, b, q.Q4_0, W, X, Y, 512, 256, 0, None) == q.OK         # nothing to compute
@@ -538,7 +538,9 @@ def test_mul_mat_validation_and_choice():
                                        None) == q.E_VARIANT
     assert q.mul_mat_choice(q.Q4_K, 4096, 14336, 4096) == q.VARIANT_WS_128x128
     assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 16) == q.VARIANT_SKINNY
-    assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 17) == q.VARIANT_WS_32x128
+    assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 17) == q.VARIANT_SKINNY     # passes: 32 tiles of 32 x 128
+    assert q.mul_mat_choice(q.Q4_K, 14336, 4096, 128) == q.VARIANT_SKINNY
+    assert q.mul_mat_choice(q.Q4_K, 4096, 14336, 64) == q.VARIANT_WS_32x128   # 224 tiles: one round
     assert q.mul_mat_choice(q.F16, 301, 64, 100) == q.VARIANT_SIMPLE      # x rows not in 16-byte units
     assert q.mul_mat_choice(q.F16, 301, 64, 9) == q.VARIANT_SIMPLE
     assert q.mul_mat_choice(q.F16, 300, 64, 9) == q.VARIANT_SKINNY

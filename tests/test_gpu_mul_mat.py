@@ -78,7 +78,7 @@ def test_mul_mat_matches_oracle(q, wtype, shape):
     dense = wtype in (wl.F32, wl.F16, wl.BF16)
     tiled = {"ws_256x128", "ws_128x128", "ws_64x128", "ws_32x128"}
     assert ("simple" in ran) and (tiled <= set(ran)) == (not dense or K % 4 == 0), ran
-    assert ("skinny" in ran) == (T <= 16), ran
+    assert "skinny" in ran, ran  # any T, one pass per 16 rows of x
 
 
 @pytest.mark.parametrize("wtype", [wl.Q4_K, wl.Q6_K, wl.MXFP4, wl.NVFP4, wl.Q5_1, wl.BF16])
