@@ -644,9 +644,9 @@ bool mm_tile_applies(const MmTile& v, int type, int64_t K, int64_t N, int64_t T)
 
 bool mm_variant_applies(int variant, int type, int64_t K, int64_t N, int64_t T) {
     if (variant == RETRO_VARIANT_SIMPLE) return cdiv(T * N, 256) < kGridLimit;
-    if (variant == RETRO_VARIANT_SKINNY)  // 16 rows of W and of x (a pass) addressed with 32-bit offsets
+    if (variant == RETRO_VARIANT_SKINNY)  // 16 rows of W and 64 of x (a pass) addressed with 32-bit offsets
         return cdiv(N, 16) < kGridLimit && !(is_dense(type) && K % 4) &&
-               16 * row_bytes_of(type, K) < (int64_t(1) << 31) && 16 * K * 4 < (int64_t(1) << 31);
+               16 * row_bytes_of(type, K) < (int64_t(1) << 31) && kSkinnyMaxT * K * 4 < (int64_t(1) << 31);
     for (const auto& v : kMmTiles)
         if (v.id == variant) return mm_tile_applies(v, type, K, N, T);
     return false;
@@ -667,15 +667,20 @@ Choice mm_choose_tile(int type, int64_t K, int64_t N, int64_t T) {
     return best;
 }
 
-// Estimated times (us) for the forward. The skinny kernel, one pass per 16
-// rows of x: about 4 us plus 0.88 us per 64-element k group of a wave (eight
+// Estimated times (us) for the forward. The skinny kernel, one pass per 64
+// rows of x: about 4 us (and 1.5 per further block of 16 rows of x) plus, per
+// 64-element k group of a wave, 0.88 us and 0.62 per further block (eight
 // waves, one workgroup of 16 W rows per CU per round; fitted to Q4_K 4096 x
-// 14336 and 14336 x 4096 and Q4_0 17408 x 5120 at T = 16: 28.8, 32.1 and
-// 48.8 us). A tile: rounds of one tile per CU, bt x bn x K MACs at 128 per
+// 14336 and 14336 x 4096 and Q4_0 17408 x 5120: 28.8, 32.1 and 48.8 us at
+// T = 16, 50.8 and 88 us at T = 32 and 64 on the first). A tile: rounds of one tile per CU, bt x bn x K MACs at 128 per
 // cycle per CU and the efficiency of its rows of x (as for out_prod).
 double mm_skinny_estimate_us(int64_t K, int64_t N, int64_t T) {
     const double rounds = double(cdiv(cdiv(N, 16), kNumCUs)), per_wave = double(cdiv(cdiv(K, 64), 8));
-    return double(cdiv(T, 16)) * (4.0 + rounds * per_wave * 0.88);
+    auto pass = [&](int64_t t) {
+        const double blocks = double(skinny_blocks(t));
+        return 4.0 + 1.5 * (blocks - 1.0) + rounds * per_wave * (0.88 + 0.62 * (blocks - 1.0));
+    };
+    return passes_us(T, kSkinnyMaxT, pass);
 }
 
 double mm_tile_estimate_us(const MmTile& v, int64_t K, int64_t N, int64_t T) {
@@ -687,7 +692,7 @@ double mm_tile_estimate_us(const MmTile& v, int64_t K, int64_t N, int64_t T) {
 // The skinny kernel for T <= 16, and above where its passes are estimated
 // 10% faster than the best tile (with few tiles per CU the tiles leave most
 // CUs idle: Q4_K 4096 x 14336 at T = 17 .. 128 ran 352 us in 32 x 128
-// tiles, against 28.8 us per pass).
+// tiles, against 51 us for the skinny kernel at T = 32).
 int mm_choose(int type, int64_t K, int64_t N, int64_t T) {
     const bool skinny = mm_variant_applies(RETRO_VARIANT_SKINNY, type, K, N, T);
     if (skinny && T <= 16) return RETRO_VARIANT_SKINNY;

@@ -6,12 +6,15 @@
 // runs over n, across the rows of W. The block-quantized direction k is the
 // output-column direction, so one decoded weight feeds T outputs.
 //
-// Three kernels:
+// Four kernels:
 //   tile     fused decode -> LDS -> v_mfma_f32_32x32x2_f32, one BT x BK tile of
 //            dst per workgroup, loop over n in chunks of 32 rows of W.
-//   skinny   T <= 16: v_mfma_f32_16x16x4_f32 with M = 16, one 64-column slab
-//            of dst per workgroup, all of n inside the workgroup (waves split
-//            n and reduce through LDS in a fixed order), one pass over W.
+//   skinny   T <= 64 a launch: v_mfma_f32_16x16x4_f32 with M = 16 rows of G
+//            per block, one 64-column slab of dst per workgroup, all of n
+//            inside the workgroup (waves split n and reduce through LDS in a
+//            fixed order), one pass over W.
+//   skinny split  the same, with n cut into one equal share per CU and the
+//            parts of a slab added through a caller's workspace.
 //   dequant  decode-only, for bit-exact checks of the decoders.
 // None allocates memory and none materialises a decoded copy of W.
 #pragma once
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(256, 2) void out_prod_tile_kernel(TileArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel (T <= 16)
+// Skinny kernel (up to T = 64 a launch)
 // ---------------------------------------------------------------------------
 
 struct SkinnyArgs {
@@ -1153,7 +1156,7 @@ __device__ __forceinline__ void skinny_decode(const SkinnyRaw<TYPE, TB>& r, int 
     }
 }
 
-// dst[t][k0 .. k0+63] for all t < T (T <= 16 TB). MFMA 16x16x4 operands:
+// dst[t][k0 .. k0+63] for all t < T (T <= 16 TB <= 64). MFMA 16x16x4 operands:
 // lane l supplies A[i = l%16][kk = l/16] and B[kk = l/16][j = l%16]. Step s
 // of a 16-row group starting at n0 uses W row n0 + 4*(l/16) + s for lane l,
 // so a lane reads G[t][n0 + 4*(l/16) .. +3] with one float4 per block of 16
@@ -1263,7 +1266,8 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel with n split across workgroups (T <= 16, needs a workspace)
+// Skinny kernel with n split across workgroups (T <= 48 a launch, needs a
+// workspace)
 // ---------------------------------------------------------------------------
 //
 // The skinny kernel gives each 64-column slab of dst to one workgroup, so
@@ -1278,9 +1282,10 @@ __global__ __launch_bounds__(NWAVES * 64) void out_prod_skinny_kernel(SkinnyArgs
 // whichever workgroup finishes last. Only a share's first and last piece can
 // be part of a slab, so each workgroup owns two slots, and the counter of a
 // split slab belongs to the workgroup holding its first group (no workgroup
-// holds the first group of two split slabs): the workspace is a fixed
-// 2 x 4 TB KiB + 4 bytes per workgroup whatever the shape. Slots and counters are
-// read and written at device scope (the pieces of a slab may run on
+// holds the first group of two split slabs): the workspace is 4 bytes plus
+// two slots of 4 KiB per block of 16 rows of G per workgroup, whatever N and
+// K. Slots and counters are read and written at device scope (the pieces of
+// a slab may run on
 // different XCDs); every counter is back at zero when the call ends. There is
 // no waiting on other workgroups: each one runs to its end whatever the
 // others do.

@@ -453,26 +453,29 @@ __global__ __launch_bounds__((MmShape<TYPE, WA, WB, CT, NC>::kThreads),
     ws_consume<S, WA, WB, 1>(lds_all, tid, wave, nloc, t0, n0, T, N, args.Y, args.ldy);
 }
 
-// mul_mat for T <= 16: one workgroup (NW = 8 or 16 waves) per 16 rows of W over all
-// of k, v_mfma_f32_16x16x4_f32 with M = t, N = W row, K = 4 steps of k.
+// mul_mat for T <= 16 TB a launch (the host runs one launch per 64 rows of
+// x): one workgroup (NW = 8 or 16 waves) per 16 rows of W over all of k,
+// v_mfma_f32_16x16x4_f32 with M = t, N = W row, K = 4 steps of k.
 // Iteration g of a wave covers k = 64 g .. 64 g + 63: lane l decodes the 16
 // elements 64 g + 16 (l / 16) .. + 15 of row n0 + l % 16 (one MmCodec unit,
-// one header decode) and takes the same 16 x values of row t = l % 16, and
-// round r, step s of the 16 MFMAs uses element 4 r + s. x goes through a
-// tile of the wave's own in LDS: loaded with 16 lanes per 256-byte row
-// segment (the MFMA layout would give each lane its own 64-byte region and
-// keep the address unit busy four times as long), then read back in the
+// one header decode) and, for each block of 16 rows of x, takes the same 16
+// x values of row t = 16 tb + l % 16, and round r, step s of the block's 16
+// MFMAs uses element 4 r + s: the decode is shared by all TB blocks. x goes
+// through a tile of the wave's own in LDS: loaded with 16 lanes per 256-byte
+// row segment (the MFMA layout would give each lane its own 64-byte region
+// and keep the address unit busy four times as long), then read back in the
 // MFMA layout. The next iteration's loads are issued before the current one
 // is decoded. Partial sums are added over waves in increasing wave order in
-// LDS.
-template <int TYPE, int NW>
+// LDS (the x tiles' space, once the loop is done).
+template <int TYPE, int NW, int TB>
 __global__ __launch_bounds__(NW * 64) void mul_mat_skinny_kernel(MmSimpleArgs a) {
     static_assert(NW >= 4, "the final sum uses 256 threads");
     using C = MmCodec<TYPE>;
     using F = Format<TYPE>;
     constexpr int XP = 68;  // floats per t row of a wave's x tile (64 + 4: conflict-free reads)
-    __shared__ __attribute__((aligned(16))) float part[NW * 256];
-    __shared__ __attribute__((aligned(16))) float xtile[NW * 16 * XP];
+    constexpr int XT = NW * 16 * TB * XP, PT = NW * 256 * TB;
+    __shared__ __attribute__((aligned(16))) float lds[XT > PT ? XT : PT];
+    float* const part = lds;  // after the loop
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = blockIdx.x * 16;
@@ -487,16 +490,18 @@ __global__ __launch_bounds__(NW * 64) void mul_mat_skinny_kernel(MmSimpleArgs a)
     const long long x_end = K == 0 ? 0 : (long long)(a.T - 1) * a.ldx + K;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.X, uint32_t(max(0ll, min(4 * x_end, (long long)0x7FFFFFFF))));
     const uint32_t ro = uint32_t(j * a.pitch);
-    // x load i of an iteration: row 4 i + l / 16, floats 4 (l % 16) .. + 3
-    // of the iteration's 64
-    uint32_t xo[4];
+    // x load i of an iteration: row 4 i + l / 16 of its block of 16, floats
+    // 4 (l % 16) .. + 3 of the iteration's 64
+    uint32_t xo[TB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xo[i] = uint32_t(((4 * i + kk) * a.ldx + 4 * j) * 4);
-    float* const xt = xtile + wave * 16 * XP;
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xo[tb][i] = uint32_t(((16 * tb + 4 * i + kk) * a.ldx + 4 * j) * 4);
+    float* const xt = lds + wave * 16 * TB * XP;
     const int groups = (K + 63) / 64;
 
     uint32_t wraw[2][C::WORDS];
-    u32x4 xraw[2][4];
+    u32x4 xraw[2][TB][4];
     // Loads of group g into slot S: always issued (a group past the last
     // reads bytes it never uses), so that they stay in flight.
     auto fetch = [&](auto slot, int g) {
@@ -504,39 +509,65 @@ __global__ __launch_bounds__(NW * 64) void mul_mat_skinny_kernel(MmSimpleArgs a)
         const int k = 64 * g + 16 * kk;
         C::fetch(wr, ro, k, wraw[S]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xraw[S][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i] + 256u * g, 0, 0);
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xraw[S][tb][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[tb][i] + 256u * g, 0, 0);
     };
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](auto slot, int g) {
         constexpr int S = decltype(slot)::value;
         const int k = 64 * g + 16 * kk;
-        float e[16], xv[16];
+        float e[16];
         // the x tile through LDS; the fences keep the wave's LDS accesses in
         // program order (the previous iteration's reads before these writes,
         // these writes before the reads below)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xt + (4 * i + kk) * XP + 4 * j) = xraw[S][i];
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4*>(xt + (16 * tb + 4 * i + kk) * XP + 4 * j) = xraw[S][tb][i];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // x of block tb, row t = 16 tb + l % 16, in the MFMA layout
+        auto read_x = [&](int tb, float* xv) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(xt + j * XP + 16 * kk + 4 * i);
-            xv[4 * i] = v[0];
-            xv[4 * i + 1] = v[1];
-            xv[4 * i + 2] = v[2];
-            xv[4 * i + 3] = v[3];
-        }
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(xt + (16 * tb + j) * XP + 16 * kk + 4 * i);
+                xv[4 * i] = v[0];
+                xv[4 * i + 1] = v[1];
+                xv[4 * i + 2] = v[2];
+                xv[4 * i + 3] = v[3];
+            }
+        };
+        // the first block's x reads are in flight during the decode, each
+        // later block's during the previous block's MFMAs
+        float xv[2][16];
+        read_x(0, xv[0]);
         C::decode(wraw[S], k, e);
-        if (k + 16 > K) {  // elements at or past K: zero on both sides
+        const bool tail = k + 16 > K;  // elements at or past K: zero on both sides
+        if (tail) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (k + i >= K) e[i] = xv[i] = 0.f;
+                if (k + i >= K) e[i] = 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i], e[i], acc, 0, 0, 0);
+        for (int tb = 0; tb < TB; ++tb) {
+            float* cur = xv[tb & 1];
+            if (tb + 1 < TB) read_x(tb + 1, xv[(tb + 1) & 1]);
+            if (tail) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (k + i >= K) cur[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[tb] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[i], e[i], acc[tb], 0, 0, 0);
+        }
     };
     using Slot0 = std::integral_constant<int, 0>;
     using Slot1 = std::integral_constant<int, 1>;
@@ -551,15 +582,19 @@ __global__ __launch_bounds__(NW * 64) void mul_mat_skinny_kernel(MmSimpleArgs a)
             compute(Slot1{}, g + NW);
         }
     }
-    // D layout: lane l, register v holds t = 4 (l / 16) + v, row n0 + l % 16
+    // D layout: lane l, register v holds t = 16 tb + 4 (l / 16) + v, row n0 + l % 16
+    __syncthreads();  // every wave is done with its x tile
 #pragma unroll
-    for (int v = 0; v < 4; ++v) part[wave * 256 + (4 * kk + v) * 16 + j] = acc[v];
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[(wave * TB + tb) * 256 + (4 * kk + v) * 16 + j] = acc[tb][v];
     __syncthreads();
-    if (tid < 256) {
-        const int t = tid >> 4, nn = tid & 15;
-        float sum = part[tid];
+    for (int o = tid; o < 256 * TB; o += NW * 64) {
+        const int tb = o >> 8, r = o & 255;
+        const int t = 16 * tb + (r >> 4), nn = r & 15;
+        float sum = part[tb * 256 + r];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) sum += part[w * 256 + tid];
+        for (int w = 1; w < NW; ++w) sum += part[(w * TB + tb) * 256 + r];
         if (t < a.T && n0 + nn < a.N) a.Y[(long long)t * a.ldy + n0 + nn] = sum;
     }
 }

@@ -300,21 +300,27 @@ int launch_mul_mat(int variant, const void* W, const float* X, float* Y, int64_t
             return launch_status();
         }
         case RETRO_VARIANT_SKINNY: {
-            // one pass over W per 16 rows of x and Y
-            for (int64_t t0 = 0; t0 < T; t0 += 16) {
-                const int64_t tc = T - t0 < 16 ? T - t0 : 16;
+            // one pass over W per 64 rows of x and Y
+            const dim3 grid(unsigned(cdiv(N, 16)));
+            for (int64_t t0 = 0; t0 < T; t0 += kSkinnyMaxT) {
+                const int64_t tc = T - t0 < kSkinnyMaxT ? T - t0 : kSkinnyMaxT;
                 const MmSimpleArgs a = mm_simple_args(TYPE, W, X + t0 * K, Y + t0 * ldy, K, N, tc, ldy);
                 clear_last_error();
                 // the out_prod skinny kernel's wave rule; measured on the forward at
                 // T = 16: eight waves 0.96-0.98x the time of sixteen for Q4_K, Q6_K,
                 // Q4_0 and Q8_0 at N = 4096, K = 14336 (0.83x at N = 14336, K =
                 // 4096), 1.007x for Q2_K, 1.025x for Q4_K at T = 4
-                if (skinny_waves(TYPE, tc) == 8)
-                    hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 8>), dim3(unsigned(cdiv(N, 16))), dim3(512), 0, st,
-                                       a);
-                else
-                    hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 16>), dim3(unsigned(cdiv(N, 16))), dim3(1024), 0,
-                                       st, a);
+                switch (skinny_blocks(tc)) {
+                    case 1:
+                        if (skinny_waves(TYPE, tc) == 8)
+                            hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 8, 1>), grid, dim3(512), 0, st, a);
+                        else
+                            hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 16, 1>), grid, dim3(1024), 0, st, a);
+                        break;
+                    case 2: hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 8, 2>), grid, dim3(512), 0, st, a); break;
+                    case 3: hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 8, 3>), grid, dim3(512), 0, st, a); break;
+                    default: hipLaunchKernelGGL((mul_mat_skinny_kernel<TYPE, 8, 4>), grid, dim3(512), 0, st, a); break;
+                }
                 const int rc = launch_status();
                 if (rc != RETRO_OK) return rc;
             }
