@@ -420,7 +420,8 @@ int retro_out_prod_choice(int type, int64_t K, int64_t N, int64_t T);
  * operands): returns 1 (one launch of *variant0 over all of dst; *k_split = K,
  * *variant1 = 0) or 2 (*variant0 over dst columns [0, *k_split), then
  * *variant1 over [*k_split, K)), or a negative error code (the three
- * pointers NULL: RETRO_E_NULL). Touches no device.
+ * pointers NULL: RETRO_E_NULL). RETRO_VARIANT_SKINNY counts as one launch
+ * here; it makes one per 64 rows of G. Touches no device.
  * Two launches are planned when the tiles of one variant would leave the
  * last round over the 256 CUs partly empty and a larger tile fills whole
  * rounds on a leading column range (e.g. Q4_0, K = 5120, T = 2048: 128 x 256
