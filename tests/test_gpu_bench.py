@@ -42,3 +42,11 @@ def test_bench_prints_one_contract_line():
     c = d["ceilings"]
     assert c["mfma_f32_tflops"] > 100 and c["copy_gbs"] > 1000
     assert 0.0 <= c["mfma_f32_beside_valu"]["serial_frac"] <= 1.2
+    # beside the step: the skinny kernel at T = 32 and 64, and the workspace
+    # call against retro_out_prod on the 64-slab T = 16 shape
+    assert [m["workload"] for m in d["mid_t"]] == ["q4_k_n4096_k14336_t32", "q4_k_n4096_k14336_t64"]
+    for m in d["mid_t"]:
+        assert m["kernel"] == "skinny" and 0.0 < m["f32_mfma_frac"] < 1.0, m
+    sp = d["skinny_split"]
+    assert sp["slabs_of_dst"] == 64 and sp["workspace_bytes"] > 0
+    assert sp["speedup"] > 1.0 and sp["workspace"]["avg_launch_us"] < sp["skinny"]["avg_launch_us"]
