@@ -218,6 +218,17 @@ def test_skinny_blocks_of_t_match_oracle(q, wtype, T, N):
     check_close(out.cpu().numpy(), acc, ab, "skinny, G t-fastest")
 
 
+@pytest.mark.parametrize("wtype,K", [(wl.F32, 301), (wl.F16, 301), (wl.BF16, 302)])
+@pytest.mark.parametrize("T", [33, 70])
+def test_skinny_blocks_of_t_dense_odd_k(q, wtype, K, T):
+    """Dense rows whose K is not a multiple of 4 take the masked loads, also
+    with several blocks of G and several passes over W."""
+    c = wl.make_case(wtype, 96, K, T, seed=360 + T + K)
+    _, acc, ab = oracle.out_prod(wtype, c["W"], c["G"], K, nthreads=ORACLE_THREADS)
+    for v in ("skinny", "skinny_8"):
+        check_close(run(q, c, v), acc, ab, v)
+
+
 def test_q8_0_tiny_workload(q):
     c = wl.workload("q8_0_n128_k256_t64")
     dst, acc, ab = oracle.out_prod(c["type"], c["W"], c["G"], c["K"])
