@@ -131,6 +131,29 @@ def test_shapes_in_turn_share_one_workspace(q, ws):
     assert torch.equal(outs[0].view(torch.int32), outs[3].view(torch.int32))
 
 
+def test_two_streams_with_their_own_workspaces(q):
+    """Split calls on two streams at once, each stream with its own
+    workspace, give the bits of the same calls made one after another."""
+    cases = [wl.make_case(wl.Q4_K, 1024, 2048, 16, seed=975), wl.make_case(wl.Q4_0, 2048, 1024 - 32, 9, seed=976)]
+    ins = [(dev(c["W"]), dev(c["G"])) for c in cases]
+    want = [q.out_prod_ws(c["type"], W, G, c["K"], q.new_workspace(), variant=q.VARIANT_SKINNY_SPLIT)
+            for c, (W, G) in zip(cases, ins)]
+    spaces = [q.new_workspace(), q.new_workspace()]
+    outs = [[torch.empty_like(y) for _ in range(4)] for y in want]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for i in range(4):
+        for j, (c, (W, G)) in enumerate(zip(cases, ins)):
+            with torch.cuda.stream(streams[j]):
+                q.out_prod_ws(c["type"], W, G, c["K"], spaces[j], out=outs[j][i], variant=q.VARIANT_SKINNY_SPLIT,
+                              stream=streams[j])
+    torch.cuda.synchronize()
+    for j in range(2):
+        assert not counters(q, spaces[j]).any()
+        for y in outs[j]:
+            assert torch.equal(y.view(torch.int32), want[j].view(torch.int32)), (j, cases[j]["type"])
+
+
 def test_other_variants_through_the_workspace_call(q, ws):
     """Variants that need no workspace run as retro_out_prod_variant would."""
     c = wl.make_case(wl.Q8_0, 300, 512, 40, seed=980)
