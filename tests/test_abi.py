@@ -155,6 +155,13 @@ def test_plan():
         (q.Q4_K, 14336, 4096, 4096): (q.VARIANT_WS_128x256, 2048, q.VARIANT_WS_256x256),
         (q.Q4_K, 4352, 4096, 4096): (q.VARIANT_WS_256x256, 4096, q.VARIANT_WS_32x256),
         (q.Q4_K, 11008, 4096, 4096): (q.VARIANT_WS_256x256, 8192, q.VARIANT_WS_64x256),
+        # below T = 1024 too: 0.88 against 1.13 ms (Q4_K), 0.91 against 1.15 ms
+        # (Q6_K), 1.47 against 2.07 ms (Q2_K at T = 1000), 0.75 against 0.82 ms
+        # (Q4_0 4096 x 11008)
+        (q.Q4_K, 17408, 5120, 512): (q.VARIANT_WS_128x256, 16384, q.VARIANT_WS_32x256),
+        (q.Q6_K, 17408, 5120, 512): (q.VARIANT_WS_128x256, 16384, q.VARIANT_WS_32x256),
+        (q.Q2_K, 17408, 5120, 1000): (q.VARIANT_WS_256x256, 16384, q.VARIANT_WS_32x256),
+        (q.Q4_0, 11008, 4096, 1000): (q.VARIANT_WS_128x256, 8192, q.VARIANT_WS_32x128),
     }
     for wtype in (q.Q8_0, q.Q4_1, q.Q5_0, q.Q5_1, q.MXFP4, q.NVFP4, q.F16, q.BF16, q.F32):
         two[(wtype, 5120, 17408, 2048)] = (q.VARIANT_WS_128x256, 4096, q.VARIANT_WS2_64x128)
